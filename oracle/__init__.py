@@ -1,0 +1,218 @@
+"""CPU oracle for the n-rank all-reduce path -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product library
+(``reduce_scatter_amd``) never imports it, and this package imports nothing
+from the product: the two share no code.
+
+The arithmetic lives in ``ar_oracle.c`` (plain C, built with gcc and
+``-ffp-contract=off``); this module only marshals numpy arrays to it.  The
+functions follow:
+
+* "NCCL all-reduce" post (rakshithvasudev.github.io), sections "What
+  all-reduce promises" and "The ring, exactly as the kernel runs it":
+  :func:`ring_allreduce`, :func:`ring_reduce_scatter`, :func:`ring_all_gather`;
+  section "The double binary tree": :func:`tree_parent`, :func:`tree_allreduce`.
+* "FSDP collectives 101" (rakshithvasudev.github.io), sections "All-gather:
+  everyone shows their piece" and "Why backward needs a different collective":
+  the semantics of reduce-scatter (rank r keeps slice r) and all-gather.
+
+Array conventions: ``f32`` arrays are ``np.float32``, ``f16`` arrays are
+``np.float16``, ``i32`` arrays are ``np.int32`` and ``bf16`` arrays are
+``np.uint16`` holding the bfloat16 bit patterns.
+
+Parity status: every function here is pinned by ``tests/test_oracle.py``
+(worked examples from the pages, exact brute force, closed forms and
+hand-derived rounding cases).  The exact floating-point hop order inside a
+chunk is a reading (chunk c starts at rank c+1 and ends at rank c); the pages'
+step diagrams were lost, so that order is pinned by hand-derived cases built
+from the reading, not by a printed example.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ar_oracle.c")
+_LIB = os.path.join(_HERE, "libar_oracle.so")
+
+DTYPE_CODE = {"f32": 0, "bf16": 1, "f16": 2, "i32": 3}
+NP_DTYPE = {"f32": np.float32, "bf16": np.uint16, "f16": np.float16, "i32": np.int32}
+OP_CODE = {"sum": 0, "prod": 1, "min": 2, "max": 3, "avg": 4}
+
+_lock = threading.Lock()
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile ``ar_oracle.c`` into ``libar_oracle.so`` with gcc."""
+    if not force and os.path.exists(_LIB) and os.path.getmtime(_LIB) >= os.path.getmtime(_SRC):
+        return _LIB
+    tmp = _LIB + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=gnu11", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+           "-Wall", "-Wextra", "-shared", "-fPIC", _SRC, "-o", tmp]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB):
+            build()
+        lib = ctypes.CDLL(_LIB)
+        vpp = ctypes.POINTER(ctypes.c_void_p)
+        llp = ctypes.POINTER(ctypes.c_longlong)
+        for name in ("orc_ring_allreduce", "orc_ring_reduce_scatter"):
+            f = getattr(lib, name)
+            f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_size_t, vpp, vpp, llp, llp]
+            f.restype = ctypes.c_int
+        lib.orc_ring_all_gather.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_size_t, vpp, vpp, llp, llp]
+        lib.orc_ring_all_gather.restype = ctypes.c_int
+        lib.orc_tree_allreduce.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_size_t, vpp, vpp]
+        lib.orc_tree_allreduce.restype = ctypes.c_int
+        lib.orc_tree_parent.argtypes = [ctypes.c_int, ctypes.c_int]
+        lib.orc_tree_parent.restype = ctypes.c_int
+        lib.orc_allreduce_chunks.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_size_t,
+                                             ctypes.POINTER(ctypes.c_size_t)]
+        lib.orc_allreduce_chunks.restype = None
+        lib.orc_f32_to_bf16.argtypes = [ctypes.c_float]
+        lib.orc_f32_to_bf16.restype = ctypes.c_uint16
+        lib.orc_bf16_to_f32.argtypes = [ctypes.c_uint16]
+        lib.orc_bf16_to_f32.restype = ctypes.c_float
+        lib.orc_f32_to_f16.argtypes = [ctypes.c_float]
+        lib.orc_f32_to_f16.restype = ctypes.c_uint16
+        lib.orc_f16_to_f32.argtypes = [ctypes.c_uint16]
+        lib.orc_f16_to_f32.restype = ctypes.c_float
+        lib.orc_num_threads.argtypes = []
+        lib.orc_num_threads.restype = ctypes.c_int
+        _lib = lib
+        return lib
+
+
+def _ptrs(arrays):
+    arr = (ctypes.c_void_p * max(1, len(arrays)))()
+    for i, a in enumerate(arrays):
+        arr[i] = a.ctypes.data
+    return arr
+
+
+def _check_inputs(xs, dtype, count):
+    want = NP_DTYPE[dtype]
+    for a in xs:
+        if a.dtype != want or not a.flags.c_contiguous or a.ndim != 1 or a.size != count:
+            raise ValueError("oracle input must be a contiguous 1-D %s array of %d elements"
+                             % (np.dtype(want).name, count))
+
+
+def _call(rc):
+    if rc != 0:
+        raise RuntimeError("oracle call failed with code %d" % rc)
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's element loops use."""
+    return int(_load().orc_num_threads())
+
+
+def allreduce_chunks(dtype: str, n: int, count: int) -> list[int]:
+    """All-reduce chunk bounds [off_0 .. off_n] (16-byte units, clamped)."""
+    out = (ctypes.c_size_t * (n + 1))()
+    _load().orc_allreduce_chunks(DTYPE_CODE[dtype], n, count, out)
+    return [int(v) for v in out]
+
+
+def ring_allreduce(xs, dtype: str, op: str, out=None, counters: bool = False):
+    """Ring all-reduce of the rank buffers ``xs`` (list of n 1-D arrays).
+
+    Returns the list of n outputs (``out`` if given; ``out is xs`` is the
+    in-place call), plus ``(hops_per_chunk, bytes_sent_per_rank)`` when
+    ``counters`` is true.
+    """
+    n = len(xs)
+    count = xs[0].size if n else 0
+    _check_inputs(xs, dtype, count)
+    ys = out if out is not None else [np.empty(count, NP_DTYPE[dtype]) for _ in range(n)]
+    _check_inputs(ys, dtype, count)
+    hops = (ctypes.c_longlong * max(1, n))()
+    sent = (ctypes.c_longlong * max(1, n))()
+    _call(_load().orc_ring_allreduce(DTYPE_CODE[dtype], OP_CODE[op], n, count,
+                                     _ptrs(xs), _ptrs(ys), hops, sent))
+    if counters:
+        return ys, list(hops)[:n], list(sent)[:n]
+    return ys
+
+
+def ring_reduce_scatter(xs, dtype: str, op: str, out=None, counters: bool = False):
+    """Ring reduce-scatter: each x_r has n*R elements; rank r gets slice r (R elements)."""
+    n = len(xs)
+    total = xs[0].size
+    if total % n:
+        raise ValueError("reduce-scatter input size must be a multiple of n")
+    R = total // n
+    _check_inputs(xs, dtype, total)
+    ys = out if out is not None else [np.empty(R, NP_DTYPE[dtype]) for _ in range(n)]
+    _check_inputs(ys, dtype, R)
+    hops = (ctypes.c_longlong * n)()
+    sent = (ctypes.c_longlong * n)()
+    _call(_load().orc_ring_reduce_scatter(DTYPE_CODE[dtype], OP_CODE[op], n, R,
+                                          _ptrs(xs), _ptrs(ys), hops, sent))
+    if counters:
+        return ys, list(hops), list(sent)
+    return ys
+
+
+def ring_all_gather(xs, dtype: str, out=None, counters: bool = False):
+    """Ring all-gather: each x_r has R elements; every rank gets x_0 || ... || x_{n-1}."""
+    n = len(xs)
+    R = xs[0].size
+    _check_inputs(xs, dtype, R)
+    ys = out if out is not None else [np.empty(n * R, NP_DTYPE[dtype]) for _ in range(n)]
+    _check_inputs(ys, dtype, n * R)
+    hops = (ctypes.c_longlong * n)()
+    sent = (ctypes.c_longlong * n)()
+    _call(_load().orc_ring_all_gather(DTYPE_CODE[dtype], n, R, _ptrs(xs), _ptrs(ys), hops, sent))
+    if counters:
+        return ys, list(hops), list(sent)
+    return ys
+
+
+def tree_parent(n: int, v: int) -> int:
+    """Parent of rank v in the bit-trick tree over n ranks (-1 for the root 0)."""
+    return int(_load().orc_tree_parent(n, v))
+
+
+def tree_allreduce(xs, dtype: str, op: str, out=None):
+    """Tree all-reduce: reduce up to rank 0 (own first, children ascending), broadcast down."""
+    n = len(xs)
+    count = xs[0].size
+    _check_inputs(xs, dtype, count)
+    ys = out if out is not None else [np.empty(count, NP_DTYPE[dtype]) for _ in range(n)]
+    _check_inputs(ys, dtype, count)
+    _call(_load().orc_tree_allreduce(DTYPE_CODE[dtype], OP_CODE[op], n, count, _ptrs(xs), _ptrs(ys)))
+    return ys
+
+
+# scalar conversions (exposed for the pins of the oracle's own rounding code)
+def f32_to_bf16_bits(v: float) -> int:
+    return int(_load().orc_f32_to_bf16(v))
+
+
+def bf16_bits_to_f32(h: int) -> float:
+    return float(_load().orc_bf16_to_f32(h))
+
+
+def f32_to_f16_bits(v: float) -> int:
+    return int(_load().orc_f32_to_f16(v))
+
+
+def f16_bits_to_f32(h: int) -> float:
+    return float(_load().orc_f16_to_f32(h))

@@ -1,0 +1,579 @@
+"""Pins for the CPU oracle (``oracle/``), CPU only.
+
+Each test ties the oracle to something other than itself: values the pages
+print (``tests/golden/``), exact brute force with Python integers and
+``fractions.Fraction`` on tiny inputs, closed forms the pages state, IEEE
+rounding cases derived by hand from the stated hop order, and library
+conversions (numpy, torch) for the oracle's own rounding code.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+DTYPES = ["f32", "bf16", "f16", "i32"]
+OPS = ["sum", "prod", "min", "max", "avg"]
+
+
+def golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------------------
+# helpers: typed arrays <-> exact Python values
+# ---------------------------------------------------------------------------
+
+def to_dtype(values, dtype):
+    a = np.asarray(values, dtype=np.float64)
+    if dtype == "f32":
+        return a.astype(np.float32)
+    if dtype == "f16":
+        return a.astype(np.float16)
+    if dtype == "i32":
+        return a.astype(np.int32)
+    f = a.astype(np.float32)
+    assert np.all(f == a), "bf16 test values must be exact"
+    bits = f.view(np.uint32)
+    assert np.all(bits & 0xFFFF == 0), "bf16 test values must be exact in bf16"
+    return (bits >> 16).astype(np.uint16)
+
+
+def as_float(arr, dtype):
+    """Exact float64 view of a typed array."""
+    if dtype == "bf16":
+        return (arr.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return arr.astype(np.float64)
+
+
+def wrap32(v: int) -> int:
+    return ((v + (1 << 31)) % (1 << 32)) - (1 << 31)
+
+
+def brute_int(values, op, n):
+    """Direct reduction of exact Python integers, rank order 0..n-1, wrapped to int32."""
+    if op in ("sum", "avg"):
+        s = wrap32(sum(values))
+        if op == "avg":
+            q = abs(s) // n
+            return -q if s < 0 else q          # C division: truncate toward zero
+        return s
+    if op == "prod":
+        p = 1
+        for v in values:
+            p *= v
+        return wrap32(p)
+    return min(values) if op == "min" else max(values)
+
+
+def gamma(k, u):
+    return k * u / (1 - k * u)
+
+
+UNIT_ROUNDOFF = {"f32": 2.0 ** -24, "bf16": 2.0 ** -8 + 2.0 ** -24, "f16": 2.0 ** -11 + 2.0 ** -24}
+
+
+# ---------------------------------------------------------------------------
+# 1. worked examples printed on the pages, in every dtype
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_worked_example_allreduce_sum(dtype):
+    g = golden("worked_examples.json")["allreduce_sum"]
+    xs = [to_dtype(v, dtype) for v in g["inputs"]]
+    for fn in (oracle.ring_allreduce, oracle.tree_allreduce):
+        ys = fn(xs, dtype, "sum")
+        for y, want in zip(ys, g["outputs"]):
+            assert as_float(y, dtype).tolist() == want
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_worked_example_reduce_scatter_avg(dtype):
+    g = golden("worked_examples.json")["reduce_scatter_avg"]
+    xs = [to_dtype(v, dtype) for v in g["inputs"]]
+    ys = oracle.ring_reduce_scatter(xs, dtype, "avg")
+    for y, want in zip(ys, g["outputs"]):
+        assert as_float(y, dtype).tolist() == want
+    # the full average is what all-reduce(avg) would leave on every rank
+    full = oracle.ring_allreduce(xs, dtype, "avg")
+    assert as_float(full[0], dtype).tolist() == g["never_assembled"]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_worked_example_all_gather(dtype):
+    g = golden("worked_examples.json")["all_gather"]
+    xs = [to_dtype(v, dtype) for v in g["inputs"]]
+    ys = oracle.ring_all_gather(xs, dtype)
+    for y, want in zip(ys, g["outputs"]):
+        assert as_float(y, dtype).tolist() == want
+
+
+def test_worked_example_gloo_route_matches_for_two_ranks():
+    """The demo's CPU branch sums and then divides by the world size; with n = 2
+    pre-scaling by 1/2 is exact, so both routes print the same numbers."""
+    g = golden("worked_examples.json")["reduce_scatter_avg"]
+    xs = [to_dtype(v, "f32") for v in g["inputs"]]
+    summed = oracle.ring_reduce_scatter(xs, "f32", "sum")
+    avg = oracle.ring_reduce_scatter(xs, "f32", "avg")
+    for s, a in zip(summed, avg):
+        assert np.array_equal(s / np.float32(2), a)
+
+
+# ---------------------------------------------------------------------------
+# 2. exact brute force on tiny inputs (all n in 1..9, many counts)
+# ---------------------------------------------------------------------------
+
+def _data(dtype, op, n, count, seed):
+    """Per-rank data for which the reduction is exact in every dtype."""
+    rg = np.random.default_rng([seed, n, count])
+    if dtype == "i32":
+        if op == "prod":
+            return [rg.integers(-(1 << 16), 1 << 16, size=count).astype(np.int32) for _ in range(n)]
+        return [rg.integers(-(1 << 30), 1 << 30, size=count).astype(np.int32) for _ in range(n)]
+    if op == "prod":
+        return [to_dtype(rg.choice([-2.0, -1.0, -0.5, 0.5, 1.0, 2.0], size=count), dtype) for _ in range(n)]
+    if op in ("min", "max"):
+        return [to_dtype(rg.normal(size=count).astype(np.float32).astype(np.float64)
+                         if dtype == "f32" else rg.integers(-100, 100, size=count), dtype) for _ in range(n)]
+    return [to_dtype(rg.integers(-8, 9, size=count), dtype) for _ in range(n)]
+
+
+def _brute_elem(vals, dtype, op, n):
+    if dtype == "i32":
+        return brute_int([int(v) for v in vals], op, n)
+    fr = [Fraction(float(v)) for v in vals]
+    if op == "sum":
+        return sum(fr)
+    if op == "avg":
+        return sum(fr) / n
+    if op == "prod":
+        p = Fraction(1)
+        for v in fr:
+            p *= v
+        return p
+    return min(fr) if op == "min" else max(fr)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("op", OPS)
+def test_brute_force_allreduce(dtype, op):
+    for n in range(1, 10):
+        if op == "avg" and dtype != "i32" and n not in (1, 2, 4, 8):
+            continue                       # inexact pre-scale: covered by the error-bound test
+        for count in list(range(0, 21)) + [31, 37]:
+            xs = _data(dtype, op, n, count, 7)
+            ring = oracle.ring_allreduce(xs, dtype, op)
+            tree = oracle.tree_allreduce(xs, dtype, op)
+            fx = [as_float(x, dtype) if dtype != "i32" else x.astype(np.int64) for x in xs]
+            want = [_brute_elem([f[i] for f in fx], dtype, op, n) for i in range(count)]
+            for r in range(n):
+                for ys in (ring, tree):
+                    got = as_float(ys[r], dtype) if dtype != "i32" else ys[r].astype(np.int64)
+                    assert [Fraction(float(v)) if dtype != "i32" else int(v) for v in got] == want, \
+                        (dtype, op, n, count, r)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("op", OPS)
+def test_brute_force_reduce_scatter_and_all_gather(dtype, op):
+    for n in range(1, 10):
+        if op == "avg" and dtype != "i32" and n not in (1, 2, 4, 8):
+            continue
+        for R in range(0, 6):
+            xs = _data(dtype, op, n, n * R, 11)
+            ys = oracle.ring_reduce_scatter(xs, dtype, op)
+            fx = [as_float(x, dtype) if dtype != "i32" else x.astype(np.int64) for x in xs]
+            for r in range(n):
+                want = [_brute_elem([f[r * R + i] for f in fx], dtype, op, n) for i in range(R)]
+                got = as_float(ys[r], dtype) if dtype != "i32" else ys[r].astype(np.int64)
+                assert [Fraction(float(v)) if dtype != "i32" else int(v) for v in got] == want
+            # all-gather is pure assembly: bit copies of every piece, in rank order
+            gs = oracle.ring_all_gather(ys, dtype)
+            cat = np.concatenate(ys) if n else np.empty(0)
+            for g in gs:
+                assert g.tobytes() == cat.tobytes()
+
+
+def test_c1_workload_is_exact():
+    """C1: integers in [-8, 8] stored as fp32, n = 4: every sum is exact, so the
+    ring, the tree and a direct integer sum agree bit for bit."""
+    xs = workloads.c1_inputs()
+    want = sum(x.astype(np.int64) for x in xs).astype(np.float32)
+    for fn in (oracle.ring_allreduce, oracle.tree_allreduce):
+        for y in fn(xs, "f32", "sum"):
+            assert y.tobytes() == want.tobytes()
+
+
+# ---------------------------------------------------------------------------
+# 3. error bounds against exact sums (general data, order-dependent rounding)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("op", ["sum", "avg"])
+def test_recursive_summation_bound(dtype, op):
+    """|computed - exact| <= gamma_k * sum|x_i| (recursive summation; the avg
+    pre-scale adds two more roundings: fp32(1/n) and the multiply)."""
+    u = UNIT_ROUNDOFF[dtype]
+    for n in (2, 3, 5, 7, 8, 9, 16, 72):
+        count = 48
+        xs = [workloads.normal(5, n, r, count, 1.0, dtype) for r in range(n)]
+        fx = [as_float(x, dtype) for x in xs]
+        for fn in (oracle.ring_allreduce, oracle.tree_allreduce):
+            got = as_float(fn(xs, dtype, op)[0], dtype)
+            for i in range(count):
+                terms = [Fraction(f[i]) for f in fx]
+                exact = sum(terms) / (n if op == "avg" else 1)
+                k = (n - 1) if op == "sum" else (n + 1)
+                bound = gamma(k, u) * float(sum(abs(t) for t in terms) / (n if op == "avg" else 1))
+                # bf16/fp16: the final fp32 -> storage rounding of an exact value
+                assert abs(Fraction(got[i]) - exact) <= Fraction(bound) + Fraction(abs(float(exact)) * u), \
+                    (dtype, op, n, i)
+
+
+def test_prod_relative_bound():
+    u = 2.0 ** -24
+    for n in (3, 5, 9, 17):
+        xs = [workloads.uniform(6, n, r, 64, 0.5, 2.0, "f32") for r in range(n)]
+        got = oracle.ring_allreduce(xs, "f32", "prod")[0]
+        for i in range(64):
+            exact = Fraction(1)
+            for x in xs:
+                exact *= Fraction(float(x[i]))
+            assert abs(Fraction(float(got[i])) - exact) <= Fraction(gamma(n - 1, u)) * abs(exact)
+
+
+def test_float_avg_power_of_two_is_scaled_sum():
+    """For n = 2^k the pre-scale by 2^-k is exact (no underflow here), so
+    avg == sum * 2^-k bit for bit, whatever the hop order."""
+    for n in (2, 4, 8, 16):
+        xs = [workloads.normal(8, n, r, 256, 1e-3, "f32") for r in range(n)]
+        s = oracle.ring_allreduce(xs, "f32", "sum")[0]
+        a = oracle.ring_allreduce(xs, "f32", "avg")[0]
+        assert a.tobytes() == (s * np.float32(1.0 / n)).tobytes()
+
+
+def test_float_avg_pre_scale_vs_sum_then_divide():
+    """The two float-avg routes on the pages (pre-scale by 1/n as read; the
+    demo's sum-then-divide) agree closely for n = 72 but not bit for bit."""
+    n = 72
+    xs = [workloads.normal(9, 0, r, 4096, 1e-3, "f32") for r in range(n)]
+    a = oracle.ring_allreduce(xs, "f32", "avg")[0].astype(np.float64)
+    s = (oracle.ring_allreduce(xs, "f32", "sum")[0] / np.float32(n)).astype(np.float64)
+    scale = np.abs(s).max()
+    assert np.max(np.abs(a - s)) <= 1e-5 * scale
+    assert not np.array_equal(a, s)      # the reading matters: the routes differ
+
+
+# ---------------------------------------------------------------------------
+# 4. the hop order, pinned by IEEE rounding cases derived by hand
+# ---------------------------------------------------------------------------
+#
+# With B = 2^p (p = 24 for fp32, 8 for bf16, 11 for fp16: the first power of
+# two whose ulp is 2), B + 1 is a tie that rounds back to B (even), while
+# 1 - B = -(B - 1) is exact.  Take contributions {+B, -B, +1} with zeros on
+# the other ranks and add them left to right with per-hop rounding:
+#   +B .. 1 .. -B  ->  (B + 1) - B = 0        1 .. +B .. -B  ->  (1 + B) - B = 0
+#   +B .. -B .. 1  ->  0 + 1 = 1              -B first, or 1 .. -B .. +B  ->  1
+# so the result is 0 exactly when +B and the 1 both come before -B.  The
+# expected values below apply that rule to the stated order: chunk c's chain
+# is ranks c+1, c+2, ..., c (mod n).
+
+BIG = {"f32": 2.0 ** 24, "bf16": 2.0 ** 8, "f16": 2.0 ** 11}
+
+
+def _chain_result(chain, pos_big, pos_neg, pos_one):
+    i_b, i_n, i_1 = chain.index(pos_big), chain.index(pos_neg), chain.index(pos_one)
+    return 0.0 if (i_b < i_n and i_1 < i_n) else 1.0
+
+
+def _stated_chain(n, c):
+    return [(c + k) % n for k in range(1, n + 1)]
+
+
+def _order_cases(dtype, n, trials, seed, chain_of=_stated_chain):
+    B = BIG[dtype]
+    u = 16 // (4 if dtype == "f32" else 2)
+    count = n * u                                      # chunk c = elements [c*u, (c+1)*u)
+    rg = np.random.default_rng(seed)
+    cases = []
+    for _ in range(trials):
+        xs = [np.zeros(count) for _ in range(n)]
+        expect = np.zeros(count)
+        for c in range(n):
+            pb, pn, p1 = (int(v) for v in rg.choice(n, size=3, replace=False))
+            for i in range(c * u, (c + 1) * u):
+                xs[pb][i], xs[pn][i], xs[p1][i] = B, -B, 1.0
+                expect[i] = _chain_result(chain_of(n, c), pb, pn, p1)
+        cases.append((xs, expect))
+    return cases
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+def test_ring_hop_order_rounding_cases(dtype):
+    for n in (3, 4, 5, 8):
+        u = 16 // (4 if dtype == "f32" else 2)
+        assert oracle.allreduce_chunks(dtype, n, n * u) == [c * u for c in range(n + 1)]
+        for xs, expect in _order_cases(dtype, n, 12, n):
+            for y in oracle.ring_allreduce([to_dtype(x, dtype) for x in xs], dtype, "sum"):
+                assert as_float(y, dtype).tolist() == expect.tolist(), (dtype, n)
+
+
+def test_ring_hop_order_cases_have_power():
+    """The same cases, with the two nearest misreadings of the order (the chain
+    starts at the owner; every chunk in rank order 0..n-1), predict different
+    results, so the test above would catch either mistake."""
+    owner_first = lambda n, c: [(c + k) % n for k in range(n)]
+    rank_order = lambda n, c: list(range(n))
+    for n in (3, 4, 5, 8):
+        stated = [e for _, e in _order_cases("f32", n, 12, n)]
+        for alt in (owner_first, rank_order):
+            other = [e for _, e in _order_cases("f32", n, 12, n, chain_of=alt)]
+            assert any(not np.array_equal(a, b) for a, b in zip(stated, other)), n
+
+
+def test_bf16_rounds_at_every_hop():
+    """bf16 partials are rounded to bf16 after each hop: 256 + 1 -> 256, so
+    (256 + 1) - 256 = 0, where an fp32 accumulator would give 1."""
+    n, u = 3, 8
+    xs = [np.zeros(n * u) for _ in range(n)]
+    # chunk 0's chain is 1, 2, 0
+    xs[1][:u], xs[2][:u], xs[0][:u] = 256.0, 1.0, -256.0
+    y = oracle.ring_allreduce([to_dtype(x, "bf16") for x in xs], "bf16", "sum")[0]
+    assert as_float(y, "bf16")[:u].tolist() == [0.0] * u
+    y32 = oracle.ring_allreduce([x.astype(np.float32) for x in xs], "f32", "sum")[0]
+    assert y32[:u].tolist() == [1.0] * u
+
+
+def test_min_max_ties_keep_incoming():
+    """min/max keep the incoming partial on ties: visible with -0.0 and +0.0."""
+    n, u = 2, 4
+    # chunk 0's chain: rank 1 then rank 0.  incoming = rank 1's value.
+    a = np.zeros(n * u, np.float32)
+    b = np.zeros(n * u, np.float32)
+    b[:u] = -0.0
+    ymin = oracle.ring_allreduce([a, b], "f32", "min")[0]
+    ymax = oracle.ring_allreduce([a, b], "f32", "max")[0]
+    assert np.signbit(ymin[:u]).all() and np.signbit(ymax[:u]).all()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+def test_two_ranks_is_one_ieee_operation(dtype):
+    """With n = 2 every element is a single operation, so each result equals the
+    library's own correctly rounded operation in that dtype (numpy for fp32
+    and fp16, torch for bf16)."""
+    import torch
+    count = 4096
+    xs = [workloads.normal(10, 0, r, count, 1.0, dtype) for r in range(2)]
+    fx = [as_float(x, dtype) for x in xs]
+    for op in ("sum", "prod", "avg"):
+        got = as_float(oracle.ring_allreduce(xs, dtype, op)[0], dtype)
+        if dtype == "bf16":
+            ta = torch.tensor(fx[0], dtype=torch.float32).to(torch.bfloat16)
+            tb = torch.tensor(fx[1], dtype=torch.float32).to(torch.bfloat16)
+            if op == "avg":
+                ta, tb = (ta.float() * 0.5).to(torch.bfloat16), (tb.float() * 0.5).to(torch.bfloat16)
+            r = (ta + tb) if op != "prod" else (ta * tb)
+            want = r.float().numpy().astype(np.float64)
+        else:
+            npd = np.float32 if dtype == "f32" else np.float16
+            a, b = fx[0].astype(npd), fx[1].astype(npd)
+            if op == "avg":
+                a, b = a * npd(0.5), b * npd(0.5)
+            want = ((a + b) if op != "prod" else (a * b)).astype(np.float64)
+        # chunk 0 is summed as rank1 (+) rank0, chunk 1 as rank0 (+) rank1: the same for + and *
+        assert np.array_equal(got, want), (dtype, op)
+
+
+# ---------------------------------------------------------------------------
+# 5. closed forms: hop counts and bytes on the wire
+# ---------------------------------------------------------------------------
+
+def test_ring_hops_and_bytes_closed_forms():
+    cf = golden("closed_forms.json")["ring_steps"]["n_to_hops"]
+    for n in (2, 3, 4, 8, 16):
+        count = n * 4 * 3
+        xs = [np.ones(count, np.float32) for _ in range(n)]
+        _, hops, sent = oracle.ring_allreduce(xs, "f32", "sum", counters=True)
+        assert hops == [2 * (n - 1)] * n
+        S = count * 4
+        assert sent == [2 * (n - 1) * S // n] * n          # a hair under 2S per rank
+        if str(n) in cf:
+            assert hops[0] == cf[str(n)]
+    assert 2 * (1024 - 1) == cf["1024"]
+    # reduce-scatter and all-gather each move half of that
+    n, R = 8, 12
+    xs = [np.ones(n * R, np.float32) for _ in range(n)]
+    ys, hops, sent = oracle.ring_reduce_scatter(xs, "f32", "sum", counters=True)
+    assert hops == [n - 1] * n and sent == [(n - 1) * R * 4] * n
+    _, hops, sent = oracle.ring_all_gather(ys, "f32", counters=True)
+    assert hops == [n - 1] * n and sent == [(n - 1) * R * 4] * n
+
+
+def test_allreduce_chunks_16_byte_units():
+    for dtype, u in (("f32", 4), ("bf16", 8), ("i32", 4)):
+        for n in (1, 3, 8, 72):
+            for count in (0, 1, 5, 17, 1000, 4099, 25 * 2 ** 20 // 4):
+                off = oracle.allreduce_chunks(dtype, n, count)
+                assert off[0] == 0 and off[-1] == count and len(off) == n + 1
+                assert all(a <= b for a, b in zip(off, off[1:]))
+                assert all(o % u == 0 for o in off[:-1])
+                V = -(-count // u)
+                lens = [-(-min(count, b) // u) * u - a for a, b in zip(off, off[1:])]
+                assert max(lens) - min(lens) <= u if V >= n else True
+                if count % (n * u) == 0:
+                    assert off == [c * count // n for c in range(n + 1)]
+
+
+# ---------------------------------------------------------------------------
+# 6. the tree
+# ---------------------------------------------------------------------------
+
+def test_tree_matches_the_14_rank_picture():
+    g = golden("tree14.json")
+    n = g["n"]
+    parent = [oracle.tree_parent(n, v) for v in range(n)]
+    assert parent == g["parent"]
+    children = {v: [c for c in range(n) if parent[c] == v] for v in range(n)}
+    assert sorted(v for v in range(n) if not children[v]) == g["leaves"]
+
+
+def _depth(n):
+    d = 0
+    for v in range(n):
+        k, p = 0, v
+        while p != 0:
+            p = oracle.tree_parent(n, p)
+            k += 1
+            assert k <= n
+        d = max(d, k)
+    return d
+
+
+def test_tree_shape_for_all_small_n():
+    cf = golden("closed_forms.json")["tree_depth"]["n_to_depth"]
+    for n in range(1, 130):
+        parent = [oracle.tree_parent(n, v) for v in range(n)]
+        assert parent[0] == -1
+        assert all(0 <= parent[v] < n for v in range(1, n))
+        nchild = [sum(1 for c in range(n) if parent[c] == v) for v in range(n)]
+        assert max(nchild) <= 2
+        assert _depth(n) == (math.ceil(math.log2(n)) if n > 1 else 0)
+    assert _depth(1024) == cf["1024"]
+
+
+def test_tree_order_own_first_then_children_ascending():
+    """n = 4: parent(1) = parent(3) = 2, parent(2) = 0, so the root value is
+    x0 + ((x2 + x1) + x3).  Cases derived by hand with B = 2^24:
+      x2 = B, x1 = 1, x3 = -B: (B + 1) -> B, B - B = 0            -> 0
+        (children first, (x1 + x3) + x2 = (1 - B) + B, would give 1;
+         children descending, (x2 + x3) + x1 = 0 + 1, would give 1)
+      x2 = 1, x1 = -B, x3 = B: (1 - B) exact, + B = 1             -> 1
+      x0 = -B, x2 = B, x1 = x3 = 0: 0 + 0, then -B + B = 0        -> 0
+      x0 = 1, x1 = B, x3 = -B, x2 = 0: (0 + B) - B = 0, 1 + 0     -> 1"""
+    B = 2.0 ** 24
+
+    def run(x0, x1, x2, x3):
+        xs = [np.full(4, v, np.float32) for v in (x0, x1, x2, x3)]
+        out = oracle.tree_allreduce(xs, "f32", "sum")
+        assert all(o.tobytes() == out[0].tobytes() for o in out)
+        return float(out[3][0])
+
+    assert [oracle.tree_parent(4, v) for v in range(4)] == [-1, 2, 0, 2]
+    assert run(0.0, 1.0, B, -B) == 0.0
+    assert run(0.0, -B, 1.0, B) == 1.0
+    assert run(-B, 0.0, B, 0.0) == 0.0
+    assert run(1.0, B, 0.0, -B) == 1.0
+
+
+def test_tree_and_ring_agree_when_exact_and_within_bound_otherwise():
+    n = 8
+    xs = [workloads.normal(12, 0, r, 1024, 1e-3, "f32") for r in range(n)]
+    ring = oracle.ring_allreduce(xs, "f32", "sum")[0].astype(np.float64)
+    tree = oracle.tree_allreduce(xs, "f32", "sum")[0].astype(np.float64)
+    assert np.max(np.abs(ring - tree)) <= 1e-6 * np.max(np.abs(ring))
+
+
+# ---------------------------------------------------------------------------
+# 7. invariants the pages state
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_allreduce_is_reduce_scatter_then_all_gather(dtype):
+    """all-reduce = reduce-scatter + all-gather, bit for bit, when the chunks of
+    the two calls coincide (count a multiple of n 16-byte units)."""
+    for n in (1, 2, 3, 5, 8):
+        u = 16 // workloads.ELEM_SIZE[dtype]
+        count = n * u * 7
+        for op in OPS:
+            xs = [workloads.random_values(13, n, r, count, dtype) for r in range(n)]
+            ar = oracle.ring_allreduce(xs, dtype, op)
+            ag = oracle.ring_all_gather(oracle.ring_reduce_scatter(xs, dtype, op), dtype)
+            for a, b in zip(ar, ag):
+                assert a.tobytes() == b.tobytes(), (dtype, n, op)
+            for a in ar[1:]:
+                assert a.tobytes() == ar[0].tobytes()          # every rank identical
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_in_place_equals_out_of_place(dtype):
+    n, count = 5, 203
+    for op in OPS:
+        xs = [workloads.random_values(14, 0, r, count, dtype) for r in range(n)]
+        ref = oracle.ring_allreduce(xs, dtype, op)
+        buf = [x.copy() for x in xs]
+        oracle.ring_allreduce(buf, dtype, op, out=buf)
+        for a, b in zip(ref, buf):
+            assert a.tobytes() == b.tobytes()
+        buf = [x.copy() for x in xs]
+        oracle.tree_allreduce(buf, dtype, op, out=buf)
+        for a, b in zip(oracle.tree_allreduce(xs, dtype, op), buf):
+            assert a.tobytes() == b.tobytes()
+
+
+# ---------------------------------------------------------------------------
+# 8. the oracle's own conversions, against library routines
+# ---------------------------------------------------------------------------
+
+def _edge_f32():
+    vals = [0.0, -0.0, 1.0, -1.0, 65504.0, 65519.99, 65520.0, 1e-8, 2.0 ** -24, 2.0 ** -25,
+            2.0 ** -25 * 1.0000001, 3 * 2.0 ** -26, 2.0 ** -14, 2.0 ** -14 - 2.0 ** -25,
+            float(np.finfo(np.float32).max), float(np.finfo(np.float32).tiny), float("inf"), float("-inf"),
+            1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -9, 256.0 + 1.0, 3.0e38]
+    rg = np.random.default_rng(0)
+    bits = rg.integers(0, 2 ** 32, size=60000, dtype=np.uint64).astype(np.uint32)
+    rnd = bits.view(np.float32)
+    rnd = rnd[np.isfinite(rnd)]
+    scaled = (rg.standard_normal(60000) * 10.0 ** rg.uniform(-9, 6, 60000)).astype(np.float32)
+    return np.concatenate([np.array(vals, np.float32), rnd, scaled])
+
+
+def test_bf16_rounding_matches_torch():
+    import torch
+    v = _edge_f32()
+    want = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = np.array([oracle.f32_to_bf16_bits(float(x)) for x in v], np.uint16)
+    assert np.array_equal(got, want)
+    back = np.array([oracle.bf16_bits_to_f32(int(h)) for h in want[:5000]], np.float32)
+    assert np.array_equal(back.view(np.uint32), want[:5000].astype(np.uint32) << 16)
+
+
+def test_f16_conversions_match_numpy():
+    v = _edge_f32()
+    want = v.astype(np.float16).view(np.uint16)
+    got = np.array([oracle.f32_to_f16_bits(float(x)) for x in v], np.uint16)
+    assert np.array_equal(got, want)
+    allh = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    exp = allh.view(np.float16).astype(np.float32)
+    got32 = np.array([oracle.f16_bits_to_f32(int(h)) for h in allh], np.float32)
+    finite = np.isfinite(exp)
+    assert np.array_equal(got32[finite].view(np.uint32), exp[finite].view(np.uint32))
+    assert np.all(np.isnan(got32[np.isnan(exp)]))
