@@ -1,0 +1,211 @@
+#!/usr/bin/env python3
+"""Benchmark: all-reduce of n = 8 fp32 rank buffers of 256 MB each (64 Mi
+elements per rank, N(0, 1e-3) synthetic gradients), all resident in one
+MI355X's HBM.
+
+One step = one ``ar_allreduce`` call through the C ABI with the schedule left
+to the cost model (it plans, partitions, loads with the avg/sum pre-op, runs
+the reduce-scatter hops, the postOp and the all-gather hops in one fused
+pass).  The JSON line reports:
+
+* ``value``: algbw = S / t_step (S = 256 MB per rank), GB/s (1e9 bytes/s);
+* ``roofline``: the dominant kernel (the fused all-reduce) against HBM peak,
+  ``achieved`` = 2*n*S algorithmic bytes / its average launch duration,
+  timed with HIP events recorded on the launch stream around every launch;
+  ``traffic`` = measured HBM bytes per launch from the committed counter
+  summary when it was taken on the current kernel source, else null;
+* ``cpu_baseline``: the CPU oracle on a bounded sample of the same workload;
+* ``detail``: the other schedules and ops on the same buffers.
+
+``--gpus N`` with N > 1 exits: the rank buffers live on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+N_RANKS = 8
+COUNT = 64 << 20                      # fp32 elements per rank (256 MB)
+PEAK_HBM_GBPS = 8000.0                # MI355X published HBM3E bandwidth
+METRIC = "all-reduce algbw GB/s + % peak HBM BW (n=8, fp32, 256MB/rank)"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_allreduce_n8_f32_256MB.traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "reduce_scatter_amd", "csrc", "fused.hip")
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--op", default="sum", choices=["sum", "avg"])
+    p.add_argument("--sched", default="auto", choices=["auto", "ring", "tree", "fused"])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-detail", action="store_true")
+    p.add_argument("--copy-probe", action="store_true",
+                   help="time only a plain device copy of 2 GB (for HBM counter calibration) and exit")
+    return p.parse_args()
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on this exact kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def time_calls(fn, steps, warmup, stream):
+    """Warm up, then time ``steps`` calls: one event pair around the whole
+    region and one around every call, all recorded on ``stream``."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(steps):
+        starts[i].record(stream)
+        fn()
+        ends[i].record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    per = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    return total_ms / steps, sum(per) / steps, per[len(per) // 2]
+
+
+def copy_probe(args):
+    import torch
+    src = torch.empty(512 << 20, dtype=torch.float32, device="cuda")      # 2 GB
+    dst = torch.empty_like(src)
+    src.fill_(1.0)
+    stream = torch.cuda.current_stream()
+    step_ms, launch_ms, _ = time_calls(lambda: dst.copy_(src), args.steps, args.warmup, stream)
+    print(json.dumps({"copy_probe_bytes_read": src.numel() * 4, "copy_probe_bytes_written": src.numel() * 4,
+                      "launch_ms": round(launch_ms, 4),
+                      "gbps": round(2 * src.numel() * 4 / (launch_ms * 1e-3) / 1e9, 1)}), flush=True)
+
+
+def cpu_baseline():
+    """The oracle, as it stands, on a bounded sample of the workload: the same
+    ring all-reduce over n = 8 ranks of 16 Mi fp32 elements (a quarter of a
+    rank buffer), N(0, 1e-3).  A first call warms the host allocator; the
+    second is timed.  Reported as algbw GB/s of the sample."""
+    import oracle
+    import workloads
+    count = 16 << 20
+    xs = [workloads.normal(1, 0, r, count, 1e-3) for r in range(N_RANKS)]
+    oracle.ring_allreduce(xs, "f32", "sum")
+    t = time.perf_counter()
+    oracle.ring_allreduce(xs, "f32", "sum")
+    dt = time.perf_counter() - t
+    return {"value": round(count * 4 / dt / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": "ring all-reduce (sum), n=8, fp32, 16 Mi elements per rank (1/4 of the 256 MB workload), "
+                      "%.2f s" % dt}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py: this workload keeps all %d logical ranks in ONE GPU's HBM; "
+              "runs on more than one GPU are not part of it (got --gpus %d)" % (N_RANKS, args.gpus),
+              file=sys.stderr)
+        return 2
+    if args.steps < 1:
+        print("--steps must be >= 1", file=sys.stderr)
+        return 2
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 2
+    torch.cuda.set_device(0)
+    if args.copy_probe:
+        copy_probe(args)
+        return 0
+
+    import reduce_scatter_amd as ar
+    import workloads
+
+    stream = torch.cuda.current_stream()
+    xs = [workloads.device_normal(1, 0, r, COUNT, 1e-3, "f32") for r in range(N_RANKS)]
+    ys = [torch.empty_like(x) for x in xs]
+    torch.cuda.synchronize()
+    S = COUNT * 4
+    alg_bytes = 2 * N_RANKS * S
+
+    def step():
+        ar.ar_allreduce(xs, ys, COUNT, "f32", args.op, sched=args.sched, stream=stream)
+
+    plan = ar.ar_plan("allreduce", COUNT, "f32", args.op, N_RANKS)
+    chosen = plan.chosen if args.sched == "auto" else args.sched
+    step_ms, launch_ms, launch_med_ms = time_calls(step, args.steps, args.warmup, stream)
+    algbw = S / (step_ms * 1e-3) / 1e9
+    achieved = alg_bytes / (launch_ms * 1e-3) / 1e9
+
+    detail = {}
+    if not args.no_detail:
+        for sched in ("fused", "ring", "tree"):
+            for op in ("sum", "avg"):
+                ms, lms, _ = time_calls(
+                    lambda: ar.ar_allreduce(xs, ys, COUNT, "f32", op, sched=sched, stream=stream), 10, 2, stream)
+                detail["%s_%s" % (sched, op)] = {"ms": round(lms, 4),
+                                                 "algbw_GBps": round(S / (lms * 1e-3) / 1e9, 1),
+                                                 "hbm_GBps": round(alg_bytes / (lms * 1e-3) / 1e9, 1)}
+        detail["planner"] = {"chosen": plan.chosen, "predicted_us": {k: round(v, 1) for k, v in
+                                                                    plan.predicted_us.items()}}
+
+    out = {
+        "metric": METRIC,
+        "value": round(algbw, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "all-reduce, n=8 logical ranks on one GPU, fp32, 64Mi elements (256 MB) per rank, "
+                               "N(0,1e-3), op=%s, schedule=%s (%s), out of place" % (args.op, args.sched, chosen),
+                   "n_ranks": N_RANKS, "count_per_rank": COUNT, "bytes_per_rank": S, "op": args.op,
+                   "schedule": chosen},
+        "hbm_GBps": round(achieved, 1),
+        "pct_peak_hbm": round(100.0 * achieved / PEAK_HBM_GBPS, 2),
+        "busbw_GBps": round(algbw * 2 * (N_RANKS - 1) / N_RANKS, 2),
+        "roofline": {"bound": "hbm", "kernel": "fused_allreduce_kernel<f32,%s>" % args.op,
+                     "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": measured_traffic(),
+                     "algorithmic_bytes_per_launch": alg_bytes, "avg_launch_ms": round(launch_ms, 4),
+                     "median_launch_ms": round(launch_med_ms, 4)},
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(),
+        "detail": detail,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -12,7 +12,9 @@ functions follow:
 * "NCCL all-reduce" post (rakshithvasudev.github.io), sections "What
   all-reduce promises" and "The ring, exactly as the kernel runs it":
   :func:`ring_allreduce`, :func:`ring_reduce_scatter`, :func:`ring_all_gather`;
-  section "The double binary tree": :func:`tree_parent`, :func:`tree_allreduce`.
+  section "The double binary tree": :func:`tree_parent`, :func:`tree_allreduce`;
+  the plain element-wise definition (exact for int32 and min/max):
+  :func:`direct_reduce`.
 * "FSDP collectives 101" (rakshithvasudev.github.io), sections "All-gather:
   everyone shows their piece" and "Why backward needs a different collective":
   the semantics of reduce-scatter (rank r keeps slice r) and all-gather.
@@ -79,6 +81,9 @@ def _load():
         lib.orc_ring_all_gather.restype = ctypes.c_int
         lib.orc_tree_allreduce.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_size_t, vpp, vpp]
         lib.orc_tree_allreduce.restype = ctypes.c_int
+        lib.orc_direct_reduce.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_size_t, vpp,
+                                          ctypes.c_void_p]
+        lib.orc_direct_reduce.restype = ctypes.c_int
         lib.orc_tree_parent.argtypes = [ctypes.c_int, ctypes.c_int]
         lib.orc_tree_parent.restype = ctypes.c_int
         lib.orc_allreduce_chunks.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_size_t,
@@ -183,6 +188,18 @@ def ring_all_gather(xs, dtype: str, out=None, counters: bool = False):
     if counters:
         return ys, list(hops), list(sent)
     return ys
+
+
+def direct_reduce(xs, dtype: str, op: str):
+    """The plain definition x_0 (+) ... (+) x_{n-1} (then the avg rule), one
+    output array.  Exact for every schedule when dtype is i32 or op is
+    min/max; works on any slice of the rank buffers."""
+    n = len(xs)
+    count = xs[0].size
+    _check_inputs(xs, dtype, count)
+    y = np.empty(count, NP_DTYPE[dtype])
+    _call(_load().orc_direct_reduce(DTYPE_CODE[dtype], OP_CODE[op], n, count, _ptrs(xs), y.ctypes.data))
+    return y
 
 
 def tree_parent(n: int, v: int) -> int:

@@ -525,6 +525,30 @@ int orc_tree_allreduce(int dtype, int op, int n, size_t count, const void *const
     return ORC_OK;
 }
 
+/* ------------------------------------------------------------------------ */
+/* The plain definition, y = x_0 (+) x_1 (+) ... (+) x_{n-1} in rank order,   */
+/* then the avg rule.  For int32 (sum / prod wrap modulo 2^32, which is       */
+/* associative and commutative) and for min / max this is exactly what every */
+/* schedule computes, whatever its order ("What all-reduce promises": the     */
+/* buffers are combined element-wise and every rank gets the same result).   */
+/* It reads element i of every rank at offset i, so it can be applied to      */
+/* any slice of the buffers.  Only int32 of any op, or min / max of any      */
+/* dtype, are accepted.                                                      */
+/* ------------------------------------------------------------------------ */
+int orc_direct_reduce(int dtype, int op, int n, size_t count, const void *const *x, void *y)
+{
+    if (bad_args(dtype, op, n)) return ORC_EBADARG;
+    if (dtype != ORC_I32 && op != ORC_MIN && op != ORC_MAX) return ORC_EBADARG;
+    long long i;
+#pragma omp parallel for schedule(static)
+    for (i = 0; i < (long long)count; ++i) {
+        val_t acc = load_elem(dtype, x[0], (size_t)i);
+        for (int r = 1; r < n; ++r) acc = combine(dtype, op, acc, load_elem(dtype, x[r], (size_t)i));
+        store_elem(dtype, y, (size_t)i, post_op(dtype, op, n, acc));
+    }
+    return ORC_OK;
+}
+
 int orc_num_threads(void)
 {
 #ifdef _OPENMP

@@ -1,0 +1,45 @@
+"""reduce_scatter_amd -- n-rank all-reduce / reduce-scatter / all-gather on one
+MI355X, with the n rank buffers resident in its HBM.
+
+This package is a thin ctypes binding over ``libar.so`` (HIP kernels for
+gfx950 plus the C ABI declared in ``include/ar.h``).  The functions keep the C
+names and only marshal arguments: every step of the collective runs in the
+library's kernels.  There is no CPU fallback; importing the package fails
+loudly when the library has not been built (``python -m
+reduce_scatter_amd.build``).
+"""
+from __future__ import annotations
+
+from ._binding import (  # noqa: F401
+    AR_MAX_RANKS,
+    COLLS,
+    DTYPES,
+    OPS,
+    SCHEDS,
+    ArError,
+    Plan,
+    ar_all_gather,
+    ar_allreduce,
+    ar_plan,
+    ar_reduce_scatter,
+    ar_status_string,
+    ar_tree_parent,
+    library_path,
+)
+
+__all__ = [
+    "ar_allreduce",
+    "ar_reduce_scatter",
+    "ar_all_gather",
+    "ar_plan",
+    "ar_tree_parent",
+    "ar_status_string",
+    "ArError",
+    "Plan",
+    "DTYPES",
+    "OPS",
+    "SCHEDS",
+    "COLLS",
+    "AR_MAX_RANKS",
+    "library_path",
+]

@@ -1,0 +1,164 @@
+"""ctypes marshalling for libar.so (see ``include/ar.h`` for the contract).
+
+Buffers may be given as torch tensors (their ``data_ptr()`` is used) or as
+integer device addresses.  ``stream`` may be a ``torch.cuda.Stream``, an
+integer ``hipStream_t`` handle, or None for torch's current stream on the
+current device (the NULL stream when torch is absent).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libar.so")
+
+AR_MAX_RANKS = 128
+DTYPES = {"f32": 0, "bf16": 1, "f16": 2, "i32": 3}
+OPS = {"sum": 0, "prod": 1, "min": 2, "max": 3, "avg": 4}
+SCHEDS = {"auto": 0, "ring": 1, "tree": 2, "fused": 3}
+COLLS = {"allreduce": 0, "reduce_scatter": 1, "all_gather": 2}
+_SCHED_NAMES = {v: k for k, v in SCHEDS.items()}
+_STATUS = {0: "AR_OK", 1: "AR_ERR_INVALID_ARG", 2: "AR_ERR_UNSUPPORTED", 3: "AR_ERR_ALIGNMENT", 4: "AR_ERR_HIP"}
+
+if not os.path.exists(_LIB_PATH):
+    raise ImportError("libar.so is not built (expected at %s); build it with `python -m reduce_scatter_amd.build` "
+                      "or __graft_entry__.build()" % _LIB_PATH)
+
+_lib = ctypes.CDLL(_LIB_PATH)
+
+
+class _PlanStruct(ctypes.Structure):
+    _fields_ = [("chosen", ctypes.c_int), ("legal_mask", ctypes.c_uint), ("steps", ctypes.c_int * 4),
+                ("bytes", ctypes.c_double * 4), ("predicted_us", ctypes.c_double * 4)]
+
+
+_vpp = ctypes.POINTER(ctypes.c_void_p)
+_lib.ar_allreduce.argtypes = [_vpp, _vpp, ctypes.c_size_t, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                              ctypes.c_void_p]
+_lib.ar_reduce_scatter.argtypes = _lib.ar_allreduce.argtypes
+_lib.ar_all_gather.argtypes = [_vpp, _vpp, ctypes.c_size_t, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                               ctypes.c_void_p]
+_lib.ar_plan.argtypes = [ctypes.c_int, ctypes.c_size_t, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                         ctypes.POINTER(_PlanStruct)]
+_lib.ar_tree_parent.argtypes = [ctypes.c_int, ctypes.c_int]
+_lib.ar_tree_parent.restype = ctypes.c_int
+_lib.ar_status_string.argtypes = [ctypes.c_int]
+_lib.ar_status_string.restype = ctypes.c_char_p
+for _f in (_lib.ar_allreduce, _lib.ar_reduce_scatter, _lib.ar_all_gather, _lib.ar_plan):
+    _f.restype = ctypes.c_int
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+class ArError(RuntimeError):
+    def __init__(self, status: int):
+        self.status = status
+        self.name = _STATUS.get(status, str(status))
+        super().__init__(ar_status_string(status))
+
+
+@dataclass
+class Plan:
+    chosen: str
+    legal: list
+    steps: dict
+    bytes: dict
+    predicted_us: dict
+
+
+def ar_status_string(status: int) -> str:
+    return _lib.ar_status_string(int(status)).decode()
+
+
+def _code(table, value, what):
+    if isinstance(value, str):
+        if value not in table:
+            raise ValueError("unknown %s %r (expected one of %s)" % (what, value, sorted(table)))
+        return table[value]
+    return int(value)
+
+
+def _dtype_code(dtype):
+    try:
+        import torch
+        tmap = {torch.float32: "f32", torch.bfloat16: "bf16", torch.float16: "f16", torch.int32: "i32"}
+        if dtype in tmap:
+            dtype = tmap[dtype]
+    except ImportError:
+        pass
+    return _code(DTYPES, dtype, "dtype")
+
+
+def _ptr(b):
+    if b is None:
+        return None
+    if isinstance(b, int):
+        return b
+    return int(b.data_ptr())
+
+
+def _ptr_array(bufs):
+    arr = (ctypes.c_void_p * max(1, len(bufs)))()
+    for i, b in enumerate(bufs):
+        arr[i] = _ptr(b)
+    return arr
+
+
+def _stream(stream):
+    if stream is None:
+        try:
+            import torch
+            if torch.cuda.is_available():
+                return int(torch.cuda.current_stream().cuda_stream)
+        except ImportError:
+            pass
+        return 0
+    if isinstance(stream, int):
+        return stream
+    return int(stream.cuda_stream)
+
+
+def _check(status):
+    if status != 0:
+        raise ArError(status)
+
+
+def ar_allreduce(sendbufs, recvbufs, count, dtype, op, n=None, sched="auto", stream=None):
+    """All-reduce ``count`` elements of each of the n rank buffers (in place when recvbufs is sendbufs)."""
+    n = len(sendbufs) if n is None else n
+    _check(_lib.ar_allreduce(_ptr_array(sendbufs), _ptr_array(recvbufs), count, _dtype_code(dtype),
+                             _code(OPS, op, "op"), n, _code(SCHEDS, sched, "schedule"), _stream(stream)))
+
+
+def ar_reduce_scatter(sendbufs, recvbufs, recvcount, dtype, op, n=None, sched="auto", stream=None):
+    """Reduce-scatter: each send buffer holds n*recvcount elements; rank r receives slice r."""
+    n = len(sendbufs) if n is None else n
+    _check(_lib.ar_reduce_scatter(_ptr_array(sendbufs), _ptr_array(recvbufs), recvcount, _dtype_code(dtype),
+                                  _code(OPS, op, "op"), n, _code(SCHEDS, sched, "schedule"), _stream(stream)))
+
+
+def ar_all_gather(sendbufs, recvbufs, sendcount, dtype, n=None, sched="auto", stream=None):
+    """All-gather: each rank receives the n pieces of sendcount elements, in rank order."""
+    n = len(sendbufs) if n is None else n
+    _check(_lib.ar_all_gather(_ptr_array(sendbufs), _ptr_array(recvbufs), sendcount, _dtype_code(dtype), n,
+                              _code(SCHEDS, sched, "schedule"), _stream(stream)))
+
+
+def ar_plan(coll, count, dtype, op, n) -> Plan:
+    """The cost model's choice for a call (host only; no GPU needed)."""
+    p = _PlanStruct()
+    _check(_lib.ar_plan(_code(COLLS, coll, "collective"), count, _dtype_code(dtype), _code(OPS, op, "op"), n,
+                        ctypes.byref(p)))
+    legal = [name for name, s in SCHEDS.items() if s and (p.legal_mask >> s) & 1]
+    return Plan(chosen=_SCHED_NAMES[p.chosen], legal=legal,
+                steps={s: p.steps[SCHEDS[s]] for s in legal},
+                bytes={s: p.bytes[SCHEDS[s]] for s in legal},
+                predicted_us={s: p.predicted_us[SCHEDS[s]] for s in legal})
+
+
+def ar_tree_parent(n: int, v: int) -> int:
+    return int(_lib.ar_tree_parent(n, v))

@@ -1,0 +1,336 @@
+// api.cpp -- the C ABI: argument validation, schedule choice and launch.
+//
+// Every entry point validates everything it can on the host before touching
+// the GPU, so argument errors are reported without a launch (and without a
+// GPU).  Calls allocate nothing: the rank pointer tables are copied by value
+// into the kernel arguments.  Calls are ordered on the caller's stream.
+#include <stdint.h>
+
+#include <atomic>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+
+#include "../../include/ar.h"
+#include "ar_host.hpp"
+#include "ar_kernels.hpp"
+
+using namespace ar;
+
+namespace {
+
+const char *kDtypeName[] = {"fp32", "bf16", "fp16", "int32"};
+const char *kOpName[] = {"sum", "prod", "min", "max", "avg"};
+const char *kSchedName[] = {"AUTO", "RING", "TREE", "FUSED"};
+const char *kCollName[] = {"AllReduce", "ReduceScatter", "AllGather"};
+
+bool valid_dtype(int d) { return d >= AR_FLOAT32 && d <= AR_INT32; }
+bool valid_op(int o) { return o >= AR_SUM && o <= AR_AVG; }
+bool valid_sched(int s) { return s >= AR_SCHED_AUTO && s <= AR_SCHED_FUSED; }
+
+bool debug_enabled() {
+    static int v = -1;
+    if (v < 0) {
+        const char *e = getenv("AR_DEBUG");
+        v = (e && *e && strcmp(e, "0") != 0) ? 1 : 0;
+    }
+    return v == 1;
+}
+
+ar_sched_t forced_schedule() {
+    const char *e = getenv("AR_SCHEDULE");
+    if (!e) return AR_SCHED_AUTO;
+    if (!strcmp(e, "ring")) return AR_SCHED_RING;
+    if (!strcmp(e, "tree")) return AR_SCHED_TREE;
+    if (!strcmp(e, "fused")) return AR_SCHED_FUSED;
+    return AR_SCHED_AUTO;
+}
+
+// Compute units of each device, queried once.
+std::atomic<int> g_cus[64];
+
+ar_status_t device_cus(int *cus) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return AR_ERR_HIP;
+    if (dev < 0 || dev >= 64) return AR_ERR_HIP;
+    int v = g_cus[dev].load(std::memory_order_relaxed);
+    if (v <= 0) {
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+            return AR_ERR_HIP;
+        g_cus[dev].store(v, std::memory_order_relaxed);
+    }
+    *cus = v;
+    return AR_OK;
+}
+
+// Workgroups for a persistent launch over ``units`` independent work units.
+int grid_for(long long units, int cus, int per_cu) {
+    const char *e = getenv("AR_GRID");
+    long long g = (e && atoll(e) > 0) ? atoll(e) : (long long)cus * per_cu;
+    if (g > units) g = units;
+    return (int)(g < 1 ? 1 : g);
+}
+
+// Window width (16-byte vectors per rank) for the LDS-staged schedules:
+// n * W items of one workgroup, at most kThreads * kItemsPerThread.
+int lds_window(int n) {
+    int w = (n <= 32) ? (kThreads * 2) / n : (kThreads * kItemsPerThread) / n;
+    return w < 1 ? 1 : w;
+}
+
+bool overlaps(uintptr_t a, size_t alen, uintptr_t b, size_t blen) {
+    return alen && blen && a < b + blen && b < a + alen;
+}
+
+bool null_entry(const void *const *p, int n) {
+    for (int r = 0; r < n; ++r)
+        if (!p[r]) return true;
+    return false;
+}
+
+bool misaligned(const void *const *p, int n, size_t align) {
+    for (int r = 0; r < n; ++r)
+        if ((uintptr_t)p[r] % align) return true;
+    return false;
+}
+
+bool all16(const void *const *a, const void *const *b, int n) {
+    for (int r = 0; r < n; ++r)
+        if (((uintptr_t)a[r] | (uintptr_t)b[r]) & 15u) return false;
+    return true;
+}
+
+// recv range r may coincide with its own in-place position ``inplace[r]``
+// (a send buffer address, or 0 for none) and must not otherwise overlap any
+// send range or any other recv range.
+ar_status_t check_overlap(const void *const *send, size_t slen, void *const *recv, size_t rlen, int n,
+                          const uintptr_t *inplace_send_for_recv) {
+    for (int r = 0; r < n; ++r) {
+        const uintptr_t y = (uintptr_t)recv[r];
+        for (int k = 0; k < n; ++k) {
+            const uintptr_t x = (uintptr_t)send[k];
+            if (!overlaps(y, rlen, x, slen)) continue;
+            if (k == r && inplace_send_for_recv[r]) continue;   // the allowed in-place layout
+            return AR_ERR_INVALID_ARG;
+        }
+        for (int k = r + 1; k < n; ++k)
+            if (overlaps(y, rlen, (uintptr_t)recv[k], rlen)) return AR_ERR_INVALID_ARG;
+    }
+    return AR_OK;
+}
+
+void log_plan(ar_coll_t coll, size_t bytes_per_rank, int n, int dtype, int op, const ar_plan_t &p, ar_sched_t used,
+              bool forced) {
+    if (!debug_enabled()) return;
+    fprintf(stderr,
+            "[ar] %s: %zu Bytes x n=%d %s %s -> %s%s (predicted us: ring %.2f tree %.2f fused %.2f; calib %s)\n",
+            kCollName[coll], bytes_per_rank, n, kDtypeName[dtype], kOpName[op], kSchedName[used],
+            forced ? " (forced)" : "", p.predicted_us[AR_SCHED_RING], p.predicted_us[AR_SCHED_TREE],
+            p.predicted_us[AR_SCHED_FUSED], calib_source());
+}
+
+// Resolve AR_SCHED_AUTO (and the AR_SCHEDULE override) into a legal schedule.
+ar_status_t choose(ar_coll_t coll, size_t count, ar_dtype_t dtype, ar_op_t op, int n, ar_sched_t sched,
+                   ar_sched_t *out, size_t bytes_per_rank) {
+    ar_plan_t p;
+    ar_status_t st = make_plan(coll, count, dtype, op, n, &p);
+    if (st != AR_OK) return st;
+    bool forced = sched != AR_SCHED_AUTO;
+    if (!forced) {
+        ar_sched_t env = forced_schedule();
+        if (env != AR_SCHED_AUTO && (p.legal_mask & (1u << env))) {
+            sched = env;
+            forced = true;
+        }
+    }
+    if (sched == AR_SCHED_AUTO) sched = p.chosen;
+    if (!(p.legal_mask & (1u << sched))) return AR_ERR_UNSUPPORTED;
+    log_plan(coll, bytes_per_rank, n, dtype, op, p, sched, forced);
+    *out = sched;
+    return AR_OK;
+}
+
+ar_status_t hip_status(hipError_t e) { return e == hipSuccess ? AR_OK : AR_ERR_HIP; }
+
+void fill_table(RankTable &t, const void *const *send, void *const *recv, int n) {
+    memset(&t, 0, sizeof t);
+    for (int r = 0; r < n; ++r) {
+        t.src[r] = send[r];
+        t.dst[r] = recv[r];
+    }
+}
+
+ar_status_t common_checks(const void *const *send, void *const *recv, int dtype, int op, int n, int sched) {
+    if (n < 1 || n > AR_MAX_RANKS || !send || !recv) return AR_ERR_INVALID_ARG;
+    if (!valid_dtype(dtype) || !valid_op(op) || !valid_sched(sched)) return AR_ERR_INVALID_ARG;
+    return AR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *ar_status_string(ar_status_t s) {
+    switch (s) {
+    case AR_OK: return "AR_OK";
+    case AR_ERR_INVALID_ARG: return "AR_ERR_INVALID_ARG: invalid argument";
+    case AR_ERR_UNSUPPORTED: return "AR_ERR_UNSUPPORTED: schedule not legal for this collective";
+    case AR_ERR_ALIGNMENT: return "AR_ERR_ALIGNMENT: buffer not aligned to its element size";
+    case AR_ERR_HIP: return "AR_ERR_HIP: HIP runtime error";
+    default: return "unknown ar_status_t";
+    }
+}
+
+int ar_tree_parent(int n, int v) { return (n >= 1 && n <= AR_MAX_RANKS) ? tree_parent(n, v) : -1; }
+
+ar_status_t ar_plan(ar_coll_t coll, size_t count, ar_dtype_t dtype, ar_op_t op, int n, ar_plan_t *out) {
+    if (!out || n < 1 || n > AR_MAX_RANKS || !valid_dtype(dtype) || !valid_op(op) || (int)coll < 0 ||
+        (int)coll > AR_COLL_ALL_GATHER)
+        return AR_ERR_INVALID_ARG;
+    return make_plan(coll, count, dtype, op, n, out);
+}
+
+ar_status_t ar_allreduce(const void *const *sendbufs, void *const *recvbufs, size_t count, ar_dtype_t dtype,
+                         ar_op_t op, int n, ar_sched_t sched, hipStream_t stream) {
+    ar_status_t st = common_checks(sendbufs, recvbufs, dtype, op, n, sched);
+    if (st != AR_OK) return st;
+    if (count == 0) return AR_OK;
+    if (null_entry(sendbufs, n) || null_entry((const void *const *)recvbufs, n)) return AR_ERR_INVALID_ARG;
+    const size_t e = elem_size(dtype);
+    if (count > (SIZE_MAX / 2) / e) return AR_ERR_INVALID_ARG;
+    if (misaligned(sendbufs, n, e) || misaligned((const void *const *)recvbufs, n, e)) return AR_ERR_ALIGNMENT;
+    uintptr_t inplace[AR_MAX_RANKS];
+    for (int r = 0; r < n; ++r) inplace[r] = (recvbufs[r] == sendbufs[r]) ? 1 : 0;
+    st = check_overlap(sendbufs, count * e, recvbufs, count * e, n, inplace);
+    if (st != AR_OK) return st;
+    ar_sched_t use;
+    st = choose(AR_COLL_ALLREDUCE, count, dtype, op, n, sched, &use, count * e);
+    if (st != AR_OK) return st;
+    int cus = 0;
+    st = device_cus(&cus);
+    if (st != AR_OK) return st;
+
+    RankTable t;
+    fill_table(t, sendbufs, recvbufs, n);
+    Geometry g;
+    memset(&g, 0, sizeof g);
+    const long long lanes = 16 / (long long)e;
+    g.n = n;
+    g.s = (float)(1.0 / (double)n);
+    g.V = ((long long)count + lanes - 1) / lanes;
+    g.Vfull = (long long)count / lanes;
+    TreeShape tree;
+    if (use == AR_SCHED_TREE) tree_build(n, tree);
+
+    if (!all16(sendbufs, (const void *const *)recvbufs, n)) {
+        // element-wise path over the whole buffer
+        hipError_t h = (use == AR_SCHED_TREE)
+                           ? launch_elem_tree_allreduce(dtype, op, t, tree, g, 0, (long long)count, stream)
+                           : launch_elem_ring_allreduce(dtype, op, t, g, 0, (long long)count, stream);
+        return hip_status(h);
+    }
+    hipError_t h = hipSuccess;
+    if (g.Vfull > 0) {
+        if (use == AR_SCHED_FUSED) {
+            const long long maxlen = (g.V + n - 1) / n;                       // longest chunk, in vectors
+            g.windows = (maxlen + kFusedTile - 1) / kFusedTile;
+            h = launch_fused_allreduce(dtype, op, t, g, grid_for(g.windows * n, cus, 4), stream);
+        } else if (use == AR_SCHED_RING) {
+            g.W = lds_window(n);
+            const long long maxlen = (g.V + n - 1) / n;
+            g.windows = (maxlen + g.W - 1) / g.W;
+            h = launch_ring_allreduce(dtype, op, t, g, grid_for(g.windows, cus, 4), stream);
+        } else {
+            g.W = lds_window(n);
+            g.windows = (g.Vfull + g.W - 1) / g.W;
+            h = launch_tree_allreduce(dtype, op, t, tree, g, grid_for(g.windows, cus, 4), stream);
+        }
+    }
+    if (h == hipSuccess && g.Vfull * lanes < (long long)count) {             // tail: last count mod lanes elements
+        h = (use == AR_SCHED_TREE)
+                ? launch_elem_tree_allreduce(dtype, op, t, tree, g, g.Vfull * lanes, (long long)count, stream)
+                : launch_elem_ring_allreduce(dtype, op, t, g, g.Vfull * lanes, (long long)count, stream);
+    }
+    return hip_status(h);
+}
+
+ar_status_t ar_reduce_scatter(const void *const *sendbufs, void *const *recvbufs, size_t recvcount,
+                              ar_dtype_t dtype, ar_op_t op, int n, ar_sched_t sched, hipStream_t stream) {
+    ar_status_t st = common_checks(sendbufs, recvbufs, dtype, op, n, sched);
+    if (st != AR_OK) return st;
+    if (recvcount == 0) return AR_OK;
+    if (null_entry(sendbufs, n) || null_entry((const void *const *)recvbufs, n)) return AR_ERR_INVALID_ARG;
+    const size_t e = elem_size(dtype);
+    if (recvcount > (SIZE_MAX / 2) / e / (size_t)n) return AR_ERR_INVALID_ARG;
+    if (misaligned(sendbufs, n, e) || misaligned((const void *const *)recvbufs, n, e)) return AR_ERR_ALIGNMENT;
+    uintptr_t inplace[AR_MAX_RANKS];
+    for (int r = 0; r < n; ++r)
+        inplace[r] = ((uintptr_t)recvbufs[r] == (uintptr_t)sendbufs[r] + (uintptr_t)r * recvcount * e) ? 1 : 0;
+    st = check_overlap(sendbufs, (size_t)n * recvcount * e, recvbufs, recvcount * e, n, inplace);
+    if (st != AR_OK) return st;
+    ar_sched_t use;
+    st = choose(AR_COLL_REDUCE_SCATTER, recvcount, dtype, op, n, sched, &use, (size_t)n * recvcount * e);
+    if (st != AR_OK) return st;
+    int cus = 0;
+    st = device_cus(&cus);
+    if (st != AR_OK) return st;
+
+    RankTable t;
+    fill_table(t, sendbufs, recvbufs, n);
+    Geometry g;
+    memset(&g, 0, sizeof g);
+    g.n = n;
+    g.s = (float)(1.0 / (double)n);
+    const bool vec = all16(sendbufs, (const void *const *)recvbufs, n) && (recvcount * e) % 16 == 0;
+    if (!vec) return hip_status(launch_elem_reduce_scatter(dtype, op, t, g, (long long)recvcount, stream));
+    g.Rv = (long long)(recvcount * e / 16);
+    if (use == AR_SCHED_FUSED) {
+        g.windows = (g.Rv + kFusedTile - 1) / kFusedTile;
+        return hip_status(launch_fused_reduce_scatter(dtype, op, t, g, grid_for(g.windows * n, cus, 4), stream));
+    }
+    g.W = lds_window(n);
+    g.windows = (g.Rv + g.W - 1) / g.W;
+    return hip_status(launch_ring_reduce_scatter(dtype, op, t, g, grid_for(g.windows, cus, 4), stream));
+}
+
+ar_status_t ar_all_gather(const void *const *sendbufs, void *const *recvbufs, size_t sendcount, ar_dtype_t dtype,
+                          int n, ar_sched_t sched, hipStream_t stream) {
+    ar_status_t st = common_checks(sendbufs, recvbufs, dtype, AR_SUM, n, sched);
+    if (st != AR_OK) return st;
+    if (sendcount == 0) return AR_OK;
+    if (null_entry(sendbufs, n) || null_entry((const void *const *)recvbufs, n)) return AR_ERR_INVALID_ARG;
+    const size_t e = elem_size(dtype);
+    if (sendcount > (SIZE_MAX / 2) / e / (size_t)n) return AR_ERR_INVALID_ARG;
+    if (misaligned(sendbufs, n, e) || misaligned((const void *const *)recvbufs, n, e)) return AR_ERR_ALIGNMENT;
+    uintptr_t inplace[AR_MAX_RANKS];
+    for (int r = 0; r < n; ++r)
+        inplace[r] = ((uintptr_t)sendbufs[r] == (uintptr_t)recvbufs[r] + (uintptr_t)r * sendcount * e) ? 1 : 0;
+    st = check_overlap(sendbufs, sendcount * e, recvbufs, (size_t)n * sendcount * e, n, inplace);
+    if (st != AR_OK) return st;
+    ar_sched_t use;
+    st = choose(AR_COLL_ALL_GATHER, sendcount, dtype, AR_SUM, n, sched, &use, (size_t)n * sendcount * e);
+    if (st != AR_OK) return st;
+    int cus = 0;
+    st = device_cus(&cus);
+    if (st != AR_OK) return st;
+
+    RankTable t;
+    fill_table(t, sendbufs, recvbufs, n);
+    Geometry g;
+    memset(&g, 0, sizeof g);
+    g.n = n;
+    g.s = 1.0f;
+    const bool vec = all16(sendbufs, (const void *const *)recvbufs, n) && (sendcount * e) % 16 == 0;
+    if (!vec) return hip_status(launch_elem_all_gather((int)e, t, g, (long long)sendcount, stream));
+    g.Rv = (long long)(sendcount * e / 16);
+    if (use == AR_SCHED_FUSED) {
+        g.windows = (g.Rv + kFusedTile - 1) / kFusedTile;
+        return hip_status(launch_fused_all_gather(t, g, grid_for(g.windows * n, cus, 4), stream));
+    }
+    g.W = lds_window(n);
+    g.windows = (g.Rv + g.W - 1) / g.W;
+    return hip_status(launch_ring_all_gather(t, g, grid_for(g.windows, cus, 4), stream));
+}
+
+}  // extern "C"

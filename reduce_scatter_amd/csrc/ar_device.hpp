@@ -1,0 +1,216 @@
+// ar_device.hpp -- device-side building blocks shared by the fused, ring and
+// tree kernels: 16-byte vector packs, storage-type rounding, the reduction
+// operator and the avg pre-scale / postOp.
+//
+// Semantics (the "NCCL all-reduce" post, rakshithvasudev.github.io, section
+// "What all-reduce promises"; "FSDP collectives 101", the note that bf16
+// reductions accumulate in bf16 along the way):
+//   * sum / prod / min / max / avg; avg multiplies each floating-point
+//     contribution by s = fp32(1/n) as it is read, and divides an int32 sum
+//     by n once where the chunk completes (truncating toward zero);
+//   * bf16 / fp16 are widened to fp32 for one hop's arithmetic and rounded
+//     back (to nearest even) when the value leaves the hop;
+//   * int32 sum / prod wrap modulo 2^32;
+//   * min(acc, own) keeps acc unless own < acc (max likewise), acc being the
+//     incoming partial.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#pragma clang fp contract(off)
+
+namespace ar {
+
+enum Dtype : int { F32 = 0, BF16 = 1, F16 = 2, I32 = 3 };
+enum Op : int { SUM = 0, PROD = 1, MIN = 2, MAX = 3, AVG = 4 };
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kMaxRanks = 128;
+
+// Elements of each dtype in one 16-byte vector.
+template <int DT> struct Lanes { static constexpr int value = (DT == BF16 || DT == F16) ? 8 : 4; };
+
+// One 16-byte vector unpacked to its arithmetic type: fp32 for the float
+// dtypes (each value exactly representable in the storage type), 32-bit
+// two's complement for int32.
+template <int DT> struct Pack {
+    static constexpr int K = Lanes<DT>::value;
+    typedef typename std::conditional<DT == I32, uint32_t, float>::type T;
+    T v[K];
+};
+
+__device__ __forceinline__ float bits_f32(uint32_t u) { return __builtin_bit_cast(float, u); }
+__device__ __forceinline__ uint32_t f32_bits(float f) { return __builtin_bit_cast(uint32_t, f); }
+
+// fp32 -> nearest bf16 (ties to even), returned as the fp32 value.
+__device__ __forceinline__ float round_bf16(float f) {
+    uint32_t u = f32_bits(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return bits_f32((u | 0x00400000u) & 0xffff0000u);  // quiet NaN
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return bits_f32(u & 0xffff0000u);
+}
+
+// fp32 -> nearest fp16 (ties to even, the hardware conversion), back to fp32.
+__device__ __forceinline__ float round_f16(float f) { return (float)(_Float16)f; }
+
+template <int DT> __device__ __forceinline__ float round_to(float f) {
+    if (DT == BF16) return round_bf16(f);
+    if (DT == F16) return round_f16(f);
+    return f;
+}
+
+template <int DT> __device__ __forceinline__ Pack<DT> unpack(u32x4 w) {
+    Pack<DT> p;
+    if constexpr (DT == F32) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p.v[i] = bits_f32(w[i]);
+    } else if constexpr (DT == I32) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p.v[i] = w[i];
+    } else if constexpr (DT == BF16) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            p.v[2 * i] = bits_f32(w[i] << 16);
+            p.v[2 * i + 1] = bits_f32(w[i] & 0xffff0000u);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            p.v[2 * i] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[i] & 0xffffu));
+            p.v[2 * i + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[i] >> 16));
+        }
+    }
+    return p;
+}
+
+// Pack values that are already representable in the storage type.
+template <int DT> __device__ __forceinline__ u32x4 pack(const Pack<DT> &p) {
+    u32x4 w;
+    if constexpr (DT == F32) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = f32_bits(p.v[i]);
+    } else if constexpr (DT == I32) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = p.v[i];
+    } else if constexpr (DT == BF16) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = (f32_bits(p.v[2 * i]) >> 16) | (f32_bits(p.v[2 * i + 1]) & 0xffff0000u);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            uint32_t lo = __builtin_bit_cast(uint16_t, (_Float16)p.v[2 * i]);
+            uint32_t hi = __builtin_bit_cast(uint16_t, (_Float16)p.v[2 * i + 1]);
+            w[i] = lo | (hi << 16);
+        }
+    }
+    return w;
+}
+
+// One element: the contribution as read (float avg pre-scales by s).
+template <int DT, int OP> __device__ __forceinline__ typename Pack<DT>::T pre(typename Pack<DT>::T x, float s) {
+    if constexpr (DT != I32 && OP == AVG) return x * s;
+    else return x;
+}
+
+// One element: acc (+) own, in fp32 or in 32-bit two's complement.
+template <int DT, int OP>
+__device__ __forceinline__ typename Pack<DT>::T combine(typename Pack<DT>::T acc, typename Pack<DT>::T own) {
+    if constexpr (DT == I32) {
+        if constexpr (OP == SUM || OP == AVG) return acc + own;
+        else if constexpr (OP == PROD) return acc * own;
+        else if constexpr (OP == MIN) return ((int32_t)own < (int32_t)acc) ? own : acc;
+        else return ((int32_t)own > (int32_t)acc) ? own : acc;
+    } else {
+        if constexpr (OP == SUM || OP == AVG) return acc + own;
+        else if constexpr (OP == PROD) return acc * own;
+        else if constexpr (OP == MIN) return (own < acc) ? own : acc;
+        else return (own > acc) ? own : acc;
+    }
+}
+
+// Vector forms. ``first`` starts a chain: round(pre(x)).
+template <int DT, int OP> __device__ __forceinline__ Pack<DT> first(const Pack<DT> &x, float s) {
+    Pack<DT> r;
+#pragma unroll
+    for (int i = 0; i < Pack<DT>::K; ++i) {
+        if constexpr (DT == I32) r.v[i] = x.v[i];
+        else r.v[i] = round_to<DT>(pre<DT, OP>(x.v[i], s));
+    }
+    return r;
+}
+
+// One hop: acc = round(acc (+) pre(own)).
+template <int DT, int OP> __device__ __forceinline__ void hop(Pack<DT> &acc, const Pack<DT> &own, float s) {
+#pragma unroll
+    for (int i = 0; i < Pack<DT>::K; ++i) {
+        if constexpr (DT == I32) acc.v[i] = combine<DT, OP>(acc.v[i], own.v[i]);
+        else acc.v[i] = round_to<DT>(combine<DT, OP>(acc.v[i], pre<DT, OP>(own.v[i], s)));
+    }
+}
+
+// Combine two partials that were both already rounded (tree: parent (+) child).
+template <int DT, int OP> __device__ __forceinline__ void merge(Pack<DT> &acc, const Pack<DT> &other) {
+#pragma unroll
+    for (int i = 0; i < Pack<DT>::K; ++i) {
+        if constexpr (DT == I32) acc.v[i] = combine<DT, OP>(acc.v[i], other.v[i]);
+        else acc.v[i] = round_to<DT>(combine<DT, OP>(acc.v[i], other.v[i]));
+    }
+}
+
+// The fixup where a chunk completes: int32 avg divides by n once.
+template <int DT, int OP> __device__ __forceinline__ void post(Pack<DT> &acc, int n) {
+    if constexpr (DT == I32 && OP == AVG) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc.v[i] = (uint32_t)((int32_t)acc.v[i] / n);
+    }
+}
+
+// ---- scalar (one element) forms, for the element-wise path ----------------
+template <int DT> __device__ __forceinline__ typename Pack<DT>::T load1(const void *p, long long i) {
+    if constexpr (DT == F32) return ((const float *)p)[i];
+    else if constexpr (DT == I32) return ((const uint32_t *)p)[i];
+    else if constexpr (DT == BF16) return bits_f32((uint32_t)((const uint16_t *)p)[i] << 16);
+    else return (float)((const _Float16 *)p)[i];
+}
+
+template <int DT> __device__ __forceinline__ void store1(void *p, long long i, typename Pack<DT>::T v) {
+    if constexpr (DT == F32) ((float *)p)[i] = v;
+    else if constexpr (DT == I32) ((uint32_t *)p)[i] = v;
+    else if constexpr (DT == BF16) ((uint16_t *)p)[i] = (uint16_t)(f32_bits(v) >> 16);
+    else ((_Float16 *)p)[i] = (_Float16)v;
+}
+
+template <int DT, int OP> __device__ __forceinline__ typename Pack<DT>::T first1(typename Pack<DT>::T x, float s) {
+    if constexpr (DT == I32) return x;
+    else return round_to<DT>(pre<DT, OP>(x, s));
+}
+
+template <int DT, int OP>
+__device__ __forceinline__ typename Pack<DT>::T hop1(typename Pack<DT>::T acc, typename Pack<DT>::T own, float s) {
+    if constexpr (DT == I32) return combine<DT, OP>(acc, own);
+    else return round_to<DT>(combine<DT, OP>(acc, pre<DT, OP>(own, s)));
+}
+
+template <int DT, int OP> __device__ __forceinline__ typename Pack<DT>::T post1(typename Pack<DT>::T acc, int n) {
+    if constexpr (DT == I32 && OP == AVG) return (uint32_t)((int32_t)acc / n);
+    else return acc;
+}
+
+// Streaming 16-byte loads and stores: every byte is touched once, so they are
+// marked non-temporal.
+__device__ __forceinline__ u32x4 ld_stream(const void *base, long long vec) {
+    return __builtin_nontemporal_load((const u32x4 *)base + vec);
+}
+__device__ __forceinline__ void st_stream(void *base, long long vec, u32x4 w) {
+    __builtin_nontemporal_store(w, (u32x4 *)base + vec);
+}
+
+// (a + b) mod n for a, b in [0, n).
+__device__ __forceinline__ int add_mod(int a, int b, int n) {
+    int r = a + b;
+    return r >= n ? r - n : r;
+}
+
+}  // namespace ar

@@ -1,0 +1,76 @@
+// ar_kernels.hpp -- kernel argument blocks and launcher entry points (host
+// side of the kernels).  The pointer tables travel by value in the kernel
+// arguments, so a launch needs no device-side table and no allocation.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ar {
+
+constexpr int kTableRanks = 128;
+
+struct RankTable {
+    const void *src[kTableRanks];
+    void *dst[kTableRanks];
+};
+
+// Geometry of one collective call, in 16-byte vectors of the element type.
+//   all-reduce:     chunk c = vectors [floor(c*V/n), floor((c+1)*V/n)) of
+//                   every rank buffer; full vectors are [0, Vfull).
+//   reduce-scatter: chunk c = vectors [c*Rv, (c+1)*Rv) of every input;
+//                   output slice of rank r = vectors [0, Rv).
+//   all-gather:     piece k = vectors [0, Rv) of input k, landing at
+//                   [k*Rv, (k+1)*Rv) of every output.
+struct Geometry {
+    long long V;        // all-reduce: ceil(count / lanes)
+    long long Vfull;    // all-reduce: count / lanes (vectors with no tail)
+    long long Rv;       // reduce-scatter / all-gather: vectors per slice
+    long long windows;  // work units along a chunk (tiles or LDS windows)
+    int n;
+    int W;              // ring/tree: vectors per rank in one LDS window
+    float s;            // fp32(1/n), the float avg pre-scale
+};
+
+// The tree schedule's shape, host-built: depth, parent and up to two
+// children per rank (-1 = none); post[] lists ranks children-first.
+struct TreeShape {
+    int8_t depth[kTableRanks];
+    int8_t parent[kTableRanks];
+    int8_t child[kTableRanks][2];
+    uint8_t post[kTableRanks];
+    int max_depth;
+};
+
+// Launchers.  dt / op use the ar_dtype_t / ar_op_t numbering.  ``grid`` is
+// the number of workgroups (already clamped to the work available).
+// Vector paths (every pointer 16-byte aligned):
+hipError_t launch_fused_allreduce(int dt, int op, const RankTable &t, const Geometry &g, int grid, hipStream_t s);
+hipError_t launch_fused_reduce_scatter(int dt, int op, const RankTable &t, const Geometry &g, int grid, hipStream_t s);
+hipError_t launch_fused_all_gather(const RankTable &t, const Geometry &g, int grid, hipStream_t s);
+hipError_t launch_ring_allreduce(int dt, int op, const RankTable &t, const Geometry &g, int grid, hipStream_t s);
+hipError_t launch_ring_reduce_scatter(int dt, int op, const RankTable &t, const Geometry &g, int grid, hipStream_t s);
+hipError_t launch_ring_all_gather(const RankTable &t, const Geometry &g, int grid, hipStream_t s);
+hipError_t launch_tree_allreduce(int dt, int op, const RankTable &t, const TreeShape &tree, const Geometry &g,
+                                 int grid, hipStream_t s);
+// Element-wise paths (any alignment, and the all-reduce tail), elements
+// [e_begin, e_end) of every rank buffer / slice:
+hipError_t launch_elem_ring_allreduce(int dt, int op, const RankTable &t, const Geometry &g, long long e_begin,
+                                      long long e_end, hipStream_t s);
+hipError_t launch_elem_tree_allreduce(int dt, int op, const RankTable &t, const TreeShape &tree, const Geometry &g,
+                                      long long e_begin, long long e_end, hipStream_t s);
+hipError_t launch_elem_reduce_scatter(int dt, int op, const RankTable &t, const Geometry &g, long long R,
+                                      hipStream_t s);
+hipError_t launch_elem_all_gather(int elem_bytes, const RankTable &t, const Geometry &g, long long R, hipStream_t s);
+
+// Threads per workgroup for every vector kernel.
+constexpr int kThreads = 256;
+// Fused kernels: 16-byte vectors per thread per tile, and ranks whose loads
+// are issued before the first of them is combined.
+constexpr int kUnroll = 2;
+constexpr int kRankBatch = 8;
+constexpr int kFusedTile = kThreads * kUnroll;
+// Ring/tree kernels: at most this many (rank, vector) items per thread.
+constexpr int kItemsPerThread = 4;
+
+}  // namespace ar

@@ -1,0 +1,31 @@
+// dispatch.hpp -- turn runtime (dtype, op) codes into template arguments.
+#pragma once
+
+#include <type_traits>
+
+#include "ar_device.hpp"
+
+namespace ar {
+
+template <int DT, typename F> hipError_t dispatch_op(int op, F &&f) {
+    switch (op) {
+    case SUM: return f(std::integral_constant<int, DT>{}, std::integral_constant<int, SUM>{});
+    case PROD: return f(std::integral_constant<int, DT>{}, std::integral_constant<int, PROD>{});
+    case MIN: return f(std::integral_constant<int, DT>{}, std::integral_constant<int, MIN>{});
+    case MAX: return f(std::integral_constant<int, DT>{}, std::integral_constant<int, MAX>{});
+    case AVG: return f(std::integral_constant<int, DT>{}, std::integral_constant<int, AVG>{});
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <typename F> hipError_t dispatch(int dt, int op, F &&f) {
+    switch (dt) {
+    case F32: return dispatch_op<F32>(op, f);
+    case BF16: return dispatch_op<BF16>(op, f);
+    case F16: return dispatch_op<F16>(op, f);
+    case I32: return dispatch_op<I32>(op, f);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace ar

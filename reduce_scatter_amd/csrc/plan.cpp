@@ -1,0 +1,235 @@
+// plan.cpp -- the cost model that picks a schedule per call, and the tree
+// builder.  Host code only (no HIP calls), so it runs without a GPU.
+//
+// Cost model: the "NCCL all-reduce" post (rakshithvasudev.github.io), section
+// "How NCCL picks: a cost model, not a threshold": every legal algorithm is
+// priced as latency plus bytes over bandwidth and the cheapest one wins, per
+// call; there is no size threshold.  Tables of measured constants are filled
+// once at start-up; a candidate the hardware cannot run is simply absent
+// (section "What your hardware takes off the menu").  Here:
+//
+//   t_s = launch_us[s] + step_us[s] * steps_s(n) + bytes_s / bandwidth_s(bytes)
+//
+//   steps:  ring 2(n-1) for all-reduce, n-1 for reduce-scatter / all-gather
+//           (section "The ring, exactly as the kernel runs it"); tree
+//           2 * depth (section "The double binary tree"); fused 1.
+//   bytes:  the algorithmic HBM bytes.  All three schedules keep partial
+//           results on chip, so each moves 2*n*S for an all-reduce of S bytes
+//           per rank, (n+1)*n*R*e for reduce-scatter and all-gather.
+//   bandwidth_s(bytes): a measured sustained rate times a measured per-size
+//           correction (the role of the tree correction table in the same
+//           section: the clean model does not fit medium sizes, so a
+//           per-size factor is applied).
+//
+// Legality: the tree schedule exists for all-reduce only.
+//
+// Constants come from a calibration file (AR_CALIB, default
+// calib_gfx950.txt beside the library) written by the package's calibration
+// script from timed runs; built-in defaults apply when it is missing.
+#include <dlfcn.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "../../include/ar.h"
+#include "ar_host.hpp"
+
+namespace ar {
+
+namespace {
+
+constexpr int kColls = 3;
+constexpr int kScheds = 4;         // indexed by ar_sched_t; 0 (auto) unused
+constexpr int kSizeBins = 32;      // per-size correction for log2(bytes per rank) = 0..31
+
+struct Entry {
+    double launch_us = 0, step_us = 0, bw_gbps = 0;
+    double corr[kSizeBins];
+    bool set = false;
+};
+
+struct Calib {
+    Entry e[kColls][kScheds];
+    std::string source = "defaults";
+};
+
+Calib g_calib;
+std::once_flag g_calib_once;
+
+void set_defaults(Calib &c) {
+    // Conservative start-up constants for MI355X (replaced by the measured
+    // file when present): a few microseconds of launch cost, a workgroup
+    // barrier per dependent step, and HBM-class streaming bandwidth.
+    for (int k = 0; k < kColls; ++k)
+        for (int s = 1; s < kScheds; ++s) {
+            Entry &e = c.e[k][s];
+            e.launch_us = 8.0;
+            e.step_us = (s == AR_SCHED_FUSED) ? 0.0 : 0.25;
+            e.bw_gbps = (s == AR_SCHED_FUSED) ? 5000.0 : 4000.0;
+            for (int b = 0; b < kSizeBins; ++b) e.corr[b] = 1.0;
+            e.set = true;
+        }
+}
+
+int coll_index(const char *s) {
+    if (!strcmp(s, "allreduce")) return AR_COLL_ALLREDUCE;
+    if (!strcmp(s, "reduce_scatter")) return AR_COLL_REDUCE_SCATTER;
+    if (!strcmp(s, "all_gather")) return AR_COLL_ALL_GATHER;
+    return -1;
+}
+
+int sched_index(const char *s) {
+    if (!strcmp(s, "ring")) return AR_SCHED_RING;
+    if (!strcmp(s, "tree")) return AR_SCHED_TREE;
+    if (!strcmp(s, "fused")) return AR_SCHED_FUSED;
+    return -1;
+}
+
+std::string library_dir() {
+    Dl_info info;
+    if (dladdr((void *)&library_dir, &info) && info.dli_fname) {
+        std::string p(info.dli_fname);
+        size_t k = p.rfind('/');
+        if (k != std::string::npos) return p.substr(0, k);
+    }
+    return ".";
+}
+
+// File format, one record per line ('#' starts a comment):
+//   <coll> <sched> <launch_us> <step_us> <bw_gbps> [corr_0 ... corr_31]
+// coll in {allreduce, reduce_scatter, all_gather}, sched in {ring, tree, fused};
+// corr_b multiplies the bandwidth for calls of 2^b .. 2^(b+1)-1 bytes per rank.
+void load_file(Calib &c, const std::string &path) {
+    FILE *f = fopen(path.c_str(), "r");
+    if (!f) return;
+    char line[1024];
+    int loaded = 0;
+    while (fgets(line, sizeof line, f)) {
+        char *hash = strchr(line, '#');
+        if (hash) *hash = 0;
+        char coll[32], sched[32];
+        int used = 0;
+        double lu, su, bw;
+        if (sscanf(line, "%31s %31s %lf %lf %lf%n", coll, sched, &lu, &su, &bw, &used) != 5) continue;
+        int k = coll_index(coll), s = sched_index(sched);
+        if (k < 0 || s < 0 || !(bw > 0) || lu < 0 || su < 0) continue;
+        Entry &e = c.e[k][s];
+        e.launch_us = lu;
+        e.step_us = su;
+        e.bw_gbps = bw;
+        const char *p = line + used;
+        for (int b = 0; b < kSizeBins; ++b) {
+            double v;
+            int m = 0;
+            if (sscanf(p, "%lf%n", &v, &m) != 1) break;
+            if (v > 0) e.corr[b] = v;
+            p += m;
+        }
+        ++loaded;
+    }
+    fclose(f);
+    if (loaded) c.source = path;
+}
+
+void init_calib() {
+    set_defaults(g_calib);
+    const char *env = getenv("AR_CALIB");
+    load_file(g_calib, env && *env ? std::string(env) : library_dir() + "/calib_gfx950.txt");
+}
+
+int size_bin(double bytes_per_rank) {
+    if (bytes_per_rank < 1) return 0;
+    int b = (int)std::floor(std::log2(bytes_per_rank));
+    return b < 0 ? 0 : (b >= kSizeBins ? kSizeBins - 1 : b);
+}
+
+}  // namespace
+
+int tree_parent(int n, int v) {
+    if (v <= 0 || v >= n) return -1;                // rank 0 is the root
+    const int low = v & -v;                         // lowest set bit: fixes the depth
+    int p = (v ^ low) | (low << 1);                 // clear it, set the next bit up
+    if (p >= n) p = v ^ low;                        // at the edge of the range: just clear it
+    return p;
+}
+
+void tree_build(int n, TreeShape &t) {
+    memset(&t, 0, sizeof t);
+    for (int v = 0; v < kTableRanks; ++v) {
+        t.parent[v] = -1;
+        t.child[v][0] = t.child[v][1] = -1;
+    }
+    t.max_depth = 0;
+    for (int v = 0; v < n; ++v) {
+        int d = 0;
+        for (int p = v; p != 0; p = tree_parent(n, p)) ++d;
+        t.depth[v] = (int8_t)d;
+        if (d > t.max_depth) t.max_depth = d;
+        t.parent[v] = (int8_t)tree_parent(n, v);
+    }
+    for (int v = 1; v < n; ++v) {                   // children in ascending rank order
+        int p = t.parent[v];
+        if (t.child[p][0] < 0) t.child[p][0] = (int8_t)v;
+        else t.child[p][1] = (int8_t)v;
+    }
+    int k = 0;                                      // children first: deepest level first
+    for (int d = t.max_depth; d >= 0; --d)
+        for (int v = 0; v < n; ++v)
+            if (t.depth[v] == d) t.post[k++] = (uint8_t)v;
+}
+
+size_t elem_size(int dtype) { return (dtype == AR_BFLOAT16 || dtype == AR_FLOAT16) ? 2 : 4; }
+
+ar_status_t make_plan(ar_coll_t coll, size_t count, ar_dtype_t dtype, ar_op_t op, int n, ar_plan_t *out) {
+    (void)op;
+    std::call_once(g_calib_once, init_calib);
+    memset(out, 0, sizeof *out);
+    const double e = (double)elem_size(dtype);
+    double bytes = 0, per_rank = 0;
+    if (coll == AR_COLL_ALLREDUCE) {
+        per_rank = (double)count * e;
+        bytes = 2.0 * n * per_rank;
+    } else {                                        // RS: n*R in, R out; AG: R in, n*R out
+        per_rank = (double)n * count * e;
+        bytes = (n + 1.0) * n * (double)count * e;
+    }
+    int depth = 0;
+    for (int v = 0; v < n; ++v) {
+        int d = 0;
+        for (int p = v; p != 0; p = tree_parent(n, p)) ++d;
+        depth = d > depth ? d : depth;
+    }
+    out->legal_mask = (1u << AR_SCHED_RING) | (1u << AR_SCHED_FUSED);
+    if (coll == AR_COLL_ALLREDUCE) out->legal_mask |= (1u << AR_SCHED_TREE);
+    out->steps[AR_SCHED_RING] = (coll == AR_COLL_ALLREDUCE) ? 2 * (n - 1) : (n - 1);
+    out->steps[AR_SCHED_TREE] = (coll == AR_COLL_ALLREDUCE) ? 2 * depth : 0;
+    out->steps[AR_SCHED_FUSED] = 1;
+    double best = 0;
+    out->chosen = AR_SCHED_FUSED;
+    bool have = false;
+    const int bin = size_bin(per_rank);
+    for (int s = AR_SCHED_RING; s <= AR_SCHED_FUSED; ++s) {
+        if (!(out->legal_mask & (1u << s))) continue;
+        const Entry &c = g_calib.e[coll][s];
+        out->bytes[s] = bytes;
+        const double bw = c.bw_gbps * c.corr[bin];                 // GB/s = 1e3 bytes per microsecond
+        out->predicted_us[s] = c.launch_us + c.step_us * out->steps[s] + bytes / (bw * 1e3);
+        if (!have || out->predicted_us[s] < best) {
+            best = out->predicted_us[s];
+            out->chosen = (ar_sched_t)s;
+            have = true;
+        }
+    }
+    return AR_OK;
+}
+
+const char *calib_source() {
+    std::call_once(g_calib_once, init_calib);
+    return g_calib.source.c_str();
+}
+
+}  // namespace ar

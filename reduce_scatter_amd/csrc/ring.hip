@@ -1,0 +1,246 @@
+// ring.hip -- the ring schedule, staged through LDS.
+//
+// The "NCCL all-reduce" post (rakshithvasudev.github.io), section "The ring,
+// exactly as the kernel runs it": the buffer is split into n chunks; in the
+// reduce-scatter half every rank receives a running total from its
+// predecessor, adds its own contribution and passes it on, so chunk c's total
+// is complete after n-1 hops at the rank that owns it (the completing step
+// applies the postOp and keeps the result); in the all-gather half the
+// finished chunks are forwarded unchanged for n-1 more hops, each rank keeping
+// a copy.  Chunks are cut into slices that flow independently (section "Why a
+// 100 GB all-reduce doesn't OOM": a fixed window per connection, never a
+// message-sized buffer).
+//
+// On one GPU the ranks are buffers.  A workgroup runs the whole ring for one
+// window of W vectors at the same offset inside each of the n chunks (a
+// "channel"): a (rank r, vector w) item stands for rank r's share of that
+// window.  The wire between rank r and rank r+1 is one LDS slot per chunk:
+// at step p rank r adds its contribution to the running total of chunk
+// (r-1-p) mod n held in LDS, and a workgroup barrier is the hop to the next
+// rank.  Each rank's loads for step p+1 are issued before step p's LDS work,
+// so HBM latency overlaps the barriers.  HBM traffic is the same 2*n*S bytes
+// as the fused pass: every input vector is read once, every output written
+// once; the running totals never leave LDS.
+#include "ar_device.hpp"
+#include "ar_kernels.hpp"
+#include "dispatch.hpp"
+
+namespace ar {
+
+// Per-thread view of its (rank, vector-in-window) items.
+struct Items {
+    int count;                         // items this thread owns (<= kItemsPerThread)
+    int r[kItemsPerThread];
+    int w[kItemsPerThread];
+};
+
+__device__ __forceinline__ Items make_items(int n, int W) {
+    Items it;
+    it.count = 0;
+#pragma unroll
+    for (int k = 0; k < kItemsPerThread; ++k) {
+        const int q = threadIdx.x + k * kThreads;
+        it.r[k] = 0;
+        it.w[k] = 0;
+        if (q < n * W) {
+            it.r[k] = q / W;
+            it.w[k] = q - it.r[k] * W;
+            it.count = k + 1;
+        }
+    }
+    return it;
+}
+
+// mod n for a in [-2n, 2n)
+__device__ __forceinline__ int wrap(int a, int n) {
+    a = a < 0 ? a + n : a;
+    a = a < 0 ? a + n : a;
+    return a >= n ? a - n : a;
+}
+
+// All-reduce.  LDS: slot[c * W + w] (16 bytes each) and the chunk bounds.
+template <int DT, int OP>
+__global__ __launch_bounds__(kThreads) void ring_allreduce_kernel(const RankTable t, const Geometry g) {
+    extern __shared__ __align__(16) unsigned char lds[];
+    const int n = g.n, W = g.W;
+    u32x4 *slot = (u32x4 *)lds;
+    long long *vb = (long long *)(lds + (size_t)n * W * 16);     // chunk c = [vb[c], vb[c+1])
+    for (int c = threadIdx.x; c <= n; c += kThreads) {
+        long long b = ((long long)c * g.V) / n;
+        vb[c] = b < g.Vfull ? b : g.Vfull;
+    }
+    __syncthreads();
+    const Items it = make_items(n, W);
+
+    for (long long win = blockIdx.x; win < g.windows; win += gridDim.x) {
+        const long long pos0 = win * W;
+        // reduce-scatter half: steps p = 0..n-1; at step p rank r handles chunk (r-1-p) mod n
+        u32x4 cur[kItemsPerThread], nxt[kItemsPerThread];
+        bool ok_cur[kItemsPerThread], ok_nxt[kItemsPerThread];
+#pragma unroll
+        for (int k = 0; k < kItemsPerThread; ++k) {
+            ok_cur[k] = false;
+            if (k < it.count) {
+                const int c = wrap(it.r[k] - 1, n);
+                const long long v = vb[c] + pos0 + it.w[k];
+                ok_cur[k] = v < vb[c + 1];
+                if (ok_cur[k]) cur[k] = ld_stream(t.src[it.r[k]], v);
+            }
+        }
+        for (int p = 0; p < n; ++p) {
+            // issue the next step's loads first
+#pragma unroll
+            for (int k = 0; k < kItemsPerThread; ++k) {
+                ok_nxt[k] = false;
+                if (k < it.count && p + 1 < n) {
+                    const int c = wrap(it.r[k] - 2 - p, n);
+                    const long long v = vb[c] + pos0 + it.w[k];
+                    ok_nxt[k] = v < vb[c + 1];
+                    if (ok_nxt[k]) nxt[k] = ld_stream(t.src[it.r[k]], v);
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < kItemsPerThread; ++k) {
+                if (!ok_cur[k]) continue;
+                const int c = wrap(it.r[k] - 1 - p, n);
+                u32x4 *sl = &slot[c * W + it.w[k]];
+                Pack<DT> own = unpack<DT>(cur[k]);
+                Pack<DT> acc;
+                if (p == 0) {
+                    acc = first<DT, OP>(own, g.s);                 // send: own contribution alone
+                } else {
+                    acc = unpack<DT>(*sl);                         // recvReduceSend
+                    hop<DT, OP>(acc, own, g.s);
+                }
+                if (p == n - 1) {                                  // chunk c == r completes here
+                    post<DT, OP>(acc, n);
+                    st_stream(t.dst[it.r[k]], vb[c] + pos0 + it.w[k], pack<DT>(acc));
+                }
+                *sl = pack<DT>(acc);
+            }
+            __syncthreads();                                       // the hop to rank r+1
+#pragma unroll
+            for (int k = 0; k < kItemsPerThread; ++k) {
+                cur[k] = nxt[k];
+                ok_cur[k] = ok_nxt[k];
+            }
+        }
+        // all-gather half: at step p rank r receives finished chunk (r-1-p) mod n and keeps it
+        for (int p = 0; p < n - 1; ++p) {
+#pragma unroll
+            for (int k = 0; k < kItemsPerThread; ++k) {
+                if (k >= it.count) continue;
+                const int c = wrap(it.r[k] - 1 - p, n);
+                const long long v = vb[c] + pos0 + it.w[k];
+                if (v < vb[c + 1]) st_stream(t.dst[it.r[k]], v, slot[c * W + it.w[k]]);
+            }
+        }
+        __syncthreads();                                           // slots are reused by the next window
+    }
+}
+
+// Reduce-scatter: the reduce half only; chunk c = input vectors [c*Rv, (c+1)*Rv).
+template <int DT, int OP>
+__global__ __launch_bounds__(kThreads) void ring_reduce_scatter_kernel(const RankTable t, const Geometry g) {
+    extern __shared__ __align__(16) unsigned char lds[];
+    const int n = g.n, W = g.W;
+    u32x4 *slot = (u32x4 *)lds;
+    const Items it = make_items(n, W);
+    for (long long win = blockIdx.x; win < g.windows; win += gridDim.x) {
+        const long long pos0 = win * W;
+        u32x4 cur[kItemsPerThread], nxt[kItemsPerThread];
+        bool ok[kItemsPerThread];
+#pragma unroll
+        for (int k = 0; k < kItemsPerThread; ++k) {
+            ok[k] = k < it.count && pos0 + it.w[k] < g.Rv;        // same position in every chunk
+            if (ok[k]) cur[k] = ld_stream(t.src[it.r[k]], (long long)wrap(it.r[k] - 1, n) * g.Rv + pos0 + it.w[k]);
+        }
+        for (int p = 0; p < n; ++p) {
+#pragma unroll
+            for (int k = 0; k < kItemsPerThread; ++k)
+                if (ok[k] && p + 1 < n)
+                    nxt[k] = ld_stream(t.src[it.r[k]], (long long)wrap(it.r[k] - 2 - p, n) * g.Rv + pos0 + it.w[k]);
+#pragma unroll
+            for (int k = 0; k < kItemsPerThread; ++k) {
+                if (!ok[k]) continue;
+                const int c = wrap(it.r[k] - 1 - p, n);
+                u32x4 *sl = &slot[c * W + it.w[k]];
+                Pack<DT> own = unpack<DT>(cur[k]);
+                Pack<DT> acc;
+                if (p == 0) {
+                    acc = first<DT, OP>(own, g.s);
+                } else {
+                    acc = unpack<DT>(*sl);
+                    hop<DT, OP>(acc, own, g.s);
+                }
+                if (p == n - 1) {
+                    post<DT, OP>(acc, n);
+                    st_stream(t.dst[it.r[k]], pos0 + it.w[k], pack<DT>(acc));
+                } else {
+                    *sl = pack<DT>(acc);
+                }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int k = 0; k < kItemsPerThread; ++k) cur[k] = nxt[k];
+        }
+    }
+}
+
+// All-gather: the gather half only.  Every rank keeps its own piece, then the
+// pieces are forwarded around the ring for n-1 steps.
+__global__ __launch_bounds__(kThreads) void ring_all_gather_kernel(const RankTable t, const Geometry g) {
+    extern __shared__ __align__(16) unsigned char lds[];
+    const int n = g.n, W = g.W;
+    u32x4 *slot = (u32x4 *)lds;
+    const Items it = make_items(n, W);
+    for (long long win = blockIdx.x; win < g.windows; win += gridDim.x) {
+        const long long pos0 = win * W;
+#pragma unroll
+        for (int k = 0; k < kItemsPerThread; ++k) {
+            if (k >= it.count || pos0 + it.w[k] >= g.Rv) continue;
+            const int r = it.r[k];
+            const u32x4 x = ld_stream(t.src[r], pos0 + it.w[k]);
+            slot[r * W + it.w[k]] = x;
+            st_stream(t.dst[r], (long long)r * g.Rv + pos0 + it.w[k], x);          // keep my own piece
+        }
+        __syncthreads();
+        for (int p = 0; p < n - 1; ++p) {
+#pragma unroll
+            for (int k = 0; k < kItemsPerThread; ++k) {
+                if (k >= it.count || pos0 + it.w[k] >= g.Rv) continue;
+                const int c = wrap(it.r[k] - 1 - p, n);                            // received from r-1
+                st_stream(t.dst[it.r[k]], (long long)c * g.Rv + pos0 + it.w[k], slot[c * W + it.w[k]]);
+            }
+        }
+        __syncthreads();
+    }
+}
+
+static size_t ring_lds_bytes(const Geometry &g, bool bounds) {
+    return (size_t)g.n * g.W * 16 + (bounds ? ((size_t)g.n + 1) * sizeof(long long) : 0);
+}
+
+hipError_t launch_ring_allreduce(int dt, int op, const RankTable &t, const Geometry &g, int grid, hipStream_t s) {
+    return dispatch(dt, op, [&](auto D, auto O) {
+        hipLaunchKernelGGL((ring_allreduce_kernel<decltype(D)::value, decltype(O)::value>), dim3(grid),
+                           dim3(kThreads), ring_lds_bytes(g, true), s, t, g);
+        return hipGetLastError();
+    });
+}
+
+hipError_t launch_ring_reduce_scatter(int dt, int op, const RankTable &t, const Geometry &g, int grid,
+                                      hipStream_t s) {
+    return dispatch(dt, op, [&](auto D, auto O) {
+        hipLaunchKernelGGL((ring_reduce_scatter_kernel<decltype(D)::value, decltype(O)::value>), dim3(grid),
+                           dim3(kThreads), ring_lds_bytes(g, false), s, t, g);
+        return hipGetLastError();
+    });
+}
+
+hipError_t launch_ring_all_gather(const RankTable &t, const Geometry &g, int grid, hipStream_t s) {
+    hipLaunchKernelGGL(ring_all_gather_kernel, dim3(grid), dim3(kThreads), ring_lds_bytes(g, false), s, t, g);
+    return hipGetLastError();
+}
+
+}  // namespace ar

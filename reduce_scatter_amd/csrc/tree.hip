@@ -1,0 +1,94 @@
+// tree.hip -- the log-step tree schedule, staged through LDS.
+//
+// The "NCCL all-reduce" post (rakshithvasudev.github.io), section "The double
+// binary tree": ranks form a binary tree built by a bit trick (a rank's lowest
+// set bit fixes its depth; its parent clears that bit and sets the next one
+// up, falling back to just clearing it at the edge of the range).  Data is
+// reduced from the leaves up to the root, every node adding its own
+// contribution to what its children deliver, and the result is broadcast back
+// down, every node keeping a copy.  2 * depth dependent steps instead of the
+// ring's 2(n-1).
+//
+// One workgroup runs the whole tree for a window of W vectors at the same
+// offset of every rank buffer.  Item (rank v, vector w) holds rank v's
+// contribution; LDS holds one partial per rank.  Up phase, deepest level
+// first: partial(v) = own(v), then each child's partial in ascending rank
+// order; the root applies the postOp.  Down phase, root first: each rank
+// copies its parent's final value and stores it.  A workgroup barrier
+// separates the levels.  All of a rank's loads are issued at the start
+// (nothing they read depends on the tree), so the levels only wait on LDS.
+#include "ar_device.hpp"
+#include "ar_kernels.hpp"
+#include "dispatch.hpp"
+
+namespace ar {
+
+template <int DT, int OP>
+__global__ __launch_bounds__(kThreads) void tree_allreduce_kernel(const RankTable t, const TreeShape tree,
+                                                                  const Geometry g) {
+    extern __shared__ __align__(16) unsigned char lds[];
+    const int n = g.n, W = g.W;
+    u32x4 *slot = (u32x4 *)lds;
+    int r[kItemsPerThread], w[kItemsPerThread], cnt = 0;
+#pragma unroll
+    for (int k = 0; k < kItemsPerThread; ++k) {
+        const int q = threadIdx.x + k * kThreads;
+        r[k] = 0;
+        w[k] = 0;
+        if (q < n * W) {
+            r[k] = q / W;
+            w[k] = q - r[k] * W;
+            cnt = k + 1;
+        }
+    }
+    for (long long win = blockIdx.x; win < g.windows; win += gridDim.x) {
+        const long long pos0 = win * W;
+        u32x4 own[kItemsPerThread];
+        bool ok[kItemsPerThread];
+#pragma unroll
+        for (int k = 0; k < kItemsPerThread; ++k) {
+            ok[k] = k < cnt && pos0 + w[k] < g.Vfull;
+            if (ok[k]) own[k] = ld_stream(t.src[r[k]], pos0 + w[k]);
+        }
+        // up: deepest level first
+        for (int d = tree.max_depth; d >= 0; --d) {
+#pragma unroll
+            for (int k = 0; k < kItemsPerThread; ++k) {
+                if (!ok[k] || tree.depth[r[k]] != d) continue;
+                const int v = r[k];
+                Pack<DT> acc = first<DT, OP>(unpack<DT>(own[k]), g.s);
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const int ch = tree.child[v][e];
+                    if (ch >= 0) merge<DT, OP>(acc, unpack<DT>(slot[ch * W + w[k]]));
+                }
+                if (v == 0) post<DT, OP>(acc, n);
+                slot[v * W + w[k]] = pack<DT>(acc);
+            }
+            __syncthreads();
+        }
+        // down: the root keeps its value; each level copies from its parent
+        for (int d = 0; d <= tree.max_depth; ++d) {
+#pragma unroll
+            for (int k = 0; k < kItemsPerThread; ++k) {
+                if (!ok[k] || tree.depth[r[k]] != d) continue;
+                const int v = r[k];
+                u32x4 val = (v == 0) ? slot[w[k]] : slot[tree.parent[v] * W + w[k]];
+                slot[v * W + w[k]] = val;
+                st_stream(t.dst[v], pos0 + w[k], val);
+            }
+            __syncthreads();
+        }
+    }
+}
+
+hipError_t launch_tree_allreduce(int dt, int op, const RankTable &t, const TreeShape &tree, const Geometry &g,
+                                 int grid, hipStream_t s) {
+    return dispatch(dt, op, [&](auto D, auto O) {
+        hipLaunchKernelGGL((tree_allreduce_kernel<decltype(D)::value, decltype(O)::value>), dim3(grid),
+                           dim3(kThreads), (size_t)g.n * g.W * 16, s, t, tree, g);
+        return hipGetLastError();
+    });
+}
+
+}  // namespace ar

@@ -1,0 +1,201 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, element by
+element, at sizes the oracle finishes in seconds that still span several
+tiles / LDS windows and a ragged tail.
+
+Bar: ring and fused results are bit-identical to the ring oracle (they use
+its hop order), tree results bit-identical to the tree oracle; all-gather
+and every integer result are bit-exact by construction."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from devutil import assert_bits_equal, empty, sync, to_device, to_host
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+ar = pytest.importorskip("reduce_scatter_amd")
+
+DTYPES = ["f32", "bf16", "f16", "i32"]
+OPS = ["sum", "prod", "min", "max", "avg"]
+LANES = {"f32": 4, "i32": 4, "bf16": 8, "f16": 8}
+FUSED_TILE = 512          # 16-byte vectors per fused tile (threads x unroll)
+
+
+def counts_for(n, dtype):
+    u = LANES[dtype]
+    return [1, 5, u * n * 3, u * n * 3 + 1, n * FUSED_TILE * u * 2 + u * 3 + 3]
+
+
+def inputs(seed, n, count, dtype, op):
+    kind = "pos" if op == "prod" else "normal"
+    return [workloads.random_values(seed, n * 1000 + count, r, count, dtype, kind) for r in range(n)]
+
+
+def run_allreduce(xs, dtype, op, sched, inplace=False):
+    n = len(xs)
+    d_in = [to_device(x, dtype) for x in xs]
+    d_out = d_in if inplace else [empty(x.size, dtype, 0) for x in xs]
+    ar.ar_allreduce(d_in, d_out, xs[0].size, dtype, op, sched=sched)
+    sync()
+    return [to_host(t, dtype) for t in d_out]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("op", OPS)
+def test_allreduce_matches_oracle(dtype, op):
+    for n in (1, 2, 3, 5, 8, 16):
+        for count in counts_for(n, dtype):
+            print("allreduce", dtype, op, "n=%d count=%d" % (n, count), flush=True)
+            xs = inputs(1, n, count, dtype, op)
+            ring = oracle.ring_allreduce(xs, dtype, op)
+            tree = oracle.tree_allreduce(xs, dtype, op)
+            for sched in ("fused", "ring", "tree", "auto"):
+                got = run_allreduce(xs, dtype, op, sched)
+                ref = tree if sched == "tree" else ring
+                for r in range(n):
+                    assert_bits_equal(got[r], ref[r], "%s %s %s n=%d count=%d rank %d" % (sched, dtype, op, n, count, r))
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_allreduce_in_place_equals_out_of_place(dtype):
+    n, count = 8, 8 * FUSED_TILE * 8 + 13
+    for op in OPS:
+        xs = inputs(2, n, count, dtype, op)
+        for sched in ("fused", "ring", "tree"):
+            a = run_allreduce(xs, dtype, op, sched)
+            b = run_allreduce(xs, dtype, op, sched, inplace=True)
+            for r in range(n):
+                assert_bits_equal(b[r], a[r], "in place %s %s %s" % (sched, dtype, op))
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_allreduce_element_wise_path(dtype):
+    """Buffers that are element-aligned but not 16-byte aligned take the
+    element-wise path; results are identical."""
+    n, count = 5, 3001
+    for op in ("sum", "avg", "max"):
+        xs = inputs(3, n, count, dtype, op)
+        ring = oracle.ring_allreduce(xs, dtype, op)
+        tree = oracle.tree_allreduce(xs, dtype, op)
+        for sched in ("fused", "ring", "tree"):
+            d_in = [to_device(np.concatenate([x[:1], x]), dtype)[1:] for x in xs]
+            d_out = [empty(count + 1, dtype, 0)[1:] for _ in xs]
+            assert d_in[0].data_ptr() % 16 != 0
+            ar.ar_allreduce(d_in, d_out, count, dtype, op, sched=sched)
+            sync()
+            ref = tree if sched == "tree" else ring
+            for r in range(n):
+                assert_bits_equal(to_host(d_out[r], dtype), ref[r], "elem %s %s %s" % (sched, dtype, op))
+
+
+def run_rs(xs, dtype, op, sched, inplace=False, misalign=False):
+    n = len(xs)
+    R = xs[0].size // n
+    if misalign:
+        d_in = [to_device(np.concatenate([x[:1], x]), dtype)[1:] for x in xs]
+    else:
+        d_in = [to_device(x, dtype) for x in xs]
+    if inplace:
+        d_out = [d_in[r][r * R:(r + 1) * R] for r in range(n)]
+    else:
+        d_out = [empty(R, dtype, 0) for _ in range(n)]
+    ar.ar_reduce_scatter(d_in, d_out, R, dtype, op, sched=sched)
+    sync()
+    return [to_host(t, dtype) for t in d_out]
+
+
+def run_ag(xs, dtype, sched, inplace=False, misalign=False):
+    n = len(xs)
+    R = xs[0].size
+    if inplace:
+        d_out = [empty(n * R, dtype, 0) for _ in range(n)]
+        for r in range(n):
+            d_out[r][r * R:(r + 1) * R].copy_(to_device(xs[r], dtype))
+        d_in = [d_out[r][r * R:(r + 1) * R] for r in range(n)]
+    elif misalign:
+        d_in = [to_device(np.concatenate([x[:1], x]), dtype)[1:] for x in xs]
+        d_out = [empty(n * R + 1, dtype, 0)[1:] for _ in range(n)]
+    else:
+        d_in = [to_device(x, dtype) for x in xs]
+        d_out = [empty(n * R, dtype, 0) for _ in range(n)]
+    ar.ar_all_gather(d_in, d_out, R, dtype, sched=sched)
+    sync()
+    return [to_host(t, dtype) for t in d_out]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("op", OPS)
+def test_reduce_scatter_and_all_gather_match_oracle(dtype, op):
+    u = LANES[dtype]
+    for n in (1, 2, 3, 8, 16):
+        for R in (1, 3, u, u * 37, FUSED_TILE * u * 2 + u * 5):
+            print("rs/ag", dtype, op, "n=%d R=%d" % (n, R), flush=True)
+            xs = inputs(4, n, n * R, dtype, op)
+            ref = oracle.ring_reduce_scatter(xs, dtype, op)
+            for sched in ("fused", "ring", "auto"):
+                for kw in ({}, {"inplace": True}, {"misalign": True}):
+                    got = run_rs(xs, dtype, op, sched, **kw)
+                    for r in range(n):
+                        assert_bits_equal(got[r], ref[r], "rs %s %s %s n=%d R=%d %s" % (sched, dtype, op, n, R, kw))
+            if op != "sum":
+                continue
+            pieces = [workloads.random_values(5, n, r, R, dtype) for r in range(n)]
+            want = oracle.ring_all_gather(pieces, dtype)
+            for sched in ("fused", "ring", "auto"):
+                for kw in ({}, {"inplace": True}, {"misalign": True}):
+                    got = run_ag(pieces, dtype, sched, **kw)
+                    for r in range(n):
+                        assert_bits_equal(got[r], want[r], "ag %s %s n=%d R=%d %s" % (sched, dtype, n, R, kw))
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_allreduce_equals_reduce_scatter_then_all_gather(dtype):
+    """all-reduce = reduce-scatter + all-gather, bit for bit (count a multiple
+    of n 16-byte units, so the two calls cut the same chunks)."""
+    n = 8
+    u = LANES[dtype]
+    R = u * 1000
+    for op in OPS:
+        xs = inputs(6, n, n * R, dtype, op)
+        for sched in ("fused", "ring"):
+            full = run_allreduce(xs, dtype, op, sched)
+            parts = run_rs(xs, dtype, op, sched)
+            gathered = run_ag(parts, dtype, sched)
+            for r in range(n):
+                assert_bits_equal(gathered[r], full[r], "AR vs RS+AG %s %s %s" % (sched, dtype, op))
+
+
+def test_c1_workload_every_schedule():
+    """C1: n = 4, fp32, 1024 integer-valued elements (exact sums); AR by every
+    schedule, RS on the same input and AG of the RS outputs, all against the
+    exact integer sum."""
+    xs = workloads.c1_inputs()
+    want = sum(x.astype(np.int64) for x in xs).astype(np.float32)
+    for sched in ("fused", "ring", "tree", "auto"):
+        for y in run_allreduce(xs, "f32", "sum", sched):
+            assert_bits_equal(y, want, "c1 " + sched)
+    parts = run_rs(xs, "f32", "sum", "auto")
+    for r in range(4):
+        assert_bits_equal(parts[r], want[r * 256:(r + 1) * 256], "c1 rs")
+    for y in run_ag(parts, "f32", "auto"):
+        assert_bits_equal(y, want, "c1 ag")
+
+
+def test_large_rank_counts():
+    """n up to the table limit (128) and the bucketed workload's 72."""
+    for n in (72, 128):
+        count = n * 4 * 40 + 3
+        xs = inputs(7, n, count, "f32", "avg")
+        ring = oracle.ring_allreduce(xs, "f32", "avg")
+        tree = oracle.tree_allreduce(xs, "f32", "avg")
+        for sched in ("fused", "ring", "tree"):
+            got = run_allreduce(xs, "f32", "avg", sched)
+            ref = tree if sched == "tree" else ring
+            for r in (0, n // 2, n - 1):
+                assert_bits_equal(got[r], ref[r], "n=%d %s" % (n, sched))

@@ -203,6 +203,27 @@ def test_brute_force_reduce_scatter_and_all_gather(dtype, op):
                 assert g.tobytes() == cat.tobytes()
 
 
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("op", OPS)
+def test_direct_reduce_brute_force(dtype, op):
+    """The plain definition, for the cases where it is exact, against brute
+    force and against the ring simulation (which must agree for these)."""
+    if dtype != "i32" and op not in ("min", "max"):
+        with pytest.raises(RuntimeError):
+            oracle.direct_reduce([np.zeros(4, oracle.NP_DTYPE[dtype])], dtype, op)
+        return
+    for n in range(1, 10):
+        for count in (0, 1, 5, 37):
+            xs = _data(dtype, op, n, count, 17)
+            y = oracle.direct_reduce(xs, dtype, op)
+            fx = [as_float(x, dtype) if dtype != "i32" else x.astype(np.int64) for x in xs]
+            want = [_brute_elem([f[i] for f in fx], dtype, op, n) for i in range(count)]
+            got = as_float(y, dtype) if dtype != "i32" else y.astype(np.int64)
+            assert [Fraction(float(v)) if dtype != "i32" else int(v) for v in got] == want
+            assert y.tobytes() == oracle.ring_allreduce(xs, dtype, op)[0].tobytes() or count == 0 \
+                or (op in ("min", "max") and dtype != "i32")          # +-0 ties may differ in sign
+
+
 def test_c1_workload_is_exact():
     """C1: integers in [-8, 8] stored as fp32, n = 4: every sum is exact, so the
     ring, the tree and a direct integer sum agree bit for bit."""
