@@ -26,6 +26,16 @@ if not os.path.exists(_LIB_PATH):
     raise ImportError("libar.so is not built (expected at %s); build it with `python -m reduce_scatter_amd.build` "
                       "or __graft_entry__.build()" % _LIB_PATH)
 
+# One HIP runtime per process: PyTorch-ROCm ships its own libamdhip64 (same
+# SONAME as the system one).  Loading torch first makes libar.so bind to the
+# runtime torch already loaded; loading libar.so first would pull in the
+# system copy and torch would then load a second, separate runtime, whose
+# devices, streams and allocations are not the ones libar.so sees.
+try:
+    import torch  # noqa: F401
+except ImportError:
+    pass
+
 _lib = ctypes.CDLL(_LIB_PATH)
 
 

@@ -56,8 +56,11 @@ ar_status_t device_cus(int *cus) {
     if (dev < 0 || dev >= 64) return AR_ERR_HIP;
     int v = g_cus[dev].load(std::memory_order_relaxed);
     if (v <= 0) {
-        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+        hipError_t e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess || v <= 0) {
+            if (debug_enabled()) fprintf(stderr, "[ar] device query failed: %d\n", (int)e);
             return AR_ERR_HIP;
+        }
         g_cus[dev].store(v, std::memory_order_relaxed);
     }
     *cus = v;
@@ -151,7 +154,11 @@ ar_status_t choose(ar_coll_t coll, size_t count, ar_dtype_t dtype, ar_op_t op, i
     return AR_OK;
 }
 
-ar_status_t hip_status(hipError_t e) { return e == hipSuccess ? AR_OK : AR_ERR_HIP; }
+ar_status_t hip_status(hipError_t e) {
+    if (e == hipSuccess) return AR_OK;
+    if (debug_enabled()) fprintf(stderr, "[ar] HIP error %d: %s\n", (int)e, hipGetErrorString(e));
+    return AR_ERR_HIP;
+}
 
 void fill_table(RankTable &t, const void *const *send, void *const *recv, int n) {
     memset(&t, 0, sizeof t);

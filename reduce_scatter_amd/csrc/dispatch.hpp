@@ -7,6 +7,14 @@
 
 namespace ar {
 
+// Launch ``k`` and return the launch's own status (not the thread's last-error
+// state, which earlier unrelated runtime calls may have left set).
+template <typename... P, typename... A>
+hipError_t launch(void (*k)(P...), dim3 grid, dim3 block, size_t lds, hipStream_t s, const A &...args) {
+    void *ptrs[] = {(void *)&args...};
+    return hipLaunchKernel((const void *)k, grid, block, ptrs, lds, s);
+}
+
 template <int DT, typename F> hipError_t dispatch_op(int op, F &&f) {
     switch (op) {
     case SUM: return f(std::integral_constant<int, DT>{}, std::integral_constant<int, SUM>{});

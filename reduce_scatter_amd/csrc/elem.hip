@@ -105,9 +105,7 @@ hipError_t launch_elem_ring_allreduce(int dt, int op, const RankTable &t, const 
                                       long long e1, hipStream_t s) {
     if (e1 <= e0) return hipSuccess;
     return dispatch(dt, op, [&](auto D, auto O) {
-        hipLaunchKernelGGL((elem_ring_allreduce_kernel<decltype(D)::value, decltype(O)::value>),
-                           dim3(elem_grid(e1 - e0)), dim3(kThreads), 0, s, t, g, e0, e1);
-        return hipGetLastError();
+        return launch(elem_ring_allreduce_kernel<decltype(D)::value, decltype(O)::value>, dim3(elem_grid(e1 - e0)), dim3(kThreads), 0, s, t, g, e0, e1);
     });
 }
 
@@ -115,9 +113,7 @@ hipError_t launch_elem_tree_allreduce(int dt, int op, const RankTable &t, const 
                                       long long e0, long long e1, hipStream_t s) {
     if (e1 <= e0) return hipSuccess;
     return dispatch(dt, op, [&](auto D, auto O) {
-        hipLaunchKernelGGL((elem_tree_allreduce_kernel<decltype(D)::value, decltype(O)::value>),
-                           dim3(elem_grid(e1 - e0)), dim3(kThreads), 0, s, t, tree, g, e0, e1);
-        return hipGetLastError();
+        return launch(elem_tree_allreduce_kernel<decltype(D)::value, decltype(O)::value>, dim3(elem_grid(e1 - e0)), dim3(kThreads), 0, s, t, tree, g, e0, e1);
     });
 }
 
@@ -125,21 +121,15 @@ hipError_t launch_elem_reduce_scatter(int dt, int op, const RankTable &t, const 
                                       hipStream_t s) {
     if (R <= 0) return hipSuccess;
     return dispatch(dt, op, [&](auto D, auto O) {
-        hipLaunchKernelGGL((elem_reduce_scatter_kernel<decltype(D)::value, decltype(O)::value>),
-                           dim3(elem_grid((long long)g.n * R)), dim3(kThreads), 0, s, t, g, R);
-        return hipGetLastError();
+        return launch(elem_reduce_scatter_kernel<decltype(D)::value, decltype(O)::value>, dim3(elem_grid((long long)g.n * R)), dim3(kThreads), 0, s, t, g, R);
     });
 }
 
 hipError_t launch_elem_all_gather(int elem_bytes, const RankTable &t, const Geometry &g, long long R, hipStream_t s) {
     if (R <= 0) return hipSuccess;
-    if (elem_bytes == 4)
-        hipLaunchKernelGGL(elem_all_gather_kernel<uint32_t>, dim3(elem_grid((long long)g.n * R)), dim3(kThreads), 0,
-                           s, t, g, R);
-    else
-        hipLaunchKernelGGL(elem_all_gather_kernel<uint16_t>, dim3(elem_grid((long long)g.n * R)), dim3(kThreads), 0,
-                           s, t, g, R);
-    return hipGetLastError();
+    const dim3 grid(elem_grid((long long)g.n * R));
+    if (elem_bytes == 4) return launch(elem_all_gather_kernel<uint32_t>, grid, dim3(kThreads), 0, s, t, g, R);
+    return launch(elem_all_gather_kernel<uint16_t>, grid, dim3(kThreads), 0, s, t, g, R);
 }
 
 }  // namespace ar

@@ -182,24 +182,19 @@ __global__ __launch_bounds__(kThreads) void fused_all_gather_kernel(const RankTa
 
 hipError_t launch_fused_allreduce(int dt, int op, const RankTable &t, const Geometry &g, int grid, hipStream_t s) {
     return dispatch(dt, op, [&](auto D, auto O) {
-        hipLaunchKernelGGL((fused_allreduce_kernel<decltype(D)::value, decltype(O)::value>), dim3(grid),
-                           dim3(kThreads), 0, s, t, g);
-        return hipGetLastError();
+        return launch(fused_allreduce_kernel<decltype(D)::value, decltype(O)::value>, dim3(grid), dim3(kThreads), 0, s, t, g);
     });
 }
 
 hipError_t launch_fused_reduce_scatter(int dt, int op, const RankTable &t, const Geometry &g, int grid,
                                        hipStream_t s) {
     return dispatch(dt, op, [&](auto D, auto O) {
-        hipLaunchKernelGGL((fused_reduce_scatter_kernel<decltype(D)::value, decltype(O)::value>), dim3(grid),
-                           dim3(kThreads), 0, s, t, g);
-        return hipGetLastError();
+        return launch(fused_reduce_scatter_kernel<decltype(D)::value, decltype(O)::value>, dim3(grid), dim3(kThreads), 0, s, t, g);
     });
 }
 
 hipError_t launch_fused_all_gather(const RankTable &t, const Geometry &g, int grid, hipStream_t s) {
-    hipLaunchKernelGGL(fused_all_gather_kernel, dim3(grid), dim3(kThreads), 0, s, t, g);
-    return hipGetLastError();
+    return launch(fused_all_gather_kernel, dim3(grid), dim3(kThreads), 0, s, t, g);
 }
 
 }  // namespace ar

@@ -223,24 +223,19 @@ static size_t ring_lds_bytes(const Geometry &g, bool bounds) {
 
 hipError_t launch_ring_allreduce(int dt, int op, const RankTable &t, const Geometry &g, int grid, hipStream_t s) {
     return dispatch(dt, op, [&](auto D, auto O) {
-        hipLaunchKernelGGL((ring_allreduce_kernel<decltype(D)::value, decltype(O)::value>), dim3(grid),
-                           dim3(kThreads), ring_lds_bytes(g, true), s, t, g);
-        return hipGetLastError();
+        return launch(ring_allreduce_kernel<decltype(D)::value, decltype(O)::value>, dim3(grid), dim3(kThreads), ring_lds_bytes(g, true), s, t, g);
     });
 }
 
 hipError_t launch_ring_reduce_scatter(int dt, int op, const RankTable &t, const Geometry &g, int grid,
                                       hipStream_t s) {
     return dispatch(dt, op, [&](auto D, auto O) {
-        hipLaunchKernelGGL((ring_reduce_scatter_kernel<decltype(D)::value, decltype(O)::value>), dim3(grid),
-                           dim3(kThreads), ring_lds_bytes(g, false), s, t, g);
-        return hipGetLastError();
+        return launch(ring_reduce_scatter_kernel<decltype(D)::value, decltype(O)::value>, dim3(grid), dim3(kThreads), ring_lds_bytes(g, false), s, t, g);
     });
 }
 
 hipError_t launch_ring_all_gather(const RankTable &t, const Geometry &g, int grid, hipStream_t s) {
-    hipLaunchKernelGGL(ring_all_gather_kernel, dim3(grid), dim3(kThreads), ring_lds_bytes(g, false), s, t, g);
-    return hipGetLastError();
+    return launch(ring_all_gather_kernel, dim3(grid), dim3(kThreads), ring_lds_bytes(g, false), s, t, g);
 }
 
 }  // namespace ar

@@ -85,9 +85,7 @@ __global__ __launch_bounds__(kThreads) void tree_allreduce_kernel(const RankTabl
 hipError_t launch_tree_allreduce(int dt, int op, const RankTable &t, const TreeShape &tree, const Geometry &g,
                                  int grid, hipStream_t s) {
     return dispatch(dt, op, [&](auto D, auto O) {
-        hipLaunchKernelGGL((tree_allreduce_kernel<decltype(D)::value, decltype(O)::value>), dim3(grid),
-                           dim3(kThreads), (size_t)g.n * g.W * 16, s, t, tree, g);
-        return hipGetLastError();
+        return launch(tree_allreduce_kernel<decltype(D)::value, decltype(O)::value>, dim3(grid), dim3(kThreads), (size_t)g.n * g.W * 16, s, t, tree, g);
     });
 }
 

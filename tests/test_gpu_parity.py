@@ -199,3 +199,27 @@ def test_large_rank_counts():
             ref = tree if sched == "tree" else ring
             for r in (0, n // 2, n - 1):
                 assert_bits_equal(got[r], ref[r], "n=%d %s" % (n, sched))
+
+
+def test_one_hip_runtime_whatever_the_import_order():
+    """Importing the binding before torch must not leave two HIP runtimes in
+    the process (torch ships its own copy of libamdhip64); the call must work."""
+    import subprocess
+    import sys
+    code = r'''
+import reduce_scatter_amd as ar
+import torch
+xs = [torch.full((1000,), float(r + 1), device="cuda") for r in range(4)]
+ys = [torch.empty_like(x) for x in xs]
+ar.ar_allreduce(xs, ys, 1000, "f32", "sum")
+torch.cuda.synchronize()
+assert all(float(y.min()) == 10.0 == float(y.max()) for y in ys)
+maps = open("/proc/self/maps").read()
+hips = sorted({line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line})
+assert len(hips) == 1, hips
+print("ok", hips[0])
+'''
+    import os
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=100)
+    assert r.returncode == 0, r.stdout + r.stderr
