@@ -24,6 +24,8 @@ struct RankTable {
 //                   [k*Rv, (k+1)*Rv) of every output.
 struct Geometry {
     long long V;        // all-reduce: ceil(count / lanes)
+    long long q;        // all-reduce: V / n
+    int rem;            // all-reduce: V % n (chunk c starts at c*q + floor(c*rem/n))
     long long Vfull;    // all-reduce: count / lanes (vectors with no tail)
     long long Rv;       // reduce-scatter / all-gather: vectors per slice
     long long windows;  // work units along a chunk (tiles or LDS windows)
@@ -45,9 +47,11 @@ struct TreeShape {
 // Launchers.  dt / op use the ar_dtype_t / ar_op_t numbering.  ``grid`` is
 // the number of workgroups (already clamped to the work available).
 // Vector paths (every pointer 16-byte aligned):
-hipError_t launch_fused_allreduce(int dt, int op, const RankTable &t, const Geometry &g, int grid, hipStream_t s);
-hipError_t launch_fused_reduce_scatter(int dt, int op, const RankTable &t, const Geometry &g, int grid, hipStream_t s);
-hipError_t launch_fused_all_gather(const RankTable &t, const Geometry &g, int grid, hipStream_t s);
+// Fused kernels launch one workgroup per tile (g.windows tiles per chunk, n
+// chunks); ``lds`` is the dynamic LDS each workgroup reserves (a residency cap).
+hipError_t launch_fused_allreduce(int dt, int op, const RankTable &t, const Geometry &g, int lds, hipStream_t s);
+hipError_t launch_fused_reduce_scatter(int dt, int op, const RankTable &t, const Geometry &g, int lds, hipStream_t s);
+hipError_t launch_fused_all_gather(const RankTable &t, const Geometry &g, int lds, hipStream_t s);
 hipError_t launch_ring_allreduce(int dt, int op, const RankTable &t, const Geometry &g, int grid, hipStream_t s);
 hipError_t launch_ring_reduce_scatter(int dt, int op, const RankTable &t, const Geometry &g, int grid, hipStream_t s);
 hipError_t launch_ring_all_gather(const RankTable &t, const Geometry &g, int grid, hipStream_t s);
@@ -65,11 +69,14 @@ hipError_t launch_elem_all_gather(int elem_bytes, const RankTable &t, const Geom
 
 // Threads per workgroup for every vector kernel.
 constexpr int kThreads = 256;
-// Fused kernels: 16-byte vectors per thread per tile, and ranks whose loads
-// are issued before the first of them is combined.
-constexpr int kUnroll = 2;
-constexpr int kRankBatch = 8;
-constexpr int kFusedTile = kThreads * kUnroll;
+// Fused kernels: one wavefront per workgroup, one 16-byte vector per lane.
+constexpr int kFusedThreads = 64;
+constexpr int kFusedTile = kFusedThreads;
+// Default dynamic-LDS reservation of a fused workgroup, in KB, per collective
+// (caps the resident workgroups per CU; see fused.hip and api.cpp).
+constexpr int kFusedLdsAllReduceKB = 24;
+constexpr int kFusedLdsReduceScatterKB = 0;
+constexpr int kFusedLdsAllGatherKB = 22;
 // Ring/tree kernels: at most this many (rank, vector) items per thread.
 constexpr int kItemsPerThread = 4;
 

@@ -24,12 +24,12 @@ ar = pytest.importorskip("reduce_scatter_amd")
 DTYPES = ["f32", "bf16", "f16", "i32"]
 OPS = ["sum", "prod", "min", "max", "avg"]
 LANES = {"f32": 4, "i32": 4, "bf16": 8, "f16": 8}
-FUSED_TILE = 512          # 16-byte vectors per fused tile (threads x unroll)
+FUSED_TILE = 64           # 16-byte vectors per fused tile (one wavefront, one per lane)
 
 
 def counts_for(n, dtype):
     u = LANES[dtype]
-    return [1, 5, u * n * 3, u * n * 3 + 1, n * FUSED_TILE * u * 2 + u * 3 + 3]
+    return [1, 5, u * n * 3, u * n * 3 + 1, n * 512 * u * 2 + u * 3 + 3]
 
 
 def inputs(seed, n, count, dtype, op):
@@ -134,7 +134,7 @@ def run_ag(xs, dtype, sched, inplace=False, misalign=False):
 def test_reduce_scatter_and_all_gather_match_oracle(dtype, op):
     u = LANES[dtype]
     for n in (1, 2, 3, 8, 16):
-        for R in (1, 3, u, u * 37, FUSED_TILE * u * 2 + u * 5):
+        for R in (1, 3, u, u * 37, 512 * u * 2 + u * 5):
             print("rs/ag", dtype, op, "n=%d R=%d" % (n, R), flush=True)
             xs = inputs(4, n, n * R, dtype, op)
             ref = oracle.ring_reduce_scatter(xs, dtype, op)
