@@ -96,6 +96,24 @@ int fused_lds_bytes(ar_coll_t coll) {
     }
 }
 
+// Dynamic LDS reservation (bytes) of the ring / tree workgroups; the
+// AR_RING_LDS_KB / AR_TREE_LDS_KB variables override the defaults.
+int env_kb(const char *name, int dflt) {
+    const char *e = getenv(name);
+    long kb = (e && *e) ? atol(e) : dflt;
+    if (kb < 0) return -1;
+    return (int)(kb > 64 ? 64 : kb) * 1024;
+}
+int ring_lds_bytes(ar_coll_t coll) {
+    static int v = env_kb("AR_RING_LDS_KB", -1);
+    if (v >= 0 && getenv("AR_RING_LDS_KB")) return v;
+    return (coll == AR_COLL_ALL_GATHER ? kRingLdsAllGatherKB : kRingLdsKB) * 1024;
+}
+int tree_lds_bytes() {
+    static int v = env_kb("AR_TREE_LDS_KB", kTreeLdsKB);
+    return v < 0 ? 0 : v;
+}
+
 // Window width (16-byte vectors per rank) for the LDS-staged schedules:
 // n * W items of one workgroup, at most kThreads * kItemsPerThread.
 int lds_window(int n) {
@@ -271,11 +289,11 @@ ar_status_t ar_allreduce(const void *const *sendbufs, void *const *recvbufs, siz
             g.W = lds_window(n);
             const long long maxlen = (g.V + n - 1) / n;
             g.windows = (maxlen + g.W - 1) / g.W;
-            h = launch_ring_allreduce(dtype, op, t, g, grid_for(g.windows, cus, 4), stream);
+            h = launch_ring_allreduce(dtype, op, t, g, grid_for(g.windows, cus, 4), ring_lds_bytes(AR_COLL_ALLREDUCE), stream);
         } else {
             g.W = lds_window(n);
             g.windows = (g.Vfull + g.W - 1) / g.W;
-            h = launch_tree_allreduce(dtype, op, t, tree, g, grid_for(g.windows, cus, 4), stream);
+            h = launch_tree_allreduce(dtype, op, t, tree, g, grid_for(g.windows, cus, 4), tree_lds_bytes(), stream);
         }
     }
     if (h == hipSuccess && g.Vfull * lanes < (long long)count) {             // tail: last count mod lanes elements
@@ -323,7 +341,7 @@ ar_status_t ar_reduce_scatter(const void *const *sendbufs, void *const *recvbufs
     }
     g.W = lds_window(n);
     g.windows = (g.Rv + g.W - 1) / g.W;
-    return hip_status(launch_ring_reduce_scatter(dtype, op, t, g, grid_for(g.windows, cus, 4), stream));
+    return hip_status(launch_ring_reduce_scatter(dtype, op, t, g, grid_for(g.windows, cus, 4), ring_lds_bytes(AR_COLL_REDUCE_SCATTER), stream));
 }
 
 ar_status_t ar_all_gather(const void *const *sendbufs, void *const *recvbufs, size_t sendcount, ar_dtype_t dtype,
@@ -363,7 +381,7 @@ ar_status_t ar_all_gather(const void *const *sendbufs, void *const *recvbufs, si
     }
     g.W = lds_window(n);
     g.windows = (g.Rv + g.W - 1) / g.W;
-    return hip_status(launch_ring_all_gather(t, g, grid_for(g.windows, cus, 4), stream));
+    return hip_status(launch_ring_all_gather(t, g, grid_for(g.windows, cus, 4), ring_lds_bytes(AR_COLL_ALL_GATHER), stream));
 }
 
 }  // extern "C"

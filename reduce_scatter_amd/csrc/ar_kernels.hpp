@@ -52,11 +52,16 @@ struct TreeShape {
 hipError_t launch_fused_allreduce(int dt, int op, const RankTable &t, const Geometry &g, int lds, hipStream_t s);
 hipError_t launch_fused_reduce_scatter(int dt, int op, const RankTable &t, const Geometry &g, int lds, hipStream_t s);
 hipError_t launch_fused_all_gather(const RankTable &t, const Geometry &g, int lds, hipStream_t s);
-hipError_t launch_ring_allreduce(int dt, int op, const RankTable &t, const Geometry &g, int grid, hipStream_t s);
-hipError_t launch_ring_reduce_scatter(int dt, int op, const RankTable &t, const Geometry &g, int grid, hipStream_t s);
-hipError_t launch_ring_all_gather(const RankTable &t, const Geometry &g, int grid, hipStream_t s);
+// Ring / tree: ``grid`` sizes the persistent launch of the any-n kernels;
+// the compile-time-n kernels launch one workgroup per window and reserve
+// ``lds`` bytes of dynamic LDS (a residency cap, as for the fused kernels).
+hipError_t launch_ring_allreduce(int dt, int op, const RankTable &t, const Geometry &g, int grid, int lds,
+                                 hipStream_t s);
+hipError_t launch_ring_reduce_scatter(int dt, int op, const RankTable &t, const Geometry &g, int grid, int lds,
+                                      hipStream_t s);
+hipError_t launch_ring_all_gather(const RankTable &t, const Geometry &g, int grid, int lds, hipStream_t s);
 hipError_t launch_tree_allreduce(int dt, int op, const RankTable &t, const TreeShape &tree, const Geometry &g,
-                                 int grid, hipStream_t s);
+                                 int grid, int lds, hipStream_t s);
 // Element-wise paths (any alignment, and the all-reduce tail), elements
 // [e_begin, e_end) of every rank buffer / slice:
 hipError_t launch_elem_ring_allreduce(int dt, int op, const RankTable &t, const Geometry &g, long long e_begin,
@@ -77,6 +82,11 @@ constexpr int kFusedTile = kFusedThreads;
 constexpr int kFusedLdsAllReduceKB = 24;
 constexpr int kFusedLdsReduceScatterKB = 0;
 constexpr int kFusedLdsAllGatherKB = 22;
+// Default dynamic-LDS reservation of the compile-time-n ring and tree
+// workgroups, in KB (on top of their static LDS).
+constexpr int kRingLdsKB = 0;
+constexpr int kRingLdsAllGatherKB = 0;
+constexpr int kTreeLdsKB = 0;
 // Ring/tree kernels: at most this many (rank, vector) items per thread.
 constexpr int kItemsPerThread = 4;
 

@@ -217,24 +217,198 @@ __global__ __launch_bounds__(kThreads) void ring_all_gather_kernel(const RankTab
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// Compile-time rank counts (n = NR in {2, 4, 8, 16}): one (rank, vector) item
+// per thread, W vectors per rank per window (RingShape), and every step's
+// load issued before the first step runs (a rank's contributions do not
+// depend on the running totals, only the LDS work does), so a window costs
+// about one HBM round trip plus n barriers.  One workgroup per window, windows
+// in address order.
+// ---------------------------------------------------------------------------
+template <int NR> __device__ __forceinline__ int wrap_c(int a) { return (a + NR) % NR; }
+
+// Vectors per rank in one window: 64 (1 KB pieces, as wide as a wavefront's
+// 16-byte access), except n = 16 where 32 keeps the workgroup at 512 threads
+// within the register budget.  Threads per workgroup = NR * window.
+template <int NR> struct RingShape {
+    static constexpr int W = NR == 16 ? 32 : 64;
+    static constexpr int T = NR * W;
+};
+
+// chunk c of an all-reduce in vectors: [start(c), min(start(c+1), Vfull))
+__device__ __forceinline__ long long ring_chunk_start(int c, const Geometry &g) {
+    const long long b = (long long)c * g.q;
+    return g.rem ? b + (long long)((unsigned)(c * g.rem) / (unsigned)g.n) : b;
+}
+
+template <int DT, int OP, int NR>
+__global__ __launch_bounds__(RingShape<NR>::T) void ring_allreduce_fast(const RankTable t, const Geometry g) {
+    constexpr int W = RingShape<NR>::W;
+    __shared__ u32x4 slot[NR * W];                 // the wire: one slot per chunk and vector
+    const int r = threadIdx.x / W, w = threadIdx.x % W;
+    const long long pos = (long long)blockIdx.x * W + w;
+    u32x4 raw[NR];
+    long long vv[NR];
+    bool ok[NR];
+#pragma unroll
+    for (int p = 0; p < NR; ++p) {                 // step p: rank r handles chunk (r-1-p) mod n
+        const int c = wrap_c<NR>(r - 1 - p);
+        long long e = ring_chunk_start(c + 1, g);
+        e = e < g.Vfull ? e : g.Vfull;
+        const long long v = ring_chunk_start(c, g) + pos;
+        ok[p] = v < e;
+        vv[p] = ok[p] ? v : 0;                     // an always-valid address for lanes past the chunk
+        raw[p] = ld_stream(t.src[r], vv[p]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // reduce-scatter half: send, n-2 x receive-reduce-send, receive-reduce-copy-send with the postOp
+#pragma unroll
+    for (int p = 0; p < NR; ++p) {
+        const int c = wrap_c<NR>(r - 1 - p);
+        if (ok[p]) {
+            Pack<DT> acc;
+            if (p == 0) {
+                acc = first<DT, OP>(unpack<DT>(raw[p]), g.s);
+            } else {
+                acc = unpack<DT>(slot[c * W + w]);
+                hop<DT, OP>(acc, unpack<DT>(raw[p]), g.s);
+            }
+            if (p == NR - 1) {                     // chunk r completes here: postOp, keep it
+                post<DT, OP>(acc, NR);
+                st_stream(t.dst[r], vv[p], pack<DT>(acc));
+            }
+            slot[c * W + w] = pack<DT>(acc);
+        }
+        __syncthreads();                           // the hop to rank r+1
+    }
+    // all-gather half: at step p rank r receives finished chunk (r-1-p) mod n and keeps it
+#pragma unroll
+    for (int p = 0; p < NR - 1; ++p) {
+        const int c = wrap_c<NR>(r - 1 - p);
+        if (ok[p]) st_stream(t.dst[r], vv[p], slot[c * W + w]);
+    }
+}
+
+template <int DT, int OP, int NR>
+__global__ __launch_bounds__(RingShape<NR>::T) void ring_reduce_scatter_fast(const RankTable t, const Geometry g) {
+    constexpr int W = RingShape<NR>::W;
+    __shared__ u32x4 slot[NR * W];
+    const int r = threadIdx.x / W, w = threadIdx.x % W;
+    const long long pos = (long long)blockIdx.x * W + w;
+    const bool ok = pos < g.Rv;                    // the same position in every chunk
+    const long long vpos = ok ? pos : 0;
+    u32x4 raw[NR];
+#pragma unroll
+    for (int p = 0; p < NR; ++p)
+        raw[p] = ld_stream(t.src[r], (long long)wrap_c<NR>(r - 1 - p) * g.Rv + vpos);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int p = 0; p < NR; ++p) {
+        const int c = wrap_c<NR>(r - 1 - p);
+        if (ok) {
+            Pack<DT> acc;
+            if (p == 0) {
+                acc = first<DT, OP>(unpack<DT>(raw[p]), g.s);
+            } else {
+                acc = unpack<DT>(slot[c * W + w]);
+                hop<DT, OP>(acc, unpack<DT>(raw[p]), g.s);
+            }
+            if (p == NR - 1) {
+                post<DT, OP>(acc, NR);
+                st_stream(t.dst[r], vpos, pack<DT>(acc));
+            } else {
+                slot[c * W + w] = pack<DT>(acc);
+            }
+        }
+        __syncthreads();
+    }
+}
+
+template <int NR>
+__global__ __launch_bounds__(RingShape<NR>::T) void ring_all_gather_fast(const RankTable t, const Geometry g) {
+    constexpr int W = RingShape<NR>::W;
+    __shared__ u32x4 slot[NR * W];
+    const int r = threadIdx.x / W, w = threadIdx.x % W;
+    const long long pos = (long long)blockIdx.x * W + w;
+    const bool ok = pos < g.Rv;
+    if (ok) {
+        const u32x4 x = ld_stream(t.src[r], pos);
+        slot[r * W + w] = x;
+        st_stream(t.dst[r], (long long)r * g.Rv + pos, x);                 // keep my own piece
+    }
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < NR - 1; ++p) {
+        const int c = wrap_c<NR>(r - 1 - p);                              // received from rank r-1
+        if (ok) st_stream(t.dst[r], (long long)c * g.Rv + pos, slot[c * W + w]);
+    }
+}
+
+// Windows of the fast kernels (one workgroup each).
+long long ring_fast_windows(const Geometry &g, bool allreduce) {
+    const long long W = g.n == 16 ? 32 : 64;
+    const long long len = allreduce ? (g.V + g.n - 1) / g.n : g.Rv;
+    return (len + W - 1) / W;
+}
+
+bool ring_fast_ranks(int n) { return n == 2 || n == 4 || n == 8 || n == 16; }
+
+template <typename F> hipError_t ring_by_ranks(int n, F &&f) {
+    switch (n) {
+    case 2: return f(std::integral_constant<int, 2>{});
+    case 4: return f(std::integral_constant<int, 4>{});
+    case 8: return f(std::integral_constant<int, 8>{});
+    default: return f(std::integral_constant<int, 16>{});
+    }
+}
+
 static size_t ring_lds_bytes(const Geometry &g, bool bounds) {
     return (size_t)g.n * g.W * 16 + (bounds ? ((size_t)g.n + 1) * sizeof(long long) : 0);
 }
 
-hipError_t launch_ring_allreduce(int dt, int op, const RankTable &t, const Geometry &g, int grid, hipStream_t s) {
+hipError_t launch_ring_allreduce(int dt, int op, const RankTable &t, const Geometry &g, int grid, int lds,
+                                 hipStream_t s) {
+    if (ring_fast_ranks(g.n)) {
+        const dim3 blocks((unsigned)ring_fast_windows(g, true));
+        return dispatch(dt, op, [&](auto D, auto O) {
+            return ring_by_ranks(g.n, [&](auto R) {
+                return launch(ring_allreduce_fast<decltype(D)::value, decltype(O)::value, decltype(R)::value>,
+                              blocks, dim3(RingShape<decltype(R)::value>::T), (size_t)lds, s, t, g);
+            });
+        });
+    }
     return dispatch(dt, op, [&](auto D, auto O) {
-        return launch(ring_allreduce_kernel<decltype(D)::value, decltype(O)::value>, dim3(grid), dim3(kThreads), ring_lds_bytes(g, true), s, t, g);
+        return launch(ring_allreduce_kernel<decltype(D)::value, decltype(O)::value>, dim3(grid), dim3(kThreads),
+                      ring_lds_bytes(g, true), s, t, g);
     });
 }
 
-hipError_t launch_ring_reduce_scatter(int dt, int op, const RankTable &t, const Geometry &g, int grid,
+hipError_t launch_ring_reduce_scatter(int dt, int op, const RankTable &t, const Geometry &g, int grid, int lds,
                                       hipStream_t s) {
+    if (ring_fast_ranks(g.n)) {
+        const dim3 blocks((unsigned)ring_fast_windows(g, false));
+        return dispatch(dt, op, [&](auto D, auto O) {
+            return ring_by_ranks(g.n, [&](auto R) {
+                return launch(ring_reduce_scatter_fast<decltype(D)::value, decltype(O)::value, decltype(R)::value>,
+                              blocks, dim3(RingShape<decltype(R)::value>::T), (size_t)lds, s, t, g);
+            });
+        });
+    }
     return dispatch(dt, op, [&](auto D, auto O) {
-        return launch(ring_reduce_scatter_kernel<decltype(D)::value, decltype(O)::value>, dim3(grid), dim3(kThreads), ring_lds_bytes(g, false), s, t, g);
+        return launch(ring_reduce_scatter_kernel<decltype(D)::value, decltype(O)::value>, dim3(grid),
+                      dim3(kThreads), ring_lds_bytes(g, false), s, t, g);
     });
 }
 
-hipError_t launch_ring_all_gather(const RankTable &t, const Geometry &g, int grid, hipStream_t s) {
+hipError_t launch_ring_all_gather(const RankTable &t, const Geometry &g, int grid, int lds, hipStream_t s) {
+    if (ring_fast_ranks(g.n)) {
+        const dim3 blocks((unsigned)ring_fast_windows(g, false));
+        return ring_by_ranks(g.n, [&](auto R) {
+            return launch(ring_all_gather_fast<decltype(R)::value>, blocks, dim3(RingShape<decltype(R)::value>::T),
+                          (size_t)lds, s, t, g);
+        });
+    }
     return launch(ring_all_gather_kernel, dim3(grid), dim3(kThreads), ring_lds_bytes(g, false), s, t, g);
 }
 
