@@ -28,6 +28,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -50,6 +52,10 @@ def parse():
     p.add_argument("--no-detail", action="store_true")
     p.add_argument("--copy-probe", action="store_true",
                    help="time only a plain device copy of 2 GB (for HBM counter calibration) and exit")
+    p.add_argument("--sweep", action="store_true",
+                   help="instead of the JSON line, print a markdown report over every workload: the n=4 latency "
+                        "case, the FSDP-shard reduce-scatter/all-gather, the n=16 int32 size sweep with the "
+                        "planner's choice against the measured winner, and the 72-rank bucketed all-reduce")
     return p.parse_args()
 
 
@@ -106,6 +112,105 @@ def copy_probe(args):
                       "gbps": round(2 * src.numel() * 4 / (launch_ms * 1e-3) / 1e9, 1)}), flush=True)
 
 
+def _median_us(fn, iters=10, warmup=2):
+    import statistics
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return statistics.median(a.elapsed_time(b) * 1e3 for a, b in ev)
+
+
+def sweep():
+    """Markdown report over every workload (GPU times: median of per-call HIP event pairs)."""
+    import torch
+    import reduce_scatter_amd as ar
+    import workloads as wl
+    out = ["# Workload sweep (MI355X)", "", "GPU time per call = median over 10 calls of an event pair around each call; "
+           "HBM GB/s = algorithmic bytes / time; % of the 8 TB/s peak.", ""]
+
+    # n = 4, fp32, 1024 elements: the latency regime
+    xs = [torch.from_numpy(x).cuda() for x in wl.c1_inputs()]
+    ys = [torch.empty_like(x) for x in xs]
+    out += ["## n = 4, fp32, 1024 elements per rank (latency regime)", "", "| schedule | us |", "|---|---|"]
+    for sched in ("fused", "ring", "tree", "auto"):
+        out.append("| %s | %.2f |" % (sched, _median_us(lambda: ar.ar_allreduce(xs, ys, 1024, "f32", "sum", sched=sched))))
+    out.append("")
+
+    # FSDP shards: reduce-scatter (avg) of 8 x 128 Mi bf16, all-gather of 8 x 16 Mi bf16
+    n, R = 8, 16 << 20
+    xs = [wl.device_normal(2, 0, r, n * R, 1e-2, "bf16") for r in range(n)]
+    ys = [torch.empty(R, dtype=torch.bfloat16, device="cuda") for _ in range(n)]
+    out += ["## FSDP shards, n = 8, bf16: reduce-scatter (avg) 256 MB in per rank; all-gather 32 MB in per rank", "",
+            "| call | schedule | us | HBM GB/s | % peak |", "|---|---|---|---|---|"]
+    alg = (n + 1) * n * R * 2
+    for sched in ("fused", "ring"):
+        us = _median_us(lambda: ar.ar_reduce_scatter(xs, ys, R, "bf16", "avg", sched=sched))
+        out.append("| reduce-scatter | %s | %.1f | %.0f | %.1f |" % (sched, us, alg / us / 1e3, alg / us / 1e3 / PEAK_HBM_GBPS * 100))
+    del xs
+    pieces = [wl.device_uniform(2, 1, r, R, -1.0, 1.0, "bf16") for r in range(n)]
+    full = [torch.empty(n * R, dtype=torch.bfloat16, device="cuda") for _ in range(n)]
+    for sched in ("fused", "ring"):
+        us = _median_us(lambda: ar.ar_all_gather(pieces, full, R, "bf16", sched=sched))
+        out.append("| all-gather | %s | %.1f | %.0f | %.1f |" % (sched, us, alg / us / 1e3, alg / us / 1e3 / PEAK_HBM_GBPS * 100))
+    del pieces, full, ys
+    torch.cuda.empty_cache()
+    out.append("")
+
+    # n = 16 int32 size sweep: every schedule, the planner's choice and the measured winner
+    n = wl.C4_N
+    out += ["## n = 16, int32, 1 KB .. 1 GB per rank: schedules, planner choice, measured winner", "",
+            "Regime: n*S <= 256 MB fits the MI355X's 256 MB Infinity Cache (latency/cache regime); larger is HBM.", "",
+            "| bytes/rank | op | ring us | tree us | fused us | planner | winner | toll % | fused HBM GB/s | regime |",
+            "|---|---|---|---|---|---|---|---|---|---|"]
+    agree = cells = 0
+    for size in wl.C4_SIZES:
+        count = size // 4
+        xs = [wl.device_ints(3, int(np.log2(size)), r, count, -(1 << 20), 1 << 20, "i32") for r in range(n)]
+        ys = [torch.empty_like(x) for x in xs]
+        for op in ("sum", "min", "max", "avg"):
+            t = {s: _median_us(lambda: ar.ar_allreduce(xs, ys, count, "i32", op, sched=s)) for s in ("ring", "tree", "fused")}
+            plan = ar.ar_plan("allreduce", count, "i32", op, n).chosen
+            win = min(t, key=t.get)
+            toll = 100.0 * (t[plan] / t[win] - 1.0)
+            cells += 1
+            agree += plan == win
+            out.append("| %d | %s | %.1f | %.1f | %.1f | %s | %s | %.1f | %.0f | %s |" % (
+                size, op, t["ring"], t["tree"], t["fused"], plan, win, toll, 2 * n * size / t["fused"] / 1e3,
+                "cache" if n * size <= (256 << 20) else "HBM"))
+        del xs, ys
+        torch.cuda.empty_cache()
+    out += ["", "Planner agreed with the measured winner in %d of %d cells." % (agree, cells), ""]
+
+    # 72 ranks, gradient buckets, avg, in place, back to back on one stream
+    n = wl.C5_N
+    buckets, total = wl.c5_buckets()
+    grads = [wl.device_spiky_normal(4, r, total // 4, 1e-3, 0.01, 100.0) for r in range(n)]
+    views = [[g[off // 4:(off + nb) // 4] for g in grads] for off, nb in buckets]
+
+    def all_buckets():
+        for v in views:
+            ar.ar_allreduce(v, v, v[0].numel(), "f32", "avg")
+    us = _median_us(all_buckets, iters=5, warmup=1)
+    per = [_median_us(lambda v=v: ar.ar_allreduce(v, v, v[0].numel(), "f32", "avg"), iters=5, warmup=1) for v in views]
+    alg = 2 * n * total
+    out += ["## 72 ranks, fp32 avg, %d gradient buckets (%.1f MB per rank), in place, back to back" % (len(buckets), total / 2**20), "",
+            "| quantity | value |", "|---|---|",
+            "| total per sweep (us) | %.1f |" % us,
+            "| effective HBM GB/s (2*72*bytes / t) | %.0f (%.1f %% of peak) |" % (alg / us / 1e3, alg / us / 1e3 / PEAK_HBM_GBPS * 100),
+            "| per bucket us: min / median / max | %.1f / %.1f / %.1f |" % (min(per), sorted(per)[len(per) // 2], max(per)),
+            "| planner choice for a 25 MB bucket | %s |" % ar.ar_plan("allreduce", (25 << 20) // 4, "f32", "avg", n).chosen, ""]
+    del grads, views
+    torch.cuda.empty_cache()
+    print("\n".join(out), flush=True)
+
+
 def cpu_baseline():
     """The oracle, as it stands, on a bounded sample of the workload: the same
     ring all-reduce over n = 8 ranks of 16 Mi fp32 elements (a quarter of a
@@ -142,6 +247,9 @@ def main():
     torch.cuda.set_device(0)
     if args.copy_probe:
         copy_probe(args)
+        return 0
+    if args.sweep:
+        sweep()
         return 0
 
     import reduce_scatter_amd as ar

@@ -1,0 +1,188 @@
+"""Measure the cost model's constants on the GPU and write ``calib_gfx950.txt``.
+
+    python -m reduce_scatter_amd.calibrate [--out PATH] [--quick]
+
+The planner prices every legal schedule s of a call as
+
+    t_s = launch_us[s] + step_us[s] * steps_s(n) + bytes_s / (bandwidth_s * corr_s[size bin])
+
+("NCCL all-reduce" post, rakshithvasudev.github.io, section "How NCCL picks: a
+cost model, not a threshold": latency plus bytes over bandwidth, argmin per
+call, constants measured once; the tree's per-size correction table in the same
+section is the model for ``corr``).  This script times every (collective,
+schedule) over several rank counts and message sizes, fits launch_us, step_us
+and bandwidth by least squares on relative error, then sets each size bin's
+correction so the model matches the measured bandwidth-bound times.  Buffers
+are torch device tensors (plumbing only); every timed call goes through the C
+ABI, timed with HIP events on the launch stream.
+"""
+from __future__ import annotations
+
+import argparse
+import math
+import os
+import sys
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+DEFAULT_OUT = os.path.join(HERE, "calib_gfx950.txt")
+COLLS = ("allreduce", "reduce_scatter", "all_gather")
+SIZE_BINS = 48
+
+
+def _steps(coll, sched, n):
+    if sched == "fused":
+        return 1
+    if sched == "ring":
+        return 2 * (n - 1) if coll == "allreduce" else n - 1
+    depth = math.ceil(math.log2(n)) if n > 1 else 0              # depth of the bit-trick tree
+    return 2 * depth
+
+
+def _bytes(coll, n, per_rank):
+    """Algorithmic HBM bytes; per_rank = bytes of one rank's all-reduce buffer,
+    reduce-scatter input or all-gather output."""
+    return 2 * n * per_rank if coll == "allreduce" else (n + 1) * per_rank
+
+
+def time_call(fn, iters, warmup=2):
+    """Median GPU time (us) of one call, from an event pair around each call."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return float(np.median([a.elapsed_time(b) * 1e3 for a, b in ev]))
+
+
+def measure(ns, sizes, iters):
+    import torch
+    import reduce_scatter_amd as ar
+    rows = []                                   # (coll, sched, n, per_rank_bytes, us)
+    for n in ns:
+        for per_rank in sizes:
+            count = per_rank // 4               # fp32
+            if count < n * 4 or n * per_rank > (8 << 30):
+                continue
+            xs = [torch.randn(count, device="cuda") for _ in range(n)]
+            ys = [torch.empty_like(x) for x in xs]
+            R = count // n
+            outs = [torch.empty(R, device="cuda") for _ in range(n)]
+            for sched in ("ring", "tree", "fused"):
+                us = time_call(lambda: ar.ar_allreduce(xs, ys, count, "f32", "sum", n=n, sched=sched), iters)
+                rows.append(("allreduce", sched, n, per_rank, us))
+                if sched == "tree":
+                    continue
+                us = time_call(lambda: ar.ar_reduce_scatter(xs, outs, R, "f32", "sum", n=n, sched=sched), iters)
+                rows.append(("reduce_scatter", sched, n, per_rank, us))
+                us = time_call(lambda: ar.ar_all_gather(outs, ys, R, "f32", n=n, sched=sched), iters)
+                rows.append(("all_gather", sched, n, per_rank, us))
+            print("calibrate: n=%d %d bytes per rank done" % (n, per_rank), flush=True)
+            del xs, ys, outs
+            torch.cuda.empty_cache()
+    return rows
+
+
+def fit(rows):
+    """Per (coll, sched): launch_us, step_us, bw_gbps, corr[SIZE_BINS].
+
+    Fitted by regime: launch and per-step costs from the calls that move at
+    most 1 MB (pure latency: t = launch + step * steps), the sustained
+    bandwidth from the calls that move at least 1 GB, then one correction per
+    power-of-two footprint so the model meets the measured time wherever the
+    bandwidth term is at least a quarter of it.  The footprint (total
+    algorithmic bytes) is the size axis because it decides whether the data
+    stays in the 256 MB Infinity Cache."""
+    out = {}
+    for coll in COLLS:
+        for sched in ("ring", "tree", "fused"):
+            pts = [(n, pr, us, _bytes(coll, n, pr)) for c, s, n, pr, us in rows if c == coll and s == sched]
+            if not pts:
+                continue
+            small_all = [(n, us) for n, pr, us, b in pts if b <= (1 << 20)]
+            small = [(n, us) for n, us in small_all if n <= 16]    # the compile-time-n kernels
+            if sched == "fused" or len({n for n, _ in small}) < 2:
+                launch = float(np.median([us for _, us in small])) if small else 0.0
+                step = 0.0
+            else:
+                A = np.array([[1.0, _steps(coll, sched, n)] for n, _ in small])
+                t = np.array([us for _, us in small])
+                (launch, step), *_ = np.linalg.lstsq(A, t, rcond=None)
+                launch, step = max(float(launch), 0.0), max(float(step), 0.0)
+            extra = {}                                    # rank class -> latency beyond launch + step * steps
+            for rc in sorted({math.ceil(math.log2(n)) for n, _ in small_all}):
+                res = [us - launch - step * _steps(coll, sched, n) for n, us in small_all
+                       if math.ceil(math.log2(n)) == rc]
+                if abs(float(np.median(res))) > 1.0:
+                    extra[rc] = float(np.median(res))
+            big = [(n, us, b) for n, pr, us, b in pts if b >= (1 << 30)]
+            ref = big or [(n, us, b) for n, pr, us, b in pts]
+            bws = [b / 1e3 / max(us - launch - step * _steps(coll, sched, n), 1e-3) for n, us, b in ref]
+            bw = float(np.median(bws))
+            corr = {}                                     # rank class -> [SIZE_BINS]
+            per_bin = {}
+            for n, pr, us, b in pts:
+                term = us - launch - step * _steps(coll, sched, n) - extra.get(math.ceil(math.log2(n)), 0.0)
+                if term < 0.25 * us:                      # latency-bound: no bandwidth information
+                    continue
+                key = (math.ceil(math.log2(n)), int(math.log2(b)))
+                per_bin.setdefault(key, []).append(b / 1e3 / term / bw)
+            for rc in sorted({k for k, _ in per_bin}):
+                row = [1.0] * SIZE_BINS
+                bins = {b: v for (k, b), v in per_bin.items() if k == rc}
+                for b, v in bins.items():
+                    row[b] = float(np.exp(np.mean(np.log(v))))
+                top = max(bins)                           # beyond the largest measured footprint: keep its factor
+                for b in range(top + 1, SIZE_BINS):
+                    row[b] = row[top]
+                corr[rc] = [min(4.0, max(0.05, c)) for c in row]
+            out[(coll, sched)] = (launch, step, bw, corr, extra)
+    return out
+
+
+def write(path, model, gpu_name):
+    with open(path, "w") as f:
+        f.write("# cost-model constants for libar (written by reduce_scatter_amd/calibrate.py)\n")
+        f.write("# device: %s\n" % gpu_name)
+        f.write("# <coll> <sched> <launch_us> <step_us> <bw_GBps>\n")
+        f.write("# corr <coll> <sched> <ceil(log2 n)> <bandwidth factor for log2(total algorithmic bytes) = 0..47>\n")
+        f.write("# lat <coll> <sched> <ceil(log2 n)> <latency beyond launch + step * steps, us>\n")
+        for (coll, sched), (launch, step, bw, corr, extra) in sorted(model.items()):
+            f.write("%s %s %.3f %.4f %.1f\n" % (coll, sched, launch, step, bw))
+            for rc, row in sorted(corr.items()):
+                f.write("corr %s %s %d %s\n" % (coll, sched, rc, " ".join("%.3f" % c for c in row)))
+            for rc, us in sorted(extra.items()):
+                f.write("lat %s %s %d %.3f\n" % (coll, sched, rc, us))
+
+
+def main(argv=None):
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--out", default=DEFAULT_OUT)
+    p.add_argument("--quick", action="store_true", help="fewer sizes and rank counts")
+    a = p.parse_args(argv)
+    import torch
+    if not torch.cuda.is_available():
+        print("calibrate: no GPU visible", file=sys.stderr)
+        return 2
+    torch.cuda.set_device(0)
+    ns = (2, 8) if a.quick else (2, 4, 8, 16, 72)
+    sizes = [1 << k for k in ((12, 16, 20, 24, 28) if a.quick else (10, 12, 14, 16, 18, 20, 21, 22, 23, 24, 25, 26, 27, 28))]
+    rows = measure(ns, sizes, iters=5 if a.quick else 10)
+    model = fit(rows)
+    write(a.out, model, torch.cuda.get_device_name(0) + " " + getattr(torch.cuda.get_device_properties(0),
+                                                                      "gcnArchName", ""))
+    for (coll, sched), (launch, step, bw, corr, extra) in sorted(model.items()):
+        print("%-15s %-6s launch %7.2f us  step %6.3f us  bw %7.1f GB/s  extra %s" % (
+            coll, sched, launch, step, bw, {k: round(v, 1) for k, v in extra.items()}))
+    print("calibrate: wrote", a.out)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

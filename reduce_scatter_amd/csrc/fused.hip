@@ -47,7 +47,7 @@ __device__ __forceinline__ int hop_rank(int c, int k, int n) {
 // plus a 32-bit vector offset.  Every lane passes a valid offset (lanes past
 // the end of the chunk re-read its last vector and discard the result), so no
 // load sits in a divergent branch and a whole batch of loads is in flight at
-// once.  NR > 0: n == NR known at compile time; NR == 0: any n, 8 loads per
+// once.  NR > 0: n == NR known at compile time; NR == 0: any n, 16 loads per
 // batch.
 template <int DT, int OP, int NR>
 __device__ __forceinline__ Pack<DT> chain(const RankTable &t, int n, int c, long long base, unsigned lane_off,
@@ -65,7 +65,7 @@ __device__ __forceinline__ Pack<DT> chain(const RankTable &t, int n, int c, long
 #pragma unroll
         for (int k = 1; k < NR; ++k) hop<DT, OP>(acc, unpack<DT>(raw[k]), s);
     } else {
-        constexpr int B = 8;
+        constexpr int B = 16;
         for (int k0 = 0; k0 < n; k0 += B) {
             u32x4 raw[B];
 #pragma unroll

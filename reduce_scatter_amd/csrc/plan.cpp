@@ -19,7 +19,7 @@
 //   bandwidth_s(bytes): a measured sustained rate times a measured per-size
 //           correction (the role of the tree correction table in the same
 //           section: the clean model does not fit medium sizes, so a
-//           per-size factor is applied).
+//           per-size factor is applied), indexed by the call's total bytes.
 //
 // Legality: the tree schedule exists for all-reduce only.
 //
@@ -44,11 +44,15 @@ namespace {
 
 constexpr int kColls = 3;
 constexpr int kScheds = 4;         // indexed by ar_sched_t; 0 (auto) unused
-constexpr int kSizeBins = 32;      // per-size correction for log2(bytes per rank) = 0..31
+constexpr int kSizeBins = 48;      // per-size correction for log2(algorithmic bytes of the call) = 0..47
+
+constexpr int kRankClasses = 8;    // ceil(log2 n) = 0..7 for n = 1..128
 
 struct Entry {
     double launch_us = 0, step_us = 0, bw_gbps = 0;
-    double corr[kSizeBins];
+    double corr[kRankClasses][kSizeBins];
+    bool measured[kRankClasses];       // a corr row was read for this rank class
+    double extra_us[kRankClasses];     // measured latency beyond launch + step * steps, per rank class
     bool set = false;
 };
 
@@ -70,7 +74,11 @@ void set_defaults(Calib &c) {
             e.launch_us = 8.0;
             e.step_us = (s == AR_SCHED_FUSED) ? 0.0 : 0.25;
             e.bw_gbps = (s == AR_SCHED_FUSED) ? 5000.0 : 4000.0;
-            for (int b = 0; b < kSizeBins; ++b) e.corr[b] = 1.0;
+            for (int k2 = 0; k2 < kRankClasses; ++k2) {
+                e.measured[k2] = false;
+                e.extra_us[k2] = 0.0;
+                for (int b = 0; b < kSizeBins; ++b) e.corr[k2][b] = 1.0;
+            }
             e.set = true;
         }
 }
@@ -100,20 +108,48 @@ std::string library_dir() {
 }
 
 // File format, one record per line ('#' starts a comment):
-//   <coll> <sched> <launch_us> <step_us> <bw_gbps> [corr_0 ... corr_31]
+//   <coll> <sched> <launch_us> <step_us> <bw_gbps>
+//   corr <coll> <sched> <rank class> <corr_0 ... corr_47>
+//   lat <coll> <sched> <rank class> <extra_us>
 // coll in {allreduce, reduce_scatter, all_gather}, sched in {ring, tree, fused};
-// corr_b multiplies the bandwidth for calls of 2^b .. 2^(b+1)-1 bytes per rank.
+// rank class = ceil(log2 n); corr_b multiplies the bandwidth for calls that
+// move 2^b .. 2^(b+1)-1 algorithmic bytes in total (the footprint decides
+// whether the data stays in the 256 MB Infinity Cache, and how that bends the
+// bandwidth depends on n).  A rank class without a row uses the nearest one
+// that has one.  extra_us is added to the latency of calls in that rank class
+// (kernels for different rank counts do not share one per-step cost).
 void load_file(Calib &c, const std::string &path) {
     FILE *f = fopen(path.c_str(), "r");
     if (!f) return;
-    char line[1024];
+    char line[2048];
     int loaded = 0;
     while (fgets(line, sizeof line, f)) {
         char *hash = strchr(line, '#');
         if (hash) *hash = 0;
         char coll[32], sched[32];
-        int used = 0;
+        int used = 0, rc = -1;
         double lu, su, bw;
+        double extra = 0;
+        if (sscanf(line, "lat %31s %31s %d %lf", coll, sched, &rc, &extra) == 4) {
+            int k = coll_index(coll), s = sched_index(sched);
+            if (k >= 0 && s >= 0 && rc >= 0 && rc < kRankClasses) c.e[k][s].extra_us[rc] = extra;
+            continue;
+        }
+        if (sscanf(line, "corr %31s %31s %d%n", coll, sched, &rc, &used) == 3) {
+            int k = coll_index(coll), s = sched_index(sched);
+            if (k < 0 || s < 0 || rc < 0 || rc >= kRankClasses) continue;
+            Entry &e = c.e[k][s];
+            const char *p = line + used;
+            for (int b = 0; b < kSizeBins; ++b) {
+                double v;
+                int m = 0;
+                if (sscanf(p, "%lf%n", &v, &m) != 1) break;
+                if (v > 0) e.corr[rc][b] = v;
+                p += m;
+            }
+            e.measured[rc] = true;
+            continue;
+        }
         if (sscanf(line, "%31s %31s %lf %lf %lf%n", coll, sched, &lu, &su, &bw, &used) != 5) continue;
         int k = coll_index(coll), s = sched_index(sched);
         if (k < 0 || s < 0 || !(bw > 0) || lu < 0 || su < 0) continue;
@@ -121,14 +157,6 @@ void load_file(Calib &c, const std::string &path) {
         e.launch_us = lu;
         e.step_us = su;
         e.bw_gbps = bw;
-        const char *p = line + used;
-        for (int b = 0; b < kSizeBins; ++b) {
-            double v;
-            int m = 0;
-            if (sscanf(p, "%lf%n", &v, &m) != 1) break;
-            if (v > 0) e.corr[b] = v;
-            p += m;
-        }
         ++loaded;
     }
     fclose(f);
@@ -141,9 +169,24 @@ void init_calib() {
     load_file(g_calib, env && *env ? std::string(env) : library_dir() + "/calib_gfx950.txt");
 }
 
-int size_bin(double bytes_per_rank) {
-    if (bytes_per_rank < 1) return 0;
-    int b = (int)std::floor(std::log2(bytes_per_rank));
+int rank_class(int n) {
+    int k = 0;
+    while ((1 << k) < n) ++k;
+    return k < kRankClasses ? k : kRankClasses - 1;
+}
+
+// The measured correction row nearest to rank class k (all ones if none).
+const double *corr_row(const Entry &e, int k) {
+    for (int d = 0; d < kRankClasses; ++d) {
+        if (k - d >= 0 && e.measured[k - d]) return e.corr[k - d];
+        if (k + d < kRankClasses && e.measured[k + d]) return e.corr[k + d];
+    }
+    return e.corr[k];                              // nothing measured: the all-ones defaults
+}
+
+int size_bin(double bytes) {
+    if (bytes < 1) return 0;
+    int b = (int)std::floor(std::log2(bytes));
     return b < 0 ? 0 : (b >= kSizeBins ? kSizeBins - 1 : b);
 }
 
@@ -211,13 +254,15 @@ ar_status_t make_plan(ar_coll_t coll, size_t count, ar_dtype_t dtype, ar_op_t op
     double best = 0;
     out->chosen = AR_SCHED_FUSED;
     bool have = false;
-    const int bin = size_bin(per_rank);
+    (void)per_rank;
+    const int bin = size_bin(bytes);
+    const int rclass = rank_class(n);
     for (int s = AR_SCHED_RING; s <= AR_SCHED_FUSED; ++s) {
         if (!(out->legal_mask & (1u << s))) continue;
         const Entry &c = g_calib.e[coll][s];
         out->bytes[s] = bytes;
-        const double bw = c.bw_gbps * c.corr[bin];                 // GB/s = 1e3 bytes per microsecond
-        out->predicted_us[s] = c.launch_us + c.step_us * out->steps[s] + bytes / (bw * 1e3);
+        const double bw = c.bw_gbps * corr_row(c, rclass)[bin];    // GB/s = 1e3 bytes per microsecond
+        out->predicted_us[s] = c.launch_us + c.step_us * out->steps[s] + c.extra_us[rclass] + bytes / (bw * 1e3);
         if (!have || out->predicted_us[s] < best) {
             best = out->predicted_us[s];
             out->chosen = (ar_sched_t)s;

@@ -112,14 +112,43 @@ def test_plan_steps_bytes_and_legality():
             assert all(b == (n + 1) * n * count * 2 for b in q.bytes.values())
 
 
-def test_plan_is_monotone_in_size():
-    prev = None
-    for k in range(0, 31, 2):
-        p = ar.ar_plan("allreduce", 1 << k, "i32", "sum", 16)
-        t = p.predicted_us[p.chosen]
-        if prev is not None:
-            assert t >= prev
-        prev = t
+def _plan_in_subprocess(calib, calls):
+    """Run ar_plan in a fresh process (the calibration file is read once per process)."""
+    import subprocess
+    import sys
+    code = "import json, sys; sys.path.insert(0, %r); import reduce_scatter_amd as ar; " \
+           "print(json.dumps([ar.ar_plan(*c).__dict__ for c in %r]))" % (ROOT, calls)
+    env = dict(os.environ, AR_CALIB=calib)
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env, timeout=120)
+    assert r.returncode == 0, r.stderr
+    return json.loads(r.stdout.strip().splitlines()[-1])
+
+
+def test_plan_is_monotone_in_size_with_default_constants():
+    calls = [("allreduce", 1 << k, "i32", "sum", 16) for k in range(0, 31, 2)]
+    plans = _plan_in_subprocess("/nonexistent/calib.txt", calls)
+    times = [p["predicted_us"][p["chosen"]] for p in plans]
+    assert times == sorted(times)
+
+
+def test_plan_reads_the_calibration_file(tmp_path):
+    """Constants and the (rank class x footprint) correction come from the file:
+    t = launch + step * steps + bytes / (bw * corr)."""
+    f = tmp_path / "calib.txt"
+    corr = ["1.0"] * 48
+    corr[27] = "0.5"                     # 2^27 .. 2^28 - 1 bytes in total
+    f.write_text("allreduce ring 10 0.5 1000\nallreduce tree 20 1 1000\nallreduce fused 5 0 500\n"
+                 "corr allreduce fused 3 " + " ".join(corr) + "\n")
+    count = (1 << 27) // (2 * 8 * 4)     # n = 8 fp32: 2*n*S = 2^27 bytes
+    p = _plan_in_subprocess(str(f), [("allreduce", count, "f32", "sum", 8)])[0]
+    b = 2 * 8 * count * 4
+    assert abs(p["predicted_us"]["ring"] - (10 + 0.5 * 14 + b / 1e3 / 1000)) < 1e-6
+    assert abs(p["predicted_us"]["tree"] - (20 + 1 * 6 + b / 1e3 / 1000)) < 1e-6
+    assert abs(p["predicted_us"]["fused"] - (5 + b / 1e3 / (500 * 0.5))) < 1e-6
+    assert p["chosen"] == min(p["predicted_us"], key=p["predicted_us"].get)
+    # a rank class with no row of its own uses the nearest measured one (class 3 for n = 16)
+    p16 = _plan_in_subprocess(str(f), [("allreduce", count // 2, "f32", "sum", 16)])[0]
+    assert abs(p16["predicted_us"]["fused"] - (5 + b / 1e3 / (500 * 0.5))) < 1e-6
 
 
 def test_plan_rejects_bad_arguments():
