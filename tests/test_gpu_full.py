@@ -53,6 +53,7 @@ def test_c2_fused_and_ring_full_size(c2_inputs, op):
     count = xs[0].numel()
     print("c2 oracle", op, flush=True)
     want = oracle.ring_allreduce(host, "f32", op)[0]
+    assert ar.ar_plan("allreduce", count, "f32", op, 8).chosen in ("fused", "ring")    # ring hop order
     for sched in ("auto", "fused", "ring"):
         print("c2", op, sched, flush=True)
         ys = [torch.empty_like(x) for x in xs]
