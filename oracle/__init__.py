@@ -14,7 +14,9 @@ functions follow:
   :func:`ring_allreduce`, :func:`ring_reduce_scatter`, :func:`ring_all_gather`;
   section "The double binary tree": :func:`tree_parent`, :func:`tree_allreduce`;
   the plain element-wise definition (exact for int32 and min/max):
-  :func:`direct_reduce`.
+  :func:`direct_reduce`; section "When the switch does the math" (every rank
+  combined at once, in an order the post leaves open; read as the aligned
+  pairwise tree over rank indices): :func:`pairwise_reduce`.
 * "FSDP collectives 101" (rakshithvasudev.github.io), sections "All-gather:
   everyone shows their piece" and "Why backward needs a different collective":
   the semantics of reduce-scatter (rank r keeps slice r) and all-gather.
@@ -84,6 +86,9 @@ def _load():
         lib.orc_direct_reduce.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_size_t, vpp,
                                           ctypes.c_void_p]
         lib.orc_direct_reduce.restype = ctypes.c_int
+        lib.orc_pairwise_reduce.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_size_t, vpp,
+                                            ctypes.c_void_p]
+        lib.orc_pairwise_reduce.restype = ctypes.c_int
         lib.orc_tree_parent.argtypes = [ctypes.c_int, ctypes.c_int]
         lib.orc_tree_parent.restype = ctypes.c_int
         lib.orc_allreduce_chunks.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_size_t,
@@ -199,6 +204,19 @@ def direct_reduce(xs, dtype: str, op: str):
     _check_inputs(xs, dtype, count)
     y = np.empty(count, NP_DTYPE[dtype])
     _call(_load().orc_direct_reduce(DTYPE_CODE[dtype], OP_CODE[op], n, count, _ptrs(xs), y.ctypes.data))
+    return y
+
+
+def pairwise_reduce(xs, dtype: str, op: str):
+    """All ranks combined at once in the aligned pairwise order over rank
+    indices ([lo, lo+len) = [lo, lo+h) (+) [lo+h, lo+len), h the largest power
+    of two below len), each combine rounded to the storage type; then the avg
+    rule.  One output array (every rank receives it); works on any slice."""
+    n = len(xs)
+    count = xs[0].size
+    _check_inputs(xs, dtype, count)
+    y = np.empty(count, NP_DTYPE[dtype])
+    _call(_load().orc_pairwise_reduce(DTYPE_CODE[dtype], OP_CODE[op], n, count, _ptrs(xs), y.ctypes.data))
     return y
 
 

@@ -40,7 +40,10 @@
  *  - the tree: parent(v) = (v ^ b) | (b << 1) with b the lowest set bit of v,
  *    falling back to v ^ b when that is >= n; own value first, then the
  *    children's partials in ascending rank order; the root applies the
- *    integer-avg postOp and every rank receives the root's value.
+ *    integer-avg postOp and every rank receives the root's value;
+ *  - the fused pass that combines all ranks at once uses the aligned binary
+ *    tree over rank indices (split at the largest power of two below the
+ *    range length), lower ranks on the left.
  *
  * Build: gcc -O2 -std=c11 -fopenmp -ffp-contract=off -fno-fast-math -shared -fPIC
  */
@@ -546,6 +549,42 @@ int orc_direct_reduce(int dtype, int op, int n, size_t count, const void *const 
         for (int r = 1; r < n; ++r) acc = combine(dtype, op, acc, load_elem(dtype, x[r], (size_t)i));
         store_elem(dtype, y, (size_t)i, post_op(dtype, op, n, acc));
     }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* The fused pass with all ranks combined at once: the model is the switch   */
+/* that sums in transit ("NCCL all-reduce", section "When the switch does     */
+/* the math": one load returns the value combined over every rank, one store  */
+/* lands it on every rank), whose order of additions the post leaves open.    */
+/* Reading: a fixed pairwise order, the aligned binary tree over the rank    */
+/* indices.  Ranks [lo, lo+len) combine as [lo, lo+h) (+) [lo+h, lo+len),    */
+/* h the largest power of two below len; the lower ranks are the left        */
+/* operand (so min / max ties keep them).  A rank's contribution enters as a */
+/* storage-type value (float avg pre-scales it by s = fp32(1/n) first), every */
+/* combine is computed in fp32 (int32: wrapping) and rounded to the storage   */
+/* type, and integer avg divides the finished total by n once.  Reads element */
+/* i of every rank at offset i, so it applies to any slice of the buffers;    */
+/* writes one output array (every rank receives the same values).            */
+/* ------------------------------------------------------------------------ */
+static val_t pairwise_partial(int dtype, int op, int lo, int len, const void *const *x, size_t i, float s)
+{
+    if (len == 1) return round_to_type(dtype, pre_op(dtype, op, load_elem(dtype, x[lo], i), s));
+    int h = 1;
+    while (2 * h < len) h *= 2;                            /* largest power of two below len */
+    val_t left = pairwise_partial(dtype, op, lo, h, x, i, s);
+    val_t right = pairwise_partial(dtype, op, lo + h, len - h, x, i, s);
+    return round_to_type(dtype, combine(dtype, op, left, right));
+}
+
+int orc_pairwise_reduce(int dtype, int op, int n, size_t count, const void *const *x, void *y)
+{
+    if (bad_args(dtype, op, n)) return ORC_EBADARG;
+    const float s = (float)(1.0 / (double)n);
+    long long i;
+#pragma omp parallel for schedule(static)
+    for (i = 0; i < (long long)count; ++i)
+        store_elem(dtype, y, (size_t)i, post_op(dtype, op, n, pairwise_partial(dtype, op, 0, n, x, (size_t)i, s)));
     return ORC_OK;
 }
 

@@ -173,10 +173,11 @@ def test_brute_force_allreduce(dtype, op):
             xs = _data(dtype, op, n, count, 7)
             ring = oracle.ring_allreduce(xs, dtype, op)
             tree = oracle.tree_allreduce(xs, dtype, op)
+            pair = [oracle.pairwise_reduce(xs, dtype, op)] * n
             fx = [as_float(x, dtype) if dtype != "i32" else x.astype(np.int64) for x in xs]
             want = [_brute_elem([f[i] for f in fx], dtype, op, n) for i in range(count)]
             for r in range(n):
-                for ys in (ring, tree):
+                for ys in (ring, tree, pair):
                     got = as_float(ys[r], dtype) if dtype != "i32" else ys[r].astype(np.int64)
                     assert [Fraction(float(v)) if dtype != "i32" else int(v) for v in got] == want, \
                         (dtype, op, n, count, r)
@@ -258,6 +259,28 @@ def test_recursive_summation_bound(dtype, op):
                 # bf16/fp16: the final fp32 -> storage rounding of an exact value
                 assert abs(Fraction(got[i]) - exact) <= Fraction(bound) + Fraction(abs(float(exact)) * u), \
                     (dtype, op, n, i)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("op", ["sum", "avg"])
+def test_pairwise_summation_bound(dtype, op):
+    """Pairwise summation over a tree of depth d = ceil(log2 n):
+    |computed - exact| <= gamma_d * sum|x_i|; the avg pre-scale adds fp32(1/n),
+    the multiply and the leaf's rounding to the storage type."""
+    u = UNIT_ROUNDOFF[dtype]
+    for n in (2, 3, 5, 7, 8, 9, 16, 72):
+        count = 48
+        xs = [workloads.normal(5, n, r, count, 1.0, dtype) for r in range(n)]
+        fx = [as_float(x, dtype) for x in xs]
+        got = as_float(oracle.pairwise_reduce(xs, dtype, op), dtype)
+        d = math.ceil(math.log2(n))
+        k = d if op == "sum" else d + 3
+        for i in range(count):
+            terms = [Fraction(f[i]) for f in fx]
+            exact = sum(terms) / (n if op == "avg" else 1)
+            bound = gamma(k, u) * float(sum(abs(t) for t in terms) / (n if op == "avg" else 1))
+            assert abs(Fraction(got[i]) - exact) <= Fraction(bound) + Fraction(abs(float(exact)) * u), \
+                (dtype, op, n, i)
 
 
 def test_prod_relative_bound():
@@ -521,6 +544,116 @@ def test_tree_and_ring_agree_when_exact_and_within_bound_otherwise():
     ring = oracle.ring_allreduce(xs, "f32", "sum")[0].astype(np.float64)
     tree = oracle.tree_allreduce(xs, "f32", "sum")[0].astype(np.float64)
     assert np.max(np.abs(ring - tree)) <= 1e-6 * np.max(np.abs(ring))
+
+
+# ---------------------------------------------------------------------------
+# 6b. the all-ranks-at-once fused pass: the aligned pairwise order
+# ---------------------------------------------------------------------------
+#
+# In the aligned binary tree over rank indices, leaves i and j first meet at
+# the level given by the highest bit in which i and j differ, i.e.
+# (i ^ j).bit_length(); of three leaves, exactly one pair meets strictly
+# first.  With contributions {+B, -B, +1} and zeros elsewhere (B as in
+# section 4), adding zero is exact, so the result is (B + 1) - B = 0 when +B
+# and the 1 meet first, and 1 when either other pair meets first.  This
+# closed form is independent of the oracle's recursion.
+
+def _meet(i, j):
+    return (i ^ j).bit_length()
+
+
+def _pairwise_rule(pb, pn, p1):
+    return 0.0 if _meet(pb, p1) < min(_meet(pb, pn), _meet(p1, pn)) else 1.0
+
+
+def _pairwise_cases(dtype, n, trials, seed):
+    B = BIG[dtype]
+    rg = np.random.default_rng(seed)
+    xs = [np.zeros(trials) for _ in range(n)]
+    expect = np.zeros(trials)
+    placements = []
+    for i in range(trials):
+        pb, pn, p1 = (int(v) for v in rg.choice(n, size=3, replace=False))
+        xs[pb][i], xs[pn][i], xs[p1][i] = B, -B, 1.0
+        expect[i] = _pairwise_rule(pb, pn, p1)
+        placements.append((pb, pn, p1))
+    return xs, expect, placements
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+def test_pairwise_rounding_cases(dtype):
+    for n in (3, 4, 5, 6, 7, 8, 13, 16, 72, 128):
+        xs, expect, _ = _pairwise_cases(dtype, n, 64, n)
+        got = oracle.pairwise_reduce([to_dtype(x, dtype) for x in xs], dtype, "sum")
+        assert as_float(got, dtype).tolist() == expect.tolist(), (dtype, n)
+        assert 0.0 in expect and 1.0 in expect
+
+
+def _eval_tree(split, vals):
+    """fp32 evaluation of a combine tree given by ``split(lo, len) -> h``."""
+    def rec(lo, ln):
+        if ln == 1:
+            return np.float32(vals[lo])
+        h = split(lo, ln)
+        return np.float32(rec(lo, h) + rec(lo + h, ln - h))
+    return float(rec(0, len(vals)))
+
+
+def test_pairwise_cases_have_power():
+    """The nearest misreadings (split a range in halves rather than at a power
+    of two; rank order 0..n-1; the ring's order for chunk 0) predict other
+    results on these cases, so the test above would catch each of them."""
+    halves = lambda lo, ln: ln // 2
+    chain = lambda lo, ln: ln - 1                  # ((x0 + x1) + x2) + ...
+    for n in (6, 7, 13, 72):
+        xs, expect, placements = _pairwise_cases("f32", n, 64, n)
+        vals = [[x[i] for x in xs] for i in range(len(expect))]
+        for alt in (halves, chain):
+            assert any(_eval_tree(alt, v) != e for v, e in zip(vals, expect)), n
+        ring_pred = [_eval_tree(chain, v[1:] + v[:1]) for v in vals]   # chunk 0: ranks 1, ..., n-1, 0
+        assert any(a != b for a, b in zip(ring_pred, expect)), n
+
+
+def test_pairwise_worked_cases():
+    """Hand-evaluated cases: n = 3 combines (x0 + x1) + x2; n = 6 combines
+    (x0..x3) with (x4, x5); n = 72 combines ranks 0..63 with 64..71."""
+    t = 2.0 ** -24
+    cases = [
+        ([1.0, t, t], 1.0),                        # (1 + t) -> 1, 1 + t -> 1;  1 + (t + t) would be 1 + 2t
+        ([1.0, 0.0, t, t], 1.0 + 2 * t),           # (1 + 0) + (t + t)
+        ([1.0, 0.0, 0.0, t, t, 0.0], 1.0),         # ((1+0)+(0+t)) + (t+0): halves would give 1 + 2t
+    ]
+    x72 = [0.0] * 72
+    x72[0], x72[63], x72[64] = 1.0, t, t           # ranks 0..63 -> 1 + t -> 1; then + t -> 1
+    cases.append((x72, 1.0))
+    for vals, want in cases:
+        xs = [np.array([v], np.float32) for v in vals]
+        assert float(oracle.pairwise_reduce(xs, "f32", "sum")[0]) == want, vals
+
+
+def test_pairwise_min_max_ties_keep_lower_ranks():
+    a, b = np.zeros(4, np.float32), np.full(4, -0.0, np.float32)
+    assert not np.signbit(oracle.pairwise_reduce([a, b], "f32", "min")).any()
+    assert np.signbit(oracle.pairwise_reduce([b, a], "f32", "min")).all()
+    assert np.signbit(oracle.pairwise_reduce([b, a], "f32", "max")).all()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+def test_pairwise_two_ranks_is_the_ring(dtype):
+    """n = 2: one operation per element, which the ring also computes (and the
+    ring's n = 2 result is pinned to the library's own operation above)."""
+    xs = [workloads.normal(10, 0, r, 4096, 1.0, dtype) for r in range(2)]
+    for op in ("sum", "prod", "avg"):
+        want = oracle.ring_allreduce(xs, dtype, op)[0]
+        assert oracle.pairwise_reduce(xs, dtype, op).tobytes() == want.tobytes(), (dtype, op)
+
+
+def test_pairwise_power_of_two_avg_is_scaled_sum():
+    for n in (4, 8, 16, 64):
+        xs = [workloads.normal(8, n, r, 256, 1e-3, "f32") for r in range(n)]
+        s = oracle.pairwise_reduce(xs, "f32", "sum")
+        a = oracle.pairwise_reduce(xs, "f32", "avg")
+        assert a.tobytes() == (s * np.float32(1.0 / n)).tobytes()
 
 
 # ---------------------------------------------------------------------------
