@@ -59,6 +59,11 @@ def parse():
     return p.parse_args()
 
 
+# The kernel each schedule launches at this shape (n = 8, 16-byte aligned buffers).
+KERNEL_OF = {"fused": "fused_allreduce_kernel", "ring": "ring_allreduce_fast", "tree": "tree_allreduce_fast",
+             "split": "split_allreduce_kernel"}
+
+
 def kernel_source_hash() -> str:
     with open(KERNEL_SRC, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -138,28 +143,31 @@ def sweep():
     # n = 4, fp32, 1024 elements: the latency regime
     xs = [torch.from_numpy(x).cuda() for x in wl.c1_inputs()]
     ys = [torch.empty_like(x) for x in xs]
+    xs, ys = ar.pointers(xs), ar.pointers(ys)          # host pointer tables built once, outside the timing
     out += ["## n = 4, fp32, 1024 elements per rank (latency regime)", "", "| schedule | us |", "|---|---|"]
-    for sched in ("fused", "ring", "tree", "auto"):
+    for sched in ("fused", "ring", "tree", "split", "auto"):
         out.append("| %s | %.2f |" % (sched, _median_us(lambda: ar.ar_allreduce(xs, ys, 1024, "f32", "sum", sched=sched))))
     out.append("")
 
     # FSDP shards: reduce-scatter (avg) of 8 x 128 Mi bf16, all-gather of 8 x 16 Mi bf16
     n, R = 8, 16 << 20
-    xs = [wl.device_normal(2, 0, r, n * R, 1e-2, "bf16") for r in range(n)]
-    ys = [torch.empty(R, dtype=torch.bfloat16, device="cuda") for _ in range(n)]
+    xs_t = [wl.device_normal(2, 0, r, n * R, 1e-2, "bf16") for r in range(n)]
+    ys_t = [torch.empty(R, dtype=torch.bfloat16, device="cuda") for _ in range(n)]
+    xs, ys = ar.pointers(xs_t), ar.pointers(ys_t)
     out += ["## FSDP shards, n = 8, bf16: reduce-scatter (avg) 256 MB in per rank; all-gather 32 MB in per rank", "",
             "| call | schedule | us | HBM GB/s | % peak |", "|---|---|---|---|---|"]
     alg = (n + 1) * n * R * 2
     for sched in ("fused", "ring"):
         us = _median_us(lambda: ar.ar_reduce_scatter(xs, ys, R, "bf16", "avg", sched=sched))
         out.append("| reduce-scatter | %s | %.1f | %.0f | %.1f |" % (sched, us, alg / us / 1e3, alg / us / 1e3 / PEAK_HBM_GBPS * 100))
-    del xs
-    pieces = [wl.device_uniform(2, 1, r, R, -1.0, 1.0, "bf16") for r in range(n)]
-    full = [torch.empty(n * R, dtype=torch.bfloat16, device="cuda") for _ in range(n)]
+    del xs, xs_t
+    pieces_t = [wl.device_uniform(2, 1, r, R, -1.0, 1.0, "bf16") for r in range(n)]
+    full_t = [torch.empty(n * R, dtype=torch.bfloat16, device="cuda") for _ in range(n)]
+    pieces, full = ar.pointers(pieces_t), ar.pointers(full_t)
     for sched in ("fused", "ring"):
         us = _median_us(lambda: ar.ar_all_gather(pieces, full, R, "bf16", sched=sched))
         out.append("| all-gather | %s | %.1f | %.0f | %.1f |" % (sched, us, alg / us / 1e3, alg / us / 1e3 / PEAK_HBM_GBPS * 100))
-    del pieces, full, ys
+    del pieces, full, ys, pieces_t, full_t, ys_t
     torch.cuda.empty_cache()
     out.append("")
 
@@ -167,24 +175,26 @@ def sweep():
     n = wl.C4_N
     out += ["## n = 16, int32, 1 KB .. 1 GB per rank: schedules, planner choice, measured winner", "",
             "Regime: n*S <= 256 MB fits the MI355X's 256 MB Infinity Cache (latency/cache regime); larger is HBM.", "",
-            "| bytes/rank | op | ring us | tree us | fused us | planner | winner | toll % | fused HBM GB/s | regime |",
-            "|---|---|---|---|---|---|---|---|---|---|"]
+            "| bytes/rank | op | ring us | tree us | fused us | split us | planner | winner | toll % | best HBM GB/s | regime |",
+            "|---|---|---|---|---|---|---|---|---|---|---|"]
     agree = cells = 0
     for size in wl.C4_SIZES:
         count = size // 4
-        xs = [wl.device_ints(3, int(np.log2(size)), r, count, -(1 << 20), 1 << 20, "i32") for r in range(n)]
-        ys = [torch.empty_like(x) for x in xs]
+        xs_t = [wl.device_ints(3, int(np.log2(size)), r, count, -(1 << 20), 1 << 20, "i32") for r in range(n)]
+        ys_t = [torch.empty_like(x) for x in xs_t]
+        xs, ys = ar.pointers(xs_t), ar.pointers(ys_t)
         for op in ("sum", "min", "max", "avg"):
-            t = {s: _median_us(lambda: ar.ar_allreduce(xs, ys, count, "i32", op, sched=s)) for s in ("ring", "tree", "fused")}
+            t = {s: _median_us(lambda: ar.ar_allreduce(xs, ys, count, "i32", op, n=n, sched=s))
+                 for s in ("ring", "tree", "fused", "split")}
             plan = ar.ar_plan("allreduce", count, "i32", op, n).chosen
             win = min(t, key=t.get)
             toll = 100.0 * (t[plan] / t[win] - 1.0)
             cells += 1
             agree += plan == win
-            out.append("| %d | %s | %.1f | %.1f | %.1f | %s | %s | %.1f | %.0f | %s |" % (
-                size, op, t["ring"], t["tree"], t["fused"], plan, win, toll, 2 * n * size / t["fused"] / 1e3,
+            out.append("| %d | %s | %.1f | %.1f | %.1f | %.1f | %s | %s | %.1f | %.0f | %s |" % (
+                size, op, t["ring"], t["tree"], t["fused"], t["split"], plan, win, toll, 2 * n * size / t[win] / 1e3,
                 "cache" if n * size <= (256 << 20) else "HBM"))
-        del xs, ys
+        del xs, ys, xs_t, ys_t
         torch.cuda.empty_cache()
     out += ["", "Planner agreed with the measured winner in %d of %d cells." % (agree, cells), ""]
 
@@ -192,20 +202,22 @@ def sweep():
     n = wl.C5_N
     buckets, total = wl.c5_buckets()
     grads = [wl.device_spiky_normal(4, r, total // 4, 1e-3, 0.01, 100.0) for r in range(n)]
-    views = [[g[off // 4:(off + nb) // 4] for g in grads] for off, nb in buckets]
+    views = [(ar.pointers([g[off // 4:(off + nb) // 4] for g in grads]), nb // 4) for off, nb in buckets]
 
-    def all_buckets():
-        for v in views:
-            ar.ar_allreduce(v, v, v[0].numel(), "f32", "avg")
-    us = _median_us(all_buckets, iters=5, warmup=1)
-    per = [_median_us(lambda v=v: ar.ar_allreduce(v, v, v[0].numel(), "f32", "avg"), iters=5, warmup=1) for v in views]
+    def all_buckets(sched):
+        for v, c in views:
+            ar.ar_allreduce(v, v, c, "f32", "avg", n=n, sched=sched)
     alg = 2 * n * total
     out += ["## 72 ranks, fp32 avg, %d gradient buckets (%.1f MB per rank), in place, back to back" % (len(buckets), total / 2**20), "",
-            "| quantity | value |", "|---|---|",
-            "| total per sweep (us) | %.1f |" % us,
-            "| effective HBM GB/s (2*72*bytes / t) | %.0f (%.1f %% of peak) |" % (alg / us / 1e3, alg / us / 1e3 / PEAK_HBM_GBPS * 100),
-            "| per bucket us: min / median / max | %.1f / %.1f / %.1f |" % (min(per), sorted(per)[len(per) // 2], max(per)),
-            "| planner choice for a 25 MB bucket | %s |" % ar.ar_plan("allreduce", (25 << 20) // 4, "f32", "avg", n).chosen, ""]
+            "| schedule | total per sweep (us) | effective HBM GB/s (2*72*bytes / t) | % of peak | per bucket us: min / median / max |",
+            "|---|---|---|---|---|"]
+    for sched in ("auto", "split", "fused"):
+        us = _median_us(lambda: all_buckets(sched), iters=5, warmup=1)
+        per = sorted(_median_us(lambda v=v, c=c: ar.ar_allreduce(v, v, c, "f32", "avg", n=n, sched=sched), iters=5, warmup=1)
+                     for v, c in views)
+        out.append("| %s | %.1f | %.0f | %.1f | %.1f / %.1f / %.1f |" % (
+            sched, us, alg / us / 1e3, alg / us / 1e3 / PEAK_HBM_GBPS * 100, per[0], per[len(per) // 2], per[-1]))
+    out += ["", "Planner choice for a 25 MB bucket: %s." % ar.ar_plan("allreduce", (25 << 20) // 4, "f32", "avg", n).chosen, ""]
     del grads, views
     torch.cuda.empty_cache()
     print("\n".join(out), flush=True)
@@ -256,8 +268,9 @@ def main():
     import workloads
 
     stream = torch.cuda.current_stream()
-    xs = [workloads.device_normal(1, 0, r, COUNT, 1e-3, "f32") for r in range(N_RANKS)]
-    ys = [torch.empty_like(x) for x in xs]
+    xs_t = [workloads.device_normal(1, 0, r, COUNT, 1e-3, "f32") for r in range(N_RANKS)]
+    ys_t = [torch.empty_like(x) for x in xs_t]
+    xs, ys = ar.pointers(xs_t), ar.pointers(ys_t)       # the rank pointer tables, built once
     torch.cuda.synchronize()
     S = COUNT * 4
     alg_bytes = 2 * N_RANKS * S
@@ -273,7 +286,7 @@ def main():
 
     detail = {}
     if not args.no_detail:
-        for sched in ("fused", "ring", "tree"):
+        for sched in ("fused", "ring", "tree", "split"):
             for op in ("sum", "avg"):
                 ms, lms, _ = time_calls(
                     lambda: ar.ar_allreduce(xs, ys, COUNT, "f32", op, sched=sched, stream=stream), 10, 2, stream)
@@ -303,9 +316,10 @@ def main():
         "hbm_GBps": round(achieved, 1),
         "pct_peak_hbm": round(100.0 * achieved / PEAK_HBM_GBPS, 2),
         "busbw_GBps": round(algbw * 2 * (N_RANKS - 1) / N_RANKS, 2),
-        "roofline": {"bound": "hbm", "kernel": "fused_allreduce_kernel<f32,%s>" % args.op,
+        "roofline": {"bound": "hbm", "kernel": "%s<f32,%s>" % (KERNEL_OF[chosen], args.op),
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": measured_traffic(),
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                     "traffic": measured_traffic() if chosen == "fused" else None,
                      "algorithmic_bytes_per_launch": alg_bytes, "avg_launch_ms": round(launch_ms, 4),
                      "median_launch_ms": round(launch_med_ms, 4)},
         "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(),

@@ -33,6 +33,14 @@
  * their floating-point results are identical bit for bit.  The tree schedule
  * reduces up the bit-trick binary tree rooted at rank 0 (own value first,
  * then the children in ascending rank order) and broadcasts back down.
+ * The split schedule (all-reduce only) is the fused single pass with every
+ * rank combined at once, in the aligned pairwise order over rank indices:
+ * ranks [lo, lo+len) combine as [lo, lo+h) (+) [lo+h, lo+len), h the largest
+ * power of two below len, the lower ranks being the left operand; every
+ * contribution enters as a storage-type value (float avg pre-scaled), every
+ * combine is rounded to the storage type, int32 avg divides the total once.
+ * Its floating-point sums therefore differ from the ring's in the last bits
+ * (integer results, min and max are the same under every schedule).
  * All-reduce chunks are cut in 16-byte units:
  *   u = 16 / element size, V = ceil(count / u),
  *   chunk c = [u*floor(c*V/n), u*floor((c+1)*V/n)) clamped to count.
@@ -64,7 +72,7 @@
  * environment, which logs one line per planned call to stderr) and no
  * exception crosses the ABI.  count == 0 returns AR_OK without a launch.
  *
- * Environment: AR_SCHEDULE=auto|ring|tree|fused forces a schedule for calls
+ * Environment: AR_SCHEDULE=auto|ring|tree|fused|split forces a schedule for calls
  * made with AR_SCHED_AUTO; AR_CALIB=<path> names the cost-model calibration
  * file (default: calib_gfx950.txt beside the library); AR_GRID=<n> overrides
  * the number of workgroups per launch.
@@ -84,14 +92,14 @@ extern "C" {
 typedef enum {
     AR_OK = 0,
     AR_ERR_INVALID_ARG = 1,   /* null pointer, n out of range, bad enum, overlapping buffers */
-    AR_ERR_UNSUPPORTED = 2,   /* schedule not legal for this collective (tree for RS/AG) */
+    AR_ERR_UNSUPPORTED = 2,   /* schedule not legal for this collective (tree, split for RS/AG) */
     AR_ERR_ALIGNMENT = 3,     /* a pointer not aligned to the element size */
     AR_ERR_HIP = 4            /* the HIP runtime reported an error (launch, device query) */
 } ar_status_t;
 
 typedef enum { AR_FLOAT32 = 0, AR_BFLOAT16 = 1, AR_FLOAT16 = 2, AR_INT32 = 3 } ar_dtype_t;
 typedef enum { AR_SUM = 0, AR_PROD = 1, AR_MIN = 2, AR_MAX = 3, AR_AVG = 4 } ar_op_t;
-typedef enum { AR_SCHED_AUTO = 0, AR_SCHED_RING = 1, AR_SCHED_TREE = 2, AR_SCHED_FUSED = 3 } ar_sched_t;
+typedef enum { AR_SCHED_AUTO = 0, AR_SCHED_RING = 1, AR_SCHED_TREE = 2, AR_SCHED_FUSED = 3, AR_SCHED_SPLIT = 4 } ar_sched_t;
 typedef enum { AR_COLL_ALLREDUCE = 0, AR_COLL_REDUCE_SCATTER = 1, AR_COLL_ALL_GATHER = 2 } ar_coll_t;
 
 /* Result of the cost model, indexed by ar_sched_t (entry 0, AUTO, is unused).
@@ -101,9 +109,9 @@ typedef enum { AR_COLL_ALLREDUCE = 0, AR_COLL_REDUCE_SCATTER = 1, AR_COLL_ALL_GA
 typedef struct {
     ar_sched_t chosen;
     unsigned legal_mask;        /* bit s set when schedule s is legal for the call */
-    int steps[4];               /* dependent steps: ring 2(n-1) (n-1 for RS/AG), tree 2*depth, fused 1 */
-    double bytes[4];            /* algorithmic HBM bytes the schedule moves */
-    double predicted_us[4];     /* cost-model time; 0 for illegal schedules */
+    int steps[5];               /* dependent steps: ring 2(n-1) (n-1 for RS/AG), tree 2*depth, fused 1, split 1 */
+    double bytes[5];            /* algorithmic HBM bytes the schedule moves */
+    double predicted_us[5];     /* cost-model time; 0 for illegal schedules */
 } ar_plan_t;
 
 /* All-reduce ``count`` elements per rank.
@@ -112,21 +120,24 @@ typedef struct {
  * Source: "NCCL all-reduce", sections "What all-reduce promises" and "The
  * ring, exactly as the kernel runs it" (ring), "The double binary tree"
  * (tree), "When the switch does the math" (one read and one write per byte:
- * the model for the fused single pass). */
+ * the model for the fused single pass; every rank combined at once in an
+ * order the switch leaves open: the split schedule). */
 ar_status_t ar_allreduce(const void *const *sendbufs, void *const *recvbufs, size_t count,
                          ar_dtype_t dtype, ar_op_t op, int n, ar_sched_t sched, hipStream_t stream);
 
 /* Reduce-scatter: sendbufs[r] holds n*recvcount elements, recvbufs[r]
  * receives recvcount elements (slice r of the combined result).
  * Source: "FSDP collectives 101", section "Why backward needs a different
- * collective"; the ring's reduce-scatter half. Schedules: ring, fused. */
+ * collective"; the ring's reduce-scatter half. Schedules: ring, fused
+ * (tree and split: AR_ERR_UNSUPPORTED). */
 ar_status_t ar_reduce_scatter(const void *const *sendbufs, void *const *recvbufs, size_t recvcount,
                               ar_dtype_t dtype, ar_op_t op, int n, ar_sched_t sched, hipStream_t stream);
 
 /* All-gather: sendbufs[r] holds sendcount elements, recvbufs[r] receives
  * n*sendcount elements (x_0 || x_1 || ... || x_{n-1}).
  * Source: "FSDP collectives 101", section "All-gather: everyone shows their
- * piece"; the ring's all-gather half. Schedules: ring, fused. */
+ * piece"; the ring's all-gather half. Schedules: ring, fused
+ * (tree and split: AR_ERR_UNSUPPORTED). */
 ar_status_t ar_all_gather(const void *const *sendbufs, void *const *recvbufs, size_t sendcount,
                           ar_dtype_t dtype, int n, ar_sched_t sched, hipStream_t stream);
 

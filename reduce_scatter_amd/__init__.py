@@ -18,6 +18,7 @@ from ._binding import (  # noqa: F401
     SCHEDS,
     ArError,
     Plan,
+    PointerTable,
     ar_all_gather,
     ar_allreduce,
     ar_plan,
@@ -25,6 +26,7 @@ from ._binding import (  # noqa: F401
     ar_status_string,
     ar_tree_parent,
     library_path,
+    pointers,
 )
 
 __all__ = [
@@ -42,4 +44,6 @@ __all__ = [
     "COLLS",
     "AR_MAX_RANKS",
     "library_path",
+    "pointers",
+    "PointerTable",
 ]

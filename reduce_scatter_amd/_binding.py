@@ -17,7 +17,7 @@ _LIB_PATH = os.path.join(_HERE, "libar.so")
 AR_MAX_RANKS = 128
 DTYPES = {"f32": 0, "bf16": 1, "f16": 2, "i32": 3}
 OPS = {"sum": 0, "prod": 1, "min": 2, "max": 3, "avg": 4}
-SCHEDS = {"auto": 0, "ring": 1, "tree": 2, "fused": 3}
+SCHEDS = {"auto": 0, "ring": 1, "tree": 2, "fused": 3, "split": 4}
 COLLS = {"allreduce": 0, "reduce_scatter": 1, "all_gather": 2}
 _SCHED_NAMES = {v: k for k, v in SCHEDS.items()}
 _STATUS = {0: "AR_OK", 1: "AR_ERR_INVALID_ARG", 2: "AR_ERR_UNSUPPORTED", 3: "AR_ERR_ALIGNMENT", 4: "AR_ERR_HIP"}
@@ -40,8 +40,8 @@ _lib = ctypes.CDLL(_LIB_PATH)
 
 
 class _PlanStruct(ctypes.Structure):
-    _fields_ = [("chosen", ctypes.c_int), ("legal_mask", ctypes.c_uint), ("steps", ctypes.c_int * 4),
-                ("bytes", ctypes.c_double * 4), ("predicted_us", ctypes.c_double * 4)]
+    _fields_ = [("chosen", ctypes.c_int), ("legal_mask", ctypes.c_uint), ("steps", ctypes.c_int * 5),
+                ("bytes", ctypes.c_double * 5), ("predicted_us", ctypes.c_double * 5)]
 
 
 _vpp = ctypes.POINTER(ctypes.c_void_p)
@@ -111,11 +111,35 @@ def _ptr(b):
     return int(b.data_ptr())
 
 
+class PointerTable:
+    """A host array of device pointers built once and reusable across calls
+    (a list of tensors costs a ``data_ptr()`` call per buffer on every call;
+    at 128 ranks that host time is comparable to a small collective).  The
+    table keeps references to the tensors it was built from."""
+
+    def __init__(self, bufs):
+        self.n = len(bufs)
+        self.array = (ctypes.c_void_p * max(1, self.n))(*[_ptr(b) for b in bufs])
+        self._bufs = list(bufs)          # tensors stay alive (and their memory owned) while the table exists
+
+    def __len__(self):
+        return self.n
+
+
+def pointers(bufs) -> PointerTable:
+    """Build a reusable pointer table for ``bufs`` (tensors or integer addresses)."""
+    return PointerTable(bufs)
+
+
 def _ptr_array(bufs):
-    arr = (ctypes.c_void_p * max(1, len(bufs)))()
-    for i, b in enumerate(bufs):
-        arr[i] = _ptr(b)
-    return arr
+    if isinstance(bufs, PointerTable):
+        return bufs.array
+    return (ctypes.c_void_p * max(1, len(bufs)))(*[_ptr(b) for b in bufs])
+
+
+def _tables(sendbufs, recvbufs):
+    send = _ptr_array(sendbufs)
+    return send, (send if recvbufs is sendbufs else _ptr_array(recvbufs))
 
 
 def _stream(stream):
@@ -140,21 +164,24 @@ def _check(status):
 def ar_allreduce(sendbufs, recvbufs, count, dtype, op, n=None, sched="auto", stream=None):
     """All-reduce ``count`` elements of each of the n rank buffers (in place when recvbufs is sendbufs)."""
     n = len(sendbufs) if n is None else n
-    _check(_lib.ar_allreduce(_ptr_array(sendbufs), _ptr_array(recvbufs), count, _dtype_code(dtype),
+    send, recv = _tables(sendbufs, recvbufs)
+    _check(_lib.ar_allreduce(send, recv, count, _dtype_code(dtype),
                              _code(OPS, op, "op"), n, _code(SCHEDS, sched, "schedule"), _stream(stream)))
 
 
 def ar_reduce_scatter(sendbufs, recvbufs, recvcount, dtype, op, n=None, sched="auto", stream=None):
     """Reduce-scatter: each send buffer holds n*recvcount elements; rank r receives slice r."""
     n = len(sendbufs) if n is None else n
-    _check(_lib.ar_reduce_scatter(_ptr_array(sendbufs), _ptr_array(recvbufs), recvcount, _dtype_code(dtype),
+    send, recv = _tables(sendbufs, recvbufs)
+    _check(_lib.ar_reduce_scatter(send, recv, recvcount, _dtype_code(dtype),
                                   _code(OPS, op, "op"), n, _code(SCHEDS, sched, "schedule"), _stream(stream)))
 
 
 def ar_all_gather(sendbufs, recvbufs, sendcount, dtype, n=None, sched="auto", stream=None):
     """All-gather: each rank receives the n pieces of sendcount elements, in rank order."""
     n = len(sendbufs) if n is None else n
-    _check(_lib.ar_all_gather(_ptr_array(sendbufs), _ptr_array(recvbufs), sendcount, _dtype_code(dtype), n,
+    send, recv = _tables(sendbufs, recvbufs)
+    _check(_lib.ar_all_gather(send, recv, sendcount, _dtype_code(dtype), n,
                               _code(SCHEDS, sched, "schedule"), _stream(stream)))
 
 

@@ -32,7 +32,7 @@ SIZE_BINS = 48
 
 
 def _steps(coll, sched, n):
-    if sched == "fused":
+    if sched in ("fused", "split"):
         return 1
     if sched == "ring":
         return 2 * (n - 1) if coll == "allreduce" else n - 1
@@ -70,21 +70,23 @@ def measure(ns, sizes, iters):
             count = per_rank // 4               # fp32
             if count < n * 4 or n * per_rank > (8 << 30):
                 continue
-            xs = [torch.randn(count, device="cuda") for _ in range(n)]
-            ys = [torch.empty_like(x) for x in xs]
+            xs_t = [torch.randn(count, device="cuda") for _ in range(n)]
+            ys_t = [torch.empty_like(x) for x in xs_t]
             R = count // n
-            outs = [torch.empty(R, device="cuda") for _ in range(n)]
-            for sched in ("ring", "tree", "fused"):
+            outs_t = [torch.empty(R, device="cuda") for _ in range(n)]
+            # host pointer tables built once: the timings are the library's, not Python's marshalling
+            xs, ys, outs = ar.pointers(xs_t), ar.pointers(ys_t), ar.pointers(outs_t)
+            for sched in ("ring", "tree", "fused", "split"):
                 us = time_call(lambda: ar.ar_allreduce(xs, ys, count, "f32", "sum", n=n, sched=sched), iters)
                 rows.append(("allreduce", sched, n, per_rank, us))
-                if sched == "tree":
+                if sched in ("tree", "split"):
                     continue
                 us = time_call(lambda: ar.ar_reduce_scatter(xs, outs, R, "f32", "sum", n=n, sched=sched), iters)
                 rows.append(("reduce_scatter", sched, n, per_rank, us))
                 us = time_call(lambda: ar.ar_all_gather(outs, ys, R, "f32", n=n, sched=sched), iters)
                 rows.append(("all_gather", sched, n, per_rank, us))
             print("calibrate: n=%d %d bytes per rank done" % (n, per_rank), flush=True)
-            del xs, ys, outs
+            del xs, ys, outs, xs_t, ys_t, outs_t
             torch.cuda.empty_cache()
     return rows
 
@@ -101,13 +103,13 @@ def fit(rows):
     stays in the 256 MB Infinity Cache."""
     out = {}
     for coll in COLLS:
-        for sched in ("ring", "tree", "fused"):
+        for sched in ("ring", "tree", "fused", "split"):
             pts = [(n, pr, us, _bytes(coll, n, pr)) for c, s, n, pr, us in rows if c == coll and s == sched]
             if not pts:
                 continue
             small_all = [(n, us) for n, pr, us, b in pts if b <= (1 << 20)]
             small = [(n, us) for n, us in small_all if n <= 16]    # the compile-time-n kernels
-            if sched == "fused" or len({n for n, _ in small}) < 2:
+            if sched in ("fused", "split") or len({n for n, _ in small}) < 2:
                 launch = float(np.median([us for _, us in small])) if small else 0.0
                 step = 0.0
             else:
@@ -171,7 +173,7 @@ def main(argv=None):
         print("calibrate: no GPU visible", file=sys.stderr)
         return 2
     torch.cuda.set_device(0)
-    ns = (2, 8) if a.quick else (2, 4, 8, 16, 72)
+    ns = (2, 8) if a.quick else (2, 4, 8, 16, 32, 72, 128)
     sizes = [1 << k for k in ((12, 16, 20, 24, 28) if a.quick else (10, 12, 14, 16, 18, 20, 21, 22, 23, 24, 25, 26, 27, 28))]
     rows = measure(ns, sizes, iters=5 if a.quick else 10)
     model = fit(rows)

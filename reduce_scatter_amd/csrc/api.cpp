@@ -6,6 +6,7 @@
 // into the kernel arguments.  Calls are ordered on the caller's stream.
 #include <stdint.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstdio>
 #include <cstdlib>
@@ -22,12 +23,12 @@ namespace {
 
 const char *kDtypeName[] = {"fp32", "bf16", "fp16", "int32"};
 const char *kOpName[] = {"sum", "prod", "min", "max", "avg"};
-const char *kSchedName[] = {"AUTO", "RING", "TREE", "FUSED"};
+const char *kSchedName[] = {"AUTO", "RING", "TREE", "FUSED", "SPLIT"};
 const char *kCollName[] = {"AllReduce", "ReduceScatter", "AllGather"};
 
 bool valid_dtype(int d) { return d >= AR_FLOAT32 && d <= AR_INT32; }
 bool valid_op(int o) { return o >= AR_SUM && o <= AR_AVG; }
-bool valid_sched(int s) { return s >= AR_SCHED_AUTO && s <= AR_SCHED_FUSED; }
+bool valid_sched(int s) { return s >= AR_SCHED_AUTO && s <= AR_SCHED_SPLIT; }
 
 bool debug_enabled() {
     static int v = -1;
@@ -44,6 +45,7 @@ ar_sched_t forced_schedule() {
     if (!strcmp(e, "ring")) return AR_SCHED_RING;
     if (!strcmp(e, "tree")) return AR_SCHED_TREE;
     if (!strcmp(e, "fused")) return AR_SCHED_FUSED;
+    if (!strcmp(e, "split")) return AR_SCHED_SPLIT;
     return AR_SCHED_AUTO;
 }
 
@@ -121,10 +123,6 @@ int lds_window(int n) {
     return w < 1 ? 1 : w;
 }
 
-bool overlaps(uintptr_t a, size_t alen, uintptr_t b, size_t blen) {
-    return alen && blen && a < b + blen && b < a + alen;
-}
-
 bool null_entry(const void *const *p, int n) {
     for (int r = 0; r < n; ++r)
         if (!p[r]) return true;
@@ -143,21 +141,41 @@ bool all16(const void *const *a, const void *const *b, int n) {
     return true;
 }
 
-// recv range r may coincide with its own in-place position ``inplace[r]``
-// (a send buffer address, or 0 for none) and must not otherwise overlap any
-// send range or any other recv range.
+// recv range r may coincide with its own in-place position (``inplace[r]``
+// set: the layout the header allows for rank r) and must not otherwise
+// overlap any send range or any other recv range; send ranges may overlap
+// each other.  Every recv range is a writable span and every send range a
+// read-only span, except that for an allowed (send r, recv r) pair only the
+// parts of send r outside recv r are emitted (read-only), so the pair does not
+// conflict with itself.  After sorting by start, a span conflicts iff it
+// starts before the end of an earlier writable span, or is writable and starts
+// before the end of any earlier span.  O(n log n) for up to 3n spans.
+struct Span {
+    uintptr_t lo, hi;
+    bool writable;
+};
+
 ar_status_t check_overlap(const void *const *send, size_t slen, void *const *recv, size_t rlen, int n,
-                          const uintptr_t *inplace_send_for_recv) {
+                          const uintptr_t *inplace) {
+    Span sp[3 * AR_MAX_RANKS];
+    int m = 0;
     for (int r = 0; r < n; ++r) {
-        const uintptr_t y = (uintptr_t)recv[r];
-        for (int k = 0; k < n; ++k) {
-            const uintptr_t x = (uintptr_t)send[k];
-            if (!overlaps(y, rlen, x, slen)) continue;
-            if (k == r && inplace_send_for_recv[r]) continue;   // the allowed in-place layout
-            return AR_ERR_INVALID_ARG;
+        const uintptr_t s0 = (uintptr_t)send[r], s1 = s0 + slen;
+        const uintptr_t d0 = (uintptr_t)recv[r], d1 = d0 + rlen;
+        sp[m++] = {d0, d1, true};
+        if (!inplace[r]) {
+            sp[m++] = {s0, s1, false};
+            continue;
         }
-        for (int k = r + 1; k < n; ++k)
-            if (overlaps(y, rlen, (uintptr_t)recv[k], rlen)) return AR_ERR_INVALID_ARG;
+        if (s0 < d0) sp[m++] = {s0, s1 < d0 ? s1 : d0, false};      // send r below recv r
+        if (s1 > d1) sp[m++] = {s0 > d1 ? s0 : d1, s1, false};      // send r above recv r
+    }
+    std::sort(sp, sp + m, [](const Span &a, const Span &b) { return a.lo < b.lo; });
+    uintptr_t end_all = 0, end_w = 0;
+    for (int i = 0; i < m; ++i) {
+        if (i > 0 && (sp[i].lo < end_w || (sp[i].writable && sp[i].lo < end_all))) return AR_ERR_INVALID_ARG;
+        if (sp[i].hi > end_all) end_all = sp[i].hi;
+        if (sp[i].writable && sp[i].hi > end_w) end_w = sp[i].hi;
     }
     return AR_OK;
 }
@@ -166,10 +184,11 @@ void log_plan(ar_coll_t coll, size_t bytes_per_rank, int n, int dtype, int op, c
               bool forced) {
     if (!debug_enabled()) return;
     fprintf(stderr,
-            "[ar] %s: %zu Bytes x n=%d %s %s -> %s%s (predicted us: ring %.2f tree %.2f fused %.2f; calib %s)\n",
+            "[ar] %s: %zu Bytes x n=%d %s %s -> %s%s (predicted us: ring %.2f tree %.2f fused %.2f split %.2f; "
+            "calib %s)\n",
             kCollName[coll], bytes_per_rank, n, kDtypeName[dtype], kOpName[op], kSchedName[used],
             forced ? " (forced)" : "", p.predicted_us[AR_SCHED_RING], p.predicted_us[AR_SCHED_TREE],
-            p.predicted_us[AR_SCHED_FUSED], calib_source());
+            p.predicted_us[AR_SCHED_FUSED], p.predicted_us[AR_SCHED_SPLIT], calib_source());
 }
 
 // Resolve AR_SCHED_AUTO (and the AR_SCHEDULE override) into a legal schedule.
@@ -268,21 +287,24 @@ ar_status_t ar_allreduce(const void *const *sendbufs, void *const *recvbufs, siz
     g.Vfull = (long long)count / lanes;
     g.q = g.V / n;
     g.rem = (int)(g.V % n);
+    g.ref = (long long)((uintptr_t)recvbufs[0] >> 4);          // fused / split tiles follow rank 0's output
     TreeShape tree;
     if (use == AR_SCHED_TREE) tree_build(n, tree);
 
-    if (!all16(sendbufs, (const void *const *)recvbufs, n)) {
-        // element-wise path over the whole buffer
-        hipError_t h = (use == AR_SCHED_TREE)
-                           ? launch_elem_tree_allreduce(dtype, op, t, tree, g, 0, (long long)count, stream)
-                           : launch_elem_ring_allreduce(dtype, op, t, g, 0, (long long)count, stream);
-        return hip_status(h);
-    }
+    auto elem = [&](long long e_begin) {
+        if (use == AR_SCHED_TREE) return launch_elem_tree_allreduce(dtype, op, t, tree, g, e_begin, (long long)count, stream);
+        if (use == AR_SCHED_SPLIT) return launch_elem_split_allreduce(dtype, op, t, g, e_begin, (long long)count, stream);
+        return launch_elem_ring_allreduce(dtype, op, t, g, e_begin, (long long)count, stream);
+    };
+    if (!all16(sendbufs, (const void *const *)recvbufs, n)) return hip_status(elem(0));   // element-wise path
     hipError_t h = hipSuccess;
     if (g.Vfull > 0) {
-        if (use == AR_SCHED_FUSED) {
+        if (use == AR_SCHED_SPLIT) {
+            if ((g.Vfull + kFusedTile - 1) / kFusedTile > 0x7fffffffLL) return AR_ERR_UNSUPPORTED;   // grid x limit
+            h = launch_split_allreduce(dtype, op, t, g, stream);
+        } else if (use == AR_SCHED_FUSED) {
             const long long maxlen = (g.V + n - 1) / n;                       // longest chunk, in vectors
-            g.windows = (maxlen + kFusedTile - 1) / kFusedTile;
+            g.windows = aligned_tiles(maxlen, kFusedTile);
             if (g.windows > 0x7fffffffLL) return AR_ERR_UNSUPPORTED;   // grid x limit
             h = launch_fused_allreduce(dtype, op, t, g, fused_lds_bytes(AR_COLL_ALLREDUCE), stream);
         } else if (use == AR_SCHED_RING) {
@@ -296,11 +318,7 @@ ar_status_t ar_allreduce(const void *const *sendbufs, void *const *recvbufs, siz
             h = launch_tree_allreduce(dtype, op, t, tree, g, grid_for(g.windows, cus, 4), tree_lds_bytes(), stream);
         }
     }
-    if (h == hipSuccess && g.Vfull * lanes < (long long)count) {             // tail: last count mod lanes elements
-        h = (use == AR_SCHED_TREE)
-                ? launch_elem_tree_allreduce(dtype, op, t, tree, g, g.Vfull * lanes, (long long)count, stream)
-                : launch_elem_ring_allreduce(dtype, op, t, g, g.Vfull * lanes, (long long)count, stream);
-    }
+    if (h == hipSuccess && g.Vfull * lanes < (long long)count) h = elem(g.Vfull * lanes);   // tail: count mod lanes
     return hip_status(h);
 }
 
@@ -334,8 +352,9 @@ ar_status_t ar_reduce_scatter(const void *const *sendbufs, void *const *recvbufs
     const bool vec = all16(sendbufs, (const void *const *)recvbufs, n) && (recvcount * e) % 16 == 0;
     if (!vec) return hip_status(launch_elem_reduce_scatter(dtype, op, t, g, (long long)recvcount, stream));
     g.Rv = (long long)(recvcount * e / 16);
+    g.ref = (long long)((uintptr_t)sendbufs[0] >> 4);          // fused tiles follow the input slices' alignment
     if (use == AR_SCHED_FUSED) {
-        g.windows = (g.Rv + kFusedTile - 1) / kFusedTile;
+        g.windows = aligned_tiles(g.Rv, kFusedTile);
         if (g.windows > 0x7fffffffLL) return AR_ERR_UNSUPPORTED;   // grid x limit
         return hip_status(launch_fused_reduce_scatter(dtype, op, t, g, fused_lds_bytes(AR_COLL_REDUCE_SCATTER), stream));
     }
@@ -374,8 +393,9 @@ ar_status_t ar_all_gather(const void *const *sendbufs, void *const *recvbufs, si
     const bool vec = all16(sendbufs, (const void *const *)recvbufs, n) && (sendcount * e) % 16 == 0;
     if (!vec) return hip_status(launch_elem_all_gather((int)e, t, g, (long long)sendcount, stream));
     g.Rv = (long long)(sendcount * e / 16);
+    g.ref = (long long)((uintptr_t)recvbufs[0] >> 4);          // fused tiles follow the outputs' alignment
     if (use == AR_SCHED_FUSED) {
-        g.windows = (g.Rv + kFusedTile - 1) / kFusedTile;
+        g.windows = aligned_tiles(g.Rv, kFusedTile);
         if (g.windows > 0x7fffffffLL) return AR_ERR_UNSUPPORTED;   // grid x limit
         return hip_status(launch_fused_all_gather(t, g, fused_lds_bytes(AR_COLL_ALL_GATHER), stream));
     }

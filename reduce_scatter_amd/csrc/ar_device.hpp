@@ -193,6 +193,12 @@ __device__ __forceinline__ typename Pack<DT>::T hop1(typename Pack<DT>::T acc, t
     else return round_to<DT>(combine<DT, OP>(acc, pre<DT, OP>(own, s)));
 }
 
+template <int DT, int OP>
+__device__ __forceinline__ typename Pack<DT>::T merge1(typename Pack<DT>::T acc, typename Pack<DT>::T other) {
+    if constexpr (DT == I32) return combine<DT, OP>(acc, other);
+    else return round_to<DT>(combine<DT, OP>(acc, other));
+}
+
 template <int DT, int OP> __device__ __forceinline__ typename Pack<DT>::T post1(typename Pack<DT>::T acc, int n) {
     if constexpr (DT == I32 && OP == AVG) return (uint32_t)((int32_t)acc / n);
     else return acc;

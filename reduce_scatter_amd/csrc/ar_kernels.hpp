@@ -32,7 +32,40 @@ struct Geometry {
     int n;
     int W;              // ring/tree: vectors per rank in one LDS window
     float s;            // fp32(1/n), the float avg pre-scale
+    long long ref;      // fused / split: address / 16 of the buffer whose alignment cuts the tiles
 };
+
+// Tiles are cut on a grid aligned to absolute T-vector boundaries of a
+// reference buffer (vector v of the range sits at address (ref + v) * 16): the
+// first tile of a range may be partial, every later one covers a whole
+// aligned run.  Measured on MI355X: a 16-byte misalignment of the rank buffers
+// costs the one-vector-per-lane kernels about a quarter of their bandwidth
+// when tiles follow the range start instead.
+struct TileSpan {
+    long long start;    // first vector of the aligned tile (may lie before lo)
+    long long lo, hi;   // the tile's vectors inside the range: [lo, hi), empty when lo >= hi
+};
+
+__host__ __device__ inline TileSpan aligned_tile(long long lo, long long hi, long long j, long long ref, long long T) {
+    const long long a = (ref + lo) & (T - 1);                 // T is a power of two
+    TileSpan s;
+    s.start = lo - a + j * T;
+    s.lo = s.start > lo ? s.start : lo;
+    s.hi = s.start + T < hi ? s.start + T : hi;
+    return s;
+}
+
+// Vector v of an aligned tile: its byte offset from the tile's first in-range
+// vector, and whether it is in range (a lane outside re-reads an in-range
+// vector and drops the result, so no load needs a branch).
+__device__ __forceinline__ unsigned tile_lane(const TileSpan &ts, long long v, bool &ok) {
+    ok = v >= ts.lo && v < ts.hi;
+    const long long c = v < ts.lo ? ts.lo : (v >= ts.hi ? ts.hi - 1 : v);
+    return (unsigned)(c - ts.lo) * 16u;
+}
+
+// Tiles needed for a range of len vectors, whatever its alignment.
+inline long long aligned_tiles(long long len, long long T) { return len > 0 ? (len + T - 1) / T + 1 : 0; }
 
 // The tree schedule's shape, host-built: depth, parent and up to two
 // children per rank (-1 = none); post[] lists ranks children-first.
@@ -52,6 +85,9 @@ struct TreeShape {
 hipError_t launch_fused_allreduce(int dt, int op, const RankTable &t, const Geometry &g, int lds, hipStream_t s);
 hipError_t launch_fused_reduce_scatter(int dt, int op, const RankTable &t, const Geometry &g, int lds, hipStream_t s);
 hipError_t launch_fused_all_gather(const RankTable &t, const Geometry &g, int lds, hipStream_t s);
+// Fused pass in the aligned pairwise order over ranks (all-reduce only): one
+// workgroup of ceil(n / K) waves per 64-vector tile of [0, Vfull).
+hipError_t launch_split_allreduce(int dt, int op, const RankTable &t, const Geometry &g, hipStream_t s);
 // Ring / tree: ``grid`` sizes the persistent launch of the any-n kernels;
 // the compile-time-n kernels launch one workgroup per window and reserve
 // ``lds`` bytes of dynamic LDS (a residency cap, as for the fused kernels).
@@ -68,6 +104,8 @@ hipError_t launch_elem_ring_allreduce(int dt, int op, const RankTable &t, const 
                                       long long e_end, hipStream_t s);
 hipError_t launch_elem_tree_allreduce(int dt, int op, const RankTable &t, const TreeShape &tree, const Geometry &g,
                                       long long e_begin, long long e_end, hipStream_t s);
+hipError_t launch_elem_split_allreduce(int dt, int op, const RankTable &t, const Geometry &g, long long e_begin,
+                                       long long e_end, hipStream_t s);
 hipError_t launch_elem_reduce_scatter(int dt, int op, const RankTable &t, const Geometry &g, long long R,
                                       hipStream_t s);
 hipError_t launch_elem_all_gather(int elem_bytes, const RankTable &t, const Geometry &g, long long R, hipStream_t s);

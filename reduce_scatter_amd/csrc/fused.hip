@@ -111,17 +111,16 @@ __global__ __launch_bounds__(kFusedThreads) void fused_allreduce_kernel(const Ra
     int c;
     long long j;
     tile_coords(c, j);
-    const long long v0 = chunk_start(c, g) + j * kFusedTile;
     long long vend = chunk_start(c + 1, g);
     vend = vend < g.Vfull ? vend : g.Vfull;
-    if (v0 >= vend) return;                                   // short chunk: nothing in this tile
-    const unsigned last = (unsigned)min((long long)kFusedTile, vend - v0) - 1u;   // last valid lane of this tile
-    const bool ok = threadIdx.x <= last;
-    const unsigned lane_off = (ok ? threadIdx.x : last) * 16u;
-    Pack<DT> acc = chain<DT, OP, NR>(t, n, c, v0 * 16, lane_off, g.s);
+    const TileSpan ts = aligned_tile(chunk_start(c, g), vend, j, g.ref, kFusedTile);
+    if (ts.lo >= ts.hi) return;                               // past the chunk's end: nothing in this tile
+    bool ok;
+    const unsigned lane_off = tile_lane(ts, ts.start + threadIdx.x, ok);
+    Pack<DT> acc = chain<DT, OP, NR>(t, n, c, ts.lo * 16, lane_off, g.s);
     if (!ok) return;
     post<DT, OP>(acc, n);
-    store_all<NR>(t, n, v0 * 16, lane_off, pack<DT>(acc));
+    store_all<NR>(t, n, ts.lo * 16, lane_off, pack<DT>(acc));
 }
 
 // Many ranks (n > 16): with 2n streams per tile, DRAM locality comes from
@@ -142,19 +141,15 @@ __global__ __launch_bounds__(kFusedThreads) void fused_allreduce_wide_kernel(con
     int c;
     long long j;
     tile_coords(c, j);
-    const long long v0 = chunk_start(c, g) + j * (kFusedThreads * U);
     long long vend = chunk_start(c + 1, g);
     vend = vend < g.Vfull ? vend : g.Vfull;
-    if (v0 >= vend) return;
+    const TileSpan ts = aligned_tile(chunk_start(c, g), vend, j, g.ref, kFusedThreads * U);
+    if (ts.lo >= ts.hi) return;
     unsigned off[U];
     bool ok[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const long long v = v0 + threadIdx.x + u * kFusedThreads;
-        ok[u] = v < vend;
-        off[u] = (unsigned)((ok[u] ? v : vend - 1) - v0) * 16u;       // past the chunk: re-read its last vector
-    }
-    const long long base = v0 * 16;
+    for (int u = 0; u < U; ++u) off[u] = tile_lane(ts, ts.start + threadIdx.x + u * kFusedThreads, ok[u]);
+    const long long base = ts.lo * 16;
     Pack<DT> acc[U];
     for (int k0 = 0; k0 < n; k0 += B) {
         u32x4 raw[B][U];
@@ -198,14 +193,15 @@ __global__ __launch_bounds__(kFusedThreads) void fused_reduce_scatter_kernel(con
     int c;
     long long j;
     tile_coords(c, j);
-    const long long v0 = j * kFusedTile;                      // within the slice
-    const unsigned last = (unsigned)min((long long)kFusedTile, g.Rv - v0) - 1u;
-    const bool ok = threadIdx.x <= last;
-    const unsigned lane_off = (ok ? threadIdx.x : last) * 16u;
-    Pack<DT> acc = chain<DT, OP, NR>(t, n, c, ((long long)c * g.Rv + v0) * 16, lane_off, g.s);
+    // tiles follow the alignment of the n input slices (slice c of the reference input)
+    const TileSpan ts = aligned_tile(0, g.Rv, j, g.ref + (long long)c * g.Rv, kFusedTile);
+    if (ts.lo >= ts.hi) return;
+    bool ok;
+    const unsigned lane_off = tile_lane(ts, ts.start + threadIdx.x, ok);
+    Pack<DT> acc = chain<DT, OP, NR>(t, n, c, ((long long)c * g.Rv + ts.lo) * 16, lane_off, g.s);
     if (!ok) return;
     post<DT, OP>(acc, n);
-    __builtin_nontemporal_store(pack<DT>(acc), (u32x4 *)((char *)t.dst[c] + v0 * 16 + lane_off));
+    __builtin_nontemporal_store(pack<DT>(acc), (u32x4 *)((char *)t.dst[c] + ts.lo * 16 + lane_off));
 }
 
 // All-gather: input vector v of piece k is read once and written to vector
@@ -216,11 +212,13 @@ __global__ __launch_bounds__(kFusedThreads) void fused_all_gather_kernel(const R
     int k;
     long long j;
     tile_coords(k, j);
-    const long long v0 = j * kFusedTile;
-    if (v0 + threadIdx.x >= g.Rv) return;
-    const unsigned lane_off = threadIdx.x * 16u;
-    const u32x4 w = __builtin_nontemporal_load((const u32x4 *)((const char *)t.src[k] + v0 * 16 + lane_off));
-    store_all<NR>(t, n, ((long long)k * g.Rv + v0) * 16, lane_off, w);
+    // tiles follow the alignment of the n outputs (piece k of the reference output)
+    const TileSpan ts = aligned_tile(0, g.Rv, j, g.ref + (long long)k * g.Rv, kFusedTile);
+    bool ok;
+    const unsigned lane_off = tile_lane(ts, ts.start + threadIdx.x, ok);
+    if (!ok) return;
+    const u32x4 w = __builtin_nontemporal_load((const u32x4 *)((const char *)t.src[k] + ts.lo * 16 + lane_off));
+    store_all<NR>(t, n, ((long long)k * g.Rv + ts.lo) * 16, lane_off, w);
 }
 
 // Pick the compile-time rank count when there is one.
@@ -237,7 +235,7 @@ template <typename F> hipError_t by_ranks(int n, F &&f) {
 // Tiles per chunk of the wide (n > 16) all-reduce kernel.
 long long fused_wide_windows(int dt, long long maxlen) {
     const long long tile = kFusedThreads * ((dt == BF16 || dt == F16) ? WideTile<BF16>::U : WideTile<F32>::U);
-    return (maxlen + tile - 1) / tile;
+    return aligned_tiles(maxlen, tile);
 }
 
 hipError_t launch_fused_allreduce(int dt, int op, const RankTable &t, const Geometry &g, int lds, hipStream_t s) {

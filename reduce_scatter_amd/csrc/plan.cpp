@@ -12,7 +12,8 @@
 //
 //   steps:  ring 2(n-1) for all-reduce, n-1 for reduce-scatter / all-gather
 //           (section "The ring, exactly as the kernel runs it"); tree
-//           2 * depth (section "The double binary tree"); fused 1.
+//           2 * depth (section "The double binary tree"); fused 1; split 1
+//           (one pass; its log-depth combine stays inside a workgroup).
 //   bytes:  the algorithmic HBM bytes.  All three schedules keep partial
 //           results on chip, so each moves 2*n*S for an all-reduce of S bytes
 //           per rank, (n+1)*n*R*e for reduce-scatter and all-gather.
@@ -21,7 +22,7 @@
 //           section: the clean model does not fit medium sizes, so a
 //           per-size factor is applied), indexed by the call's total bytes.
 //
-// Legality: the tree schedule exists for all-reduce only.
+// Legality: the tree and split schedules exist for all-reduce only.
 //
 // Constants come from a calibration file (AR_CALIB, default
 // calib_gfx950.txt beside the library) written by the package's calibration
@@ -43,7 +44,7 @@ namespace ar {
 namespace {
 
 constexpr int kColls = 3;
-constexpr int kScheds = 4;         // indexed by ar_sched_t; 0 (auto) unused
+constexpr int kScheds = 5;         // indexed by ar_sched_t; 0 (auto) unused
 constexpr int kSizeBins = 48;      // per-size correction for log2(algorithmic bytes of the call) = 0..47
 
 constexpr int kRankClasses = 8;    // ceil(log2 n) = 0..7 for n = 1..128
@@ -72,8 +73,9 @@ void set_defaults(Calib &c) {
         for (int s = 1; s < kScheds; ++s) {
             Entry &e = c.e[k][s];
             e.launch_us = 8.0;
-            e.step_us = (s == AR_SCHED_FUSED) ? 0.0 : 0.25;
-            e.bw_gbps = (s == AR_SCHED_FUSED) ? 5000.0 : 4000.0;
+            const bool one_pass = s == AR_SCHED_FUSED || s == AR_SCHED_SPLIT;
+            e.step_us = one_pass ? 0.0 : 0.25;
+            e.bw_gbps = s == AR_SCHED_FUSED ? 5000.0 : 4000.0;
             for (int k2 = 0; k2 < kRankClasses; ++k2) {
                 e.measured[k2] = false;
                 e.extra_us[k2] = 0.0;
@@ -94,6 +96,7 @@ int sched_index(const char *s) {
     if (!strcmp(s, "ring")) return AR_SCHED_RING;
     if (!strcmp(s, "tree")) return AR_SCHED_TREE;
     if (!strcmp(s, "fused")) return AR_SCHED_FUSED;
+    if (!strcmp(s, "split")) return AR_SCHED_SPLIT;
     return -1;
 }
 
@@ -111,7 +114,7 @@ std::string library_dir() {
 //   <coll> <sched> <launch_us> <step_us> <bw_gbps>
 //   corr <coll> <sched> <rank class> <corr_0 ... corr_47>
 //   lat <coll> <sched> <rank class> <extra_us>
-// coll in {allreduce, reduce_scatter, all_gather}, sched in {ring, tree, fused};
+// coll in {allreduce, reduce_scatter, all_gather}, sched in {ring, tree, fused, split};
 // rank class = ceil(log2 n); corr_b multiplies the bandwidth for calls that
 // move 2^b .. 2^(b+1)-1 algorithmic bytes in total (the footprint decides
 // whether the data stays in the 256 MB Infinity Cache, and how that bends the
@@ -240,24 +243,21 @@ ar_status_t make_plan(ar_coll_t coll, size_t count, ar_dtype_t dtype, ar_op_t op
         per_rank = (double)n * count * e;
         bytes = (n + 1.0) * n * (double)count * e;
     }
-    int depth = 0;
-    for (int v = 0; v < n; ++v) {
-        int d = 0;
-        for (int p = v; p != 0; p = tree_parent(n, p)) ++d;
-        depth = d > depth ? d : depth;
-    }
+    int depth = 0;                                  // the bit-trick tree over n ranks is ceil(log2 n) deep
+    while ((1 << depth) < n) ++depth;
     out->legal_mask = (1u << AR_SCHED_RING) | (1u << AR_SCHED_FUSED);
-    if (coll == AR_COLL_ALLREDUCE) out->legal_mask |= (1u << AR_SCHED_TREE);
+    if (coll == AR_COLL_ALLREDUCE) out->legal_mask |= (1u << AR_SCHED_TREE) | (1u << AR_SCHED_SPLIT);
     out->steps[AR_SCHED_RING] = (coll == AR_COLL_ALLREDUCE) ? 2 * (n - 1) : (n - 1);
     out->steps[AR_SCHED_TREE] = (coll == AR_COLL_ALLREDUCE) ? 2 * depth : 0;
     out->steps[AR_SCHED_FUSED] = 1;
+    out->steps[AR_SCHED_SPLIT] = (coll == AR_COLL_ALLREDUCE) ? 1 : 0;
     double best = 0;
     out->chosen = AR_SCHED_FUSED;
     bool have = false;
     (void)per_rank;
     const int bin = size_bin(bytes);
     const int rclass = rank_class(n);
-    for (int s = AR_SCHED_RING; s <= AR_SCHED_FUSED; ++s) {
+    for (int s = AR_SCHED_RING; s <= AR_SCHED_SPLIT; ++s) {
         if (!(out->legal_mask & (1u << s))) continue;
         const Entry &c = g_calib.e[coll][s];
         out->bytes[s] = bytes;

@@ -58,9 +58,10 @@ def test_invalid_arguments_are_rejected_before_launch():
     # misaligned for the element size
     assert _err(ar.ar_allreduce, [A[0] + 2, A[1]], B[:2], 16, "f32", "sum") == "AR_ERR_ALIGNMENT"
     assert _err(ar.ar_allreduce, [A[0] + 1, A[1]], B[:2], 16, "bf16", "sum") == "AR_ERR_ALIGNMENT"
-    # tree is not a reduce-scatter / all-gather schedule
-    assert _err(ar.ar_reduce_scatter, A[:2], B[:2], 16, "f32", "sum", sched="tree") == "AR_ERR_UNSUPPORTED"
-    assert _err(ar.ar_all_gather, A[:2], B[:2], 16, "f32", sched="tree") == "AR_ERR_UNSUPPORTED"
+    # tree and split are all-reduce schedules only
+    for sched in ("tree", "split"):
+        assert _err(ar.ar_reduce_scatter, A[:2], B[:2], 16, "f32", "sum", sched=sched) == "AR_ERR_UNSUPPORTED"
+        assert _err(ar.ar_all_gather, A[:2], B[:2], 16, "f32", sched=sched) == "AR_ERR_UNSUPPORTED"
 
 
 def test_zero_count_is_a_no_op():
@@ -88,6 +89,67 @@ def test_overlap_rules():
     assert _err(ar.ar_all_gather, [B[1], A[1]], B[:2], R, "f32") == "AR_ERR_INVALID_ARG"
 
 
+def _brute_conflict(send, slen, recv, rlen, allowed):
+    """Pairwise rule: a recv range may overlap nothing but its own send range in
+    the allowed in-place layout; send ranges may overlap each other."""
+    ov = lambda a, al, b, bl: a < b + bl and b < a + al
+    n = len(send)
+    for r in range(n):
+        for k in range(n):
+            if ov(recv[r], rlen, send[k], slen) and not (k == r and allowed[r]):
+                return True
+        for k in range(r + 1, n):
+            if ov(recv[r], rlen, recv[k], rlen):
+                return True
+    return False
+
+
+def test_overlap_check_matches_the_pairwise_rule():
+    """Random layouts on a coarse address grid (overlaps are frequent): the
+    library rejects exactly the layouts the pairwise rule rejects; accepted
+    layouts get as far as the device query, which fails without a GPU."""
+    import random
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("host-logic test: an accepted layout would launch on addresses nobody owns")
+    rng = random.Random(5)
+    base = 1 << 32
+    unit = 256                                            # bytes: 64 fp32
+    for trial in range(3000):
+        n = rng.randint(1, 9)
+        coll = rng.choice(["allreduce", "reduce_scatter", "all_gather"])
+        R = 64                                            # elements per slice
+        if coll == "allreduce":
+            slen = rlen = R * 4
+        elif coll == "reduce_scatter":
+            slen, rlen = n * R * 4, R * 4
+        else:
+            slen, rlen = R * 4, n * R * 4
+        span = 4 * n * max(slen, rlen) // unit
+        send = [base + unit * rng.randrange(span) for _ in range(n)]
+        recv = [base + unit * rng.randrange(span) for _ in range(n)]
+        for r in range(n):                                # make some ranks use the in-place layout
+            if rng.random() < 0.3:
+                if coll == "allreduce":
+                    recv[r] = send[r]
+                elif coll == "reduce_scatter":
+                    recv[r] = send[r] + r * R * 4
+                else:
+                    send[r] = recv[r] + r * R * 4
+        if coll == "allreduce":
+            allowed = [recv[r] == send[r] for r in range(n)]
+            call = lambda: ar.ar_allreduce(send, recv, R, "f32", "sum", sched="fused")
+        elif coll == "reduce_scatter":
+            allowed = [recv[r] == send[r] + r * R * 4 for r in range(n)]
+            call = lambda: ar.ar_reduce_scatter(send, recv, R, "f32", "sum", sched="fused")
+        else:
+            allowed = [send[r] == recv[r] + r * R * 4 for r in range(n)]
+            call = lambda: ar.ar_all_gather(send, recv, R, "f32", sched="fused")
+        want = _brute_conflict(send, slen, recv, rlen, allowed)
+        got = _err(call) == "AR_ERR_INVALID_ARG"
+        assert got == want, (trial, coll, n, send, recv)
+
+
 def test_tree_parent_matches_the_14_rank_picture():
     with open(os.path.join(ROOT, "tests", "golden", "tree14.json")) as f:
         g = json.load(f)
@@ -99,10 +161,10 @@ def test_plan_steps_bytes_and_legality():
     for n in (1, 2, 4, 8, 16, 72, 128):
         count = 1 << 20
         p = ar.ar_plan("allreduce", count, "f32", "sum", n)
-        assert p.legal == ["ring", "tree", "fused"]
+        assert p.legal == ["ring", "tree", "fused", "split"]
         assert p.steps["ring"] == 2 * (n - 1)
         assert p.steps["tree"] == 2 * ((n - 1).bit_length() if n > 1 else 0)
-        assert p.steps["fused"] == 1
+        assert p.steps["fused"] == 1 and p.steps["split"] == 1
         assert all(b == 2 * n * count * 4 for b in p.bytes.values())
         assert p.chosen == min(p.predicted_us, key=lambda s: (p.predicted_us[s], ar.SCHEDS[s]))
         for coll in ("reduce_scatter", "all_gather"):
@@ -138,6 +200,7 @@ def test_plan_reads_the_calibration_file(tmp_path):
     corr = ["1.0"] * 48
     corr[27] = "0.5"                     # 2^27 .. 2^28 - 1 bytes in total
     f.write_text("allreduce ring 10 0.5 1000\nallreduce tree 20 1 1000\nallreduce fused 5 0 500\n"
+                 "allreduce split 7 0 400\nlat allreduce split 3 2.5\n"
                  "corr allreduce fused 3 " + " ".join(corr) + "\n")
     count = (1 << 27) // (2 * 8 * 4)     # n = 8 fp32: 2*n*S = 2^27 bytes
     p = _plan_in_subprocess(str(f), [("allreduce", count, "f32", "sum", 8)])[0]
@@ -145,6 +208,7 @@ def test_plan_reads_the_calibration_file(tmp_path):
     assert abs(p["predicted_us"]["ring"] - (10 + 0.5 * 14 + b / 1e3 / 1000)) < 1e-6
     assert abs(p["predicted_us"]["tree"] - (20 + 1 * 6 + b / 1e3 / 1000)) < 1e-6
     assert abs(p["predicted_us"]["fused"] - (5 + b / 1e3 / (500 * 0.5))) < 1e-6
+    assert abs(p["predicted_us"]["split"] - (7 + 2.5 + b / 1e3 / 400)) < 1e-6
     assert p["chosen"] == min(p["predicted_us"], key=p["predicted_us"].get)
     # a rank class with no row of its own uses the nearest measured one (class 3 for n = 16)
     p16 = _plan_in_subprocess(str(f), [("allreduce", count // 2, "f32", "sum", 16)])[0]

@@ -10,7 +10,9 @@
   the plain element-wise definition is exact on any slice).
 * 72 ranks, 29 gradient buckets of up to 25 MB packed from 256 tensors, avg,
   in place, back to back: three buckets (first, middle, last: ragged chunk
-  splits) checked element by element against the ring oracle.
+  splits) checked element by element against the oracle of the planner's
+  choice; the split schedule on one 25 MB bucket against the pairwise oracle.
+* The split schedule at the 8 x 256 MB shape against the pairwise oracle.
 """
 from __future__ import annotations
 
@@ -62,6 +64,21 @@ def test_c2_fused_and_ring_full_size(c2_inputs, op):
         _same_on_all_ranks(ys)
         assert_bits_equal(to_host(ys[0], "f32"), want, "c2 %s %s" % (op, sched))
         del ys
+
+
+def test_c2_split_full_size(c2_inputs):
+    xs, host = c2_inputs
+    count = xs[0].numel()
+    print("c2 split oracle", flush=True)
+    want = oracle.pairwise_reduce(host, "f32", "sum")
+    ys = [torch.empty_like(x) for x in xs]
+    ar.ar_allreduce(xs, ys, count, "f32", "sum", sched="split")
+    torch.cuda.synchronize()
+    _same_on_all_ranks(ys)
+    got = to_host(ys[0], "f32")
+    assert_bits_equal(got, want, "c2 split")
+    ring = oracle.ring_allreduce(host, "f32", "sum")[0]
+    assert np.max(np.abs(got.astype(np.float64) - ring)) <= 1e-6 * np.max(np.abs(ring))
 
 
 def test_c2_tree_and_in_place_full_size(c2_inputs):
@@ -155,8 +172,14 @@ def test_c5_bucketed_72_ranks_in_place():
         off, nbytes = buckets[b]
         a, e = off // 4, (off + nbytes) // 4
         host = [to_host(g[a:e], "f32") for g in grads]
-        print("c5 oracle bucket", b, nbytes, flush=True)
-        want[b] = oracle.ring_allreduce(host, "f32", "avg")[0]
+        chosen = ar.ar_plan("allreduce", e - a, "f32", "avg", n).chosen
+        print("c5 oracle bucket", b, nbytes, chosen, flush=True)
+        if chosen == "split":
+            want[b] = oracle.pairwise_reduce(host, "f32", "avg")
+        elif chosen == "tree":
+            want[b] = oracle.tree_allreduce(host, "f32", "avg")[0]
+        else:
+            want[b] = oracle.ring_allreduce(host, "f32", "avg")[0]
     for b, (off, nbytes) in enumerate(buckets):           # back to back on one stream, in place
         a, e = off // 4, (off + nbytes) // 4
         views = [g[a:e] for g in grads]
@@ -167,5 +190,23 @@ def test_c5_bucketed_72_ranks_in_place():
         a, e = off // 4, (off + nbytes) // 4
         for r in (0, 35, n - 1):
             assert_bits_equal(to_host(grads[r][a:e], "f32"), want[b], "c5 bucket %d rank %d" % (b, r))
+    del grads
+    torch.cuda.empty_cache()
+
+
+def test_c5_split_one_bucket_in_place():
+    """The split schedule on the 72-rank workload's first (25 MB) bucket, in place."""
+    n = workloads.C5_N
+    buckets, _ = workloads.c5_buckets()
+    off, nbytes = buckets[0]
+    count = nbytes // 4
+    grads = [workloads.device_spiky_normal(4, r, count, 1e-3, 0.01, 100.0) for r in range(n)]
+    host = [to_host(g, "f32") for g in grads]
+    print("c5 split oracle", nbytes, flush=True)
+    want = oracle.pairwise_reduce(host, "f32", "avg")
+    ar.ar_allreduce(grads, grads, count, "f32", "avg", sched="split")
+    torch.cuda.synchronize()
+    for r in (0, 35, n - 1):
+        assert_bits_equal(to_host(grads[r], "f32"), want, "c5 split rank %d" % r)
     del grads
     torch.cuda.empty_cache()

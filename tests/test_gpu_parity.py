@@ -3,8 +3,9 @@ element, at sizes the oracle finishes in seconds that still span several
 tiles / LDS windows and a ragged tail.
 
 Bar: ring and fused results are bit-identical to the ring oracle (they use
-its hop order), tree results bit-identical to the tree oracle; all-gather
-and every integer result are bit-exact by construction."""
+its hop order), tree results bit-identical to the tree oracle, split results
+bit-identical to the pairwise oracle; all-gather and every integer result are
+bit-exact by construction."""
 from __future__ import annotations
 
 import numpy as np
@@ -37,6 +38,17 @@ def inputs(seed, n, count, dtype, op):
     return [workloads.random_values(seed, n * 1000 + count, r, count, dtype, kind) for r in range(n)]
 
 
+def reference(sched, xs, dtype, op):
+    """The oracle of a schedule's reduction order (AUTO: of the planner's choice)."""
+    if sched == "auto":
+        sched = ar.ar_plan("allreduce", xs[0].size, dtype, op, len(xs)).chosen
+    if sched == "tree":
+        return oracle.tree_allreduce(xs, dtype, op)
+    if sched == "split":
+        return [oracle.pairwise_reduce(xs, dtype, op)] * len(xs)
+    return oracle.ring_allreduce(xs, dtype, op)
+
+
 def run_allreduce(xs, dtype, op, sched, inplace=False):
     n = len(xs)
     d_in = [to_device(x, dtype) for x in xs]
@@ -53,12 +65,9 @@ def test_allreduce_matches_oracle(dtype, op):
         for count in counts_for(n, dtype):
             print("allreduce", dtype, op, "n=%d count=%d" % (n, count), flush=True)
             xs = inputs(1, n, count, dtype, op)
-            ring = oracle.ring_allreduce(xs, dtype, op)
-            tree = oracle.tree_allreduce(xs, dtype, op)
-            chosen = ar.ar_plan("allreduce", count, dtype, op, n).chosen
-            for sched in ("fused", "ring", "tree", "auto"):
+            for sched in ("fused", "ring", "tree", "split", "auto"):
                 got = run_allreduce(xs, dtype, op, sched)
-                ref = tree if (sched == "tree" or (sched == "auto" and chosen == "tree")) else ring
+                ref = reference(sched, xs, dtype, op)
                 for r in range(n):
                     assert_bits_equal(got[r], ref[r], "%s %s %s n=%d count=%d rank %d" % (sched, dtype, op, n, count, r))
 
@@ -68,7 +77,7 @@ def test_allreduce_in_place_equals_out_of_place(dtype):
     n, count = 8, 8 * FUSED_TILE * 8 + 13
     for op in OPS:
         xs = inputs(2, n, count, dtype, op)
-        for sched in ("fused", "ring", "tree"):
+        for sched in ("fused", "ring", "tree", "split"):
             a = run_allreduce(xs, dtype, op, sched)
             b = run_allreduce(xs, dtype, op, sched, inplace=True)
             for r in range(n):
@@ -82,15 +91,13 @@ def test_allreduce_element_wise_path(dtype):
     n, count = 5, 3001
     for op in ("sum", "avg", "max"):
         xs = inputs(3, n, count, dtype, op)
-        ring = oracle.ring_allreduce(xs, dtype, op)
-        tree = oracle.tree_allreduce(xs, dtype, op)
-        for sched in ("fused", "ring", "tree"):
+        for sched in ("fused", "ring", "tree", "split"):
             d_in = [to_device(np.concatenate([x[:1], x]), dtype)[1:] for x in xs]
             d_out = [empty(count + 1, dtype, 0)[1:] for _ in xs]
             assert d_in[0].data_ptr() % 16 != 0
             ar.ar_allreduce(d_in, d_out, count, dtype, op, sched=sched)
             sync()
-            ref = tree if sched == "tree" else ring
+            ref = reference(sched, xs, dtype, op)
             for r in range(n):
                 assert_bits_equal(to_host(d_out[r], dtype), ref[r], "elem %s %s %s" % (sched, dtype, op))
 
@@ -178,7 +185,7 @@ def test_c1_workload_every_schedule():
     exact integer sum."""
     xs = workloads.c1_inputs()
     want = sum(x.astype(np.int64) for x in xs).astype(np.float32)
-    for sched in ("fused", "ring", "tree", "auto"):
+    for sched in ("fused", "ring", "tree", "split", "auto"):
         for y in run_allreduce(xs, "f32", "sum", sched):
             assert_bits_equal(y, want, "c1 " + sched)
     parts = run_rs(xs, "f32", "sum", "auto")
@@ -193,13 +200,87 @@ def test_large_rank_counts():
     for n in (72, 128):
         count = n * 4 * 40 + 3
         xs = inputs(7, n, count, "f32", "avg")
-        ring = oracle.ring_allreduce(xs, "f32", "avg")
-        tree = oracle.tree_allreduce(xs, "f32", "avg")
-        for sched in ("fused", "ring", "tree"):
+        for sched in ("fused", "ring", "tree", "split"):
             got = run_allreduce(xs, "f32", "avg", sched)
-            ref = tree if sched == "tree" else ring
+            ref = reference(sched, xs, "f32", "avg")
             for r in (0, n // 2, n - 1):
                 assert_bits_equal(got[r], ref[r], "n=%d %s" % (n, sched))
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_split_many_ranks_every_op(dtype):
+    """The split schedule at rank counts that exercise every ranks-per-wave
+    choice (1, 2, 4, 8 ranks per wave; partial last waves), all ops."""
+    u = LANES[dtype]
+    for n in (17, 31, 33, 72, 100, 128):
+        count = 64 * u * 3 + u * 5 + 3                   # 3 full tiles, a partial tile, a ragged tail
+        for op in OPS:
+            print("split", dtype, op, "n=%d" % n, flush=True)
+            xs = inputs(8, n, count, dtype, op)
+            want = oracle.pairwise_reduce(xs, dtype, op)
+            got = run_allreduce(xs, dtype, op, "split")
+            for r in (0, n // 2, n - 1):
+                assert_bits_equal(got[r], want, "split %s %s n=%d rank %d" % (dtype, op, n, r))
+            if dtype == "i32" or op in ("min", "max"):
+                assert_bits_equal(want, oracle.direct_reduce(xs, dtype, op), "split exact")
+
+
+def _at_offset(x, dtype, off_bytes):
+    """A device copy of host array x starting off_bytes past a fresh allocation."""
+    pad = off_bytes // (4 if dtype in ("f32", "i32") else 2)
+    return to_device(np.concatenate([np.zeros(pad, x.dtype), x]), dtype)[pad:]
+
+
+def _empty_at_offset(count, dtype, off_bytes):
+    pad = off_bytes // (4 if dtype in ("f32", "i32") else 2)
+    return empty(count + pad, dtype, 0)[pad:]
+
+
+OFFSET_SETS = {
+    "same 48 B": lambda n: [48] * n,
+    "same 1040 B": lambda n: [1040] * n,
+    "mixed": lambda n: [16 * (r % 7) for r in range(n)],
+}
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_tiles_cut_on_an_aligned_grid(dtype):
+    """Rank buffers 16-byte aligned but off 1 KB boundaries (the same offset on
+    every rank, or different ones): the fused and split kernels cut tiles on
+    rank 0's aligned grid, leaving partial first tiles; results unchanged."""
+    u = LANES[dtype]
+    for n in (3, 8, 72):
+        count = 64 * u * 5 + u * 3 + 1
+        for label, offs in OFFSET_SETS.items():
+            offsets = offs(n)
+            print("aligned grid", dtype, n, label, flush=True)
+            xs = inputs(9, n, count, dtype, "avg")
+            for sched in ("fused", "split", "ring", "tree"):
+                d_in = [_at_offset(x, dtype, o) for x, o in zip(xs, offsets)]
+                d_out = [_empty_at_offset(count, dtype, (o + 32) % 1024) for o in offsets]
+                ar.ar_allreduce(d_in, d_out, count, dtype, "avg", sched=sched)
+                ar.ar_allreduce(d_in, d_in, count, dtype, "avg", sched=sched)          # in place
+                sync()
+                ref = reference(sched, xs, dtype, "avg")
+                for r in (0, n // 2, n - 1):
+                    assert_bits_equal(to_host(d_out[r], dtype), ref[r], "%s n=%d %s rank %d" % (sched, n, label, r))
+                    assert_bits_equal(to_host(d_in[r], dtype), ref[r], "%s n=%d %s in place" % (sched, n, label))
+            R = 64 * u * 3 + u * 2                                  # 16-byte multiple: the vector path
+            ys = inputs(10, n, n * R, dtype, "sum")
+            want = oracle.ring_reduce_scatter(ys, dtype, "sum")
+            pieces = [workloads.random_values(11, n, r, R, dtype) for r in range(n)]
+            gathered = oracle.ring_all_gather(pieces, dtype)
+            for sched in ("fused", "ring"):
+                d_in = [_at_offset(y, dtype, o) for y, o in zip(ys, offsets)]
+                d_out = [_empty_at_offset(R, dtype, (o + 16) % 1024) for o in offsets]
+                ar.ar_reduce_scatter(d_in, d_out, R, dtype, "sum", sched=sched)
+                g_in = [_at_offset(pc, dtype, o) for pc, o in zip(pieces, offsets)]
+                g_out = [_empty_at_offset(n * R, dtype, (o + 80) % 1024) for o in offsets]
+                ar.ar_all_gather(g_in, g_out, R, dtype, sched=sched)
+                sync()
+                for r in (0, n // 2, n - 1):
+                    assert_bits_equal(to_host(d_out[r], dtype), want[r], "rs %s n=%d %s" % (sched, n, label))
+                    assert_bits_equal(to_host(g_out[r], dtype), gathered[r], "ag %s n=%d %s" % (sched, n, label))
 
 
 def test_one_hip_runtime_whatever_the_import_order():
