@@ -68,7 +68,7 @@ def measure(ns, sizes, iters):
     for n in ns:
         for per_rank in sizes:
             count = per_rank // 4               # fp32
-            if count < n * 4 or n * per_rank > (8 << 30):
+            if count < n * 4 or n * per_rank > (16 << 30):
                 continue
             xs_t = [torch.randn(count, device="cuda") for _ in range(n)]
             ys_t = [torch.empty_like(x) for x in xs_t]
@@ -174,7 +174,7 @@ def main(argv=None):
         return 2
     torch.cuda.set_device(0)
     ns = (2, 8) if a.quick else (2, 4, 8, 16, 32, 72, 128)
-    sizes = [1 << k for k in ((12, 16, 20, 24, 28) if a.quick else (10, 12, 14, 16, 18, 20, 21, 22, 23, 24, 25, 26, 27, 28))]
+    sizes = [1 << k for k in ((12, 16, 20, 24, 28) if a.quick else (10, 12, 14, 16, 18, 20, 21, 22, 23, 24, 25, 26, 27, 28, 29, 30))]
     rows = measure(ns, sizes, iters=5 if a.quick else 10)
     model = fit(rows)
     write(a.out, model, torch.cuda.get_device_name(0) + " " + getattr(torch.cuda.get_device_properties(0),
