@@ -12,7 +12,8 @@ functions follow:
 * "NCCL all-reduce" post (rakshithvasudev.github.io), sections "What
   all-reduce promises" and "The ring, exactly as the kernel runs it":
   :func:`ring_allreduce`, :func:`ring_reduce_scatter`, :func:`ring_all_gather`;
-  section "The double binary tree": :func:`tree_parent`, :func:`tree_allreduce`;
+  section "The double binary tree": :func:`tree_parent`, :func:`tree_allreduce`,
+  and the two complementary trees: :func:`dtree_parent`, :func:`dtree_allreduce`;
   the plain element-wise definition (exact for int32 and min/max):
   :func:`direct_reduce`; section "When the switch does the math" (every rank
   combined at once, in an order the post leaves open; read as the aligned
@@ -89,6 +90,10 @@ def _load():
         lib.orc_pairwise_reduce.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_size_t, vpp,
                                             ctypes.c_void_p]
         lib.orc_pairwise_reduce.restype = ctypes.c_int
+        lib.orc_dtree_allreduce.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_size_t, vpp, vpp]
+        lib.orc_dtree_allreduce.restype = ctypes.c_int
+        lib.orc_dtree_parent.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+        lib.orc_dtree_parent.restype = ctypes.c_int
         lib.orc_tree_parent.argtypes = [ctypes.c_int, ctypes.c_int]
         lib.orc_tree_parent.restype = ctypes.c_int
         lib.orc_allreduce_chunks.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_size_t,
@@ -233,6 +238,24 @@ def tree_allreduce(xs, dtype: str, op: str, out=None):
     ys = out if out is not None else [np.empty(count, NP_DTYPE[dtype]) for _ in range(n)]
     _check_inputs(ys, dtype, count)
     _call(_load().orc_tree_allreduce(DTYPE_CODE[dtype], OP_CODE[op], n, count, _ptrs(xs), _ptrs(ys)))
+    return ys
+
+
+def dtree_parent(n: int, which: int, v: int) -> int:
+    """Parent of rank v in tree ``which`` (0: the bit-trick tree; 1: its mirror
+    for even n, its +1 shift for odd n) of the double binary tree; -1 for a root."""
+    return int(_load().orc_dtree_parent(n, which, v))
+
+
+def dtree_allreduce(xs, dtype: str, op: str, out=None):
+    """Double binary tree all-reduce: elements [0, u*floor(V/2)) up the first
+    tree, the rest up the second (u = 16 / element size, V = ceil(count / u))."""
+    n = len(xs)
+    count = xs[0].size
+    _check_inputs(xs, dtype, count)
+    ys = out if out is not None else [np.empty(count, NP_DTYPE[dtype]) for _ in range(n)]
+    _check_inputs(ys, dtype, count)
+    _call(_load().orc_dtree_allreduce(DTYPE_CODE[dtype], OP_CODE[op], n, count, _ptrs(xs), _ptrs(ys)))
     return ys
 
 

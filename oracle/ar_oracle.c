@@ -41,6 +41,9 @@
  *    falling back to v ^ b when that is >= n; own value first, then the
  *    children's partials in ascending rank order; the root applies the
  *    integer-avg postOp and every rank receives the root's value;
+ *  - the double binary tree's second tree mirrors the first (n even) or
+ *    shifts it by +1 rank (n odd); the first u*floor(V/2) elements go up the
+ *    first tree, the rest up the second;
  *  - the fused pass that combines all ranks at once uses the aligned binary
  *    tree over rank indices (split at the largest power of two below the
  *    range length), lower ranks on the left.
@@ -498,15 +501,45 @@ int orc_tree_parent(int n, int v)
     return p;
 }
 
+/* The second tree of the double binary tree ("The double binary tree": the
+ * roles swapped so that the first tree's leaves work as interior nodes): the
+ * mirror image of the first when n is even (rank v plays the part of rank
+ * n-1-v), the first shifted by one rank when n is odd (rank v plays the part
+ * of rank v-1 mod n; the shift direction is a reading).  which = 0 is the
+ * first tree itself.  Returns -1 for the root and for v outside [0, n). */
+int orc_dtree_parent(int n, int which, int v)
+{
+    if (v < 0 || v >= n) return -1;
+    if (which == 0) return orc_tree_parent(n, v);
+    if (n % 2 == 0) {
+        int p = orc_tree_parent(n, n - 1 - v);
+        return p < 0 ? -1 : n - 1 - p;
+    }
+    int p = orc_tree_parent(n, (v - 1 + n) % n);
+    return p < 0 ? -1 : (p + 1) % n;
+}
+
 /* Up phase, for one element: own value first, then each child's partial in
  * ascending rank order. */
-static val_t tree_partial(int dtype, int op, int n, int v, const void *const *x, size_t i, float s)
+static val_t tree_partial_of(int dtype, int op, int n, int which, int v, const void *const *x, size_t i, float s)
 {
     val_t p = round_to_type(dtype, pre_op(dtype, op, load_elem(dtype, x[v], i), s));
-    for (int ch = 1; ch < n; ++ch)                       /* children may rank below or above v */
-        if (orc_tree_parent(n, ch) == v)
-            p = round_to_type(dtype, combine(dtype, op, p, tree_partial(dtype, op, n, ch, x, i, s)));
+    for (int ch = 0; ch < n; ++ch)                       /* children may rank below or above v */
+        if (ch != v && orc_dtree_parent(n, which, ch) == v)
+            p = round_to_type(dtype, combine(dtype, op, p, tree_partial_of(dtype, op, n, which, ch, x, i, s)));
     return p;
+}
+
+static val_t tree_partial(int dtype, int op, int n, int v, const void *const *x, size_t i, float s)
+{
+    return tree_partial_of(dtype, op, n, 0, v, x, i, s);
+}
+
+static int tree_root(int n, int which)
+{
+    for (int v = 0; v < n; ++v)
+        if (orc_dtree_parent(n, which, v) < 0) return v;
+    return 0;
 }
 
 /* Tree all-reduce: reduce up to rank 0, postOp there, broadcast back down.
@@ -525,6 +558,36 @@ int orc_tree_allreduce(int dtype, int op, int n, size_t count, const void *const
     for (int v = 0; v < n; ++v)
         for (size_t j = 0; j < count; ++j) store_elem(dtype, y[v], j, root[j]);
     free(root);
+    return ORC_OK;
+}
+
+/* Double binary tree all-reduce: half of every buffer is reduced up (and
+ * broadcast down) the first tree, the other half the second ("NCCL then
+ * assigns half its channels to each tree").  Reading: the halves are cut in
+ * 16-byte units like the ring's chunks with n = 2: elements
+ * [0, u*floor(V/2)) go up the first tree and the rest up the second, where
+ * u = 16 / element size and V = ceil(count / u).  Each tree reduces as the
+ * single tree does (own value first, children in ascending rank order, postOp
+ * at its root) and every rank receives its root's value. */
+int orc_dtree_allreduce(int dtype, int op, int n, size_t count, const void *const *x, void *const *y)
+{
+    if (bad_args(dtype, op, n)) return ORC_EBADARG;
+    const float s = (float)(1.0 / (double)n);
+    const size_t u = 16 / elem_size(dtype);
+    const size_t V = (count + u - 1) / u;
+    const size_t half = u * (V / 2);
+    const int root[2] = {tree_root(n, 0), tree_root(n, 1)};
+    val_t *res = malloc((count ? count : 1) * sizeof(val_t));
+    if (!res) return ORC_ENOMEM;
+    long long i;
+#pragma omp parallel for schedule(static)
+    for (i = 0; i < (long long)count; ++i) {
+        const int which = (size_t)i < half ? 0 : 1;
+        res[i] = post_op(dtype, op, n, tree_partial_of(dtype, op, n, which, root[which], x, (size_t)i, s));
+    }
+    for (int v = 0; v < n; ++v)
+        for (size_t j = 0; j < count; ++j) store_elem(dtype, y[v], j, res[j]);
+    free(res);
     return ORC_OK;
 }
 

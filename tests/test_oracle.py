@@ -174,10 +174,11 @@ def test_brute_force_allreduce(dtype, op):
             ring = oracle.ring_allreduce(xs, dtype, op)
             tree = oracle.tree_allreduce(xs, dtype, op)
             pair = [oracle.pairwise_reduce(xs, dtype, op)] * n
+            dtree = oracle.dtree_allreduce(xs, dtype, op)
             fx = [as_float(x, dtype) if dtype != "i32" else x.astype(np.int64) for x in xs]
             want = [_brute_elem([f[i] for f in fx], dtype, op, n) for i in range(count)]
             for r in range(n):
-                for ys in (ring, tree, pair):
+                for ys in (ring, tree, pair, dtree):
                     got = as_float(ys[r], dtype) if dtype != "i32" else ys[r].astype(np.int64)
                     assert [Fraction(float(v)) if dtype != "i32" else int(v) for v in got] == want, \
                         (dtype, op, n, count, r)
@@ -544,6 +545,142 @@ def test_tree_and_ring_agree_when_exact_and_within_bound_otherwise():
     ring = oracle.ring_allreduce(xs, "f32", "sum")[0].astype(np.float64)
     tree = oracle.tree_allreduce(xs, "f32", "sum")[0].astype(np.float64)
     assert np.max(np.abs(ring - tree)) <= 1e-6 * np.max(np.abs(ring))
+
+
+# ---------------------------------------------------------------------------
+# 6a. the double binary tree
+# ---------------------------------------------------------------------------
+
+def _bit_trick_parent(n, v):
+    """The first tree as the pages describe it (lowest set bit fixes the depth;
+    clear it and set the next bit up, or just clear it past the end)."""
+    if v == 0:
+        return -1
+    b = v & -v
+    p = (v ^ b) | (b << 1)
+    return v ^ b if p >= n else p
+
+
+def _second_tree_parent(n, v):
+    """The mirror image of the first tree for even n, the first tree shifted by
+    one rank (+1) for odd n."""
+    if n % 2 == 0:
+        p = _bit_trick_parent(n, n - 1 - v)
+        return -1 if p < 0 else n - 1 - p
+    p = _bit_trick_parent(n, (v - 1) % n)
+    return -1 if p < 0 else (p + 1) % n
+
+
+def test_dtree_parents_follow_the_construction():
+    for n in range(1, 129):
+        for which, ref in ((0, _bit_trick_parent), (1, _second_tree_parent)):
+            assert [oracle.dtree_parent(n, which, v) for v in range(n)] == [ref(n, v) for v in range(n)], (n, which)
+
+
+def test_dtree_second_tree_mirrors_the_14_rank_picture():
+    g = golden("tree14.json")
+    n, par = g["n"], g["parent"]
+    want = [-1 if par[n - 1 - v] < 0 else n - 1 - par[n - 1 - v] for v in range(n)]
+    assert [oracle.dtree_parent(n, 1, v) for v in range(n)] == want
+
+
+def test_dtree_trees_are_complementary():
+    """Every rank is interior in at most one of the two trees, except one
+    boundary rank interior in both when n is odd; both trees are ceil(log2 n)
+    deep, with at most two children per node; the first tree's leaves are the
+    odd ranks."""
+    for n in range(2, 129):
+        interior = []
+        for which in (0, 1):
+            par = [oracle.dtree_parent(n, which, v) for v in range(n)]
+            assert sum(p < 0 for p in par) == 1
+            kids = {v: [c for c in range(n) if par[c] == v] for v in range(n)}
+            assert max(len(k) for k in kids.values()) <= 2
+            depth = 0
+            for v in range(n):
+                d, u = 0, v
+                while par[u] >= 0:
+                    u, d = par[u], d + 1
+                    assert d <= n
+                depth = max(depth, d)
+            assert depth == math.ceil(math.log2(n)), (n, which)
+            interior.append({v for v in range(n) if kids[v]})
+        both = interior[0] & interior[1]
+        assert len(both) == (n % 2), (n, both)
+        assert {v for v in range(n) if v not in interior[0]} == {v for v in range(1, n, 2)}
+
+
+def _first_pair(par, a, b, c):
+    """Of three ranks holding the only non-zero contributions, the two whose
+    values are combined first in a tree reduce (own value first, then children
+    in ascending rank order): the pair with the deepest lowest common ancestor;
+    when all three share it, the ancestor's own value and the one in its
+    lower-ranked child's subtree."""
+    def chain(v):
+        out = [v]
+        while par[out[-1]] >= 0:
+            out.append(par[out[-1]])
+        return out
+
+    def lca(x, y):
+        cx = chain(x)
+        return next(v for v in chain(y) if v in cx)
+    pairs = [(a, b), (a, c), (b, c)]
+    depth = {p: len(chain(lca(*p))) for p in pairs}
+    deepest = max(depth.values())
+    best = [p for p in pairs if depth[p] == deepest]
+    if len(best) == 1:
+        return set(best[0])
+    m = lca(a, b)                                      # all three meet at m, in three slots
+    kids = sorted(v for v in range(len(par)) if par[v] == m)
+    slot = {}
+    for x in (a, b, c):
+        slot[x] = 0 if x == m else 1 + next(i for i, k in enumerate(kids) if m != x and k in chain(x))
+    order = sorted((a, b, c), key=slot.get)
+    return {order[0], order[1]}
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+def test_dtree_rounding_cases_on_both_halves(dtype):
+    """+B, -B, +1 on three ranks (zeros elsewhere): the result is 0 exactly when
+    +B and 1 are combined first.  Elements [0, u*floor(V/2)) follow the first
+    tree, the rest the second, including a ragged count."""
+    B = BIG[dtype]
+    u = 16 // (4 if dtype == "f32" else 2)
+    for n in (3, 5, 6, 8, 13, 14):
+        trees = [[_bit_trick_parent(n, v) for v in range(n)], [_second_tree_parent(n, v) for v in range(n)]]
+        for count in (u * 12, u * 13, u * 13 + 3):
+            rg = np.random.default_rng([n, count])
+            xs = [np.zeros(count) for _ in range(n)]
+            expect = np.zeros(count)
+            V = -(-count // u)
+            half = u * (V // 2)
+            place = []
+            for i in range(count):
+                pb, pn, p1 = (int(v) for v in rg.choice(n, size=3, replace=False))
+                xs[pb][i], xs[pn][i], xs[p1][i] = B, -B, 1.0
+                place.append((pb, pn, p1))
+                expect[i] = 0.0 if _first_pair(trees[0 if i < half else 1], pb, pn, p1) == {pb, p1} else 1.0
+            got = oracle.dtree_allreduce([to_dtype(x, dtype) for x in xs], dtype, "sum")
+            for y in got:
+                assert as_float(y, dtype).tolist() == expect.tolist(), (dtype, n, count)
+            # the cases tell the trees apart: the other tree predicts otherwise somewhere in each half
+            other = [0.0 if _first_pair(trees[1 if i < half else 0], pb, pn, p1) == {pb, p1} else 1.0
+                     for i, (pb, pn, p1) in enumerate(place)]
+            if n > 3:
+                assert other[:half] != expect[:half].tolist() and other[half:] != expect[half:].tolist(), (n, count)
+
+
+def test_dtree_first_half_is_the_single_tree():
+    for n in (2, 5, 8, 16, 72):
+        count = 4 * 40 + 3
+        xs = [workloads.normal(12, n, r, count, 1.0, "f32") for r in range(n)]
+        d = oracle.dtree_allreduce(xs, "f32", "sum")[0]
+        t = oracle.tree_allreduce(xs, "f32", "sum")[0]
+        half = 4 * ((-(-count // 4)) // 2)
+        assert d[:half].tobytes() == t[:half].tobytes()
+        if n > 2:
+            assert d[half:].tobytes() != t[half:].tobytes()
 
 
 # ---------------------------------------------------------------------------
