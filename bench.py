@@ -61,7 +61,7 @@ def parse():
 
 # The kernel each schedule launches at this shape (n = 8, 16-byte aligned buffers).
 KERNEL_OF = {"fused": "fused_allreduce_kernel", "ring": "ring_allreduce_fast", "tree": "tree_allreduce_fast",
-             "split": "split_allreduce_kernel"}
+             "split": "split_allreduce_kernel", "dtree": "tree_allreduce_fast"}
 
 
 def kernel_source_hash() -> str:
@@ -145,7 +145,7 @@ def sweep():
     ys = [torch.empty_like(x) for x in xs]
     xs, ys = ar.pointers(xs), ar.pointers(ys)          # host pointer tables built once, outside the timing
     out += ["## n = 4, fp32, 1024 elements per rank (latency regime)", "", "| schedule | us |", "|---|---|"]
-    for sched in ("fused", "ring", "tree", "split", "auto"):
+    for sched in ("fused", "ring", "tree", "split", "dtree", "auto"):
         out.append("| %s | %.2f |" % (sched, _median_us(lambda: ar.ar_allreduce(xs, ys, 1024, "f32", "sum", sched=sched))))
     out.append("")
 
@@ -175,8 +175,8 @@ def sweep():
     n = wl.C4_N
     out += ["## n = 16, int32, 1 KB .. 1 GB per rank: schedules, planner choice, measured winner", "",
             "Regime: n*S <= 256 MB fits the MI355X's 256 MB Infinity Cache (latency/cache regime); larger is HBM.", "",
-            "| bytes/rank | op | ring us | tree us | fused us | split us | planner | winner | toll % | best HBM GB/s | regime |",
-            "|---|---|---|---|---|---|---|---|---|---|---|"]
+            "| bytes/rank | op | ring us | tree us | dtree us | fused us | split us | planner | winner | toll % | best HBM GB/s "
+            "| regime |", "|---|---|---|---|---|---|---|---|---|---|---|---|"]
     agree = cells = near = 0
     for size in wl.C4_SIZES:
         count = size // 4
@@ -185,15 +185,16 @@ def sweep():
         xs, ys = ar.pointers(xs_t), ar.pointers(ys_t)
         for op in ("sum", "min", "max", "avg"):
             t = {s: _median_us(lambda: ar.ar_allreduce(xs, ys, count, "i32", op, n=n, sched=s))
-                 for s in ("ring", "tree", "fused", "split")}
+                 for s in ("ring", "tree", "dtree", "fused", "split")}
             plan = ar.ar_plan("allreduce", count, "i32", op, n).chosen
             win = min(t, key=t.get)
             toll = 100.0 * (t[plan] / t[win] - 1.0)
             cells += 1
             agree += plan == win
             near += toll <= 5.0
-            out.append("| %d | %s | %.1f | %.1f | %.1f | %.1f | %s | %s | %.1f | %.0f | %s |" % (
-                size, op, t["ring"], t["tree"], t["fused"], t["split"], plan, win, toll, 2 * n * size / t[win] / 1e3,
+            out.append("| %d | %s | %.1f | %.1f | %.1f | %.1f | %.1f | %s | %s | %.1f | %.0f | %s |" % (
+                size, op, t["ring"], t["tree"], t["dtree"], t["fused"], t["split"], plan, win, toll,
+                2 * n * size / t[win] / 1e3,
                 "cache" if n * size <= (256 << 20) else "HBM"))
         del xs, ys, xs_t, ys_t
         torch.cuda.empty_cache()
@@ -289,7 +290,7 @@ def main():
 
     detail = {}
     if not args.no_detail:
-        for sched in ("fused", "ring", "tree", "split"):
+        for sched in ("fused", "ring", "tree", "split", "dtree"):
             for op in ("sum", "avg"):
                 ms, lms, _ = time_calls(
                     lambda: ar.ar_allreduce(xs, ys, COUNT, "f32", op, sched=sched, stream=stream), 10, 2, stream)

@@ -33,6 +33,13 @@
  * their floating-point results are identical bit for bit.  The tree schedule
  * reduces up the bit-trick binary tree rooted at rank 0 (own value first,
  * then the children in ascending rank order) and broadcasts back down.
+ * The dtree schedule (all-reduce only) is the double binary tree: the first
+ * u*floor(V/2) elements (u, V below) are reduced up and broadcast down the
+ * tree above, the rest up its complement, whose leaves are the first tree's
+ * interior ranks: the mirror image (rank v in the place of rank n-1-v) when n
+ * is even, the same tree shifted by one rank (rank v in the place of rank
+ * v-1) when n is odd; each tree combines own value first, then the children
+ * in ascending rank order, and its root applies the postOp.
  * The split schedule (all-reduce only) is the fused single pass with every
  * rank combined at once, in the aligned pairwise order over rank indices:
  * ranks [lo, lo+len) combine as [lo, lo+h) (+) [lo+h, lo+len), h the largest
@@ -72,7 +79,7 @@
  * environment, which logs one line per planned call to stderr) and no
  * exception crosses the ABI.  count == 0 returns AR_OK without a launch.
  *
- * Environment: AR_SCHEDULE=auto|ring|tree|fused|split forces a schedule for calls
+ * Environment: AR_SCHEDULE=auto|ring|tree|fused|split|dtree forces a schedule for calls
  * made with AR_SCHED_AUTO; AR_CALIB=<path> names the cost-model calibration
  * file (default: calib_gfx950.txt beside the library); AR_GRID=<n> overrides
  * the number of workgroups per launch.
@@ -92,14 +99,21 @@ extern "C" {
 typedef enum {
     AR_OK = 0,
     AR_ERR_INVALID_ARG = 1,   /* null pointer, n out of range, bad enum, overlapping buffers */
-    AR_ERR_UNSUPPORTED = 2,   /* schedule not legal for this collective (tree, split for RS/AG) */
+    AR_ERR_UNSUPPORTED = 2,   /* schedule not legal for this collective (tree, split, dtree for RS/AG) */
     AR_ERR_ALIGNMENT = 3,     /* a pointer not aligned to the element size */
     AR_ERR_HIP = 4            /* the HIP runtime reported an error (launch, device query) */
 } ar_status_t;
 
 typedef enum { AR_FLOAT32 = 0, AR_BFLOAT16 = 1, AR_FLOAT16 = 2, AR_INT32 = 3 } ar_dtype_t;
 typedef enum { AR_SUM = 0, AR_PROD = 1, AR_MIN = 2, AR_MAX = 3, AR_AVG = 4 } ar_op_t;
-typedef enum { AR_SCHED_AUTO = 0, AR_SCHED_RING = 1, AR_SCHED_TREE = 2, AR_SCHED_FUSED = 3, AR_SCHED_SPLIT = 4 } ar_sched_t;
+typedef enum {
+    AR_SCHED_AUTO = 0,
+    AR_SCHED_RING = 1,
+    AR_SCHED_TREE = 2,
+    AR_SCHED_FUSED = 3,
+    AR_SCHED_SPLIT = 4,
+    AR_SCHED_DTREE = 5
+} ar_sched_t;
 typedef enum { AR_COLL_ALLREDUCE = 0, AR_COLL_REDUCE_SCATTER = 1, AR_COLL_ALL_GATHER = 2 } ar_coll_t;
 
 /* Result of the cost model, indexed by ar_sched_t (entry 0, AUTO, is unused).
@@ -109,9 +123,9 @@ typedef enum { AR_COLL_ALLREDUCE = 0, AR_COLL_REDUCE_SCATTER = 1, AR_COLL_ALL_GA
 typedef struct {
     ar_sched_t chosen;
     unsigned legal_mask;        /* bit s set when schedule s is legal for the call */
-    int steps[5];               /* dependent steps: ring 2(n-1) (n-1 for RS/AG), tree 2*depth, fused 1, split 1 */
-    double bytes[5];            /* algorithmic HBM bytes the schedule moves */
-    double predicted_us[5];     /* cost-model time; 0 for illegal schedules */
+    int steps[6];               /* dependent steps: ring 2(n-1) (n-1 for RS/AG), tree and dtree 2*depth, fused 1, split 1 */
+    double bytes[6];            /* algorithmic HBM bytes the schedule moves */
+    double predicted_us[6];     /* cost-model time; 0 for illegal schedules */
 } ar_plan_t;
 
 /* All-reduce ``count`` elements per rank.
@@ -129,7 +143,7 @@ ar_status_t ar_allreduce(const void *const *sendbufs, void *const *recvbufs, siz
  * receives recvcount elements (slice r of the combined result).
  * Source: "FSDP collectives 101", section "Why backward needs a different
  * collective"; the ring's reduce-scatter half. Schedules: ring, fused
- * (tree and split: AR_ERR_UNSUPPORTED). */
+ * (tree, split and dtree: AR_ERR_UNSUPPORTED). */
 ar_status_t ar_reduce_scatter(const void *const *sendbufs, void *const *recvbufs, size_t recvcount,
                               ar_dtype_t dtype, ar_op_t op, int n, ar_sched_t sched, hipStream_t stream);
 
@@ -137,7 +151,7 @@ ar_status_t ar_reduce_scatter(const void *const *sendbufs, void *const *recvbufs
  * n*sendcount elements (x_0 || x_1 || ... || x_{n-1}).
  * Source: "FSDP collectives 101", section "All-gather: everyone shows their
  * piece"; the ring's all-gather half. Schedules: ring, fused
- * (tree and split: AR_ERR_UNSUPPORTED). */
+ * (tree, split and dtree: AR_ERR_UNSUPPORTED). */
 ar_status_t ar_all_gather(const void *const *sendbufs, void *const *recvbufs, size_t sendcount,
                           ar_dtype_t dtype, int n, ar_sched_t sched, hipStream_t stream);
 
@@ -153,6 +167,13 @@ ar_status_t ar_plan(ar_coll_t coll, size_t count, ar_dtype_t dtype, ar_op_t op, 
  * (-1 for the root, rank 0, or for v outside [0, n)).  Host only.
  * Source: "NCCL all-reduce", section "The double binary tree". */
 int ar_tree_parent(int n, int v);
+
+/* Parent of rank v in tree ``which`` of the dtree schedule (0: the tree of
+ * ar_tree_parent; 1: its complement, the mirror image for even n or the
+ * one-rank shift for odd n); -1 for that tree's root or for v outside
+ * [0, n).  Host only.  Source: "NCCL all-reduce", section "The double binary
+ * tree" (a second tree with the roles of leaves and interior ranks swapped). */
+int ar_dtree_parent(int n, int which, int v);
 
 /* Human-readable name of a status code (static storage). */
 const char *ar_status_string(ar_status_t s);

@@ -5,8 +5,8 @@ This package is a thin ctypes binding over ``libar.so`` (HIP kernels for
 gfx950 plus the C ABI declared in ``include/ar.h``).  The functions keep the C
 names and only marshal arguments: every step of the collective runs in the
 library's kernels.  There is no CPU fallback; importing the package fails
-loudly when the library has not been built (``python -m
-reduce_scatter_amd.build``).
+loudly when the library has not been built (``python
+reduce_scatter_amd/build.py``).
 """
 from __future__ import annotations
 
@@ -25,6 +25,7 @@ from ._binding import (  # noqa: F401
     ar_reduce_scatter,
     ar_status_string,
     ar_tree_parent,
+    ar_dtree_parent,
     library_path,
     pointers,
 )
@@ -35,6 +36,7 @@ __all__ = [
     "ar_all_gather",
     "ar_plan",
     "ar_tree_parent",
+    "ar_dtree_parent",
     "ar_status_string",
     "ArError",
     "Plan",

@@ -17,13 +17,13 @@ _LIB_PATH = os.path.join(_HERE, "libar.so")
 AR_MAX_RANKS = 128
 DTYPES = {"f32": 0, "bf16": 1, "f16": 2, "i32": 3}
 OPS = {"sum": 0, "prod": 1, "min": 2, "max": 3, "avg": 4}
-SCHEDS = {"auto": 0, "ring": 1, "tree": 2, "fused": 3, "split": 4}
+SCHEDS = {"auto": 0, "ring": 1, "tree": 2, "fused": 3, "split": 4, "dtree": 5}
 COLLS = {"allreduce": 0, "reduce_scatter": 1, "all_gather": 2}
 _SCHED_NAMES = {v: k for k, v in SCHEDS.items()}
 _STATUS = {0: "AR_OK", 1: "AR_ERR_INVALID_ARG", 2: "AR_ERR_UNSUPPORTED", 3: "AR_ERR_ALIGNMENT", 4: "AR_ERR_HIP"}
 
 if not os.path.exists(_LIB_PATH):
-    raise ImportError("libar.so is not built (expected at %s); build it with `python -m reduce_scatter_amd.build` "
+    raise ImportError("libar.so is not built (expected at %s); build it with `python reduce_scatter_amd/build.py` "
                       "or __graft_entry__.build()" % _LIB_PATH)
 
 # One HIP runtime per process: PyTorch-ROCm ships its own libamdhip64 (same
@@ -40,8 +40,8 @@ _lib = ctypes.CDLL(_LIB_PATH)
 
 
 class _PlanStruct(ctypes.Structure):
-    _fields_ = [("chosen", ctypes.c_int), ("legal_mask", ctypes.c_uint), ("steps", ctypes.c_int * 5),
-                ("bytes", ctypes.c_double * 5), ("predicted_us", ctypes.c_double * 5)]
+    _fields_ = [("chosen", ctypes.c_int), ("legal_mask", ctypes.c_uint), ("steps", ctypes.c_int * 6),
+                ("bytes", ctypes.c_double * 6), ("predicted_us", ctypes.c_double * 6)]
 
 
 _vpp = ctypes.POINTER(ctypes.c_void_p)
@@ -54,6 +54,8 @@ _lib.ar_plan.argtypes = [ctypes.c_int, ctypes.c_size_t, ctypes.c_int, ctypes.c_i
                          ctypes.POINTER(_PlanStruct)]
 _lib.ar_tree_parent.argtypes = [ctypes.c_int, ctypes.c_int]
 _lib.ar_tree_parent.restype = ctypes.c_int
+_lib.ar_dtree_parent.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+_lib.ar_dtree_parent.restype = ctypes.c_int
 _lib.ar_status_string.argtypes = [ctypes.c_int]
 _lib.ar_status_string.restype = ctypes.c_char_p
 for _f in (_lib.ar_allreduce, _lib.ar_reduce_scatter, _lib.ar_all_gather, _lib.ar_plan):
@@ -199,3 +201,7 @@ def ar_plan(coll, count, dtype, op, n) -> Plan:
 
 def ar_tree_parent(n: int, v: int) -> int:
     return int(_lib.ar_tree_parent(n, v))
+
+
+def ar_dtree_parent(n: int, which: int, v: int) -> int:
+    return int(_lib.ar_dtree_parent(n, which, v))

@@ -1,6 +1,7 @@
 """Build ``libar.so`` (the HIP kernels and the C ABI) for gfx950 with hipcc.
 
-``python -m reduce_scatter_amd.build`` or ``reduce_scatter_amd.build.build()``.
+``python reduce_scatter_amd/build.py`` (by path: it imports nothing from the
+package, whose import would load the library being replaced).
 Objects are compiled in parallel into ``reduce_scatter_amd/_build/`` and
 linked into ``reduce_scatter_amd/libar.so``.
 """

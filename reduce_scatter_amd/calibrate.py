@@ -76,10 +76,10 @@ def measure(ns, sizes, iters):
             outs_t = [torch.empty(R, device="cuda") for _ in range(n)]
             # host pointer tables built once: the timings are the library's, not Python's marshalling
             xs, ys, outs = ar.pointers(xs_t), ar.pointers(ys_t), ar.pointers(outs_t)
-            for sched in ("ring", "tree", "fused", "split"):
+            for sched in ("ring", "tree", "fused", "split", "dtree"):
                 us = time_call(lambda: ar.ar_allreduce(xs, ys, count, "f32", "sum", n=n, sched=sched), iters)
                 rows.append(("allreduce", sched, n, per_rank, us))
-                if sched in ("tree", "split"):
+                if sched in ("tree", "split", "dtree"):
                     continue
                 us = time_call(lambda: ar.ar_reduce_scatter(xs, outs, R, "f32", "sum", n=n, sched=sched), iters)
                 rows.append(("reduce_scatter", sched, n, per_rank, us))
@@ -103,7 +103,7 @@ def fit(rows):
     stays in the 256 MB Infinity Cache."""
     out = {}
     for coll in COLLS:
-        for sched in ("ring", "tree", "fused", "split"):
+        for sched in ("ring", "tree", "fused", "split", "dtree"):
             pts = [(n, pr, us, _bytes(coll, n, pr)) for c, s, n, pr, us in rows if c == coll and s == sched]
             if not pts:
                 continue

@@ -23,12 +23,12 @@ namespace {
 
 const char *kDtypeName[] = {"fp32", "bf16", "fp16", "int32"};
 const char *kOpName[] = {"sum", "prod", "min", "max", "avg"};
-const char *kSchedName[] = {"AUTO", "RING", "TREE", "FUSED", "SPLIT"};
+const char *kSchedName[] = {"AUTO", "RING", "TREE", "FUSED", "SPLIT", "DTREE"};
 const char *kCollName[] = {"AllReduce", "ReduceScatter", "AllGather"};
 
 bool valid_dtype(int d) { return d >= AR_FLOAT32 && d <= AR_INT32; }
 bool valid_op(int o) { return o >= AR_SUM && o <= AR_AVG; }
-bool valid_sched(int s) { return s >= AR_SCHED_AUTO && s <= AR_SCHED_SPLIT; }
+bool valid_sched(int s) { return s >= AR_SCHED_AUTO && s <= AR_SCHED_DTREE; }
 
 bool debug_enabled() {
     static int v = -1;
@@ -46,6 +46,7 @@ ar_sched_t forced_schedule() {
     if (!strcmp(e, "tree")) return AR_SCHED_TREE;
     if (!strcmp(e, "fused")) return AR_SCHED_FUSED;
     if (!strcmp(e, "split")) return AR_SCHED_SPLIT;
+    if (!strcmp(e, "dtree")) return AR_SCHED_DTREE;
     return AR_SCHED_AUTO;
 }
 
@@ -184,11 +185,12 @@ void log_plan(ar_coll_t coll, size_t bytes_per_rank, int n, int dtype, int op, c
               bool forced) {
     if (!debug_enabled()) return;
     fprintf(stderr,
-            "[ar] %s: %zu Bytes x n=%d %s %s -> %s%s (predicted us: ring %.2f tree %.2f fused %.2f split %.2f; "
-            "calib %s)\n",
+            "[ar] %s: %zu Bytes x n=%d %s %s -> %s%s (predicted us: ring %.2f tree %.2f fused %.2f split %.2f "
+            "dtree %.2f; calib %s)\n",
             kCollName[coll], bytes_per_rank, n, kDtypeName[dtype], kOpName[op], kSchedName[used],
             forced ? " (forced)" : "", p.predicted_us[AR_SCHED_RING], p.predicted_us[AR_SCHED_TREE],
-            p.predicted_us[AR_SCHED_FUSED], p.predicted_us[AR_SCHED_SPLIT], calib_source());
+            p.predicted_us[AR_SCHED_FUSED], p.predicted_us[AR_SCHED_SPLIT], p.predicted_us[AR_SCHED_DTREE],
+            calib_source());
 }
 
 // Resolve AR_SCHED_AUTO (and the AR_SCHEDULE override) into a legal schedule.
@@ -249,6 +251,10 @@ const char *ar_status_string(ar_status_t s) {
 
 int ar_tree_parent(int n, int v) { return (n >= 1 && n <= AR_MAX_RANKS) ? tree_parent(n, v) : -1; }
 
+int ar_dtree_parent(int n, int which, int v) {
+    return (n >= 1 && n <= AR_MAX_RANKS && (which == 0 || which == 1)) ? dtree_parent(n, which, v) : -1;
+}
+
 ar_status_t ar_plan(ar_coll_t coll, size_t count, ar_dtype_t dtype, ar_op_t op, int n, ar_plan_t *out) {
     if (!out || n < 1 || n > AR_MAX_RANKS || !valid_dtype(dtype) || !valid_op(op) || (int)coll < 0 ||
         (int)coll > AR_COLL_ALL_GATHER)
@@ -288,11 +294,19 @@ ar_status_t ar_allreduce(const void *const *sendbufs, void *const *recvbufs, siz
     g.q = g.V / n;
     g.rem = (int)(g.V % n);
     g.ref = (long long)((uintptr_t)recvbufs[0] >> 4);          // fused / split tiles follow rank 0's output
-    TreeShape tree;
-    if (use == AR_SCHED_TREE) tree_build(n, tree);
+    TreeShape tree, tree2;
+    if (use == AR_SCHED_TREE || use == AR_SCHED_DTREE) tree_build(n, tree, 0);
+    if (use == AR_SCHED_DTREE) tree_build(n, tree2, 1);
+    g.split = g.V / 2;                                          // dtree: vectors up the first tree (<= Vfull)
 
     auto elem = [&](long long e_begin) {
         if (use == AR_SCHED_TREE) return launch_elem_tree_allreduce(dtype, op, t, tree, g, e_begin, (long long)count, stream);
+        if (use == AR_SCHED_DTREE) {                                // two element ranges, one per tree
+            const long long cut = g.split * lanes;
+            hipError_t e1 = launch_elem_tree_allreduce(dtype, op, t, tree, g, e_begin, cut > e_begin ? cut : e_begin, stream);
+            if (e1 != hipSuccess) return e1;
+            return launch_elem_tree_allreduce(dtype, op, t, tree2, g, cut > e_begin ? cut : e_begin, (long long)count, stream);
+        }
         if (use == AR_SCHED_SPLIT) return launch_elem_split_allreduce(dtype, op, t, g, e_begin, (long long)count, stream);
         return launch_elem_ring_allreduce(dtype, op, t, g, e_begin, (long long)count, stream);
     };
@@ -312,6 +326,10 @@ ar_status_t ar_allreduce(const void *const *sendbufs, void *const *recvbufs, siz
             const long long maxlen = (g.V + n - 1) / n;
             g.windows = (maxlen + g.W - 1) / g.W;
             h = launch_ring_allreduce(dtype, op, t, g, grid_for(g.windows, cus, 4), ring_lds_bytes(AR_COLL_ALLREDUCE), stream);
+        } else if (use == AR_SCHED_DTREE) {
+            g.W = lds_window(n);
+            g.windows = (g.split + g.W - 1) / g.W + (g.Vfull - g.split + g.W - 1) / g.W;
+            h = launch_dtree_allreduce(dtype, op, t, tree, tree2, g, grid_for(g.windows, cus, 4), stream);
         } else {
             g.W = lds_window(n);
             g.windows = (g.Vfull + g.W - 1) / g.W;

@@ -9,7 +9,8 @@
 namespace ar {
 
 int tree_parent(int n, int v);
-void tree_build(int n, TreeShape &t);
+int dtree_parent(int n, int which, int v);
+void tree_build(int n, TreeShape &t, int which = 0);
 size_t elem_size(int dtype);
 ar_status_t make_plan(ar_coll_t coll, size_t count, ar_dtype_t dtype, ar_op_t op, int n, ar_plan_t *out);
 const char *calib_source();

@@ -33,6 +33,7 @@ struct Geometry {
     int W;              // ring/tree: vectors per rank in one LDS window
     float s;            // fp32(1/n), the float avg pre-scale
     long long ref;      // fused / split: address / 16 of the buffer whose alignment cuts the tiles
+    long long split;    // double tree: vectors [0, split) go up the first tree, the rest up the second
 };
 
 // Tiles are cut on a grid aligned to absolute T-vector boundaries of a
@@ -67,14 +68,16 @@ __device__ __forceinline__ unsigned tile_lane(const TileSpan &ts, long long v, b
 // Tiles needed for a range of len vectors, whatever its alignment.
 inline long long aligned_tiles(long long len, long long T) { return len > 0 ? (len + T - 1) / T + 1 : 0; }
 
-// The tree schedule's shape, host-built: depth, parent and up to two
-// children per rank (-1 = none); post[] lists ranks children-first.
+// A tree schedule's shape, host-built: depth, parent and up to two children
+// per rank (-1 = none, in ascending rank order), the root, and post[] listing
+// the ranks children-first.
 struct TreeShape {
     int8_t depth[kTableRanks];
     int8_t parent[kTableRanks];
     int8_t child[kTableRanks][2];
     uint8_t post[kTableRanks];
     int max_depth;
+    int root;
 };
 
 // Launchers.  dt / op use the ar_dtype_t / ar_op_t numbering.  ``grid`` is
@@ -96,8 +99,12 @@ hipError_t launch_ring_allreduce(int dt, int op, const RankTable &t, const Geome
 hipError_t launch_ring_reduce_scatter(int dt, int op, const RankTable &t, const Geometry &g, int grid, int lds,
                                       hipStream_t s);
 hipError_t launch_ring_all_gather(const RankTable &t, const Geometry &g, int grid, int lds, hipStream_t s);
+// Tree: one shape over all of [0, Vfull); double tree: ``tree`` over vectors
+// [0, g.split) and ``tree2`` over [g.split, Vfull), in one launch.
 hipError_t launch_tree_allreduce(int dt, int op, const RankTable &t, const TreeShape &tree, const Geometry &g,
                                  int grid, int lds, hipStream_t s);
+hipError_t launch_dtree_allreduce(int dt, int op, const RankTable &t, const TreeShape &tree, const TreeShape &tree2,
+                                  const Geometry &g, int grid, hipStream_t s);
 // Element-wise paths (any alignment, and the all-reduce tail), elements
 // [e_begin, e_end) of every rank buffer / slice:
 hipError_t launch_elem_ring_allreduce(int dt, int op, const RankTable &t, const Geometry &g, long long e_begin,

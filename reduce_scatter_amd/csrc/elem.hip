@@ -59,7 +59,7 @@ __global__ __launch_bounds__(kThreads) void elem_tree_allreduce_kernel(const Ran
             }
             part[v] = acc;
         }
-        const typename Pack<DT>::T root = post1<DT, OP>(part[0], n);
+        const typename Pack<DT>::T root = post1<DT, OP>(part[tree.root], n);
         for (int v = 0; v < n; ++v) store1<DT>(t.dst[v], e, root);
     }
 }

@@ -12,8 +12,9 @@
 //
 //   steps:  ring 2(n-1) for all-reduce, n-1 for reduce-scatter / all-gather
 //           (section "The ring, exactly as the kernel runs it"); tree
-//           2 * depth (section "The double binary tree"); fused 1; split 1
-//           (one pass; its log-depth combine stays inside a workgroup).
+//           2 * depth (section "The double binary tree"), the same for the
+//           double tree; fused 1; split 1 (one pass; its log-depth combine
+//           stays inside a workgroup).
 //   bytes:  the algorithmic HBM bytes.  All three schedules keep partial
 //           results on chip, so each moves 2*n*S for an all-reduce of S bytes
 //           per rank, (n+1)*n*R*e for reduce-scatter and all-gather.
@@ -22,7 +23,7 @@
 //           section: the clean model does not fit medium sizes, so a
 //           per-size factor is applied), indexed by the call's total bytes.
 //
-// Legality: the tree and split schedules exist for all-reduce only.
+// Legality: the tree, double-tree and split schedules exist for all-reduce only.
 //
 // Constants come from a calibration file (AR_CALIB, default
 // calib_gfx950.txt beside the library) written by the package's calibration
@@ -44,7 +45,7 @@ namespace ar {
 namespace {
 
 constexpr int kColls = 3;
-constexpr int kScheds = 5;         // indexed by ar_sched_t; 0 (auto) unused
+constexpr int kScheds = 6;         // indexed by ar_sched_t; 0 (auto) unused
 constexpr int kSizeBins = 48;      // per-size correction for log2(algorithmic bytes of the call) = 0..47
 
 constexpr int kRankClasses = 8;    // ceil(log2 n) = 0..7 for n = 1..128
@@ -97,6 +98,7 @@ int sched_index(const char *s) {
     if (!strcmp(s, "tree")) return AR_SCHED_TREE;
     if (!strcmp(s, "fused")) return AR_SCHED_FUSED;
     if (!strcmp(s, "split")) return AR_SCHED_SPLIT;
+    if (!strcmp(s, "dtree")) return AR_SCHED_DTREE;
     return -1;
 }
 
@@ -114,7 +116,7 @@ std::string library_dir() {
 //   <coll> <sched> <launch_us> <step_us> <bw_gbps>
 //   corr <coll> <sched> <rank class> <corr_0 ... corr_47>
 //   lat <coll> <sched> <rank class> <extra_us>
-// coll in {allreduce, reduce_scatter, all_gather}, sched in {ring, tree, fused, split};
+// coll in {allreduce, reduce_scatter, all_gather}, sched in {ring, tree, fused, split, dtree};
 // rank class = ceil(log2 n); corr_b multiplies the bandwidth for calls that
 // move 2^b .. 2^(b+1)-1 algorithmic bytes in total (the footprint decides
 // whether the data stays in the 256 MB Infinity Cache, and how that bends the
@@ -203,22 +205,41 @@ int tree_parent(int n, int v) {
     return p;
 }
 
-void tree_build(int n, TreeShape &t) {
+// The double binary tree's second tree (section "The double binary tree":
+// the roles of leaves and interior ranks swapped): the mirror image of the
+// first when n is even (rank v takes rank n-1-v's place), the first shifted by
+// one rank when n is odd (rank v takes rank v-1's place).  which = 0 is the
+// first tree.
+int dtree_parent(int n, int which, int v) {
+    if (v < 0 || v >= n) return -1;
+    if (which == 0) return tree_parent(n, v);
+    if (n % 2 == 0) {
+        const int p = tree_parent(n, n - 1 - v);
+        return p < 0 ? -1 : n - 1 - p;
+    }
+    const int p = tree_parent(n, (v + n - 1) % n);
+    return p < 0 ? -1 : (p + 1) % n;
+}
+
+void tree_build(int n, TreeShape &t, int which) {
     memset(&t, 0, sizeof t);
     for (int v = 0; v < kTableRanks; ++v) {
         t.parent[v] = -1;
         t.child[v][0] = t.child[v][1] = -1;
     }
     t.max_depth = 0;
+    t.root = 0;
     for (int v = 0; v < n; ++v) {
         int d = 0;
-        for (int p = v; p != 0; p = tree_parent(n, p)) ++d;
+        for (int p = dtree_parent(n, which, v); p >= 0; p = dtree_parent(n, which, p)) ++d;
         t.depth[v] = (int8_t)d;
         if (d > t.max_depth) t.max_depth = d;
-        t.parent[v] = (int8_t)tree_parent(n, v);
+        t.parent[v] = (int8_t)dtree_parent(n, which, v);
+        if (t.parent[v] < 0) t.root = v;
     }
-    for (int v = 1; v < n; ++v) {                   // children in ascending rank order
-        int p = t.parent[v];
+    for (int v = 0; v < n; ++v) {                   // children in ascending rank order
+        const int p = t.parent[v];
+        if (p < 0) continue;
         if (t.child[p][0] < 0) t.child[p][0] = (int8_t)v;
         else t.child[p][1] = (int8_t)v;
     }
@@ -246,18 +267,20 @@ ar_status_t make_plan(ar_coll_t coll, size_t count, ar_dtype_t dtype, ar_op_t op
     int depth = 0;                                  // the bit-trick tree over n ranks is ceil(log2 n) deep
     while ((1 << depth) < n) ++depth;
     out->legal_mask = (1u << AR_SCHED_RING) | (1u << AR_SCHED_FUSED);
-    if (coll == AR_COLL_ALLREDUCE) out->legal_mask |= (1u << AR_SCHED_TREE) | (1u << AR_SCHED_SPLIT);
+    if (coll == AR_COLL_ALLREDUCE)
+        out->legal_mask |= (1u << AR_SCHED_TREE) | (1u << AR_SCHED_SPLIT) | (1u << AR_SCHED_DTREE);
     out->steps[AR_SCHED_RING] = (coll == AR_COLL_ALLREDUCE) ? 2 * (n - 1) : (n - 1);
     out->steps[AR_SCHED_TREE] = (coll == AR_COLL_ALLREDUCE) ? 2 * depth : 0;
     out->steps[AR_SCHED_FUSED] = 1;
     out->steps[AR_SCHED_SPLIT] = (coll == AR_COLL_ALLREDUCE) ? 1 : 0;
+    out->steps[AR_SCHED_DTREE] = out->steps[AR_SCHED_TREE];
     double best = 0;
     out->chosen = AR_SCHED_FUSED;
     bool have = false;
     (void)per_rank;
     const int bin = size_bin(bytes);
     const int rclass = rank_class(n);
-    for (int s = AR_SCHED_RING; s <= AR_SCHED_SPLIT; ++s) {
+    for (int s = AR_SCHED_RING; s <= AR_SCHED_DTREE; ++s) {
         if (!(out->legal_mask & (1u << s))) continue;
         const Entry &c = g_calib.e[coll][s];
         out->bytes[s] = bytes;

@@ -17,15 +17,70 @@
 // copies its parent's final value and stores it.  A workgroup barrier
 // separates the levels.  All of a rank's loads are issued at the start
 // (nothing they read depends on the tree), so the levels only wait on LDS.
+//
+// The double binary tree (same section: a second tree with the roles of
+// leaves and interior ranks swapped, and half of every buffer sent up each)
+// uses the same kernels with two host-built shapes: the windows of the first
+// half take the first tree, those of the second half its complement.  On one
+// GPU there are no per-rank links to balance, so it costs what the single tree
+// costs; its results differ from the single tree's in the second half.
 #include "ar_device.hpp"
 #include "ar_kernels.hpp"
 #include "dispatch.hpp"
 
 namespace ar {
 
+// One window of the generic kernel: vectors [pos0, pos0 + W) of every rank,
+// clipped to hi, reduced up ``tree`` and broadcast down it.
 template <int DT, int OP>
-__global__ __launch_bounds__(kThreads) void tree_allreduce_kernel(const RankTable t, const TreeShape tree,
-                                                                  const Geometry g) {
+__device__ __forceinline__ void tree_window(const RankTable &t, const TreeShape &tree, const Geometry &g,
+                                            long long pos0, long long hi, const int *r, const int *w, int cnt,
+                                            u32x4 *slot) {
+    const int n = g.n, W = g.W;
+    u32x4 own[kItemsPerThread];
+    bool ok[kItemsPerThread];
+#pragma unroll
+    for (int k = 0; k < kItemsPerThread; ++k) {
+        ok[k] = k < cnt && pos0 + w[k] < hi;
+        if (ok[k]) own[k] = ld_stream(t.src[r[k]], pos0 + w[k]);
+    }
+    // up: deepest level first
+    for (int d = tree.max_depth; d >= 0; --d) {
+#pragma unroll
+        for (int k = 0; k < kItemsPerThread; ++k) {
+            if (!ok[k] || tree.depth[r[k]] != d) continue;
+            const int v = r[k];
+            Pack<DT> acc = first<DT, OP>(unpack<DT>(own[k]), g.s);
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int ch = tree.child[v][e];
+                if (ch >= 0) merge<DT, OP>(acc, unpack<DT>(slot[ch * W + w[k]]));
+            }
+            if (v == tree.root) post<DT, OP>(acc, n);
+            slot[v * W + w[k]] = pack<DT>(acc);
+        }
+        __syncthreads();
+    }
+    // down: the root keeps its value; each level copies from its parent
+    for (int d = 0; d <= tree.max_depth; ++d) {
+#pragma unroll
+        for (int k = 0; k < kItemsPerThread; ++k) {
+            if (!ok[k] || tree.depth[r[k]] != d) continue;
+            const int v = r[k];
+            const u32x4 val = (v == tree.root) ? slot[v * W + w[k]] : slot[tree.parent[v] * W + w[k]];
+            slot[v * W + w[k]] = val;
+            st_stream(t.dst[v], pos0 + w[k], val);
+        }
+        __syncthreads();
+    }
+}
+
+// Any n: a persistent grid walks the windows.  A single tree takes the
+// windows of [0, Vfull); the double tree (DUAL) takes the windows of
+// [0, g.split) up the first tree and those of [g.split, Vfull) up the second.
+template <int DT, int OP, bool DUAL>
+__global__ __launch_bounds__(kThreads) void tree_allreduce_kernel(const RankTable t, const TreeShape tree0,
+                                                                  const TreeShape tree1, const Geometry g) {
     extern __shared__ __align__(16) unsigned char lds[];
     const int n = g.n, W = g.W;
     u32x4 *slot = (u32x4 *)lds;
@@ -41,44 +96,10 @@ __global__ __launch_bounds__(kThreads) void tree_allreduce_kernel(const RankTabl
             cnt = k + 1;
         }
     }
+    const long long first = DUAL ? (g.split + W - 1) / W : g.windows;     // windows of the first tree
     for (long long win = blockIdx.x; win < g.windows; win += gridDim.x) {
-        const long long pos0 = win * W;
-        u32x4 own[kItemsPerThread];
-        bool ok[kItemsPerThread];
-#pragma unroll
-        for (int k = 0; k < kItemsPerThread; ++k) {
-            ok[k] = k < cnt && pos0 + w[k] < g.Vfull;
-            if (ok[k]) own[k] = ld_stream(t.src[r[k]], pos0 + w[k]);
-        }
-        // up: deepest level first
-        for (int d = tree.max_depth; d >= 0; --d) {
-#pragma unroll
-            for (int k = 0; k < kItemsPerThread; ++k) {
-                if (!ok[k] || tree.depth[r[k]] != d) continue;
-                const int v = r[k];
-                Pack<DT> acc = first<DT, OP>(unpack<DT>(own[k]), g.s);
-#pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    const int ch = tree.child[v][e];
-                    if (ch >= 0) merge<DT, OP>(acc, unpack<DT>(slot[ch * W + w[k]]));
-                }
-                if (v == 0) post<DT, OP>(acc, n);
-                slot[v * W + w[k]] = pack<DT>(acc);
-            }
-            __syncthreads();
-        }
-        // down: the root keeps its value; each level copies from its parent
-        for (int d = 0; d <= tree.max_depth; ++d) {
-#pragma unroll
-            for (int k = 0; k < kItemsPerThread; ++k) {
-                if (!ok[k] || tree.depth[r[k]] != d) continue;
-                const int v = r[k];
-                u32x4 val = (v == 0) ? slot[w[k]] : slot[tree.parent[v] * W + w[k]];
-                slot[v * W + w[k]] = val;
-                st_stream(t.dst[v], pos0 + w[k], val);
-            }
-            __syncthreads();
-        }
+        if (win < first) tree_window<DT, OP>(t, tree0, g, win * W, DUAL ? g.split : g.Vfull, r, w, cnt, slot);
+        else tree_window<DT, OP>(t, tree1, g, g.split + (win - first) * W, g.Vfull, r, w, cnt, slot);
     }
 }
 
@@ -91,23 +112,22 @@ __global__ __launch_bounds__(kThreads) void tree_allreduce_kernel(const RankTabl
 constexpr int kTreeK = 8;
 
 template <int DT, int OP, int NR>
-__global__ __launch_bounds__(kThreads) void tree_allreduce_fast(const RankTable t, const TreeShape tree,
-                                                                const Geometry g) {
+__device__ __forceinline__ void tree_window_fast(const RankTable &t, const TreeShape &tree, const Geometry &g,
+                                                 long long lo, long long hi, long long win, u32x4 *slot) {
     constexpr int TPR = kThreads / NR;             // threads per rank
     constexpr int W = TPR * kTreeK;                // vectors per rank per window
-    __shared__ u32x4 slot[NR * W];
     const int r = threadIdx.x / TPR, sub = threadIdx.x % TPR;
-    const long long pos0 = (long long)blockIdx.x * W + sub;
+    const long long pos0 = lo + win * W + sub;
     u32x4 own[kTreeK];
     bool ok[kTreeK];
 #pragma unroll
     for (int k = 0; k < kTreeK; ++k) {
         const long long v = pos0 + (long long)k * TPR;
-        ok[k] = v < g.Vfull;
-        own[k] = ld_stream(t.src[r], ok[k] ? v : 0);
+        ok[k] = v < hi;
+        own[k] = ld_stream(t.src[r], ok[k] ? v : lo);          // past hi: a valid, ignored load
     }
     __builtin_amdgcn_sched_barrier(0);
-    const int d = tree.depth[r];
+    const int d = tree.depth[r], root = tree.root;
     const int ch0 = tree.child[r][0], ch1 = tree.child[r][1], par = tree.parent[r];
     for (int lev = tree.max_depth; lev >= 0; --lev) {          // up: deepest level first
         if (d == lev) {
@@ -118,7 +138,7 @@ __global__ __launch_bounds__(kThreads) void tree_allreduce_fast(const RankTable 
                 Pack<DT> acc = first<DT, OP>(unpack<DT>(own[k]), g.s);
                 if (ch0 >= 0) merge<DT, OP>(acc, unpack<DT>(slot[ch0 * W + i]));
                 if (ch1 >= 0) merge<DT, OP>(acc, unpack<DT>(slot[ch1 * W + i]));
-                if (r == 0) post<DT, OP>(acc, NR);
+                if (r == root) post<DT, OP>(acc, NR);
                 slot[r * W + i] = pack<DT>(acc);
             }
         }
@@ -130,7 +150,7 @@ __global__ __launch_bounds__(kThreads) void tree_allreduce_fast(const RankTable 
             for (int k = 0; k < kTreeK; ++k) {
                 if (!ok[k]) continue;
                 const int i = sub + k * TPR;
-                const u32x4 val = (r == 0) ? slot[i] : slot[par * W + i];
+                const u32x4 val = (r == root) ? slot[r * W + i] : slot[par * W + i];
                 slot[r * W + i] = val;
                 st_stream(t.dst[r], pos0 + (long long)k * TPR, val);
             }
@@ -139,15 +159,29 @@ __global__ __launch_bounds__(kThreads) void tree_allreduce_fast(const RankTable 
     }
 }
 
-hipError_t launch_tree_allreduce(int dt, int op, const RankTable &t, const TreeShape &tree, const Geometry &g,
-                                 int grid, int lds, hipStream_t s) {
+template <int DT, int OP, int NR, bool DUAL>
+__global__ __launch_bounds__(kThreads) void tree_allreduce_fast(const RankTable t, const TreeShape tree0,
+                                                                const TreeShape tree1, const Geometry g) {
+    constexpr int W = (kThreads / NR) * kTreeK;
+    __shared__ u32x4 slot[NR * W];
+    const long long first = DUAL ? (g.split + W - 1) / W : (long long)gridDim.x;   // windows of the first tree
+    const long long win = blockIdx.x;
+    if (win < first) tree_window_fast<DT, OP, NR>(t, tree0, g, 0, DUAL ? g.split : g.Vfull, win, slot);
+    else tree_window_fast<DT, OP, NR>(t, tree1, g, g.split, g.Vfull, win - first, slot);
+}
+
+template <bool DUAL>
+hipError_t launch_trees(int dt, int op, const RankTable &t, const TreeShape &tree, const TreeShape &tree2,
+                        const Geometry &g, int grid, int lds, hipStream_t s) {
     if (g.n == 2 || g.n == 4 || g.n == 8 || g.n == 16) {
         const long long W = (kThreads / g.n) * kTreeK;
-        const dim3 blocks((unsigned)((g.Vfull + W - 1) / W));
+        const long long windows =
+            DUAL ? (g.split + W - 1) / W + (g.Vfull - g.split + W - 1) / W : (g.Vfull + W - 1) / W;
+        const dim3 blocks((unsigned)windows);
         return dispatch(dt, op, [&](auto D, auto O) {
             auto go = [&](auto R) {
-                return launch(tree_allreduce_fast<decltype(D)::value, decltype(O)::value, decltype(R)::value>, blocks,
-                              dim3(kThreads), (size_t)lds, s, t, tree, g);
+                return launch(tree_allreduce_fast<decltype(D)::value, decltype(O)::value, decltype(R)::value, DUAL>,
+                              blocks, dim3(kThreads), (size_t)lds, s, t, tree, tree2, g);
             };
             switch (g.n) {
             case 2: return go(std::integral_constant<int, 2>{});
@@ -158,9 +192,19 @@ hipError_t launch_tree_allreduce(int dt, int op, const RankTable &t, const TreeS
         });
     }
     return dispatch(dt, op, [&](auto D, auto O) {
-        return launch(tree_allreduce_kernel<decltype(D)::value, decltype(O)::value>, dim3(grid), dim3(kThreads),
-                      (size_t)g.n * g.W * 16, s, t, tree, g);
+        return launch(tree_allreduce_kernel<decltype(D)::value, decltype(O)::value, DUAL>, dim3(grid), dim3(kThreads),
+                      (size_t)g.n * g.W * 16, s, t, tree, tree2, g);
     });
+}
+
+hipError_t launch_tree_allreduce(int dt, int op, const RankTable &t, const TreeShape &tree, const Geometry &g,
+                                 int grid, int lds, hipStream_t s) {
+    return launch_trees<false>(dt, op, t, tree, tree, g, grid, lds, s);
+}
+
+hipError_t launch_dtree_allreduce(int dt, int op, const RankTable &t, const TreeShape &tree, const TreeShape &tree2,
+                                  const Geometry &g, int grid, hipStream_t s) {
+    return launch_trees<true>(dt, op, t, tree, tree2, g, grid, 0, s);
 }
 
 }  // namespace ar

@@ -52,14 +52,14 @@ def test_invalid_arguments_are_rejected_before_launch():
     assert _err(ar.ar_allreduce, A[:2], B[:2], 16, "f32", "sum", n=129) == "AR_ERR_INVALID_ARG"
     assert _err(ar.ar_allreduce, A[:2], B[:2], 16, 7, "sum") == "AR_ERR_INVALID_ARG"
     assert _err(ar.ar_allreduce, A[:2], B[:2], 16, "f32", 9) == "AR_ERR_INVALID_ARG"
-    assert _err(ar.ar_allreduce, A[:2], B[:2], 16, "f32", "sum", sched=5) == "AR_ERR_INVALID_ARG"
+    assert _err(ar.ar_allreduce, A[:2], B[:2], 16, "f32", "sum", sched=6) == "AR_ERR_INVALID_ARG"
     assert _err(ar.ar_allreduce, [A[0], 0], B[:2], 16, "f32", "sum") == "AR_ERR_INVALID_ARG"
     assert _err(ar.ar_allreduce, A[:2], [B[0], 0], 16, "f32", "sum") == "AR_ERR_INVALID_ARG"
     # misaligned for the element size
     assert _err(ar.ar_allreduce, [A[0] + 2, A[1]], B[:2], 16, "f32", "sum") == "AR_ERR_ALIGNMENT"
     assert _err(ar.ar_allreduce, [A[0] + 1, A[1]], B[:2], 16, "bf16", "sum") == "AR_ERR_ALIGNMENT"
     # tree and split are all-reduce schedules only
-    for sched in ("tree", "split"):
+    for sched in ("tree", "split", "dtree"):
         assert _err(ar.ar_reduce_scatter, A[:2], B[:2], 16, "f32", "sum", sched=sched) == "AR_ERR_UNSUPPORTED"
         assert _err(ar.ar_all_gather, A[:2], B[:2], 16, "f32", sched=sched) == "AR_ERR_UNSUPPORTED"
 
@@ -157,14 +157,37 @@ def test_tree_parent_matches_the_14_rank_picture():
     assert ar.ar_tree_parent(4, 7) == -1 and ar.ar_tree_parent(0, 0) == -1
 
 
+def test_dtree_parent_is_the_complementary_tree():
+    """The second tree: the mirror image of the first for even n, the first
+    shifted by one rank for odd n; the first is ar_tree_parent's tree."""
+    def first(n, v):
+        if v == 0:
+            return -1
+        b = v & -v
+        p = (v ^ b) | (b << 1)
+        return v ^ b if p >= n else p
+    for n in range(1, 129):
+        for v in range(n):
+            assert ar.ar_dtree_parent(n, 0, v) == ar.ar_tree_parent(n, v) == first(n, v)
+            if n % 2 == 0:
+                q = first(n, n - 1 - v)
+                want = -1 if q < 0 else n - 1 - q
+            else:
+                q = first(n, (v - 1) % n)
+                want = -1 if q < 0 else (q + 1) % n
+            assert ar.ar_dtree_parent(n, 1, v) == want, (n, v)
+    assert ar.ar_dtree_parent(8, 2, 1) == -1 and ar.ar_dtree_parent(8, 1, 8) == -1
+
+
 def test_plan_steps_bytes_and_legality():
     for n in (1, 2, 4, 8, 16, 72, 128):
         count = 1 << 20
         p = ar.ar_plan("allreduce", count, "f32", "sum", n)
-        assert p.legal == ["ring", "tree", "fused", "split"]
+        assert p.legal == ["ring", "tree", "fused", "split", "dtree"]
         assert p.steps["ring"] == 2 * (n - 1)
         assert p.steps["tree"] == 2 * ((n - 1).bit_length() if n > 1 else 0)
         assert p.steps["fused"] == 1 and p.steps["split"] == 1
+        assert p.steps["dtree"] == p.steps["tree"]
         assert all(b == 2 * n * count * 4 for b in p.bytes.values())
         assert p.chosen == min(p.predicted_us, key=lambda s: (p.predicted_us[s], ar.SCHEDS[s]))
         for coll in ("reduce_scatter", "all_gather"):

@@ -92,6 +92,12 @@ def test_c2_tree_and_in_place_full_size(c2_inputs):
     _same_on_all_ranks(ys)
     got = to_host(ys[0], "f32")
     assert_bits_equal(got, want_tree, "c2 tree")
+    print("c2 dtree oracle", flush=True)
+    want_dtree = oracle.dtree_allreduce(host, "f32", "sum")[0]
+    ar.ar_allreduce(xs, ys, count, "f32", "sum", sched="dtree")
+    torch.cuda.synchronize()
+    _same_on_all_ranks(ys)
+    assert_bits_equal(to_host(ys[0], "f32"), want_dtree, "c2 dtree")
     ring = oracle.ring_allreduce(host, "f32", "sum")[0]
     # the tree's order differs from the ring's: normwise 1e-6
     assert np.max(np.abs(got.astype(np.float64) - ring)) <= 1e-6 * np.max(np.abs(ring))
@@ -144,7 +150,7 @@ def test_c4_int32_size_sweep(op):
         full = size <= 16 * MB
         if full:
             want = oracle.direct_reduce([to_host(x, "i32") for x in xs], "i32", op)
-        for sched in ("auto", "fused", "ring", "tree"):
+        for sched in ("auto", "fused", "ring", "tree", "split", "dtree"):
             print("c4", op, size, sched, flush=True)
             ar.ar_allreduce(xs, ys, count, "i32", op, sched=sched)
             torch.cuda.synchronize()
@@ -176,6 +182,8 @@ def test_c5_bucketed_72_ranks_in_place():
         print("c5 oracle bucket", b, nbytes, chosen, flush=True)
         if chosen == "split":
             want[b] = oracle.pairwise_reduce(host, "f32", "avg")
+        elif chosen == "dtree":
+            want[b] = oracle.dtree_allreduce(host, "f32", "avg")[0]
         elif chosen == "tree":
             want[b] = oracle.tree_allreduce(host, "f32", "avg")[0]
         else:

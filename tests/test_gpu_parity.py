@@ -4,8 +4,9 @@ tiles / LDS windows and a ragged tail.
 
 Bar: ring and fused results are bit-identical to the ring oracle (they use
 its hop order), tree results bit-identical to the tree oracle, split results
-bit-identical to the pairwise oracle; all-gather and every integer result are
-bit-exact by construction."""
+bit-identical to the pairwise oracle, double-tree results bit-identical to the
+double-tree oracle; all-gather and every integer result are bit-exact by
+construction."""
 from __future__ import annotations
 
 import numpy as np
@@ -46,6 +47,8 @@ def reference(sched, xs, dtype, op):
         return oracle.tree_allreduce(xs, dtype, op)
     if sched == "split":
         return [oracle.pairwise_reduce(xs, dtype, op)] * len(xs)
+    if sched == "dtree":
+        return oracle.dtree_allreduce(xs, dtype, op)
     return oracle.ring_allreduce(xs, dtype, op)
 
 
@@ -65,7 +68,7 @@ def test_allreduce_matches_oracle(dtype, op):
         for count in counts_for(n, dtype):
             print("allreduce", dtype, op, "n=%d count=%d" % (n, count), flush=True)
             xs = inputs(1, n, count, dtype, op)
-            for sched in ("fused", "ring", "tree", "split", "auto"):
+            for sched in ("fused", "ring", "tree", "split", "dtree", "auto"):
                 got = run_allreduce(xs, dtype, op, sched)
                 ref = reference(sched, xs, dtype, op)
                 for r in range(n):
@@ -77,7 +80,7 @@ def test_allreduce_in_place_equals_out_of_place(dtype):
     n, count = 8, 8 * FUSED_TILE * 8 + 13
     for op in OPS:
         xs = inputs(2, n, count, dtype, op)
-        for sched in ("fused", "ring", "tree", "split"):
+        for sched in ("fused", "ring", "tree", "split", "dtree"):
             a = run_allreduce(xs, dtype, op, sched)
             b = run_allreduce(xs, dtype, op, sched, inplace=True)
             for r in range(n):
@@ -91,7 +94,7 @@ def test_allreduce_element_wise_path(dtype):
     n, count = 5, 3001
     for op in ("sum", "avg", "max"):
         xs = inputs(3, n, count, dtype, op)
-        for sched in ("fused", "ring", "tree", "split"):
+        for sched in ("fused", "ring", "tree", "split", "dtree"):
             d_in = [to_device(np.concatenate([x[:1], x]), dtype)[1:] for x in xs]
             d_out = [empty(count + 1, dtype, 0)[1:] for _ in xs]
             assert d_in[0].data_ptr() % 16 != 0
@@ -185,7 +188,7 @@ def test_c1_workload_every_schedule():
     exact integer sum."""
     xs = workloads.c1_inputs()
     want = sum(x.astype(np.int64) for x in xs).astype(np.float32)
-    for sched in ("fused", "ring", "tree", "split", "auto"):
+    for sched in ("fused", "ring", "tree", "split", "dtree", "auto"):
         for y in run_allreduce(xs, "f32", "sum", sched):
             assert_bits_equal(y, want, "c1 " + sched)
     parts = run_rs(xs, "f32", "sum", "auto")
@@ -200,7 +203,7 @@ def test_large_rank_counts():
     for n in (72, 128):
         count = n * 4 * 40 + 3
         xs = inputs(7, n, count, "f32", "avg")
-        for sched in ("fused", "ring", "tree", "split"):
+        for sched in ("fused", "ring", "tree", "split", "dtree"):
             got = run_allreduce(xs, "f32", "avg", sched)
             ref = reference(sched, xs, "f32", "avg")
             for r in (0, n // 2, n - 1):
@@ -255,7 +258,7 @@ def test_tiles_cut_on_an_aligned_grid(dtype):
             offsets = offs(n)
             print("aligned grid", dtype, n, label, flush=True)
             xs = inputs(9, n, count, dtype, "avg")
-            for sched in ("fused", "split", "ring", "tree"):
+            for sched in ("fused", "split", "ring", "tree", "dtree"):
                 d_in = [_at_offset(x, dtype, o) for x, o in zip(xs, offsets)]
                 d_out = [_empty_at_offset(count, dtype, (o + 32) % 1024) for o in offsets]
                 ar.ar_allreduce(d_in, d_out, count, dtype, "avg", sched=sched)
