@@ -18,6 +18,9 @@ functions follow:
   :func:`direct_reduce`; section "When the switch does the math" (every rank
   combined at once, in an order the post leaves open; read as the aligned
   pairwise tree over rank indices): :func:`pairwise_reduce`.
+* "FSDP collectives 101", the notes that bf16 reductions accumulate in bf16
+  (hence reducing in fp32) and that fp16 averages split the divisor across pre-
+  and post-scaling: the ``acc32`` and ``avg_split`` options (:func:`split_p`).
 * "FSDP collectives 101" (rakshithvasudev.github.io), sections "All-gather:
   everyone shows their piece" and "Why backward needs a different collective":
   the semantics of reduce-scatter (rank r keeps slice r) and all-gather.
@@ -76,10 +79,20 @@ def _load():
         lib = ctypes.CDLL(_LIB)
         vpp = ctypes.POINTER(ctypes.c_void_p)
         llp = ctypes.POINTER(ctypes.c_longlong)
-        for name in ("orc_ring_allreduce", "orc_ring_reduce_scatter"):
+        for name in ("orc_ring_allreduce_ex", "orc_ring_reduce_scatter_ex"):
             f = getattr(lib, name)
-            f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_size_t, vpp, vpp, llp, llp]
+            f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_size_t, vpp, vpp, llp, llp,
+                          ctypes.c_int, ctypes.c_int]
             f.restype = ctypes.c_int
+        for name in ("orc_tree_allreduce_ex", "orc_dtree_allreduce_ex"):
+            f = getattr(lib, name)
+            f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_size_t, vpp, vpp, ctypes.c_int, ctypes.c_int]
+            f.restype = ctypes.c_int
+        lib.orc_pairwise_reduce_ex.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_size_t, vpp,
+                                               ctypes.c_void_p, ctypes.c_int, ctypes.c_int]
+        lib.orc_pairwise_reduce_ex.restype = ctypes.c_int
+        lib.orc_split_p.argtypes = [ctypes.c_int]
+        lib.orc_split_p.restype = ctypes.c_int
         lib.orc_ring_all_gather.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_size_t, vpp, vpp, llp, llp]
         lib.orc_ring_all_gather.restype = ctypes.c_int
         lib.orc_tree_allreduce.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_size_t, vpp, vpp]
@@ -145,12 +158,20 @@ def allreduce_chunks(dtype: str, n: int, count: int) -> list[int]:
     return [int(v) for v in out]
 
 
-def ring_allreduce(xs, dtype: str, op: str, out=None, counters: bool = False):
+def split_p(n: int) -> int:
+    """The split avg's pre-scale divisor p (2^e, e the least with 4^e >= n)."""
+    return int(_load().orc_split_p(n))
+
+
+def ring_allreduce(xs, dtype: str, op: str, out=None, counters: bool = False, acc32: bool = False,
+                   avg_split: bool = False):
     """Ring all-reduce of the rank buffers ``xs`` (list of n 1-D arrays).
 
     Returns the list of n outputs (``out`` if given; ``out is xs`` is the
     in-place call), plus ``(hops_per_chunk, bytes_sent_per_rank)`` when
-    ``counters`` is true.
+    ``counters`` is true.  ``acc32``: bf16/fp16 partials stay fp32 between
+    hops, rounded once at the end; ``avg_split``: float avg pre-scales by
+    1/p and divides the finished sum by n/p (``split_p``).
     """
     n = len(xs)
     count = xs[0].size if n else 0
@@ -159,14 +180,15 @@ def ring_allreduce(xs, dtype: str, op: str, out=None, counters: bool = False):
     _check_inputs(ys, dtype, count)
     hops = (ctypes.c_longlong * max(1, n))()
     sent = (ctypes.c_longlong * max(1, n))()
-    _call(_load().orc_ring_allreduce(DTYPE_CODE[dtype], OP_CODE[op], n, count,
-                                     _ptrs(xs), _ptrs(ys), hops, sent))
+    _call(_load().orc_ring_allreduce_ex(DTYPE_CODE[dtype], OP_CODE[op], n, count,
+                                        _ptrs(xs), _ptrs(ys), hops, sent, int(acc32), int(avg_split)))
     if counters:
         return ys, list(hops)[:n], list(sent)[:n]
     return ys
 
 
-def ring_reduce_scatter(xs, dtype: str, op: str, out=None, counters: bool = False):
+def ring_reduce_scatter(xs, dtype: str, op: str, out=None, counters: bool = False, acc32: bool = False,
+                        avg_split: bool = False):
     """Ring reduce-scatter: each x_r has n*R elements; rank r gets slice r (R elements)."""
     n = len(xs)
     total = xs[0].size
@@ -178,8 +200,8 @@ def ring_reduce_scatter(xs, dtype: str, op: str, out=None, counters: bool = Fals
     _check_inputs(ys, dtype, R)
     hops = (ctypes.c_longlong * n)()
     sent = (ctypes.c_longlong * n)()
-    _call(_load().orc_ring_reduce_scatter(DTYPE_CODE[dtype], OP_CODE[op], n, R,
-                                          _ptrs(xs), _ptrs(ys), hops, sent))
+    _call(_load().orc_ring_reduce_scatter_ex(DTYPE_CODE[dtype], OP_CODE[op], n, R,
+                                             _ptrs(xs), _ptrs(ys), hops, sent, int(acc32), int(avg_split)))
     if counters:
         return ys, list(hops), list(sent)
     return ys
@@ -212,7 +234,7 @@ def direct_reduce(xs, dtype: str, op: str):
     return y
 
 
-def pairwise_reduce(xs, dtype: str, op: str):
+def pairwise_reduce(xs, dtype: str, op: str, acc32: bool = False, avg_split: bool = False):
     """All ranks combined at once in the aligned pairwise order over rank
     indices ([lo, lo+len) = [lo, lo+h) (+) [lo+h, lo+len), h the largest power
     of two below len), each combine rounded to the storage type; then the avg
@@ -221,7 +243,8 @@ def pairwise_reduce(xs, dtype: str, op: str):
     count = xs[0].size
     _check_inputs(xs, dtype, count)
     y = np.empty(count, NP_DTYPE[dtype])
-    _call(_load().orc_pairwise_reduce(DTYPE_CODE[dtype], OP_CODE[op], n, count, _ptrs(xs), y.ctypes.data))
+    _call(_load().orc_pairwise_reduce_ex(DTYPE_CODE[dtype], OP_CODE[op], n, count, _ptrs(xs), y.ctypes.data,
+                                         int(acc32), int(avg_split)))
     return y
 
 
@@ -230,14 +253,15 @@ def tree_parent(n: int, v: int) -> int:
     return int(_load().orc_tree_parent(n, v))
 
 
-def tree_allreduce(xs, dtype: str, op: str, out=None):
+def tree_allreduce(xs, dtype: str, op: str, out=None, acc32: bool = False, avg_split: bool = False):
     """Tree all-reduce: reduce up to rank 0 (own first, children ascending), broadcast down."""
     n = len(xs)
     count = xs[0].size
     _check_inputs(xs, dtype, count)
     ys = out if out is not None else [np.empty(count, NP_DTYPE[dtype]) for _ in range(n)]
     _check_inputs(ys, dtype, count)
-    _call(_load().orc_tree_allreduce(DTYPE_CODE[dtype], OP_CODE[op], n, count, _ptrs(xs), _ptrs(ys)))
+    _call(_load().orc_tree_allreduce_ex(DTYPE_CODE[dtype], OP_CODE[op], n, count, _ptrs(xs), _ptrs(ys),
+                                        int(acc32), int(avg_split)))
     return ys
 
 
@@ -247,7 +271,7 @@ def dtree_parent(n: int, which: int, v: int) -> int:
     return int(_load().orc_dtree_parent(n, which, v))
 
 
-def dtree_allreduce(xs, dtype: str, op: str, out=None):
+def dtree_allreduce(xs, dtype: str, op: str, out=None, acc32: bool = False, avg_split: bool = False):
     """Double binary tree all-reduce: elements [0, u*floor(V/2)) up the first
     tree, the rest up the second (u = 16 / element size, V = ceil(count / u))."""
     n = len(xs)
@@ -255,7 +279,8 @@ def dtree_allreduce(xs, dtype: str, op: str, out=None):
     _check_inputs(xs, dtype, count)
     ys = out if out is not None else [np.empty(count, NP_DTYPE[dtype]) for _ in range(n)]
     _check_inputs(ys, dtype, count)
-    _call(_load().orc_dtree_allreduce(DTYPE_CODE[dtype], OP_CODE[op], n, count, _ptrs(xs), _ptrs(ys)))
+    _call(_load().orc_dtree_allreduce_ex(DTYPE_CODE[dtype], OP_CODE[op], n, count, _ptrs(xs), _ptrs(ys),
+                                         int(acc32), int(avg_split)))
     return ys
 
 

@@ -231,6 +231,53 @@ static val_t post_op(int dtype, int op, int n, val_t acc)
     return acc;
 }
 
+/* ------------------------------------------------------------------------ */
+/* Numerics variants: the two accuracy trades the pages name ("FSDP          */
+/* collectives 101": bf16 reductions accumulate in bf16 along the way, which */
+/* grows lossy with the world size, hence reducing in fp32; fp16 averages    */
+/* split the divisor across pre- and post-scaling to avoid overflow).        */
+/*   acc32:     bf16 / fp16 partials stay in fp32 between hops; the result   */
+/*              is rounded to the storage type once, where it completes.     */
+/*   avg_split: float avg pre-scales by 1/p as read, p = 2^e with e the      */
+/*              least integer such that 4^e >= n (p near sqrt(n), a power of */
+/*              two so the pre-scale is exact), and divides the finished sum */
+/*              by q = n/p (the value of p is a reading: the pages give none).*/
+/* The defaults (both 0) are the behaviour described everywhere above.       */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+    int acc32;
+    int avg_split;
+} numerics_t;
+
+
+static int split_p(int n)
+{
+    int p = 1;
+    while (p * p < n) p *= 2;                               /* 4^e >= n  <=>  (2^e)^2 >= n */
+    return p;
+}
+
+/* The avg pre-scale of every floating-point contribution. */
+static float avg_scale(int n, const numerics_t *nm)
+{
+    return nm->avg_split ? (float)(1.0 / (double)split_p(n)) : (float)(1.0 / (double)n);
+}
+
+/* A partial as it leaves a hop. */
+static val_t round_partial(int dtype, val_t v, const numerics_t *nm)
+{
+    return nm->acc32 ? v : round_to_type(dtype, v);
+}
+
+/* Where a reduction completes: the postOp, the split avg's post-division
+ * (an fp32 division), and the rounding to the storage type. */
+static val_t finish(int dtype, int op, int n, val_t v, const numerics_t *nm)
+{
+    v = post_op(dtype, op, n, v);
+    if (op == ORC_AVG && dtype != ORC_I32 && nm->avg_split) v.f = v.f / (float)((double)n / split_p(n));
+    return round_to_type(dtype, v);
+}
+
 static int bad_args(int dtype, int op, int n)
 {
     return dtype < ORC_F32 || dtype > ORC_I32 || op < ORC_SUM || op > ORC_AVG || n < 1;
@@ -265,9 +312,9 @@ static void count_send(counters_t *k, int rank, int chunk, size_t bytes)
 /* finished chunk is left in fin[r].                                         */
 /* ------------------------------------------------------------------------ */
 static int ring_reduce_phase(int dtype, int op, int n, const size_t *off,
-                             const void *const *x, val_t **fin, counters_t *k)
+                             const void *const *x, val_t **fin, counters_t *k, const numerics_t *nm)
 {
-    const float s = (float)(1.0 / (double)n);
+    const float s = avg_scale(n, nm);
     size_t maxlen = 0;
     for (int c = 0; c < n; ++c)
         if (off[c + 1] - off[c] > maxlen) maxlen = off[c + 1] - off[c];
@@ -297,8 +344,8 @@ static int ring_reduce_phase(int dtype, int op, int n, const size_t *off,
 #pragma omp parallel for schedule(static)
             for (i = 0; i < (long long)len; ++i) {
                 val_t own = pre_op(dtype, op, load_elem(dtype, mine, off[c] + (size_t)i), s);
-                msg[i] = (t == 0) ? round_to_type(dtype, own)
-                                  : round_to_type(dtype, combine(dtype, op, in[i], own));
+                msg[i] = (t == 0) ? round_partial(dtype, own, nm)
+                                  : round_partial(dtype, combine(dtype, op, in[i], own), nm);
             }
             count_send(k, r, c, len * esz);
         }
@@ -322,9 +369,9 @@ static int ring_reduce_phase(int dtype, int op, int n, const size_t *off,
 #pragma omp parallel for schedule(static)
         for (i = 0; i < (long long)len; ++i) {
             val_t own = pre_op(dtype, op, load_elem(dtype, mine, off[c] + (size_t)i), s);
-            val_t v = (n == 1) ? round_to_type(dtype, own)
-                               : round_to_type(dtype, combine(dtype, op, in[i], own));
-            out[i] = post_op(dtype, op, n, v);
+            val_t v = (n == 1) ? round_partial(dtype, own, nm)
+                               : round_partial(dtype, combine(dtype, op, in[i], own), nm);
+            out[i] = finish(dtype, op, n, v, nm);
         }
     }
 
@@ -429,42 +476,57 @@ void orc_allreduce_chunks(int dtype, int n, size_t count, size_t *off /* [n+1] *
 
 /* Ring all-reduce: y_r[i] for every rank r = the chunk's ring reduction.
  * In place (x[r] == y[r]) is allowed.  hops/bytes may be NULL. */
-int orc_ring_allreduce(int dtype, int op, int n, size_t count, const void *const *x,
-                       void *const *y, long long *hops_per_chunk, long long *bytes_sent)
+int orc_ring_allreduce_ex(int dtype, int op, int n, size_t count, const void *const *x,
+                          void *const *y, long long *hops_per_chunk, long long *bytes_sent, int acc32, int avg_split)
 {
     if (bad_args(dtype, op, n)) return ORC_EBADARG;
+    const numerics_t nm = {acc32, avg_split};
     size_t *off = malloc(((size_t)n + 1) * sizeof(size_t));
     if (!off) return ORC_ENOMEM;
     orc_allreduce_chunks(dtype, n, count, off);
     counters_t k = {hops_per_chunk, bytes_sent};
     val_t **fin = NULL;
     int rc = alloc_fin(n, off, &fin);
-    if (rc == ORC_OK) rc = ring_reduce_phase(dtype, op, n, off, x, fin, &k);
+    if (rc == ORC_OK) rc = ring_reduce_phase(dtype, op, n, off, x, fin, &k, &nm);
     if (rc == ORC_OK) rc = ring_gather_phase(dtype, n, off, fin, y, &k);
     free_fin(n, fin);
     free(off);
     return rc;
 }
 
+int orc_ring_allreduce(int dtype, int op, int n, size_t count, const void *const *x,
+                       void *const *y, long long *hops_per_chunk, long long *bytes_sent)
+{
+    return orc_ring_allreduce_ex(dtype, op, n, count, x, y, hops_per_chunk, bytes_sent, 0, 0);
+}
+
 /* Ring reduce-scatter: every rank contributes n*recvcount elements; rank r
  * receives the finished chunk r = elements [r*recvcount, (r+1)*recvcount). */
-int orc_ring_reduce_scatter(int dtype, int op, int n, size_t recvcount, const void *const *x,
-                            void *const *y, long long *hops_per_chunk, long long *bytes_sent)
+int orc_ring_reduce_scatter_ex(int dtype, int op, int n, size_t recvcount, const void *const *x,
+                               void *const *y, long long *hops_per_chunk, long long *bytes_sent, int acc32,
+                               int avg_split)
 {
     if (bad_args(dtype, op, n)) return ORC_EBADARG;
+    const numerics_t nm = {acc32, avg_split};
     size_t *off = malloc(((size_t)n + 1) * sizeof(size_t));
     if (!off) return ORC_ENOMEM;
     for (int c = 0; c <= n; ++c) off[c] = (size_t)c * recvcount;
     counters_t k = {hops_per_chunk, bytes_sent};
     val_t **fin = NULL;
     int rc = alloc_fin(n, off, &fin);
-    if (rc == ORC_OK) rc = ring_reduce_phase(dtype, op, n, off, x, fin, &k);
+    if (rc == ORC_OK) rc = ring_reduce_phase(dtype, op, n, off, x, fin, &k, &nm);
     if (rc == ORC_OK)
         for (int r = 0; r < n; ++r)
             for (size_t i = 0; i < recvcount; ++i) store_elem(dtype, y[r], i, fin[r][i]);
     free_fin(n, fin);
     free(off);
     return rc;
+}
+
+int orc_ring_reduce_scatter(int dtype, int op, int n, size_t recvcount, const void *const *x,
+                            void *const *y, long long *hops_per_chunk, long long *bytes_sent)
+{
+    return orc_ring_reduce_scatter_ex(dtype, op, n, recvcount, x, y, hops_per_chunk, bytes_sent, 0, 0);
 }
 
 /* Ring all-gather: rank r contributes sendcount elements; every rank
@@ -521,18 +583,14 @@ int orc_dtree_parent(int n, int which, int v)
 
 /* Up phase, for one element: own value first, then each child's partial in
  * ascending rank order. */
-static val_t tree_partial_of(int dtype, int op, int n, int which, int v, const void *const *x, size_t i, float s)
+static val_t tree_partial_of(int dtype, int op, int n, int which, int v, const void *const *x, size_t i, float s,
+                             const numerics_t *nm)
 {
-    val_t p = round_to_type(dtype, pre_op(dtype, op, load_elem(dtype, x[v], i), s));
+    val_t p = round_partial(dtype, pre_op(dtype, op, load_elem(dtype, x[v], i), s), nm);
     for (int ch = 0; ch < n; ++ch)                       /* children may rank below or above v */
         if (ch != v && orc_dtree_parent(n, which, ch) == v)
-            p = round_to_type(dtype, combine(dtype, op, p, tree_partial_of(dtype, op, n, which, ch, x, i, s)));
+            p = round_partial(dtype, combine(dtype, op, p, tree_partial_of(dtype, op, n, which, ch, x, i, s, nm)), nm);
     return p;
-}
-
-static val_t tree_partial(int dtype, int op, int n, int v, const void *const *x, size_t i, float s)
-{
-    return tree_partial_of(dtype, op, n, 0, v, x, i, s);
 }
 
 static int tree_root(int n, int which)
@@ -544,21 +602,28 @@ static int tree_root(int n, int which)
 
 /* Tree all-reduce: reduce up to rank 0, postOp there, broadcast back down.
  * Every rank ends with the root's value. */
-int orc_tree_allreduce(int dtype, int op, int n, size_t count, const void *const *x, void *const *y)
+int orc_tree_allreduce_ex(int dtype, int op, int n, size_t count, const void *const *x, void *const *y, int acc32,
+                          int avg_split)
 {
     if (bad_args(dtype, op, n)) return ORC_EBADARG;
-    const float s = (float)(1.0 / (double)n);
+    const numerics_t nm = {acc32, avg_split};
+    const float s = avg_scale(n, &nm);
     val_t *root = malloc((count ? count : 1) * sizeof(val_t));
     if (!root) return ORC_ENOMEM;
     long long i;
 #pragma omp parallel for schedule(static)
     for (i = 0; i < (long long)count; ++i)
-        root[i] = post_op(dtype, op, n, tree_partial(dtype, op, n, 0, x, (size_t)i, s));
+        root[i] = finish(dtype, op, n, tree_partial_of(dtype, op, n, 0, 0, x, (size_t)i, s, &nm), &nm);
     /* broadcast down (the value is unchanged on the way) */
     for (int v = 0; v < n; ++v)
         for (size_t j = 0; j < count; ++j) store_elem(dtype, y[v], j, root[j]);
     free(root);
     return ORC_OK;
+}
+
+int orc_tree_allreduce(int dtype, int op, int n, size_t count, const void *const *x, void *const *y)
+{
+    return orc_tree_allreduce_ex(dtype, op, n, count, x, y, 0, 0);
 }
 
 /* Double binary tree all-reduce: half of every buffer is reduced up (and
@@ -569,10 +634,12 @@ int orc_tree_allreduce(int dtype, int op, int n, size_t count, const void *const
  * u = 16 / element size and V = ceil(count / u).  Each tree reduces as the
  * single tree does (own value first, children in ascending rank order, postOp
  * at its root) and every rank receives its root's value. */
-int orc_dtree_allreduce(int dtype, int op, int n, size_t count, const void *const *x, void *const *y)
+int orc_dtree_allreduce_ex(int dtype, int op, int n, size_t count, const void *const *x, void *const *y, int acc32,
+                           int avg_split)
 {
     if (bad_args(dtype, op, n)) return ORC_EBADARG;
-    const float s = (float)(1.0 / (double)n);
+    const numerics_t nm = {acc32, avg_split};
+    const float s = avg_scale(n, &nm);
     const size_t u = 16 / elem_size(dtype);
     const size_t V = (count + u - 1) / u;
     const size_t half = u * (V / 2);
@@ -583,12 +650,17 @@ int orc_dtree_allreduce(int dtype, int op, int n, size_t count, const void *cons
 #pragma omp parallel for schedule(static)
     for (i = 0; i < (long long)count; ++i) {
         const int which = (size_t)i < half ? 0 : 1;
-        res[i] = post_op(dtype, op, n, tree_partial_of(dtype, op, n, which, root[which], x, (size_t)i, s));
+        res[i] = finish(dtype, op, n, tree_partial_of(dtype, op, n, which, root[which], x, (size_t)i, s, &nm), &nm);
     }
     for (int v = 0; v < n; ++v)
         for (size_t j = 0; j < count; ++j) store_elem(dtype, y[v], j, res[j]);
     free(res);
     return ORC_OK;
+}
+
+int orc_dtree_allreduce(int dtype, int op, int n, size_t count, const void *const *x, void *const *y)
+{
+    return orc_dtree_allreduce_ex(dtype, op, n, count, x, y, 0, 0);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -630,26 +702,36 @@ int orc_direct_reduce(int dtype, int op, int n, size_t count, const void *const 
 /* i of every rank at offset i, so it applies to any slice of the buffers;    */
 /* writes one output array (every rank receives the same values).            */
 /* ------------------------------------------------------------------------ */
-static val_t pairwise_partial(int dtype, int op, int lo, int len, const void *const *x, size_t i, float s)
+static val_t pairwise_partial(int dtype, int op, int lo, int len, const void *const *x, size_t i, float s,
+                              const numerics_t *nm)
 {
-    if (len == 1) return round_to_type(dtype, pre_op(dtype, op, load_elem(dtype, x[lo], i), s));
+    if (len == 1) return round_partial(dtype, pre_op(dtype, op, load_elem(dtype, x[lo], i), s), nm);
     int h = 1;
     while (2 * h < len) h *= 2;                            /* largest power of two below len */
-    val_t left = pairwise_partial(dtype, op, lo, h, x, i, s);
-    val_t right = pairwise_partial(dtype, op, lo + h, len - h, x, i, s);
-    return round_to_type(dtype, combine(dtype, op, left, right));
+    val_t left = pairwise_partial(dtype, op, lo, h, x, i, s, nm);
+    val_t right = pairwise_partial(dtype, op, lo + h, len - h, x, i, s, nm);
+    return round_partial(dtype, combine(dtype, op, left, right), nm);
+}
+
+int orc_pairwise_reduce_ex(int dtype, int op, int n, size_t count, const void *const *x, void *y, int acc32,
+                           int avg_split)
+{
+    if (bad_args(dtype, op, n)) return ORC_EBADARG;
+    const numerics_t nm = {acc32, avg_split};
+    const float s = avg_scale(n, &nm);
+    long long i;
+#pragma omp parallel for schedule(static)
+    for (i = 0; i < (long long)count; ++i)
+        store_elem(dtype, y, (size_t)i, finish(dtype, op, n, pairwise_partial(dtype, op, 0, n, x, (size_t)i, s, &nm), &nm));
+    return ORC_OK;
 }
 
 int orc_pairwise_reduce(int dtype, int op, int n, size_t count, const void *const *x, void *y)
 {
-    if (bad_args(dtype, op, n)) return ORC_EBADARG;
-    const float s = (float)(1.0 / (double)n);
-    long long i;
-#pragma omp parallel for schedule(static)
-    for (i = 0; i < (long long)count; ++i)
-        store_elem(dtype, y, (size_t)i, post_op(dtype, op, n, pairwise_partial(dtype, op, 0, n, x, (size_t)i, s)));
-    return ORC_OK;
+    return orc_pairwise_reduce_ex(dtype, op, n, count, x, y, 0, 0);
 }
+
+int orc_split_p(int n) { return split_p(n); }
 
 int orc_num_threads(void)
 {

@@ -794,6 +794,133 @@ def test_pairwise_power_of_two_avg_is_scaled_sum():
 
 
 # ---------------------------------------------------------------------------
+# 6c. numerics variants: fp32 accumulation, split avg divisor
+# ---------------------------------------------------------------------------
+
+def test_split_p_is_the_power_of_two_nearest_above_sqrt_n():
+    for n in range(1, 129):
+        p = oracle.split_p(n)
+        assert p & (p - 1) == 0 and p * p >= n and (p == 1 or (p // 2) ** 2 < n), (n, p)
+    assert [oracle.split_p(n) for n in (2, 4, 8, 16, 72)] == [2, 2, 4, 4, 16]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_acc32_keeps_what_per_hop_rounding_loses(dtype):
+    """Chunk 0's chain is ranks 1, 2, 0: B + 1 - B.  Rounded to the storage
+    type after each hop it is 0 (B + 1 ties back to B); with fp32 partials it is
+    the exact 1."""
+    B = BIG[dtype]
+    n, u = 3, 8
+    xs = [np.zeros(n * u) for _ in range(n)]
+    xs[1][:u], xs[2][:u], xs[0][:u] = B, 1.0, -B
+    t = [to_dtype(x, dtype) for x in xs]
+    assert as_float(oracle.ring_allreduce(t, dtype, "sum")[0], dtype)[:u].tolist() == [0.0] * u
+    for fn in (lambda: oracle.ring_allreduce(t, dtype, "sum", acc32=True)[0],
+               lambda: oracle.ring_reduce_scatter(t, dtype, "sum", acc32=True)[0]):
+        assert as_float(fn(), dtype)[:u].tolist() == [1.0] * u
+
+
+def _round_once(values_f64, dtype):
+    """Storage-type rounding by library code: numpy for fp16, torch for bf16."""
+    if dtype == "f16":
+        return values_f64.astype(np.float32).astype(np.float16).astype(np.float64)
+    import torch
+    return torch.tensor(values_f64.astype(np.float32)).to(torch.bfloat16).float().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("op", ["sum", "prod", "avg", "max"])
+def test_acc32_is_the_fp32_ring_rounded_once(dtype, op):
+    """fp32 partials in the ring's hop order, rounded once: the fp32 ring (pinned
+    above) on the widened inputs, rounded by numpy / torch."""
+    for n in (2, 5, 8, 16, 72):
+        count = n * 8 * 3 + 5
+        kind = "pos" if op == "prod" else "normal"
+        xs = [workloads.random_values(13, n, r, count, dtype, kind) for r in range(n)]
+        wide = [as_float(x, dtype).astype(np.float32) for x in xs]
+        want = _round_once(oracle.ring_allreduce(wide, "f32", op)[0].astype(np.float64), dtype)
+        got = as_float(oracle.ring_allreduce(xs, dtype, op, acc32=True)[0], dtype)
+        assert got.tolist() == want.tolist(), (dtype, op, n)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_acc32_error_bound_and_the_per_hop_loss(dtype):
+    """With fp32 partials the error is one storage rounding plus fp32's
+    recursive-summation bound; per-hop storage rounding exceeds that bound at
+    72 ranks (the loss the pages attribute to bf16 accumulation)."""
+    n, count = 72, 512
+    xs = [workloads.normal(14, n, r, count, 1.0, dtype) for r in range(n)]
+    fx = [as_float(x, dtype) for x in xs]
+    uT = UNIT_ROUNDOFF[dtype]
+    acc = as_float(oracle.ring_allreduce(xs, dtype, "sum", acc32=True)[0], dtype)
+    hop = as_float(oracle.ring_allreduce(xs, dtype, "sum")[0], dtype)
+    worst_hop = 0.0
+    for i in range(count):
+        terms = [Fraction(f[i]) for f in fx]
+        exact = sum(terms)
+        bound = Fraction(abs(float(exact)) * uT) + Fraction(gamma(n - 1, 2.0 ** -24) * float(sum(abs(t) for t in terms)))
+        assert abs(Fraction(acc[i]) - exact) <= bound * (1 + uT), i
+        worst_hop = max(worst_hop, float(abs(Fraction(hop[i]) - exact) / bound))
+    assert worst_hop > 1.0
+
+
+def test_acc32_is_a_no_op_for_fp32_and_int32():
+    for dtype in ("f32", "i32"):
+        xs = [workloads.random_values(15, 6, r, 301, dtype) for r in range(6)]
+        for op in OPS:
+            a = oracle.ring_allreduce(xs, dtype, op)[0]
+            b = oracle.ring_allreduce(xs, dtype, op, acc32=True)[0]
+            assert a.tobytes() == b.tobytes(), (dtype, op)
+
+
+def test_avg_split_fp16_keeps_what_the_prescale_underflows():
+    """fp16, n = 8 (p = 4, q = 2), every contribution 2^-22: pre-scaled by 1/8
+    each is 2^-25, half the smallest subnormal, which rounds (to even) to 0;
+    split, each is 2^-24, the sum 2^-21 and the average the exact 2^-22."""
+    n = 8
+    xs = [np.full(64, 2.0 ** -22, np.float16) for _ in range(n)]
+    for fn in (oracle.ring_allreduce, oracle.tree_allreduce, oracle.dtree_allreduce):
+        assert fn(xs, "f16", "avg")[0].astype(np.float64).tolist() == [0.0] * 64
+        assert fn(xs, "f16", "avg", avg_split=True)[0].astype(np.float64).tolist() == [2.0 ** -22] * 64
+    assert oracle.pairwise_reduce(xs, "f16", "avg", avg_split=True).astype(np.float64).tolist() == [2.0 ** -22] * 64
+
+
+def test_avg_split_fp16_overflows_where_the_prescale_does_not():
+    """The other side of the trade: n = 16 (p = q = 4), every contribution 2^15:
+    pre-scaled by 1/16 each is 2048 and every partial sum a multiple of 2048,
+    exact in fp16, so the average is 2^15; split, each is 8192 and the partial
+    sums pass the fp16 maximum 65504 (8 * 8192 = 65536 rounds to +inf)."""
+    xs = [np.full(64, 32768.0, np.float16) for _ in range(16)]
+    assert oracle.ring_allreduce(xs, "f16", "avg")[0].astype(np.float64).tolist() == [32768.0] * 64
+    assert np.isposinf(oracle.ring_allreduce(xs, "f16", "avg", avg_split=True)[0].astype(np.float64)).all()
+
+
+def test_avg_split_equals_the_prescale_when_both_factors_are_exact():
+    """n = 4^k: p = q = 2^k, so x/p and sum/q are exact power-of-two scalings and
+    the split route gives the pre-scale route's bits (fp32, no under/overflow)."""
+    for n in (4, 16, 64):
+        xs = [workloads.normal(16, n, r, 300, 1e-3, "f32") for r in range(n)]
+        for fn in (lambda **k: oracle.ring_allreduce(xs, "f32", "avg", **k)[0],
+                   lambda **k: oracle.tree_allreduce(xs, "f32", "avg", **k)[0],
+                   lambda **k: oracle.pairwise_reduce(xs, "f32", "avg", **k)):
+            assert fn().tobytes() == fn(avg_split=True).tobytes(), n
+
+
+def test_avg_split_divides_once_in_fp32():
+    """n = 72: p = 16, q = 4.5; fp32 values whose sum / 16 is exact: the split
+    result is the correctly rounded fp32 quotient of the exact sum by 72."""
+    n = 72
+    rg = np.random.default_rng(17)
+    xs = [(rg.integers(-1000, 1000, size=40) * 16).astype(np.float32) for _ in range(n)]
+    got = oracle.ring_allreduce(xs, "f32", "avg", avg_split=True)[0]
+    total = sum(x.astype(np.int64) for x in xs)
+    want = ((total // 16).astype(np.float32) / np.float32(4.5)).astype(np.float32)
+    assert got.tobytes() == want.tobytes()
+    i = oracle.ring_allreduce([x.astype(np.int32) for x in xs], "i32", "avg", avg_split=True)[0]
+    assert i.tobytes() == oracle.ring_allreduce([x.astype(np.int32) for x in xs], "i32", "avg")[0].tobytes()
+
+
+# ---------------------------------------------------------------------------
 # 7. invariants the pages state
 # ---------------------------------------------------------------------------
 
