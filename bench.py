@@ -160,6 +160,17 @@ def sweep():
     for sched in ("fused", "ring"):
         us = _median_us(lambda: ar.ar_reduce_scatter(xs, ys, R, "bf16", "avg", sched=sched))
         out.append("| reduce-scatter | %s | %.1f | %.0f | %.1f |" % (sched, us, alg / us / 1e3, alg / us / 1e3 / PEAK_HBM_GBPS * 100))
+    # reducing in fp32: fp32 partials over the bf16 buffers, against a reduce-scatter of fp32 copies
+    us = _median_us(lambda: ar.ar_reduce_scatter_ex(xs, ys, R, "bf16", "avg", sched="fused", acc="fp32"))
+    out.append("| reduce-scatter, fp32 partials (bf16 in and out) | fused | %.1f | %.0f | %.1f |" % (
+        us, alg / us / 1e3, alg / us / 1e3 / PEAK_HBM_GBPS * 100))
+    x32_t = [x.float() for x in xs_t]
+    y32_t = [torch.empty(R, device="cuda") for _ in range(n)]
+    x32, y32 = ar.pointers(x32_t), ar.pointers(y32_t)
+    us32 = _median_us(lambda: ar.ar_reduce_scatter(x32, y32, R, "f32", "avg", sched="fused"))
+    out.append("| reduce-scatter of fp32 copies (twice the bytes; the cast not timed) | fused | %.1f | %.0f | %.1f |" % (
+        us32, 2 * alg / us32 / 1e3, 2 * alg / us32 / 1e3 / PEAK_HBM_GBPS * 100))
+    del x32, y32, x32_t, y32_t
     del xs, xs_t
     pieces_t = [wl.device_uniform(2, 1, r, R, -1.0, 1.0, "bf16") for r in range(n)]
     full_t = [torch.empty(n * R, dtype=torch.bfloat16, device="cuda") for _ in range(n)]

@@ -116,6 +116,31 @@ typedef enum {
 } ar_sched_t;
 typedef enum { AR_COLL_ALLREDUCE = 0, AR_COLL_REDUCE_SCATTER = 1, AR_COLL_ALL_GATHER = 2 } ar_coll_t;
 
+/* Numerics of a floating-point reduction: the two accuracy trades named in
+ * "FSDP collectives 101" (bf16 reductions accumulate in bf16 along the way,
+ * which grows lossy with the number of ranks, hence reducing in fp32; fp16
+ * averages split the divisor across pre- and post-scaling).  A zeroed struct
+ * (or NULL) is the behaviour of ar_allreduce / ar_reduce_scatter. */
+typedef enum {
+    AR_ACC_STORAGE = 0,  /* every partial rounded to the storage type when it leaves a hop */
+    AR_ACC_FP32 = 1      /* bf16 / fp16: partials stay fp32 and the result is rounded once where it
+                          * completes; same bytes moved.  Only the fused schedule keeps partials in
+                          * registers: other schedules return AR_ERR_UNSUPPORTED and AUTO picks fused.
+                          * No effect for fp32 / int32. */
+} ar_acc_t;
+typedef enum {
+    AR_AVG_PRESCALE = 0, /* float avg: every contribution times fp32(1/n) as it is read */
+    AR_AVG_SPLIT = 1     /* float avg: every contribution times 1/p as read, p = 2^e with e the least
+                          * integer such that 4^e >= n (a power of two near sqrt(n), so the pre-scale is
+                          * exact), and the finished sum divided by n/p in fp32 before the final
+                          * rounding: fewer underflows than 1/n, fewer overflows than sum-then-divide.
+                          * Every schedule.  No effect for int32 or other ops. */
+} ar_avg_t;
+typedef struct {
+    ar_acc_t acc;
+    ar_avg_t avg;
+} ar_numerics_t;
+
 /* Result of the cost model, indexed by ar_sched_t (entry 0, AUTO, is unused).
  * predicted_us[s] = launch_us[s] + step_us[s] * steps[s] + bytes[s] / bandwidth[s]
  * for every legal schedule s; ``chosen`` is the legal schedule with the
@@ -139,6 +164,13 @@ typedef struct {
 ar_status_t ar_allreduce(const void *const *sendbufs, void *const *recvbufs, size_t count,
                          ar_dtype_t dtype, ar_op_t op, int n, ar_sched_t sched, hipStream_t stream);
 
+/* All-reduce with explicit numerics (``numerics`` NULL: the defaults, as
+ * ar_allreduce).  AR_ERR_INVALID_ARG for values outside the enums;
+ * AR_ERR_UNSUPPORTED when the forced schedule cannot honour them. */
+ar_status_t ar_allreduce_ex(const void *const *sendbufs, void *const *recvbufs, size_t count,
+                            ar_dtype_t dtype, ar_op_t op, int n, ar_sched_t sched,
+                            const ar_numerics_t *numerics, hipStream_t stream);
+
 /* Reduce-scatter: sendbufs[r] holds n*recvcount elements, recvbufs[r]
  * receives recvcount elements (slice r of the combined result).
  * Source: "FSDP collectives 101", section "Why backward needs a different
@@ -146,6 +178,13 @@ ar_status_t ar_allreduce(const void *const *sendbufs, void *const *recvbufs, siz
  * (tree, split and dtree: AR_ERR_UNSUPPORTED). */
 ar_status_t ar_reduce_scatter(const void *const *sendbufs, void *const *recvbufs, size_t recvcount,
                               ar_dtype_t dtype, ar_op_t op, int n, ar_sched_t sched, hipStream_t stream);
+
+/* Reduce-scatter with explicit numerics (as ar_allreduce_ex).  FSDP's
+ * "reduce in fp32" for bf16 gradients without moving fp32 bytes:
+ * AR_ACC_FP32 reads and writes bf16 and keeps the partials in fp32. */
+ar_status_t ar_reduce_scatter_ex(const void *const *sendbufs, void *const *recvbufs, size_t recvcount,
+                                 ar_dtype_t dtype, ar_op_t op, int n, ar_sched_t sched,
+                                 const ar_numerics_t *numerics, hipStream_t stream);
 
 /* All-gather: sendbufs[r] holds sendcount elements, recvbufs[r] receives
  * n*sendcount elements (x_0 || x_1 || ... || x_{n-1}).

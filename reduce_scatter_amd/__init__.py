@@ -21,8 +21,10 @@ from ._binding import (  # noqa: F401
     PointerTable,
     ar_all_gather,
     ar_allreduce,
+    ar_allreduce_ex,
     ar_plan,
     ar_reduce_scatter,
+    ar_reduce_scatter_ex,
     ar_status_string,
     ar_tree_parent,
     ar_dtree_parent,
@@ -32,6 +34,8 @@ from ._binding import (  # noqa: F401
 
 __all__ = [
     "ar_allreduce",
+    "ar_allreduce_ex",
+    "ar_reduce_scatter_ex",
     "ar_reduce_scatter",
     "ar_all_gather",
     "ar_plan",

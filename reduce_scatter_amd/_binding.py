@@ -19,6 +19,8 @@ DTYPES = {"f32": 0, "bf16": 1, "f16": 2, "i32": 3}
 OPS = {"sum": 0, "prod": 1, "min": 2, "max": 3, "avg": 4}
 SCHEDS = {"auto": 0, "ring": 1, "tree": 2, "fused": 3, "split": 4, "dtree": 5}
 COLLS = {"allreduce": 0, "reduce_scatter": 1, "all_gather": 2}
+ACCS = {"storage": 0, "fp32": 1}
+AVGS = {"prescale": 0, "split": 1}
 _SCHED_NAMES = {v: k for k, v in SCHEDS.items()}
 _STATUS = {0: "AR_OK", 1: "AR_ERR_INVALID_ARG", 2: "AR_ERR_UNSUPPORTED", 3: "AR_ERR_ALIGNMENT", 4: "AR_ERR_HIP"}
 
@@ -39,6 +41,10 @@ except ImportError:
 _lib = ctypes.CDLL(_LIB_PATH)
 
 
+class _Numerics(ctypes.Structure):
+    _fields_ = [("acc", ctypes.c_int), ("avg", ctypes.c_int)]
+
+
 class _PlanStruct(ctypes.Structure):
     _fields_ = [("chosen", ctypes.c_int), ("legal_mask", ctypes.c_uint), ("steps", ctypes.c_int * 6),
                 ("bytes", ctypes.c_double * 6), ("predicted_us", ctypes.c_double * 6)]
@@ -48,6 +54,9 @@ _vpp = ctypes.POINTER(ctypes.c_void_p)
 _lib.ar_allreduce.argtypes = [_vpp, _vpp, ctypes.c_size_t, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                               ctypes.c_void_p]
 _lib.ar_reduce_scatter.argtypes = _lib.ar_allreduce.argtypes
+_lib.ar_allreduce_ex.argtypes = [_vpp, _vpp, ctypes.c_size_t, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                 ctypes.c_void_p, ctypes.c_void_p]
+_lib.ar_reduce_scatter_ex.argtypes = _lib.ar_allreduce_ex.argtypes
 _lib.ar_all_gather.argtypes = [_vpp, _vpp, ctypes.c_size_t, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                ctypes.c_void_p]
 _lib.ar_plan.argtypes = [ctypes.c_int, ctypes.c_size_t, ctypes.c_int, ctypes.c_int, ctypes.c_int,
@@ -58,7 +67,8 @@ _lib.ar_dtree_parent.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
 _lib.ar_dtree_parent.restype = ctypes.c_int
 _lib.ar_status_string.argtypes = [ctypes.c_int]
 _lib.ar_status_string.restype = ctypes.c_char_p
-for _f in (_lib.ar_allreduce, _lib.ar_reduce_scatter, _lib.ar_all_gather, _lib.ar_plan):
+for _f in (_lib.ar_allreduce, _lib.ar_reduce_scatter, _lib.ar_all_gather, _lib.ar_plan, _lib.ar_allreduce_ex,
+           _lib.ar_reduce_scatter_ex):
     _f.restype = ctypes.c_int
 
 
@@ -177,6 +187,29 @@ def ar_reduce_scatter(sendbufs, recvbufs, recvcount, dtype, op, n=None, sched="a
     send, recv = _tables(sendbufs, recvbufs)
     _check(_lib.ar_reduce_scatter(send, recv, recvcount, _dtype_code(dtype),
                                   _code(OPS, op, "op"), n, _code(SCHEDS, sched, "schedule"), _stream(stream)))
+
+
+def _numerics(acc, avg):
+    return ctypes.byref(_Numerics(_code(ACCS, acc, "accumulation"), _code(AVGS, avg, "avg route")))
+
+
+def ar_allreduce_ex(sendbufs, recvbufs, count, dtype, op, n=None, sched="auto", acc="storage", avg="prescale",
+                    stream=None):
+    """All-reduce with explicit numerics: ``acc`` "storage" | "fp32" (bf16 / fp16
+    partials kept in fp32, fused schedule), ``avg`` "prescale" | "split"."""
+    n = len(sendbufs) if n is None else n
+    send, recv = _tables(sendbufs, recvbufs)
+    _check(_lib.ar_allreduce_ex(send, recv, count, _dtype_code(dtype), _code(OPS, op, "op"), n,
+                                _code(SCHEDS, sched, "schedule"), _numerics(acc, avg), _stream(stream)))
+
+
+def ar_reduce_scatter_ex(sendbufs, recvbufs, recvcount, dtype, op, n=None, sched="auto", acc="storage",
+                         avg="prescale", stream=None):
+    """Reduce-scatter with explicit numerics (as :func:`ar_allreduce_ex`)."""
+    n = len(sendbufs) if n is None else n
+    send, recv = _tables(sendbufs, recvbufs)
+    _check(_lib.ar_reduce_scatter_ex(send, recv, recvcount, _dtype_code(dtype), _code(OPS, op, "op"), n,
+                                     _code(SCHEDS, sched, "schedule"), _numerics(acc, avg), _stream(stream)))
 
 
 def ar_all_gather(sendbufs, recvbufs, sendcount, dtype, n=None, sched="auto", stream=None):

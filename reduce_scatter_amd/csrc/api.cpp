@@ -193,12 +193,26 @@ void log_plan(ar_coll_t coll, size_t bytes_per_rank, int n, int dtype, int op, c
             calib_source());
 }
 
-// Resolve AR_SCHED_AUTO (and the AR_SCHEDULE override) into a legal schedule.
+// Resolve AR_SCHED_AUTO (and the AR_SCHEDULE override) into a legal schedule;
+// ``allowed`` further restricts the legal set (numerics some schedules lack).
 ar_status_t choose(ar_coll_t coll, size_t count, ar_dtype_t dtype, ar_op_t op, int n, ar_sched_t sched,
-                   ar_sched_t *out, size_t bytes_per_rank) {
+                   ar_sched_t *out, size_t bytes_per_rank, unsigned allowed = ~0u) {
     ar_plan_t p;
     ar_status_t st = make_plan(coll, count, dtype, op, n, &p);
     if (st != AR_OK) return st;
+    if ((p.legal_mask & allowed) != p.legal_mask) {             // re-pick among what is left
+        p.legal_mask &= allowed;
+        double best = 0;
+        bool have = false;
+        for (int s = AR_SCHED_RING; s <= AR_SCHED_DTREE; ++s) {
+            if (!(p.legal_mask & (1u << s))) continue;
+            if (!have || p.predicted_us[s] < best) {
+                best = p.predicted_us[s];
+                p.chosen = (ar_sched_t)s;
+                have = true;
+            }
+        }
+    }
     bool forced = sched != AR_SCHED_AUTO;
     if (!forced) {
         ar_sched_t env = forced_schedule();
@@ -234,6 +248,34 @@ ar_status_t common_checks(const void *const *send, void *const *recv, int dtype,
     return AR_OK;
 }
 
+// The numerics of a call in the geometry: the float avg pre-scale s (1/n, or
+// 1/p for the split route with p = 2^e, e the least with 4^e >= n), the split
+// route's post-divisor n/p, and fp32 partials for bf16 / fp16.  Returns the
+// schedules that support them (fp32 partials: the fused pass only, where the
+// partials never leave registers).
+ar_status_t apply_numerics(const ar_numerics_t *num, int dtype, int op, int n, Geometry &g, unsigned *allowed) {
+    *allowed = ~0u;
+    g.s = (float)(1.0 / (double)n);
+    g.post_div = 0.0f;
+    g.acc32 = 0;
+    if (!num) return AR_OK;
+    if ((num->acc != AR_ACC_STORAGE && num->acc != AR_ACC_FP32) ||
+        (num->avg != AR_AVG_PRESCALE && num->avg != AR_AVG_SPLIT))
+        return AR_ERR_INVALID_ARG;
+    const bool is_float = dtype != AR_INT32;
+    if (num->avg == AR_AVG_SPLIT && is_float && op == AR_AVG) {
+        int p = 1;
+        while (p * p < n) p *= 2;
+        g.s = (float)(1.0 / (double)p);
+        g.post_div = (float)((double)n / (double)p);           // exact: n <= 128, p a power of two
+    }
+    if (num->acc == AR_ACC_FP32 && (dtype == AR_BFLOAT16 || dtype == AR_FLOAT16)) {
+        g.acc32 = 1;
+        *allowed = 1u << AR_SCHED_FUSED;
+    }
+    return AR_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -264,6 +306,11 @@ ar_status_t ar_plan(ar_coll_t coll, size_t count, ar_dtype_t dtype, ar_op_t op, 
 
 ar_status_t ar_allreduce(const void *const *sendbufs, void *const *recvbufs, size_t count, ar_dtype_t dtype,
                          ar_op_t op, int n, ar_sched_t sched, hipStream_t stream) {
+    return ar_allreduce_ex(sendbufs, recvbufs, count, dtype, op, n, sched, nullptr, stream);
+}
+
+ar_status_t ar_allreduce_ex(const void *const *sendbufs, void *const *recvbufs, size_t count, ar_dtype_t dtype,
+                            ar_op_t op, int n, ar_sched_t sched, const ar_numerics_t *numerics, hipStream_t stream) {
     ar_status_t st = common_checks(sendbufs, recvbufs, dtype, op, n, sched);
     if (st != AR_OK) return st;
     if (count == 0) return AR_OK;
@@ -275,8 +322,13 @@ ar_status_t ar_allreduce(const void *const *sendbufs, void *const *recvbufs, siz
     for (int r = 0; r < n; ++r) inplace[r] = (recvbufs[r] == sendbufs[r]) ? 1 : 0;
     st = check_overlap(sendbufs, count * e, recvbufs, count * e, n, inplace);
     if (st != AR_OK) return st;
+    Geometry g;
+    memset(&g, 0, sizeof g);
+    unsigned allowed;
+    st = apply_numerics(numerics, dtype, op, n, g, &allowed);
+    if (st != AR_OK) return st;
     ar_sched_t use;
-    st = choose(AR_COLL_ALLREDUCE, count, dtype, op, n, sched, &use, count * e);
+    st = choose(AR_COLL_ALLREDUCE, count, dtype, op, n, sched, &use, count * e, allowed);
     if (st != AR_OK) return st;
     int cus = 0;
     st = device_cus(&cus);
@@ -284,11 +336,8 @@ ar_status_t ar_allreduce(const void *const *sendbufs, void *const *recvbufs, siz
 
     RankTable t;
     fill_table(t, sendbufs, recvbufs, n);
-    Geometry g;
-    memset(&g, 0, sizeof g);
     const long long lanes = 16 / (long long)e;
     g.n = n;
-    g.s = (float)(1.0 / (double)n);
     g.V = ((long long)count + lanes - 1) / lanes;
     g.Vfull = (long long)count / lanes;
     g.q = g.V / n;
@@ -342,6 +391,12 @@ ar_status_t ar_allreduce(const void *const *sendbufs, void *const *recvbufs, siz
 
 ar_status_t ar_reduce_scatter(const void *const *sendbufs, void *const *recvbufs, size_t recvcount,
                               ar_dtype_t dtype, ar_op_t op, int n, ar_sched_t sched, hipStream_t stream) {
+    return ar_reduce_scatter_ex(sendbufs, recvbufs, recvcount, dtype, op, n, sched, nullptr, stream);
+}
+
+ar_status_t ar_reduce_scatter_ex(const void *const *sendbufs, void *const *recvbufs, size_t recvcount,
+                                 ar_dtype_t dtype, ar_op_t op, int n, ar_sched_t sched,
+                                 const ar_numerics_t *numerics, hipStream_t stream) {
     ar_status_t st = common_checks(sendbufs, recvbufs, dtype, op, n, sched);
     if (st != AR_OK) return st;
     if (recvcount == 0) return AR_OK;
@@ -354,8 +409,13 @@ ar_status_t ar_reduce_scatter(const void *const *sendbufs, void *const *recvbufs
         inplace[r] = ((uintptr_t)recvbufs[r] == (uintptr_t)sendbufs[r] + (uintptr_t)r * recvcount * e) ? 1 : 0;
     st = check_overlap(sendbufs, (size_t)n * recvcount * e, recvbufs, recvcount * e, n, inplace);
     if (st != AR_OK) return st;
+    Geometry g;
+    memset(&g, 0, sizeof g);
+    unsigned allowed;
+    st = apply_numerics(numerics, dtype, op, n, g, &allowed);
+    if (st != AR_OK) return st;
     ar_sched_t use;
-    st = choose(AR_COLL_REDUCE_SCATTER, recvcount, dtype, op, n, sched, &use, (size_t)n * recvcount * e);
+    st = choose(AR_COLL_REDUCE_SCATTER, recvcount, dtype, op, n, sched, &use, (size_t)n * recvcount * e, allowed);
     if (st != AR_OK) return st;
     int cus = 0;
     st = device_cus(&cus);
@@ -363,10 +423,7 @@ ar_status_t ar_reduce_scatter(const void *const *sendbufs, void *const *recvbufs
 
     RankTable t;
     fill_table(t, sendbufs, recvbufs, n);
-    Geometry g;
-    memset(&g, 0, sizeof g);
     g.n = n;
-    g.s = (float)(1.0 / (double)n);
     const bool vec = all16(sendbufs, (const void *const *)recvbufs, n) && (recvcount * e) % 16 == 0;
     if (!vec) return hip_status(launch_elem_reduce_scatter(dtype, op, t, g, (long long)recvcount, stream));
     g.Rv = (long long)(recvcount * e / 16);

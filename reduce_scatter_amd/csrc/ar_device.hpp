@@ -52,8 +52,24 @@ __device__ __forceinline__ float round_bf16(float f) {
     return bits_f32(u & 0xffff0000u);
 }
 
-// fp32 -> nearest fp16 (ties to even, the hardware conversion), back to fp32.
-__device__ __forceinline__ float round_f16(float f) { return (float)(_Float16)f; }
+// fp32 -> nearest fp16 value (ties to even), as an fp32.  Written with exact
+// power-of-two scalings and an integer round-to-nearest-even instead of a
+// float-to-half conversion: the compiler fuses a multiply followed by that
+// conversion into one mixed-precision FMA that rounds the exact product once,
+// which differs from rounding the fp32 product when the operands are not fp16
+// values (fp32 partials).  The fp16 quantum is 2^(e-10) in the binade 2^e,
+// and 2^-24 below 2^-14 (subnormals); past the largest finite fp16 (65504)
+// the value rounds to infinity.
+__device__ __forceinline__ float round_f16(float f) {
+    const uint32_t a = f32_bits(f) & 0x7fffffffu;
+    if (a >= 0x7f800000u) return f;                                  // inf, NaN
+    int e = (int)(a >> 23) - 127;                                      // binade of |f|
+    e = e < -14 ? -14 : e;
+    const float inv_q = bits_f32((uint32_t)(127 + 10 - e) << 23);     // 2^(10-e)
+    const float q = bits_f32((uint32_t)(127 - 10 + e) << 23);         // 2^(e-10)
+    const float r = __builtin_rintf(f * inv_q) * q;
+    return __builtin_fabsf(r) > 65504.0f ? __builtin_copysignf(__builtin_inff(), f) : r;
+}
 
 template <int DT> __device__ __forceinline__ float round_to(float f) {
     if (DT == BF16) return round_bf16(f);
@@ -130,23 +146,32 @@ __device__ __forceinline__ typename Pack<DT>::T combine(typename Pack<DT>::T acc
     }
 }
 
-// Vector forms. ``first`` starts a chain: round(pre(x)).
-template <int DT, int OP> __device__ __forceinline__ Pack<DT> first(const Pack<DT> &x, float s) {
+// Vector forms. ``first`` starts a chain: pre(x), rounded to the storage type
+// unless the partials are kept in fp32 (keep32: bf16 / fp16 accumulation in
+// fp32, rounded once where the reduction completes).
+template <int DT, int OP> __device__ __forceinline__ Pack<DT> first(const Pack<DT> &x, float s, bool keep32 = false) {
     Pack<DT> r;
 #pragma unroll
     for (int i = 0; i < Pack<DT>::K; ++i) {
         if constexpr (DT == I32) r.v[i] = x.v[i];
-        else r.v[i] = round_to<DT>(pre<DT, OP>(x.v[i], s));
+        else {
+            const float v = pre<DT, OP>(x.v[i], s);
+            r.v[i] = keep32 ? v : round_to<DT>(v);
+        }
     }
     return r;
 }
 
-// One hop: acc = round(acc (+) pre(own)).
-template <int DT, int OP> __device__ __forceinline__ void hop(Pack<DT> &acc, const Pack<DT> &own, float s) {
+// One hop: acc = round(acc (+) pre(own)) (no rounding with keep32).
+template <int DT, int OP>
+__device__ __forceinline__ void hop(Pack<DT> &acc, const Pack<DT> &own, float s, bool keep32 = false) {
 #pragma unroll
     for (int i = 0; i < Pack<DT>::K; ++i) {
         if constexpr (DT == I32) acc.v[i] = combine<DT, OP>(acc.v[i], own.v[i]);
-        else acc.v[i] = round_to<DT>(combine<DT, OP>(acc.v[i], pre<DT, OP>(own.v[i], s)));
+        else {
+            const float v = combine<DT, OP>(acc.v[i], pre<DT, OP>(own.v[i], s));
+            acc.v[i] = keep32 ? v : round_to<DT>(v);
+        }
     }
 }
 
@@ -159,11 +184,24 @@ template <int DT, int OP> __device__ __forceinline__ void merge(Pack<DT> &acc, c
     }
 }
 
-// The fixup where a chunk completes: int32 avg divides by n once.
-template <int DT, int OP> __device__ __forceinline__ void post(Pack<DT> &acc, int n) {
-    if constexpr (DT == I32 && OP == AVG) {
+// Where a reduction completes (the postOp): int32 avg divides the wrapped sum
+// by n once; the split float avg divides the finished sum by g.post_div
+// (n / p) in fp32; a result kept in fp32 (g.acc32) or divided is rounded to
+// the storage type.  ``G`` is the launch geometry (post_div, acc32).
+template <int DT, int OP, typename G> __device__ __forceinline__ void finish(Pack<DT> &acc, int n, const G &g) {
+    if constexpr (DT == I32) {
+        if constexpr (OP == AVG) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc.v[i] = (uint32_t)((int32_t)acc.v[i] / n);
+            for (int i = 0; i < 4; ++i) acc.v[i] = (uint32_t)((int32_t)acc.v[i] / n);
+        }
+    } else {
+        const bool divide = OP == AVG && g.post_div != 0.0f;
+#pragma unroll
+        for (int i = 0; i < Pack<DT>::K; ++i) {
+            float v = acc.v[i];
+            if (divide) v = v / g.post_div;
+            acc.v[i] = (g.acc32 || divide) ? round_to<DT>(v) : v;
+        }
     }
 }
 
@@ -182,15 +220,20 @@ template <int DT> __device__ __forceinline__ void store1(void *p, long long i, t
     else ((_Float16 *)p)[i] = (_Float16)v;
 }
 
-template <int DT, int OP> __device__ __forceinline__ typename Pack<DT>::T first1(typename Pack<DT>::T x, float s) {
+template <int DT, int OP>
+__device__ __forceinline__ typename Pack<DT>::T first1(typename Pack<DT>::T x, float s, bool keep32 = false) {
     if constexpr (DT == I32) return x;
-    else return round_to<DT>(pre<DT, OP>(x, s));
+    else return keep32 ? pre<DT, OP>(x, s) : round_to<DT>(pre<DT, OP>(x, s));
 }
 
 template <int DT, int OP>
-__device__ __forceinline__ typename Pack<DT>::T hop1(typename Pack<DT>::T acc, typename Pack<DT>::T own, float s) {
+__device__ __forceinline__ typename Pack<DT>::T hop1(typename Pack<DT>::T acc, typename Pack<DT>::T own, float s,
+                                                     bool keep32 = false) {
     if constexpr (DT == I32) return combine<DT, OP>(acc, own);
-    else return round_to<DT>(combine<DT, OP>(acc, pre<DT, OP>(own, s)));
+    else {
+        const float v = combine<DT, OP>(acc, pre<DT, OP>(own, s));
+        return keep32 ? v : round_to<DT>(v);
+    }
 }
 
 template <int DT, int OP>
@@ -199,9 +242,16 @@ __device__ __forceinline__ typename Pack<DT>::T merge1(typename Pack<DT>::T acc,
     else return round_to<DT>(combine<DT, OP>(acc, other));
 }
 
-template <int DT, int OP> __device__ __forceinline__ typename Pack<DT>::T post1(typename Pack<DT>::T acc, int n) {
-    if constexpr (DT == I32 && OP == AVG) return (uint32_t)((int32_t)acc / n);
-    else return acc;
+template <int DT, int OP, typename G>
+__device__ __forceinline__ typename Pack<DT>::T finish1(typename Pack<DT>::T acc, int n, const G &g) {
+    if constexpr (DT == I32) {
+        if constexpr (OP == AVG) return (uint32_t)((int32_t)acc / n);
+        else return acc;
+    } else {
+        const bool divide = OP == AVG && g.post_div != 0.0f;
+        const float v = divide ? acc / g.post_div : acc;
+        return (g.acc32 || divide) ? round_to<DT>(v) : v;
+    }
 }
 
 // Streaming 16-byte loads and stores: every byte is touched once, so they are

@@ -34,6 +34,8 @@ struct Geometry {
     float s;            // fp32(1/n), the float avg pre-scale
     long long ref;      // fused / split: address / 16 of the buffer whose alignment cuts the tiles
     long long split;    // double tree: vectors [0, split) go up the first tree, the rest up the second
+    float post_div;     // split float avg: the finished sum is divided by n / p (0: no post-division)
+    int acc32;          // bf16 / fp16 partials kept in fp32, rounded once (the fused schedule)
 };
 
 // Tiles are cut on a grid aligned to absolute T-vector boundaries of a

@@ -26,14 +26,14 @@ __global__ __launch_bounds__(kThreads) void elem_ring_allreduce_kernel(const Ran
          e += (long long)gridDim.x * kThreads) {
         const long long vec = e / Lanes<DT>::value;
         const int c = (int)(((vec + 1) * n - 1) / g.V);
-        typename Pack<DT>::T acc = first1<DT, OP>(load1<DT>(t.src[add_mod(c, 1 % n, n)], e), g.s);
+        typename Pack<DT>::T acc = first1<DT, OP>(load1<DT>(t.src[add_mod(c, 1 % n, n)], e), g.s, g.acc32);
         for (int k = 2; k <= n; ++k) {
             int r = c + k;
             r = r >= n ? r - n : r;
             r = r >= n ? r - n : r;
-            acc = hop1<DT, OP>(acc, load1<DT>(t.src[r], e), g.s);
+            acc = hop1<DT, OP>(acc, load1<DT>(t.src[r], e), g.s, g.acc32);
         }
-        acc = post1<DT, OP>(acc, n);
+        acc = finish1<DT, OP>(acc, n, g);
         for (int r = 0; r < n; ++r) store1<DT>(t.dst[r], e, acc);
     }
 }
@@ -59,7 +59,7 @@ __global__ __launch_bounds__(kThreads) void elem_tree_allreduce_kernel(const Ran
             }
             part[v] = acc;
         }
-        const typename Pack<DT>::T root = post1<DT, OP>(part[tree.root], n);
+        const typename Pack<DT>::T root = finish1<DT, OP>(part[tree.root], n, g);
         for (int v = 0; v < n; ++v) store1<DT>(t.dst[v], e, root);
     }
 }
@@ -76,14 +76,14 @@ __global__ __launch_bounds__(kThreads) void elem_reduce_scatter_kernel(const Ran
         const int c = (int)(q / R);
         const long long i = q - (long long)c * R;
         const long long e = (long long)c * R + i;
-        typename Pack<DT>::T acc = first1<DT, OP>(load1<DT>(t.src[add_mod(c, 1 % n, n)], e), g.s);
+        typename Pack<DT>::T acc = first1<DT, OP>(load1<DT>(t.src[add_mod(c, 1 % n, n)], e), g.s, g.acc32);
         for (int k = 2; k <= n; ++k) {
             int r = c + k;
             r = r >= n ? r - n : r;
             r = r >= n ? r - n : r;
-            acc = hop1<DT, OP>(acc, load1<DT>(t.src[r], e), g.s);
+            acc = hop1<DT, OP>(acc, load1<DT>(t.src[r], e), g.s, g.acc32);
         }
-        store1<DT>(t.dst[c], i, post1<DT, OP>(acc, n));
+        store1<DT>(t.dst[c], i, finish1<DT, OP>(acc, n, g));
     }
 }
 

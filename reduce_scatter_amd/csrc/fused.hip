@@ -51,7 +51,7 @@ __device__ __forceinline__ int hop_rank(int c, int k, int n) {
 // batch.
 template <int DT, int OP, int NR>
 __device__ __forceinline__ Pack<DT> chain(const RankTable &t, int n, int c, long long base, unsigned lane_off,
-                                          float s) {
+                                          float s, bool keep32) {
     Pack<DT> acc;
     if constexpr (NR > 0) {
         u32x4 raw[NR];
@@ -61,9 +61,9 @@ __device__ __forceinline__ Pack<DT> chain(const RankTable &t, int n, int c, long
             raw[k] = __builtin_nontemporal_load((const u32x4 *)(p + lane_off));
         }
         __builtin_amdgcn_sched_barrier(0);                   // every load issued before the first combine
-        acc = first<DT, OP>(unpack<DT>(raw[0]), s);
+        acc = first<DT, OP>(unpack<DT>(raw[0]), s, keep32);
 #pragma unroll
-        for (int k = 1; k < NR; ++k) hop<DT, OP>(acc, unpack<DT>(raw[k]), s);
+        for (int k = 1; k < NR; ++k) hop<DT, OP>(acc, unpack<DT>(raw[k]), s, keep32);
     } else {
         constexpr int B = 16;
         for (int k0 = 0; k0 < n; k0 += B) {
@@ -78,8 +78,8 @@ __device__ __forceinline__ Pack<DT> chain(const RankTable &t, int n, int c, long
 #pragma unroll
             for (int kk = 0; kk < B; ++kk) {
                 if (k0 + kk >= n) break;
-                if (k0 + kk == 0) acc = first<DT, OP>(unpack<DT>(raw[kk]), s);
-                else hop<DT, OP>(acc, unpack<DT>(raw[kk]), s);
+                if (k0 + kk == 0) acc = first<DT, OP>(unpack<DT>(raw[kk]), s, keep32);
+                else hop<DT, OP>(acc, unpack<DT>(raw[kk]), s, keep32);
             }
         }
     }
@@ -117,9 +117,9 @@ __global__ __launch_bounds__(kFusedThreads) void fused_allreduce_kernel(const Ra
     if (ts.lo >= ts.hi) return;                               // past the chunk's end: nothing in this tile
     bool ok;
     const unsigned lane_off = tile_lane(ts, ts.start + threadIdx.x, ok);
-    Pack<DT> acc = chain<DT, OP, NR>(t, n, c, ts.lo * 16, lane_off, g.s);
+    Pack<DT> acc = chain<DT, OP, NR>(t, n, c, ts.lo * 16, lane_off, g.s, g.acc32);
     if (!ok) return;
-    post<DT, OP>(acc, n);
+    finish<DT, OP>(acc, n, g);
     store_all<NR>(t, n, ts.lo * 16, lane_off, pack<DT>(acc));
 }
 
@@ -166,15 +166,15 @@ __global__ __launch_bounds__(kFusedThreads) void fused_allreduce_wide_kernel(con
             if (k0 + kk >= n) break;
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                if (k0 + kk == 0) acc[u] = first<DT, OP>(unpack<DT>(raw[kk][u]), g.s);
-                else hop<DT, OP>(acc[u], unpack<DT>(raw[kk][u]), g.s);
+                if (k0 + kk == 0) acc[u] = first<DT, OP>(unpack<DT>(raw[kk][u]), g.s, g.acc32);
+                else hop<DT, OP>(acc[u], unpack<DT>(raw[kk][u]), g.s, g.acc32);
             }
         }
     }
     u32x4 w[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        post<DT, OP>(acc[u], n);
+        finish<DT, OP>(acc[u], n, g);
         w[u] = pack<DT>(acc[u]);
     }
     for (int r = 0; r < n; ++r) {
@@ -198,9 +198,9 @@ __global__ __launch_bounds__(kFusedThreads) void fused_reduce_scatter_kernel(con
     if (ts.lo >= ts.hi) return;
     bool ok;
     const unsigned lane_off = tile_lane(ts, ts.start + threadIdx.x, ok);
-    Pack<DT> acc = chain<DT, OP, NR>(t, n, c, ((long long)c * g.Rv + ts.lo) * 16, lane_off, g.s);
+    Pack<DT> acc = chain<DT, OP, NR>(t, n, c, ((long long)c * g.Rv + ts.lo) * 16, lane_off, g.s, g.acc32);
     if (!ok) return;
-    post<DT, OP>(acc, n);
+    finish<DT, OP>(acc, n, g);
     __builtin_nontemporal_store(pack<DT>(acc), (u32x4 *)((char *)t.dst[c] + ts.lo * 16 + lane_off));
 }
 

@@ -113,7 +113,7 @@ __global__ __launch_bounds__(kThreads) void ring_allreduce_kernel(const RankTabl
                     hop<DT, OP>(acc, own, g.s);
                 }
                 if (p == n - 1) {                                  // chunk c == r completes here
-                    post<DT, OP>(acc, n);
+                    finish<DT, OP>(acc, n, g);
                     st_stream(t.dst[it.r[k]], vb[c] + pos0 + it.w[k], pack<DT>(acc));
                 }
                 *sl = pack<DT>(acc);
@@ -174,7 +174,7 @@ __global__ __launch_bounds__(kThreads) void ring_reduce_scatter_kernel(const Ran
                     hop<DT, OP>(acc, own, g.s);
                 }
                 if (p == n - 1) {
-                    post<DT, OP>(acc, n);
+                    finish<DT, OP>(acc, n, g);
                     st_stream(t.dst[it.r[k]], pos0 + it.w[k], pack<DT>(acc));
                 } else {
                     *sl = pack<DT>(acc);
@@ -275,7 +275,7 @@ __global__ __launch_bounds__(RingShape<NR>::T) void ring_allreduce_fast(const Ra
                 hop<DT, OP>(acc, unpack<DT>(raw[p]), g.s);
             }
             if (p == NR - 1) {                     // chunk r completes here: postOp, keep it
-                post<DT, OP>(acc, NR);
+                finish<DT, OP>(acc, NR, g);
                 st_stream(t.dst[r], vv[p], pack<DT>(acc));
             }
             slot[c * W + w] = pack<DT>(acc);
@@ -315,7 +315,7 @@ __global__ __launch_bounds__(RingShape<NR>::T) void ring_reduce_scatter_fast(con
                 hop<DT, OP>(acc, unpack<DT>(raw[p]), g.s);
             }
             if (p == NR - 1) {
-                post<DT, OP>(acc, NR);
+                finish<DT, OP>(acc, NR, g);
                 st_stream(t.dst[r], vpos, pack<DT>(acc));
             } else {
                 slot[c * W + w] = pack<DT>(acc);

@@ -142,7 +142,7 @@ __global__ __launch_bounds__(kFusedThreads *kSplitMaxWaves) void split_allreduce
         PairStack<DT, OP, Log2Ceil<kSplitMaxWaves>::value + 1> hi;
         push_waves<0>(hi, part + v, T, waves);
         Pack<DT> acc = hi.finish(waves);
-        post<DT, OP>(acc, n);
+        finish<DT, OP>(acc, n, g);
         part[v] = pack<DT>(acc);                                // only this thread touches index v here
     }
     __syncthreads();
@@ -181,7 +181,7 @@ __global__ __launch_bounds__(kThreads) void elem_split_allreduce_kernel(const Ra
         acc = have ? merge1<DT, OP>(st[l], acc) : st[l];
         have = true;
     }
-    acc = post1<DT, OP>(acc, n);
+    acc = finish1<DT, OP>(acc, n, g);
     for (int r = 0; r < n; ++r) store1<DT>(t.dst[r], i, acc);
 }
 

@@ -56,7 +56,7 @@ __device__ __forceinline__ void tree_window(const RankTable &t, const TreeShape 
                 const int ch = tree.child[v][e];
                 if (ch >= 0) merge<DT, OP>(acc, unpack<DT>(slot[ch * W + w[k]]));
             }
-            if (v == tree.root) post<DT, OP>(acc, n);
+            if (v == tree.root) finish<DT, OP>(acc, n, g);
             slot[v * W + w[k]] = pack<DT>(acc);
         }
         __syncthreads();
@@ -138,7 +138,7 @@ __device__ __forceinline__ void tree_window_fast(const RankTable &t, const TreeS
                 Pack<DT> acc = first<DT, OP>(unpack<DT>(own[k]), g.s);
                 if (ch0 >= 0) merge<DT, OP>(acc, unpack<DT>(slot[ch0 * W + i]));
                 if (ch1 >= 0) merge<DT, OP>(acc, unpack<DT>(slot[ch1 * W + i]));
-                if (r == root) post<DT, OP>(acc, NR);
+                if (r == root) finish<DT, OP>(acc, NR, g);
                 slot[r * W + i] = pack<DT>(acc);
             }
         }

@@ -64,6 +64,22 @@ def test_invalid_arguments_are_rejected_before_launch():
         assert _err(ar.ar_all_gather, A[:2], B[:2], 16, "f32", sched=sched) == "AR_ERR_UNSUPPORTED"
 
 
+def test_numerics_are_validated_before_launch():
+    bad = [("acc", 2), ("avg", 7), ("acc", -1)]
+    for field, value in bad:
+        kw = {"acc": "storage", "avg": "prescale"}
+        kw[field] = value
+        assert _err(ar.ar_allreduce_ex, A[:2], B[:2], 64, "bf16", "avg", **kw) == "AR_ERR_INVALID_ARG"
+        assert _err(ar.ar_reduce_scatter_ex, A[:2], B[:2], 64, "bf16", "avg", **kw) == "AR_ERR_INVALID_ARG"
+    # fp32 partials for bf16 / fp16 exist on the fused schedule only
+    for dtype in ("bf16", "f16"):
+        for sched in ("ring", "tree", "split", "dtree"):
+            assert _err(ar.ar_allreduce_ex, A[:2], B[:2], 64, dtype, "sum", sched=sched, acc="fp32") == \
+                "AR_ERR_UNSUPPORTED"
+        assert _err(ar.ar_reduce_scatter_ex, A[:2], B[:2], 64, dtype, "sum", sched="ring", acc="fp32") == \
+            "AR_ERR_UNSUPPORTED"
+
+
 def test_zero_count_is_a_no_op():
     ar.ar_allreduce(A[:2], B[:2], 0, "f32", "sum")
     ar.ar_reduce_scatter(A[:2], B[:2], 0, "bf16", "avg")

@@ -120,6 +120,14 @@ def test_c3_fsdp_reduce_scatter_then_all_gather():
         torch.cuda.synchronize()
         for r in range(n):
             assert_bits_equal(to_host(ys[r], "bf16"), want[r], "c3 rs %s rank %d" % (sched, r))
+    # reduce in fp32 at bf16 bytes: fp32 partials, one rounding
+    print("c3 rs acc32 oracle", flush=True)
+    want32 = oracle.ring_reduce_scatter(host, "bf16", "avg", acc32=True)
+    ys = [torch.empty(R, dtype=torch.bfloat16, device="cuda") for _ in range(n)]
+    ar.ar_reduce_scatter_ex(xs, ys, R, "bf16", "avg", acc="fp32")
+    torch.cuda.synchronize()
+    for r in range(n):
+        assert_bits_equal(to_host(ys[r], "bf16"), want32[r], "c3 rs acc32 rank %d" % r)
     del xs
     pieces = [workloads.device_uniform(2, 1, r, R, -1.0, 1.0, "bf16") for r in range(n)]
     cat = np.concatenate([to_host(p, "bf16") for p in pieces])

@@ -286,6 +286,75 @@ def test_tiles_cut_on_an_aligned_grid(dtype):
                     assert_bits_equal(to_host(g_out[r], dtype), gathered[r], "ag %s n=%d %s" % (sched, n, label))
 
 
+NUMERICS = [("storage", "split"), ("fp32", "prescale"), ("fp32", "split")]
+
+
+def _numerics_reference(sched, xs, dtype, op, acc, avg, coll="allreduce"):
+    kw = {"acc32": acc == "fp32", "avg_split": avg == "split"}
+    if coll == "reduce_scatter":
+        return oracle.ring_reduce_scatter(xs, dtype, op, **kw)
+    if sched == "tree":
+        return oracle.tree_allreduce(xs, dtype, op, **kw)
+    if sched == "dtree":
+        return oracle.dtree_allreduce(xs, dtype, op, **kw)
+    if sched == "split":
+        return [oracle.pairwise_reduce(xs, dtype, op, **kw)] * len(xs)
+    return oracle.ring_allreduce(xs, dtype, op, **kw)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16", "i32"])
+def test_numerics_variants_match_oracle(dtype):
+    """fp32 partials (fused; other schedules refuse bf16 / fp16) and the split
+    avg divisor (every schedule), all-reduce and reduce-scatter, against the
+    oracle with the same options; vector and element-wise paths."""
+    u = LANES[dtype]
+    for n in (3, 8, 16, 72):
+        count = 64 * u * 4 + u * 3 + 5
+        for op in ("sum", "avg", "prod", "max"):
+            xs = inputs(20, n, count, dtype, op)
+            for acc, avg in NUMERICS:
+                refuse = acc == "fp32" and dtype in ("bf16", "f16")
+                for sched in ("fused", "ring", "tree", "split", "dtree", "auto"):
+                    print("numerics", dtype, op, n, acc, avg, sched, flush=True)
+                    d_in = [to_device(x, dtype) for x in xs]
+                    d_out = [empty(count, dtype, 0) for _ in xs]
+                    if refuse and sched not in ("fused", "auto"):
+                        with pytest.raises(ar.ArError):
+                            ar.ar_allreduce_ex(d_in, d_out, count, dtype, op, sched=sched, acc=acc, avg=avg)
+                        continue
+                    ar.ar_allreduce_ex(d_in, d_out, count, dtype, op, sched=sched, acc=acc, avg=avg)
+                    sync()
+                    used = sched
+                    if sched == "auto":
+                        used = "fused" if refuse else ar.ar_plan("allreduce", count, dtype, op, n).chosen
+                    ref = _numerics_reference(used, xs, dtype, op, acc, avg)
+                    for r in (0, n - 1):
+                        assert_bits_equal(to_host(d_out[r], dtype), ref[r], "%s %s %s n=%d %s/%s rank %d" % (
+                            sched, dtype, op, n, acc, avg, r))
+                # element-wise path (buffers off 16-byte alignment), fused
+                d_in = [to_device(np.concatenate([x[:1], x]), dtype)[1:] for x in xs]
+                d_out = [empty(count + 1, dtype, 0)[1:] for _ in xs]
+                ar.ar_allreduce_ex(d_in, d_out, count, dtype, op, sched="fused", acc=acc, avg=avg)
+                sync()
+                ref = _numerics_reference("fused", xs, dtype, op, acc, avg)
+                assert_bits_equal(to_host(d_out[0], dtype), ref[0], "elem %s %s n=%d %s/%s" % (dtype, op, n, acc, avg))
+            # reduce-scatter
+            R = 64 * u * 2 + u
+            ys = inputs(21, n, n * R, dtype, op)
+            for acc, avg in NUMERICS:
+                ref = _numerics_reference("ring", ys, dtype, op, acc, avg, coll="reduce_scatter")
+                for sched in ("fused", "ring"):
+                    if acc == "fp32" and dtype in ("bf16", "f16") and sched == "ring":
+                        continue
+                    d_in = [to_device(y, dtype) for y in ys]
+                    d_out = [empty(R, dtype, 0) for _ in ys]
+                    ar.ar_reduce_scatter_ex(d_in, d_out, R, dtype, op, sched=sched, acc=acc, avg=avg)
+                    sync()
+                    for r in (0, n - 1):
+                        assert_bits_equal(to_host(d_out[r], dtype), ref[r], "rs %s %s %s n=%d %s/%s" % (
+                            sched, dtype, op, n, acc, avg))
+
+
 def test_one_hip_runtime_whatever_the_import_order():
     """Importing the binding before torch must not leave two HIP runtimes in
     the process (torch ships its own copy of libamdhip64); the call must work."""
