@@ -44,37 +44,55 @@ template <int DT> struct Pack {
 __device__ __forceinline__ float bits_f32(uint32_t u) { return __builtin_bit_cast(float, u); }
 __device__ __forceinline__ uint32_t f32_bits(float f) { return __builtin_bit_cast(uint32_t, f); }
 
-// fp32 -> nearest bf16 (ties to even), returned as the fp32 value.
-__device__ __forceinline__ float round_bf16(float f) {
-    uint32_t u = f32_bits(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return bits_f32((u | 0x00400000u) & 0xffff0000u);  // quiet NaN
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return bits_f32(u & 0xffff0000u);
+// Rounding to the storage type uses gfx950's conversions (v_cvt_pk_bf16_f32,
+// v_cvt_pk_f16_f32: round to nearest even in the default float mode, denormals
+// kept, overflow to infinity, NaN stays NaN).  The value to convert first
+// passes through an empty asm statement, so the conversion stays a separate
+// rounding of an fp32 value: without it the compiler folds an fp32 multiply
+// (or add) followed by a float-to-half conversion into one mixed-precision
+// FMA that rounds the exact result once, which differs from rounding the fp32
+// result when the operands are not already fp16 values (fp32 partials).
+__device__ __forceinline__ float fence_value(float f) {
+    asm("" : "+v"(f));
+    return f;
 }
 
-// fp32 -> nearest fp16 value (ties to even), as an fp32.  Written with exact
-// power-of-two scalings and an integer round-to-nearest-even instead of a
-// float-to-half conversion: the compiler fuses a multiply followed by that
-// conversion into one mixed-precision FMA that rounds the exact product once,
-// which differs from rounding the fp32 product when the operands are not fp16
-// values (fp32 partials).  The fp16 quantum is 2^(e-10) in the binade 2^e,
-// and 2^-24 below 2^-14 (subnormals); past the largest finite fp16 (65504)
-// the value rounds to infinity.
-__device__ __forceinline__ float round_f16(float f) {
-    const uint32_t a = f32_bits(f) & 0x7fffffffu;
-    if (a >= 0x7f800000u) return f;                                  // inf, NaN
-    int e = (int)(a >> 23) - 127;                                      // binade of |f|
-    e = e < -14 ? -14 : e;
-    const float inv_q = bits_f32((uint32_t)(127 + 10 - e) << 23);     // 2^(10-e)
-    const float q = bits_f32((uint32_t)(127 - 10 + e) << 23);         // 2^(e-10)
-    const float r = __builtin_rintf(f * inv_q) * q;
-    return __builtin_fabsf(r) > 65504.0f ? __builtin_copysignf(__builtin_inff(), f) : r;
+// fp32 -> nearest bf16 (ties to even), returned as the fp32 value.
+__device__ __forceinline__ float round_bf16(float f) { return (float)(__bf16)fence_value(f); }
+
+// fp32 -> nearest fp16 (ties to even), returned as the fp32 value.
+__device__ __forceinline__ float round_f16(float f) { return (float)(_Float16)fence_value(f); }
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// Two values rounded by one packed conversion.
+template <int DT> __device__ __forceinline__ void round_pair(float &a, float &b) {
+    const f32x2 v = {fence_value(a), fence_value(b)};
+    if constexpr (DT == BF16) {
+        const uint32_t u = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+        a = bits_f32(u << 16);
+        b = bits_f32(u & 0xffff0000u);
+    } else {
+        const f16x2 h = __builtin_convertvector(v, f16x2);
+        a = (float)h.x;
+        b = (float)h.y;
+    }
 }
 
 template <int DT> __device__ __forceinline__ float round_to(float f) {
     if (DT == BF16) return round_bf16(f);
     if (DT == F16) return round_f16(f);
     return f;
+}
+
+// Every element of a pack rounded to the storage type (no-op for fp32 / int32).
+template <int DT> __device__ __forceinline__ void round_all(Pack<DT> &p) {
+    if constexpr (DT == BF16 || DT == F16) {
+#pragma unroll
+        for (int i = 0; i < Pack<DT>::K; i += 2) round_pair<DT>(p.v[i], p.v[i + 1]);
+    }
 }
 
 template <int DT> __device__ __forceinline__ Pack<DT> unpack(u32x4 w) {
@@ -147,41 +165,29 @@ __device__ __forceinline__ typename Pack<DT>::T combine(typename Pack<DT>::T acc
 }
 
 // Vector forms. ``first`` starts a chain: pre(x), rounded to the storage type
-// unless the partials are kept in fp32 (keep32: bf16 / fp16 accumulation in
+// unless the partials are kept in fp32 (KEEP32: bf16 / fp16 accumulation in
 // fp32, rounded once where the reduction completes).
-template <int DT, int OP> __device__ __forceinline__ Pack<DT> first(const Pack<DT> &x, float s, bool keep32 = false) {
+template <int DT, int OP, bool KEEP32 = false> __device__ __forceinline__ Pack<DT> first(const Pack<DT> &x, float s) {
     Pack<DT> r;
 #pragma unroll
-    for (int i = 0; i < Pack<DT>::K; ++i) {
-        if constexpr (DT == I32) r.v[i] = x.v[i];
-        else {
-            const float v = pre<DT, OP>(x.v[i], s);
-            r.v[i] = keep32 ? v : round_to<DT>(v);
-        }
-    }
+    for (int i = 0; i < Pack<DT>::K; ++i) r.v[i] = pre<DT, OP>(x.v[i], s);
+    if constexpr (!KEEP32) round_all<DT>(r);
     return r;
 }
 
-// One hop: acc = round(acc (+) pre(own)) (no rounding with keep32).
-template <int DT, int OP>
-__device__ __forceinline__ void hop(Pack<DT> &acc, const Pack<DT> &own, float s, bool keep32 = false) {
+// One hop: acc = round(acc (+) pre(own)) (no rounding with KEEP32).
+template <int DT, int OP, bool KEEP32 = false>
+__device__ __forceinline__ void hop(Pack<DT> &acc, const Pack<DT> &own, float s) {
 #pragma unroll
-    for (int i = 0; i < Pack<DT>::K; ++i) {
-        if constexpr (DT == I32) acc.v[i] = combine<DT, OP>(acc.v[i], own.v[i]);
-        else {
-            const float v = combine<DT, OP>(acc.v[i], pre<DT, OP>(own.v[i], s));
-            acc.v[i] = keep32 ? v : round_to<DT>(v);
-        }
-    }
+    for (int i = 0; i < Pack<DT>::K; ++i) acc.v[i] = combine<DT, OP>(acc.v[i], pre<DT, OP>(own.v[i], s));
+    if constexpr (!KEEP32) round_all<DT>(acc);
 }
 
 // Combine two partials that were both already rounded (tree: parent (+) child).
 template <int DT, int OP> __device__ __forceinline__ void merge(Pack<DT> &acc, const Pack<DT> &other) {
 #pragma unroll
-    for (int i = 0; i < Pack<DT>::K; ++i) {
-        if constexpr (DT == I32) acc.v[i] = combine<DT, OP>(acc.v[i], other.v[i]);
-        else acc.v[i] = round_to<DT>(combine<DT, OP>(acc.v[i], other.v[i]));
-    }
+    for (int i = 0; i < Pack<DT>::K; ++i) acc.v[i] = combine<DT, OP>(acc.v[i], other.v[i]);
+    round_all<DT>(acc);
 }
 
 // Where a reduction completes (the postOp): int32 avg divides the wrapped sum
@@ -196,12 +202,11 @@ template <int DT, int OP, typename G> __device__ __forceinline__ void finish(Pac
         }
     } else {
         const bool divide = OP == AVG && g.post_div != 0.0f;
+        if (divide) {
 #pragma unroll
-        for (int i = 0; i < Pack<DT>::K; ++i) {
-            float v = acc.v[i];
-            if (divide) v = v / g.post_div;
-            acc.v[i] = (g.acc32 || divide) ? round_to<DT>(v) : v;
+            for (int i = 0; i < Pack<DT>::K; ++i) acc.v[i] = acc.v[i] / g.post_div;
         }
+        if (g.acc32 || divide) round_all<DT>(acc);
     }
 }
 

@@ -48,10 +48,10 @@ __device__ __forceinline__ int hop_rank(int c, int k, int n) {
 // the end of the chunk re-read its last vector and discard the result), so no
 // load sits in a divergent branch and a whole batch of loads is in flight at
 // once.  NR > 0: n == NR known at compile time; NR == 0: any n, 16 loads per
-// batch.
-template <int DT, int OP, int NR>
-__device__ __forceinline__ Pack<DT> chain(const RankTable &t, int n, int c, long long base, unsigned lane_off,
-                                          float s, bool keep32) {
+// batch.  KEEP32: bf16 / fp16 partials stay fp32 (rounded in ``finish``).
+template <int DT, int OP, int NR, bool KEEP32>
+__device__ __forceinline__ Pack<DT> chain_in(const RankTable &t, int n, int c, long long base, unsigned lane_off,
+                                             float s) {
     Pack<DT> acc;
     if constexpr (NR > 0) {
         u32x4 raw[NR];
@@ -61,9 +61,9 @@ __device__ __forceinline__ Pack<DT> chain(const RankTable &t, int n, int c, long
             raw[k] = __builtin_nontemporal_load((const u32x4 *)(p + lane_off));
         }
         __builtin_amdgcn_sched_barrier(0);                   // every load issued before the first combine
-        acc = first<DT, OP>(unpack<DT>(raw[0]), s, keep32);
+        acc = first<DT, OP, KEEP32>(unpack<DT>(raw[0]), s);
 #pragma unroll
-        for (int k = 1; k < NR; ++k) hop<DT, OP>(acc, unpack<DT>(raw[k]), s, keep32);
+        for (int k = 1; k < NR; ++k) hop<DT, OP, KEEP32>(acc, unpack<DT>(raw[k]), s);
     } else {
         constexpr int B = 16;
         for (int k0 = 0; k0 < n; k0 += B) {
@@ -78,12 +78,23 @@ __device__ __forceinline__ Pack<DT> chain(const RankTable &t, int n, int c, long
 #pragma unroll
             for (int kk = 0; kk < B; ++kk) {
                 if (k0 + kk >= n) break;
-                if (k0 + kk == 0) acc = first<DT, OP>(unpack<DT>(raw[kk]), s, keep32);
-                else hop<DT, OP>(acc, unpack<DT>(raw[kk]), s, keep32);
+                if (k0 + kk == 0) acc = first<DT, OP, KEEP32>(unpack<DT>(raw[kk]), s);
+                else hop<DT, OP, KEEP32>(acc, unpack<DT>(raw[kk]), s);
             }
         }
     }
     return acc;
+}
+
+// The chain with the partials' precision chosen once per tile (a uniform
+// branch; only bf16 / fp16 have two).
+template <int DT, int OP, int NR>
+__device__ __forceinline__ Pack<DT> chain(const RankTable &t, int n, int c, long long base, unsigned lane_off,
+                                          float s, bool keep32) {
+    if constexpr (DT == BF16 || DT == F16) {
+        if (keep32) return chain_in<DT, OP, NR, true>(t, n, c, base, lane_off, s);
+    }
+    return chain_in<DT, OP, NR, false>(t, n, c, base, lane_off, s);
 }
 
 template <int NR>
@@ -134,8 +145,8 @@ template <int DT> struct WideTile {
     static constexpr int B = 2;
 };
 
-template <int DT, int OP>
-__global__ __launch_bounds__(kFusedThreads) void fused_allreduce_wide_kernel(const RankTable t, const Geometry g) {
+template <int DT, int OP, bool KEEP32>
+__device__ __forceinline__ void fused_allreduce_wide(const RankTable &t, const Geometry &g) {
     constexpr int U = WideTile<DT>::U, B = WideTile<DT>::B;
     const int n = g.n;
     int c;
@@ -166,8 +177,8 @@ __global__ __launch_bounds__(kFusedThreads) void fused_allreduce_wide_kernel(con
             if (k0 + kk >= n) break;
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                if (k0 + kk == 0) acc[u] = first<DT, OP>(unpack<DT>(raw[kk][u]), g.s, g.acc32);
-                else hop<DT, OP>(acc[u], unpack<DT>(raw[kk][u]), g.s, g.acc32);
+                if (k0 + kk == 0) acc[u] = first<DT, OP, KEEP32>(unpack<DT>(raw[kk][u]), g.s);
+                else hop<DT, OP, KEEP32>(acc[u], unpack<DT>(raw[kk][u]), g.s);
             }
         }
     }
@@ -183,6 +194,17 @@ __global__ __launch_bounds__(kFusedThreads) void fused_allreduce_wide_kernel(con
         for (int u = 0; u < U; ++u)
             if (ok[u]) __builtin_nontemporal_store(w[u], (u32x4 *)(p + off[u]));
     }
+}
+
+template <int DT, int OP>
+__global__ __launch_bounds__(kFusedThreads) void fused_allreduce_wide_kernel(const RankTable t, const Geometry g) {
+    if constexpr (DT == BF16 || DT == F16) {
+        if (g.acc32) {
+            fused_allreduce_wide<DT, OP, true>(t, g);
+            return;
+        }
+    }
+    fused_allreduce_wide<DT, OP, false>(t, g);
 }
 
 // Reduce-scatter: output vector v of rank c is chunk c's reduction over input

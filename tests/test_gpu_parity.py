@@ -355,6 +355,36 @@ def test_numerics_variants_match_oracle(dtype):
                             sched, dtype, op, n, acc, avg))
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+def test_float_extremes_match_oracle(dtype):
+    """Subnormal-range contributions (the rounding of partials and of the
+    avg pre-scale among subnormals), sums and products that overflow to +inf,
+    and ±0 from underflowing products, on every schedule and with both
+    numerics options: the storage-type conversions keep subnormals and round
+    to nearest even like the oracle's."""
+    u = LANES[dtype]
+    for n in (3, 8):
+        count = 64 * u * 3 + 7
+        xs = [workloads.random_values(30, n, r, count, dtype, "extremes") for r in range(n)]
+        for op in OPS:
+            for sched in ("fused", "ring", "tree", "split", "dtree"):
+                print("extremes", dtype, op, n, sched, flush=True)
+                got = run_allreduce(xs, dtype, op, sched)
+                ref = reference(sched, xs, dtype, op)
+                for r in (0, n - 1):
+                    assert_bits_equal(got[r], ref[r], "extremes %s %s %s n=%d rank %d" % (sched, dtype, op, n, r))
+            for acc, avg in NUMERICS:
+                sched = "fused" if acc == "fp32" else "ring"
+                print("extremes", dtype, op, n, acc, avg, sched, flush=True)
+                d_in = [to_device(x, dtype) for x in xs]
+                d_out = [empty(count, dtype, 0) for _ in xs]
+                ar.ar_allreduce_ex(d_in, d_out, count, dtype, op, sched=sched, acc=acc, avg=avg)
+                sync()
+                ref = _numerics_reference(sched, xs, dtype, op, acc, avg)
+                assert_bits_equal(to_host(d_out[0], dtype), ref[0], "extremes %s %s n=%d %s/%s" % (
+                    dtype, op, n, acc, avg))
+
+
 def test_one_hip_runtime_whatever_the_import_order():
     """Importing the binding before torch must not leave two HIP runtimes in
     the process (torch ships its own copy of libamdhip64); the call must work."""

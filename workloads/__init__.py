@@ -88,8 +88,36 @@ def uniform(seed, stream, rank, count, lo, hi, dtype="f32"):
     return _f32_to_bf16_bits_host(v)
 
 
+# Scales of the ``extremes`` test data per float type: a factor that puts
+# N(0,1) samples among the type's subnormals, and a large magnitude whose sums
+# over a few ranks overflow to infinity.
+_TINY = {"f32": 2.0 ** -140, "bf16": 2.0 ** -130, "f16": 2.0 ** -20}
+_HUGE = {"f32": 2.0 ** 127, "bf16": 2.0 ** 127, "f16": 2.0 ** 14}
+
+
+def extremes(seed, stream, rank, count, dtype):
+    """Float test data by element position (the same class on every rank):
+    i % 4 == 0: N(0,1); 1: subnormal-range values; 2: large positive values
+    (sums and products overflow to +inf, never inf - inf); 3: N(0,1) on even
+    ranks, subnormal-range on odd ones."""
+    g = rng(seed, stream, rank)
+    z = g.standard_normal(count)
+    big = g.uniform(0.5, 1.0, size=count)
+    cls = np.arange(count) % 4
+    tiny = _TINY[dtype]
+    v = np.where(cls == 0, z, np.where(cls == 1, z * tiny, np.where(cls == 2, big * _HUGE[dtype],
+                                                                     z * (1.0 if rank % 2 == 0 else tiny))))
+    if dtype == "f16":
+        return v.astype(np.float16)
+    v32 = v.astype(np.float32)
+    return v32 if dtype == "f32" else _f32_to_bf16_bits_host(v32)
+
+
 def random_values(seed, stream, rank, count, dtype, kind="normal"):
-    """Generic test data: ``normal`` (N(0,1)), ``ints`` (small integers) or ``pos`` (uniform [0.5, 2])."""
+    """Generic test data: ``normal`` (N(0,1)), ``ints`` (small integers), ``pos``
+    (uniform [0.5, 2]) or ``extremes`` (float types: subnormals and overflow)."""
+    if kind == "extremes":
+        return extremes(seed, stream, rank, count, dtype)
     if kind == "ints":
         lo, hi = (-(1 << 20), 1 << 20) if dtype == "i32" else (-8, 8)
         return ints(seed, stream, rank, count, lo, hi, dtype)
