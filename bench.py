@@ -137,7 +137,8 @@ def sweep():
     import torch
     import reduce_scatter_amd as ar
     import workloads as wl
-    out = ["# Workload sweep (MI355X)", "", "GPU time per call = median over 10 calls of an event pair around each call; "
+    out = ["# Workload sweep (MI355X)", "", "Command: `python bench.py --sweep` (from the repository root).", "",
+           "GPU time per call = median over 10 calls of an event pair around each call; "
            "HBM GB/s = algorithmic bytes / time; % of the 8 TB/s peak.", ""]
 
     # n = 4, fp32, 1024 elements: the latency regime

@@ -80,11 +80,13 @@ int grid_for(long long units, int cus, int per_cu) {
 
 // Dynamic LDS (bytes) a fused workgroup reserves to cap how many one-wave
 // workgroups are resident per CU (LDS is 160 KB per CU on gfx950).  Measured
-// on MI355X with gradient-like data (n = 8): the all-reduce (n loads and n
-// stores per lane) is fastest at about 6 resident workgroups per CU, the
-// all-gather (1 load, n stores) at about 7, and the reduce-scatter (n loads,
-// 1 store) with no cap at all.  AR_FUSED_LDS_KB overrides all three.
-int fused_lds_bytes(ar_coll_t coll) {
+// on MI355X with gradient-like data: the all-reduce (n loads and n stores per
+// lane) wants fewer resident workgroups the more ranks it streams (the
+// per-rank-count table in ar_kernels.hpp; past 16 ranks the wide kernel runs
+// uncapped), the all-gather (1 load, n stores) about 7 per CU at n = 8, and
+// the reduce-scatter (n loads, 1 store) no cap at all.  AR_FUSED_LDS_KB
+// overrides all of them.
+int fused_lds_bytes(ar_coll_t coll, int n) {
     static int env = -2;
     if (env == -2) {
         const char *e = getenv("AR_FUSED_LDS_KB");
@@ -93,7 +95,11 @@ int fused_lds_bytes(ar_coll_t coll) {
     }
     if (env >= 0) return env * 1024;
     switch (coll) {
-    case AR_COLL_ALLREDUCE: return kFusedLdsAllReduceKB * 1024;
+    case AR_COLL_ALLREDUCE: {
+        int lg = 0;
+        while ((1 << lg) < n) ++lg;
+        return (lg < 5 ? kFusedLdsAllReduceByLog2N[lg] : kFusedLdsAllReduceKB) * 1024;
+    }
     case AR_COLL_ALL_GATHER: return kFusedLdsAllGatherKB * 1024;
     default: return kFusedLdsReduceScatterKB * 1024;
     }
@@ -369,7 +375,7 @@ ar_status_t ar_allreduce_ex(const void *const *sendbufs, void *const *recvbufs, 
             const long long maxlen = (g.V + n - 1) / n;                       // longest chunk, in vectors
             g.windows = aligned_tiles(maxlen, kFusedTile);
             if (g.windows > 0x7fffffffLL) return AR_ERR_UNSUPPORTED;   // grid x limit
-            h = launch_fused_allreduce(dtype, op, t, g, fused_lds_bytes(AR_COLL_ALLREDUCE), stream);
+            h = launch_fused_allreduce(dtype, op, t, g, fused_lds_bytes(AR_COLL_ALLREDUCE, n), stream);
         } else if (use == AR_SCHED_RING) {
             g.W = lds_window(n);
             const long long maxlen = (g.V + n - 1) / n;
@@ -431,7 +437,7 @@ ar_status_t ar_reduce_scatter_ex(const void *const *sendbufs, void *const *recvb
     if (use == AR_SCHED_FUSED) {
         g.windows = aligned_tiles(g.Rv, kFusedTile);
         if (g.windows > 0x7fffffffLL) return AR_ERR_UNSUPPORTED;   // grid x limit
-        return hip_status(launch_fused_reduce_scatter(dtype, op, t, g, fused_lds_bytes(AR_COLL_REDUCE_SCATTER), stream));
+        return hip_status(launch_fused_reduce_scatter(dtype, op, t, g, fused_lds_bytes(AR_COLL_REDUCE_SCATTER, n), stream));
     }
     g.W = lds_window(n);
     g.windows = (g.Rv + g.W - 1) / g.W;
@@ -472,7 +478,7 @@ ar_status_t ar_all_gather(const void *const *sendbufs, void *const *recvbufs, si
     if (use == AR_SCHED_FUSED) {
         g.windows = aligned_tiles(g.Rv, kFusedTile);
         if (g.windows > 0x7fffffffLL) return AR_ERR_UNSUPPORTED;   // grid x limit
-        return hip_status(launch_fused_all_gather(t, g, fused_lds_bytes(AR_COLL_ALL_GATHER), stream));
+        return hip_status(launch_fused_all_gather(t, g, fused_lds_bytes(AR_COLL_ALL_GATHER, n), stream));
     }
     g.W = lds_window(n);
     g.windows = (g.Rv + g.W - 1) / g.W;

@@ -125,7 +125,12 @@ constexpr int kThreads = 256;
 constexpr int kFusedThreads = 64;
 constexpr int kFusedTile = kFusedThreads;
 // Default dynamic-LDS reservation of a fused workgroup, in KB, per collective
-// (caps the resident workgroups per CU; see fused.hip and api.cpp).
+// (caps the resident workgroups per CU; see fused.hip and api.cpp).  The
+// all-reduce's reservation grows with the rank count (index: ceil(log2 n),
+// n <= 16): every resident wave has 2n DRAM streams open, and the best
+// number of resident waves per CU falls as n grows (about 20 at n = 2, 11 at
+// n = 4, 6 at n = 8, 5 at n = 16 measured on MI355X, 256 MB - 1 GB per rank).
+constexpr int kFusedLdsAllReduceByLog2N[5] = {0, 8, 14, 24, 32};
 constexpr int kFusedLdsAllReduceKB = 24;
 constexpr int kFusedLdsReduceScatterKB = 0;
 constexpr int kFusedLdsAllGatherKB = 22;
