@@ -25,6 +25,10 @@ functions follow:
   everyone shows their piece" and "Why backward needs a different collective":
   the semantics of reduce-scatter (rank r keeps slice r) and all-gather.
 
+The M-to-N layout reshard of the "NCCL M2N" paper (arxiv.org/html/2610.07516)
+has its own oracle in :mod:`oracle.reshard` (plain numpy: layouts, Eq. (1)
+and (2), the reshard's definition, the §V-A schedule and §V-B leaders).
+
 Array conventions: ``f32`` arrays are ``np.float32``, ``f16`` arrays are
 ``np.float16``, ``i32`` arrays are ``np.int32`` and ``bf16`` arrays are
 ``np.uint16`` holding the bfloat16 bit patterns.
