@@ -2,7 +2,8 @@
 MI355X, with the n rank buffers resident in its HBM.
 
 This package is a thin ctypes binding over ``libar.so`` (HIP kernels for
-gfx950 plus the C ABI declared in ``include/ar.h``).  The functions keep the C
+gfx950 plus the C ABI declared in ``include/ar.h`` and, for the M-to-N layout
+reshard, ``include/ar_reshard.h``).  The functions keep the C
 names and only marshal arguments: every step of the collective runs in the
 library's kernels.  There is no CPU fallback; importing the package fails
 loudly when the library has not been built (``python
@@ -30,6 +31,11 @@ from ._binding import (  # noqa: F401
     ar_dtree_parent,
     library_path,
     pointers,
+    REPLICATE,
+    ROUTES,
+    ReshardPlan,
+    ar_reshard,
+    ar_reshard_plan,
 )
 
 __all__ = [
@@ -52,4 +58,9 @@ __all__ = [
     "library_path",
     "pointers",
     "PointerTable",
+    "REPLICATE",
+    "ROUTES",
+    "ReshardPlan",
+    "ar_reshard",
+    "ar_reshard_plan",
 ]

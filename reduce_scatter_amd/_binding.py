@@ -238,3 +238,94 @@ def ar_tree_parent(n: int, v: int) -> int:
 
 def ar_dtree_parent(n: int, which: int, v: int) -> int:
     return int(_lib.ar_dtree_parent(n, which, v))
+
+
+# ---------------------------------------------------------------------------
+# M-to-N layout reshard (include/ar_reshard.h)
+# ---------------------------------------------------------------------------
+
+REPLICATE = -1
+ROUTES = {"auto": 0, "flat": 1, "hier": 2, "fused": 3}
+_ROUTE_NAMES = {v: k for k, v in ROUTES.items()}
+
+
+class _Layout(ctypes.Structure):
+    _fields_ = [("ndim", ctypes.c_int), ("shape", ctypes.c_longlong * 3), ("mesh_ndim", ctypes.c_int),
+                ("mesh", ctypes.c_int * 2), ("placement", ctypes.c_int * 2), ("base_rank", ctypes.c_int)]
+
+
+class _Transfer(ctypes.Structure):
+    _fields_ = [("src_rank", ctypes.c_int), ("dst_rank", ctypes.c_int), ("leader_rank", ctypes.c_int),
+                ("lo", ctypes.c_longlong * 3), ("hi", ctypes.c_longlong * 3), ("bytes", ctypes.c_longlong)]
+
+
+class _ReshardPlanStruct(ctypes.Structure):
+    _fields_ = [("chosen", ctypes.c_int), ("n_transfers", ctypes.c_int), ("n_sources", ctypes.c_int),
+                ("n_shards", ctypes.c_int), ("max_replicas", ctypes.c_int), ("unique_bytes", ctypes.c_longlong),
+                ("bytes", ctypes.c_double * 4), ("launches", ctypes.c_int * 4), ("predicted_us", ctypes.c_double * 4)]
+
+
+_lib.ar_reshard_plan.argtypes = [ctypes.POINTER(_Layout), ctypes.POINTER(_Layout), ctypes.c_size_t, ctypes.c_int,
+                                 ctypes.POINTER(_ReshardPlanStruct), ctypes.POINTER(_Transfer), ctypes.c_int]
+_lib.ar_reshard_plan.restype = ctypes.c_int
+_lib.ar_reshard.argtypes = [_vpp, _vpp, ctypes.POINTER(_Layout), ctypes.POINTER(_Layout), ctypes.c_size_t,
+                            ctypes.c_int, ctypes.c_void_p]
+_lib.ar_reshard.restype = ctypes.c_int
+
+
+def _layout(L):
+    """Any object with ``shape``, ``mesh``, ``placements`` (REPLICATE or the
+    sharded tensor dimension per mesh axis) and optionally ``base_rank``."""
+    s = _Layout()
+    shape, mesh, pl = tuple(L.shape), tuple(L.mesh), tuple(L.placements)
+    if not (1 <= len(shape) <= 3 and 1 <= len(mesh) <= 2 and len(pl) == len(mesh)):
+        raise ValueError("a layout has 1-3 tensor dimensions and 1-2 mesh axes, one placement per axis")
+    s.ndim, s.mesh_ndim = len(shape), len(mesh)
+    for d, v in enumerate(shape):
+        s.shape[d] = int(v)
+    for k in range(len(mesh)):
+        s.mesh[k] = int(mesh[k])
+        s.placement[k] = int(pl[k])
+    s.base_rank = int(getattr(L, "base_rank", 0))
+    return s
+
+
+@dataclass
+class ReshardPlan:
+    chosen: str
+    n_transfers: int
+    n_sources: int
+    n_shards: int
+    max_replicas: int
+    unique_bytes: int
+    bytes: dict
+    launches: dict
+    predicted_us: dict
+    transfers: list        # (src_rank, dst_rank, leader_rank, [(lo, hi)] per tensor dim, bytes)
+
+
+def ar_reshard_plan(src, dst, elem_size, domains=1) -> ReshardPlan:
+    """The layout-derived schedule and route costs (host only)."""
+    ls, ld = _layout(src), _layout(dst)
+    out = _ReshardPlanStruct()
+    _check(_lib.ar_reshard_plan(ctypes.byref(ls), ctypes.byref(ld), elem_size, domains, ctypes.byref(out), None, 0))
+    n = out.n_transfers
+    arr = (_Transfer * max(1, n))()
+    _check(_lib.ar_reshard_plan(ctypes.byref(ls), ctypes.byref(ld), elem_size, domains, ctypes.byref(out), arr, n))
+    nd = ls.ndim
+    transfers = [(t.src_rank, t.dst_rank, t.leader_rank, [(t.lo[d], t.hi[d]) for d in range(nd)], t.bytes)
+                 for t in arr[:n]]
+    names = ("flat", "hier", "fused")
+    return ReshardPlan(_ROUTE_NAMES[out.chosen], n, out.n_sources, out.n_shards, out.max_replicas,
+                       out.unique_bytes, {k: out.bytes[ROUTES[k]] for k in names},
+                       {k: out.launches[ROUTES[k]] for k in names},
+                       {k: out.predicted_us[ROUTES[k]] for k in names}, transfers)
+
+
+def ar_reshard(src_bufs, dst_bufs, src, dst, elem_size, route="auto", stream=None):
+    """Reshard from layout ``src`` (buffers ``src_bufs``, one per source mesh
+    slot; None allowed for replicas that are not the owner of their shard)
+    to layout ``dst`` (``dst_bufs``, one per destination slot)."""
+    ls, ld = _layout(src), _layout(dst)
+    _check(_lib.ar_reshard(_ptr_array(src_bufs), _ptr_array(dst_bufs), ctypes.byref(ls), ctypes.byref(ld),
+                           elem_size, _code(ROUTES, route, "route"), _stream(stream)))
