@@ -52,6 +52,8 @@ def parse():
     p.add_argument("--no-detail", action="store_true")
     p.add_argument("--copy-probe", action="store_true",
                    help="time only a plain device copy of 2 GB (for HBM counter calibration) and exit")
+    p.add_argument("--reshard", action="store_true",
+                   help="instead of the JSON line, print the M-to-N reshard report (MoE layer, every route)")
     p.add_argument("--sweep", action="store_true",
                    help="instead of the JSON line, print a markdown report over every workload: the n=4 latency "
                         "case, the FSDP-shard reduce-scatter/all-gather, the n=16 int32 size sweep with the "
@@ -236,7 +238,42 @@ def sweep():
     out += ["", "Planner choice for a 25 MB bucket: %s." % ar.ar_plan("allreduce", (25 << 20) // 4, "f32", "avg", n).chosen, ""]
     del grads, views
     torch.cuda.empty_cache()
+    out += reshard_report()
     print("\n".join(out), flush=True)
+
+
+def reshard_report():
+    """The M-to-N reshard of the NCCL M2N paper's single-layer microbenchmark
+    on one GPU: a [256, 2048, 7168] bf16 tensor (7168 MB) from 16 EP shards
+    (Shard(0)) to TP8 x DP r_d (Shard(1), r_d replicas), every route.  HBM
+    GB/s = the route's own bytes / time; "vs fused bound" = (1 + r_d) * B /
+    time, B the unique payload (each source byte read once, each destination
+    byte written once)."""
+    import torch
+    import reduce_scatter_amd as ar
+    S = (256, 2048, 7168)
+    src = ar.Layout(S, (1, 16), (ar.REPLICATE, 0), 0)
+    src_t = [torch.empty(ar.local_shape(src, s), dtype=torch.bfloat16, device="cuda").uniform_(-1, 1)
+             for s in range(16)]
+    out = ["## M-to-N reshard, [256, 2048, 7168] bf16 (7168 MB), 16 EP shards -> TP8 x DP r_d, one GPU", "",
+           "| r_d | route | ms | route bytes (GB) | HBM GB/s | % peak | vs fused bound GB/s | planner |",
+           "|---|---|---|---|---|---|---|---|"]
+    for rd in (2, 4, 8):
+        dst = ar.Layout(S, (rd, 8), (ar.REPLICATE, 1), 16)
+        dst_t = [torch.empty(ar.local_shape(dst, t), dtype=torch.bfloat16, device="cuda") for t in range(8 * rd)]
+        sp, dp = ar.pointers(src_t), ar.pointers(dst_t)
+        plan = ar.ar_reshard_plan(src, dst, 2)
+        bound = (1 + rd) * plan.unique_bytes
+        for route in ("flat", "hier", "fused"):
+            us = _median_us(lambda: ar.ar_reshard(sp, dp, src, dst, 2, route=route), iters=5, warmup=1)
+            b = plan.bytes[route]
+            out.append("| %d | %s | %.3f | %.1f | %.0f | %.1f | %.0f | %s |" % (
+                rd, route, us / 1e3, b / 1e9, b / us / 1e3, b / us / 1e3 / PEAK_HBM_GBPS * 100, bound / us / 1e3,
+                "chosen" if plan.chosen == route else ""))
+        del dst_t, dp
+        torch.cuda.empty_cache()
+    out.append("")
+    return out
 
 
 def cpu_baseline():
@@ -278,6 +315,9 @@ def main():
         return 0
     if args.sweep:
         sweep()
+        return 0
+    if args.reshard:
+        print("\n".join(reshard_report()), flush=True)
         return 0
 
     import reduce_scatter_amd as ar

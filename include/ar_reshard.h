@@ -112,6 +112,14 @@ typedef struct {
     double predicted_us[4];     /* launches * launch_us + bytes / bandwidth */
 } ar_reshard_plan_t;
 
+/* Eq. (2) and Eq. (1): the local shard of mesh slot ``slot`` under
+ * ``layout`` as [lo[d], hi[d]) per tensor dimension (AR_RESHARD_MAX_DIMS
+ * entries each; unused dimensions [0, 1)), and its communicator rank in
+ * ``*rank`` when ``rank`` is not NULL.  A local buffer of that slot holds
+ * prod(hi - lo) elements.  AR_ERR_INVALID_ARG for a malformed layout or a
+ * slot outside [0, D_0 * D_1); AR_ERR_UNSUPPORTED as ar_reshard_plan. */
+ar_status_t ar_layout_shard(const ar_layout_t *layout, int slot, long long *lo, long long *hi, int *rank);
+
 /* Plan a reshard from ``src`` to ``dst`` for elements of ``elem_size`` bytes,
  * with the destination replicas of every shard split evenly over ``domains``
  * domains (leaders come from the first; 1 = every replica local, the
@@ -128,9 +136,11 @@ ar_status_t ar_reshard_plan(const ar_layout_t *src, const ar_layout_t *dst, size
 /* Run the reshard on ``stream`` with ``route`` (AR_ROUTE_AUTO: the cost
  * model's choice).  ``src_bufs[s]`` must be valid for every owner source slot
  * (NULL allowed for the other replicas); ``dst_bufs[t]`` for every
- * destination slot.  Errors as ar_reshard_plan, plus AR_ERR_INVALID_ARG for a
- * NULL buffer that is needed or overlapping buffers, AR_ERR_ALIGNMENT for a
- * pointer not aligned to elem_size, AR_ERR_HIP for a failed launch. */
+ * destination slot; NULL is also allowed for any slot whose shard has no
+ * elements (Eq. (2) gives empty shards when D_k > S_d).  Errors as
+ * ar_reshard_plan, plus AR_ERR_INVALID_ARG for a NULL buffer that is needed
+ * or overlapping buffers, AR_ERR_ALIGNMENT for a pointer not aligned to
+ * elem_size, AR_ERR_HIP for a failed launch. */
 ar_status_t ar_reshard(const void *const *src_bufs, void *const *dst_bufs, const ar_layout_t *src,
                        const ar_layout_t *dst, size_t elem_size, ar_route_t route, hipStream_t stream);
 

@@ -33,9 +33,12 @@ from ._binding import (  # noqa: F401
     pointers,
     REPLICATE,
     ROUTES,
+    Layout,
     ReshardPlan,
+    ar_layout_shard,
     ar_reshard,
     ar_reshard_plan,
+    local_shape,
 )
 
 __all__ = [
@@ -60,7 +63,10 @@ __all__ = [
     "PointerTable",
     "REPLICATE",
     "ROUTES",
+    "Layout",
     "ReshardPlan",
+    "ar_layout_shard",
     "ar_reshard",
     "ar_reshard_plan",
+    "local_shape",
 ]

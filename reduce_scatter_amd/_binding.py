@@ -273,6 +273,22 @@ _lib.ar_reshard.argtypes = [_vpp, _vpp, ctypes.POINTER(_Layout), ctypes.POINTER(
 _lib.ar_reshard.restype = ctypes.c_int
 
 
+@dataclass(frozen=True)
+class Layout:
+    """An endpoint layout (S, M, p): global ``shape``, ``mesh`` extents, one
+    placement per mesh axis (REPLICATE or the sharded tensor dimension) and
+    the mesh's ``base_rank``."""
+    shape: tuple
+    mesh: tuple
+    placements: tuple
+    base_rank: int = 0
+
+
+_lib.ar_layout_shard.argtypes = [ctypes.POINTER(_Layout), ctypes.c_int, ctypes.POINTER(ctypes.c_longlong),
+                                 ctypes.POINTER(ctypes.c_longlong), ctypes.POINTER(ctypes.c_int)]
+_lib.ar_layout_shard.restype = ctypes.c_int
+
+
 def _layout(L):
     """Any object with ``shape``, ``mesh``, ``placements`` (REPLICATE or the
     sharded tensor dimension per mesh axis) and optionally ``base_rank``."""
@@ -288,6 +304,19 @@ def _layout(L):
         s.placement[k] = int(pl[k])
     s.base_rank = int(getattr(L, "base_rank", 0))
     return s
+
+
+def ar_layout_shard(layout, slot):
+    """([(lo, hi)] per tensor dimension, communicator rank) of mesh slot ``slot``."""
+    L = _layout(layout)
+    lo, hi, rank = (ctypes.c_longlong * 3)(), (ctypes.c_longlong * 3)(), ctypes.c_int()
+    _check(_lib.ar_layout_shard(ctypes.byref(L), slot, lo, hi, ctypes.byref(rank)))
+    return [(lo[d], hi[d]) for d in range(L.ndim)], rank.value
+
+
+def local_shape(layout, slot):
+    """Shape of mesh slot ``slot``'s local buffer."""
+    return tuple(h - l for l, h in ar_layout_shard(layout, slot)[0])
 
 
 @dataclass

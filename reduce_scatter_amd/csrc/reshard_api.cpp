@@ -24,14 +24,20 @@ namespace {
 
 constexpr int kD = AR_RESHARD_MAX_DIMS;
 
-// Cost-model constants of the reshard routes (measured on MI355X: the copy
-// kernel's sustained HBM rate with one read and several writes per byte, and
-// the cost of one launch from the host).
+// Cost-model constants of the reshard routes, measured on MI355X: the copy
+// kernel sustains 6.3-6.5 TB/s of HBM traffic with one read and 1-8 writes per
+// byte (the MoE layer workload, every route), and a launch costs about 13 us
+// from the host.
 constexpr double kReshardLaunchUs = 13.0;
-constexpr double kReshardGBps = 6000.0;
-// Dynamic LDS a copy workgroup reserves (a residency cap, as for the fused
-// all-gather, whose access pattern it shares).
-constexpr int kReshardLdsKB = 22;
+constexpr double kReshardGBps = 6300.0;
+// Copy kernel shape, measured on MI355X at the MoE layer workload (7 GB,
+// 2-8 replicas): with one vector per lane the kernel is latency-bound (2.0 TB/s
+// flat, 2.8-5.2 fused); 4 vectors per lane with 8 KB of LDS reserved (at
+// most 20 resident workgroups per CU) gave 6.2-6.6 TB/s for every route and
+// replica count in repeated runs, where other shapes swung by up to 20 %
+// from one process to the next.
+constexpr int kReshardLdsKB = 8;
+constexpr int kReshardU = 4;
 
 struct Box {
     long long lo[kD], hi[kD];
@@ -257,7 +263,7 @@ struct Piece {
 };
 
 // Pack pieces (all of one shard's table, in order) into launches.
-ar_status_t run_pieces(const std::vector<Piece> &pieces, const std::vector<void *> &table, int vb, int lds,
+ar_status_t run_pieces(const std::vector<Piece> &pieces, const std::vector<void *> &table, int vb, int u, int lds,
                        hipStream_t stream, int *launches) {
     ReshardArgs a;
     memset(&a, 0, sizeof a);
@@ -265,13 +271,13 @@ ar_status_t run_pieces(const std::vector<Piece> &pieces, const std::vector<void 
     long long units = 0;
     auto flush = [&]() -> ar_status_t {
         if (a.nseg == 0) return AR_OK;
-        hipError_t e = launch_reshard(a, units, vb, lds, stream);
+        hipError_t e = launch_reshard(a, units, vb, u, lds, stream);
         if (launches) ++*launches;
         a.nseg = 0;
         units = 0;
         return e == hipSuccess ? AR_OK : AR_ERR_HIP;
     };
-    const long long tile_bytes = (long long)kReshardThreads * vb;
+    const long long tile_bytes = (long long)kReshardThreads * u * vb;
     for (const Piece &p : pieces) {
         if (p.dst_count == 0) continue;
         const long long tiles = (p.f.row + tile_bytes - 1) / tile_bytes;
@@ -392,9 +398,33 @@ int reshard_lds_bytes() {
     return v;
 }
 
+// Vectors per lane of the copy kernel (AR_RESHARD_U overrides: 1, 2, 4, 8).
+int reshard_u() {
+    static int v = -2;
+    if (v == -2) {
+        const char *e = getenv("AR_RESHARD_U");
+        const long x = (e && *e) ? atol(e) : kReshardU;
+        v = (x == 1 || x == 2 || x == 4 || x == 8) ? (int)x : kReshardU;
+    }
+    return v;
+}
+
 }  // namespace
 
 extern "C" {
+
+ar_status_t ar_layout_shard(const ar_layout_t *layout, int slot, long long *lo, long long *hi, int *rank) {
+    ar_status_t st = check_layout(layout);
+    if (st != AR_OK) return st;
+    if (!lo || !hi || slot < 0 || slot >= slots_of(*layout)) return AR_ERR_INVALID_ARG;
+    const Box b = shard_of(*layout, slot);
+    for (int d = 0; d < kD; ++d) {
+        lo[d] = b.lo[d];
+        hi[d] = b.hi[d];
+    }
+    if (rank) *rank = comm_rank(*layout, slot);
+    return AR_OK;
+}
 
 ar_status_t ar_reshard_plan(const ar_layout_t *src, const ar_layout_t *dst, size_t elem_size, int domains,
                             ar_reshard_plan_t *out, ar_transfer_t *transfers, int max_transfers) {
@@ -443,13 +473,13 @@ ar_status_t ar_reshard(const void *const *src_bufs, void *const *dst_bufs, const
     ar_status_t st = derive(src, dst, elem_size, g);
     if (st != AR_OK) return st;
     const long long e = (long long)elem_size;
-    // buffers: owners and every destination non-null and element-aligned
+    // buffers: owners and destinations non-null (unless their shard is empty) and element-aligned
     for (int s : g.owners) {
-        if (!src_bufs[s]) return AR_ERR_INVALID_ARG;
+        if (!src_bufs[s] && box_elems(g.src_box[s], g.nd) > 0) return AR_ERR_INVALID_ARG;
         if ((uintptr_t)src_bufs[s] % elem_size) return AR_ERR_ALIGNMENT;
     }
     for (int t = 0; t < g.ndst; ++t) {
-        if (!dst_bufs[t]) return AR_ERR_INVALID_ARG;
+        if (!dst_bufs[t] && box_elems(g.dst_box[t], g.nd) > 0) return AR_ERR_INVALID_ARG;
         if ((uintptr_t)dst_bufs[t] % elem_size) return AR_ERR_ALIGNMENT;
     }
     // no destination range may overlap another destination or a source that is read
@@ -506,7 +536,7 @@ ar_status_t ar_reshard(const void *const *src_bufs, void *const *dst_bufs, const
         for (size_t j = 0; j < g.replicas.size(); ++j) {
             std::vector<void *> table;
             for (int t : g.replicas[j]) table.push_back(dst_bufs[t]);
-            st = run_pieces(ph[j], table, vb, lds, stream, nullptr);
+            st = run_pieces(ph[j], table, vb, reshard_u(), lds, stream, nullptr);
             if (st != AR_OK) return st;
         }
     }

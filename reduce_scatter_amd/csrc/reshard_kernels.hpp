@@ -28,7 +28,7 @@ struct ReshardSeg {
     long long n1;             // rows per step of the outer dimension
     long long src_s1, dst_s1; // byte strides between consecutive rows of the middle dimension
     long long src_s0, dst_s0; // byte strides of the outer dimension
-    long long tiles;          // tiles per row (kReshardThreads vectors each)
+    long long tiles;          // tiles per row (kReshardThreads * u vectors each)
     long long unit0;          // first work unit of this segment within the launch
     int dst_first;            // destinations: dst[dst_first, dst_first + dst_count)
     int dst_count;
@@ -42,8 +42,9 @@ struct ReshardArgs {
 
 // Launch the copy of ``a`` (work units [0, units): one tile of one row each)
 // with ``vb``-byte vectors (16, 8, 4, 2 or 1: every address, offset, stride
-// and row length of the launch is a multiple of vb); ``lds`` bytes of
-// dynamic LDS reserved per workgroup cap the resident workgroups per CU.
-hipError_t launch_reshard(const ReshardArgs &a, long long units, int vb, int lds, hipStream_t s);
+// and row length of the launch is a multiple of vb), ``u`` vectors per lane
+// (1, 2, 4 or 8: tiles of 64 * u * vb bytes); ``lds`` bytes of dynamic LDS
+// reserved per workgroup cap the resident workgroups per CU.
+hipError_t launch_reshard(const ReshardArgs &a, long long units, int vb, int u, int lds, hipStream_t s);
 
 }  // namespace ar

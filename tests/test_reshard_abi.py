@@ -68,10 +68,22 @@ def test_every_declared_function_is_exported():
     text = open(os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "ar_reshard.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = set(re.findall(r"\b(ar_[a-z_]+)\s*\(", text))
-    assert names == {"ar_reshard", "ar_reshard_plan"}
+    assert names == {"ar_reshard", "ar_reshard_plan", "ar_layout_shard"}
     lib = ctypes.CDLL(ar.library_path())
     for name in names:
         assert hasattr(lib, name), name
+
+
+def test_layout_shards_match_the_oracle():
+    for src, dst in layout_pairs(12, 300):
+        for L in (src, dst):
+            for s in range(L.size):
+                bounds, rank = ar.ar_layout_shard(L, s)
+                assert bounds == m2n.shard_bounds(L, s) and rank == m2n.comm_rank(L, s)
+                assert ar.local_shape(L, s) == m2n.local_shape(L, s)
+    L = m2n.Layout((4, 8), (2,), (0,))
+    assert _err(ar.ar_layout_shard, L, 2) == "AR_ERR_INVALID_ARG"
+    assert _err(ar.ar_layout_shard, L, -1) == "AR_ERR_INVALID_ARG"
 
 
 def test_plan_matches_the_oracle_on_random_layouts():
@@ -163,6 +175,13 @@ def test_reshard_validates_buffers_before_launch():
     assert _err(ar.ar_reshard, sb, [sb[0] + 16] + db[1:], src, dst, 4) == "AR_ERR_INVALID_ARG"  # dst over a source
     with pytest.raises(ValueError):
         ar.ar_reshard(sb, db, src, dst, 4, route="nope")
+    # a slot whose shard is empty (S_d < D_k) may pass NULL; the call then
+    # still fails here only at the planted overlap
+    tiny_src = m2n.Layout((1, 8), (2,), (0,))                   # slot 0 holds [0, 0): empty
+    assert _err(ar.ar_reshard, [None, A], [A + 16], tiny_src, m2n.Layout((1, 8), (1,), (-1,)), 4) == \
+        "AR_ERR_INVALID_ARG"
+    assert _err(ar.ar_reshard, [None, None], [A + 4096], tiny_src, m2n.Layout((1, 8), (1,), (-1,)), 4) == \
+        "AR_ERR_INVALID_ARG"
     # a tensor with no elements is a no-op (no launch)
     empty = m2n.Layout((0, 8), (2,), (0,))
     assert _err(ar.ar_reshard, sb, db[:2], empty, m2n.Layout((0, 8), (2,), (1,)), 4) == "AR_OK"
