@@ -208,15 +208,28 @@ int split_vectors_per_lane(int K) {
     return K >= 8 ? 1 : 2;
 }
 
+// Dynamic LDS a split workgroup reserves beyond its static partials (a
+// residency cap; AR_SPLIT_LDS_KB overrides the default of none).
+int split_lds_bytes() {
+    static int v = -1;
+    if (v < 0) {
+        const char *e = getenv("AR_SPLIT_LDS_KB");
+        const long kb = e ? atol(e) : 0;
+        v = (int)(kb < 0 ? 0 : (kb > 128 ? 128 : kb)) * 1024;
+    }
+    return v;
+}
+
 template <int DT, int OP, int K>
 hipError_t launch_split_u(int U, const RankTable &t, const Geometry &g, dim3 block, hipStream_t s) {
     const long long T = (long long)kFusedThreads * U;
     const dim3 grid((unsigned)((((g.ref & (T - 1)) + g.Vfull) + T - 1) / T));       // tiles of the aligned grid
+    const size_t lds = (size_t)split_lds_bytes();
     switch (U) {
-    case 1: return launch(split_allreduce_kernel<DT, OP, K, 1>, grid, block, 0, s, t, g);
-    case 2: return launch(split_allreduce_kernel<DT, OP, K, 2>, grid, block, 0, s, t, g);
+    case 1: return launch(split_allreduce_kernel<DT, OP, K, 1>, grid, block, lds, s, t, g);
+    case 2: return launch(split_allreduce_kernel<DT, OP, K, 2>, grid, block, lds, s, t, g);
     default:
-        if constexpr (K < 8) return launch(split_allreduce_kernel<DT, OP, K, 4>, grid, block, 0, s, t, g);
+        if constexpr (K < 8) return launch(split_allreduce_kernel<DT, OP, K, 4>, grid, block, lds, s, t, g);
         return hipErrorInvalidValue;
     }
 }
