@@ -150,6 +150,21 @@ def sweep():
     out += ["## n = 4, fp32, 1024 elements per rank (latency regime)", "", "| schedule | us |", "|---|---|"]
     for sched in ("fused", "ring", "tree", "split", "dtree", "auto"):
         out.append("| %s | %.2f |" % (sched, _median_us(lambda: ar.ar_allreduce(xs, ys, 1024, "f32", "sum", sched=sched))))
+    # the same call captured 100 times into one HIP graph (torch's graph API): GPU time per call without the
+    # host's per-call cost
+    reps = 100
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        ar.ar_allreduce(xs, ys, 1024, "f32", "sum", sched="fused")
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(reps):
+            ar.ar_allreduce(xs, ys, 1024, "f32", "sum", sched="fused")
+    out.append("| fused, %d calls replayed from one HIP graph (per call) | %.2f |" % (
+        reps, _median_us(graph.replay, iters=5) / reps))
+    del graph
     out.append("")
 
     # FSDP shards: reduce-scatter (avg) of 8 x 128 Mi bf16, all-gather of 8 x 16 Mi bf16
