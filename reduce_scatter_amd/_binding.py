@@ -154,15 +154,28 @@ def _tables(sendbufs, recvbufs):
     return send, (send if recvbufs is sendbufs else _ptr_array(recvbufs))
 
 
+_gpu_state = []     # [current-stream getter] once known; [None] without torch or a GPU
+
+
+def _current_stream_getter():
+    try:
+        import torch
+    except ImportError:
+        return None
+    if not torch.cuda.is_available():
+        return None
+    raw, dev = getattr(torch._C, "_cuda_getCurrentRawStream", None), getattr(torch._C, "_cuda_getDevice", None)
+    if raw is not None and dev is not None:
+        return lambda: raw(dev())                      # the handle of torch's current stream, without a Stream object
+    return lambda: int(torch.cuda.current_stream().cuda_stream)
+
+
 def _stream(stream):
     if stream is None:
-        try:
-            import torch
-            if torch.cuda.is_available():
-                return int(torch.cuda.current_stream().cuda_stream)
-        except ImportError:
-            pass
-        return 0
+        if not _gpu_state:
+            _gpu_state.append(_current_stream_getter())
+        get = _gpu_state[0]
+        return get() if get is not None else 0
     if isinstance(stream, int):
         return stream
     return int(stream.cuda_stream)

@@ -128,3 +128,12 @@ def test_reshard_captured():
             ar.ar_reshard([x.clone() for x in xs], zs, src, dst, 4, route=route)
             return zs
         _replays(g, xs, ys, eager)             # the source replicas (mesh row 1) are never read
+
+
+def test_default_stream_is_torchs_current_stream():
+    from reduce_scatter_amd import _binding
+    assert _binding._stream(None) == torch.cuda.current_stream().cuda_stream
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        assert _binding._stream(None) == s.cuda_stream
+    assert _binding._stream(None) == torch.cuda.current_stream().cuda_stream
