@@ -47,8 +47,8 @@ __device__ __forceinline__ int hop_rank(int c, int k, int n) {
 // plus a 32-bit vector offset.  Every lane passes a valid offset (lanes past
 // the end of the chunk re-read its last vector and discard the result), so no
 // load sits in a divergent branch and a whole batch of loads is in flight at
-// once.  NR > 0: n == NR known at compile time; NR == 0: any n, 16 loads per
-// batch.  KEEP32: bf16 / fp16 partials stay fp32 (rounded in ``finish``).
+// once.  NR > 0: n == NR known at compile time (n <= 16); NR == 0: any n, 16
+// loads per batch.  KEEP32: bf16 / fp16 partials stay fp32 (rounded in ``finish``).
 template <int DT, int OP, int NR, bool KEEP32>
 __device__ __forceinline__ Pack<DT> chain_in(const RankTable &t, int n, int c, long long base, unsigned lane_off,
                                              float s) {
@@ -243,16 +243,20 @@ __global__ __launch_bounds__(kFusedThreads) void fused_all_gather_kernel(const R
     store_all<NR>(t, n, ((long long)k * g.Rv + ts.lo) * 16, lane_off, w);
 }
 
-// Pick the compile-time rank count when there is one.
-template <typename F> hipError_t by_ranks(int n, F &&f) {
-    switch (n) {
-    case 2: return f(std::integral_constant<int, 2>{});
-    case 4: return f(std::integral_constant<int, 4>{});
-    case 8: return f(std::integral_constant<int, 8>{});
-    case 16: return f(std::integral_constant<int, 16>{});
-    default: return f(std::integral_constant<int, 0>{});
+// Pick the compile-time rank count: every n up to 16 has its own kernels, so a
+// lane issues exactly n loads.  (A generic kernel loading ranks in batches of
+// 16 wasted the loads past n: measured on MI355X at 128 MB per rank it ran at
+// 3.6 TB/s for n = 3 and 4.9-5.6 TB/s for n = 5-7, against 6.4-6.5 TB/s for
+// n = 4 and 8 with their own kernels.)
+template <int NR, typename F> hipError_t by_ranks_from(int n, F &&f) {
+    if constexpr (NR > 16) {
+        return f(std::integral_constant<int, 0>{});
+    } else {
+        if (n == NR) return f(std::integral_constant<int, NR>{});
+        return by_ranks_from<NR + 1>(n, f);
     }
 }
+template <typename F> hipError_t by_ranks(int n, F &&f) { return by_ranks_from<2>(n, f); }
 
 // Tiles per chunk of the wide (n > 16) all-reduce kernel.
 long long fused_wide_windows(int dt, long long maxlen) {

@@ -219,7 +219,7 @@ __global__ __launch_bounds__(kThreads) void ring_all_gather_kernel(const RankTab
 
 
 // ---------------------------------------------------------------------------
-// Compile-time rank counts (n = NR in {2, 4, 8, 16}): one (rank, vector) item
+// Compile-time rank counts (every n = NR from 2 to 16): one (rank, vector) item
 // per thread, W vectors per rank per window (RingShape), and every step's
 // load issued before the first step runs (a rank's contributions do not
 // depend on the running totals, only the LDS work does), so a window costs
@@ -229,10 +229,11 @@ __global__ __launch_bounds__(kThreads) void ring_all_gather_kernel(const RankTab
 template <int NR> __device__ __forceinline__ int wrap_c(int a) { return (a + NR) % NR; }
 
 // Vectors per rank in one window: 64 (1 KB pieces, as wide as a wavefront's
-// 16-byte access), except n = 16 where 32 keeps the workgroup at 512 threads
-// within the register budget.  Threads per workgroup = NR * window.
+// 16-byte access) up to 8 ranks, 32 beyond, which keeps the workgroup at 512
+// threads or fewer within the register budget.  Threads per workgroup =
+// NR * window.
 template <int NR> struct RingShape {
-    static constexpr int W = NR == 16 ? 32 : 64;
+    static constexpr int W = NR > 8 ? 32 : 64;
     static constexpr int T = NR * W;
 };
 
@@ -347,21 +348,25 @@ __global__ __launch_bounds__(RingShape<NR>::T) void ring_all_gather_fast(const R
 
 // Windows of the fast kernels (one workgroup each).
 long long ring_fast_windows(const Geometry &g, bool allreduce) {
-    const long long W = g.n == 16 ? 32 : 64;
+    const long long W = g.n > 8 ? 32 : 64;
     const long long len = allreduce ? (g.V + g.n - 1) / g.n : g.Rv;
     return (len + W - 1) / W;
 }
 
-bool ring_fast_ranks(int n) { return n == 2 || n == 4 || n == 8 || n == 16; }
+// Measured on MI355X (fp32, 128 MB per rank): the persistent any-n kernels
+// ran at 2.8-3.3 TB/s for n = 3, 5, 6, 7 and 12, against 5.1-5.6 TB/s for the
+// compile-time kernels at n = 4, 8 and 16; every n up to 16 now has its own.
+bool ring_fast_ranks(int n) { return n >= 2 && n <= 16; }
 
-template <typename F> hipError_t ring_by_ranks(int n, F &&f) {
-    switch (n) {
-    case 2: return f(std::integral_constant<int, 2>{});
-    case 4: return f(std::integral_constant<int, 4>{});
-    case 8: return f(std::integral_constant<int, 8>{});
-    default: return f(std::integral_constant<int, 16>{});
+template <int NR, typename F> hipError_t ring_by_ranks_from(int n, F &&f) {
+    if constexpr (NR >= 16) {
+        return f(std::integral_constant<int, 16>{});
+    } else {
+        if (n == NR) return f(std::integral_constant<int, NR>{});
+        return ring_by_ranks_from<NR + 1>(n, f);
     }
 }
+template <typename F> hipError_t ring_by_ranks(int n, F &&f) { return ring_by_ranks_from<2>(n, f); }
 
 static size_t ring_lds_bytes(const Geometry &g, bool bounds) {
     return (size_t)g.n * g.W * 16 + (bounds ? ((size_t)g.n + 1) * sizeof(long long) : 0);

@@ -407,3 +407,32 @@ print("ok", hips[0])
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
     r = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=100)
     assert r.returncode == 0, r.stdout + r.stderr
+
+
+@pytest.mark.parametrize("sched", ["fused", "ring"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_every_rank_count_up_to_17(dtype, sched):
+    """Every n up to 16 has its own compile-time fused and ring kernels (17
+    takes the any-n paths): all-reduce, reduce-scatter and all-gather against
+    the oracle."""
+    u = LANES[dtype]
+    for n in range(2, 18):
+        for op in ("sum", "avg", "max"):
+            print("%s n=%d %s %s" % (sched, n, dtype, op), flush=True)
+            count = n * 64 * u * 3 + u * 5 + 3
+            xs = inputs(40, n, count, dtype, op)
+            got = run_allreduce(xs, dtype, op, sched)
+            want = oracle.ring_allreduce(xs, dtype, op)
+            for r in (0, n - 1):
+                assert_bits_equal(got[r], want[r], "%s ar n=%d %s %s rank %d" % (sched, n, dtype, op, r))
+            R = 64 * u * 2 + u
+            ys = inputs(41, n, n * R, dtype, op)
+            got = run_rs(ys, dtype, op, sched)
+            want = oracle.ring_reduce_scatter(ys, dtype, op)
+            for r in range(n):
+                assert_bits_equal(got[r], want[r], "%s rs n=%d %s %s rank %d" % (sched, n, dtype, op, r))
+        pieces = inputs(42, n, 64 * u + u, dtype, "sum")
+        got = run_ag(pieces, dtype, sched)
+        want = oracle.ring_all_gather(pieces, dtype)
+        for r in (0, n - 1):
+            assert_bits_equal(got[r], want[r], "%s ag n=%d %s rank %d" % (sched, n, dtype, r))
