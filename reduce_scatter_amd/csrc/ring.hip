@@ -224,7 +224,11 @@ __global__ __launch_bounds__(kThreads) void ring_all_gather_kernel(const RankTab
 // load issued before the first step runs (a rank's contributions do not
 // depend on the running totals, only the LDS work does), so a window costs
 // about one HBM round trip plus n barriers.  One workgroup per window, windows
-// in address order.
+// in address order.  Window j of a chunk (or slice, or piece) is the j-th
+// W-vector run of an address-aligned grid (the reference buffer's, as for the
+// fused tiles), so chunks whose starts are not W-vector multiples still read
+// and write whole 1 KB runs; every rank computes the same window of every
+// chunk, which is all the LDS exchange needs.
 // ---------------------------------------------------------------------------
 template <int NR> __device__ __forceinline__ int wrap_c(int a) { return (a + NR) % NR; }
 
@@ -248,7 +252,6 @@ __global__ __launch_bounds__(RingShape<NR>::T) void ring_allreduce_fast(const Ra
     constexpr int W = RingShape<NR>::W;
     __shared__ u32x4 slot[NR * W];                 // the wire: one slot per chunk and vector
     const int r = threadIdx.x / W, w = threadIdx.x % W;
-    const long long pos = (long long)blockIdx.x * W + w;
     u32x4 raw[NR];
     long long vv[NR];
     bool ok[NR];
@@ -257,9 +260,11 @@ __global__ __launch_bounds__(RingShape<NR>::T) void ring_allreduce_fast(const Ra
         const int c = wrap_c<NR>(r - 1 - p);
         long long e = ring_chunk_start(c + 1, g);
         e = e < g.Vfull ? e : g.Vfull;
-        const long long v = ring_chunk_start(c, g) + pos;
-        ok[p] = v < e;
-        vv[p] = ok[p] ? v : 0;                     // an always-valid address for lanes past the chunk
+        // window blockIdx.x of chunk c, cut on the W-vector grid of rank 0's output addresses
+        const TileSpan ts = aligned_tile(ring_chunk_start(c, g), e, blockIdx.x, g.ref, W);
+        const long long v = ts.start + w;
+        ok[p] = v >= ts.lo && v < ts.hi;
+        vv[p] = ok[p] ? v : 0;                     // an always-valid address for lanes outside the chunk
         raw[p] = ld_stream(t.src[r], vv[p]);
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -296,18 +301,24 @@ __global__ __launch_bounds__(RingShape<NR>::T) void ring_reduce_scatter_fast(con
     constexpr int W = RingShape<NR>::W;
     __shared__ u32x4 slot[NR * W];
     const int r = threadIdx.x / W, w = threadIdx.x % W;
-    const long long pos = (long long)blockIdx.x * W + w;
-    const bool ok = pos < g.Rv;                    // the same position in every chunk
-    const long long vpos = ok ? pos : 0;
     u32x4 raw[NR];
+    long long vpos[NR];
+    bool ok[NR];
 #pragma unroll
-    for (int p = 0; p < NR; ++p)
-        raw[p] = ld_stream(t.src[r], (long long)wrap_c<NR>(r - 1 - p) * g.Rv + vpos);
+    for (int p = 0; p < NR; ++p) {
+        const int c = wrap_c<NR>(r - 1 - p);
+        // window blockIdx.x of slice c, cut on the W-vector grid of rank 0's input addresses
+        const TileSpan ts = aligned_tile(0, g.Rv, blockIdx.x, g.ref + (long long)c * g.Rv, W);
+        const long long v = ts.start + w;
+        ok[p] = v >= ts.lo && v < ts.hi;
+        vpos[p] = ok[p] ? v : 0;
+        raw[p] = ld_stream(t.src[r], (long long)c * g.Rv + vpos[p]);
+    }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int p = 0; p < NR; ++p) {
         const int c = wrap_c<NR>(r - 1 - p);
-        if (ok) {
+        if (ok[p]) {
             Pack<DT> acc;
             if (p == 0) {
                 acc = first<DT, OP>(unpack<DT>(raw[p]), g.s);
@@ -317,7 +328,7 @@ __global__ __launch_bounds__(RingShape<NR>::T) void ring_reduce_scatter_fast(con
             }
             if (p == NR - 1) {
                 finish<DT, OP>(acc, NR, g);
-                st_stream(t.dst[r], vpos, pack<DT>(acc));
+                st_stream(t.dst[r], vpos[p], pack<DT>(acc));
             } else {
                 slot[c * W + w] = pack<DT>(acc);
             }
@@ -331,26 +342,36 @@ __global__ __launch_bounds__(RingShape<NR>::T) void ring_all_gather_fast(const R
     constexpr int W = RingShape<NR>::W;
     __shared__ u32x4 slot[NR * W];
     const int r = threadIdx.x / W, w = threadIdx.x % W;
-    const long long pos = (long long)blockIdx.x * W + w;
-    const bool ok = pos < g.Rv;
-    if (ok) {
-        const u32x4 x = ld_stream(t.src[r], pos);
+    // window blockIdx.x of piece k, cut on the W-vector grid of rank 0's output addresses
+    auto at = [&](int k, bool &ok) {
+        const TileSpan ts = aligned_tile(0, g.Rv, blockIdx.x, g.ref + (long long)k * g.Rv, W);
+        const long long v = ts.start + w;
+        ok = v >= ts.lo && v < ts.hi;
+        return v;
+    };
+    bool mine_ok;
+    const long long mine = at(r, mine_ok);
+    if (mine_ok) {
+        const u32x4 x = ld_stream(t.src[r], mine);
         slot[r * W + w] = x;
-        st_stream(t.dst[r], (long long)r * g.Rv + pos, x);                 // keep my own piece
+        st_stream(t.dst[r], (long long)r * g.Rv + mine, x);                // keep my own piece
     }
     __syncthreads();
 #pragma unroll
     for (int p = 0; p < NR - 1; ++p) {
         const int c = wrap_c<NR>(r - 1 - p);                              // received from rank r-1
-        if (ok) st_stream(t.dst[r], (long long)c * g.Rv + pos, slot[c * W + w]);
+        bool ok;
+        const long long v = at(c, ok);
+        if (ok) st_stream(t.dst[r], (long long)c * g.Rv + v, slot[c * W + w]);
     }
 }
 
-// Windows of the fast kernels (one workgroup each).
+// Windows of the fast kernels (one workgroup each): enough aligned W-vector
+// windows for the longest chunk or slice, whatever its alignment.
 long long ring_fast_windows(const Geometry &g, bool allreduce) {
     const long long W = g.n > 8 ? 32 : 64;
     const long long len = allreduce ? (g.V + g.n - 1) / g.n : g.Rv;
-    return (len + W - 1) / W;
+    return aligned_tiles(len, W);
 }
 
 // Measured on MI355X (fp32, 128 MB per rank): the persistent any-n kernels
