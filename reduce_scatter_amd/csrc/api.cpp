@@ -95,11 +95,7 @@ int fused_lds_bytes(ar_coll_t coll, int n) {
     }
     if (env >= 0) return env * 1024;
     switch (coll) {
-    case AR_COLL_ALLREDUCE: {
-        int lg = 0;
-        while ((1 << lg) < n) ++lg;
-        return (lg < 5 ? kFusedLdsAllReduceByLog2N[lg] : kFusedLdsAllReduceKB) * 1024;
-    }
+    case AR_COLL_ALLREDUCE: return (n >= 0 && n <= 16 ? kFusedLdsAllReduceByN[n] : kFusedLdsAllReduceKB) * 1024;
     case AR_COLL_ALL_GATHER: return kFusedLdsAllGatherKB * 1024;
     default: return kFusedLdsReduceScatterKB * 1024;
     }

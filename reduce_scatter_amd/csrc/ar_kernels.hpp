@@ -126,11 +126,12 @@ constexpr int kFusedThreads = 64;
 constexpr int kFusedTile = kFusedThreads;
 // Default dynamic-LDS reservation of a fused workgroup, in KB, per collective
 // (caps the resident workgroups per CU; see fused.hip and api.cpp).  The
-// all-reduce's reservation grows with the rank count (index: ceil(log2 n),
-// n <= 16): every resident wave has 2n DRAM streams open, and the best
-// number of resident waves per CU falls as n grows (about 20 at n = 2, 11 at
-// n = 4, 6 at n = 8, 5 at n = 16 measured on MI355X, 256 MB - 1 GB per rank).
-constexpr int kFusedLdsAllReduceByLog2N[5] = {0, 8, 14, 24, 32};
+// all-reduce's reservation grows with the rank count (indexed by n <= 16):
+// every resident wave has 2n DRAM streams open, and the best number of
+// resident waves per CU falls as n grows, to about 50 / n (26 at n = 2, 11 at
+// n = 4, 6 at n = 8, 4 at n = 16; measured on MI355X at 128 MB - 1 GB per
+// rank, every n from 2 to 16).
+constexpr int kFusedLdsAllReduceByN[17] = {0, 0, 6, 10, 14, 16, 20, 22, 24, 28, 32, 34, 36, 38, 40, 40, 40};
 constexpr int kFusedLdsAllReduceKB = 24;
 constexpr int kFusedLdsReduceScatterKB = 0;
 constexpr int kFusedLdsAllGatherKB = 22;
