@@ -29,6 +29,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 DEFAULT_OUT = os.path.join(HERE, "calib_gfx950.txt")
 COLLS = ("allreduce", "reduce_scatter", "all_gather")
 SIZE_BINS = 48
+HBM_BIN = 30                      # log2 of the footprint from which calls stream from HBM (1 GiB, 4x the MALL)
 
 
 def _steps(coll, sched, n):
@@ -98,9 +99,10 @@ def fit(rows):
     most 1 MB (pure latency: t = launch + step * steps), the sustained
     bandwidth from the calls that move at least 1 GB, then one correction per
     power-of-two footprint so the model meets the measured time wherever the
-    bandwidth term is at least a quarter of it.  The footprint (total
-    algorithmic bytes) is the size axis because it decides whether the data
-    stays in the 256 MB Infinity Cache."""
+    bandwidth term is at least a quarter of it (one pooled correction for all
+    footprints of 1 GB and more).  The footprint (total algorithmic bytes) is
+    the size axis because it decides whether the data stays in the 256 MB
+    Infinity Cache."""
     out = {}
     for coll in COLLS:
         for sched in ("ring", "tree", "fused", "split", "dtree"):
@@ -143,6 +145,13 @@ def fit(rows):
                 top = max(bins)                           # beyond the largest measured footprint: keep its factor
                 for b in range(top + 1, SIZE_BINS):
                     row[b] = row[top]
+                # footprints of 1 GB and more stream from HBM whatever their size: one factor for all of them,
+                # the geometric mean of every such measurement, so one noisy call does not flip the choice
+                hbm = [x for b, v in bins.items() if b >= HBM_BIN for x in v]
+                if len(hbm) >= 2:
+                    pooled = float(np.exp(np.mean(np.log(hbm))))
+                    for b in range(HBM_BIN, SIZE_BINS):
+                        row[b] = pooled
                 corr[rc] = [min(4.0, max(0.05, c)) for c in row]
             out[(coll, sched)] = (launch, step, bw, corr, extra)
     return out
