@@ -185,11 +185,18 @@ __global__ __launch_bounds__(kThreads) void elem_split_allreduce_kernel(const Ra
     for (int r = 0; r < n; ++r) store1<DT>(t.dst[r], i, acc);
 }
 
-// Ranks per wave: the smallest power of two with ceil(n / K) <= 16 waves.
+// Ranks per wave: the smallest power of two with ceil(n / K) <= 16 waves
+// (AR_SPLIT_K raises it: 2, 4, 8 or 16).
 int split_ranks_per_wave(int n) {
+    static int env = -1;
+    if (env < 0) {
+        const char *e = getenv("AR_SPLIT_K");
+        const int v = e ? atoi(e) : 0;
+        env = (v == 2 || v == 4 || v == 8 || v == 16) ? v : 0;
+    }
     int k = 1;
     while ((n + k - 1) / k > kSplitMaxWaves) k *= 2;
-    return k;
+    return k < env ? env : k;
 }
 
 // Vectors per lane and rank (AR_SPLIT_U overrides: 1, 2 or 4).  Measured on
@@ -204,7 +211,7 @@ int split_vectors_per_lane(int K) {
         const int v = e ? atoi(e) : 0;
         env = (v == 1 || v == 2 || v == 4) ? v : 0;
     }
-    if (env) return (K == 8 && env == 4) ? 2 : env;
+    if (env) return (K >= 8 && env == 4) ? 2 : (K == 16 ? 1 : env);
     return K >= 8 ? 1 : 2;
 }
 
@@ -227,7 +234,9 @@ hipError_t launch_split_u(int U, const RankTable &t, const Geometry &g, dim3 blo
     const size_t lds = (size_t)split_lds_bytes();
     switch (U) {
     case 1: return launch(split_allreduce_kernel<DT, OP, K, 1>, grid, block, lds, s, t, g);
-    case 2: return launch(split_allreduce_kernel<DT, OP, K, 2>, grid, block, lds, s, t, g);
+    case 2:
+        if constexpr (K < 16) return launch(split_allreduce_kernel<DT, OP, K, 2>, grid, block, lds, s, t, g);
+        return hipErrorInvalidValue;
     default:
         if constexpr (K < 8) return launch(split_allreduce_kernel<DT, OP, K, 4>, grid, block, lds, s, t, g);
         return hipErrorInvalidValue;
@@ -245,6 +254,7 @@ hipError_t launch_split_allreduce(int dt, int op, const RankTable &t, const Geom
         case 2: return launch_split_u<DT, OP, 2>(U, t, g, block, s);
         case 4: return launch_split_u<DT, OP, 4>(U, t, g, block, s);
         case 8: return launch_split_u<DT, OP, 8>(U, t, g, block, s);
+        case 16: return launch_split_u<DT, OP, 16>(U, t, g, block, s);
         default: return hipErrorInvalidValue;
         }
     });
