@@ -27,6 +27,7 @@
 #include "ar_device.hpp"
 #include "ar_kernels.hpp"
 #include "dispatch.hpp"
+#include "tree_fast.hpp"
 
 namespace ar {
 
@@ -104,93 +105,11 @@ __global__ __launch_bounds__(kThreads) void tree_allreduce_kernel(const RankTabl
 }
 
 
-// Compile-time rank counts (n = NR in {2, 4, 8, 16}): kThreads / NR threads
-// per rank, each holding K = 8 vectors of its rank, so a thread keeps 8 loads
-// in flight (the tree gives each rank one load per vector, so without K the
-// window would be one HBM round trip for 16 bytes per thread).  LDS: one
-// partial per rank and vector, NR * W * 16 = 32 KB.  One workgroup per window.
-constexpr int kTreeK = 8;
-
-template <int DT, int OP, int NR>
-__device__ __forceinline__ void tree_window_fast(const RankTable &t, const TreeShape &tree, const Geometry &g,
-                                                 long long lo, long long hi, long long win, u32x4 *slot) {
-    constexpr int TPR = kThreads / NR;             // threads per rank
-    constexpr int W = TPR * kTreeK;                // vectors per rank per window
-    const int r = threadIdx.x / TPR, sub = threadIdx.x % TPR;
-    const long long pos0 = lo + win * W + sub;
-    u32x4 own[kTreeK];
-    bool ok[kTreeK];
-#pragma unroll
-    for (int k = 0; k < kTreeK; ++k) {
-        const long long v = pos0 + (long long)k * TPR;
-        ok[k] = v < hi;
-        own[k] = ld_stream(t.src[r], ok[k] ? v : lo);          // past hi: a valid, ignored load
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    const int d = tree.depth[r], root = tree.root;
-    const int ch0 = tree.child[r][0], ch1 = tree.child[r][1], par = tree.parent[r];
-    for (int lev = tree.max_depth; lev >= 0; --lev) {          // up: deepest level first
-        if (d == lev) {
-#pragma unroll
-            for (int k = 0; k < kTreeK; ++k) {
-                if (!ok[k]) continue;
-                const int i = sub + k * TPR;
-                Pack<DT> acc = first<DT, OP>(unpack<DT>(own[k]), g.s);
-                if (ch0 >= 0) merge<DT, OP>(acc, unpack<DT>(slot[ch0 * W + i]));
-                if (ch1 >= 0) merge<DT, OP>(acc, unpack<DT>(slot[ch1 * W + i]));
-                if (r == root) finish<DT, OP>(acc, NR, g);
-                slot[r * W + i] = pack<DT>(acc);
-            }
-        }
-        __syncthreads();
-    }
-    for (int lev = 0; lev <= tree.max_depth; ++lev) {          // down: root first
-        if (d == lev) {
-#pragma unroll
-            for (int k = 0; k < kTreeK; ++k) {
-                if (!ok[k]) continue;
-                const int i = sub + k * TPR;
-                const u32x4 val = (r == root) ? slot[r * W + i] : slot[par * W + i];
-                slot[r * W + i] = val;
-                st_stream(t.dst[r], pos0 + (long long)k * TPR, val);
-            }
-        }
-        __syncthreads();
-    }
-}
-
-template <int DT, int OP, int NR, bool DUAL>
-__global__ __launch_bounds__(kThreads) void tree_allreduce_fast(const RankTable t, const TreeShape tree0,
-                                                                const TreeShape tree1, const Geometry g) {
-    constexpr int W = (kThreads / NR) * kTreeK;
-    __shared__ u32x4 slot[NR * W];
-    const long long first = DUAL ? (g.split + W - 1) / W : (long long)gridDim.x;   // windows of the first tree
-    const long long win = blockIdx.x;
-    if (win < first) tree_window_fast<DT, OP, NR>(t, tree0, g, 0, DUAL ? g.split : g.Vfull, win, slot);
-    else tree_window_fast<DT, OP, NR>(t, tree1, g, g.split, g.Vfull, win - first, slot);
-}
-
 template <bool DUAL>
 hipError_t launch_trees(int dt, int op, const RankTable &t, const TreeShape &tree, const TreeShape &tree2,
                         const Geometry &g, int grid, int lds, hipStream_t s) {
-    if (g.n == 2 || g.n == 4 || g.n == 8 || g.n == 16) {
-        const long long W = (kThreads / g.n) * kTreeK;
-        const long long windows =
-            DUAL ? (g.split + W - 1) / W + (g.Vfull - g.split + W - 1) / W : (g.Vfull + W - 1) / W;
-        const dim3 blocks((unsigned)windows);
-        return dispatch(dt, op, [&](auto D, auto O) {
-            auto go = [&](auto R) {
-                return launch(tree_allreduce_fast<decltype(D)::value, decltype(O)::value, decltype(R)::value, DUAL>,
-                              blocks, dim3(kThreads), (size_t)lds, s, t, tree, tree2, g);
-            };
-            switch (g.n) {
-            case 2: return go(std::integral_constant<int, 2>{});
-            case 4: return go(std::integral_constant<int, 4>{});
-            case 8: return go(std::integral_constant<int, 8>{});
-            default: return go(std::integral_constant<int, 16>{});
-            }
-        });
-    }
+    if (g.n >= 2 && g.n <= 8) return launch_tree_fast_range<2, 8, DUAL>(dt, op, t, tree, tree2, g, lds, s);
+    if (g.n >= 9 && g.n <= 16) return launch_tree_fast_hi(DUAL, dt, op, t, tree, tree2, g, lds, s);
     return dispatch(dt, op, [&](auto D, auto O) {
         return launch(tree_allreduce_kernel<decltype(D)::value, decltype(O)::value, DUAL>, dim3(grid), dim3(kThreads),
                       (size_t)g.n * g.W * 16, s, t, tree, tree2, g);

@@ -436,3 +436,20 @@ def test_every_rank_count_up_to_17(dtype, sched):
         want = oracle.ring_all_gather(pieces, dtype)
         for r in (0, n - 1):
             assert_bits_equal(got[r], want[r], "%s ag n=%d %s rank %d" % (sched, n, dtype, r))
+
+
+@pytest.mark.parametrize("sched", ["tree", "dtree"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_trees_every_rank_count_up_to_17(dtype, sched):
+    """Every n up to 16 has its own compile-time tree kernels (17 takes the
+    any-n path), for the single and the double binary tree."""
+    u = LANES[dtype]
+    for n in range(2, 18):
+        for op in ("sum", "avg", "min"):
+            print("%s n=%d %s %s" % (sched, n, dtype, op), flush=True)
+            count = n * 64 * u * 5 + u * 7 + 3
+            xs = inputs(43, n, count, dtype, op)
+            got = run_allreduce(xs, dtype, op, sched)
+            want = reference(sched, xs, dtype, op)
+            for r in (0, n // 2, n - 1):
+                assert_bits_equal(got[r], want[r], "%s n=%d %s %s rank %d" % (sched, n, dtype, op, r))
