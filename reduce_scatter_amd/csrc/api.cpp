@@ -80,11 +80,10 @@ int grid_for(long long units, int cus, int per_cu) {
 
 // Dynamic LDS (bytes) a fused workgroup reserves to cap how many one-wave
 // workgroups are resident per CU (LDS is 160 KB per CU on gfx950).  Measured
-// on MI355X with gradient-like data: the all-reduce (n loads and n stores per
-// lane) wants fewer resident workgroups the more ranks it streams (the
-// per-rank-count table in ar_kernels.hpp; past 16 ranks the wide kernel runs
-// uncapped), the all-gather (1 load, n stores) about 7 per CU at n = 8, and
-// the reduce-scatter (n loads, 1 store) no cap at all.  AR_FUSED_LDS_KB
+// on MI355X with gradient-like data: every collective wants fewer resident
+// workgroups the more ranks it streams (the per-rank-count tables in
+// ar_kernels.hpp; past 16 ranks the all-reduce's wide kernel runs uncapped,
+// the all-gather keeps 22 KB and the reduce-scatter none).  AR_FUSED_LDS_KB
 // overrides all of them.
 int fused_lds_bytes(ar_coll_t coll, int n) {
     static int env = -2;
@@ -96,8 +95,8 @@ int fused_lds_bytes(ar_coll_t coll, int n) {
     if (env >= 0) return env * 1024;
     switch (coll) {
     case AR_COLL_ALLREDUCE: return (n >= 0 && n <= 16 ? kFusedLdsAllReduceByN[n] : kFusedLdsAllReduceKB) * 1024;
-    case AR_COLL_ALL_GATHER: return kFusedLdsAllGatherKB * 1024;
-    default: return kFusedLdsReduceScatterKB * 1024;
+    case AR_COLL_ALL_GATHER: return (n >= 0 && n <= 16 ? kFusedLdsAllGatherByN[n] : kFusedLdsAllGatherKB) * 1024;
+    default: return (n >= 0 && n <= 16 ? kFusedLdsReduceScatterByN[n] : kFusedLdsReduceScatterKB) * 1024;
     }
 }
 

@@ -132,6 +132,13 @@ constexpr int kFusedTile = kFusedThreads;
 // n = 4, 6 at n = 8, 4 at n = 16; measured on MI355X at 128 MB - 1 GB per
 // rank, every n from 2 to 16).
 constexpr int kFusedLdsAllReduceByN[17] = {0, 0, 6, 10, 14, 16, 20, 22, 24, 28, 32, 34, 36, 38, 40, 40, 40};
+// The reduce-scatter (n loads, one store per lane) and the all-gather (one
+// load, n stores) likewise, from the same kind of sweep (128 MB per rank on
+// the big side): reduce-scatter best at 0 KB for n = 2, 14 KB for n = 6-8,
+// 22-26 KB for n = 12-16 (6.4-6.7 TB/s); all-gather 10 KB for n = 2-3, 22 KB
+// for n = 8, 32 KB for n = 16 (6.1-6.4 TB/s).
+constexpr int kFusedLdsReduceScatterByN[17] = {0, 0, 0, 6, 10, 12, 14, 14, 14, 16, 18, 20, 22, 22, 24, 24, 24};
+constexpr int kFusedLdsAllGatherByN[17] = {0, 0, 10, 10, 14, 16, 18, 20, 22, 24, 26, 28, 30, 32, 32, 34, 36};
 constexpr int kFusedLdsAllReduceKB = 24;
 constexpr int kFusedLdsReduceScatterKB = 0;
 constexpr int kFusedLdsAllGatherKB = 22;
