@@ -1,7 +1,9 @@
 // elem.hip -- element-wise paths: the same arithmetic, in the same order, as
 // the vector kernels, one element per thread.  Used for buffers that are not
-// 16-byte aligned and for the all-reduce tail (the last count mod lanes
-// elements).  Throughput is not a goal here; identical results are.
+// 16-byte aligned, reduce-scatter / all-gather slices that are not whole
+// 16-byte vectors, and the all-reduce tail (the last count mod lanes
+// elements).  Identical results first; loads are batched so the paths are
+// not latency-bound.
 #include "ar_device.hpp"
 #include "ar_kernels.hpp"
 #include "dispatch.hpp"
@@ -15,24 +17,52 @@ static int elem_grid(long long work) {
     return (int)(b < 1 ? 1 : (b > kElemGridCap ? kElemGridCap : b));
 }
 
-// All-reduce in ring hop order.  Element e lies in vector e / lanes, which
-// lies in chunk c = ((vec+1)*n - 1) / V (the chunk whose 16-byte-unit range
-// [floor(c*V/n), floor((c+1)*V/n)) contains it).
+// Element e's chain in the hop order of chunk c: ranks c+1, ..., c (mod n).
+// Loads go out in batches of 8 before the batch is combined (a load per hop,
+// each waited for before the next, had left the element-wise paths
+// latency-bound); lanes past n re-read rank c's element and ignore it.
+template <int DT, int OP>
+__device__ __forceinline__ typename Pack<DT>::T chain1(const RankTable &t, int n, int c, long long e, float s,
+                                                       bool keep32) {
+    constexpr int B = 8;
+    typename Pack<DT>::T acc{};
+    for (int k0 = 0; k0 < n; k0 += B) {
+        typename Pack<DT>::T v[B];
+#pragma unroll
+        for (int kk = 0; kk < B; ++kk) {
+            const int k = k0 + kk < n ? k0 + kk : n - 1;
+            int r = c + 1 + k;
+            r = r >= n ? r - n : r;
+            r = r >= n ? r - n : r;
+            v[kk] = load1<DT>(t.src[r], e);
+        }
+#pragma unroll
+        for (int kk = 0; kk < B; ++kk) {
+            if (k0 + kk >= n) break;
+            acc = (k0 + kk == 0) ? first1<DT, OP>(v[kk], s, keep32) : hop1<DT, OP>(acc, v[kk], s, keep32);
+        }
+    }
+    return acc;
+}
+
+// All-reduce in ring hop order.  Chunk c (grid y) covers the elements of its
+// 16-byte units [floor(c*V/n), floor((c+1)*V/n)); this launch does the part of
+// it inside [e0, e1).  The chunk index is uniform across a workgroup, so the
+// rank pointers stay in scalar registers (an index computed per element had
+// made every pointer a per-lane load).
 template <int DT, int OP>
 __global__ __launch_bounds__(kThreads) void elem_ring_allreduce_kernel(const RankTable t, const Geometry g,
                                                                       long long e0, long long e1) {
     const int n = g.n;
-    for (long long e = e0 + blockIdx.x * (long long)kThreads + threadIdx.x; e < e1;
+    const int c = (int)blockIdx.y;
+    constexpr long long u = Lanes<DT>::value;
+    long long lo = u * ((long long)c * g.q + (g.rem ? (long long)((unsigned)(c * g.rem) / (unsigned)n) : 0));
+    long long hi = u * ((long long)(c + 1) * g.q + (g.rem ? (long long)((unsigned)((c + 1) * g.rem) / (unsigned)n) : 0));
+    lo = lo > e0 ? lo : e0;
+    hi = hi < e1 ? hi : e1;
+    for (long long e = lo + blockIdx.x * (long long)kThreads + threadIdx.x; e < hi;
          e += (long long)gridDim.x * kThreads) {
-        const long long vec = e / Lanes<DT>::value;
-        const int c = (int)(((vec + 1) * n - 1) / g.V);
-        typename Pack<DT>::T acc = first1<DT, OP>(load1<DT>(t.src[add_mod(c, 1 % n, n)], e), g.s, g.acc32);
-        for (int k = 2; k <= n; ++k) {
-            int r = c + k;
-            r = r >= n ? r - n : r;
-            r = r >= n ? r - n : r;
-            acc = hop1<DT, OP>(acc, load1<DT>(t.src[r], e), g.s, g.acc32);
-        }
+        typename Pack<DT>::T acc = chain1<DT, OP>(t, n, c, e, g.s, g.acc32);
         acc = finish1<DT, OP>(acc, n, g);
         for (int r = 0; r < n; ++r) store1<DT>(t.dst[r], e, acc);
     }
@@ -64,48 +94,47 @@ __global__ __launch_bounds__(kThreads) void elem_tree_allreduce_kernel(const Ran
     }
 }
 
-// Reduce-scatter: output element i of rank r = chunk r's chain over inputs
-// r*R + i of ranks r+1, ..., r.
+// Reduce-scatter: output element i of rank c (grid y) = chunk c's chain over
+// inputs c*R + i of ranks c+1, ..., c.
 template <int DT, int OP>
 __global__ __launch_bounds__(kThreads) void elem_reduce_scatter_kernel(const RankTable t, const Geometry g,
                                                                       long long R) {
     const int n = g.n;
-    const long long total = (long long)n * R;
-    for (long long q = blockIdx.x * (long long)kThreads + threadIdx.x; q < total;
-         q += (long long)gridDim.x * kThreads) {
-        const int c = (int)(q / R);
-        const long long i = q - (long long)c * R;
-        const long long e = (long long)c * R + i;
-        typename Pack<DT>::T acc = first1<DT, OP>(load1<DT>(t.src[add_mod(c, 1 % n, n)], e), g.s, g.acc32);
-        for (int k = 2; k <= n; ++k) {
-            int r = c + k;
-            r = r >= n ? r - n : r;
-            r = r >= n ? r - n : r;
-            acc = hop1<DT, OP>(acc, load1<DT>(t.src[r], e), g.s, g.acc32);
-        }
+    const int c = (int)blockIdx.y;
+    for (long long i = blockIdx.x * (long long)kThreads + threadIdx.x; i < R; i += (long long)gridDim.x * kThreads) {
+        const typename Pack<DT>::T acc = chain1<DT, OP>(t, n, c, (long long)c * R + i, g.s, g.acc32);
         store1<DT>(t.dst[c], i, finish1<DT, OP>(acc, n, g));
     }
 }
 
-// All-gather: bit copies of 2- or 4-byte elements.
+// All-gather: bit copies of 2- or 4-byte elements; piece k is grid y.
 template <typename E>
 __global__ __launch_bounds__(kThreads) void elem_all_gather_kernel(const RankTable t, const Geometry g, long long R) {
     const int n = g.n;
-    const long long total = (long long)n * R;
-    for (long long q = blockIdx.x * (long long)kThreads + threadIdx.x; q < total;
-         q += (long long)gridDim.x * kThreads) {
-        const int k = (int)(q / R);
-        const long long i = q - (long long)k * R;
+    const int k = (int)blockIdx.y;
+    for (long long i = blockIdx.x * (long long)kThreads + threadIdx.x; i < R; i += (long long)gridDim.x * kThreads) {
         const E v = ((const E *)t.src[k])[i];
         for (int r = 0; r < n; ++r) ((E *)t.dst[r])[(long long)k * R + i] = v;
     }
 }
 
+// Workgroups along one chunk / slice / piece of ``len`` elements, with n of
+// them side by side (grid y).
+static dim3 elem_grid2(long long len, int n) {
+    long long x = (len + kThreads - 1) / kThreads;
+    const long long cap = (kElemGridCap * 4 + n - 1) / n;
+    x = x < 1 ? 1 : (x > cap ? cap : x);
+    return dim3((unsigned)x, (unsigned)n);
+}
+
 hipError_t launch_elem_ring_allreduce(int dt, int op, const RankTable &t, const Geometry &g, long long e0,
                                       long long e1, hipStream_t s) {
     if (e1 <= e0) return hipSuccess;
+    const long long chunk = (e1 - e0 + g.n - 1) / g.n + 16;     // at most this many elements of [e0, e1) per chunk
+    const dim3 grid = elem_grid2(chunk < e1 - e0 ? chunk : e1 - e0, g.n);
     return dispatch(dt, op, [&](auto D, auto O) {
-        return launch(elem_ring_allreduce_kernel<decltype(D)::value, decltype(O)::value>, dim3(elem_grid(e1 - e0)), dim3(kThreads), 0, s, t, g, e0, e1);
+        return launch(elem_ring_allreduce_kernel<decltype(D)::value, decltype(O)::value>, grid, dim3(kThreads), 0, s, t,
+                      g, e0, e1);
     });
 }
 
@@ -121,13 +150,14 @@ hipError_t launch_elem_reduce_scatter(int dt, int op, const RankTable &t, const 
                                       hipStream_t s) {
     if (R <= 0) return hipSuccess;
     return dispatch(dt, op, [&](auto D, auto O) {
-        return launch(elem_reduce_scatter_kernel<decltype(D)::value, decltype(O)::value>, dim3(elem_grid((long long)g.n * R)), dim3(kThreads), 0, s, t, g, R);
+        return launch(elem_reduce_scatter_kernel<decltype(D)::value, decltype(O)::value>, elem_grid2(R, g.n),
+                      dim3(kThreads), 0, s, t, g, R);
     });
 }
 
 hipError_t launch_elem_all_gather(int elem_bytes, const RankTable &t, const Geometry &g, long long R, hipStream_t s) {
     if (R <= 0) return hipSuccess;
-    const dim3 grid(elem_grid((long long)g.n * R));
+    const dim3 grid = elem_grid2(R, g.n);
     if (elem_bytes == 4) return launch(elem_all_gather_kernel<uint32_t>, grid, dim3(kThreads), 0, s, t, g, R);
     return launch(elem_all_gather_kernel<uint16_t>, grid, dim3(kThreads), 0, s, t, g, R);
 }
