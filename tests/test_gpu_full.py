@@ -13,6 +13,10 @@
   splits) checked element by element against the oracle of the planner's
   choice; the split schedule on one 25 MB bucket against the pairwise oracle.
 * The split schedule at the 8 x 256 MB shape against the pairwise oracle.
+* Past every 32-bit byte offset: n = 2 fp32 all-reduce of 4.3 GB per rank
+  (every schedule), reduce-scatter and all-gather of 4.3 GB slices: every
+  element checked on the device (n = 2 is one IEEE operation per element),
+  sampled windows against the oracle.
 """
 from __future__ import annotations
 
@@ -225,4 +229,65 @@ def test_c5_split_one_bucket_in_place():
     for r in (0, 35, n - 1):
         assert_bits_equal(to_host(grads[r], "f32"), want, "c5 split rank %d" % r)
     del grads
+    torch.cuda.empty_cache()
+
+
+BIG = (1 << 30) + (1 << 20) + 7          # fp32 elements per rank: 4.3 GB, past every 32-bit byte offset
+
+
+def _windows(count, rng, k=48, w=1024):
+    starts = sorted(set([0, count - w] + [int(s) for s in rng.integers(0, count - w, size=k)]))
+    return [(s, s + w) for s in starts]
+
+
+def _check_windows(got_t, xs_t, dtype, op, rng, count):
+    """Sampled windows of an n = 2 result against the ring oracle run on the
+    window (for n = 2 each element is one IEEE operation whichever rank comes
+    first, so the window's own chunking gives the same bits as the call's)."""
+    for lo, hi in _windows(count, rng):
+        xs = [to_host(x[lo:hi], dtype) for x in xs_t]
+        want = oracle.ring_allreduce(xs, dtype, op)[0]
+        assert_bits_equal(to_host(got_t[lo:hi], dtype), want, "window [%d, %d)" % (lo, hi))
+
+
+@pytest.mark.parametrize("sched", ["fused", "ring", "tree", "split", "dtree", "auto"])
+def test_allreduce_past_4GB_per_rank(sched):
+    """n = 2 fp32 all-reduce of 4.3 GB per rank (a ragged count), every
+    schedule: every element equals x0 + x1 (checked on the device against
+    torch's add, one IEEE addition), all ranks agree, and sampled windows
+    match the oracle."""
+    print("past 4 GB allreduce", sched, flush=True)
+    xs = [workloads.device_normal(9, 0, r, BIG, 1.0, "f32") for r in range(2)]
+    ys = [torch.empty_like(x) for x in xs]
+    ar.ar_allreduce(xs, ys, BIG, "f32", "sum", sched=sched)
+    torch.cuda.synchronize()
+    _same_on_all_ranks(ys)
+    assert torch.equal((xs[0] + xs[1]).view(torch.int32), ys[0].view(torch.int32))
+    _check_windows(ys[0], xs, "f32", "sum", np.random.default_rng(1), BIG)
+    del xs, ys
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("sched", ["fused", "ring"])
+def test_reduce_scatter_and_all_gather_past_4GB(sched):
+    """n = 2: reduce-scatter of 2 x 4.3 GB slices per rank, then all-gather of
+    the 4.3 GB results, past every 32-bit byte offset."""
+    print("past 4 GB rs/ag", sched, flush=True)
+    R = BIG
+    xs = [workloads.device_normal(9, 1, r, 2 * R, 1.0, "f32") for r in range(2)]
+    ys = [torch.empty(R, device="cuda") for _ in range(2)]
+    ar.ar_reduce_scatter(xs, ys, R, "f32", "sum", sched=sched)
+    torch.cuda.synchronize()
+    for c in range(2):
+        assert torch.equal((xs[0][c * R:(c + 1) * R] + xs[1][c * R:(c + 1) * R]).view(torch.int32),
+                           ys[c].view(torch.int32)), "slice %d" % c
+    del xs
+    torch.cuda.empty_cache()
+    zs = [torch.empty(2 * R, device="cuda") for _ in range(2)]
+    ar.ar_all_gather(ys, zs, R, "f32", sched=sched)
+    torch.cuda.synchronize()
+    for z in zs:
+        for k in range(2):
+            assert torch.equal(z[k * R:(k + 1) * R].view(torch.int32), ys[k].view(torch.int32))
+    del ys, zs
     torch.cuda.empty_cache()
