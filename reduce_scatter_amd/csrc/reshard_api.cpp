@@ -34,8 +34,8 @@ constexpr double kReshardGBps = 6300.0;
 // 2-8 replicas): with one vector per lane the kernel is latency-bound (2.0 TB/s
 // flat, 2.8-5.2 fused); 4 vectors per lane with 8 KB of LDS reserved (at
 // most 20 resident workgroups per CU) gave 6.2-6.6 TB/s for every route and
-// replica count in repeated runs, where other shapes swung by up to 20 %
-// from one process to the next.
+// replica count in repeated runs.  (The first process on a freshly started
+// GPU runs this copy up to 20 % slower; later ones do not.)
 constexpr int kReshardLdsKB = 8;
 constexpr int kReshardU = 4;
 
