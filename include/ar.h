@@ -58,9 +58,12 @@
  * The caller owns the arrays and the buffers; the library reads the two
  * arrays during the call only (they are copied by value into the kernel
  * arguments) and allocates no device memory on any call.  Buffers must be
- * aligned to their element size; 16-byte alignment of every pointer (and, for
- * reduce-scatter and all-gather, R * element size a multiple of 16) selects
- * the vector path, otherwise an element-wise path gives identical results.
+ * aligned to their element size; 16-byte alignment of every pointer selects
+ * the vector paths, otherwise an element-wise path gives identical results.
+ * For reduce-scatter and all-gather with R * element size not a multiple of
+ * 16, the vector path reads the input slices through aligned 16-byte vectors
+ * and may read (never write) the rest of the 16-byte block that holds an
+ * input buffer's last byte.
  *
  * Aliasing: send buffers may alias one another (they are only read).
  *   all-reduce      in place when recvbufs[r] == sendbufs[r];

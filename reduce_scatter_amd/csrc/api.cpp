@@ -425,8 +425,21 @@ ar_status_t ar_reduce_scatter_ex(const void *const *sendbufs, void *const *recvb
     RankTable t;
     fill_table(t, sendbufs, recvbufs, n);
     g.n = n;
-    const bool vec = all16(sendbufs, (const void *const *)recvbufs, n) && (recvcount * e) % 16 == 0;
-    if (!vec) return hip_status(launch_elem_reduce_scatter(dtype, op, t, g, (long long)recvcount, stream));
+    const bool aligned = all16(sendbufs, (const void *const *)recvbufs, n);
+    const bool vec = aligned && (recvcount * e) % 16 == 0;
+    if (aligned && !vec) {
+        // slices that are not whole 16-byte vectors: the phased fused pass for every whole output vector (any
+        // schedule: the ring computes the same hop order), the element-wise kernel for each output's last bytes
+        g.slice_bytes = (long long)(recvcount * e);
+        g.Rv = g.slice_bytes / 16;
+        if (aligned_tiles(g.Rv, kFusedTile) > 0x7fffffffLL) return AR_ERR_UNSUPPORTED;   // grid x limit
+        const hipError_t h = launch_fused_reduce_scatter_phased(dtype, op, t, g,
+                                                                fused_lds_bytes(AR_COLL_REDUCE_SCATTER, n), stream);
+        if (h != hipSuccess) return hip_status(h);
+        return hip_status(launch_elem_reduce_scatter(dtype, op, t, g, (long long)recvcount,
+                                                     g.Rv * (long long)(16 / e), stream));
+    }
+    if (!vec) return hip_status(launch_elem_reduce_scatter(dtype, op, t, g, (long long)recvcount, 0, stream));
     g.Rv = (long long)(recvcount * e / 16);
     g.ref = (long long)((uintptr_t)sendbufs[0] >> 4);          // fused tiles follow the input slices' alignment
     if (use == AR_SCHED_FUSED) {
@@ -466,7 +479,18 @@ ar_status_t ar_all_gather(const void *const *sendbufs, void *const *recvbufs, si
     memset(&g, 0, sizeof g);
     g.n = n;
     g.s = 1.0f;
-    const bool vec = all16(sendbufs, (const void *const *)recvbufs, n) && (sendcount * e) % 16 == 0;
+    const bool aligned = all16(sendbufs, (const void *const *)recvbufs, n);
+    const bool vec = aligned && (sendcount * e) % 16 == 0;
+    if (aligned && !vec) {
+        // pieces that are not whole 16-byte vectors: the phased pass writes every output vector that lies wholly
+        // inside one piece, the element-wise kernel the few elements at each piece's ends
+        g.slice_bytes = (long long)(sendcount * e);
+        g.ref = (long long)((uintptr_t)recvbufs[0] >> 4);      // tiles follow the outputs' alignment
+        if (aligned_tiles(g.slice_bytes / 16, kFusedTile) > 0x7fffffffLL) return AR_ERR_UNSUPPORTED;
+        const hipError_t h = launch_fused_all_gather_phased(t, g, fused_lds_bytes(AR_COLL_ALL_GATHER, n), stream);
+        if (h != hipSuccess) return hip_status(h);
+        return hip_status(launch_elem_all_gather_edges((int)e, t, g, (long long)sendcount, stream));
+    }
     if (!vec) return hip_status(launch_elem_all_gather((int)e, t, g, (long long)sendcount, stream));
     g.Rv = (long long)(sendcount * e / 16);
     g.ref = (long long)((uintptr_t)recvbufs[0] >> 4);          // fused tiles follow the outputs' alignment

@@ -268,6 +268,26 @@ __device__ __forceinline__ void st_stream(void *base, long long vec, u32x4 w) {
     __builtin_nontemporal_store(w, (u32x4 *)base + vec);
 }
 
+// Bytes [phase, phase + 16) of the 32 bytes a:b (a's bytes first), phase in
+// [0, 16): a 16-byte vector read at an address that is not 16-byte aligned,
+// assembled from the two aligned vectors around it.  Little-endian: byte 0 of
+// a sits in the low bits of a.x.
+__device__ __forceinline__ u32x4 funnel16(u32x4 a, u32x4 b, unsigned phase) {
+    const uint64_t q0 = (uint64_t)a.x | ((uint64_t)a.y << 32), q1 = (uint64_t)a.z | ((uint64_t)a.w << 32);
+    const uint64_t q2 = (uint64_t)b.x | ((uint64_t)b.y << 32), q3 = (uint64_t)b.z | ((uint64_t)b.w << 32);
+    const bool hi = phase >= 8;
+    const unsigned sh = (phase & 7u) * 8u;
+    const uint64_t x0 = hi ? q1 : q0, x1 = hi ? q2 : q1, x2 = hi ? q3 : q2;
+    const uint64_t r0 = sh ? (x0 >> sh) | (x1 << (64u - sh)) : x0;
+    const uint64_t r1 = sh ? (x1 >> sh) | (x2 << (64u - sh)) : x1;
+    u32x4 r;
+    r.x = (uint32_t)r0;
+    r.y = (uint32_t)(r0 >> 32);
+    r.z = (uint32_t)r1;
+    r.w = (uint32_t)(r1 >> 32);
+    return r;
+}
+
 // (a + b) mod n for a, b in [0, n).
 __device__ __forceinline__ int add_mod(int a, int b, int n) {
     int r = a + b;

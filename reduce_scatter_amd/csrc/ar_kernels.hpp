@@ -36,6 +36,7 @@ struct Geometry {
     long long split;    // double tree: vectors [0, split) go up the first tree, the rest up the second
     float post_div;     // split float avg: the finished sum is divided by n / p (0: no post-division)
     int acc32;          // bf16 / fp16 partials kept in fp32, rounded once (the fused schedule)
+    long long slice_bytes;  // phased reduce-scatter / all-gather: bytes per slice or piece (not a multiple of 16)
 };
 
 // Tiles are cut on a grid aligned to absolute T-vector boundaries of a
@@ -90,6 +91,15 @@ struct TreeShape {
 hipError_t launch_fused_allreduce(int dt, int op, const RankTable &t, const Geometry &g, int lds, hipStream_t s);
 hipError_t launch_fused_reduce_scatter(int dt, int op, const RankTable &t, const Geometry &g, int lds, hipStream_t s);
 hipError_t launch_fused_all_gather(const RankTable &t, const Geometry &g, int lds, hipStream_t s);
+// Phased forms for slices of g.slice_bytes bytes, not a multiple of 16 (every
+// pointer 16-byte aligned): the full 16-byte vectors of every output
+// (reduce-scatter: g.Rv per output; all-gather: those wholly inside each piece,
+// tiles on the grid of g.ref), the inputs read through aligned pairs of
+// vectors.  The partial vectors at the slice edges go through
+// launch_elem_reduce_scatter (from element i0) and launch_elem_all_gather_edges.
+hipError_t launch_fused_reduce_scatter_phased(int dt, int op, const RankTable &t, const Geometry &g, int lds,
+                                              hipStream_t s);
+hipError_t launch_fused_all_gather_phased(const RankTable &t, const Geometry &g, int lds, hipStream_t s);
 // Fused pass in the aligned pairwise order over ranks (all-reduce only): one
 // workgroup of ceil(n / K) waves per 64-vector tile of [0, Vfull).
 hipError_t launch_split_allreduce(int dt, int op, const RankTable &t, const Geometry &g, hipStream_t s);
@@ -116,8 +126,12 @@ hipError_t launch_elem_tree_allreduce(int dt, int op, const RankTable &t, const 
 hipError_t launch_elem_split_allreduce(int dt, int op, const RankTable &t, const Geometry &g, long long e_begin,
                                        long long e_end, hipStream_t s);
 hipError_t launch_elem_reduce_scatter(int dt, int op, const RankTable &t, const Geometry &g, long long R,
-                                      hipStream_t s);
+                                      long long i0, hipStream_t s);
 hipError_t launch_elem_all_gather(int elem_bytes, const RankTable &t, const Geometry &g, long long R, hipStream_t s);
+// The elements of every all-gather piece outside the 16-byte output vectors
+// the phased kernel writes (at most 15 bytes at each end of a piece).
+hipError_t launch_elem_all_gather_edges(int elem_bytes, const RankTable &t, const Geometry &g, long long R,
+                                        hipStream_t s);
 
 // Threads per workgroup for every vector kernel.
 constexpr int kThreads = 256;

@@ -95,13 +95,14 @@ __global__ __launch_bounds__(kThreads) void elem_tree_allreduce_kernel(const Ran
 }
 
 // Reduce-scatter: output element i of rank c (grid y) = chunk c's chain over
-// inputs c*R + i of ranks c+1, ..., c.
+// inputs c*R + i of ranks c+1, ..., c; elements [i0, R) of every slice.
 template <int DT, int OP>
 __global__ __launch_bounds__(kThreads) void elem_reduce_scatter_kernel(const RankTable t, const Geometry g,
-                                                                      long long R) {
+                                                                      long long R, long long i0) {
     const int n = g.n;
     const int c = (int)blockIdx.y;
-    for (long long i = blockIdx.x * (long long)kThreads + threadIdx.x; i < R; i += (long long)gridDim.x * kThreads) {
+    for (long long i = i0 + blockIdx.x * (long long)kThreads + threadIdx.x; i < R;
+         i += (long long)gridDim.x * kThreads) {
         const typename Pack<DT>::T acc = chain1<DT, OP>(t, n, c, (long long)c * R + i, g.s, g.acc32);
         store1<DT>(t.dst[c], i, finish1<DT, OP>(acc, n, g));
     }
@@ -115,6 +116,29 @@ __global__ __launch_bounds__(kThreads) void elem_all_gather_kernel(const RankTab
     for (long long i = blockIdx.x * (long long)kThreads + threadIdx.x; i < R; i += (long long)gridDim.x * kThreads) {
         const E v = ((const E *)t.src[k])[i];
         for (int r = 0; r < n; ++r) ((E *)t.dst[r])[(long long)k * R + i] = v;
+    }
+}
+
+// The elements of all-gather piece k (grid y) outside the output's 16-byte
+// vectors that lie wholly inside the piece: [0, head) and [tail, R) of the
+// piece, where the piece covers output bytes [k*Rb, (k+1)*Rb), Rb = R * e.
+template <typename E>
+__global__ __launch_bounds__(kFusedThreads) void elem_all_gather_edges_kernel(const RankTable t, const Geometry g,
+                                                                             long long R) {
+    const int n = g.n;
+    const int k = (int)blockIdx.y;
+    const long long e = (long long)sizeof(E);
+    const long long b0 = (long long)k * R * e, b1 = b0 + R * e;     // the piece's output bytes
+    const long long o0 = (b0 + 15) / 16, o1 = b1 / 16;               // its whole 16-byte vectors [o0, o1)
+    long long head = R, tail = R;
+    if (o1 > o0) {
+        head = (o0 * 16 - b0) / e;
+        tail = (o1 * 16 - b0) / e;
+    }
+    for (long long i = threadIdx.x; i < R - tail + head; i += kFusedThreads) {
+        const long long q = i < head ? i : tail + (i - head);
+        const E v = ((const E *)t.src[k])[q];
+        for (int r = 0; r < n; ++r) ((E *)t.dst[r])[(long long)k * R + q] = v;
     }
 }
 
@@ -147,12 +171,20 @@ hipError_t launch_elem_tree_allreduce(int dt, int op, const RankTable &t, const 
 }
 
 hipError_t launch_elem_reduce_scatter(int dt, int op, const RankTable &t, const Geometry &g, long long R,
-                                      hipStream_t s) {
-    if (R <= 0) return hipSuccess;
+                                      long long i0, hipStream_t s) {
+    if (R <= i0) return hipSuccess;
     return dispatch(dt, op, [&](auto D, auto O) {
-        return launch(elem_reduce_scatter_kernel<decltype(D)::value, decltype(O)::value>, elem_grid2(R, g.n),
-                      dim3(kThreads), 0, s, t, g, R);
+        return launch(elem_reduce_scatter_kernel<decltype(D)::value, decltype(O)::value>, elem_grid2(R - i0, g.n),
+                      dim3(kThreads), 0, s, t, g, R, i0);
     });
+}
+
+hipError_t launch_elem_all_gather_edges(int elem_bytes, const RankTable &t, const Geometry &g, long long R,
+                                        hipStream_t s) {
+    if (R <= 0) return hipSuccess;
+    const dim3 grid(1, (unsigned)g.n);
+    if (elem_bytes == 4) return launch(elem_all_gather_edges_kernel<uint32_t>, grid, dim3(kFusedThreads), 0, s, t, g, R);
+    return launch(elem_all_gather_edges_kernel<uint16_t>, grid, dim3(kFusedThreads), 0, s, t, g, R);
 }
 
 hipError_t launch_elem_all_gather(int elem_bytes, const RankTable &t, const Geometry &g, long long R, hipStream_t s) {

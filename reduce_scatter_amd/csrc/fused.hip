@@ -23,6 +23,7 @@
 #include "ar_device.hpp"
 #include "ar_kernels.hpp"
 #include "dispatch.hpp"
+#include "fused_common.hpp"
 
 namespace ar {
 
@@ -31,13 +32,6 @@ namespace ar {
 __device__ __forceinline__ void tile_coords(int &c, long long &j) {
     c = (int)blockIdx.y;
     j = (long long)blockIdx.x;
-}
-
-// Rank holding hop k (k = 0..n-1) of chunk c: c+1+k mod n.
-__device__ __forceinline__ int hop_rank(int c, int k, int n) {
-    int r = c + 1 + k;
-    r = r >= n ? r - n : r;
-    return r >= n ? r - n : r;
 }
 
 // Combine the n ranks' vectors at byte ``base + lane_off`` in the hop order
@@ -242,21 +236,6 @@ __global__ __launch_bounds__(kFusedThreads) void fused_all_gather_kernel(const R
     const u32x4 w = __builtin_nontemporal_load((const u32x4 *)((const char *)t.src[k] + ts.lo * 16 + lane_off));
     store_all<NR>(t, n, ((long long)k * g.Rv + ts.lo) * 16, lane_off, w);
 }
-
-// Pick the compile-time rank count: every n up to 16 has its own kernels, so a
-// lane issues exactly n loads.  (A generic kernel loading ranks in batches of
-// 16 wasted the loads past n: measured on MI355X at 128 MB per rank it ran at
-// 3.6 TB/s for n = 3 and 4.9-5.6 TB/s for n = 5-7, against 6.4-6.5 TB/s for
-// n = 4 and 8 with their own kernels.)
-template <int NR, typename F> hipError_t by_ranks_from(int n, F &&f) {
-    if constexpr (NR > 16) {
-        return f(std::integral_constant<int, 0>{});
-    } else {
-        if (n == NR) return f(std::integral_constant<int, NR>{});
-        return by_ranks_from<NR + 1>(n, f);
-    }
-}
-template <typename F> hipError_t by_ranks(int n, F &&f) { return by_ranks_from<2>(n, f); }
 
 // Tiles per chunk of the wide (n > 16) all-reduce kernel.
 long long fused_wide_windows(int dt, long long maxlen) {

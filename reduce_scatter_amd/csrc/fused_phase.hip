@@ -1,0 +1,158 @@
+// fused_phase.hip -- the fused reduce-scatter and all-gather for slices whose
+// byte length is not a multiple of 16.
+//
+// Reduce-scatter input slice c of every rank starts c*R*e bytes into a
+// 16-byte-aligned buffer, so with R*e not a multiple of 16 the slices sit at
+// different phases within 16-byte vectors, while every output is aligned.
+// Each lane reads the two aligned vectors around its 16 input bytes and
+// assembles them (funnel16; the phase is the same for every rank of a slice,
+// so it is uniform across the workgroup), combines the n contributions in the
+// ring hop order exactly as the aligned kernel does, and stores one aligned
+// output vector.  (A first form loaded the second vector only for a non-zero
+// phase; that branch made the compiler wait for each rank's pair before
+// issuing the next, and n = 16 ran at 3.1 TB/s.)  The all-gather is the mirror image: aligned input pieces,
+// output pieces at phase k*R*e mod 16, each lane assembling the 16 input bytes
+// that land in one whole output vector.  The elements of the partial vectors
+// at the slice edges go through the element-wise kernels.  Every input byte is
+// still fetched from HBM once (the second vector of a pair is the neighbour
+// lane's first, served by the cache).
+#include "ar_device.hpp"
+#include "ar_kernels.hpp"
+#include "dispatch.hpp"
+#include "fused_common.hpp"
+
+namespace ar {
+
+// Combine the n ranks' 16 bytes at byte ``base + lane_off + ph`` (``base`` a
+// multiple of 16, the same for the whole workgroup, and so is the phase
+// ``ph``) in the hop order of chunk c.  Each lane loads the two aligned
+// vectors that hold its bytes, every load of the chain issued before the first
+// combine; the second vector of a lane is its neighbour's first (a cache hit).
+template <int DT, int OP, int NR, bool KEEP32>
+__device__ __forceinline__ Pack<DT> chain_phased(const RankTable &t, int n, int c, long long base, unsigned lane_off,
+                                                 unsigned ph, float s) {
+    Pack<DT> acc;
+    if constexpr (NR > 0) {
+        u32x4 lo[NR], hi[NR];
+#pragma unroll
+        for (int k = 0; k < NR; ++k) {
+            const char *p = (const char *)t.src[hop_rank(c, k, NR)] + base + lane_off;
+            lo[k] = __builtin_nontemporal_load((const u32x4 *)p);
+            hi[k] = *(const u32x4 *)(p + 16);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        acc = first<DT, OP, KEEP32>(unpack<DT>(funnel16(lo[0], hi[0], ph)), s);
+#pragma unroll
+        for (int k = 1; k < NR; ++k) hop<DT, OP, KEEP32>(acc, unpack<DT>(funnel16(lo[k], hi[k], ph)), s);
+    } else {
+        constexpr int B = 8;
+        for (int k0 = 0; k0 < n; k0 += B) {
+            u32x4 lo[B], hi[B];
+#pragma unroll
+            for (int kk = 0; kk < B; ++kk) {
+                const int k = k0 + kk < n ? k0 + kk : n - 1;                 // past n: a valid, ignored load
+                const char *p = (const char *)t.src[hop_rank(c, k, n)] + base + lane_off;
+                lo[kk] = __builtin_nontemporal_load((const u32x4 *)p);
+                hi[kk] = *(const u32x4 *)(p + 16);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int kk = 0; kk < B; ++kk) {
+                if (k0 + kk >= n) break;
+                const Pack<DT> x = unpack<DT>(funnel16(lo[kk], hi[kk], ph));
+                if (k0 + kk == 0) acc = first<DT, OP, KEEP32>(x, s);
+                else hop<DT, OP, KEEP32>(acc, x, s);
+            }
+        }
+    }
+    return acc;
+}
+
+// Reduce-scatter: grid x = tiles of output vectors, y = slice c.  Output
+// vector o of rank c is chunk c's chain over input bytes c*Rb + 16*o of ranks
+// c+1, ..., c (Rb = g.slice_bytes bytes per slice, g.Rv whole output vectors).
+// Tiles follow output c's alignment: its writes are the ones a cache line
+// split between two workgroups would cost; the reads sit at the slice's phase
+// whatever the tiling.  Neither load of a lane passes the input's end: with Rb
+// not a multiple of 16, the byte after a whole output vector's last input byte
+// is still in the buffer, so its vector exists (whole, as buffers start on a
+// 16-byte boundary).
+template <int DT, int OP, int NR, bool KEEP32>
+__device__ __forceinline__ void rs_phased(const RankTable &t, const Geometry &g) {
+    const int n = NR > 0 ? NR : g.n;
+    const int c = (int)blockIdx.y;
+    const TileSpan ts = aligned_tile(0, g.Rv, (long long)blockIdx.x, (long long)((uintptr_t)t.dst[c] >> 4), kFusedTile);
+    if (ts.lo >= ts.hi) return;
+    bool ok;
+    const unsigned lane_off = tile_lane(ts, ts.start + threadIdx.x, ok);
+    const long long a = (long long)c * g.slice_bytes + ts.lo * 16;     // the tile's first input byte
+    Pack<DT> acc = chain_phased<DT, OP, NR, KEEP32>(t, n, c, a & ~15LL, lane_off, (unsigned)(a & 15), g.s);
+    if (!ok) return;
+    finish<DT, OP>(acc, n, g);
+    __builtin_nontemporal_store(pack<DT>(acc), (u32x4 *)((char *)t.dst[c] + ts.lo * 16 + lane_off));
+}
+
+template <int DT, int OP, int NR>
+__global__ __launch_bounds__(kFusedThreads) void fused_reduce_scatter_phased_kernel(const RankTable t,
+                                                                                   const Geometry g) {
+    if constexpr (DT == BF16 || DT == F16) {
+        if (g.acc32) {
+            rs_phased<DT, OP, NR, true>(t, g);
+            return;
+        }
+    }
+    rs_phased<DT, OP, NR, false>(t, g);
+}
+
+// All-gather: grid x = tiles of output vectors, y = piece k.  Piece k covers
+// output bytes [k*Rb, (k+1)*Rb); its whole output vectors are
+// [ceil(k*Rb/16), floor((k+1)*Rb/16)), vector o holding input bytes
+// 16*o - k*Rb.  Tiles follow the outputs' alignment (g.ref); the same bound
+// as above keeps both loads of a lane inside the input piece's vectors.
+template <int NR>
+__global__ __launch_bounds__(kFusedThreads) void fused_all_gather_phased_kernel(const RankTable t, const Geometry g) {
+    const int n = NR > 0 ? NR : g.n;
+    const int k = (int)blockIdx.y;
+    const long long b0 = (long long)k * g.slice_bytes;
+    const TileSpan ts = aligned_tile((b0 + 15) >> 4, (b0 + g.slice_bytes) >> 4, (long long)blockIdx.x, g.ref, kFusedTile);
+    if (ts.lo >= ts.hi) return;
+    bool ok;
+    const unsigned lane_off = tile_lane(ts, ts.start + threadIdx.x, ok);
+    const long long in = ts.lo * 16 - b0;                                 // the tile's first input byte
+    const char *p = (const char *)t.src[k] + (in & ~15LL) + lane_off;
+    const u32x4 lo = __builtin_nontemporal_load((const u32x4 *)p);
+    const u32x4 hi = *(const u32x4 *)(p + 16);
+    const u32x4 w = funnel16(lo, hi, (unsigned)(in & 15));
+    if (!ok) return;
+    const long long out = ts.lo * 16 + lane_off;
+    if constexpr (NR > 0) {
+#pragma unroll
+        for (int r = 0; r < NR; ++r) __builtin_nontemporal_store(w, (u32x4 *)((char *)t.dst[r] + out));
+    } else {
+        for (int r = 0; r < n; ++r) __builtin_nontemporal_store(w, (u32x4 *)((char *)t.dst[r] + out));
+    }
+}
+
+hipError_t launch_fused_reduce_scatter_phased(int dt, int op, const RankTable &t, const Geometry &g, int lds,
+                                              hipStream_t s) {
+    if (g.Rv <= 0) return hipSuccess;
+    const dim3 grid((unsigned)aligned_tiles(g.Rv, kFusedTile), (unsigned)g.n);
+    return dispatch(dt, op, [&](auto D, auto O) {
+        return by_ranks(g.n, [&](auto R) {
+            return launch(fused_reduce_scatter_phased_kernel<decltype(D)::value, decltype(O)::value, decltype(R)::value>,
+                          grid, dim3(kFusedThreads), (size_t)lds, s, t, g);
+        });
+    });
+}
+
+hipError_t launch_fused_all_gather_phased(const RankTable &t, const Geometry &g, int lds, hipStream_t s) {
+    const long long most = g.slice_bytes >> 4;                    // whole output vectors of any piece, at most
+    if (most <= 0) return hipSuccess;
+    const dim3 grid((unsigned)aligned_tiles(most, kFusedTile), (unsigned)g.n);
+    return by_ranks(g.n, [&](auto R) {
+        return launch(fused_all_gather_phased_kernel<decltype(R)::value>, grid, dim3(kFusedThreads), (size_t)lds, s,
+                      t, g);
+    });
+}
+
+}  // namespace ar

@@ -355,6 +355,49 @@ def test_numerics_variants_match_oracle(dtype):
                             sched, dtype, op, n, acc, avg))
 
 
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_slices_off_the_vector_grid(dtype):
+    """Slices whose byte length is not a multiple of 16 bytes, with 16-byte
+    aligned buffers (the phased pass for every whole output vector, the
+    element-wise kernels for the ends): every residue of the slice length
+    modulo a vector, slices shorter than one vector, n from 2 to 17 (17 takes
+    the any-n kernels), every op, fp32 partials and the split avg divisor,
+    reduce-scatter and all-gather, bit for bit against the oracle."""
+    u = LANES[dtype]
+    sizes = [u - 1, u + 1] + [64 * u * 2 + j for j in range(1, u)]
+    for n in (2, 3, 5, 8, 16, 17):
+        for R in sizes:
+            print("phased", dtype, "n=%d R=%d" % (n, R), flush=True)
+            for op in OPS:
+                xs = inputs(50 + R, n, n * R, dtype, op)
+                ref = oracle.ring_reduce_scatter(xs, dtype, op)
+                for sched in ("fused", "ring"):
+                    got = run_rs(xs, dtype, op, sched)
+                    for r in range(n):
+                        assert_bits_equal(got[r], ref[r], "rs %s %s %s n=%d R=%d rank %d" % (
+                            sched, dtype, op, n, R, r))
+            pieces = inputs(60 + R, n, R, dtype, "sum")
+            want = oracle.ring_all_gather(pieces, dtype)
+            for sched in ("fused", "ring"):
+                got = run_ag(pieces, dtype, sched)
+                for r in range(n):
+                    assert_bits_equal(got[r], want[r], "ag %s %s n=%d R=%d rank %d" % (sched, dtype, n, R, r))
+    R = 64 * u * 3 + u - 1
+    for n in (3, 8, 17):
+        for op in ("sum", "avg", "prod", "max"):
+            ys = inputs(70, n, n * R, dtype, op)
+            for acc, avg in NUMERICS:
+                print("phased numerics", dtype, op, n, acc, avg, flush=True)
+                ref = _numerics_reference("ring", ys, dtype, op, acc, avg, coll="reduce_scatter")
+                d_in = [to_device(y, dtype) for y in ys]
+                d_out = [empty(R, dtype, 0) for _ in ys]
+                ar.ar_reduce_scatter_ex(d_in, d_out, R, dtype, op, sched="fused", acc=acc, avg=avg)
+                sync()
+                for r in range(n):
+                    assert_bits_equal(to_host(d_out[r], dtype), ref[r], "rs %s %s n=%d %s/%s rank %d" % (
+                        dtype, op, n, acc, avg, r))
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 def test_float_extremes_match_oracle(dtype):
     """Subnormal-range contributions (the rounding of partials and of the
