@@ -182,6 +182,11 @@ def sweep():
     us = _median_us(lambda: ar.ar_reduce_scatter_ex(xs, ys, R, "bf16", "avg", sched="fused", acc="fp32"))
     out.append("| reduce-scatter, fp32 partials (bf16 in and out) | fused | %.1f | %.0f | %.1f |" % (
         us, alg / us / 1e3, alg / us / 1e3 / PEAK_HBM_GBPS * 100))
+    # an odd shard length: slices of R - 1 elements (not whole 16-byte vectors: the phased pass)
+    R1, alg1 = R - 1, (n + 1) * n * (R - 1) * 2
+    us = _median_us(lambda: ar.ar_reduce_scatter(xs, ys, R1, "bf16", "avg", sched="fused"))
+    out.append("| reduce-scatter, R - 1 elements per slice (phased) | fused | %.1f | %.0f | %.1f |" % (
+        us, alg1 / us / 1e3, alg1 / us / 1e3 / PEAK_HBM_GBPS * 100))
     x32_t = [x.float() for x in xs_t]
     y32_t = [torch.empty(R, device="cuda") for _ in range(n)]
     x32, y32 = ar.pointers(x32_t), ar.pointers(y32_t)
@@ -196,6 +201,9 @@ def sweep():
     for sched in ("fused", "ring"):
         us = _median_us(lambda: ar.ar_all_gather(pieces, full, R, "bf16", sched=sched))
         out.append("| all-gather | %s | %.1f | %.0f | %.1f |" % (sched, us, alg / us / 1e3, alg / us / 1e3 / PEAK_HBM_GBPS * 100))
+    us = _median_us(lambda: ar.ar_all_gather(pieces, full, R1, "bf16", sched="fused"))
+    out.append("| all-gather, R - 1 elements per piece (phased) | fused | %.1f | %.0f | %.1f |" % (
+        us, alg1 / us / 1e3, alg1 / us / 1e3 / PEAK_HBM_GBPS * 100))
     del pieces, full, ys, pieces_t, full_t, ys_t
     torch.cuda.empty_cache()
     out.append("")

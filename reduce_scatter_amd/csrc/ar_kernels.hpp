@@ -149,13 +149,16 @@ constexpr int kFusedLdsAllReduceByN[17] = {0, 0, 6, 10, 14, 16, 20, 22, 24, 28, 
 // The reduce-scatter (n loads, one store per lane) and the all-gather (one
 // load, n stores) likewise, from the same kind of sweep (128 MB per rank on
 // the big side): reduce-scatter best at 0 KB for n = 2, 14 KB for n = 6-8,
-// 22-26 KB for n = 12-16 (6.4-6.7 TB/s); all-gather 10 KB for n = 2-3, 22 KB
-// for n = 8, 32 KB for n = 16 (6.1-6.4 TB/s).
+// 22-26 KB for n = 12-16 (6.4-6.7 TB/s).  The all-gather (ordinary input
+// loads) runs best with about 30 / (n + 1) resident waves per CU: 14 KB (11
+// per CU) at n = 2, 26 KB (6) at n = 4, 34 KB (4) at n = 6-7, 48 KB (3) at
+// n = 8-14, 64 KB (2) from n = 15 on, 24, 32 and 72 included (7.0-7.5 TB/s up
+// to n = 16, 6.9 at 32, 6.1 at 72).
 constexpr int kFusedLdsReduceScatterByN[17] = {0, 0, 0, 6, 10, 12, 14, 14, 14, 16, 18, 20, 22, 22, 24, 24, 24};
-constexpr int kFusedLdsAllGatherByN[17] = {0, 0, 10, 10, 14, 16, 18, 20, 22, 24, 26, 28, 30, 32, 32, 34, 36};
+constexpr int kFusedLdsAllGatherByN[17] = {0, 0, 14, 18, 26, 30, 34, 34, 48, 48, 48, 48, 48, 48, 48, 64, 64};
 constexpr int kFusedLdsAllReduceKB = 24;
-constexpr int kFusedLdsReduceScatterKB = 0;
-constexpr int kFusedLdsAllGatherKB = 22;
+constexpr int kFusedLdsReduceScatterKB = 26;   // n > 16: 6.3-6.6 TB/s at n = 24, 32, 72 (0 KB: 6.1-6.2)
+constexpr int kFusedLdsAllGatherKB = 64;
 // Default dynamic-LDS reservation of the compile-time-n ring and tree
 // workgroups, in KB (on top of their static LDS).
 constexpr int kRingLdsKB = 0;

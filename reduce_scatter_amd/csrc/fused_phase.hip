@@ -120,8 +120,8 @@ __global__ __launch_bounds__(kFusedThreads) void fused_all_gather_phased_kernel(
     const unsigned lane_off = tile_lane(ts, ts.start + threadIdx.x, ok);
     const long long in = ts.lo * 16 - b0;                                 // the tile's first input byte
     const char *p = (const char *)t.src[k] + (in & ~15LL) + lane_off;
-    const u32x4 lo = __builtin_nontemporal_load((const u32x4 *)p);
-    const u32x4 hi = *(const u32x4 *)(p + 16);
+    const u32x4 lo = *(const u32x4 *)p;                                   // ordinary loads, as the aligned
+    const u32x4 hi = *(const u32x4 *)(p + 16);                            // all-gather reads its input
     const u32x4 w = funnel16(lo, hi, (unsigned)(in & 15));
     if (!ok) return;
     const long long out = ts.lo * 16 + lane_off;
