@@ -443,9 +443,9 @@ ar_status_t ar_reduce_scatter_ex(const void *const *sendbufs, void *const *recvb
     g.Rv = (long long)(recvcount * e / 16);
     g.ref = (long long)((uintptr_t)sendbufs[0] >> 4);          // fused tiles follow the input slices' alignment
     if (use == AR_SCHED_FUSED) {
-        g.windows = aligned_tiles(g.Rv, kFusedTile);
-        if (g.windows > 0x7fffffffLL) return AR_ERR_UNSUPPORTED;   // grid x limit
-        return hip_status(launch_fused_reduce_scatter(dtype, op, t, g, fused_lds_bytes(AR_COLL_REDUCE_SCATTER, n), stream));
+        if (aligned_tiles(g.Rv, kFusedTile) > 0x7fffffffLL) return AR_ERR_UNSUPPORTED;   // grid x limit
+        return hip_status(launch_fused_reduce_scatter(dtype, op, t, g, fused_lds_bytes(AR_COLL_REDUCE_SCATTER, n),
+                                                      stream));
     }
     g.W = lds_window(n);
     g.windows = (g.Rv + g.W - 1) / g.W;

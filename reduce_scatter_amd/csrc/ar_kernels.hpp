@@ -89,6 +89,8 @@ struct TreeShape {
 // Fused kernels launch one workgroup per tile (g.windows tiles per chunk, n
 // chunks); ``lds`` is the dynamic LDS each workgroup reserves (a residency cap).
 hipError_t launch_fused_allreduce(int dt, int op, const RankTable &t, const Geometry &g, int lds, hipStream_t s);
+// The reduce-scatter sizes its grid itself (tiles of 64 vectors, 128 above 16
+// ranks).
 hipError_t launch_fused_reduce_scatter(int dt, int op, const RankTable &t, const Geometry &g, int lds, hipStream_t s);
 hipError_t launch_fused_all_gather(const RankTable &t, const Geometry &g, int lds, hipStream_t s);
 // Phased forms for slices of g.slice_bytes bytes, not a multiple of 16 (every
@@ -157,7 +159,7 @@ constexpr int kFusedLdsAllReduceByN[17] = {0, 0, 6, 10, 14, 16, 20, 22, 24, 28, 
 constexpr int kFusedLdsReduceScatterByN[17] = {0, 0, 0, 6, 10, 12, 14, 14, 14, 16, 18, 20, 22, 22, 24, 24, 24};
 constexpr int kFusedLdsAllGatherByN[17] = {0, 0, 14, 18, 26, 30, 34, 34, 48, 48, 48, 48, 48, 48, 48, 64, 64};
 constexpr int kFusedLdsAllReduceKB = 24;
-constexpr int kFusedLdsReduceScatterKB = 26;   // n > 16: 6.3-6.6 TB/s at n = 24, 32, 72 (0 KB: 6.1-6.2)
+constexpr int kFusedLdsReduceScatterKB = 48;   // n > 16, two vectors per lane (3 workgroups per CU)
 constexpr int kFusedLdsAllGatherKB = 64;
 // Default dynamic-LDS reservation of the compile-time-n ring and tree
 // workgroups, in KB (on top of their static LDS).

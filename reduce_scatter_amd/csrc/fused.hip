@@ -34,63 +34,6 @@ __device__ __forceinline__ void tile_coords(int &c, long long &j) {
     j = (long long)blockIdx.x;
 }
 
-// Combine the n ranks' vectors at byte ``base + lane_off`` in the hop order
-// of chunk c (ranks c+1, ..., c).  ``base`` is the tile's byte offset (the
-// same for the whole wavefront: it is folded into the scalar rank pointer)
-// and ``lane_off`` a 32-bit per-lane offset, so every access is a scalar base
-// plus a 32-bit vector offset.  Every lane passes a valid offset (lanes past
-// the end of the chunk re-read its last vector and discard the result), so no
-// load sits in a divergent branch and a whole batch of loads is in flight at
-// once.  NR > 0: n == NR known at compile time (n <= 16); NR == 0: any n, 16
-// loads per batch.  KEEP32: bf16 / fp16 partials stay fp32 (rounded in ``finish``).
-template <int DT, int OP, int NR, bool KEEP32>
-__device__ __forceinline__ Pack<DT> chain_in(const RankTable &t, int n, int c, long long base, unsigned lane_off,
-                                             float s) {
-    Pack<DT> acc;
-    if constexpr (NR > 0) {
-        u32x4 raw[NR];
-#pragma unroll
-        for (int k = 0; k < NR; ++k) {
-            const char *p = (const char *)t.src[hop_rank(c, k, NR)] + base;
-            raw[k] = __builtin_nontemporal_load((const u32x4 *)(p + lane_off));
-        }
-        __builtin_amdgcn_sched_barrier(0);                   // every load issued before the first combine
-        acc = first<DT, OP, KEEP32>(unpack<DT>(raw[0]), s);
-#pragma unroll
-        for (int k = 1; k < NR; ++k) hop<DT, OP, KEEP32>(acc, unpack<DT>(raw[k]), s);
-    } else {
-        constexpr int B = 16;
-        for (int k0 = 0; k0 < n; k0 += B) {
-            u32x4 raw[B];
-#pragma unroll
-            for (int kk = 0; kk < B; ++kk) {
-                const int k = k0 + kk < n ? k0 + kk : n - 1;                 // past n: a valid, ignored load
-                const char *p = (const char *)t.src[hop_rank(c, k, n)] + base;
-                raw[kk] = __builtin_nontemporal_load((const u32x4 *)(p + lane_off));
-            }
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int kk = 0; kk < B; ++kk) {
-                if (k0 + kk >= n) break;
-                if (k0 + kk == 0) acc = first<DT, OP, KEEP32>(unpack<DT>(raw[kk]), s);
-                else hop<DT, OP, KEEP32>(acc, unpack<DT>(raw[kk]), s);
-            }
-        }
-    }
-    return acc;
-}
-
-// The chain with the partials' precision chosen once per tile (a uniform
-// branch; only bf16 / fp16 have two).
-template <int DT, int OP, int NR>
-__device__ __forceinline__ Pack<DT> chain(const RankTable &t, int n, int c, long long base, unsigned lane_off,
-                                          float s, bool keep32) {
-    if constexpr (DT == BF16 || DT == F16) {
-        if (keep32) return chain_in<DT, OP, NR, true>(t, n, c, base, lane_off, s);
-    }
-    return chain_in<DT, OP, NR, false>(t, n, c, base, lane_off, s);
-}
-
 template <int NR>
 __device__ __forceinline__ void store_all(const RankTable &t, int n, long long base, unsigned lane_off, u32x4 w) {
     if constexpr (NR > 0) {
@@ -122,10 +65,12 @@ __global__ __launch_bounds__(kFusedThreads) void fused_allreduce_kernel(const Ra
     if (ts.lo >= ts.hi) return;                               // past the chunk's end: nothing in this tile
     bool ok;
     const unsigned lane_off = tile_lane(ts, ts.start + threadIdx.x, ok);
-    Pack<DT> acc = chain<DT, OP, NR>(t, n, c, ts.lo * 16, lane_off, g.s, g.acc32);
+    const unsigned off[1] = {lane_off};
+    Pack<DT> acc[1];
+    chain<DT, OP, NR, 1>(t, n, c, ts.lo * 16, off, g.s, g.acc32, acc);
     if (!ok) return;
-    finish<DT, OP>(acc, n, g);
-    store_all<NR>(t, n, ts.lo * 16, lane_off, pack<DT>(acc));
+    finish<DT, OP>(acc[0], n, g);
+    store_all<NR>(t, n, ts.lo * 16, lane_off, pack<DT>(acc[0]));
 }
 
 // Many ranks (n > 16): with 2n streams per tile, DRAM locality comes from
@@ -201,25 +146,6 @@ __global__ __launch_bounds__(kFusedThreads) void fused_allreduce_wide_kernel(con
     fused_allreduce_wide<DT, OP, false>(t, g);
 }
 
-// Reduce-scatter: output vector v of rank c is chunk c's reduction over input
-// vectors c*Rv + v of ranks c+1, ..., c.
-template <int DT, int OP, int NR>
-__global__ __launch_bounds__(kFusedThreads) void fused_reduce_scatter_kernel(const RankTable t, const Geometry g) {
-    const int n = NR > 0 ? NR : g.n;
-    int c;
-    long long j;
-    tile_coords(c, j);
-    // tiles follow the alignment of the n input slices (slice c of the reference input)
-    const TileSpan ts = aligned_tile(0, g.Rv, j, g.ref + (long long)c * g.Rv, kFusedTile);
-    if (ts.lo >= ts.hi) return;
-    bool ok;
-    const unsigned lane_off = tile_lane(ts, ts.start + threadIdx.x, ok);
-    Pack<DT> acc = chain<DT, OP, NR>(t, n, c, ((long long)c * g.Rv + ts.lo) * 16, lane_off, g.s, g.acc32);
-    if (!ok) return;
-    finish<DT, OP>(acc, n, g);
-    __builtin_nontemporal_store(pack<DT>(acc), (u32x4 *)((char *)t.dst[c] + ts.lo * 16 + lane_off));
-}
-
 // All-gather: input vector v of piece k is read once and written to vector
 // k*Rv + v of every output.  Pure assembly, no arithmetic.  The input is read
 // with an ordinary load and the outputs written non-temporally: measured on
@@ -262,16 +188,6 @@ hipError_t launch_fused_allreduce(int dt, int op, const RankTable &t, const Geom
         return by_ranks(g.n, [&](auto R) {
             return launch(fused_allreduce_kernel<decltype(D)::value, decltype(O)::value, decltype(R)::value>, grid,
                           dim3(kFusedThreads), (size_t)lds, s, t, g);
-        });
-    });
-}
-
-hipError_t launch_fused_reduce_scatter(int dt, int op, const RankTable &t, const Geometry &g, int lds, hipStream_t s) {
-    const dim3 grid((unsigned)g.windows, (unsigned)g.n);
-    return dispatch(dt, op, [&](auto D, auto O) {
-        return by_ranks(g.n, [&](auto R) {
-            return launch(fused_reduce_scatter_kernel<decltype(D)::value, decltype(O)::value, decltype(R)::value>,
-                          grid, dim3(kFusedThreads), (size_t)lds, s, t, g);
         });
     });
 }

@@ -1,11 +1,13 @@
 // fused_common.hpp -- pieces shared by the fused kernels' translation units
-// (fused.hip, fused_phase.hip): the ring hop order and the compile-time rank
+// (fused.hip, fused_rs.hip, fused_phase.hip): the ring hop order, the chain
+// that combines the n ranks' vectors in that order, and the compile-time rank
 // count dispatch.
 #pragma once
 
 #include <type_traits>
 
 #include "ar_device.hpp"
+#include "ar_kernels.hpp"
 
 namespace ar {
 
@@ -14,6 +16,74 @@ __device__ __forceinline__ int hop_rank(int c, int k, int n) {
     int r = c + 1 + k;
     r = r >= n ? r - n : r;
     return r >= n ? r - n : r;
+}
+
+// Combine the n ranks' vectors at bytes ``base + lane_off[u]`` (u < U) in the
+// hop order of chunk c (ranks c+1, ..., c) into acc[u].  ``base`` is the
+// tile's byte offset (the same for the whole wavefront: it is folded into the
+// scalar rank pointer) and ``lane_off`` 32-bit per-lane offsets, so every
+// access is a scalar base plus a 32-bit vector offset.  Every lane passes
+// valid offsets (lanes past the end of the range re-read its last vector and
+// discard the result), so no load sits in a divergent branch and a whole batch
+// of loads is in flight at once.  NR > 0: n == NR known at compile time
+// (n <= 16), all n*U loads issued before the first combine; NR == 0: any n,
+// batches of 16 loads.  KEEP32: bf16 / fp16 partials stay fp32 (rounded in
+// ``finish``).  Each acc[u] sees the ranks in the same order whatever U is.
+template <int DT, int OP, int NR, bool KEEP32, int U>
+__device__ __forceinline__ void chain_in(const RankTable &t, int n, int c, long long base,
+                                         const unsigned (&lane_off)[U], float s, Pack<DT> (&acc)[U]) {
+    if constexpr (NR > 0) {
+        u32x4 raw[NR][U];
+#pragma unroll
+        for (int k = 0; k < NR; ++k) {
+            const char *p = (const char *)t.src[hop_rank(c, k, NR)] + base;
+#pragma unroll
+            for (int u = 0; u < U; ++u) raw[k][u] = __builtin_nontemporal_load((const u32x4 *)(p + lane_off[u]));
+        }
+        __builtin_amdgcn_sched_barrier(0);                   // every load issued before the first combine
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            acc[u] = first<DT, OP, KEEP32>(unpack<DT>(raw[0][u]), s);
+#pragma unroll
+            for (int k = 1; k < NR; ++k) hop<DT, OP, KEEP32>(acc[u], unpack<DT>(raw[k][u]), s);
+        }
+    } else {
+        constexpr int B = 16 / U > 0 ? 16 / U : 1;
+        for (int k0 = 0; k0 < n; k0 += B) {
+            u32x4 raw[B][U];
+#pragma unroll
+            for (int kk = 0; kk < B; ++kk) {
+                const int k = k0 + kk < n ? k0 + kk : n - 1;                 // past n: a valid, ignored load
+                const char *p = (const char *)t.src[hop_rank(c, k, n)] + base;
+#pragma unroll
+                for (int u = 0; u < U; ++u) raw[kk][u] = __builtin_nontemporal_load((const u32x4 *)(p + lane_off[u]));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int kk = 0; kk < B; ++kk) {
+                if (k0 + kk >= n) break;
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    if (k0 + kk == 0) acc[u] = first<DT, OP, KEEP32>(unpack<DT>(raw[kk][u]), s);
+                    else hop<DT, OP, KEEP32>(acc[u], unpack<DT>(raw[kk][u]), s);
+                }
+            }
+        }
+    }
+}
+
+// The chain with the partials' precision chosen once per tile (a uniform
+// branch; only bf16 / fp16 have two).
+template <int DT, int OP, int NR, int U>
+__device__ __forceinline__ void chain(const RankTable &t, int n, int c, long long base, const unsigned (&lane_off)[U],
+                                      float s, bool keep32, Pack<DT> (&acc)[U]) {
+    if constexpr (DT == BF16 || DT == F16) {
+        if (keep32) {
+            chain_in<DT, OP, NR, true, U>(t, n, c, base, lane_off, s, acc);
+            return;
+        }
+    }
+    chain_in<DT, OP, NR, false, U>(t, n, c, base, lane_off, s, acc);
 }
 
 // Pick the compile-time rank count: every n up to 16 has its own kernels, so a
