@@ -100,8 +100,19 @@ int fused_lds_bytes(ar_coll_t coll, int n) {
     }
 }
 
+// AR_TREE_STAGED=1 sends the n <= 16 tree schedules through the LDS-staged
+// kernel (level by level, as for n > 16) instead of the register-evaluated
+// ones; both give the same bits.
+bool tree_staged() {
+    static const int v = [] {
+        const char *e = getenv("AR_TREE_STAGED");
+        return (e && *e == '1') ? 1 : 0;
+    }();
+    return v != 0;
+}
+
 // Dynamic LDS reservation (bytes) of the ring / tree workgroups; the
-// AR_RING_LDS_KB / AR_TREE_LDS_KB variables override the defaults.
+// AR_RING_LDS_KB variable overrides the default.
 int env_kb(const char *name, int dflt) {
     const char *e = getenv(name);
     long kb = (e && *e) ? atol(e) : dflt;
@@ -112,10 +123,6 @@ int ring_lds_bytes(ar_coll_t coll) {
     static int v = env_kb("AR_RING_LDS_KB", -1);
     if (v >= 0 && getenv("AR_RING_LDS_KB")) return v;
     return (coll == AR_COLL_ALL_GATHER ? kRingLdsAllGatherKB : kRingLdsKB) * 1024;
-}
-int tree_lds_bytes() {
-    static int v = env_kb("AR_TREE_LDS_KB", kTreeLdsKB);
-    return v < 0 ? 0 : v;
 }
 
 // Window width (16-byte vectors per rank) for the LDS-staged schedules:
@@ -376,6 +383,10 @@ ar_status_t ar_allreduce_ex(const void *const *sendbufs, void *const *recvbufs, 
             const long long maxlen = (g.V + n - 1) / n;
             g.windows = (maxlen + g.W - 1) / g.W;
             h = launch_ring_allreduce(dtype, op, t, g, grid_for(g.windows, cus, 4), ring_lds_bytes(AR_COLL_ALLREDUCE), stream);
+        } else if (n >= 2 && n <= 16 && !tree_staged()) {               // tree / dtree, in registers
+            if (aligned_tiles(g.Vfull, kFusedTile) > 0x7fffffffLL) return AR_ERR_UNSUPPORTED;   // grid x limit
+            h = launch_tree_reg_allreduce(use == AR_SCHED_DTREE, dtype, op, t, g,
+                                          fused_lds_bytes(AR_COLL_ALLREDUCE, n), stream);
         } else if (use == AR_SCHED_DTREE) {
             g.W = lds_window(n);
             g.windows = (g.split + g.W - 1) / g.W + (g.Vfull - g.split + g.W - 1) / g.W;
@@ -383,7 +394,7 @@ ar_status_t ar_allreduce_ex(const void *const *sendbufs, void *const *recvbufs, 
         } else {
             g.W = lds_window(n);
             g.windows = (g.Vfull + g.W - 1) / g.W;
-            h = launch_tree_allreduce(dtype, op, t, tree, g, grid_for(g.windows, cus, 4), tree_lds_bytes(), stream);
+            h = launch_tree_allreduce(dtype, op, t, tree, g, grid_for(g.windows, cus, 4), stream);
         }
     }
     if (h == hipSuccess && g.Vfull * lanes < (long long)count) h = elem(g.Vfull * lanes);   // tail: count mod lanes

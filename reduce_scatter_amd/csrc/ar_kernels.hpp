@@ -105,18 +105,24 @@ hipError_t launch_fused_all_gather_phased(const RankTable &t, const Geometry &g,
 // Fused pass in the aligned pairwise order over ranks (all-reduce only): one
 // workgroup of ceil(n / K) waves per 64-vector tile of [0, Vfull).
 hipError_t launch_split_allreduce(int dt, int op, const RankTable &t, const Geometry &g, hipStream_t s);
-// Ring / tree: ``grid`` sizes the persistent launch of the any-n kernels;
-// the compile-time-n kernels launch one workgroup per window and reserve
-// ``lds`` bytes of dynamic LDS (a residency cap, as for the fused kernels).
+// Ring / staged tree: ``grid`` sizes the persistent launch of the any-n
+// kernels; the compile-time-n ring kernels launch one workgroup per window and
+// reserve ``lds`` bytes of dynamic LDS (a residency cap, as for the fused
+// kernels).
 hipError_t launch_ring_allreduce(int dt, int op, const RankTable &t, const Geometry &g, int grid, int lds,
                                  hipStream_t s);
 hipError_t launch_ring_reduce_scatter(int dt, int op, const RankTable &t, const Geometry &g, int grid, int lds,
                                       hipStream_t s);
 hipError_t launch_ring_all_gather(const RankTable &t, const Geometry &g, int grid, int lds, hipStream_t s);
+// Tree and double tree for n <= 16 in one register pass (shapes fixed at
+// compile time; dual: the first tree over [0, g.split), the second over
+// [g.split, Vfull)); ``lds`` as for the fused kernels.
+hipError_t launch_tree_reg_allreduce(bool dual, int dt, int op, const RankTable &t, const Geometry &g, int lds,
+                                     hipStream_t s);
 // Tree: one shape over all of [0, Vfull); double tree: ``tree`` over vectors
 // [0, g.split) and ``tree2`` over [g.split, Vfull), in one launch.
 hipError_t launch_tree_allreduce(int dt, int op, const RankTable &t, const TreeShape &tree, const Geometry &g,
-                                 int grid, int lds, hipStream_t s);
+                                 int grid, hipStream_t s);
 hipError_t launch_dtree_allreduce(int dt, int op, const RankTable &t, const TreeShape &tree, const TreeShape &tree2,
                                   const Geometry &g, int grid, hipStream_t s);
 // Element-wise paths (any alignment, and the all-reduce tail), elements
@@ -161,11 +167,10 @@ constexpr int kFusedLdsAllGatherByN[17] = {0, 0, 14, 18, 26, 30, 34, 34, 48, 48,
 constexpr int kFusedLdsAllReduceKB = 24;
 constexpr int kFusedLdsReduceScatterKB = 48;   // n > 16, two vectors per lane (3 workgroups per CU)
 constexpr int kFusedLdsAllGatherKB = 64;
-// Default dynamic-LDS reservation of the compile-time-n ring and tree
-// workgroups, in KB (on top of their static LDS).
+// Default dynamic-LDS reservation of the compile-time-n ring workgroups, in
+// KB (on top of their static LDS).
 constexpr int kRingLdsKB = 0;
 constexpr int kRingLdsAllGatherKB = 0;
-constexpr int kTreeLdsKB = 0;
 // Ring/tree kernels: at most this many (rank, vector) items per thread.
 constexpr int kItemsPerThread = 4;
 

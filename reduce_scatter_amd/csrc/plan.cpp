@@ -39,6 +39,9 @@
 
 #include "../../include/ar.h"
 #include "ar_host.hpp"
+#include "tree_shape.hpp"
+
+static_assert(ar::kTopoRanks == ar::kTableRanks, "tree shapes cover the rank table");
 
 namespace ar {
 
@@ -197,56 +200,22 @@ int size_bin(double bytes) {
 
 }  // namespace
 
-int tree_parent(int n, int v) {
-    if (v <= 0 || v >= n) return -1;                // rank 0 is the root
-    const int low = v & -v;                         // lowest set bit: fixes the depth
-    int p = (v ^ low) | (low << 1);                 // clear it, set the next bit up
-    if (p >= n) p = v ^ low;                        // at the edge of the range: just clear it
-    return p;
-}
+int tree_parent(int n, int v) { return topo_tree_parent(n, v); }
 
-// The double binary tree's second tree (section "The double binary tree":
-// the roles of leaves and interior ranks swapped): the mirror image of the
-// first when n is even (rank v takes rank n-1-v's place), the first shifted by
-// one rank when n is odd (rank v takes rank v-1's place).  which = 0 is the
-// first tree.
-int dtree_parent(int n, int which, int v) {
-    if (v < 0 || v >= n) return -1;
-    if (which == 0) return tree_parent(n, v);
-    if (n % 2 == 0) {
-        const int p = tree_parent(n, n - 1 - v);
-        return p < 0 ? -1 : n - 1 - p;
-    }
-    const int p = tree_parent(n, (v + n - 1) % n);
-    return p < 0 ? -1 : (p + 1) % n;
-}
+int dtree_parent(int n, int which, int v) { return topo_dtree_parent(n, which, v); }
 
 void tree_build(int n, TreeShape &t, int which) {
+    const TreeTopo s = tree_topo(n, which);
     memset(&t, 0, sizeof t);
     for (int v = 0; v < kTableRanks; ++v) {
-        t.parent[v] = -1;
-        t.child[v][0] = t.child[v][1] = -1;
+        t.depth[v] = (int8_t)s.depth[v];
+        t.parent[v] = (int8_t)s.parent[v];
+        t.child[v][0] = (int8_t)s.child[v][0];
+        t.child[v][1] = (int8_t)s.child[v][1];
+        t.post[v] = (uint8_t)s.post[v];
     }
-    t.max_depth = 0;
-    t.root = 0;
-    for (int v = 0; v < n; ++v) {
-        int d = 0;
-        for (int p = dtree_parent(n, which, v); p >= 0; p = dtree_parent(n, which, p)) ++d;
-        t.depth[v] = (int8_t)d;
-        if (d > t.max_depth) t.max_depth = d;
-        t.parent[v] = (int8_t)dtree_parent(n, which, v);
-        if (t.parent[v] < 0) t.root = v;
-    }
-    for (int v = 0; v < n; ++v) {                   // children in ascending rank order
-        const int p = t.parent[v];
-        if (p < 0) continue;
-        if (t.child[p][0] < 0) t.child[p][0] = (int8_t)v;
-        else t.child[p][1] = (int8_t)v;
-    }
-    int k = 0;                                      // children first: deepest level first
-    for (int d = t.max_depth; d >= 0; --d)
-        for (int v = 0; v < n; ++v)
-            if (t.depth[v] == d) t.post[k++] = (uint8_t)v;
+    t.max_depth = s.max_depth;
+    t.root = s.root;
 }
 
 size_t elem_size(int dtype) { return (dtype == AR_BFLOAT16 || dtype == AR_FLOAT16) ? 2 : 4; }

@@ -9,6 +9,10 @@
 // down, every node keeping a copy.  2 * depth dependent steps instead of the
 // ring's 2(n-1).
 //
+// These LDS-staged kernels serve n > 16 (and n <= 16 under AR_TREE_STAGED=1);
+// up to 16 ranks tree_reg.hip evaluates the same trees in registers in one
+// pass, with the same results.
+//
 // One workgroup runs the whole tree for a window of W vectors at the same
 // offset of every rank buffer.  Item (rank v, vector w) holds rank v's
 // contribution; LDS holds one partial per rank.  Up phase, deepest level
@@ -27,7 +31,6 @@
 #include "ar_device.hpp"
 #include "ar_kernels.hpp"
 #include "dispatch.hpp"
-#include "tree_fast.hpp"
 
 namespace ar {
 
@@ -107,9 +110,7 @@ __global__ __launch_bounds__(kThreads) void tree_allreduce_kernel(const RankTabl
 
 template <bool DUAL>
 hipError_t launch_trees(int dt, int op, const RankTable &t, const TreeShape &tree, const TreeShape &tree2,
-                        const Geometry &g, int grid, int lds, hipStream_t s) {
-    if (g.n >= 2 && g.n <= 8) return launch_tree_fast_range<2, 8, DUAL>(dt, op, t, tree, tree2, g, lds, s);
-    if (g.n >= 9 && g.n <= 16) return launch_tree_fast_hi(DUAL, dt, op, t, tree, tree2, g, lds, s);
+                        const Geometry &g, int grid, hipStream_t s) {
     return dispatch(dt, op, [&](auto D, auto O) {
         return launch(tree_allreduce_kernel<decltype(D)::value, decltype(O)::value, DUAL>, dim3(grid), dim3(kThreads),
                       (size_t)g.n * g.W * 16, s, t, tree, tree2, g);
@@ -117,13 +118,13 @@ hipError_t launch_trees(int dt, int op, const RankTable &t, const TreeShape &tre
 }
 
 hipError_t launch_tree_allreduce(int dt, int op, const RankTable &t, const TreeShape &tree, const Geometry &g,
-                                 int grid, int lds, hipStream_t s) {
-    return launch_trees<false>(dt, op, t, tree, tree, g, grid, lds, s);
+                                 int grid, hipStream_t s) {
+    return launch_trees<false>(dt, op, t, tree, tree, g, grid, s);
 }
 
 hipError_t launch_dtree_allreduce(int dt, int op, const RankTable &t, const TreeShape &tree, const TreeShape &tree2,
                                   const Geometry &g, int grid, hipStream_t s) {
-    return launch_trees<true>(dt, op, t, tree, tree2, g, grid, 0, s);
+    return launch_trees<true>(dt, op, t, tree, tree2, g, grid, s);
 }
 
 }  // namespace ar
