@@ -83,7 +83,7 @@ int grid_for(long long units, int cus, int per_cu) {
 // on MI355X with gradient-like data: every collective wants fewer resident
 // workgroups the more ranks it streams (the per-rank-count tables in
 // ar_kernels.hpp; past 16 ranks the all-reduce's wide kernel runs uncapped,
-// the all-gather keeps 22 KB and the reduce-scatter none).  AR_FUSED_LDS_KB
+// the all-gather reserves 64 KB and the reduce-scatter 48 KB).  AR_FUSED_LDS_KB
 // overrides all of them.
 int fused_lds_bytes(ar_coll_t coll, int n) {
     static int env = -2;

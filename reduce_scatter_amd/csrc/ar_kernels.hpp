@@ -164,7 +164,7 @@ constexpr int kFusedLdsAllReduceByN[17] = {0, 0, 6, 10, 14, 16, 20, 22, 24, 28, 
 // to n = 16, 6.9 at 32, 6.1 at 72).
 constexpr int kFusedLdsReduceScatterByN[17] = {0, 0, 0, 6, 10, 12, 14, 14, 14, 16, 18, 20, 22, 22, 24, 24, 24};
 constexpr int kFusedLdsAllGatherByN[17] = {0, 0, 14, 18, 26, 30, 34, 34, 48, 48, 48, 48, 48, 48, 48, 64, 64};
-constexpr int kFusedLdsAllReduceKB = 24;
+constexpr int kFusedLdsAllReduceKB = 0;      // n > 16 (the wide kernel): every cap from 10 to 64 KB measured slower
 constexpr int kFusedLdsReduceScatterKB = 48;   // n > 16, two vectors per lane (3 workgroups per CU)
 constexpr int kFusedLdsAllGatherKB = 64;
 // Default dynamic-LDS reservation of the compile-time-n ring workgroups, in

@@ -180,7 +180,7 @@ hipError_t launch_fused_allreduce(int dt, int op, const RankTable &t, const Geom
         const dim3 grid((unsigned)fused_wide_windows(dt, maxlen), (unsigned)g.n);
         return dispatch(dt, op, [&](auto D, auto O) {
             return launch(fused_allreduce_wide_kernel<decltype(D)::value, decltype(O)::value>, grid,
-                          dim3(kFusedThreads), 0, s, t, g);
+                          dim3(kFusedThreads), (size_t)lds, s, t, g);
         });
     }
     const dim3 grid((unsigned)g.windows, (unsigned)g.n);
