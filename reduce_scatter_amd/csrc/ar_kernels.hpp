@@ -10,10 +10,28 @@ namespace ar {
 
 constexpr int kTableRanks = 128;
 
-struct RankTable {
-    const void *src[kTableRanks];
-    void *dst[kTableRanks];
+// One pointer pair per rank, by value in the kernel arguments.  Kernels built
+// for a compile-time rank count NR take a table of exactly NR entries
+// (RankTableFor<NR>): the runtime copies every kernel argument on every
+// launch, and the full 128-rank table (2 KB) cost about 1.4 us of host time
+// per launch on MI355X (4.1 against 2.7 us for a kernel with one int argument).
+template <int CAP> struct RankTableN {
+    const void *src[CAP];
+    void *dst[CAP];
 };
+using RankTable = RankTableN<kTableRanks>;
+template <int NR> using RankTableFor = RankTableN<(NR > 0 ? NR : kTableRanks)>;
+
+// The first entries of ``t`` as the table a kernel for NR ranks takes.
+template <int NR> inline RankTableFor<NR> narrow(const RankTable &t) {
+    constexpr int cap = NR > 0 ? NR : kTableRanks;
+    RankTableFor<NR> r;
+    for (int i = 0; i < cap; ++i) {
+        r.src[i] = t.src[i];
+        r.dst[i] = t.dst[i];
+    }
+    return r;
+}
 
 // Geometry of one collective call, in 16-byte vectors of the element type.
 //   all-reduce:     chunk c = vectors [floor(c*V/n), floor((c+1)*V/n)) of

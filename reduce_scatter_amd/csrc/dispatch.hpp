@@ -8,9 +8,13 @@
 namespace ar {
 
 // Launch ``k`` and return the launch's own status (not the thread's last-error
-// state, which earlier unrelated runtime calls may have left set).
+// state, which earlier unrelated runtime calls may have left set).  The
+// runtime reads each argument through its address with the size of the
+// kernel's parameter, so every argument must have exactly the parameter's type.
 template <typename... P, typename... A>
 hipError_t launch(void (*k)(P...), dim3 grid, dim3 block, size_t lds, hipStream_t s, const A &...args) {
+    static_assert(sizeof...(P) == sizeof...(A), "kernel argument count");
+    static_assert((std::is_same<typename std::decay<P>::type, A>::value && ...), "kernel argument types");
     void *ptrs[] = {(void *)&args...};
     return hipLaunchKernel((const void *)k, grid, block, ptrs, lds, s);
 }

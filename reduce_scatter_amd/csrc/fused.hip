@@ -34,8 +34,8 @@ __device__ __forceinline__ void tile_coords(int &c, long long &j) {
     j = (long long)blockIdx.x;
 }
 
-template <int NR>
-__device__ __forceinline__ void store_all(const RankTable &t, int n, long long base, unsigned lane_off, u32x4 w) {
+template <int NR, class TAB>
+__device__ __forceinline__ void store_all(const TAB &t, int n, long long base, unsigned lane_off, u32x4 w) {
     if constexpr (NR > 0) {
 #pragma unroll
         for (int r = 0; r < NR; ++r)
@@ -54,7 +54,7 @@ __device__ __forceinline__ long long chunk_start(int c, const Geometry &g) {
 }
 
 template <int DT, int OP, int NR>
-__global__ __launch_bounds__(kFusedThreads) void fused_allreduce_kernel(const RankTable t, const Geometry g) {
+__global__ __launch_bounds__(kFusedThreads) void fused_allreduce_kernel(const RankTableFor<NR> t, const Geometry g) {
     const int n = NR > 0 ? NR : g.n;
     int c;
     long long j;
@@ -154,7 +154,7 @@ __global__ __launch_bounds__(kFusedThreads) void fused_allreduce_wide_kernel(con
 // the reduce-scatter and the all-reduce (n loads per store) ran best with
 // non-temporal loads and stores.
 template <int NR>
-__global__ __launch_bounds__(kFusedThreads) void fused_all_gather_kernel(const RankTable t, const Geometry g) {
+__global__ __launch_bounds__(kFusedThreads) void fused_all_gather_kernel(const RankTableFor<NR> t, const Geometry g) {
     const int n = NR > 0 ? NR : g.n;
     int k;
     long long j;
@@ -187,7 +187,7 @@ hipError_t launch_fused_allreduce(int dt, int op, const RankTable &t, const Geom
     return dispatch(dt, op, [&](auto D, auto O) {
         return by_ranks(g.n, [&](auto R) {
             return launch(fused_allreduce_kernel<decltype(D)::value, decltype(O)::value, decltype(R)::value>, grid,
-                          dim3(kFusedThreads), (size_t)lds, s, t, g);
+                          dim3(kFusedThreads), (size_t)lds, s, narrow<decltype(R)::value>(t), g);
         });
     });
 }
@@ -195,7 +195,8 @@ hipError_t launch_fused_allreduce(int dt, int op, const RankTable &t, const Geom
 hipError_t launch_fused_all_gather(const RankTable &t, const Geometry &g, int lds, hipStream_t s) {
     const dim3 grid((unsigned)g.windows, (unsigned)g.n);
     return by_ranks(g.n, [&](auto R) {
-        return launch(fused_all_gather_kernel<decltype(R)::value>, grid, dim3(kFusedThreads), (size_t)lds, s, t, g);
+        return launch(fused_all_gather_kernel<decltype(R)::value>, grid, dim3(kFusedThreads), (size_t)lds, s,
+                      narrow<decltype(R)::value>(t), g);
     });
 }
 

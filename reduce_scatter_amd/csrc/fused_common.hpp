@@ -29,8 +29,8 @@ __device__ __forceinline__ int hop_rank(int c, int k, int n) {
 // (n <= 16), all n*U loads issued before the first combine; NR == 0: any n,
 // batches of 16 loads.  KEEP32: bf16 / fp16 partials stay fp32 (rounded in
 // ``finish``).  Each acc[u] sees the ranks in the same order whatever U is.
-template <int DT, int OP, int NR, bool KEEP32, int U>
-__device__ __forceinline__ void chain_in(const RankTable &t, int n, int c, long long base,
+template <int DT, int OP, int NR, bool KEEP32, int U, class TAB>
+__device__ __forceinline__ void chain_in(const TAB &t, int n, int c, long long base,
                                          const unsigned (&lane_off)[U], float s, Pack<DT> (&acc)[U]) {
     if constexpr (NR > 0) {
         u32x4 raw[NR][U];
@@ -74,16 +74,16 @@ __device__ __forceinline__ void chain_in(const RankTable &t, int n, int c, long 
 
 // The chain with the partials' precision chosen once per tile (a uniform
 // branch; only bf16 / fp16 have two).
-template <int DT, int OP, int NR, int U>
-__device__ __forceinline__ void chain(const RankTable &t, int n, int c, long long base, const unsigned (&lane_off)[U],
+template <int DT, int OP, int NR, int U, class TAB>
+__device__ __forceinline__ void chain(const TAB &t, int n, int c, long long base, const unsigned (&lane_off)[U],
                                       float s, bool keep32, Pack<DT> (&acc)[U]) {
     if constexpr (DT == BF16 || DT == F16) {
         if (keep32) {
-            chain_in<DT, OP, NR, true, U>(t, n, c, base, lane_off, s, acc);
+            chain_in<DT, OP, NR, true, U, TAB>(t, n, c, base, lane_off, s, acc);
             return;
         }
     }
-    chain_in<DT, OP, NR, false, U>(t, n, c, base, lane_off, s, acc);
+    chain_in<DT, OP, NR, false, U, TAB>(t, n, c, base, lane_off, s, acc);
 }
 
 // Pick the compile-time rank count: every n up to 16 has its own kernels, so a

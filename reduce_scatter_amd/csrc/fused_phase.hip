@@ -28,8 +28,8 @@ namespace ar {
 // ``ph``) in the hop order of chunk c.  Each lane loads the two aligned
 // vectors that hold its bytes, every load of the chain issued before the first
 // combine; the second vector of a lane is its neighbour's first (a cache hit).
-template <int DT, int OP, int NR, bool KEEP32>
-__device__ __forceinline__ Pack<DT> chain_phased(const RankTable &t, int n, int c, long long base, unsigned lane_off,
+template <int DT, int OP, int NR, bool KEEP32, class TAB>
+__device__ __forceinline__ Pack<DT> chain_phased(const TAB &t, int n, int c, long long base, unsigned lane_off,
                                                  unsigned ph, float s) {
     Pack<DT> acc;
     if constexpr (NR > 0) {
@@ -78,7 +78,7 @@ __device__ __forceinline__ Pack<DT> chain_phased(const RankTable &t, int n, int 
 // is still in the buffer, so its vector exists (whole, as buffers start on a
 // 16-byte boundary).
 template <int DT, int OP, int NR, bool KEEP32>
-__device__ __forceinline__ void rs_phased(const RankTable &t, const Geometry &g) {
+__device__ __forceinline__ void rs_phased(const RankTableFor<NR> &t, const Geometry &g) {
     const int n = NR > 0 ? NR : g.n;
     const int c = (int)blockIdx.y;
     const TileSpan ts = aligned_tile(0, g.Rv, (long long)blockIdx.x, (long long)((uintptr_t)t.dst[c] >> 4), kFusedTile);
@@ -93,7 +93,7 @@ __device__ __forceinline__ void rs_phased(const RankTable &t, const Geometry &g)
 }
 
 template <int DT, int OP, int NR>
-__global__ __launch_bounds__(kFusedThreads) void fused_reduce_scatter_phased_kernel(const RankTable t,
+__global__ __launch_bounds__(kFusedThreads) void fused_reduce_scatter_phased_kernel(const RankTableFor<NR> t,
                                                                                    const Geometry g) {
     if constexpr (DT == BF16 || DT == F16) {
         if (g.acc32) {
@@ -110,7 +110,8 @@ __global__ __launch_bounds__(kFusedThreads) void fused_reduce_scatter_phased_ker
 // 16*o - k*Rb.  Tiles follow the outputs' alignment (g.ref); the same bound
 // as above keeps both loads of a lane inside the input piece's vectors.
 template <int NR>
-__global__ __launch_bounds__(kFusedThreads) void fused_all_gather_phased_kernel(const RankTable t, const Geometry g) {
+__global__ __launch_bounds__(kFusedThreads) void fused_all_gather_phased_kernel(const RankTableFor<NR> t,
+                                                                                const Geometry g) {
     const int n = NR > 0 ? NR : g.n;
     const int k = (int)blockIdx.y;
     const long long b0 = (long long)k * g.slice_bytes;
@@ -140,7 +141,7 @@ hipError_t launch_fused_reduce_scatter_phased(int dt, int op, const RankTable &t
     return dispatch(dt, op, [&](auto D, auto O) {
         return by_ranks(g.n, [&](auto R) {
             return launch(fused_reduce_scatter_phased_kernel<decltype(D)::value, decltype(O)::value, decltype(R)::value>,
-                          grid, dim3(kFusedThreads), (size_t)lds, s, t, g);
+                          grid, dim3(kFusedThreads), (size_t)lds, s, narrow<decltype(R)::value>(t), g);
         });
     });
 }
@@ -151,7 +152,7 @@ hipError_t launch_fused_all_gather_phased(const RankTable &t, const Geometry &g,
     const dim3 grid((unsigned)aligned_tiles(most, kFusedTile), (unsigned)g.n);
     return by_ranks(g.n, [&](auto R) {
         return launch(fused_all_gather_phased_kernel<decltype(R)::value>, grid, dim3(kFusedThreads), (size_t)lds, s,
-                      t, g);
+                      narrow<decltype(R)::value>(t), g);
     });
 }
 

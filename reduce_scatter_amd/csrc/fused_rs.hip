@@ -19,7 +19,7 @@
 namespace ar {
 
 template <int DT, int OP, int NR, int U>
-__global__ __launch_bounds__(kFusedThreads) void fused_reduce_scatter_kernel(const RankTable t, const Geometry g) {
+__global__ __launch_bounds__(kFusedThreads) void fused_reduce_scatter_kernel(const RankTableFor<NR> t, const Geometry g) {
     const int n = NR > 0 ? NR : g.n;
     const int c = (int)blockIdx.y;
     // tiles follow the alignment of the n input slices (slice c of the reference input)
@@ -54,7 +54,7 @@ hipError_t launch_fused_reduce_scatter(int dt, int op, const RankTable &t, const
     return dispatch(dt, op, [&](auto D, auto O) {
         return by_ranks(g.n, [&](auto R) {
             return launch(fused_reduce_scatter_kernel<decltype(D)::value, decltype(O)::value, decltype(R)::value, 1>,
-                          grid, dim3(kFusedThreads), (size_t)lds, s, t, g);
+                          grid, dim3(kFusedThreads), (size_t)lds, s, narrow<decltype(R)::value>(t), g);
         });
     });
 }

@@ -248,7 +248,7 @@ __device__ __forceinline__ long long ring_chunk_start(int c, const Geometry &g) 
 }
 
 template <int DT, int OP, int NR>
-__global__ __launch_bounds__(RingShape<NR>::T) void ring_allreduce_fast(const RankTable t, const Geometry g) {
+__global__ __launch_bounds__(RingShape<NR>::T) void ring_allreduce_fast(const RankTableFor<NR> t, const Geometry g) {
     constexpr int W = RingShape<NR>::W;
     __shared__ u32x4 slot[NR * W];                 // the wire: one slot per chunk and vector
     const int r = threadIdx.x / W, w = threadIdx.x % W;
@@ -297,7 +297,7 @@ __global__ __launch_bounds__(RingShape<NR>::T) void ring_allreduce_fast(const Ra
 }
 
 template <int DT, int OP, int NR>
-__global__ __launch_bounds__(RingShape<NR>::T) void ring_reduce_scatter_fast(const RankTable t, const Geometry g) {
+__global__ __launch_bounds__(RingShape<NR>::T) void ring_reduce_scatter_fast(const RankTableFor<NR> t, const Geometry g) {
     constexpr int W = RingShape<NR>::W;
     __shared__ u32x4 slot[NR * W];
     const int r = threadIdx.x / W, w = threadIdx.x % W;
@@ -338,7 +338,7 @@ __global__ __launch_bounds__(RingShape<NR>::T) void ring_reduce_scatter_fast(con
 }
 
 template <int NR>
-__global__ __launch_bounds__(RingShape<NR>::T) void ring_all_gather_fast(const RankTable t, const Geometry g) {
+__global__ __launch_bounds__(RingShape<NR>::T) void ring_all_gather_fast(const RankTableFor<NR> t, const Geometry g) {
     constexpr int W = RingShape<NR>::W;
     __shared__ u32x4 slot[NR * W];
     const int r = threadIdx.x / W, w = threadIdx.x % W;
@@ -400,7 +400,8 @@ hipError_t launch_ring_allreduce(int dt, int op, const RankTable &t, const Geome
         return dispatch(dt, op, [&](auto D, auto O) {
             return ring_by_ranks(g.n, [&](auto R) {
                 return launch(ring_allreduce_fast<decltype(D)::value, decltype(O)::value, decltype(R)::value>,
-                              blocks, dim3(RingShape<decltype(R)::value>::T), (size_t)lds, s, t, g);
+                              blocks, dim3(RingShape<decltype(R)::value>::T), (size_t)lds, s,
+                              narrow<decltype(R)::value>(t), g);
             });
         });
     }
@@ -417,7 +418,8 @@ hipError_t launch_ring_reduce_scatter(int dt, int op, const RankTable &t, const 
         return dispatch(dt, op, [&](auto D, auto O) {
             return ring_by_ranks(g.n, [&](auto R) {
                 return launch(ring_reduce_scatter_fast<decltype(D)::value, decltype(O)::value, decltype(R)::value>,
-                              blocks, dim3(RingShape<decltype(R)::value>::T), (size_t)lds, s, t, g);
+                              blocks, dim3(RingShape<decltype(R)::value>::T), (size_t)lds, s,
+                              narrow<decltype(R)::value>(t), g);
             });
         });
     }
@@ -432,7 +434,7 @@ hipError_t launch_ring_all_gather(const RankTable &t, const Geometry &g, int gri
         const dim3 blocks((unsigned)ring_fast_windows(g, false));
         return ring_by_ranks(g.n, [&](auto R) {
             return launch(ring_all_gather_fast<decltype(R)::value>, blocks, dim3(RingShape<decltype(R)::value>::T),
-                          (size_t)lds, s, t, g);
+                          (size_t)lds, s, narrow<decltype(R)::value>(t), g);
         });
     }
     return launch(ring_all_gather_kernel, dim3(grid), dim3(kThreads), ring_lds_bytes(g, false), s, t, g);

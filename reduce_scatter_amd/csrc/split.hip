@@ -104,8 +104,8 @@ __device__ __forceinline__ void push_waves(PairStack<DT, OP, L> &ps, const u32x4
 // wave).  Phase 2: each tile vector's partials are combined once, by one
 // thread, the postOp applied, the result written back to LDS.  Phase 3: every
 // wave stores the finished tile to its own ranks.
-template <int DT, int OP, int K, int U>
-__global__ __launch_bounds__(kFusedThreads *kSplitMaxWaves) void split_allreduce_kernel(const RankTable t,
+template <int DT, int OP, int K, int U, int CAP>
+__global__ __launch_bounds__(kFusedThreads *kSplitMaxWaves) void split_allreduce_kernel(const RankTableN<CAP> t,
                                                                                         const Geometry g) {
     constexpr int T = kFusedThreads * U;                        // vectors per tile
     __shared__ u32x4 part[kSplitMaxWaves * T];                  // part[w * T + v]
@@ -227,20 +227,30 @@ int split_lds_bytes() {
     return v;
 }
 
+// The rank table goes in at 16 entries for n <= 16 (256 bytes of kernel
+// arguments instead of 2 KB: the split kernel serves the small calls, where
+// the launch's host time is the call's cost).
+template <int DT, int OP, int K, int CAP>
+hipError_t launch_split_cap(int U, const RankTableN<CAP> &t, const Geometry &g, dim3 grid, dim3 block, size_t lds,
+                            hipStream_t s) {
+    switch (U) {
+    case 1: return launch(split_allreduce_kernel<DT, OP, K, 1, CAP>, grid, block, lds, s, t, g);
+    case 2:
+        if constexpr (K < 16) return launch(split_allreduce_kernel<DT, OP, K, 2, CAP>, grid, block, lds, s, t, g);
+        return hipErrorInvalidValue;
+    default:
+        if constexpr (K < 8) return launch(split_allreduce_kernel<DT, OP, K, 4, CAP>, grid, block, lds, s, t, g);
+        return hipErrorInvalidValue;
+    }
+}
+
 template <int DT, int OP, int K>
 hipError_t launch_split_u(int U, const RankTable &t, const Geometry &g, dim3 block, hipStream_t s) {
     const long long T = (long long)kFusedThreads * U;
     const dim3 grid((unsigned)((((g.ref & (T - 1)) + g.Vfull) + T - 1) / T));       // tiles of the aligned grid
     const size_t lds = (size_t)split_lds_bytes();
-    switch (U) {
-    case 1: return launch(split_allreduce_kernel<DT, OP, K, 1>, grid, block, lds, s, t, g);
-    case 2:
-        if constexpr (K < 16) return launch(split_allreduce_kernel<DT, OP, K, 2>, grid, block, lds, s, t, g);
-        return hipErrorInvalidValue;
-    default:
-        if constexpr (K < 8) return launch(split_allreduce_kernel<DT, OP, K, 4>, grid, block, lds, s, t, g);
-        return hipErrorInvalidValue;
-    }
+    if (g.n <= 16) return launch_split_cap<DT, OP, K, 16>(U, narrow<16>(t), g, grid, block, lds, s);
+    return launch_split_cap<DT, OP, K, kTableRanks>(U, t, g, grid, block, lds, s);
 }
 
 hipError_t launch_split_allreduce(int dt, int op, const RankTable &t, const Geometry &g, hipStream_t s) {

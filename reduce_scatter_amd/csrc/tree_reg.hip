@@ -51,7 +51,7 @@ __device__ __forceinline__ u32x4 tree_value(const u32x4 (&raw)[NR], const Geomet
 }
 
 template <int DT, int OP, int NR, bool DUAL>
-__global__ __launch_bounds__(kFusedThreads) void tree_reg_kernel(const RankTable t, const Geometry g) {
+__global__ __launch_bounds__(kFusedThreads) void tree_reg_kernel(const RankTableFor<NR> t, const Geometry g) {
     const bool second = DUAL && blockIdx.y == 1;
     const long long lo = second ? g.split : 0;
     const long long hi = (DUAL && !second) ? g.split : g.Vfull;
@@ -85,11 +85,12 @@ hipError_t launch_tree_reg_allreduce(bool dual, int dt, int op, const RankTable 
             if constexpr (NR == 0) {
                 return hipErrorInvalidValue;
             } else {
+                const RankTableFor<NR> tn = narrow<NR>(t);
                 if (dual)
                     return launch(tree_reg_kernel<decltype(D)::value, decltype(O)::value, NR, true>, grid,
-                                  dim3(kFusedThreads), (size_t)lds, s, t, g);
+                                  dim3(kFusedThreads), (size_t)lds, s, tn, g);
                 return launch(tree_reg_kernel<decltype(D)::value, decltype(O)::value, NR, false>, grid,
-                              dim3(kFusedThreads), (size_t)lds, s, t, g);
+                              dim3(kFusedThreads), (size_t)lds, s, tn, g);
             }
         });
     });
