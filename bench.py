@@ -52,6 +52,9 @@ def parse():
     p.add_argument("--no-detail", action="store_true")
     p.add_argument("--copy-probe", action="store_true",
                    help="time only a plain device copy of 2 GB (for HBM counter calibration) and exit")
+    p.add_argument("--kernels", action="store_true",
+                   help="instead of the JSON line, run each main kernel family 5 times at its workload's size and "
+                        "print one JSON line per call (for kernel-trace and HBM-counter runs)")
     p.add_argument("--reshard", action="store_true",
                    help="instead of the JSON line, print the M-to-N reshard report (MoE layer, every route)")
     p.add_argument("--sweep", action="store_true",
@@ -62,8 +65,8 @@ def parse():
 
 
 # The kernel each schedule launches at this shape (n = 8, 16-byte aligned buffers).
-KERNEL_OF = {"fused": "fused_allreduce_kernel", "ring": "ring_allreduce_fast", "tree": "tree_allreduce_fast",
-             "split": "split_allreduce_kernel", "dtree": "tree_allreduce_fast"}
+KERNEL_OF = {"fused": "fused_allreduce_kernel", "ring": "ring_allreduce_fast", "tree": "tree_reg_kernel",
+             "split": "split_allreduce_kernel", "dtree": "tree_reg_kernel"}
 
 
 def kernel_source_hash() -> str:
@@ -117,6 +120,54 @@ def copy_probe(args):
     print(json.dumps({"copy_probe_bytes_read": src.numel() * 4, "copy_probe_bytes_written": src.numel() * 4,
                       "launch_ms": round(launch_ms, 4),
                       "gbps": round(2 * src.numel() * 4 / (launch_ms * 1e-3) / 1e9, 1)}), flush=True)
+
+
+def kernel_calls(reps=5):
+    """Each main kernel family at its workload's size, ``reps`` calls each,
+    synchronised per call so a kernel trace or counter run sees whole,
+    separate launches.  Prints the call, its kernel and its algorithmic
+    bytes."""
+    import torch
+    import reduce_scatter_amd as ar
+    import workloads as wl
+    MB = 1 << 20
+
+    def run(name, kernel, alg_bytes, fn):
+        for _ in range(reps):
+            fn()
+            torch.cuda.synchronize()
+        print(json.dumps({"call": name, "kernel": kernel, "algorithmic_bytes": alg_bytes, "calls": reps}), flush=True)
+
+    n, C = N_RANKS, COUNT                                   # n = 8 fp32 all-reduce, 256 MB per rank
+    xs_t = [wl.device_normal(1, 0, r, C, 1e-3, "f32") for r in range(n)]
+    ys_t = [torch.empty(C, device="cuda") for _ in range(n)]
+    xs, ys = ar.pointers(xs_t), ar.pointers(ys_t)
+    for sched, kern in (("fused", "fused_allreduce_kernel"), ("ring", "ring_allreduce_fast"),
+                        ("tree", "tree_reg_kernel"), ("dtree", "tree_reg_kernel"), ("split", "split_allreduce_kernel")):
+        run("all-reduce n=8 f32 256MB/rank sum, %s" % sched, kern, 2 * n * C * 4,
+            lambda: ar.ar_allreduce(xs, ys, C, "f32", "sum", sched=sched))
+    del xs, ys, xs_t, ys_t
+    R = 16 << 20                                            # FSDP shards: n = 8 bf16, 16 Mi elements per shard
+    xs_t = [wl.device_normal(2, 0, r, n * R, 1e-2, "bf16") for r in range(n)]
+    ys_t = [torch.empty(R, dtype=torch.bfloat16, device="cuda") for _ in range(n)]
+    full_t = [torch.empty(n * R, dtype=torch.bfloat16, device="cuda") for _ in range(n)]
+    xs, ys, full = ar.pointers(xs_t), ar.pointers(ys_t), ar.pointers(full_t)
+    for r_, tag in ((R, ""), (R - 1, ", R-1 (phased)")):
+        kern = "fused_reduce_scatter_kernel" if r_ == R else "fused_reduce_scatter_phased_kernel"
+        run("reduce-scatter n=8 bf16 avg R=%d%s" % (r_, tag), kern, (n + 1) * n * r_ * 2,
+            lambda: ar.ar_reduce_scatter(xs, ys, r_, "bf16", "avg", sched="fused"))
+        kern = "fused_all_gather_kernel" if r_ == R else "fused_all_gather_phased_kernel"
+        run("all-gather n=8 bf16 R=%d%s" % (r_, tag), kern, (n + 1) * n * r_ * 2,
+            lambda: ar.ar_all_gather(ys, full, r_, "bf16", sched="fused"))
+    del xs, ys, full, xs_t, ys_t, full_t
+    n72, c72 = 72, 25 * MB // 4                             # 72 ranks, one 25 MB fp32 bucket, in place
+    bufs_t = [wl.device_normal(4, 1, r, c72, 1e-3, "f32") for r in range(n72)]
+    bufs = ar.pointers(bufs_t)
+    for sched, kern in (("split", "split_allreduce_kernel"), ("fused", "fused_allreduce_wide_kernel")):
+        run("all-reduce n=72 f32 25MB/rank avg in place, %s" % sched, kern, 2 * n72 * c72 * 4,
+            lambda: ar.ar_allreduce(bufs, bufs, c72, "f32", "avg", sched=sched))
+    del bufs, bufs_t
+    torch.cuda.empty_cache()
 
 
 def _median_us(fn, iters=10, warmup=2):
@@ -344,6 +395,9 @@ def main():
     torch.cuda.set_device(0)
     if args.copy_probe:
         copy_probe(args)
+        return 0
+    if args.kernels:
+        kernel_calls()
         return 0
     if args.sweep:
         sweep()

@@ -15,18 +15,19 @@ constexpr int kTableRanks = 128;
 // (RankTableFor<NR>): the runtime copies every kernel argument on every
 // launch, and the full 128-rank table (2 KB) cost about 1.4 us of host time
 // per launch on MI355X (4.1 against 2.7 us for a kernel with one int argument).
+// CAP = 0 is the full table of kTableRanks entries (the any-n kernels').
 template <int CAP> struct RankTableN {
-    const void *src[CAP];
-    void *dst[CAP];
+    static constexpr int kCap = CAP > 0 ? CAP : kTableRanks;
+    const void *src[kCap];
+    void *dst[kCap];
 };
-using RankTable = RankTableN<kTableRanks>;
-template <int NR> using RankTableFor = RankTableN<(NR > 0 ? NR : kTableRanks)>;
+using RankTable = RankTableN<0>;
+template <int NR> using RankTableFor = RankTableN<NR>;
 
 // The first entries of ``t`` as the table a kernel for NR ranks takes.
 template <int NR> inline RankTableFor<NR> narrow(const RankTable &t) {
-    constexpr int cap = NR > 0 ? NR : kTableRanks;
     RankTableFor<NR> r;
-    for (int i = 0; i < cap; ++i) {
+    for (int i = 0; i < RankTableFor<NR>::kCap; ++i) {
         r.src[i] = t.src[i];
         r.dst[i] = t.dst[i];
     }

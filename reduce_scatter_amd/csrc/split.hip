@@ -250,7 +250,7 @@ hipError_t launch_split_u(int U, const RankTable &t, const Geometry &g, dim3 blo
     const dim3 grid((unsigned)((((g.ref & (T - 1)) + g.Vfull) + T - 1) / T));       // tiles of the aligned grid
     const size_t lds = (size_t)split_lds_bytes();
     if (g.n <= 16) return launch_split_cap<DT, OP, K, 16>(U, narrow<16>(t), g, grid, block, lds, s);
-    return launch_split_cap<DT, OP, K, kTableRanks>(U, t, g, grid, block, lds, s);
+    return launch_split_cap<DT, OP, K, 0>(U, t, g, grid, block, lds, s);
 }
 
 hipError_t launch_split_allreduce(int dt, int op, const RankTable &t, const Geometry &g, hipStream_t s) {
