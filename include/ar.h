@@ -59,7 +59,11 @@
  * arrays during the call only (they are copied by value into the kernel
  * arguments) and allocates no device memory on any call.  Buffers must be
  * aligned to their element size; 16-byte alignment of every pointer selects
- * the vector paths, otherwise an element-wise path gives identical results.
+ * the vector paths.  All-reduce buffers that all sit at one 16-byte phase
+ * (every address the same mod 16, e.g. views at one offset of per-rank flat
+ * buffers) run the vector kernels from the first 16-byte boundary, the few
+ * elements around it element-wise; other alignments take an element-wise path.
+ * Every path gives identical results.
  * For reduce-scatter and all-gather with R * element size not a multiple of
  * 16, the vector path reads the input slices through aligned 16-byte vectors
  * and may read (never write) the rest of the 16-byte block that holds an

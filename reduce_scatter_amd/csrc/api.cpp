@@ -132,6 +132,14 @@ int lds_window(int n) {
     return w < 1 ? 1 : w;
 }
 
+// The 16-byte phase (address mod 16) shared by all 2n pointers, or -1.
+int common_phase(const void *const *a, const void *const *b, int n) {
+    const int ph = (int)((uintptr_t)a[0] & 15);
+    for (int r = 0; r < n; ++r)
+        if ((int)((uintptr_t)a[r] & 15) != ph || (int)((uintptr_t)b[r] & 15) != ph) return -1;
+    return ph;
+}
+
 bool null_entry(const void *const *p, int n) {
     for (int r = 0; r < n; ++r)
         if (!p[r]) return true;
@@ -367,38 +375,95 @@ ar_status_t ar_allreduce_ex(const void *const *sendbufs, void *const *recvbufs, 
         if (use == AR_SCHED_SPLIT) return launch_elem_split_allreduce(dtype, op, t, g, e_begin, (long long)count, stream);
         return launch_elem_ring_allreduce(dtype, op, t, g, e_begin, (long long)count, stream);
     };
-    if (!all16(sendbufs, (const void *const *)recvbufs, n)) return hip_status(elem(0));   // element-wise path
-    hipError_t h = hipSuccess;
-    if (g.Vfull > 0) {
+    g.split2 = g.split;
+
+    // The schedule's vector kernels over frame vectors [0, g.Vfull) of the pointers in ``tv``.
+    auto vectors = [&](const RankTable &tv) -> ar_status_t {
+        hipError_t h = hipSuccess;
+        if (g.Vfull <= 0) return AR_OK;
         if (use == AR_SCHED_SPLIT) {
             if ((g.Vfull + kFusedTile - 1) / kFusedTile > 0x7fffffffLL) return AR_ERR_UNSUPPORTED;   // grid x limit
-            h = launch_split_allreduce(dtype, op, t, g, stream);
+            h = launch_split_allreduce(dtype, op, tv, g, stream);
         } else if (use == AR_SCHED_FUSED) {
             const long long maxlen = (g.V + n - 1) / n;                       // longest chunk, in vectors
             g.windows = aligned_tiles(maxlen, kFusedTile);
             if (g.windows > 0x7fffffffLL) return AR_ERR_UNSUPPORTED;   // grid x limit
-            h = launch_fused_allreduce(dtype, op, t, g, fused_lds_bytes(AR_COLL_ALLREDUCE, n), stream);
+            h = launch_fused_allreduce(dtype, op, tv, g, fused_lds_bytes(AR_COLL_ALLREDUCE, n), stream);
         } else if (use == AR_SCHED_RING) {
             g.W = lds_window(n);
             const long long maxlen = (g.V + n - 1) / n;
             g.windows = (maxlen + g.W - 1) / g.W;
-            h = launch_ring_allreduce(dtype, op, t, g, grid_for(g.windows, cus, 4), ring_lds_bytes(AR_COLL_ALLREDUCE), stream);
+            h = launch_ring_allreduce(dtype, op, tv, g, grid_for(g.windows, cus, 4), ring_lds_bytes(AR_COLL_ALLREDUCE), stream);
         } else if (n >= 2 && n <= 16 && !tree_staged()) {               // tree / dtree, in registers
             if (aligned_tiles(g.Vfull, kFusedTile) > 0x7fffffffLL) return AR_ERR_UNSUPPORTED;   // grid x limit
-            h = launch_tree_reg_allreduce(use == AR_SCHED_DTREE, dtype, op, t, g,
+            h = launch_tree_reg_allreduce(use == AR_SCHED_DTREE, dtype, op, tv, g,
                                           fused_lds_bytes(AR_COLL_ALLREDUCE, n), stream);
         } else if (use == AR_SCHED_DTREE) {
             g.W = lds_window(n);
-            g.windows = (g.split + g.W - 1) / g.W + (g.Vfull - g.split + g.W - 1) / g.W;
-            h = launch_dtree_allreduce(dtype, op, t, tree, tree2, g, grid_for(g.windows, cus, 4), stream);
+            g.windows = (g.split + g.W - 1) / g.W + (g.Vfull - g.split2 + g.W - 1) / g.W;
+            h = launch_dtree_allreduce(dtype, op, tv, tree, tree2, g, grid_for(g.windows, cus, 4), stream);
         } else {
             g.W = lds_window(n);
             g.windows = (g.Vfull + g.W - 1) / g.W;
-            h = launch_tree_allreduce(dtype, op, t, tree, g, grid_for(g.windows, cus, 4), stream);
+            h = launch_tree_allreduce(dtype, op, tv, tree, g, grid_for(g.windows, cus, 4), stream);
         }
+        return hip_status(h);
+    };
+
+    if (all16(sendbufs, (const void *const *)recvbufs, n)) {
+        st = vectors(t);
+        if (st != AR_OK) return st;
+        if (g.Vfull * lanes < (long long)count) return hip_status(elem(g.Vfull * lanes));   // tail: count mod lanes
+        return AR_OK;
     }
-    if (h == hipSuccess && g.Vfull * lanes < (long long)count) h = elem(g.Vfull * lanes);   // tail: count mod lanes
-    return hip_status(h);
+
+    // Buffers off 16-byte alignment.  When all 2n pointers sit at the same
+    // 16-byte phase, the vectors run in the frame that starts at the first
+    // 16-byte boundary (``head`` elements in), with the chunks and the double
+    // tree's split still those of element index 0; the element-wise kernels
+    // take exactly the rest: each chunk's first ``head`` elements and the frame
+    // vector across its end (ring order), the head, the vector across the
+    // double tree's split and the tail (tree orders).  Otherwise, or for the
+    // LDS-staged ring past 16 ranks, everything goes element-wise.
+    const int ph = common_phase(sendbufs, (const void *const *)recvbufs, n);
+    const long long head = ph > 0 ? (long long)((16 - ph) / (int)e) : 0;
+    if (ph <= 0 || (long long)count <= head || (use == AR_SCHED_RING && n > 16)) return hip_status(elem(0));
+    RankTable tv = t;
+    for (int r = 0; r < n; ++r) {
+        tv.src[r] = (const char *)sendbufs[r] + head * (long long)e;
+        tv.dst[r] = (char *)recvbufs[r] + head * (long long)e;
+    }
+    const long long S = g.split;                                // the double tree's split, in element-index vectors
+    g.shift = 1;
+    g.Vfull = ((long long)count - head) / lanes;
+    g.ref = (long long)((uintptr_t)tv.dst[0] >> 4);
+    g.split = S >= 1 ? (S - 1 < g.Vfull ? S - 1 : g.Vfull) : 0;  // frame vectors wholly below element lanes*S
+    g.split2 = S < g.Vfull ? S : g.Vfull;                       // ... and wholly at or above it
+    st = vectors(tv);
+    if (st != AR_OK) return st;
+    if (use == AR_SCHED_FUSED || use == AR_SCHED_RING)
+        return hip_status(launch_elem_ring_gaps(dtype, op, t, g, head, (long long)count, stream));
+    const long long end = head + lanes * g.Vfull;               // element ranges the vectors left
+    const long long ranges[3][2] = {{0, head},
+                                    {head + lanes * g.split, use == AR_SCHED_DTREE ? head + lanes * g.split2
+                                                                                   : head + lanes * g.split},
+                                    {end, (long long)count}};
+    for (const auto &rg : ranges) {
+        if (rg[1] <= rg[0]) continue;
+        hipError_t h;
+        if (use == AR_SCHED_SPLIT) {
+            h = launch_elem_split_allreduce(dtype, op, t, g, rg[0], rg[1], stream);
+        } else if (use == AR_SCHED_TREE) {
+            h = launch_elem_tree_allreduce(dtype, op, t, tree, g, rg[0], rg[1], stream);
+        } else {                                                // dtree: element index lanes*S splits the trees
+            const long long cut = lanes * S;
+            const long long m = cut < rg[0] ? rg[0] : (cut > rg[1] ? rg[1] : cut);
+            h = launch_elem_tree_allreduce(dtype, op, t, tree, g, rg[0], m, stream);
+            if (h == hipSuccess) h = launch_elem_tree_allreduce(dtype, op, t, tree2, g, m, rg[1], stream);
+        }
+        if (h != hipSuccess) return hip_status(h);
+    }
+    return AR_OK;
 }
 
 ar_status_t ar_reduce_scatter(const void *const *sendbufs, void *const *recvbufs, size_t recvcount,

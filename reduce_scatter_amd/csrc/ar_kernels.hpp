@@ -52,7 +52,11 @@ struct Geometry {
     int W;              // ring/tree: vectors per rank in one LDS window
     float s;            // fp32(1/n), the float avg pre-scale
     long long ref;      // fused / split: address / 16 of the buffer whose alignment cuts the tiles
-    long long split;    // double tree: vectors [0, split) go up the first tree, the rest up the second
+    long long split;    // double tree: vectors [0, split) go up the first tree, [split2, Vfull) up the second
+    long long split2;   //   (split2 = split, or split + 1 in the shifted frame below)
+    int shift;          // all-reduce in the shifted frame (every buffer at one 16-byte phase, vectors counted
+                        // from the first 16-byte boundary): 1, and chunk c's vectors end one early, the
+                        // vector across each chunk boundary going to the element-wise kernel; else 0
     float post_div;     // split float avg: the finished sum is divided by n / p (0: no post-division)
     int acc32;          // bf16 / fp16 partials kept in fp32, rounded once (the fused schedule)
     long long slice_bytes;  // phased reduce-scatter / all-gather: bytes per slice or piece (not a multiple of 16)
@@ -148,6 +152,10 @@ hipError_t launch_dtree_allreduce(int dt, int op, const RankTable &t, const Tree
 // [e_begin, e_end) of every rank buffer / slice:
 hipError_t launch_elem_ring_allreduce(int dt, int op, const RankTable &t, const Geometry &g, long long e_begin,
                                       long long e_end, hipStream_t s);
+// The ring-order remainder of a shifted-frame all-reduce (every chunk's head,
+// boundary-straddling vector and the tail), ``t`` the callers' pointers.
+hipError_t launch_elem_ring_gaps(int dt, int op, const RankTable &t, const Geometry &g, long long head,
+                                 long long count, hipStream_t s);
 hipError_t launch_elem_tree_allreduce(int dt, int op, const RankTable &t, const TreeShape &tree, const Geometry &g,
                                       long long e_begin, long long e_end, hipStream_t s);
 hipError_t launch_elem_split_allreduce(int dt, int op, const RankTable &t, const Geometry &g, long long e_begin,

@@ -68,6 +68,35 @@ __global__ __launch_bounds__(kThreads) void elem_ring_allreduce_kernel(const Ran
     }
 }
 
+// The element-wise remainder of an all-reduce in ring hop order whose vectors
+// ran in the shifted frame (every buffer at one 16-byte phase; g.Vfull whole
+// vectors counted from element ``head``, chunk c taking frame vectors
+// [B_c, min(B_{c+1} - 1, Vfull))): chunk c (grid y) minus those vectors, i.e.
+// its first ``head`` elements, the vector that straddles its end, and the tail
+// after the last whole frame vector.  ``t`` holds the callers' pointers.
+template <int DT, int OP>
+__global__ __launch_bounds__(kThreads) void elem_ring_gaps_kernel(const RankTable t, const Geometry g,
+                                                                 long long head, long long count) {
+    const int n = g.n;
+    const int c = (int)blockIdx.y;
+    constexpr long long u = Lanes<DT>::value;
+    const long long b0 = (long long)c * g.q + (g.rem ? (long long)((unsigned)(c * g.rem) / (unsigned)n) : 0);
+    const long long b1 = (long long)(c + 1) * g.q + (g.rem ? (long long)((unsigned)((c + 1) * g.rem) / (unsigned)n) : 0);
+    const long long lo = u * b0;
+    const long long hi = u * b1 < count ? u * b1 : count;
+    const long long fe = b1 - 1 < g.Vfull ? b1 - 1 : g.Vfull;       // frame vectors [b0, fe) were done
+    const long long s0 = head + u * b0, s1 = fe > b0 ? head + u * fe : s0;
+    const long long a1 = s0 < hi ? s0 : hi;                          // piece 1: [lo, a1)
+    const long long a2 = s1 > lo ? s1 : lo;                          // piece 2: [a2, hi)
+    const long long len1 = a1 > lo ? a1 - lo : 0, len2 = hi > a2 ? hi - a2 : 0;
+    for (long long i = threadIdx.x; i < len1 + len2; i += kThreads) {
+        const long long e = i < len1 ? lo + i : a2 + (i - len1);
+        typename Pack<DT>::T acc = chain1<DT, OP>(t, n, c, e, g.s, g.acc32);
+        acc = finish1<DT, OP>(acc, n, g);
+        for (int r = 0; r < n; ++r) store1<DT>(t.dst[r], e, acc);
+    }
+}
+
 // All-reduce in tree order: ranks are visited children-first (tree.post), so
 // every child's partial is final before its parent combines it.
 template <int DT, int OP>
@@ -159,6 +188,14 @@ hipError_t launch_elem_ring_allreduce(int dt, int op, const RankTable &t, const 
     return dispatch(dt, op, [&](auto D, auto O) {
         return launch(elem_ring_allreduce_kernel<decltype(D)::value, decltype(O)::value>, grid, dim3(kThreads), 0, s, t,
                       g, e0, e1);
+    });
+}
+
+hipError_t launch_elem_ring_gaps(int dt, int op, const RankTable &t, const Geometry &g, long long head,
+                                 long long count, hipStream_t s) {
+    return dispatch(dt, op, [&](auto D, auto O) {
+        return launch(elem_ring_gaps_kernel<decltype(D)::value, decltype(O)::value>, dim3(1, (unsigned)g.n),
+                      dim3(kThreads), 0, s, t, g, head, count);
     });
 }
 

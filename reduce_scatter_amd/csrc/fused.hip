@@ -59,7 +59,7 @@ __global__ __launch_bounds__(kFusedThreads) void fused_allreduce_kernel(const Ra
     int c;
     long long j;
     tile_coords(c, j);
-    long long vend = chunk_start(c + 1, g);
+    long long vend = chunk_start(c + 1, g) - g.shift;
     vend = vend < g.Vfull ? vend : g.Vfull;
     const TileSpan ts = aligned_tile(chunk_start(c, g), vend, j, g.ref, kFusedTile);
     if (ts.lo >= ts.hi) return;                               // past the chunk's end: nothing in this tile
@@ -91,7 +91,7 @@ __device__ __forceinline__ void fused_allreduce_wide(const RankTable &t, const G
     int c;
     long long j;
     tile_coords(c, j);
-    long long vend = chunk_start(c + 1, g);
+    long long vend = chunk_start(c + 1, g) - g.shift;
     vend = vend < g.Vfull ? vend : g.Vfull;
     const TileSpan ts = aligned_tile(chunk_start(c, g), vend, j, g.ref, kFusedThreads * U);
     if (ts.lo >= ts.hi) return;

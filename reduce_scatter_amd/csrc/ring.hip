@@ -258,7 +258,7 @@ __global__ __launch_bounds__(RingShape<NR>::T) void ring_allreduce_fast(const Ra
 #pragma unroll
     for (int p = 0; p < NR; ++p) {                 // step p: rank r handles chunk (r-1-p) mod n
         const int c = wrap_c<NR>(r - 1 - p);
-        long long e = ring_chunk_start(c + 1, g);
+        long long e = ring_chunk_start(c + 1, g) - g.shift;
         e = e < g.Vfull ? e : g.Vfull;
         // window blockIdx.x of chunk c, cut on the W-vector grid of rank 0's output addresses
         const TileSpan ts = aligned_tile(ring_chunk_start(c, g), e, blockIdx.x, g.ref, W);

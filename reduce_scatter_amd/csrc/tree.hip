@@ -81,7 +81,7 @@ __device__ __forceinline__ void tree_window(const RankTable &t, const TreeShape 
 
 // Any n: a persistent grid walks the windows.  A single tree takes the
 // windows of [0, Vfull); the double tree (DUAL) takes the windows of
-// [0, g.split) up the first tree and those of [g.split, Vfull) up the second.
+// [0, g.split) up the first tree and those of [g.split2, Vfull) up the second.
 template <int DT, int OP, bool DUAL>
 __global__ __launch_bounds__(kThreads) void tree_allreduce_kernel(const RankTable t, const TreeShape tree0,
                                                                   const TreeShape tree1, const Geometry g) {
@@ -103,7 +103,7 @@ __global__ __launch_bounds__(kThreads) void tree_allreduce_kernel(const RankTabl
     const long long first = DUAL ? (g.split + W - 1) / W : g.windows;     // windows of the first tree
     for (long long win = blockIdx.x; win < g.windows; win += gridDim.x) {
         if (win < first) tree_window<DT, OP>(t, tree0, g, win * W, DUAL ? g.split : g.Vfull, r, w, cnt, slot);
-        else tree_window<DT, OP>(t, tree1, g, g.split + (win - first) * W, g.Vfull, r, w, cnt, slot);
+        else tree_window<DT, OP>(t, tree1, g, g.split2 + (win - first) * W, g.Vfull, r, w, cnt, slot);
     }
 }
 

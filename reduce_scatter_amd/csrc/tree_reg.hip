@@ -12,7 +12,7 @@
 // shape), and stores the root's value to every rank: every byte read once and
 // written once, as in the fused pass, instead of staging partials level by
 // level through LDS.  The double tree takes the first tree over vectors
-// [0, g.split) and the second over [g.split, Vfull): grid y picks the range,
+// [0, g.split) and the second over [g.split2, Vfull): grid y picks the range,
 // so the choice is uniform per workgroup.  Bit-identical to the LDS-staged
 // kernels (and the oracle's trees).
 #include "ar_device.hpp"
@@ -53,7 +53,7 @@ __device__ __forceinline__ u32x4 tree_value(const u32x4 (&raw)[NR], const Geomet
 template <int DT, int OP, int NR, bool DUAL>
 __global__ __launch_bounds__(kFusedThreads) void tree_reg_kernel(const RankTableFor<NR> t, const Geometry g) {
     const bool second = DUAL && blockIdx.y == 1;
-    const long long lo = second ? g.split : 0;
+    const long long lo = second ? g.split2 : 0;
     const long long hi = (DUAL && !second) ? g.split : g.Vfull;
     const TileSpan ts = aligned_tile(lo, hi, (long long)blockIdx.x, g.ref, kFusedTile);
     if (ts.lo >= ts.hi) return;
@@ -76,7 +76,7 @@ __global__ __launch_bounds__(kFusedThreads) void tree_reg_kernel(const RankTable
 hipError_t launch_tree_reg_allreduce(bool dual, int dt, int op, const RankTable &t, const Geometry &g, int lds,
                                      hipStream_t s) {
     if (g.n < 2 || g.n > 16) return hipErrorInvalidValue;
-    const long long len = dual ? (g.split > g.Vfull - g.split ? g.split : g.Vfull - g.split) : g.Vfull;
+    const long long len = dual ? (g.split > g.Vfull - g.split2 ? g.split : g.Vfull - g.split2) : g.Vfull;
     if (len <= 0) return hipSuccess;
     const dim3 grid((unsigned)aligned_tiles(len, kFusedTile), dual ? 2u : 1u);
     return dispatch(dt, op, [&](auto D, auto O) {

@@ -355,6 +355,55 @@ def test_numerics_variants_match_oracle(dtype):
                             sched, dtype, op, n, acc, avg))
 
 
+def _at_phase(x, dtype, k, extra=0):
+    """A device copy of ``x`` starting ``k`` elements past a 16-byte boundary
+    (``extra`` more elements of room after it)."""
+    d = to_device(np.concatenate([np.zeros(k, dtype=x.dtype), x, np.zeros(extra, dtype=x.dtype)]), dtype)
+    assert d.data_ptr() % 16 == 0
+    return d[k:k + x.size]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_allreduce_buffers_at_one_phase(dtype):
+    """Buffers that all sit at the same 16-byte phase (element-aligned, not
+    16-byte aligned): the vectors run from the first 16-byte boundary and the
+    element-wise kernels take each chunk's head, the vector across each chunk
+    boundary and the tail.  Every phase, every schedule, n from 2 to 72
+    (chunks of zero, one and many vectors), in and out of place, against the
+    oracle bit for bit; pointers at two different phases go element-wise."""
+    u = LANES[dtype]
+    for n in (2, 3, 8, 16, 17, 72):
+        for count in sorted({u - 1, 3 * u + 1, n * u, n * u * 2 + 3, 64 * u * 3 + u * n + 5}):
+            for k in range(1, u):
+                op = ("sum", "avg", "prod", "max")[(n + k) % 4]
+                xs = inputs(80 + k, n, count, dtype, op)
+                print("phase", dtype, op, "n=%d count=%d k=%d" % (n, count, k), flush=True)
+                for sched in ("fused", "ring", "tree", "dtree", "split"):
+                    ref = reference(sched, xs, dtype, op)
+                    d_in = [_at_phase(x, dtype, k) for x in xs]
+                    d_out = [_at_phase(np.zeros_like(x), dtype, k) for x in xs]
+                    ar.ar_allreduce(d_in, d_out, count, dtype, op, sched=sched)
+                    sync()
+                    for r in (0, n // 2, n - 1):
+                        assert_bits_equal(to_host(d_out[r], dtype), ref[r], "phase %s %s %s n=%d count=%d k=%d rank %d"
+                                          % (sched, dtype, op, n, count, k, r))
+                    ar.ar_allreduce(d_in, d_in, count, dtype, op, sched=sched)          # in place
+                    sync()
+                    for r in (0, n - 1):
+                        assert_bits_equal(to_host(d_in[r], dtype), ref[r], "phase in place %s %s %s n=%d count=%d k=%d"
+                                          % (sched, dtype, op, n, count, k))
+    # sends and receives at different phases: the element-wise path, same bits
+    n, count = 8, 64 * u * 2 + 7
+    xs = inputs(90, n, count, dtype, "sum")
+    d_in = [_at_phase(x, dtype, 1) for x in xs]
+    d_out = [_at_phase(np.zeros_like(x), dtype, u - 1) for x in xs]
+    ar.ar_allreduce(d_in, d_out, count, dtype, "sum", sched="fused")
+    sync()
+    ref = reference("fused", xs, dtype, "sum")
+    for r in range(n):
+        assert_bits_equal(to_host(d_out[r], dtype), ref[r], "mixed phases rank %d" % r)
+
+
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_slices_off_the_vector_grid(dtype):
     """Slices whose byte length is not a multiple of 16 bytes, with 16-byte
