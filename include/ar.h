@@ -62,12 +62,13 @@
  * the vector paths.  All-reduce buffers that all sit at one 16-byte phase
  * (every address the same mod 16, e.g. views at one offset of per-rank flat
  * buffers) run the vector kernels from the first 16-byte boundary, the few
- * elements around it element-wise; other alignments take an element-wise path.
- * Every path gives identical results.
- * For reduce-scatter and all-gather with R * element size not a multiple of
- * 16, the vector path reads the input slices through aligned 16-byte vectors
- * and may read (never write) the rest of the 16-byte block that holds an
- * input buffer's last byte.
+ * elements around it element-wise; reduce-scatter and all-gather do the same
+ * when all inputs share one phase and all outputs share one (possibly another)
+ * phase, and when R * element size is not a multiple of 16.  Other alignments
+ * take an element-wise path.  Every path gives identical results.  Reading
+ * through aligned 16-byte vectors, the reduce-scatter and all-gather may read
+ * (never write) the rest of the 16-byte blocks that hold an input buffer's
+ * first and last bytes.
  *
  * Aliasing: send buffers may alias one another (they are only read).
  *   all-reduce      in place when recvbufs[r] == sendbufs[r];

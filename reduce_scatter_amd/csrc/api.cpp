@@ -132,6 +132,14 @@ int lds_window(int n) {
     return w < 1 ? 1 : w;
 }
 
+// The 16-byte phase (address mod 16) shared by n pointers, or -1.
+int one_phase(const void *const *p, int n) {
+    const int ph = (int)((uintptr_t)p[0] & 15);
+    for (int r = 1; r < n; ++r)
+        if ((int)((uintptr_t)p[r] & 15) != ph) return -1;
+    return ph;
+}
+
 // The 16-byte phase (address mod 16) shared by all 2n pointers, or -1.
 int common_phase(const void *const *a, const void *const *b, int n) {
     const int ph = (int)((uintptr_t)a[0] & 15);
@@ -501,21 +509,33 @@ ar_status_t ar_reduce_scatter_ex(const void *const *sendbufs, void *const *recvb
     RankTable t;
     fill_table(t, sendbufs, recvbufs, n);
     g.n = n;
-    const bool aligned = all16(sendbufs, (const void *const *)recvbufs, n);
-    const bool vec = aligned && (recvcount * e) % 16 == 0;
-    if (aligned && !vec) {
-        // slices that are not whole 16-byte vectors: the phased fused pass for every whole output vector (any
-        // schedule: the ring computes the same hop order), the element-wise kernel for each output's last bytes
-        g.slice_bytes = (long long)(recvcount * e);
-        g.Rv = g.slice_bytes / 16;
+    const bool vec = all16(sendbufs, (const void *const *)recvbufs, n) && (recvcount * e) % 16 == 0;
+    if (!vec) {
+        // Slices that are not whole 16-byte vectors, or buffers off 16-byte alignment.  With every input at
+        // one 16-byte phase and every output at one phase, the phased pass (any schedule: the ring computes
+        // the same hop order) writes every whole vector of the output frame that starts at the outputs' first
+        // 16-byte boundary, reading the inputs through aligned pairs of vectors; the element-wise kernel
+        // takes each output's first and last few elements.  Mixed phases go element-wise.
+        const long long R = (long long)recvcount, Rb = R * (long long)e;
+        const int ps = one_phase(sendbufs, n), pr = one_phase((const void *const *)recvbufs, n);
+        const long long head = pr > 0 ? (long long)((16 - pr) / (int)e) : 0;
+        if (ps < 0 || pr < 0 || head >= R) return hip_status(launch_elem_reduce_scatter(dtype, op, t, g, R, 0, 0, stream));
+        g.slice_bytes = Rb;
+        g.out_off = head * (long long)e;
+        g.in_off = ps + g.out_off;
+        g.Rv = (Rb - g.out_off) / 16;
+        g.last_off = ((ps + (long long)n * Rb - 1) >> 4) << 4;
         if (aligned_tiles(g.Rv, kFusedTile) > 0x7fffffffLL) return AR_ERR_UNSUPPORTED;   // grid x limit
-        const hipError_t h = launch_fused_reduce_scatter_phased(dtype, op, t, g,
+        RankTable tp = t;
+        for (int r = 0; r < n; ++r) {
+            tp.src[r] = (const char *)sendbufs[r] - ps;
+            tp.dst[r] = (char *)recvbufs[r] + g.out_off;
+        }
+        const hipError_t h = launch_fused_reduce_scatter_phased(dtype, op, tp, g,
                                                                 fused_lds_bytes(AR_COLL_REDUCE_SCATTER, n), stream);
         if (h != hipSuccess) return hip_status(h);
-        return hip_status(launch_elem_reduce_scatter(dtype, op, t, g, (long long)recvcount,
-                                                     g.Rv * (long long)(16 / e), stream));
+        return hip_status(launch_elem_reduce_scatter(dtype, op, t, g, R, head, head + g.Rv * (long long)(16 / e), stream));
     }
-    if (!vec) return hip_status(launch_elem_reduce_scatter(dtype, op, t, g, (long long)recvcount, 0, stream));
     g.Rv = (long long)(recvcount * e / 16);
     g.ref = (long long)((uintptr_t)sendbufs[0] >> 4);          // fused tiles follow the input slices' alignment
     if (use == AR_SCHED_FUSED) {
@@ -555,19 +575,30 @@ ar_status_t ar_all_gather(const void *const *sendbufs, void *const *recvbufs, si
     memset(&g, 0, sizeof g);
     g.n = n;
     g.s = 1.0f;
-    const bool aligned = all16(sendbufs, (const void *const *)recvbufs, n);
-    const bool vec = aligned && (sendcount * e) % 16 == 0;
-    if (aligned && !vec) {
-        // pieces that are not whole 16-byte vectors: the phased pass writes every output vector that lies wholly
-        // inside one piece, the element-wise kernel the few elements at each piece's ends
-        g.slice_bytes = (long long)(sendcount * e);
-        g.ref = (long long)((uintptr_t)recvbufs[0] >> 4);      // tiles follow the outputs' alignment
-        if (aligned_tiles(g.slice_bytes / 16, kFusedTile) > 0x7fffffffLL) return AR_ERR_UNSUPPORTED;
-        const hipError_t h = launch_fused_all_gather_phased(t, g, fused_lds_bytes(AR_COLL_ALL_GATHER, n), stream);
+    const bool vec = all16(sendbufs, (const void *const *)recvbufs, n) && (sendcount * e) % 16 == 0;
+    if (!vec) {
+        // Pieces that are not whole 16-byte vectors, or buffers off 16-byte alignment.  With every input at
+        // one 16-byte phase and every output at one phase, the phased pass writes every vector of the output
+        // frame (from the outputs' first 16-byte boundary) that lies wholly inside one piece, the
+        // element-wise kernel the few elements at each piece's ends.  Mixed phases go element-wise.
+        const long long R = (long long)sendcount, Rb = R * (long long)e;
+        const int ps = one_phase(sendbufs, n), pr = one_phase((const void *const *)recvbufs, n);
+        if (ps < 0 || pr < 0) return hip_status(launch_elem_all_gather((int)e, t, g, R, stream));
+        g.slice_bytes = Rb;
+        g.out_off = pr > 0 ? 16 - pr : 0;
+        g.in_off = ps;
+        g.last_off = ((ps + Rb - 1) >> 4) << 4;
+        RankTable tp = t;
+        for (int r = 0; r < n; ++r) {
+            tp.src[r] = (const char *)sendbufs[r] - ps;
+            tp.dst[r] = (char *)recvbufs[r] + g.out_off;
+        }
+        g.ref = (long long)((uintptr_t)tp.dst[0] >> 4);       // tiles follow the outputs' alignment
+        if (aligned_tiles(Rb / 16, kFusedTile) > 0x7fffffffLL) return AR_ERR_UNSUPPORTED;
+        const hipError_t h = launch_fused_all_gather_phased(tp, g, fused_lds_bytes(AR_COLL_ALL_GATHER, n), stream);
         if (h != hipSuccess) return hip_status(h);
-        return hip_status(launch_elem_all_gather_edges((int)e, t, g, (long long)sendcount, stream));
+        return hip_status(launch_elem_all_gather_edges((int)e, t, g, R, stream));
     }
-    if (!vec) return hip_status(launch_elem_all_gather((int)e, t, g, (long long)sendcount, stream));
     g.Rv = (long long)(sendcount * e / 16);
     g.ref = (long long)((uintptr_t)recvbufs[0] >> 4);          // fused tiles follow the outputs' alignment
     if (use == AR_SCHED_FUSED) {

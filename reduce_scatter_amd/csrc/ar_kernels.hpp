@@ -59,7 +59,10 @@ struct Geometry {
                         // vector across each chunk boundary going to the element-wise kernel; else 0
     float post_div;     // split float avg: the finished sum is divided by n / p (0: no post-division)
     int acc32;          // bf16 / fp16 partials kept in fp32, rounded once (the fused schedule)
-    long long slice_bytes;  // phased reduce-scatter / all-gather: bytes per slice or piece (not a multiple of 16)
+    long long slice_bytes;  // phased reduce-scatter / all-gather: bytes per slice or piece
+    long long in_off;       // phased: byte offset of the first input byte past the (16-byte aligned) table pointer
+    long long out_off;      // phased: byte offset of output vector 0 past the caller's output pointer
+    long long last_off;     // phased: offset (from the table pointer) of the last 16-byte block holding input
 };
 
 // Tiles are cut on a grid aligned to absolute T-vector boundaries of a
@@ -116,12 +119,14 @@ hipError_t launch_fused_allreduce(int dt, int op, const RankTable &t, const Geom
 // ranks).
 hipError_t launch_fused_reduce_scatter(int dt, int op, const RankTable &t, const Geometry &g, int lds, hipStream_t s);
 hipError_t launch_fused_all_gather(const RankTable &t, const Geometry &g, int lds, hipStream_t s);
-// Phased forms for slices of g.slice_bytes bytes, not a multiple of 16 (every
-// pointer 16-byte aligned): the full 16-byte vectors of every output
+// Phased forms: slices of g.slice_bytes bytes in inputs at one 16-byte phase
+// (table pointers aligned down to 16 bytes, the data g.in_off bytes in) into
+// outputs at one phase (table pointers advanced g.out_off bytes to a 16-byte
+// boundary).  They write every whole 16-byte vector of that output frame
 // (reduce-scatter: g.Rv per output; all-gather: those wholly inside each piece,
-// tiles on the grid of g.ref), the inputs read through aligned pairs of
-// vectors.  The partial vectors at the slice edges go through
-// launch_elem_reduce_scatter (from element i0) and launch_elem_all_gather_edges.
+// tiles on the grid of g.ref), reading the inputs through aligned pairs of
+// vectors; the elements outside go through launch_elem_reduce_scatter and
+// launch_elem_all_gather_edges.
 hipError_t launch_fused_reduce_scatter_phased(int dt, int op, const RankTable &t, const Geometry &g, int lds,
                                               hipStream_t s);
 hipError_t launch_fused_all_gather_phased(const RankTable &t, const Geometry &g, int lds, hipStream_t s);
@@ -160,8 +165,9 @@ hipError_t launch_elem_tree_allreduce(int dt, int op, const RankTable &t, const 
                                       long long e_begin, long long e_end, hipStream_t s);
 hipError_t launch_elem_split_allreduce(int dt, int op, const RankTable &t, const Geometry &g, long long e_begin,
                                        long long e_end, hipStream_t s);
+// Elements [0, a) and [b, R) of every reduce-scatter slice (a = b = 0: all).
 hipError_t launch_elem_reduce_scatter(int dt, int op, const RankTable &t, const Geometry &g, long long R,
-                                      long long i0, hipStream_t s);
+                                      long long a, long long b, hipStream_t s);
 hipError_t launch_elem_all_gather(int elem_bytes, const RankTable &t, const Geometry &g, long long R, hipStream_t s);
 // The elements of every all-gather piece outside the 16-byte output vectors
 // the phased kernel writes (at most 15 bytes at each end of a piece).

@@ -124,14 +124,16 @@ __global__ __launch_bounds__(kThreads) void elem_tree_allreduce_kernel(const Ran
 }
 
 // Reduce-scatter: output element i of rank c (grid y) = chunk c's chain over
-// inputs c*R + i of ranks c+1, ..., c; elements [i0, R) of every slice.
+// inputs c*R + i of ranks c+1, ..., c; elements [0, a) and [b, R) of every
+// slice (the vector kernels did [a, b)).
 template <int DT, int OP>
 __global__ __launch_bounds__(kThreads) void elem_reduce_scatter_kernel(const RankTable t, const Geometry g,
-                                                                      long long R, long long i0) {
+                                                                      long long R, long long a, long long b) {
     const int n = g.n;
     const int c = (int)blockIdx.y;
-    for (long long i = i0 + blockIdx.x * (long long)kThreads + threadIdx.x; i < R;
-         i += (long long)gridDim.x * kThreads) {
+    const long long len = a + (R - b);
+    for (long long j = blockIdx.x * (long long)kThreads + threadIdx.x; j < len; j += (long long)gridDim.x * kThreads) {
+        const long long i = j < a ? j : b + (j - a);
         const typename Pack<DT>::T acc = chain1<DT, OP>(t, n, c, (long long)c * R + i, g.s, g.acc32);
         store1<DT>(t.dst[c], i, finish1<DT, OP>(acc, n, g));
     }
@@ -148,17 +150,18 @@ __global__ __launch_bounds__(kThreads) void elem_all_gather_kernel(const RankTab
     }
 }
 
-// The elements of all-gather piece k (grid y) outside the output's 16-byte
-// vectors that lie wholly inside the piece: [0, head) and [tail, R) of the
-// piece, where the piece covers output bytes [k*Rb, (k+1)*Rb), Rb = R * e.
+// The elements of all-gather piece k (grid y) outside the output frame's
+// 16-byte vectors that lie wholly inside the piece: [0, head) and [tail, R) of
+// the piece, where the piece covers frame bytes [b0, b0 + Rb), b0 = k*Rb -
+// g.out_off, Rb = R * e.
 template <typename E>
 __global__ __launch_bounds__(kFusedThreads) void elem_all_gather_edges_kernel(const RankTable t, const Geometry g,
                                                                              long long R) {
     const int n = g.n;
     const int k = (int)blockIdx.y;
     const long long e = (long long)sizeof(E);
-    const long long b0 = (long long)k * R * e, b1 = b0 + R * e;     // the piece's output bytes
-    const long long o0 = (b0 + 15) / 16, o1 = b1 / 16;               // its whole 16-byte vectors [o0, o1)
+    const long long b0 = (long long)k * R * e - g.out_off, b1 = b0 + R * e;   // the piece's frame bytes
+    const long long o0 = (b0 + 15) >> 4, o1 = b1 >> 4;               // its whole 16-byte vectors [o0, o1)
     long long head = R, tail = R;
     if (o1 > o0) {
         head = (o0 * 16 - b0) / e;
@@ -208,11 +211,11 @@ hipError_t launch_elem_tree_allreduce(int dt, int op, const RankTable &t, const 
 }
 
 hipError_t launch_elem_reduce_scatter(int dt, int op, const RankTable &t, const Geometry &g, long long R,
-                                      long long i0, hipStream_t s) {
-    if (R <= i0) return hipSuccess;
+                                      long long a, long long b, hipStream_t s) {
+    if (a + (R - b) <= 0) return hipSuccess;
     return dispatch(dt, op, [&](auto D, auto O) {
-        return launch(elem_reduce_scatter_kernel<decltype(D)::value, decltype(O)::value>, elem_grid2(R - i0, g.n),
-                      dim3(kThreads), 0, s, t, g, R, i0);
+        return launch(elem_reduce_scatter_kernel<decltype(D)::value, decltype(O)::value>, elem_grid2(a + (R - b), g.n),
+                      dim3(kThreads), 0, s, t, g, R, a, b);
     });
 }
 

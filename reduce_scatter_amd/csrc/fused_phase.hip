@@ -26,11 +26,14 @@ namespace ar {
 // Combine the n ranks' 16 bytes at byte ``base + lane_off + ph`` (``base`` a
 // multiple of 16, the same for the whole workgroup, and so is the phase
 // ``ph``) in the hop order of chunk c.  Each lane loads the two aligned
-// vectors that hold its bytes, every load of the chain issued before the first
-// combine; the second vector of a lane is its neighbour's first (a cache hit).
+// vectors that hold its bytes (the second at ``base + hi_off``, hi_off =
+// lane_off + 16 clamped to the input's last 16-byte block: past it the second
+// vector is only reached with ph = 0, where it is not used), every load of the
+// chain issued before the first combine; the second vector of a lane is its
+// neighbour's first (a cache hit).
 template <int DT, int OP, int NR, bool KEEP32, class TAB>
 __device__ __forceinline__ Pack<DT> chain_phased(const TAB &t, int n, int c, long long base, unsigned lane_off,
-                                                 unsigned ph, float s) {
+                                                 unsigned hi_off, unsigned ph, float s) {
     Pack<DT> acc;
     if constexpr (NR > 0) {
         u32x4 lo[NR], hi[NR];
@@ -38,7 +41,7 @@ __device__ __forceinline__ Pack<DT> chain_phased(const TAB &t, int n, int c, lon
         for (int k = 0; k < NR; ++k) {
             const char *p = (const char *)t.src[hop_rank(c, k, NR)] + base + lane_off;
             lo[k] = __builtin_nontemporal_load((const u32x4 *)p);
-            hi[k] = *(const u32x4 *)(p + 16);
+            hi[k] = *(const u32x4 *)(p - lane_off + hi_off);
         }
         __builtin_amdgcn_sched_barrier(0);
         acc = first<DT, OP, KEEP32>(unpack<DT>(funnel16(lo[0], hi[0], ph)), s);
@@ -53,7 +56,7 @@ __device__ __forceinline__ Pack<DT> chain_phased(const TAB &t, int n, int c, lon
                 const int k = k0 + kk < n ? k0 + kk : n - 1;                 // past n: a valid, ignored load
                 const char *p = (const char *)t.src[hop_rank(c, k, n)] + base + lane_off;
                 lo[kk] = __builtin_nontemporal_load((const u32x4 *)p);
-                hi[kk] = *(const u32x4 *)(p + 16);
+                hi[kk] = *(const u32x4 *)(p - lane_off + hi_off);
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -69,14 +72,14 @@ __device__ __forceinline__ Pack<DT> chain_phased(const TAB &t, int n, int c, lon
 }
 
 // Reduce-scatter: grid x = tiles of output vectors, y = slice c.  Output
-// vector o of rank c is chunk c's chain over input bytes c*Rb + 16*o of ranks
-// c+1, ..., c (Rb = g.slice_bytes bytes per slice, g.Rv whole output vectors).
-// Tiles follow output c's alignment: its writes are the ones a cache line
-// split between two workgroups would cost; the reads sit at the slice's phase
-// whatever the tiling.  Neither load of a lane passes the input's end: with Rb
-// not a multiple of 16, the byte after a whole output vector's last input byte
-// is still in the buffer, so its vector exists (whole, as buffers start on a
-// 16-byte boundary).
+// vector o of rank c (16 bytes at g.out_off + 16*o of the caller's output) is
+// chunk c's chain over the same element positions of input slice c of ranks
+// c+1, ..., c: bytes g.in_off + c*Rb + 16*o from the aligned table pointers (Rb
+// = g.slice_bytes bytes per slice, g.Rv whole output vectors).  Tiles follow
+// output c's alignment: its writes are the ones a cache line split between two
+// workgroups would cost; the reads sit at the slice's phase whatever the
+// tiling.  Both loads of a lane stay in 16-byte blocks that hold input bytes
+// (the second is clamped to the last one).
 template <int DT, int OP, int NR, bool KEEP32>
 __device__ __forceinline__ void rs_phased(const RankTableFor<NR> &t, const Geometry &g) {
     const int n = NR > 0 ? NR : g.n;
@@ -85,8 +88,10 @@ __device__ __forceinline__ void rs_phased(const RankTableFor<NR> &t, const Geome
     if (ts.lo >= ts.hi) return;
     bool ok;
     const unsigned lane_off = tile_lane(ts, ts.start + threadIdx.x, ok);
-    const long long a = (long long)c * g.slice_bytes + ts.lo * 16;     // the tile's first input byte
-    Pack<DT> acc = chain_phased<DT, OP, NR, KEEP32>(t, n, c, a & ~15LL, lane_off, (unsigned)(a & 15), g.s);
+    const long long a = g.in_off + (long long)c * g.slice_bytes + ts.lo * 16;     // the tile's first input byte
+    const long long rel = g.last_off - (a & ~15LL);                             // last block, from the tile base
+    const unsigned hi_off = (long long)lane_off + 16 < rel ? lane_off + 16u : (unsigned)rel;
+    Pack<DT> acc = chain_phased<DT, OP, NR, KEEP32>(t, n, c, a & ~15LL, lane_off, hi_off, (unsigned)(a & 15), g.s);
     if (!ok) return;
     finish<DT, OP>(acc, n, g);
     __builtin_nontemporal_store(pack<DT>(acc), (u32x4 *)((char *)t.dst[c] + ts.lo * 16 + lane_off));
@@ -105,27 +110,30 @@ __global__ __launch_bounds__(kFusedThreads) void fused_reduce_scatter_phased_ker
 }
 
 // All-gather: grid x = tiles of output vectors, y = piece k.  Piece k covers
-// output bytes [k*Rb, (k+1)*Rb); its whole output vectors are
-// [ceil(k*Rb/16), floor((k+1)*Rb/16)), vector o holding input bytes
-// 16*o - k*Rb.  Tiles follow the outputs' alignment (g.ref); the same bound
-// as above keeps both loads of a lane inside the input piece's vectors.
+// bytes [b0, b0 + Rb) of the output frame (b0 = k*Rb - g.out_off); its whole
+// frame vectors are [ceil(b0/16), floor((b0 + Rb)/16)), vector o holding the
+// piece's input bytes 16*o - b0 (g.in_off more from the aligned table
+// pointer).  Tiles follow the outputs' alignment (g.ref); the second load is
+// clamped as above.
 template <int NR>
 __global__ __launch_bounds__(kFusedThreads) void fused_all_gather_phased_kernel(const RankTableFor<NR> t,
                                                                                 const Geometry g) {
     const int n = NR > 0 ? NR : g.n;
     const int k = (int)blockIdx.y;
-    const long long b0 = (long long)k * g.slice_bytes;
+    const long long b0 = (long long)k * g.slice_bytes - g.out_off;      // piece k's first byte in the output frame
     const TileSpan ts = aligned_tile((b0 + 15) >> 4, (b0 + g.slice_bytes) >> 4, (long long)blockIdx.x, g.ref, kFusedTile);
     if (ts.lo >= ts.hi) return;
     bool ok;
     const unsigned lane_off = tile_lane(ts, ts.start + threadIdx.x, ok);
-    const long long in = ts.lo * 16 - b0;                                 // the tile's first input byte
-    const char *p = (const char *)t.src[k] + (in & ~15LL) + lane_off;
-    const u32x4 lo = *(const u32x4 *)p;                                   // ordinary loads, as the aligned
-    const u32x4 hi = *(const u32x4 *)(p + 16);                            // all-gather reads its input
+    const long long in = g.in_off + ts.lo * 16 - b0;                      // the tile's first input byte
+    const long long rel = g.last_off - (in & ~15LL);
+    const unsigned hi_off = (long long)lane_off + 16 < rel ? lane_off + 16u : (unsigned)rel;
+    const char *p = (const char *)t.src[k] + (in & ~15LL);
+    const u32x4 lo = *(const u32x4 *)(p + lane_off);                      // ordinary loads, as the aligned
+    const u32x4 hi = *(const u32x4 *)(p + hi_off);                        // all-gather reads its input
     const u32x4 w = funnel16(lo, hi, (unsigned)(in & 15));
     if (!ok) return;
-    const long long out = ts.lo * 16 + lane_off;
+    const long long out = ts.lo * 16 + lane_off;                          // in the output frame
     if constexpr (NR > 0) {
 #pragma unroll
         for (int r = 0; r < NR; ++r) __builtin_nontemporal_store(w, (u32x4 *)((char *)t.dst[r] + out));

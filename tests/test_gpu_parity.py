@@ -405,6 +405,50 @@ def test_allreduce_buffers_at_one_phase(dtype):
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
+def test_reduce_scatter_and_all_gather_at_phases(dtype):
+    """Inputs at one 16-byte phase and outputs at another (every pair of
+    element offsets within a vector): the phased pass writes the output frame
+    from the outputs' first 16-byte boundary, the element-wise kernels the
+    rest; slices of whole and partial vectors, n = 2, 3, 8 and 17, against the
+    oracle bit for bit.  Inputs at mixed phases go element-wise."""
+    u = LANES[dtype]
+    pairs = [(ks, kr) for ks in range(u) for kr in range(u)]
+    for n in (2, 3, 8, 17):
+        for R in (1, u - 1, u * 5, 64 * u + 3, 64 * u * 2):
+            for ks, kr in pairs[(n + R) % 3::3]:
+                op = OPS[(ks + kr + n) % len(OPS)]
+                print("rs/ag phases", dtype, op, "n=%d R=%d ks=%d kr=%d" % (n, R, ks, kr), flush=True)
+                xs = inputs(95 + ks, n, n * R, dtype, op)
+                ref = oracle.ring_reduce_scatter(xs, dtype, op)
+                d_in = [_at_phase(x, dtype, ks) for x in xs]
+                d_out = [_at_phase(np.zeros(R, dtype=xs[0].dtype), dtype, kr) for _ in range(n)]
+                ar.ar_reduce_scatter(d_in, d_out, R, dtype, op, sched="fused")
+                sync()
+                for r in range(n):
+                    assert_bits_equal(to_host(d_out[r], dtype), ref[r], "rs %s %s n=%d R=%d ks=%d kr=%d rank %d" % (
+                        dtype, op, n, R, ks, kr, r))
+                pieces = inputs(96 + kr, n, R, dtype, "sum")
+                want = oracle.ring_all_gather(pieces, dtype)
+                g_in = [_at_phase(x, dtype, ks) for x in pieces]
+                g_out = [_at_phase(np.zeros(n * R, dtype=xs[0].dtype), dtype, kr) for _ in range(n)]
+                ar.ar_all_gather(g_in, g_out, R, dtype, sched="fused")
+                sync()
+                for r in (0, n - 1):
+                    assert_bits_equal(to_host(g_out[r], dtype), want[r], "ag %s n=%d R=%d ks=%d kr=%d rank %d" % (
+                        dtype, n, R, ks, kr, r))
+    # inputs at mixed phases: element-wise
+    n, R = 8, 64 * u + 3
+    xs = inputs(97, n, n * R, dtype, "sum")
+    d_in = [_at_phase(x, dtype, r % u) for r, x in enumerate(xs)]
+    d_out = [_at_phase(np.zeros(R, dtype=xs[0].dtype), dtype, 1) for _ in range(n)]
+    ar.ar_reduce_scatter(d_in, d_out, R, dtype, "sum", sched="fused")
+    sync()
+    ref = oracle.ring_reduce_scatter(xs, dtype, "sum")
+    for r in range(n):
+        assert_bits_equal(to_host(d_out[r], dtype), ref[r], "rs mixed phases rank %d" % r)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
 def test_slices_off_the_vector_grid(dtype):
     """Slices whose byte length is not a multiple of 16 bytes, with 16-byte
     aligned buffers (the phased pass for every whole output vector, the
