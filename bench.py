@@ -122,6 +122,19 @@ def copy_probe(args):
                       "gbps": round(2 * src.numel() * 4 / (launch_ms * 1e-3) / 1e9, 1)}), flush=True)
 
 
+def _interleaved_us(fns, rounds=3, iters=5):
+    """Median GPU time (us) of each call in ``fns`` over ``rounds`` rounds that
+    visit every call in turn (``iters`` timed calls each): no schedule is
+    always the one that runs right after another's traffic or after the
+    buffers were written."""
+    import statistics
+    times = {k: [] for k in fns}
+    for _ in range(rounds):
+        for k, fn in fns.items():
+            times[k].append(_median_us(fn, iters=iters, warmup=1))
+    return {k: statistics.median(v) for k, v in times.items()}
+
+
 def kernel_calls(reps=5):
     """Each main kernel family at its workload's size, ``reps`` calls each,
     synchronised per call so a kernel trace or counter run sees whole,
@@ -272,8 +285,8 @@ def sweep():
         ys_t = [torch.empty_like(x) for x in xs_t]
         xs, ys = ar.pointers(xs_t), ar.pointers(ys_t)
         for op in ("sum", "min", "max", "avg"):
-            t = {s: _median_us(lambda: ar.ar_allreduce(xs, ys, count, "i32", op, n=n, sched=s))
-                 for s in ("ring", "tree", "dtree", "fused", "split")}
+            t = _interleaved_us({s: (lambda s=s: ar.ar_allreduce(xs, ys, count, "i32", op, n=n, sched=s))
+                                 for s in ("ring", "tree", "dtree", "fused", "split")})
             plan = ar.ar_plan("allreduce", count, "i32", op, n).chosen
             win = min(t, key=t.get)
             toll = 100.0 * (t[plan] / t[win] - 1.0)

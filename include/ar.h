@@ -152,7 +152,10 @@ typedef struct {
 /* Result of the cost model, indexed by ar_sched_t (entry 0, AUTO, is unused).
  * predicted_us[s] = launch_us[s] + step_us[s] * steps[s] + bytes[s] / bandwidth[s]
  * for every legal schedule s; ``chosen`` is the legal schedule with the
- * smallest prediction (ties go to the lower enum value). */
+ * smallest prediction (ties go to the lower enum value), except that the
+ * fused schedule is chosen whenever its prediction is within 3 % of the
+ * smallest (one-pass schedules moving the same bytes differ by less than the
+ * spread between measurements). */
 typedef struct {
     ar_sched_t chosen;
     unsigned legal_mask;        /* bit s set when schedule s is legal for the call */

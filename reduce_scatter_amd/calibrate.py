@@ -62,7 +62,7 @@ def time_call(fn, iters, warmup=2):
     return float(np.median([a.elapsed_time(b) * 1e3 for a, b in ev]))
 
 
-def measure(ns, sizes, iters):
+def measure(ns, sizes, iters, rounds=3):
     import torch
     import reduce_scatter_amd as ar
     rows = []                                   # (coll, sched, n, per_rank_bytes, us)
@@ -77,15 +77,22 @@ def measure(ns, sizes, iters):
             outs_t = [torch.empty(R, device="cuda") for _ in range(n)]
             # host pointer tables built once: the timings are the library's, not Python's marshalling
             xs, ys, outs = ar.pointers(xs_t), ar.pointers(ys_t), ar.pointers(outs_t)
+            calls = {}
             for sched in ("ring", "tree", "fused", "split", "dtree"):
-                us = time_call(lambda: ar.ar_allreduce(xs, ys, count, "f32", "sum", n=n, sched=sched), iters)
-                rows.append(("allreduce", sched, n, per_rank, us))
+                calls[("allreduce", sched)] = (lambda s=sched: ar.ar_allreduce(xs, ys, count, "f32", "sum", n=n, sched=s))
                 if sched in ("tree", "split", "dtree"):
                     continue
-                us = time_call(lambda: ar.ar_reduce_scatter(xs, outs, R, "f32", "sum", n=n, sched=sched), iters)
-                rows.append(("reduce_scatter", sched, n, per_rank, us))
-                us = time_call(lambda: ar.ar_all_gather(outs, ys, R, "f32", n=n, sched=sched), iters)
-                rows.append(("all_gather", sched, n, per_rank, us))
+                calls[("reduce_scatter", sched)] = (
+                    lambda s=sched: ar.ar_reduce_scatter(xs, outs, R, "f32", "sum", n=n, sched=s))
+                calls[("all_gather", sched)] = (lambda s=sched: ar.ar_all_gather(outs, ys, R, "f32", n=n, sched=s))
+            # rounds that visit every call in turn, so no schedule always runs right after the same other one
+            # (in the Infinity Cache regime the previous call's traffic decides what is cached)
+            times = {k: [] for k in calls}
+            for _ in range(rounds):
+                for k, fn in calls.items():
+                    times[k].append(time_call(fn, iters, warmup=1))
+            for (coll, sched), v in times.items():
+                rows.append((coll, sched, n, per_rank, float(np.median(v))))
             print("calibrate: n=%d %d bytes per rank done" % (n, per_rank), flush=True)
             del xs, ys, outs, xs_t, ys_t, outs_t
             torch.cuda.empty_cache()
@@ -99,8 +106,8 @@ def fit(rows):
     most 1 MB (pure latency: t = launch + step * steps), the sustained
     bandwidth from the calls that move at least 1 GB, then one correction per
     power-of-two footprint so the model meets the measured time wherever the
-    bandwidth term is at least a quarter of it (one pooled correction for all
-    footprints of 1 GB and more).  The footprint (total algorithmic bytes) is
+    bandwidth term is at least a quarter of it (footprints of 1 GB and more
+    smoothed over neighbouring bins).  The footprint (total algorithmic bytes) is
     the size axis because it decides whether the data stays in the 256 MB
     Infinity Cache."""
     out = {}
@@ -145,13 +152,19 @@ def fit(rows):
                 top = max(bins)                           # beyond the largest measured footprint: keep its factor
                 for b in range(top + 1, SIZE_BINS):
                     row[b] = row[top]
-                # footprints of 1 GB and more stream from HBM whatever their size: one factor for all of them,
-                # the geometric mean of every such measurement, so one noisy call does not flip the choice
-                hbm = [x for b, v in bins.items() if b >= HBM_BIN for x in v]
-                if len(hbm) >= 2:
-                    pooled = float(np.exp(np.mean(np.log(hbm))))
-                    for b in range(HBM_BIN, SIZE_BINS):
-                        row[b] = pooled
+                # footprints of 1 GB and more stream from HBM: each keeps its own factor (the split kernel, for
+                # one, slows at the largest footprints while the others do not), smoothed over its neighbouring
+                # measured bins (median of three) so one noisy point does not flip a choice
+                hb = sorted(b for b in bins if b >= HBM_BIN)
+                sm = {}
+                for i, b in enumerate(hb):
+                    near = [row[x] for x in hb[max(0, i - 1):i + 2]]
+                    sm[b] = float(np.median(near))
+                for b, v in sm.items():
+                    row[b] = v
+                if hb:
+                    for b in range(hb[-1] + 1, SIZE_BINS):
+                        row[b] = sm[hb[-1]]
                 corr[rc] = [min(4.0, max(0.05, c)) for c in row]
             out[(coll, sched)] = (launch, step, bw, corr, extra)
     return out
@@ -184,7 +197,7 @@ def main(argv=None):
     torch.cuda.set_device(0)
     ns = (2, 8) if a.quick else (2, 4, 8, 16, 32, 72, 128)
     sizes = [1 << k for k in ((12, 16, 20, 24, 28) if a.quick else (10, 12, 14, 16, 18, 20, 21, 22, 23, 24, 25, 26, 27, 28, 29, 30))]
-    rows = measure(ns, sizes, iters=5 if a.quick else 10)
+    rows = measure(ns, sizes, iters=3 if a.quick else 5)
     model = fit(rows)
     write(a.out, model, torch.cuda.get_device_name(0) + " " + getattr(torch.cuda.get_device_properties(0),
                                                                       "gcnArchName", ""))

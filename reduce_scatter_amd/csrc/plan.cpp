@@ -43,6 +43,9 @@
 
 static_assert(ar::kTopoRanks == ar::kTableRanks, "tree shapes cover the rank table");
 
+// Predicted-time margin within which the fused schedule is kept (see make_plan).
+constexpr double kTieMargin = 0.03;
+
 namespace ar {
 
 namespace {
@@ -261,6 +264,12 @@ ar_status_t make_plan(ar_coll_t coll, size_t count, ar_dtype_t dtype, ar_op_t op
             have = true;
         }
     }
+    // Schedules that move the same bytes in one pass (fused, tree and dtree in registers, split) run within a
+    // few per cent of one another, less than the spread between calibration runs and boxes: the fused
+    // schedule, whose pass needs no cross-wave exchange, keeps the call unless another is predicted faster by
+    // more than kTieMargin.
+    if (have && out->chosen != AR_SCHED_FUSED && out->predicted_us[AR_SCHED_FUSED] <= best * (1.0 + kTieMargin))
+        out->chosen = AR_SCHED_FUSED;
     return AR_OK;
 }
 

@@ -195,6 +195,15 @@ def test_dtree_parent_is_the_complementary_tree():
     assert ar.ar_dtree_parent(8, 2, 1) == -1 and ar.ar_dtree_parent(8, 1, 8) == -1
 
 
+def _expected_choice(pred):
+    """The cost model's choice: the least predicted time (ties to the lower
+    schedule code), except that fused is kept within 3 % of the least."""
+    best = min(pred, key=lambda s: (pred[s], ar.SCHEDS[s]))
+    if "fused" in pred and pred["fused"] <= pred[best] * 1.03:
+        return "fused"
+    return best
+
+
 def test_plan_steps_bytes_and_legality():
     for n in (1, 2, 4, 8, 16, 72, 128):
         count = 1 << 20
@@ -205,7 +214,7 @@ def test_plan_steps_bytes_and_legality():
         assert p.steps["fused"] == 1 and p.steps["split"] == 1
         assert p.steps["dtree"] == p.steps["tree"]
         assert all(b == 2 * n * count * 4 for b in p.bytes.values())
-        assert p.chosen == min(p.predicted_us, key=lambda s: (p.predicted_us[s], ar.SCHEDS[s]))
+        assert p.chosen == _expected_choice(p.predicted_us)
         for coll in ("reduce_scatter", "all_gather"):
             q = ar.ar_plan(coll, count, "bf16", "avg", n)
             assert q.legal == ["ring", "fused"]
@@ -248,7 +257,16 @@ def test_plan_reads_the_calibration_file(tmp_path):
     assert abs(p["predicted_us"]["tree"] - (20 + 1 * 6 + b / 1e3 / 1000)) < 1e-6
     assert abs(p["predicted_us"]["fused"] - (5 + b / 1e3 / (500 * 0.5))) < 1e-6
     assert abs(p["predicted_us"]["split"] - (7 + 2.5 + b / 1e3 / 400)) < 1e-6
-    assert p["chosen"] == min(p["predicted_us"], key=p["predicted_us"].get)
+    assert p["chosen"] == _expected_choice(p["predicted_us"])
+    # the tie margin: fused within 3 % of a faster prediction keeps the call, beyond it does not
+    g = tmp_path / "tie.txt"
+    g.write_text("allreduce ring 1000 0 1000\nallreduce tree 1000 0 1000\nallreduce split 1000 0 1000\n"
+                 "allreduce dtree 0 0 1000\nallreduce fused 2 0 1000\n")
+    near, far = _plan_in_subprocess(str(g), [("allreduce", count, "f32", "sum", 8),
+                                             ("allreduce", count // 64, "f32", "sum", 8)])
+    assert near["chosen"] == "fused" and near["predicted_us"]["dtree"] < near["predicted_us"]["fused"]
+    assert near["predicted_us"]["fused"] <= 1.03 * near["predicted_us"]["dtree"]
+    assert far["chosen"] == "dtree" and far["predicted_us"]["fused"] > 1.03 * far["predicted_us"]["dtree"]
     # a rank class with no row of its own uses the nearest measured one (class 3 for n = 16)
     p16 = _plan_in_subprocess(str(f), [("allreduce", count // 2, "f32", "sum", 16)])[0]
     assert abs(p16["predicted_us"]["fused"] - (5 + b / 1e3 / (500 * 0.5))) < 1e-6

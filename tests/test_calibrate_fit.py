@@ -1,0 +1,47 @@
+"""The cost-model fit (reduce_scatter_amd/calibrate.py) on synthetic
+measurements: it recovers launch, per-step and bandwidth constants, and each
+footprint of 1 GB and more keeps its own correction (a schedule that slows
+only at the largest footprints is priced slower there, not everywhere)."""
+from __future__ import annotations
+
+import math
+
+from reduce_scatter_amd import calibrate as cal
+
+
+def _rows(slow_big_split):
+    rows = []
+    for n in (2, 8, 16):
+        for k in range(10, 31):
+            pr = 1 << k
+            for sched, launch, step, bw in (("ring", 7.0, 0.1, 5000.0), ("fused", 8.0, 0.0, 6000.0),
+                                            ("split", 8.0, 0.0, 6000.0)):
+                b = cal._bytes("allreduce", n, pr)
+                eff = bw
+                if sched == "split" and slow_big_split and b >= (1 << 34):
+                    eff = bw * 0.8                                  # slows past 16 GB of traffic
+                us = launch + step * cal._steps("allreduce", sched, n) + b / 1e3 / eff
+                rows.append(("allreduce", sched, n, pr, us))
+    return rows
+
+
+def test_fit_recovers_the_constants():
+    model = cal.fit(_rows(False))
+    launch, step, bw, corr, extra = model[("allreduce", "ring")]
+    assert abs(launch - 7.0) < 0.05 and abs(step - 0.1) < 0.005
+    assert abs(bw - 5000.0) / 5000.0 < 0.01
+    launch, step, bw, corr, extra = model[("allreduce", "fused")]
+    assert abs(launch - 8.0) < 0.05 and step == 0.0 and abs(bw - 6000.0) / 6000.0 < 0.01
+    for rc, row in corr.items():                                    # no size dependence to correct
+        assert all(abs(c - 1.0) < 0.02 for c in row[20:])
+
+
+def test_large_footprints_keep_their_own_correction():
+    model = cal.fit(_rows(True))
+    _, _, bw_s, corr_s, _ = model[("allreduce", "split")]
+    _, _, bw_f, corr_f, _ = model[("allreduce", "fused")]
+    rc = math.ceil(math.log2(16))
+    pred = lambda bw, corr, b: b / 1e3 / (bw * corr[rc][int(math.log2(b))])
+    small, big = 1 << 31, 1 << 35                                   # 2 GB and 32 GB of traffic at n = 16
+    assert pred(bw_s, corr_s, small) <= 1.02 * pred(bw_f, corr_f, small)   # split as fast as fused at 2 GB
+    assert pred(bw_s, corr_s, big) >= 1.15 * pred(bw_f, corr_f, big)       # and priced slower at 32 GB
