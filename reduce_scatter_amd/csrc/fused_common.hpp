@@ -33,10 +33,16 @@ template <int DT, int OP, int NR, bool KEEP32, int U, class TAB>
 __device__ __forceinline__ void chain_in(const TAB &t, int n, int c, long long base,
                                          const unsigned (&lane_off)[U], float s, Pack<DT> (&acc)[U]) {
     if constexpr (NR > 0) {
+        // the n rank pointers (scalar loads from the kernel arguments at a chunk-dependent index) all issued
+        // before the first vector load: placed with the vector loads, each waited for its own pointer in turn
+        const void *ptr[NR];
+#pragma unroll
+        for (int k = 0; k < NR; ++k) ptr[k] = t.src[hop_rank(c, k, NR)];
+        __builtin_amdgcn_sched_barrier(0);
         u32x4 raw[NR][U];
 #pragma unroll
         for (int k = 0; k < NR; ++k) {
-            const char *p = (const char *)t.src[hop_rank(c, k, NR)] + base;
+            const char *p = (const char *)ptr[k] + base;
 #pragma unroll
             for (int u = 0; u < U; ++u) raw[k][u] = __builtin_nontemporal_load((const u32x4 *)(p + lane_off[u]));
         }
@@ -50,11 +56,14 @@ __device__ __forceinline__ void chain_in(const TAB &t, int n, int c, long long b
     } else {
         constexpr int B = 16 / U > 0 ? 16 / U : 1;
         for (int k0 = 0; k0 < n; k0 += B) {
+            const void *ptr[B];
+#pragma unroll
+            for (int kk = 0; kk < B; ++kk) ptr[kk] = t.src[hop_rank(c, k0 + kk < n ? k0 + kk : n - 1, n)];
+            __builtin_amdgcn_sched_barrier(0);
             u32x4 raw[B][U];
 #pragma unroll
             for (int kk = 0; kk < B; ++kk) {
-                const int k = k0 + kk < n ? k0 + kk : n - 1;                 // past n: a valid, ignored load
-                const char *p = (const char *)t.src[hop_rank(c, k, n)] + base;
+                const char *p = (const char *)ptr[kk] + base;                // past n: a valid, ignored load
 #pragma unroll
                 for (int u = 0; u < U; ++u) raw[kk][u] = __builtin_nontemporal_load((const u32x4 *)(p + lane_off[u]));
             }

@@ -26,22 +26,29 @@ namespace ar {
 // Combine the n ranks' 16 bytes at byte ``base + lane_off + ph`` (``base`` a
 // multiple of 16, the same for the whole workgroup, and so is the phase
 // ``ph``) in the hop order of chunk c.  Each lane loads the two aligned
-// vectors that hold its bytes (the second at ``base + hi_off``, hi_off =
-// lane_off + 16 clamped to the input's last 16-byte block: past it the second
-// vector is only reached with ph = 0, where it is not used), every load of the
-// chain issued before the first combine; the second vector of a lane is its
-// neighbour's first (a cache hit).
-template <int DT, int OP, int NR, bool KEEP32, class TAB>
+// vectors that hold its bytes, every load of the chain issued before the
+// first combine; the second vector of a lane is its neighbour's first (a cache
+// hit).  CLAMP (the tiles at the input's end only, a uniform choice): the
+// second vector at ``base + hi_off``, hi_off = lane_off + 16 clamped to the
+// input's last 16-byte block (past it the second vector is only reached with
+// ph = 0, where it is not used).  Elsewhere it is addressed as the first plus
+// 16: measured on MI355X, the clamp's separate address on every tile cost the
+// n = 8 bf16 reduce-scatter 13 % (5.5 -> 4.8 TB/s).
+template <int DT, int OP, int NR, bool KEEP32, bool CLAMP, class TAB>
 __device__ __forceinline__ Pack<DT> chain_phased(const TAB &t, int n, int c, long long base, unsigned lane_off,
                                                  unsigned hi_off, unsigned ph, float s) {
     Pack<DT> acc;
     if constexpr (NR > 0) {
+        const void *ptr[NR];                 // every rank pointer's scalar load issued before the vector loads
+#pragma unroll
+        for (int k = 0; k < NR; ++k) ptr[k] = t.src[hop_rank(c, k, NR)];
+        __builtin_amdgcn_sched_barrier(0);
         u32x4 lo[NR], hi[NR];
 #pragma unroll
         for (int k = 0; k < NR; ++k) {
-            const char *p = (const char *)t.src[hop_rank(c, k, NR)] + base + lane_off;
+            const char *p = (const char *)ptr[k] + base + lane_off;
             lo[k] = __builtin_nontemporal_load((const u32x4 *)p);
-            hi[k] = *(const u32x4 *)(p - lane_off + hi_off);
+            hi[k] = CLAMP ? *(const u32x4 *)(p - lane_off + hi_off) : *(const u32x4 *)(p + 16);
         }
         __builtin_amdgcn_sched_barrier(0);
         acc = first<DT, OP, KEEP32>(unpack<DT>(funnel16(lo[0], hi[0], ph)), s);
@@ -56,7 +63,7 @@ __device__ __forceinline__ Pack<DT> chain_phased(const TAB &t, int n, int c, lon
                 const int k = k0 + kk < n ? k0 + kk : n - 1;                 // past n: a valid, ignored load
                 const char *p = (const char *)t.src[hop_rank(c, k, n)] + base + lane_off;
                 lo[kk] = __builtin_nontemporal_load((const u32x4 *)p);
-                hi[kk] = *(const u32x4 *)(p - lane_off + hi_off);
+                hi[kk] = CLAMP ? *(const u32x4 *)(p - lane_off + hi_off) : *(const u32x4 *)(p + 16);
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -90,8 +97,13 @@ __device__ __forceinline__ void rs_phased(const RankTableFor<NR> &t, const Geome
     const unsigned lane_off = tile_lane(ts, ts.start + threadIdx.x, ok);
     const long long a = g.in_off + (long long)c * g.slice_bytes + ts.lo * 16;     // the tile's first input byte
     const long long rel = g.last_off - (a & ~15LL);                             // last block, from the tile base
-    const unsigned hi_off = (long long)lane_off + 16 < rel ? lane_off + 16u : (unsigned)rel;
-    Pack<DT> acc = chain_phased<DT, OP, NR, KEEP32>(t, n, c, a & ~15LL, lane_off, hi_off, (unsigned)(a & 15), g.s);
+    Pack<DT> acc;
+    if (rel >= 16 * (kFusedTile + 1)) {      // no lane's second vector can pass the input's last block
+        acc = chain_phased<DT, OP, NR, KEEP32, false>(t, n, c, a & ~15LL, lane_off, 0, (unsigned)(a & 15), g.s);
+    } else {                                 // the input's last tiles: the second load clamped (a uniform branch)
+        const unsigned hi_off = (long long)lane_off + 16 < rel ? lane_off + 16u : (unsigned)rel;
+        acc = chain_phased<DT, OP, NR, KEEP32, true>(t, n, c, a & ~15LL, lane_off, hi_off, (unsigned)(a & 15), g.s);
+    }
     if (!ok) return;
     finish<DT, OP>(acc, n, g);
     __builtin_nontemporal_store(pack<DT>(acc), (u32x4 *)((char *)t.dst[c] + ts.lo * 16 + lane_off));
