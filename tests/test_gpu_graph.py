@@ -94,6 +94,40 @@ def test_reduce_scatter_then_all_gather_captured():
     _replays(g, xs, ys + zs, eager)
 
 
+def test_paths_off_16_byte_alignment_captured():
+    """The shifted-frame all-reduce (views one element past a 16-byte
+    boundary, in place) and the phased reduce-scatter / all-gather (inputs and
+    outputs at their own phases, slices of a ragged length) under capture:
+    vector and element-wise kernels in one graph, every replay bit for bit
+    against the eager calls."""
+    n, count, R = 8, 64 * 4 * 9 + 5, 64 * 8 * 3 + 3
+    flat = [torch.empty(count + 1, device="cuda") for _ in range(n)]
+    views = [f[1:] for f in flat]
+    big = [torch.empty(n * R + 3, dtype=torch.bfloat16, device="cuda") for _ in range(n)]
+    xs = [b[3:] for b in big]
+    ys_t = [torch.empty(R + 1, dtype=torch.bfloat16, device="cuda") for _ in range(n)]
+    ys = [y[1:] for y in ys_t]
+    zs_t = [torch.empty(n * R + 5, dtype=torch.bfloat16, device="cuda") for _ in range(n)]
+    zs = [z[5:] for z in zs_t]
+    V, X, Y, Z = ar.pointers(views), ar.pointers(xs), ar.pointers(ys), ar.pointers(zs)
+
+    def body():
+        ar.ar_allreduce(V, V, count, "f32", "avg", sched="fused")
+        ar.ar_reduce_scatter(X, Y, R, "bf16", "sum")
+        ar.ar_all_gather(Y, Z, R, "bf16")
+    g = _capture(body)
+
+    def eager():
+        v2 = [v.clone() for v in views]
+        y2 = [torch.empty_like(y) for y in ys]
+        z2 = [torch.empty_like(z) for z in zs]
+        ar.ar_allreduce(v2, v2, count, "f32", "avg", sched="fused")
+        ar.ar_reduce_scatter([x.clone() for x in xs], y2, R, "bf16", "sum")
+        ar.ar_all_gather(y2, z2, R, "bf16")
+        return v2 + y2 + z2
+    _replays(g, views + xs, views + ys + zs, eager)
+
+
 def test_bucket_sequence_captured():
     """Several in-place fp32 avg all-reduce calls over buckets of one flat
     buffer per rank (72 ranks), one graph for the whole sequence."""
