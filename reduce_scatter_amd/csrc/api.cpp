@@ -119,9 +119,10 @@ int env_kb(const char *name, int dflt) {
     if (kb < 0) return -1;
     return (int)(kb > 64 ? 64 : kb) * 1024;
 }
-int ring_lds_bytes(ar_coll_t coll) {
+int ring_lds_bytes(ar_coll_t coll, int n) {
     static int v = env_kb("AR_RING_LDS_KB", -1);
     if (v >= 0 && getenv("AR_RING_LDS_KB")) return v;
+    if (coll == AR_COLL_ALLREDUCE) return (n >= 0 && n <= 16 ? kRingLdsAllReduceByN[n] : 0) * 1024;
     return (coll == AR_COLL_ALL_GATHER ? kRingLdsAllGatherKB : kRingLdsKB) * 1024;
 }
 
@@ -401,7 +402,7 @@ ar_status_t ar_allreduce_ex(const void *const *sendbufs, void *const *recvbufs, 
             g.W = lds_window(n);
             const long long maxlen = (g.V + n - 1) / n;
             g.windows = (maxlen + g.W - 1) / g.W;
-            h = launch_ring_allreduce(dtype, op, tv, g, grid_for(g.windows, cus, 4), ring_lds_bytes(AR_COLL_ALLREDUCE), stream);
+            h = launch_ring_allreduce(dtype, op, tv, g, grid_for(g.windows, cus, 4), ring_lds_bytes(AR_COLL_ALLREDUCE, n), stream);
         } else if (n >= 2 && n <= 16 && !tree_staged()) {               // tree / dtree, in registers
             if (aligned_tiles(g.Vfull, kFusedTile) > 0x7fffffffLL) return AR_ERR_UNSUPPORTED;   // grid x limit
             h = launch_tree_reg_allreduce(use == AR_SCHED_DTREE, dtype, op, tv, g,
@@ -545,7 +546,7 @@ ar_status_t ar_reduce_scatter_ex(const void *const *sendbufs, void *const *recvb
     }
     g.W = lds_window(n);
     g.windows = (g.Rv + g.W - 1) / g.W;
-    return hip_status(launch_ring_reduce_scatter(dtype, op, t, g, grid_for(g.windows, cus, 4), ring_lds_bytes(AR_COLL_REDUCE_SCATTER), stream));
+    return hip_status(launch_ring_reduce_scatter(dtype, op, t, g, grid_for(g.windows, cus, 4), ring_lds_bytes(AR_COLL_REDUCE_SCATTER, n), stream));
 }
 
 ar_status_t ar_all_gather(const void *const *sendbufs, void *const *recvbufs, size_t sendcount, ar_dtype_t dtype,
@@ -608,7 +609,7 @@ ar_status_t ar_all_gather(const void *const *sendbufs, void *const *recvbufs, si
     }
     g.W = lds_window(n);
     g.windows = (g.Rv + g.W - 1) / g.W;
-    return hip_status(launch_ring_all_gather(t, g, grid_for(g.windows, cus, 4), ring_lds_bytes(AR_COLL_ALL_GATHER), stream));
+    return hip_status(launch_ring_all_gather(t, g, grid_for(g.windows, cus, 4), ring_lds_bytes(AR_COLL_ALL_GATHER, n), stream));
 }
 
 }  // extern "C"

@@ -203,6 +203,11 @@ constexpr int kFusedLdsAllGatherKB = 64;
 // Default dynamic-LDS reservation of the compile-time-n ring workgroups, in
 // KB (on top of their static LDS).
 constexpr int kRingLdsKB = 0;
+// The all-reduce ring by n: 48 KB (two workgroups of n waves per CU) for
+// n = 4 and 6-8, where fewer resident windows kept DRAM access local
+// (measured on MI355X at 128 MB per rank: n = 4 5.50 -> 5.99 TB/s, n = 8
+// 5.56 -> 5.73); none elsewhere, where every cap measured level or slower.
+constexpr int kRingLdsAllReduceByN[17] = {0, 0, 0, 0, 48, 0, 48, 48, 48, 0, 0, 0, 0, 0, 0, 0, 0};
 constexpr int kRingLdsAllGatherKB = 0;
 // Ring/tree kernels: at most this many (rank, vector) items per thread.
 constexpr int kItemsPerThread = 4;

@@ -352,7 +352,7 @@ __global__ __launch_bounds__(RingShape<NR>::T) void ring_all_gather_fast(const R
     bool mine_ok;
     const long long mine = at(r, mine_ok);
     if (mine_ok) {
-        const u32x4 x = ld_stream(t.src[r], mine);
+        const u32x4 x = ((const u32x4 *)t.src[r])[mine];   // an ordinary load, as the fused all-gather's input
         slot[r * W + w] = x;
         st_stream(t.dst[r], (long long)r * g.Rv + mine, x);                // keep my own piece
     }
