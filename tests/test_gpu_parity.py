@@ -589,3 +589,71 @@ def test_trees_every_rank_count_up_to_17(dtype, sched):
             want = reference(sched, xs, dtype, op)
             for r in (0, n // 2, n - 1):
                 assert_bits_equal(got[r], want[r], "%s n=%d %s %s rank %d" % (sched, n, dtype, op, r))
+
+
+def test_randomized_calls_match_oracle():
+    """400 seeded random calls: collective, n (1-20 and 72), dtype, op,
+    schedule, numerics options, element counts (log-uniform, ragged), in place
+    or not, and each side's 16-byte phase (shared or mixed across ranks) --
+    every combination of the library's paths (vector, shifted frame, phased,
+    element-wise), each against the oracle bit for bit."""
+    rng = np.random.default_rng(2024)
+    for case in range(400):
+        coll = rng.choice(["allreduce", "reduce_scatter", "all_gather"])
+        n = int(rng.choice(list(range(1, 21)) + [72]))
+        dtype = str(rng.choice(DTYPES))
+        u = LANES[dtype]
+        op = str(rng.choice(OPS)) if coll != "all_gather" else "sum"
+        count = int(np.exp(rng.uniform(0, np.log(4096 if n > 20 else 40000))))
+        mixed = rng.random() < 0.15
+        ks = [int(rng.integers(u)) if mixed else 0 for _ in range(n)]
+        k_in = int(rng.integers(u))
+        k_out = int(rng.integers(u))
+        if coll == "allreduce":
+            scheds = ["fused", "ring", "tree", "dtree", "split", "auto"]
+        else:
+            scheds = ["fused", "ring", "auto"]
+        sched = str(rng.choice(scheds))
+        acc, avg = "storage", "prescale"
+        if coll != "all_gather" and rng.random() < 0.2:
+            acc, avg = NUMERICS[int(rng.integers(len(NUMERICS)))]
+            if acc == "fp32" and dtype in ("bf16", "f16") and sched not in ("fused", "auto"):
+                sched = "fused"
+        inplace = coll == "allreduce" and not mixed and rng.random() < 0.3
+        label = "case %d: %s n=%d %s %s count=%d sched=%s %s/%s in=%d out=%d mixed=%s inplace=%s" % (
+            case, coll, n, dtype, op, count, sched, acc, avg, k_in, k_out, mixed, inplace)
+        print(label, flush=True)
+        if coll == "allreduce":
+            xs = inputs(1000 + case, n, count, dtype, op)
+            d_in = [_at_phase(x, dtype, (k_in + ks[r]) % u) for r, x in enumerate(xs)]
+            d_out = d_in if inplace else [_at_phase(np.zeros_like(x), dtype, (k_out + ks[r]) % u)
+                                          for r, x in enumerate(xs)]
+            ar.ar_allreduce_ex(d_in, d_out, count, dtype, op, sched=sched, acc=acc, avg=avg)
+            sync()
+            used = sched
+            if sched == "auto":
+                used = "fused" if (acc == "fp32" and dtype in ("bf16", "f16")) else \
+                    ar.ar_plan("allreduce", count, dtype, op, n).chosen
+            ref = _numerics_reference(used, xs, dtype, op, acc, avg)
+            for r in range(n):
+                assert_bits_equal(to_host(d_out[r], dtype), ref[r], label + " rank %d" % r)
+        elif coll == "reduce_scatter":
+            R = max(1, count // max(n, 1))
+            xs = inputs(1000 + case, n, n * R, dtype, op)
+            d_in = [_at_phase(x, dtype, (k_in + ks[r]) % u) for r, x in enumerate(xs)]
+            d_out = [_at_phase(np.zeros(R, dtype=xs[0].dtype), dtype, (k_out + ks[r]) % u) for r in range(n)]
+            ar.ar_reduce_scatter_ex(d_in, d_out, R, dtype, op, sched=sched, acc=acc, avg=avg)
+            sync()
+            ref = _numerics_reference("ring", xs, dtype, op, acc, avg, coll="reduce_scatter")
+            for r in range(n):
+                assert_bits_equal(to_host(d_out[r], dtype), ref[r], label + " rank %d" % r)
+        else:
+            R = max(1, count // max(n, 1))
+            pieces = inputs(1000 + case, n, R, dtype, "sum")
+            d_in = [_at_phase(x, dtype, (k_in + ks[r]) % u) for r, x in enumerate(pieces)]
+            d_out = [_at_phase(np.zeros(n * R, dtype=pieces[0].dtype), dtype, (k_out + ks[r]) % u) for r in range(n)]
+            ar.ar_all_gather(d_in, d_out, R, dtype, sched=sched)
+            sync()
+            want = oracle.ring_all_gather(pieces, dtype)
+            for r in range(n):
+                assert_bits_equal(to_host(d_out[r], dtype), want[r], label + " rank %d" % r)
