@@ -196,15 +196,20 @@ int split_ranks_per_wave(int n) {
     }
     int k = 1;
     while ((n + k - 1) / k > kSplitMaxWaves) k *= 2;
+    // from 17 to 64 ranks fewer, fuller waves: 4 ranks per wave, one vector per lane, a 32 KB residency
+    // cap (measured on MI355X at 25 MB per rank in place, n = 17, 24, 32, 48: +1-12 % over 2 ranks per wave
+    // uncapped, in three pairs of runs); past 64 the same change measured level or slower
+    const int pref = (n > 16 && n <= 64) ? 4 : 1;
+    k = k < pref ? pref : k;
     return k < env ? env : k;
 }
 
 // Vectors per lane and rank (AR_SPLIT_U overrides: 1, 2 or 4).  Measured on
-// MI355X: 2 (2 KB runs per rank, twice the bytes in flight) is best up to 64
-// ranks (n = 8, 256 MB per rank: 6.15 TB/s against 5.62 with 1); past 64
-// ranks, where a wave already holds 8 ranks' loads, 1 is best (n = 72, 25 MB
+// MI355X: 2 (2 KB runs per rank, twice the bytes in flight) is best up to 16
+// ranks (n = 8, 256 MB per rank: 6.15 TB/s against 5.62 with 1); past 16
+// ranks, where a wave holds 4 or more ranks' loads, 1 is best (n = 72, 25 MB
 // per rank: 5.51 TB/s against 5.20 with 2).
-int split_vectors_per_lane(int K) {
+int split_vectors_per_lane(int K, int n) {
     static int env = -1;
     if (env < 0) {
         const char *e = getenv("AR_SPLIT_U");
@@ -212,19 +217,21 @@ int split_vectors_per_lane(int K) {
         env = (v == 1 || v == 2 || v == 4) ? v : 0;
     }
     if (env) return (K >= 8 && env == 4) ? 2 : (K == 16 ? 1 : env);
-    return K >= 8 ? 1 : 2;
+    return (K >= 8 || n > 16) ? 1 : 2;      // past 16 ranks K is 4 or more
 }
 
 // Dynamic LDS a split workgroup reserves beyond its static partials (a
-// residency cap; AR_SPLIT_LDS_KB overrides the default of none).
-int split_lds_bytes() {
-    static int v = -1;
-    if (v < 0) {
+// residency cap: 32 KB from 17 to 64 ranks, none otherwise; AR_SPLIT_LDS_KB
+// overrides).
+int split_lds_bytes(int n) {
+    static int v = -2;
+    if (v == -2) {
         const char *e = getenv("AR_SPLIT_LDS_KB");
-        const long kb = e ? atol(e) : 0;
-        v = (int)(kb < 0 ? 0 : (kb > 128 ? 128 : kb)) * 1024;
+        const long kb = e ? atol(e) : -1;
+        v = kb < 0 ? -1 : (int)(kb > 128 ? 128 : kb) * 1024;
     }
-    return v;
+    if (v >= 0) return v;
+    return (n > 16 && n <= 64) ? 32 * 1024 : 0;
 }
 
 // The rank table goes in at 16 entries for n <= 16 (256 bytes of kernel
@@ -248,14 +255,14 @@ template <int DT, int OP, int K>
 hipError_t launch_split_u(int U, const RankTable &t, const Geometry &g, dim3 block, hipStream_t s) {
     const long long T = (long long)kFusedThreads * U;
     const dim3 grid((unsigned)((((g.ref & (T - 1)) + g.Vfull) + T - 1) / T));       // tiles of the aligned grid
-    const size_t lds = (size_t)split_lds_bytes();
+    const size_t lds = (size_t)split_lds_bytes(g.n);
     if (g.n <= 16) return launch_split_cap<DT, OP, K, 16>(U, narrow<16>(t), g, grid, block, lds, s);
     return launch_split_cap<DT, OP, K, 0>(U, t, g, grid, block, lds, s);
 }
 
 hipError_t launch_split_allreduce(int dt, int op, const RankTable &t, const Geometry &g, hipStream_t s) {
     const int K = split_ranks_per_wave(g.n);
-    const int U = split_vectors_per_lane(K);
+    const int U = split_vectors_per_lane(K, g.n);
     const dim3 block((unsigned)(((g.n + K - 1) / K) * kFusedThreads));
     return dispatch(dt, op, [&](auto D, auto O) {
         constexpr int DT = decltype(D)::value, OP = decltype(O)::value;
