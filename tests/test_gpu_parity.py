@@ -89,8 +89,9 @@ def test_allreduce_in_place_equals_out_of_place(dtype):
 
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_allreduce_element_wise_path(dtype):
-    """Buffers that are element-aligned but not 16-byte aligned take the
-    element-wise path; results are identical."""
+    """Buffers one element past a 16-byte boundary (all at that one phase:
+    the shifted-frame path) give the same results as the oracle for every
+    schedule."""
     n, count = 5, 3001
     for op in ("sum", "avg", "max"):
         xs = inputs(3, n, count, dtype, op)
