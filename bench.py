@@ -211,7 +211,8 @@ def sweep():
     xs = [torch.from_numpy(x).cuda() for x in wl.c1_inputs()]
     ys = [torch.empty_like(x) for x in xs]
     xs, ys = ar.pointers(xs), ar.pointers(ys)          # host pointer tables built once, outside the timing
-    out += ["## n = 4, fp32, 1024 elements per rank (latency regime)", "", "| schedule | us |", "|---|---|"]
+    out += ["## n = 4, fp32, 1024 elements per rank (latency regime)", "", "| call (all-reduce unless named) | us |",
+            "|---|---|"]
     for sched in ("fused", "ring", "tree", "split", "dtree", "auto"):
         out.append("| %s | %.2f |" % (sched, _median_us(lambda: ar.ar_allreduce(xs, ys, 1024, "f32", "sum", sched=sched))))
     # the same call captured 100 times into one HIP graph (torch's graph API): GPU time per call without the
@@ -229,6 +230,14 @@ def sweep():
     out.append("| fused, %d calls replayed from one HIP graph (per call) | %.2f |" % (
         reps, _median_us(graph.replay, iters=5) / reps))
     del graph
+    # the c1 reduce-scatter of the same inputs (256 elements out per rank) and the all-gather of its outputs
+    outs_t = [torch.empty(256, device="cuda") for _ in range(4)]
+    outs = ar.pointers(outs_t)
+    for sched in ("fused", "ring"):
+        out.append("| reduce-scatter (%s), 256 elements out per rank | %.2f |" % (
+            sched, _median_us(lambda: ar.ar_reduce_scatter(xs, outs, 256, "f32", "sum", sched=sched))))
+        out.append("| all-gather (%s), 256 elements in per rank | %.2f |" % (
+            sched, _median_us(lambda: ar.ar_all_gather(outs, ys, 256, "f32", sched=sched))))
     out.append("")
 
     # FSDP shards: reduce-scatter (avg) of 8 x 128 Mi bf16, all-gather of 8 x 16 Mi bf16
