@@ -107,6 +107,7 @@ def time_calls(fn, steps, warmup, stream):
     torch.cuda.synchronize()
     total_ms = t0.elapsed_time(t1)
     per = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    time_calls.last_min = per[0]
     return total_ms / steps, sum(per) / steps, per[len(per) // 2]
 
 
@@ -400,6 +401,47 @@ def cpu_baseline(min_seconds=10.0):
                       "%d calls in %.1f s (%.2f s per call)" % (calls, dt, per)}
 
 
+def cpu_baseline_one_core(min_seconds=4.0):
+    """The same oracle call at one thread on a bounded sample (the first
+    1/16 of every rank buffer), timed until ``min_seconds`` have run."""
+    import oracle
+    import workloads
+    count = COUNT // 16
+    xs = [workloads.device_normal(1, 0, r, COUNT, 1e-3, "f32", device="cpu").numpy()[:count].copy()
+          for r in range(N_RANKS)]
+    out = [np.empty_like(x) for x in xs]
+    threads = oracle.num_threads()
+    oracle.set_num_threads(1)
+    try:
+        oracle.ring_allreduce(xs, "f32", "sum", out=out)
+        calls, t = 0, time.perf_counter()
+        while True:
+            oracle.ring_allreduce(xs, "f32", "sum", out=out)
+            calls += 1
+            dt = time.perf_counter() - t
+            if dt >= min_seconds:
+                break
+    finally:
+        oracle.set_num_threads(threads)
+    per = dt / calls
+    return {"value": round(count * 4 / per / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": "ring all-reduce (sum), n=8, fp32, the first 4 Mi elements (16 MB) of every rank, "
+                      "%d calls in %.1f s" % (calls, dt)}
+
+
+def copy_ceiling(stream, alg_bytes):
+    """A plain device copy moving the same bytes as one all-reduce (half read,
+    half written): the practical ceiling of the read/write mix."""
+    import torch
+    src = torch.empty(alg_bytes // 8, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1.0)
+    _, ms, _ = time_calls(lambda: dst.copy_(src), 10, 2, stream)
+    del src, dst
+    return {"bytes": alg_bytes, "ms": round(ms, 4), "GBps": round(alg_bytes / (ms * 1e-3) / 1e9, 1),
+            "frac": round(alg_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -445,6 +487,7 @@ def main():
     plan = ar.ar_plan("allreduce", COUNT, "f32", args.op, N_RANKS)
     chosen = plan.chosen if args.sched == "auto" else args.sched
     step_ms, launch_ms, launch_med_ms = time_calls(step, args.steps, args.warmup, stream)
+    launch_min_ms = time_calls.last_min
     algbw = S / (step_ms * 1e-3) / 1e9
     achieved = alg_bytes / (launch_ms * 1e-3) / 1e9
 
@@ -459,6 +502,9 @@ def main():
                                                  "hbm_GBps": round(alg_bytes / (lms * 1e-3) / 1e9, 1)}
         detail["planner"] = {"chosen": plan.chosen, "predicted_us": {k: round(v, 1) for k, v in
                                                                     plan.predicted_us.items()}}
+        cc = copy_ceiling(stream, alg_bytes)
+        cc["fused_over_copy"] = round(cc["ms"] / launch_ms, 4) if chosen == "fused" else None
+        detail["copy_ceiling"] = cc
 
     out = {
         "metric": METRIC,
@@ -485,10 +531,12 @@ def main():
                      "frac": round(achieved / PEAK_HBM_GBPS, 4),
                      "traffic": measured_traffic() if chosen == "fused" else None,
                      "algorithmic_bytes_per_launch": alg_bytes, "avg_launch_ms": round(launch_ms, 4),
-                     "median_launch_ms": round(launch_med_ms, 4)},
+                     "median_launch_ms": round(launch_med_ms, 4), "min_launch_ms": round(launch_min_ms, 4)},
         "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(),
         "detail": detail,
     }
+    if not args.no_cpu_baseline and not args.no_detail:
+        detail["cpu_baseline_one_core"] = cpu_baseline_one_core()
     print(json.dumps(out), flush=True)
     return 0
 

@@ -126,6 +126,8 @@ def _load():
         lib.orc_f16_to_f32.restype = ctypes.c_float
         lib.orc_num_threads.argtypes = []
         lib.orc_num_threads.restype = ctypes.c_int
+        lib.orc_set_num_threads.argtypes = [ctypes.c_int]
+        lib.orc_set_num_threads.restype = None
         _lib = lib
         return lib
 
@@ -153,6 +155,12 @@ def _call(rc):
 def num_threads() -> int:
     """OpenMP threads the oracle's element loops use."""
     return int(_load().orc_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads for the following oracle calls (every element keeps its hop
+    order, so results are identical at any thread count)."""
+    _load().orc_set_num_threads(int(n))
 
 
 def allreduce_chunks(dtype: str, n: int, count: int) -> list[int]:

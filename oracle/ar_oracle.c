@@ -741,3 +741,13 @@ int orc_num_threads(void)
     return 1;
 #endif
 }
+
+/* Threads for the following calls (timing at one core); results do not depend on it. */
+void orc_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
