@@ -30,13 +30,14 @@ bool valid_dtype(int d) { return d >= AR_FLOAT32 && d <= AR_INT32; }
 bool valid_op(int o) { return o >= AR_SUM && o <= AR_AVG; }
 bool valid_sched(int s) { return s >= AR_SCHED_AUTO && s <= AR_SCHED_DTREE; }
 
+// Environment settings are read once, in initialisers of function-local
+// statics (thread-safe: concurrent callers of the C ABI see one value).
 bool debug_enabled() {
-    static int v = -1;
-    if (v < 0) {
+    static const bool v = [] {
         const char *e = getenv("AR_DEBUG");
-        v = (e && *e && strcmp(e, "0") != 0) ? 1 : 0;
-    }
-    return v == 1;
+        return e && *e && strcmp(e, "0") != 0;
+    }();
+    return v;
 }
 
 ar_sched_t forced_schedule() {
@@ -86,12 +87,11 @@ int grid_for(long long units, int cus, int per_cu) {
 // the all-gather reserves 64 KB and the reduce-scatter 48 KB).  AR_FUSED_LDS_KB
 // overrides all of them.
 int fused_lds_bytes(ar_coll_t coll, int n) {
-    static int env = -2;
-    if (env == -2) {
+    static const int env = [] {
         const char *e = getenv("AR_FUSED_LDS_KB");
-        env = (e && *e) ? (int)atol(e) : -1;
-        if (env > 64) env = 64;
-    }
+        const long v = (e && *e) ? atol(e) : -1;
+        return (int)(v > 64 ? 64 : v);
+    }();
     if (env >= 0) return env * 1024;
     switch (coll) {
     case AR_COLL_ALLREDUCE: return (n >= 0 && n <= 16 ? kFusedLdsAllReduceByN[n] : kFusedLdsAllReduceKB) * 1024;
@@ -120,8 +120,8 @@ int env_kb(const char *name, int dflt) {
     return (int)(kb > 64 ? 64 : kb) * 1024;
 }
 int ring_lds_bytes(ar_coll_t coll, int n) {
-    static int v = env_kb("AR_RING_LDS_KB", -1);
-    if (v >= 0 && getenv("AR_RING_LDS_KB")) return v;
+    static const int v = env_kb("AR_RING_LDS_KB", -1);
+    if (v >= 0) return v;
     if (coll == AR_COLL_ALLREDUCE) return (n >= 0 && n <= 16 ? kRingLdsAllReduceByN[n] : 0) * 1024;
     return (coll == AR_COLL_ALL_GATHER ? kRingLdsAllGatherKB : kRingLdsKB) * 1024;
 }

@@ -389,23 +389,21 @@ void route_costs(const ReshardGeo &g, size_t e, ar_reshard_plan_t *out) {
 }
 
 int reshard_lds_bytes() {
-    static int v = -2;
-    if (v == -2) {
+    static const int v = [] {
         const char *e = getenv("AR_RESHARD_LDS_KB");
-        long kb = (e && *e) ? atol(e) : kReshardLdsKB;
-        v = (int)std::min(std::max(kb, 0L), 64L) * 1024;
-    }
+        const long kb = (e && *e) ? atol(e) : kReshardLdsKB;
+        return (int)std::min(std::max(kb, 0L), 64L) * 1024;
+    }();
     return v;
 }
 
 // Vectors per lane of the copy kernel (AR_RESHARD_U overrides: 1, 2, 4, 8).
 int reshard_u() {
-    static int v = -2;
-    if (v == -2) {
+    static const int v = [] {
         const char *e = getenv("AR_RESHARD_U");
         const long x = (e && *e) ? atol(e) : kReshardU;
-        v = (x == 1 || x == 2 || x == 4 || x == 8) ? (int)x : kReshardU;
-    }
+        return (x == 1 || x == 2 || x == 4 || x == 8) ? (int)x : kReshardU;
+    }();
     return v;
 }
 

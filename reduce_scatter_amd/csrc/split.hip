@@ -188,12 +188,11 @@ __global__ __launch_bounds__(kThreads) void elem_split_allreduce_kernel(const Ra
 // Ranks per wave: the smallest power of two with ceil(n / K) <= 16 waves
 // (AR_SPLIT_K raises it: 2, 4, 8 or 16).
 int split_ranks_per_wave(int n) {
-    static int env = -1;
-    if (env < 0) {
+    static const int env = [] {
         const char *e = getenv("AR_SPLIT_K");
         const int v = e ? atoi(e) : 0;
-        env = (v == 2 || v == 4 || v == 8 || v == 16) ? v : 0;
-    }
+        return (v == 2 || v == 4 || v == 8 || v == 16) ? v : 0;
+    }();
     int k = 1;
     while ((n + k - 1) / k > kSplitMaxWaves) k *= 2;
     // from 17 to 64 ranks fewer, fuller waves: 4 ranks per wave, one vector per lane, a 32 KB residency
@@ -210,12 +209,11 @@ int split_ranks_per_wave(int n) {
 // ranks, where a wave holds 4 or more ranks' loads, 1 is best (n = 72, 25 MB
 // per rank: 5.51 TB/s against 5.20 with 2).
 int split_vectors_per_lane(int K, int n) {
-    static int env = -1;
-    if (env < 0) {
+    static const int env = [] {
         const char *e = getenv("AR_SPLIT_U");
         const int v = e ? atoi(e) : 0;
-        env = (v == 1 || v == 2 || v == 4) ? v : 0;
-    }
+        return (v == 1 || v == 2 || v == 4) ? v : 0;
+    }();
     if (env) return (K >= 8 && env == 4) ? 2 : (K == 16 ? 1 : env);
     return (K >= 8 || n > 16) ? 1 : 2;      // past 16 ranks K is 4 or more
 }
@@ -224,12 +222,11 @@ int split_vectors_per_lane(int K, int n) {
 // residency cap: 32 KB from 17 to 64 ranks, none otherwise; AR_SPLIT_LDS_KB
 // overrides).
 int split_lds_bytes(int n) {
-    static int v = -2;
-    if (v == -2) {
+    static const int v = [] {
         const char *e = getenv("AR_SPLIT_LDS_KB");
         const long kb = e ? atol(e) : -1;
-        v = kb < 0 ? -1 : (int)(kb > 128 ? 128 : kb) * 1024;
-    }
+        return kb < 0 ? -1 : (int)(kb > 128 ? 128 : kb) * 1024;
+    }();
     if (v >= 0) return v;
     return (n > 16 && n <= 64) ? 32 * 1024 : 0;
 }
