@@ -13,9 +13,11 @@
 // issuing the next, and n = 16 ran at 3.1 TB/s.)  The all-gather is the mirror image: aligned input pieces,
 // output pieces at phase k*R*e mod 16, each lane assembling the 16 input bytes
 // that land in one whole output vector.  The elements of the partial vectors
-// at the slice edges go through the element-wise kernels.  Every input byte is
-// still fetched from HBM once (the second vector of a pair is the neighbour
-// lane's first, served by the cache).
+// at the slice edges go through the element-wise kernels.  The second vector
+// of a pair is the neighbour lane's first, served by the cache; only the line
+// past a tile's end is fetched twice (by this tile and the next, which runs on
+// another XCD), so the larger the tile, the closer the fetched bytes come to
+// the algorithmic ones.
 #include "ar_device.hpp"
 #include "ar_kernels.hpp"
 #include "dispatch.hpp"
@@ -23,59 +25,66 @@
 
 namespace ar {
 
-// Combine the n ranks' 16 bytes at byte ``base + lane_off + ph`` (``base`` a
-// multiple of 16, the same for the whole workgroup, and so is the phase
-// ``ph``) in the hop order of chunk c.  Each lane loads the two aligned
-// vectors that hold its bytes, every load of the chain issued before the
-// first combine; the second vector of a lane is its neighbour's first (a cache
-// hit).  CLAMP (the tiles at the input's end only, a uniform choice): the
-// second vector at ``base + hi_off``, hi_off = lane_off + 16 clamped to the
-// input's last 16-byte block (past it the second vector is only reached with
-// ph = 0, where it is not used).  Elsewhere it is addressed as the first plus
-// 16: measured on MI355X, the clamp's separate address on every tile cost the
-// n = 8 bf16 reduce-scatter 13 % (5.5 -> 4.8 TB/s).
-template <int DT, int OP, int NR, bool KEEP32, bool CLAMP, class TAB>
-__device__ __forceinline__ Pack<DT> chain_phased(const TAB &t, int n, int c, long long base, unsigned lane_off,
-                                                 unsigned hi_off, unsigned ph, float s) {
-    Pack<DT> acc;
+// Combine the n ranks' 16 bytes at byte ``base + lane_off[u] + ph`` (u < U;
+// ``base`` a multiple of 16, the same for the whole workgroup, and so is the
+// phase ``ph``) in the hop order of chunk c into acc[u].  Each lane loads the
+// two aligned vectors that hold its bytes, every load of the chain issued
+// before the first combine; the second vector of a lane is its neighbour's
+// first (a cache hit, except past the last lane of a run).  CLAMP (the tiles
+// at the input's end only, a uniform choice): the second vector at ``base +
+// hi_off[u]``, hi_off = lane_off + 16 clamped to the input's last 16-byte
+// block (past it the second vector is only reached with ph = 0, where it is
+// not used).  Elsewhere it is addressed as the first plus 16: measured on
+// MI355X, the clamp's separate address on every tile cost the n = 8 bf16
+// reduce-scatter 13 % (5.5 -> 4.8 TB/s).  NR == 0 (any n): U = 1, ranks in
+// batches of 8.
+template <int DT, int OP, int NR, bool KEEP32, bool CLAMP, int U, class TAB>
+__device__ __forceinline__ void chain_phased(const TAB &t, int n, int c, long long base, const unsigned (&lane_off)[U],
+                                             const unsigned (&hi_off)[U], unsigned ph, float s, Pack<DT> (&acc)[U]) {
     if constexpr (NR > 0) {
         const void *ptr[NR];                 // every rank pointer's scalar load issued before the vector loads
 #pragma unroll
         for (int k = 0; k < NR; ++k) ptr[k] = t.src[hop_rank(c, k, NR)];
         __builtin_amdgcn_sched_barrier(0);
-        u32x4 lo[NR], hi[NR];
+        u32x4 lo[NR][U], hi[NR][U];
 #pragma unroll
         for (int k = 0; k < NR; ++k) {
-            const char *p = (const char *)ptr[k] + base + lane_off;
-            lo[k] = __builtin_nontemporal_load((const u32x4 *)p);
-            hi[k] = CLAMP ? *(const u32x4 *)(p - lane_off + hi_off) : *(const u32x4 *)(p + 16);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const char *p = (const char *)ptr[k] + base + lane_off[u];
+                lo[k][u] = __builtin_nontemporal_load((const u32x4 *)p);
+                hi[k][u] = CLAMP ? *(const u32x4 *)(p - lane_off[u] + hi_off[u]) : *(const u32x4 *)(p + 16);
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
-        acc = first<DT, OP, KEEP32>(unpack<DT>(funnel16(lo[0], hi[0], ph)), s);
 #pragma unroll
-        for (int k = 1; k < NR; ++k) hop<DT, OP, KEEP32>(acc, unpack<DT>(funnel16(lo[k], hi[k], ph)), s);
+        for (int u = 0; u < U; ++u) {
+            acc[u] = first<DT, OP, KEEP32>(unpack<DT>(funnel16(lo[0][u], hi[0][u], ph)), s);
+#pragma unroll
+            for (int k = 1; k < NR; ++k) hop<DT, OP, KEEP32>(acc[u], unpack<DT>(funnel16(lo[k][u], hi[k][u], ph)), s);
+        }
     } else {
+        static_assert(U == 1, "the any-n chain takes one vector per lane");
         constexpr int B = 8;
         for (int k0 = 0; k0 < n; k0 += B) {
             u32x4 lo[B], hi[B];
 #pragma unroll
             for (int kk = 0; kk < B; ++kk) {
                 const int k = k0 + kk < n ? k0 + kk : n - 1;                 // past n: a valid, ignored load
-                const char *p = (const char *)t.src[hop_rank(c, k, n)] + base + lane_off;
+                const char *p = (const char *)t.src[hop_rank(c, k, n)] + base + lane_off[0];
                 lo[kk] = __builtin_nontemporal_load((const u32x4 *)p);
-                hi[kk] = CLAMP ? *(const u32x4 *)(p - lane_off + hi_off) : *(const u32x4 *)(p + 16);
+                hi[kk] = CLAMP ? *(const u32x4 *)(p - lane_off[0] + hi_off[0]) : *(const u32x4 *)(p + 16);
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int kk = 0; kk < B; ++kk) {
                 if (k0 + kk >= n) break;
                 const Pack<DT> x = unpack<DT>(funnel16(lo[kk], hi[kk], ph));
-                if (k0 + kk == 0) acc = first<DT, OP, KEEP32>(x, s);
-                else hop<DT, OP, KEEP32>(acc, x, s);
+                if (k0 + kk == 0) acc[0] = first<DT, OP, KEEP32>(x, s);
+                else hop<DT, OP, KEEP32>(acc[0], x, s);
             }
         }
     }
-    return acc;
 }
 
 // Reduce-scatter: grid x = tiles of output vectors, y = slice c.  Output
@@ -86,27 +95,47 @@ __device__ __forceinline__ Pack<DT> chain_phased(const TAB &t, int n, int c, lon
 // output c's alignment: its writes are the ones a cache line split between two
 // workgroups would cost; the reads sit at the slice's phase whatever the
 // tiling.  Both loads of a lane stay in 16-byte blocks that hold input bytes
-// (the second is clamped to the last one).
+// (the second is clamped to the last one).  A tile is 64*U output vectors, U
+// per lane spaced by the wavefront width, so each load instruction covers one
+// 1 KB run and only the last run's second vectors reach past the tile (into a
+// line the next tile, on another XCD's L2, fetches again).  U = 2 up to 8
+// ranks: measured on MI355X with R - 1 elements per slice (256 MB in per
+// rank, n = 8), 5.87 against 5.53 TB/s for bf16 and 5.74 against 5.55 for
+// fp32; level at n = 4 and 16, so 16 ranks and more keep U = 1.
+template <int NR> struct PhasedTile {
+    static constexpr int U = (NR > 0 && NR <= 8) ? 2 : 1;
+};
+
 template <int DT, int OP, int NR, bool KEEP32>
 __device__ __forceinline__ void rs_phased(const RankTableFor<NR> &t, const Geometry &g) {
+    constexpr int U = PhasedTile<NR>::U;
     const int n = NR > 0 ? NR : g.n;
     const int c = (int)blockIdx.y;
-    const TileSpan ts = aligned_tile(0, g.Rv, (long long)blockIdx.x, (long long)((uintptr_t)t.dst[c] >> 4), kFusedTile);
+    const TileSpan ts =
+        aligned_tile(0, g.Rv, (long long)blockIdx.x, (long long)((uintptr_t)t.dst[c] >> 4), kFusedTile * U);
     if (ts.lo >= ts.hi) return;
-    bool ok;
-    const unsigned lane_off = tile_lane(ts, ts.start + threadIdx.x, ok);
+    unsigned off[U];
+    bool ok[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) off[u] = tile_lane(ts, ts.start + threadIdx.x + u * kFusedTile, ok[u]);
     const long long a = g.in_off + (long long)c * g.slice_bytes + ts.lo * 16;     // the tile's first input byte
     const long long rel = g.last_off - (a & ~15LL);                             // last block, from the tile base
-    Pack<DT> acc;
-    if (rel >= 16 * (kFusedTile + 1)) {      // no lane's second vector can pass the input's last block
-        acc = chain_phased<DT, OP, NR, KEEP32, false>(t, n, c, a & ~15LL, lane_off, 0, (unsigned)(a & 15), g.s);
+    Pack<DT> acc[U];
+    if (rel >= 16 * (kFusedTile * U + 1)) {  // no lane's second vector can pass the input's last block
+        chain_phased<DT, OP, NR, KEEP32, false, U>(t, n, c, a & ~15LL, off, off, (unsigned)(a & 15), g.s, acc);
     } else {                                 // the input's last tiles: the second load clamped (a uniform branch)
-        const unsigned hi_off = (long long)lane_off + 16 < rel ? lane_off + 16u : (unsigned)rel;
-        acc = chain_phased<DT, OP, NR, KEEP32, true>(t, n, c, a & ~15LL, lane_off, hi_off, (unsigned)(a & 15), g.s);
+        unsigned hi_off[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) hi_off[u] = (long long)off[u] + 16 < rel ? off[u] + 16u : (unsigned)rel;
+        chain_phased<DT, OP, NR, KEEP32, true, U>(t, n, c, a & ~15LL, off, hi_off, (unsigned)(a & 15), g.s, acc);
     }
-    if (!ok) return;
-    finish<DT, OP>(acc, n, g);
-    __builtin_nontemporal_store(pack<DT>(acc), (u32x4 *)((char *)t.dst[c] + ts.lo * 16 + lane_off));
+    char *p = (char *)t.dst[c] + ts.lo * 16;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        if (!ok[u]) continue;
+        finish<DT, OP>(acc[u], n, g);
+        __builtin_nontemporal_store(pack<DT>(acc[u]), (u32x4 *)(p + off[u]));
+    }
 }
 
 template <int DT, int OP, int NR>
@@ -157,11 +186,12 @@ __global__ __launch_bounds__(kFusedThreads) void fused_all_gather_phased_kernel(
 hipError_t launch_fused_reduce_scatter_phased(int dt, int op, const RankTable &t, const Geometry &g, int lds,
                                               hipStream_t s) {
     if (g.Rv <= 0) return hipSuccess;
-    const dim3 grid((unsigned)aligned_tiles(g.Rv, kFusedTile), (unsigned)g.n);
     return dispatch(dt, op, [&](auto D, auto O) {
         return by_ranks(g.n, [&](auto R) {
-            return launch(fused_reduce_scatter_phased_kernel<decltype(D)::value, decltype(O)::value, decltype(R)::value>,
-                          grid, dim3(kFusedThreads), (size_t)lds, s, narrow<decltype(R)::value>(t), g);
+            constexpr int NR = decltype(R)::value;
+            const dim3 grid((unsigned)aligned_tiles(g.Rv, (long long)kFusedTile * PhasedTile<NR>::U), (unsigned)g.n);
+            return launch(fused_reduce_scatter_phased_kernel<decltype(D)::value, decltype(O)::value, NR>,
+                          grid, dim3(kFusedThreads), (size_t)lds, s, narrow<NR>(t), g);
         });
     });
 }
