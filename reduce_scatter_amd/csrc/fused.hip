@@ -152,20 +152,34 @@ __global__ __launch_bounds__(kFusedThreads) void fused_allreduce_wide_kernel(con
 // MI355X, a non-temporal input load cost this one-load, n-store pattern
 // 6-14 % (n = 8 bf16, 16 Mi elements per piece: 6.4 against 7.2 TB/s), while
 // the reduce-scatter and the all-reduce (n loads per store) ran best with
-// non-temporal loads and stores.
-template <int NR>
+// non-temporal loads and stores.  A tile is 64*U vectors, U per lane spaced by
+// the wavefront width.  Measured on MI355X at 256 MB out per rank: U = 2 ran
+// 6.4-7.3 TB/s at every n from 2 to 12, against 5.3-6.2 for n = 3, 5, 6, 7 and
+// 12 with U = 1 (level at n = 2 and 8, 3 % lower at n = 4); 16 ranks and the
+// one-rank copy ran 5 % faster with U = 1; past 16 ranks (n = 17, 24, 32, 72
+// at 64 and 256 MB out per rank) U = 2 averaged 6.1-6.8 against 5.5-6.4 TB/s.
+int gather_vectors_per_lane(int n) { return (n >= 2 && n != 16) ? 2 : 1; }
+
+template <int NR, int U>
 __global__ __launch_bounds__(kFusedThreads) void fused_all_gather_kernel(const RankTableFor<NR> t, const Geometry g) {
     const int n = NR > 0 ? NR : g.n;
     int k;
     long long j;
     tile_coords(k, j);
     // tiles follow the alignment of the n outputs (piece k of the reference output)
-    const TileSpan ts = aligned_tile(0, g.Rv, j, g.ref + (long long)k * g.Rv, kFusedTile);
-    bool ok;
-    const unsigned lane_off = tile_lane(ts, ts.start + threadIdx.x, ok);
-    if (!ok) return;
-    const u32x4 w = *(const u32x4 *)((const char *)t.src[k] + ts.lo * 16 + lane_off);
-    store_all<NR>(t, n, ((long long)k * g.Rv + ts.lo) * 16, lane_off, w);
+    const TileSpan ts = aligned_tile(0, g.Rv, j, g.ref + (long long)k * g.Rv, kFusedTile * U);
+    if (ts.lo >= ts.hi) return;
+    unsigned off[U];
+    bool ok[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) off[u] = tile_lane(ts, ts.start + threadIdx.x + u * kFusedTile, ok[u]);
+    const char *p = (const char *)t.src[k] + ts.lo * 16;
+    u32x4 w[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) w[u] = *(const u32x4 *)(p + off[u]);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+        if (ok[u]) store_all<NR>(t, n, ((long long)k * g.Rv + ts.lo) * 16, off[u], w[u]);
 }
 
 // Tiles per chunk of the wide (n > 16) all-reduce kernel.
@@ -193,10 +207,13 @@ hipError_t launch_fused_allreduce(int dt, int op, const RankTable &t, const Geom
 }
 
 hipError_t launch_fused_all_gather(const RankTable &t, const Geometry &g, int lds, hipStream_t s) {
-    const dim3 grid((unsigned)g.windows, (unsigned)g.n);
+    if (g.Rv <= 0) return hipSuccess;
+    const int U = gather_vectors_per_lane(g.n);
+    const dim3 grid((unsigned)aligned_tiles(g.Rv, (long long)kFusedTile * U), (unsigned)g.n);
     return by_ranks(g.n, [&](auto R) {
-        return launch(fused_all_gather_kernel<decltype(R)::value>, grid, dim3(kFusedThreads), (size_t)lds, s,
-                      narrow<decltype(R)::value>(t), g);
+        constexpr int NR = decltype(R)::value;
+        if (U == 2) return launch(fused_all_gather_kernel<NR, 2>, grid, dim3(kFusedThreads), (size_t)lds, s, narrow<NR>(t), g);
+        return launch(fused_all_gather_kernel<NR, 1>, grid, dim3(kFusedThreads), (size_t)lds, s, narrow<NR>(t), g);
     });
 }
 
