@@ -551,7 +551,7 @@ print("ok", hips[0])
 def test_every_rank_count_up_to_17(dtype, sched):
     """Every n up to 16 has its own compile-time fused and ring kernels (17
     takes the any-n paths): all-reduce, reduce-scatter and all-gather against
-    the oracle."""
+    the oracle, with slices on and off the 16-byte grid."""
     u = LANES[dtype]
     for n in range(2, 18):
         for op in ("sum", "avg", "max"):
@@ -568,11 +568,24 @@ def test_every_rank_count_up_to_17(dtype, sched):
             want = oracle.ring_reduce_scatter(ys, dtype, op)
             for r in range(n):
                 assert_bits_equal(got[r], want[r], "%s rs n=%d %s %s rank %d" % (sched, n, dtype, op, r))
-        pieces = inputs(42, n, 64 * u + u, dtype, "sum")
+        # pieces of several two-run tiles plus a ragged tail; then slices off the vector grid (the phased
+        # kernels, two 1 KB runs per lane up to 8 ranks) with several tiles per slice
+        pieces = inputs(42, n, 64 * u * 5 + u, dtype, "sum")
         got = run_ag(pieces, dtype, sched)
         want = oracle.ring_all_gather(pieces, dtype)
         for r in (0, n - 1):
             assert_bits_equal(got[r], want[r], "%s ag n=%d %s rank %d" % (sched, n, dtype, r))
+        Rp = 64 * u * 5 + 3
+        ys = inputs(44, n, n * Rp, dtype, "sum")
+        got = run_rs(ys, dtype, "sum", sched)
+        want = oracle.ring_reduce_scatter(ys, dtype, "sum")
+        for r in range(n):
+            assert_bits_equal(got[r], want[r], "%s phased rs n=%d %s rank %d" % (sched, n, dtype, r))
+        pieces = inputs(45, n, Rp, dtype, "sum")
+        got = run_ag(pieces, dtype, sched)
+        want = oracle.ring_all_gather(pieces, dtype)
+        for r in (0, n - 1):
+            assert_bits_equal(got[r], want[r], "%s phased ag n=%d %s rank %d" % (sched, n, dtype, r))
 
 
 @pytest.mark.parametrize("sched", ["tree", "dtree"])
