@@ -1,0 +1,191 @@
+"""Host model of the phased reduce-scatter / all-gather index arithmetic.
+
+Slices whose byte length is not a multiple of 16 go through the phased
+kernels (fused_phase.hip) plus the element-wise edge kernels (elem.hip).  This
+file restates their index arithmetic in numpy -- the tile grid
+(``aligned_tile`` / ``aligned_tiles`` / ``tile_lane``), the two aligned loads
+per lane with the clamp of the second one, the funnel shift's byte window and
+the element ranges the edge kernels take -- and checks, for every rank count,
+element size, input and output phase, slice lengths around tile boundaries
+and one, two or four vectors per lane, that
+
+* every load stays inside the 16-byte blocks that hold the rank's input bytes;
+* the 16 bytes a lane assembles are exactly the input bytes of the element
+  positions of the output vector it writes (so the clamp never changes a
+  second vector that the shift uses);
+* the phased vectors and the element-wise ranges write every output element
+  exactly once, and nothing outside the output.
+
+It models the kernels' arithmetic (no GPU, no oracle); the GPU parity tests
+check the values.
+"""
+import random
+
+import numpy as np
+import pytest
+
+TILE = 64                     # one wavefront's vectors per run
+
+
+def aligned_tile(lo, hi, j, ref, T):
+    a = (ref + lo) & (T - 1)
+    start = lo - a + j * T
+    return start, max(start, lo), min(start + T, hi)
+
+
+def aligned_tiles(length, T):
+    return (length + T - 1) // T + 1 if length > 0 else 0
+
+
+def lanes(start, lo, hi, U):
+    """Byte offsets from the tile's first in-range vector and the in-range flags of all 64*U lanes."""
+    v = start + np.arange(TILE * U, dtype=np.int64)
+    ok = (v >= lo) & (v < hi)
+    c = np.clip(v, lo, hi - 1)
+    return (c - lo) * 16, ok
+
+
+def library_u(n):
+    """Vectors per lane the library's phased kernels take (compile-time rank counts up to 8: two)."""
+    return 2 if 2 <= n <= 8 else 1
+
+
+def emulate_rs(n, e, R, ps, pr, U, refs, slack=0, edge_shift=0):
+    """One phased reduce-scatter call; returns the write count of every output element, per rank.
+    ``slack`` and ``edge_shift`` plant mistakes (a clamp that many bytes short, the edge kernel's upper
+    range moved that many elements) for the test that the model notices them."""
+    Rb = R * e
+    writes = np.zeros((n, R), dtype=np.int64)
+    head = (16 - pr) // e if pr > 0 else 0
+    if head >= R:                                    # all element-wise
+        writes += 1
+        return writes
+    out_off = head * e
+    in_off = ps + out_off
+    Rv = (Rb - out_off) // 16
+    last_off = ((ps + n * Rb - 1) >> 4) << 4
+    for c in range(n):
+        for j in range(aligned_tiles(Rv, TILE * U)):
+            start, lo, hi = aligned_tile(0, Rv, j, refs[c], TILE * U)
+            if lo >= hi:
+                continue
+            off, ok = lanes(start, lo, hi, U)
+            a = in_off + c * Rb + lo * 16
+            base, ph = a & ~15, a & 15
+            rel = last_off - base - slack
+            if rel >= 16 * (TILE * U + 1):
+                hi_off = off + 16
+            else:
+                hi_off = np.where(off + 16 < rel, off + 16, rel)
+            # both loads inside the blocks [0, last_off + 16) that hold the input bytes [ps, ps + n*Rb)
+            for ld in (base + off, base + hi_off):
+                assert ld.min() >= 0 and (ld + 16).max() <= last_off + 16, (n, e, R, ps, pr, U, c, j)
+            # the assembled window [a + off, a + off + 16) is the input of the lane's output vector
+            o = lo + off[ok] // 16
+            want = ps + c * Rb + out_off + 16 * o
+            assert np.array_equal(a + off[ok], want)
+            assert want.min() >= ps and (want + 16).max() <= ps + n * Rb
+            if ph:
+                assert np.array_equal(hi_off[ok], off[ok] + 16), (n, e, R, ps, pr, U, c, j)
+            # the written output bytes [out_off + 16*o, +16), in elements
+            for q in o:
+                first = (out_off + 16 * int(q)) // e
+                assert first + 16 // e <= R
+                writes[c, first:first + 16 // e] += 1
+    a_, b_ = head, head + Rv * (16 // e) + edge_shift   # the edge kernel takes [0, a) and [b, R)
+    writes[:, :a_] += 1
+    writes[:, b_:] += 1
+    return writes
+
+
+def emulate_ag(n, e, R, ps, pr, U, ref):
+    """One phased all-gather call; returns the write count of every output element (the same on every rank)."""
+    Rb = R * e
+    writes = np.zeros(n * R, dtype=np.int64)
+    out_off = 16 - pr if pr > 0 else 0
+    in_off = ps
+    last_off = ((ps + Rb - 1) >> 4) << 4
+    most = Rb >> 4
+    tiles = aligned_tiles(most, TILE * U) if most > 0 else 0
+    for k in range(n):
+        b0 = k * Rb - out_off
+        vlo, vhi = (b0 + 15) >> 4, (b0 + Rb) >> 4
+        covered = 0
+        for j in range(tiles):
+            start, lo, hi = aligned_tile(vlo, vhi, j, ref, TILE * U)
+            if lo >= hi:
+                continue
+            off, ok = lanes(start, lo, hi, U)
+            inb = in_off + lo * 16 - b0
+            base, ph = inb & ~15, inb & 15
+            rel = last_off - base
+            hi_off = np.where(off + 16 < rel, off + 16, rel)
+            for ld in (base + off, base + hi_off):
+                assert ld.min() >= 0 and (ld + 16).max() <= last_off + 16, (n, e, R, ps, pr, U, k, j)
+            o = lo + off[ok] // 16
+            src = inb + off[ok]                       # input bytes of frame vector o: ps + 16*o - b0
+            assert np.array_equal(src, ps + 16 * o - b0)
+            assert src.min() >= ps and (src + 16).max() <= ps + Rb
+            if ph:
+                assert np.array_equal(hi_off[ok], off[ok] + 16), (n, e, R, ps, pr, U, k, j)
+            for q in o:
+                # frame byte 16*q is byte 16*q + out_off of the caller's output, element k*R + (16*q - b0)/e
+                first = (16 * int(q) + out_off) // e
+                assert first == k * R + (16 * int(q) - b0) // e and first + 16 // e <= n * R
+                writes[first:first + 16 // e] += 1
+                covered += 1
+        assert covered == max(0, vhi - vlo), (n, e, R, ps, pr, U, k)   # the grid reaches every whole vector
+        # the edge kernel: elements [0, head) and [tail, R) of the piece
+        o0, o1 = vlo, vhi
+        head, tail = (R, R) if o1 <= o0 else ((o0 * 16 - b0) // e, (o1 * 16 - b0) // e)
+        writes[k * R:k * R + head] += 1
+        writes[k * R + tail:k * R + R] += 1
+    return writes
+
+
+def _cases(rng, e):
+    u = 16 // e
+    lengths = [1, u - 1, u + 1, TILE * u - 1, TILE * u + 1, 2 * TILE * u + 3, 3 * TILE * u + u - 1,
+               4 * TILE * u + 5]
+    lengths += [rng.randrange(1, 6 * TILE * u) for _ in range(4)]
+    return [R for R in lengths if R * e % 16]
+
+
+@pytest.mark.parametrize("e", [2, 4])
+def test_phased_reduce_scatter_index_map(e):
+    rng = random.Random(11 + e)
+    phases = list(range(0, 16, e))
+    for n in (1, 2, 3, 5, 8, 9, 17):
+        for R in _cases(rng, e):
+            for U in sorted({1, 2, 4, library_u(n)}):
+                ps, pr = rng.choice(phases), rng.choice(phases)
+                refs = [rng.randrange(0, 1 << 20) for _ in range(n)]
+                w = emulate_rs(n, e, R, ps, pr, U, refs)
+                assert (w == 1).all(), (n, e, R, ps, pr, U)
+
+
+@pytest.mark.parametrize("e", [2, 4])
+def test_phased_all_gather_index_map(e):
+    rng = random.Random(21 + e)
+    phases = list(range(0, 16, e))
+    for n in (1, 2, 3, 5, 8, 9, 17):
+        for R in _cases(rng, e):
+            for U in sorted({1, 2, 4, library_u(n)}):
+                ps, pr = rng.choice(phases), rng.choice(phases)
+                w = emulate_ag(n, e, R, ps, pr, U, rng.randrange(0, 1 << 20))
+                assert (w == 1).all(), (n, e, R, ps, pr, U)
+
+
+@pytest.mark.parametrize("mistake", [{"slack": 16}, {"edge_shift": 1}, {"edge_shift": -1}])
+def test_model_notices_planted_mistakes(mistake):
+    """A clamp one block short, or an edge range off by one element, fails the checks for some case."""
+    rng = random.Random(5)
+    failed = 0
+    for n in (2, 3, 8):
+        for R in _cases(rng, 4):
+            try:
+                w = emulate_rs(n, 4, R, 4, 0, 2, [0] * n, **mistake)
+                failed += int(not (w == 1).all())
+            except AssertionError:
+                failed += 1
+    assert failed > 0
