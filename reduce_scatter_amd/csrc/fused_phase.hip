@@ -155,14 +155,16 @@ __global__ __launch_bounds__(kFusedThreads) void fused_reduce_scatter_phased_ker
 // frame vectors are [ceil(b0/16), floor((b0 + Rb)/16)), vector o holding the
 // piece's input bytes 16*o - b0 (g.in_off more from the aligned table
 // pointer).  Tiles follow the outputs' alignment (g.ref); the second load is
-// clamped as above.  Tiles of 64*U vectors as in the reduce-scatter: U = 2 up
-// to 8 ranks measured on MI355X with R - 1 elements per piece (n = 8, 256 MB
-// out per rank) at 7.14-7.16 against 6.5-6.7 TB/s (bf16 and fp32), level at
-// n = 4 and 16.
-template <int NR>
+// clamped as above.  Tiles of 64*U vectors as in the reduce-scatter, U = 2
+// for every n from 2 on: measured on MI355X with R - 1 elements per piece at
+// 256 MB out per rank, 7.14-7.16 against 6.5-6.7 TB/s at n = 8 (bf16 and
+// fp32), 5.8-6.3 against 5.0-5.3 at n = 9, 6.0 against 4.7-4.8 at n = 24 and
+// 4.7-5.2 against 4.0-4.3 at n = 17; level at n = 4, 16 and 72, and at 64 MB.
+int phased_gather_vectors_per_lane(int n) { return n >= 2 ? 2 : 1; }
+
+template <int NR, int U>
 __global__ __launch_bounds__(kFusedThreads) void fused_all_gather_phased_kernel(const RankTableFor<NR> t,
                                                                                 const Geometry g) {
-    constexpr int U = PhasedTile<NR>::U;
     const int n = NR > 0 ? NR : g.n;
     const int k = (int)blockIdx.y;
     const long long b0 = (long long)k * g.slice_bytes - g.out_off;      // piece k's first byte in the output frame
@@ -213,10 +215,13 @@ hipError_t launch_fused_reduce_scatter_phased(int dt, int op, const RankTable &t
 hipError_t launch_fused_all_gather_phased(const RankTable &t, const Geometry &g, int lds, hipStream_t s) {
     const long long most = g.slice_bytes >> 4;                    // whole output vectors of any piece, at most
     if (most <= 0) return hipSuccess;
+    const int U = phased_gather_vectors_per_lane(g.n);
+    const dim3 grid((unsigned)aligned_tiles(most, (long long)kFusedTile * U), (unsigned)g.n);
     return by_ranks(g.n, [&](auto R) {
         constexpr int NR = decltype(R)::value;
-        const dim3 grid((unsigned)aligned_tiles(most, (long long)kFusedTile * PhasedTile<NR>::U), (unsigned)g.n);
-        return launch(fused_all_gather_phased_kernel<NR>, grid, dim3(kFusedThreads), (size_t)lds, s, narrow<NR>(t), g);
+        if (U == 2)
+            return launch(fused_all_gather_phased_kernel<NR, 2>, grid, dim3(kFusedThreads), (size_t)lds, s, narrow<NR>(t), g);
+        return launch(fused_all_gather_phased_kernel<NR, 1>, grid, dim3(kFusedThreads), (size_t)lds, s, narrow<NR>(t), g);
     });
 }
 

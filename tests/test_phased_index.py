@@ -45,8 +45,11 @@ def lanes(start, lo, hi, U):
     return (c - lo) * 16, ok
 
 
-def library_u(n):
-    """Vectors per lane the library's phased kernels take (compile-time rank counts up to 8: two)."""
+def library_u(n, coll="rs"):
+    """Vectors per lane the library's phased kernels take: the reduce-scatter two up to 8 ranks, the
+    all-gather two from 2 ranks on."""
+    if coll == "ag":
+        return 2 if n >= 2 else 1
     return 2 if 2 <= n <= 8 else 1
 
 
@@ -170,7 +173,7 @@ def test_phased_all_gather_index_map(e):
     phases = list(range(0, 16, e))
     for n in (1, 2, 3, 5, 8, 9, 17):
         for R in _cases(rng, e):
-            for U in sorted({1, 2, 4, library_u(n)}):
+            for U in sorted({1, 2, 4, library_u(n, "ag")}):
                 ps, pr = rng.choice(phases), rng.choice(phases)
                 w = emulate_ag(n, e, R, ps, pr, U, rng.randrange(0, 1 << 20))
                 assert (w == 1).all(), (n, e, R, ps, pr, U)
