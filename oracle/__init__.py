@@ -35,10 +35,14 @@ Array conventions: ``f32`` arrays are ``np.float32``, ``f16`` arrays are
 
 Parity status: every function here is pinned by ``tests/test_oracle.py``
 (worked examples from the pages, exact brute force, closed forms and
-hand-derived rounding cases).  The exact floating-point hop order inside a
-chunk is a reading (chunk c starts at rank c+1 and ends at rank c); the pages'
-step diagrams were lost, so that order is pinned by hand-derived cases built
-from the reading, not by a printed example.
+hand-derived rounding cases, hand-evaluated chunk bounds at counts n does not
+divide and hand-evaluated avg pre-scales at n = 3 and 72), agrees bit for bit
+with the independent evaluation in ``tests/brute.py`` on order-sensitive
+random data, and ``tests/test_oracle_mutants.py`` shows planted mistakes in
+``ar_oracle.c`` failing those pins.  The exact floating-point hop order inside
+a chunk is a reading (chunk c starts at rank c+1 and ends at rank c); the
+pages' step diagrams were lost, so that order is pinned by hand-derived cases
+built from the reading, not by a printed example.
 """
 from __future__ import annotations
 
@@ -80,56 +84,60 @@ def _load():
             return _lib
         if not os.path.exists(_LIB):
             build()
-        lib = ctypes.CDLL(_LIB)
-        vpp = ctypes.POINTER(ctypes.c_void_p)
-        llp = ctypes.POINTER(ctypes.c_longlong)
-        for name in ("orc_ring_allreduce_ex", "orc_ring_reduce_scatter_ex"):
-            f = getattr(lib, name)
-            f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_size_t, vpp, vpp, llp, llp,
-                          ctypes.c_int, ctypes.c_int]
-            f.restype = ctypes.c_int
-        for name in ("orc_tree_allreduce_ex", "orc_dtree_allreduce_ex"):
-            f = getattr(lib, name)
-            f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_size_t, vpp, vpp, ctypes.c_int, ctypes.c_int]
-            f.restype = ctypes.c_int
-        lib.orc_pairwise_reduce_ex.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_size_t, vpp,
-                                               ctypes.c_void_p, ctypes.c_int, ctypes.c_int]
-        lib.orc_pairwise_reduce_ex.restype = ctypes.c_int
-        lib.orc_split_p.argtypes = [ctypes.c_int]
-        lib.orc_split_p.restype = ctypes.c_int
-        lib.orc_ring_all_gather.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_size_t, vpp, vpp, llp, llp]
-        lib.orc_ring_all_gather.restype = ctypes.c_int
-        lib.orc_tree_allreduce.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_size_t, vpp, vpp]
-        lib.orc_tree_allreduce.restype = ctypes.c_int
-        lib.orc_direct_reduce.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_size_t, vpp,
-                                          ctypes.c_void_p]
-        lib.orc_direct_reduce.restype = ctypes.c_int
-        lib.orc_pairwise_reduce.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_size_t, vpp,
-                                            ctypes.c_void_p]
-        lib.orc_pairwise_reduce.restype = ctypes.c_int
-        lib.orc_dtree_allreduce.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_size_t, vpp, vpp]
-        lib.orc_dtree_allreduce.restype = ctypes.c_int
-        lib.orc_dtree_parent.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
-        lib.orc_dtree_parent.restype = ctypes.c_int
-        lib.orc_tree_parent.argtypes = [ctypes.c_int, ctypes.c_int]
-        lib.orc_tree_parent.restype = ctypes.c_int
-        lib.orc_allreduce_chunks.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_size_t,
-                                             ctypes.POINTER(ctypes.c_size_t)]
-        lib.orc_allreduce_chunks.restype = None
-        lib.orc_f32_to_bf16.argtypes = [ctypes.c_float]
-        lib.orc_f32_to_bf16.restype = ctypes.c_uint16
-        lib.orc_bf16_to_f32.argtypes = [ctypes.c_uint16]
-        lib.orc_bf16_to_f32.restype = ctypes.c_float
-        lib.orc_f32_to_f16.argtypes = [ctypes.c_float]
-        lib.orc_f32_to_f16.restype = ctypes.c_uint16
-        lib.orc_f16_to_f32.argtypes = [ctypes.c_uint16]
-        lib.orc_f16_to_f32.restype = ctypes.c_float
-        lib.orc_num_threads.argtypes = []
-        lib.orc_num_threads.restype = ctypes.c_int
-        lib.orc_set_num_threads.argtypes = [ctypes.c_int]
-        lib.orc_set_num_threads.restype = None
-        _lib = lib
-        return lib
+        _lib = _bind(ctypes.CDLL(_LIB))
+        return _lib
+
+
+def _bind(lib):
+    """Declare the C functions' argument and result types on a loaded oracle library."""
+    vpp = ctypes.POINTER(ctypes.c_void_p)
+    llp = ctypes.POINTER(ctypes.c_longlong)
+    for name in ("orc_ring_allreduce_ex", "orc_ring_reduce_scatter_ex"):
+        f = getattr(lib, name)
+        f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_size_t, vpp, vpp, llp, llp,
+                      ctypes.c_int, ctypes.c_int]
+        f.restype = ctypes.c_int
+    for name in ("orc_tree_allreduce_ex", "orc_dtree_allreduce_ex"):
+        f = getattr(lib, name)
+        f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_size_t, vpp, vpp, ctypes.c_int, ctypes.c_int]
+        f.restype = ctypes.c_int
+    lib.orc_pairwise_reduce_ex.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_size_t, vpp,
+                                           ctypes.c_void_p, ctypes.c_int, ctypes.c_int]
+    lib.orc_pairwise_reduce_ex.restype = ctypes.c_int
+    lib.orc_split_p.argtypes = [ctypes.c_int]
+    lib.orc_split_p.restype = ctypes.c_int
+    lib.orc_ring_all_gather.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_size_t, vpp, vpp, llp, llp]
+    lib.orc_ring_all_gather.restype = ctypes.c_int
+    lib.orc_tree_allreduce.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_size_t, vpp, vpp]
+    lib.orc_tree_allreduce.restype = ctypes.c_int
+    lib.orc_direct_reduce.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_size_t, vpp,
+                                      ctypes.c_void_p]
+    lib.orc_direct_reduce.restype = ctypes.c_int
+    lib.orc_pairwise_reduce.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_size_t, vpp,
+                                        ctypes.c_void_p]
+    lib.orc_pairwise_reduce.restype = ctypes.c_int
+    lib.orc_dtree_allreduce.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_size_t, vpp, vpp]
+    lib.orc_dtree_allreduce.restype = ctypes.c_int
+    lib.orc_dtree_parent.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    lib.orc_dtree_parent.restype = ctypes.c_int
+    lib.orc_tree_parent.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.orc_tree_parent.restype = ctypes.c_int
+    lib.orc_allreduce_chunks.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_size_t,
+                                         ctypes.POINTER(ctypes.c_size_t)]
+    lib.orc_allreduce_chunks.restype = None
+    lib.orc_f32_to_bf16.argtypes = [ctypes.c_float]
+    lib.orc_f32_to_bf16.restype = ctypes.c_uint16
+    lib.orc_bf16_to_f32.argtypes = [ctypes.c_uint16]
+    lib.orc_bf16_to_f32.restype = ctypes.c_float
+    lib.orc_f32_to_f16.argtypes = [ctypes.c_float]
+    lib.orc_f32_to_f16.restype = ctypes.c_uint16
+    lib.orc_f16_to_f32.argtypes = [ctypes.c_uint16]
+    lib.orc_f16_to_f32.restype = ctypes.c_float
+    lib.orc_num_threads.argtypes = []
+    lib.orc_num_threads.restype = ctypes.c_int
+    lib.orc_set_num_threads.argtypes = [ctypes.c_int]
+    lib.orc_set_num_threads.restype = None
+    return lib
 
 
 def _ptrs(arrays):

@@ -318,6 +318,40 @@ def test_float_avg_pre_scale_vs_sum_then_divide():
     assert not np.array_equal(a, s)      # the reading matters: the routes differ
 
 
+# Hand-derived float-avg values at rank counts that are not powers of two
+# ("NCCL all-reduce", section "What all-reduce promises": a floating-point
+# contribution is pre-scaled by 1/n as it is read).  With one non-zero
+# contribution x and zeros elsewhere every add is exact, so the result is
+# fp32(x * s) with s = fp32(1/n), computed by hand:
+#   n = 3:  2^25 / 3 = 11184810.67 -> s = 11184811 * 2^-25 (0x3EAAAAAB).
+#           x = 5: 5s = 55924055 * 2^-25; in [1, 2) the spacing is 2^-23 = 4 * 2^-25
+#           and 55924055 / 4 = 13981013.75 -> 13981014 * 2^-23 = 0x3FD55556,
+#           while x / 3 = 13981013.33 * 2^-23 -> 0x3FD55555.
+#   n = 72: 2^30 / 72 = 14913080.89 -> s = 14913081 * 2^-30 (0x3C638E39).
+#           x = 17: 17s = 253522377 * 2^-30; in [1/8, 1/4) the spacing is 2^-26
+#           and 253522377 / 16 = 15845148.56 -> 15845149 * 2^-26 = 0x3E71C71D,
+#           while 17 / 72 = 15845148.44 * 2^-26 -> 0x3E71C71C.
+# A per-contribution x / n, or a sum divided by n at the end, gives the second
+# pattern in both cases.
+PRESCALE_CASES = [(3, 5.0, 0x3FD55556, 0x3FD55555), (72, 17.0, 0x3E71C71D, 0x3E71C71C)]
+
+
+@pytest.mark.parametrize("n,x,want,divided", PRESCALE_CASES)
+def test_float_avg_prescale_hand_cases(n, x, want, divided):
+    assert np.float32(1.0 / n).view(np.uint32) == (0x3EAAAAAB if n == 3 else 0x3C638E39)
+    count = 4 * n + 3                               # every chunk, and a ragged tail
+    for holder in (0, n // 2, n - 1):
+        xs = [np.zeros(count, np.float32) for _ in range(n)]
+        xs[holder][:] = x
+        outs = [oracle.ring_allreduce(xs, "f32", "avg")[0], oracle.tree_allreduce(xs, "f32", "avg")[0],
+                oracle.dtree_allreduce(xs, "f32", "avg")[0], oracle.pairwise_reduce(xs, "f32", "avg")]
+        rs = oracle.ring_reduce_scatter([np.full(n * 3, x if r == holder else 0.0, np.float32) for r in range(n)],
+                                        "f32", "avg")
+        for y in outs + rs:
+            assert set(y.view(np.uint32).tolist()) == {want}, (n, holder, sorted(set(y.view(np.uint32).tolist())))
+            assert want != divided
+
+
 # ---------------------------------------------------------------------------
 # 4. the hop order, pinned by IEEE rounding cases derived by hand
 # ---------------------------------------------------------------------------
@@ -476,6 +510,54 @@ def test_allreduce_chunks_16_byte_units():
                 assert max(lens) - min(lens) <= u if V >= n else True
                 if count % (n * u) == 0:
                     assert off == [c * count // n for c in range(n + 1)]
+
+
+def test_allreduce_chunks_floor_cut_hand_cases():
+    """Chunk bounds at counts that n*u does not divide, evaluated by hand from
+    the floor of Eq. (2) (M2N paper, section IV 'Local shard bounds') in 16-byte
+    units (tests/golden/chunk_bounds.json); a ceiling cut fails every case but
+    the exact one."""
+    g = golden("chunk_bounds.json")
+    for case in g["cases"]:
+        got = oracle.allreduce_chunks(case["dtype"], case["n"], case["count"])
+        assert got == case["bounds"], case
+        if case["ceil"] != case["bounds"]:
+            assert got != case["ceil"]
+    b = g["c5_bucket"]
+    got = oracle.allreduce_chunks(b["dtype"], b["n"], b["count"])
+    for c, v in b["bounds_at"].items():
+        assert got[int(c)] == v, (c, got[int(c)], v)
+    for c, v in b["ceil_at"].items():
+        assert got[int(c)] != v
+    lens = [(got[c + 1] - got[c]) // 4 for c in range(b["n"])]
+    assert [c for c in range(b["n"]) if lens[c] == 21716] == b["long_chunks"]
+    assert all(v in (21715, 21716) for v in lens)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+def test_floor_cut_decides_the_hop_order_of_the_cut_vectors(dtype):
+    """The cut changes results, not only bounds.  n = 3, 5 vectors per rank:
+    the floor cut gives chunks of 1, 2 and 2 vectors, a ceiling cut 2, 2 and 1.
+    Vector 1 is in chunk 1 (chain 2, 0, 1) under the floor and in chunk 0
+    (chain 1, 2, 0) under the ceiling; vector 3 is in chunk 2 (chain 0, 1, 2)
+    under the floor and in chunk 1 under the ceiling.  The +B / 1 / -B rule of
+    the hop-order cases (the result is 0 exactly when +B and the 1 both come
+    before -B) then gives 0 for the stated cut and 1 for the other."""
+    n = 3
+    u = 16 // (4 if dtype == "f32" else 2)
+    B = BIG[dtype]
+    count = 5 * u
+    xs = [np.zeros(count) for _ in range(n)]
+    v1 = slice(1 * u, 2 * u)          # floor: chunk 1 = ranks 2, 0, 1
+    xs[2][v1], xs[0][v1], xs[1][v1] = B, 1.0, -B
+    v3 = slice(3 * u, 4 * u)          # floor: chunk 2 = ranks 0, 1, 2
+    xs[0][v3], xs[1][v3], xs[2][v3] = B, 1.0, -B
+    assert oracle.allreduce_chunks(dtype, n, count) == [0, u, 3 * u, 5 * u]
+    for y in oracle.ring_allreduce([to_dtype(x, dtype) for x in xs], dtype, "sum"):
+        assert as_float(y, dtype).tolist() == [0.0] * count, dtype
+    # with the owner's rank in the ceiling cut's chains the same vectors give 1
+    ceil_chain = {1: [1, 2, 0], 3: [2, 0, 1]}
+    assert _chain_result(ceil_chain[1], 2, 1, 0) == 1.0 and _chain_result(ceil_chain[3], 0, 2, 1) == 1.0
 
 
 # ---------------------------------------------------------------------------
