@@ -101,14 +101,12 @@ int fused_lds_bytes(ar_coll_t coll, int n) {
 }
 
 // AR_TREE_STAGED=1 sends the n <= 16 tree schedules through the LDS-staged
-// kernel (level by level, as for n > 16) instead of the register-evaluated
-// ones; both give the same bits.
+// kernels (as for n > 16) instead of the register-evaluated ones; both give
+// the same bits.  Read on every call (a getenv is far below a launch's cost),
+// so one process can compare the kernels.
 bool tree_staged() {
-    static const int v = [] {
-        const char *e = getenv("AR_TREE_STAGED");
-        return (e && *e == '1') ? 1 : 0;
-    }();
-    return v != 0;
+    const char *e = getenv("AR_TREE_STAGED");
+    return e && *e == '1';
 }
 
 // Dynamic LDS reservation (bytes) of the ring / tree workgroups; the
@@ -131,6 +129,23 @@ int ring_lds_bytes(ar_coll_t coll, int n) {
 int lds_window(int n) {
     int w = (n <= 32) ? (kThreads * 2) / n : (kThreads * kItemsPerThread) / n;
     return w < 1 ? 1 : w;
+}
+
+// Window width of the LDS-staged trees: a multiple of 8 vectors, so that a
+// window covers whole 128-byte lines of every rank buffer (a width of 14
+// vectors at 72 ranks read and wrote partial lines), with n * W at most
+// kThreads * kItemsPerThread items.
+int tree_window(int n) {
+    const int w = (kThreads * kItemsPerThread) / (8 * n) * 8;
+    return w < 8 ? 8 : w;
+}
+
+// Windows of the staged double tree: [0, split) in windows of W from vector 0,
+// and [split2, Vfull) in windows of W from split2 rounded down to a multiple
+// of W (the first one partial), so every window sits on the same grid.
+long long dtree_windows(const Geometry &g) {
+    const long long base = g.split2 - g.split2 % g.W;
+    return (g.split + g.W - 1) / g.W + (g.Vfull > base ? (g.Vfull - base + g.W - 1) / g.W : 0);
 }
 
 // The 16-byte phase (address mod 16) shared by n pointers, or -1.
@@ -408,13 +423,13 @@ ar_status_t ar_allreduce_ex(const void *const *sendbufs, void *const *recvbufs, 
             h = launch_tree_reg_allreduce(use == AR_SCHED_DTREE, dtype, op, tv, g,
                                           fused_lds_bytes(AR_COLL_ALLREDUCE, n), stream);
         } else if (use == AR_SCHED_DTREE) {
-            g.W = lds_window(n);
-            g.windows = (g.split + g.W - 1) / g.W + (g.Vfull - g.split2 + g.W - 1) / g.W;
-            h = launch_dtree_allreduce(dtype, op, tv, tree, tree2, g, grid_for(g.windows, cus, 4), stream);
+            g.W = tree_window(n);
+            g.windows = dtree_windows(g);
+            h = launch_dtree_allreduce(dtype, op, tv, tree, tree2, g, cus, stream);
         } else {
-            g.W = lds_window(n);
+            g.W = tree_window(n);
             g.windows = (g.Vfull + g.W - 1) / g.W;
-            h = launch_tree_allreduce(dtype, op, tv, tree, g, grid_for(g.windows, cus, 4), stream);
+            h = launch_tree_allreduce(dtype, op, tv, tree, g, cus, stream);
         }
         return hip_status(h);
     };

@@ -147,12 +147,17 @@ hipError_t launch_ring_all_gather(const RankTable &t, const Geometry &g, int gri
 // [g.split, Vfull)); ``lds`` as for the fused kernels.
 hipError_t launch_tree_reg_allreduce(bool dual, int dt, int op, const RankTable &t, const Geometry &g, int lds,
                                      hipStream_t s);
-// Tree: one shape over all of [0, Vfull); double tree: ``tree`` over vectors
-// [0, g.split) and ``tree2`` over [g.split, Vfull), in one launch.
+// Staged trees (windows of g.W vectors, a multiple of 8): one shape over all
+// of [0, Vfull); double tree: ``tree`` over vectors [0, g.split) and
+// ``tree2`` over [g.split2, Vfull), in one launch.  The launcher sizes its
+// persistent grid from the device's compute units ``cus``.
 hipError_t launch_tree_allreduce(int dt, int op, const RankTable &t, const TreeShape &tree, const Geometry &g,
-                                 int grid, hipStream_t s);
+                                 int cus, hipStream_t s);
 hipError_t launch_dtree_allreduce(int dt, int op, const RankTable &t, const TreeShape &tree, const TreeShape &tree2,
-                                  const Geometry &g, int grid, hipStream_t s);
+                                  const Geometry &g, int cus, hipStream_t s);
+// Workgroups for a persistent launch over ``units`` work units: per_cu per
+// compute unit (AR_GRID overrides), at most ``units``.
+int grid_for(long long units, int cus, int per_cu);
 // Element-wise paths (any alignment, and the all-reduce tail), elements
 // [e_begin, e_end) of every rank buffer / slice:
 hipError_t launch_elem_ring_allreduce(int dt, int op, const RankTable &t, const Geometry &g, long long e_begin,

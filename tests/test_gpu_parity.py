@@ -605,6 +605,32 @@ def test_trees_every_rank_count_up_to_17(dtype, sched):
                 assert_bits_equal(got[r], want[r], "%s n=%d %s %s rank %d" % (sched, n, dtype, op, r))
 
 
+@pytest.mark.parametrize("teams", ["1", "0"])
+def test_staged_trees_match_oracle(teams, monkeypatch):
+    """The LDS-staged tree kernels, with concurrent up/down teams (teams=1,
+    the default) and level by level (teams=0): every dtype, ops whose order
+    matters, rank counts up to 128 (n <= 16 through AR_TREE_STAGED), counts
+    spanning many windows per workgroup with a ragged end, in and out of place,
+    against the tree and double-tree oracles bit for bit."""
+    monkeypatch.setenv("AR_TREE_STAGED", "1")
+    monkeypatch.setenv("AR_TREE_TEAMS", teams)
+    for n in (2, 3, 8, 16, 17, 33, 72, 128):
+        for dtype in DTYPES:
+            u = LANES[dtype]
+            for op in (("sum", "avg", "max") if n in (17, 72) else ("avg",)):
+                count = n * u * 600 + u * 5 + 3
+                xs = inputs(61, n, count, dtype, op)
+                for sched in ("tree", "dtree"):
+                    for inplace in ((False, True) if n == 72 else (False,)):
+                        print("staged %s teams=%s n=%d %s %s inplace=%d" % (sched, teams, n, dtype, op, inplace),
+                              flush=True)
+                        got = run_allreduce(xs, dtype, op, sched, inplace=inplace)
+                        want = reference(sched, xs, dtype, op)
+                        for r in (0, n // 2, n - 1):
+                            assert_bits_equal(got[r], want[r], "staged %s teams=%s n=%d %s %s rank %d"
+                                              % (sched, teams, n, dtype, op, r))
+
+
 def test_randomized_calls_match_oracle():
     """400 seeded random calls: collective, n (1-20 and 72), dtype, op,
     schedule, numerics options, element counts (log-uniform, ragged), in place
