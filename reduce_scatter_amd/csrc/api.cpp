@@ -71,13 +71,6 @@ ar_status_t device_cus(int *cus) {
     return AR_OK;
 }
 
-// Workgroups for a persistent launch over ``units`` independent work units.
-int grid_for(long long units, int cus, int per_cu) {
-    const char *e = getenv("AR_GRID");
-    long long g = (e && atoll(e) > 0) ? atoll(e) : (long long)cus * per_cu;
-    if (g > units) g = units;
-    return (int)(g < 1 ? 1 : g);
-}
 
 // Dynamic LDS (bytes) a fused workgroup reserves to cap how many one-wave
 // workgroups are resident per CU (LDS is 160 KB per CU on gfx950).  Measured
@@ -138,14 +131,6 @@ int lds_window(int n) {
 int tree_window(int n) {
     const int w = (kThreads * kItemsPerThread) / (8 * n) * 8;
     return w < 8 ? 8 : w;
-}
-
-// Windows of the staged double tree: [0, split) in windows of W from vector 0,
-// and [split2, Vfull) in windows of W from split2 rounded down to a multiple
-// of W (the first one partial), so every window sits on the same grid.
-long long dtree_windows(const Geometry &g) {
-    const long long base = g.split2 - g.split2 % g.W;
-    return (g.split + g.W - 1) / g.W + (g.Vfull > base ? (g.Vfull - base + g.W - 1) / g.W : 0);
 }
 
 // The 16-byte phase (address mod 16) shared by n pointers, or -1.
@@ -318,6 +303,15 @@ ar_status_t apply_numerics(const ar_numerics_t *num, int dtype, int op, int n, G
 
 }  // namespace
 
+// Workgroups for a persistent launch over ``units`` independent work units:
+// per_cu per compute unit (AR_GRID overrides), at most ``units``.
+int ar::grid_for(long long units, int cus, int per_cu) {
+    const char *e = getenv("AR_GRID");
+    long long g = (e && atoll(e) > 0) ? atoll(e) : (long long)cus * per_cu;
+    if (g > units) g = units;
+    return (int)(g < 1 ? 1 : g);
+}
+
 extern "C" {
 
 const char *ar_status_string(ar_status_t s) {
@@ -424,11 +418,9 @@ ar_status_t ar_allreduce_ex(const void *const *sendbufs, void *const *recvbufs, 
                                           fused_lds_bytes(AR_COLL_ALLREDUCE, n), stream);
         } else if (use == AR_SCHED_DTREE) {
             g.W = tree_window(n);
-            g.windows = dtree_windows(g);
             h = launch_dtree_allreduce(dtype, op, tv, tree, tree2, g, cus, stream);
         } else {
             g.W = tree_window(n);
-            g.windows = (g.Vfull + g.W - 1) / g.W;
             h = launch_tree_allreduce(dtype, op, tv, tree, g, cus, stream);
         }
         return hip_status(h);

@@ -149,8 +149,8 @@ hipError_t launch_tree_reg_allreduce(bool dual, int dt, int op, const RankTable 
                                      hipStream_t s);
 // Staged trees (windows of g.W vectors, a multiple of 8): one shape over all
 // of [0, Vfull); double tree: ``tree`` over vectors [0, g.split) and
-// ``tree2`` over [g.split2, Vfull), in one launch.  The launcher sizes its
-// persistent grid from the device's compute units ``cus``.
+// ``tree2`` over [g.split2, Vfull), one launch each.  The launcher sizes its
+// persistent grids from the device's compute units ``cus``.
 hipError_t launch_tree_allreduce(int dt, int op, const RankTable &t, const TreeShape &tree, const Geometry &g,
                                  int cus, hipStream_t s);
 hipError_t launch_dtree_allreduce(int dt, int op, const RankTable &t, const TreeShape &tree, const TreeShape &tree2,

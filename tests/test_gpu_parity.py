@@ -607,8 +607,8 @@ def test_trees_every_rank_count_up_to_17(dtype, sched):
 
 @pytest.mark.parametrize("teams", ["1", "0"])
 def test_staged_trees_match_oracle(teams, monkeypatch):
-    """The LDS-staged tree kernels, with concurrent up/down teams (teams=1,
-    the default) and level by level (teams=0): every dtype, ops whose order
+    """The LDS-staged tree kernels, with concurrent up/down teams (teams=1)
+    and level by level (teams=0), each forced: every dtype, ops whose order
     matters, rank counts up to 128 (n <= 16 through AR_TREE_STAGED), counts
     spanning many windows per workgroup with a ragged end, in and out of place,
     against the tree and double-tree oracles bit for bit."""

@@ -1,12 +1,12 @@
 """Host model of the LDS-staged trees' window grid (CPU only).
 
-The staged tree and double-tree kernels walk windows of W vectors, W a
-multiple of 8 (whole 128-byte lines), on a grid from vector 0; the double
-tree's second half [split2, Vfull) starts at split2 rounded down to the grid,
-its first window partial.  This model restates the window arithmetic of the
-kernels and the host's window count and checks that every vector of
-[0, split) and [split2, Vfull) is covered exactly once, by a window of the
-right tree, and that every window starts on the grid.
+The staged tree kernels walk windows of W vectors, W a multiple of 8 (whole
+128-byte lines), over a range [lo, hi) on a grid from lo rounded down to a
+multiple of W (the first window partial); the double tree is two launches,
+[0, split) with the first tree and [split2, Vfull) with the second.  This
+model restates the window arithmetic of the launcher and the kernels and
+checks that every vector of both halves is covered exactly once, by a launch
+of the right tree, and that every window starts on the grid.
 """
 from __future__ import annotations
 
@@ -20,30 +20,32 @@ def tree_window(n):
     return max(w, 8)
 
 
-def dtree_windows(Vfull, split, split2, W):
-    base = split2 - split2 % W
-    return (split + W - 1) // W + ((Vfull - base + W - 1) // W if Vfull > base else 0)
+def range_windows(lo, hi, W):
+    base = lo - lo % W
+    windows = (hi - base + W - 1) // W if hi > base else 0
+    return base, windows
 
 
-def window_at(win, first, Vfull, split, split2, W, dual):
-    second = dual and win >= first
-    pos0 = split2 - split2 % W + (win - first) * W if second else win * W
-    lo = split2 if second else 0
-    hi = split if dual and not second else Vfull
-    return pos0, lo, hi, second
-
-
-def covered(Vfull, split, split2, W, dual):
-    windows = dtree_windows(Vfull, split, split2, W) if dual else (Vfull + W - 1) // W
-    first = (split + W - 1) // W if dual else windows
-    seen = {}
+def covered_range(lo, hi, W, seen, tag):
+    if lo >= hi:
+        return
+    base, windows = range_windows(lo, hi, W)
     for win in range(windows):
-        pos0, lo, hi, second = window_at(win, first, Vfull, split, split2, W, dual)
+        pos0 = base + win * W
         assert pos0 % W == 0
         for v in range(pos0, pos0 + W):
             if lo <= v < hi:
                 assert v not in seen, (v, win)
-                seen[v] = second
+                seen[v] = tag
+
+
+def covered(Vfull, split, split2, W, dual):
+    seen = {}
+    if dual:
+        covered_range(0, split, W, seen, False)
+        covered_range(split2, Vfull, W, seen, True)
+    else:
+        covered_range(0, Vfull, W, seen, False)
     return seen
 
 
