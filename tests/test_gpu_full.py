@@ -5,13 +5,13 @@
   every output element against the ring / tree oracle.
 * FSDP-style shards: reduce-scatter (avg) of 8 x 128 Mi bf16 and all-gather
   of 8 x 16 Mi bf16: every element against the oracle.
-* n = 16 int32 sweep, 1 KB .. 1 GB per rank: every element up to 16 MB per
-  rank; beyond that, 64 sampled windows per call (int32 sums wrap exactly, so
-  the plain element-wise definition is exact on any slice).
+* n = 16 int32 sweep, 1 KB .. 1 GB per rank: every op and schedule, every
+  element of every rank against the oracle (int32 sums wrap exactly, so the
+  plain element-wise definition is exact; computed in streamed slices).
 * 72 ranks, 29 gradient buckets of up to 25 MB packed from 256 tensors, avg,
-  in place, back to back: three buckets (first, middle, last: ragged chunk
-  splits) checked element by element against the oracle of the planner's
-  choice; the split schedule on one 25 MB bucket against the pairwise oracle.
+  in place, back to back: every bucket of every rank checked (ranks agree on
+  the device, rank 0 against the oracle of the planner's choice); the split
+  schedule on one 25 MB bucket against the pairwise oracle.
 * The split schedule at the 8 x 256 MB shape against the pairwise oracle.
 * Past every 32-bit byte offset: n = 2 fp32 all-reduce of 4.3 GB per rank
   (every schedule), reduce-scatter and all-gather of 4.3 GB slices: every
@@ -145,72 +145,89 @@ def test_c3_fsdp_reduce_scatter_then_all_gather():
     torch.cuda.empty_cache()
 
 
-def _sample_windows(count, k=64, width=4096, seed=0):
-    rg = np.random.default_rng(seed)
-    starts = sorted(set(int(s) for s in rg.integers(0, max(1, count - width), size=k)))
-    return [(0, min(width, count))] + [(s, min(s + width, count)) for s in starts] + [(max(0, count - width), count)]
+C4_OPS = ["sum", "min", "max", "avg"]
 
 
-@pytest.mark.parametrize("op", ["sum", "min", "max", "avg"])
-def test_c4_int32_size_sweep(op):
+def _first_difference(got, want):
+    bad = torch.nonzero(got != want)
+    return int(bad[0]) if bad.numel() else -1
+
+
+def _expected_int32(xs, ops, slice_elems=16 * MB):
+    """The plain definition for each op (exact for int32 whatever the order),
+    evaluated by the oracle on the host in slices of ``slice_elems`` elements
+    per rank, each slice's result copied into a device tensor."""
+    count = xs[0].numel()
+    want = {op: torch.empty_like(xs[0]) for op in ops}
+    for a in range(0, count, slice_elems):
+        b = min(count, a + slice_elems)
+        host = [to_host(x[a:b], "i32") for x in xs]
+        for op in ops:
+            want[op][a:b].copy_(torch.from_numpy(oracle.direct_reduce(host, "i32", op)))
+    return want
+
+
+@pytest.mark.parametrize("size", workloads.C4_SIZES)
+def test_c4_int32_size_sweep_every_element(size):
+    """n = 16 int32, 1 KB .. 1 GB per rank: every op and schedule, every
+    element of every rank's output against the oracle (the oracle's result is
+    computed once per op in streamed slices and compared on the device)."""
     n = workloads.C4_N
-    for size in workloads.C4_SIZES:
-        count = size // 4
-        stream = int(np.log2(size))
-        xs = [workloads.device_ints(3, stream, r, count, -(1 << 20), 1 << 20, "i32") for r in range(n)]
-        ys = [torch.empty_like(x) for x in xs]
-        full = size <= 16 * MB
-        if full:
-            want = oracle.direct_reduce([to_host(x, "i32") for x in xs], "i32", op)
+    count = size // 4
+    stream = int(np.log2(size))
+    xs = [workloads.device_ints(3, stream, r, count, -(1 << 20), 1 << 20, "i32") for r in range(n)]
+    print("c4 oracle", size, flush=True)
+    want = _expected_int32(xs, C4_OPS)
+    ys = [torch.empty_like(x) for x in xs]
+    for op in C4_OPS:
         for sched in ("auto", "fused", "ring", "tree", "split", "dtree"):
             print("c4", op, size, sched, flush=True)
+            for y in ys:
+                y.fill_(-7)
             ar.ar_allreduce(xs, ys, count, "i32", op, sched=sched)
             torch.cuda.synchronize()
-            if full:
-                for r in (0, n - 1):
-                    assert_bits_equal(to_host(ys[r], "i32"), want, "c4 %s %d %s" % (op, size, sched))
-            else:
-                for a, b in _sample_windows(count, seed=stream):
-                    w = oracle.direct_reduce([to_host(x[a:b], "i32") for x in xs], "i32", op)
-                    for r in (0, 7, n - 1):
-                        assert_bits_equal(to_host(ys[r][a:b], "i32"), w, "c4 %s %d %s [%d,%d)" % (op, size, sched, a, b))
-        del xs, ys
-        torch.cuda.empty_cache()
+            for r in range(n):
+                if not torch.equal(ys[r], want[op]):
+                    raise AssertionError("c4 %s %d %s rank %d: first difference at element %d"
+                                         % (op, size, sched, r, _first_difference(ys[r], want[op])))
+    del xs, ys, want
+    torch.cuda.empty_cache()
+
+
+def _c5_oracle(host, chosen):
+    if chosen == "split":
+        return oracle.pairwise_reduce(host, "f32", "avg")
+    if chosen == "dtree":
+        return oracle.dtree_allreduce(host, "f32", "avg")[0]
+    if chosen == "tree":
+        return oracle.tree_allreduce(host, "f32", "avg")[0]
+    return oracle.ring_allreduce(host, "f32", "avg")[0]
 
 
 def test_c5_bucketed_72_ranks_in_place():
+    """72 ranks, all 29 buckets reduced in place back to back on one stream;
+    then every bucket is checked: all 72 ranks hold the same bits (on the
+    device), and rank 0's bucket equals the oracle of the planner's choice,
+    evaluated on the same inputs regenerated from their seeds."""
     n = workloads.C5_N
     buckets, total = workloads.c5_buckets()
     assert len(buckets) >= 20
     count_total = total // 4
     grads = [workloads.device_spiky_normal(4, r, count_total, 1e-3, 0.01, 100.0) for r in range(n)]
-    checked = {0, len(buckets) // 2, len(buckets) - 1}
-    want = {}
-    for b in checked:
-        off, nbytes = buckets[b]
-        a, e = off // 4, (off + nbytes) // 4
-        host = [to_host(g[a:e], "f32") for g in grads]
-        chosen = ar.ar_plan("allreduce", e - a, "f32", "avg", n).chosen
-        print("c5 oracle bucket", b, nbytes, chosen, flush=True)
-        if chosen == "split":
-            want[b] = oracle.pairwise_reduce(host, "f32", "avg")
-        elif chosen == "dtree":
-            want[b] = oracle.dtree_allreduce(host, "f32", "avg")[0]
-        elif chosen == "tree":
-            want[b] = oracle.tree_allreduce(host, "f32", "avg")[0]
-        else:
-            want[b] = oracle.ring_allreduce(host, "f32", "avg")[0]
     for b, (off, nbytes) in enumerate(buckets):           # back to back on one stream, in place
         a, e = off // 4, (off + nbytes) // 4
         views = [g[a:e] for g in grads]
         ar.ar_allreduce(views, views, e - a, "f32", "avg")
     torch.cuda.synchronize()
-    for b in checked:
-        off, nbytes = buckets[b]
+    inputs = [workloads.device_spiky_normal(4, r, count_total, 1e-3, 0.01, 100.0) for r in range(n)]
+    for b, (off, nbytes) in enumerate(buckets):
         a, e = off // 4, (off + nbytes) // 4
-        for r in (0, 35, n - 1):
-            assert_bits_equal(to_host(grads[r][a:e], "f32"), want[b], "c5 bucket %d rank %d" % (b, r))
-    del grads
+        _same_on_all_ranks([g[a:e] for g in grads])
+        chosen = ar.ar_plan("allreduce", e - a, "f32", "avg", n).chosen
+        print("c5 bucket", b, nbytes, chosen, flush=True)
+        want = _c5_oracle([to_host(x[a:e], "f32") for x in inputs], chosen)
+        assert_bits_equal(to_host(grads[0][a:e], "f32"), want, "c5 bucket %d" % b)
+    del grads, inputs
     torch.cuda.empty_cache()
 
 
