@@ -87,28 +87,54 @@ def measured_traffic():
     return t.get("bytes_per_launch")
 
 
-def time_calls(fn, steps, warmup, stream):
-    """Warm up, then time ``steps`` calls: one event pair around the whole
-    region and one around every call, all recorded on ``stream``."""
+def warm_up(fn, warmup, min_seconds=0.3):
+    """At least ``warmup`` calls and at least ``min_seconds`` of them (wall
+    clock, synchronised), so clocks and caches have settled whatever K/W are."""
     import torch
-    for _ in range(warmup):
+    t = time.perf_counter()
+    calls = 0
+    while calls < warmup or time.perf_counter() - t < min_seconds:
         fn()
+        calls += 1
+        if calls % 8 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    return calls
+
+
+def time_region(fn, steps, stream):
+    """``steps`` calls back to back between one pair of HIP events recorded on
+    ``stream`` (the stream the kernels are launched on): the average time per
+    call, with nothing recorded between the calls."""
+    import torch
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
     t0.record(stream)
-    for i in range(steps):
-        starts[i].record(stream)
+    for _ in range(steps):
         fn()
-        ends[i].record(stream)
     t1.record(stream)
     torch.cuda.synchronize()
-    total_ms = t0.elapsed_time(t1)
-    per = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
-    time_calls.last_min = per[0]
-    return total_ms / steps, sum(per) / steps, per[len(per) // 2]
+    return t0.elapsed_time(t1) / steps
+
+
+def per_call_ms(fn, calls, stream):
+    """One event pair around each call (diagnostics only: the events
+    themselves add a few microseconds between calls)."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in ev]
+
+
+def time_calls(fn, steps, warmup, stream):
+    """Warm up, then the average time per call over ``steps`` calls (ms)."""
+    warm_up(fn, warmup)
+    return time_region(fn, steps, stream)
 
 
 def copy_probe(args):
@@ -117,7 +143,7 @@ def copy_probe(args):
     dst = torch.empty_like(src)
     src.fill_(1.0)
     stream = torch.cuda.current_stream()
-    step_ms, launch_ms, _ = time_calls(lambda: dst.copy_(src), args.steps, args.warmup, stream)
+    launch_ms = time_calls(lambda: dst.copy_(src), args.steps, args.warmup, stream)
     print(json.dumps({"copy_probe_bytes_read": src.numel() * 4, "copy_probe_bytes_written": src.numel() * 4,
                       "launch_ms": round(launch_ms, 4),
                       "gbps": round(2 * src.numel() * 4 / (launch_ms * 1e-3) / 1e9, 1)}), flush=True)
@@ -336,6 +362,7 @@ def sweep():
     del grads, views
     torch.cuda.empty_cache()
     out += reshard_report()
+    out += cpu_report()
     print("\n".join(out), flush=True)
 
 
@@ -377,9 +404,10 @@ def cpu_baseline(min_seconds=10.0):
     """The oracle, as it stands, on the benchmark's own workload: the ring
     all-reduce (sum) of n = 8 ranks of 64 Mi fp32 elements (256 MB each),
     N(0, 1e-3) host data (torch's CPU generator with the device buffers'
-    seeds).  One call warms the host allocator; then calls are
-    timed until at least ``min_seconds`` of CPU work have run.  Reported as
-    algbw GB/s (256 MB per rank / mean time per call)."""
+    seeds).  One call warms the host allocator; then calls are timed until at
+    least ``min_seconds`` of CPU work have run.  ``value`` is algbw (256 MB
+    per rank / mean time per call), the metric's own unit; ``hbm_equiv_GBps``
+    is the algorithmic bytes 2*n*S / time, the figure the GPU's roofline uses."""
     import oracle
     import workloads
     count = COUNT
@@ -396,7 +424,8 @@ def cpu_baseline(min_seconds=10.0):
             break
     per = dt / calls
     return {"value": round(count * 4 / per / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
+            "hbm_equiv_GBps": round(2 * N_RANKS * count * 4 / per / 1e9, 3),
             "sample": "the whole workload: ring all-reduce (sum), n=8, fp32, 64 Mi elements (256 MB) per rank, "
                       "%d calls in %.1f s (%.2f s per call)" % (calls, dt, per)}
 
@@ -425,8 +454,94 @@ def cpu_baseline_one_core(min_seconds=4.0):
         oracle.set_num_threads(threads)
     per = dt / calls
     return {"value": round(count * 4 / per / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "cpu_model": cpu_model(), "hbm_equiv_GBps": round(2 * N_RANKS * count * 4 / per / 1e9, 3),
             "sample": "ring all-reduce (sum), n=8, fp32, the first 4 Mi elements (16 MB) of every rank, "
                       "%d calls in %.1f s" % (calls, dt)}
+
+
+def _cpu_time(fn, min_seconds):
+    """Mean wall time per call (s) of ``fn`` after one warm-up call, over at
+    least ``min_seconds``."""
+    fn()
+    calls, t = 0, time.perf_counter()
+    while True:
+        fn()
+        calls += 1
+        dt = time.perf_counter() - t
+        if dt >= min_seconds:
+            return dt / calls, calls
+
+
+def cpu_report(min_seconds=2.0):
+    """The oracle, as it stands, on every workload (bounded samples of the
+    large ones), at all host threads and at one: time per call and GB/s of
+    algorithmic bytes (all-reduce 2*n*S, reduce-scatter and all-gather
+    (n+1)*n*R*e).  A baseline beside the GPU numbers, not a target."""
+    import oracle
+    import workloads as wl
+    MB = 1 << 20
+    threads = oracle.num_threads()
+    rows = []
+
+    def c1():
+        xs = wl.c1_inputs()
+        return (lambda: oracle.ring_allreduce(xs, "f32", "sum")), 2 * 4 * 1024 * 4, \
+            "all-reduce sum, n=4, fp32, 1024 elements per rank (the whole workload)"
+
+    def c2():
+        c = 8 * MB
+        xs = [wl.normal(1, 0, r, c, 1e-3, "f32") for r in range(8)]
+        return (lambda: oracle.ring_allreduce(xs, "f32", "sum")), 2 * 8 * c * 4, \
+            "all-reduce sum, n=8, fp32, 8 Mi elements (32 MB) per rank: 1/8 of the 256 MB per rank workload"
+
+    def c3_rs():
+        R = 2 * MB
+        xs = [wl.normal(2, 0, r, 8 * R, 1e-2, "bf16") for r in range(8)]
+        return (lambda: oracle.ring_reduce_scatter(xs, "bf16", "avg")), 9 * 8 * R * 2, \
+            "reduce-scatter avg, n=8, bf16, 2 Mi elements out per rank (16 Mi in): 1/8 of the FSDP shard"
+
+    def c3_ag():
+        R = 2 * MB
+        xs = [wl.uniform(2, 1, r, R, -1.0, 1.0, "bf16") for r in range(8)]
+        return (lambda: oracle.ring_all_gather(xs, "bf16")), 9 * 8 * R * 2, \
+            "all-gather, n=8, bf16, 2 Mi elements in per rank: 1/8 of the FSDP shard"
+
+    def c4():
+        c = 4 * MB
+        xs = [wl.ints(3, 30, r, c, -(1 << 20), 1 << 20, "i32") for r in range(16)]
+        return (lambda: oracle.ring_allreduce(xs, "i32", "sum")), 2 * 16 * c * 4, \
+            "all-reduce sum, n=16, int32, 4 Mi elements (16 MB) per rank: 1/64 of the 1 GB per rank cell"
+
+    def c5():
+        buckets, _ = wl.c5_buckets()
+        c = buckets[0][1] // 4 // 4
+        xs = [wl.normal(4, 1, r, c, 1e-3, "f32") for r in range(72)]
+        return (lambda: oracle.pairwise_reduce(xs, "f32", "avg")), 2 * 72 * c * 4, \
+            "all-reduce avg, n=72, fp32, the pairwise order the planner picks, %d elements per rank: a quarter " \
+            "of the first 25 MB bucket" % c
+
+    for name, make in (("c1", c1), ("c2", c2), ("c3 reduce-scatter", c3_rs), ("c3 all-gather", c3_ag), ("c4", c4),
+                       ("c5", c5)):
+        fn, alg, sample = make()
+        per_all, calls_all = _cpu_time(fn, min_seconds)
+        oracle.set_num_threads(1)
+        try:
+            per_one, calls_one = _cpu_time(fn, min_seconds)
+        finally:
+            oracle.set_num_threads(threads)
+        rows.append((name, sample, per_all, alg / per_all / 1e9, per_one, alg / per_one / 1e9))
+        del fn
+    out = ["## CPU oracle on every workload (a baseline, not the target)", "",
+           "Host: %s, %d threads (OpenMP over the elements of each message; results identical at any thread "
+           "count). Time per call after one warm-up call, at least %.0f s of calls per cell; GB/s = algorithmic "
+           "bytes (all-reduce 2*n*S; reduce-scatter / all-gather (n+1)*n*R*e) / time." % (cpu_model(), threads,
+                                                                                         min_seconds), "",
+           "| workload | sample | ms per call, %d threads | GB/s | ms per call, 1 thread | GB/s |" % threads,
+           "|---|---|---|---|---|---|"]
+    for name, sample, pa, ga, po, go in rows:
+        out.append("| %s | %s | %.3f | %.3f | %.3f | %.3f |" % (name, sample, pa * 1e3, ga, po * 1e3, go))
+    out.append("")
+    return out
 
 
 def copy_ceiling(stream, alg_bytes):
@@ -441,11 +556,22 @@ def copy_ceiling(stream, alg_bytes):
     dst = torch.empty_like(src)
     src.fill_(1.0)
     S, D = ar.pointers([src]), ar.pointers([dst])
-    _, ms, _ = time_calls(lambda: ar.ar_all_gather(S, D, src.numel(), "f32", n=1, sched="fused", stream=stream),
-                          10, 2, stream)
+    ms = time_calls(lambda: ar.ar_all_gather(S, D, src.numel(), "f32", n=1, sched="fused", stream=stream), 10, 2, stream)
     del src, dst
     return {"bytes": alg_bytes, "ms": round(ms, 4), "GBps": round(alg_bytes / (ms * 1e-3) / 1e9, 1),
             "frac": round(alg_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (as lscpu reports it, read from /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def main():
@@ -492,16 +618,22 @@ def main():
 
     plan = ar.ar_plan("allreduce", COUNT, "f32", args.op, N_RANKS)
     chosen = plan.chosen if args.sched == "auto" else args.sched
-    step_ms, launch_ms, launch_med_ms = time_calls(step, args.steps, args.warmup, stream)
-    launch_min_ms = time_calls.last_min
+    warm_calls = warm_up(step, args.warmup)
+    # The timed region: K steps back to back between one event pair on the launch stream.  Each step is one
+    # launch of the schedule's kernel, so the average launch duration over the region is the time per step,
+    # and ``value``, the roofline and the % of peak all use this one denominator.
+    step_ms = time_region(step, args.steps, stream)
     algbw = S / (step_ms * 1e-3) / 1e9
-    achieved = alg_bytes / (launch_ms * 1e-3) / 1e9
+    achieved = alg_bytes / (step_ms * 1e-3) / 1e9
+    # Diagnostics after the timed region: one event pair around each of K more calls.
+    per = per_call_ms(step, args.steps, stream)
+    per_sorted = sorted(per)
 
     detail = {}
     if not args.no_detail:
         for sched in ("fused", "ring", "tree", "split", "dtree"):
             for op in ("sum", "avg"):
-                ms, lms, _ = time_calls(
+                lms = time_calls(
                     lambda: ar.ar_allreduce(xs, ys, COUNT, "f32", op, sched=sched, stream=stream), 10, 2, stream)
                 detail["%s_%s" % (sched, op)] = {"ms": round(lms, 4),
                                                  "algbw_GBps": round(S / (lms * 1e-3) / 1e9, 1),
@@ -509,7 +641,7 @@ def main():
         detail["planner"] = {"chosen": plan.chosen, "predicted_us": {k: round(v, 1) for k, v in
                                                                     plan.predicted_us.items()}}
         cc = copy_ceiling(stream, alg_bytes)
-        cc["fused_over_copy"] = round(cc["ms"] / launch_ms, 4) if chosen == "fused" else None
+        cc["fused_over_copy"] = round(cc["ms"] / step_ms, 4) if chosen == "fused" else None
         detail["copy_ceiling"] = cc
 
     out = {
@@ -536,8 +668,13 @@ def main():
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4),
                      "traffic": measured_traffic() if chosen == "fused" else None,
-                     "algorithmic_bytes_per_launch": alg_bytes, "avg_launch_ms": round(launch_ms, 4),
-                     "median_launch_ms": round(launch_med_ms, 4), "min_launch_ms": round(launch_min_ms, 4)},
+                     "algorithmic_bytes_per_launch": alg_bytes, "avg_launch_ms": round(step_ms, 4),
+                     "avg_launch_ms_from": "the timed region: %d launches back to back between one event pair on "
+                                           "the launch stream" % args.steps,
+                     "per_call_events_ms": {"calls": len(per), "median": round(per_sorted[len(per) // 2], 4),
+                                            "min": round(per_sorted[0], 4), "first": round(per[0], 4),
+                                            "last": round(per[-1], 4)},
+                     "warmup_calls": warm_calls},
         "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(),
         "detail": detail,
     }
