@@ -80,12 +80,9 @@ ar_status_t device_cus(int *cus) {
 // the all-gather reserves 64 KB and the reduce-scatter 48 KB).  AR_FUSED_LDS_KB
 // overrides all of them.
 int fused_lds_bytes(ar_coll_t coll, int n) {
-    static const int env = [] {
-        const char *e = getenv("AR_FUSED_LDS_KB");
-        const long v = (e && *e) ? atol(e) : -1;
-        return (int)(v > 64 ? 64 : v);
-    }();
-    if (env >= 0) return env * 1024;
+    const char *e = getenv("AR_FUSED_LDS_KB");                  // read per call: a tuning knob
+    const long env = (e && *e) ? (atol(e) > 64 ? 64 : atol(e)) : -1;
+    if (env >= 0) return (int)env * 1024;
     switch (coll) {
     case AR_COLL_ALLREDUCE: return (n >= 0 && n <= 16 ? kFusedLdsAllReduceByN[n] : kFusedLdsAllReduceKB) * 1024;
     case AR_COLL_ALL_GATHER: return (n >= 0 && n <= 16 ? kFusedLdsAllGatherByN[n] : kFusedLdsAllGatherKB) * 1024;

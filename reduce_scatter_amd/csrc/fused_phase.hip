@@ -18,6 +18,8 @@
 // past a tile's end is fetched twice (by this tile and the next, which runs on
 // another XCD), so the larger the tile, the closer the fetched bytes come to
 // the algorithmic ones.
+#include <cstdlib>
+
 #include "ar_device.hpp"
 #include "ar_kernels.hpp"
 #include "dispatch.hpp"
@@ -111,13 +113,15 @@ __device__ __forceinline__ void rs_phased(const RankTableFor<NR> &t, const Geome
     constexpr int U = PhasedTile<NR>::U;
     const int n = NR > 0 ? NR : g.n;
     const int c = (int)blockIdx.y;
-    const TileSpan ts =
-        aligned_tile(0, g.Rv, (long long)blockIdx.x, (long long)((uintptr_t)t.dst[c] >> 4), kFusedTile * U);
+    // a workgroup of blockDim.x / 64 wavefronts takes that many consecutive tiles, one per wavefront
+    const long long j = (long long)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    const unsigned lane = threadIdx.x & 63u;
+    const TileSpan ts = aligned_tile(0, g.Rv, j, (long long)((uintptr_t)t.dst[c] >> 4), kFusedTile * U);
     if (ts.lo >= ts.hi) return;
     unsigned off[U];
     bool ok[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) off[u] = tile_lane(ts, ts.start + threadIdx.x + u * kFusedTile, ok[u]);
+    for (int u = 0; u < U; ++u) off[u] = tile_lane(ts, ts.start + lane + u * kFusedTile, ok[u]);
     const long long a = g.in_off + (long long)c * g.slice_bytes + ts.lo * 16;     // the tile's first input byte
     const long long rel = g.last_off - (a & ~15LL);                             // last block, from the tile base
     Pack<DT> acc[U];
@@ -139,8 +143,8 @@ __device__ __forceinline__ void rs_phased(const RankTableFor<NR> &t, const Geome
 }
 
 template <int DT, int OP, int NR>
-__global__ __launch_bounds__(kFusedThreads) void fused_reduce_scatter_phased_kernel(const RankTableFor<NR> t,
-                                                                                   const Geometry g) {
+__global__ __launch_bounds__(8 * kFusedThreads) void fused_reduce_scatter_phased_kernel(const RankTableFor<NR> t,
+                                                                                       const Geometry g) {
     if constexpr (DT == BF16 || DT == F16) {
         if (g.acc32) {
             rs_phased<DT, OP, NR, true>(t, g);
@@ -199,15 +203,52 @@ __global__ __launch_bounds__(kFusedThreads) void fused_all_gather_phased_kernel(
     }
 }
 
+// Wavefronts per workgroup of the phased reduce-scatter, and the LDS each
+// workgroup reserves.  The input line where two tiles meet is fetched once per
+// L2 that needs it: with one-wave workgroups neighbouring tiles run on
+// different XCDs and every tile boundary cost a second fetch (1.063x the
+// algorithmic reads with 2 KB tiles); a workgroup of W wavefronts on W
+// consecutive tiles keeps all but its outer boundary inside one L2 (measured
+// FETCH_SIZE at n = 8, R - 1 elements: 1.031x with 2, 1.016x with 4).  With 4
+// wavefronts per workgroup, fewer resident wavefronts win: 12 per compute unit
+// (48 KB per workgroup) up to 4 ranks, 8 (56 KB) beyond.  Measured on MI355X,
+// R - 1 elements per slice, 256 MB in per rank (% of peak, one wave -> four):
+// bf16 n = 2 73.0 -> 74.9, 3 69.9 -> 75.0, 8 70.7 -> 74.3, 12 70.4 -> 72.9,
+// 16 64.0 -> 73.3, 24 41.6 -> 71.3, 72 67.6 -> 76.1; fp32 n = 3 72.1 -> 75.6,
+// 8 71.4 -> 72.1, 13-15 level, 17 40.0 -> 69.3, 32 49.1 -> 73.1; fp32 at 16
+// ranks ran 64.9 with one wave and 60.3 with four, so 4-byte types keep one
+// there.  AR_PHASED_WAVES=1|2|4|8 overrides the count (the LDS then scales
+// the one-wave reservation).
+static void phased_rs_shape(int n, int dt, int lds_one_wave, int &waves, int &lds) {
+    const char *e = getenv("AR_PHASED_WAVES");
+    if (e && (*e == '1' || *e == '2' || *e == '4' || *e == '8')) {
+        waves = *e - '0';
+        lds = lds_one_wave * waves > 65536 ? 65536 : lds_one_wave * waves;
+        return;
+    }
+    const bool four_byte = dt == F32 || dt == I32;
+    if (n == 16 && four_byte) {
+        waves = 1;
+        lds = lds_one_wave;
+        return;
+    }
+    waves = 4;
+    lds = (n <= 4 ? 48 : 56) * 1024;
+}
+
 hipError_t launch_fused_reduce_scatter_phased(int dt, int op, const RankTable &t, const Geometry &g, int lds,
                                               hipStream_t s) {
     if (g.Rv <= 0) return hipSuccess;
+    int waves, lds_wg;
+    phased_rs_shape(g.n, dt, lds, waves, lds_wg);
+    if (getenv("AR_FUSED_LDS_KB") && waves > 1) lds_wg = lds * waves > 65536 ? 65536 : lds * waves;
     return dispatch(dt, op, [&](auto D, auto O) {
         return by_ranks(g.n, [&](auto R) {
             constexpr int NR = decltype(R)::value;
-            const dim3 grid((unsigned)aligned_tiles(g.Rv, (long long)kFusedTile * PhasedTile<NR>::U), (unsigned)g.n);
+            const long long tiles = aligned_tiles(g.Rv, (long long)kFusedTile * PhasedTile<NR>::U);
+            const dim3 grid((unsigned)((tiles + waves - 1) / waves), (unsigned)g.n);
             return launch(fused_reduce_scatter_phased_kernel<decltype(D)::value, decltype(O)::value, NR>,
-                          grid, dim3(kFusedThreads), (size_t)lds, s, narrow<NR>(t), g);
+                          grid, dim3(kFusedThreads * waves), (size_t)lds_wg, s, narrow<NR>(t), g);
         });
     });
 }

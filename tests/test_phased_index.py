@@ -192,3 +192,34 @@ def test_model_notices_planted_mistakes(mistake):
             except AssertionError:
                 failed += 1
     assert failed > 0
+
+
+def phased_rs_waves(n, e):
+    """Wavefronts per workgroup of the library's phased reduce-scatter (4-byte types keep one at 16 ranks)."""
+    return 1 if (n == 16 and e == 4) else 4
+
+
+@pytest.mark.parametrize("waves", [1, 2, 4, 8])
+def test_multi_wave_workgroups_cover_every_tile_once(waves):
+    """A workgroup of W wavefronts takes tiles j = blockIdx.x * W + wave; the grid has ceil(tiles / W)
+    workgroups.  Every tile of the range is taken exactly once and the extra wavefronts of the last
+    workgroup find an empty tile (their first vector lies past the range), so they write nothing."""
+    rnd = random.Random(11 + waves)
+    for _ in range(400):
+        U = rnd.choice([1, 2])
+        T = TILE * U
+        length = rnd.randint(1, 40 * T)
+        ref = rnd.randint(0, 4 * T)
+        tiles = aligned_tiles(length, T)
+        grid = (tiles + waves - 1) // waves
+        covered = np.zeros(length, dtype=np.int64)
+        for bx in range(grid):
+            for w in range(waves):
+                j = bx * waves + w
+                start, lo, hi = aligned_tile(0, length, j, ref, T)
+                if j >= tiles:
+                    assert lo >= hi, (length, ref, T, j)
+                if lo < hi:
+                    covered[lo:hi] += 1
+        assert (covered == 1).all()
+    assert phased_rs_waves(8, 2) == 4 and phased_rs_waves(16, 4) == 1 and phased_rs_waves(16, 2) == 4
