@@ -206,6 +206,20 @@ def kernel_calls(reps=5):
     for sched, kern in (("split", "split_allreduce_kernel"), ("fused", "fused_allreduce_wide_kernel")):
         run("all-reduce n=72 f32 25MB/rank avg in place, %s" % sched, kern, 2 * n72 * c72 * 4,
             lambda: ar.ar_allreduce(bufs, bufs, c72, "f32", "avg", sched=sched))
+    # the LDS-staged tree past 16 ranks, each of its two kernels forced
+    for teams, kern in (("0", "tree_allreduce_kernel"), ("1", "tree_team_kernel")):
+        os.environ["AR_TREE_TEAMS"] = teams
+        run("all-reduce n=72 f32 25MB/rank avg in place, tree (staged, %s)" % ("teams" if teams == "1" else "level by level"),
+            kern, 2 * n72 * c72 * 4, lambda: ar.ar_allreduce(bufs, bufs, c72, "f32", "avg", sched="tree"))
+    del bufs, bufs_t
+    n17, c17 = 17, 128 * MB // 4                            # 17 ranks, 128 MB per rank, in place
+    bufs_t = [wl.device_normal(4, 1, r, c17, 1e-3, "f32") for r in range(n17)]
+    bufs = ar.pointers(bufs_t)
+    for teams, kern in (("0", "tree_allreduce_kernel"), ("1", "tree_team_kernel")):
+        os.environ["AR_TREE_TEAMS"] = teams
+        run("all-reduce n=17 f32 128MB/rank avg in place, tree (staged, %s)" % ("teams" if teams == "1" else "level by level"),
+            kern, 2 * n17 * c17 * 4, lambda: ar.ar_allreduce(bufs, bufs, c17, "f32", "avg", sched="tree"))
+    os.environ.pop("AR_TREE_TEAMS", None)
     del bufs, bufs_t
     torch.cuda.empty_cache()
 
