@@ -62,29 +62,34 @@ def time_call(fn, iters, warmup=2):
     return float(np.median([a.elapsed_time(b) * 1e3 for a, b in ev]))
 
 
-def measure(ns, sizes, iters, rounds=3):
+def measure(ns, sizes, iters, rounds=3, dtype="f32"):
+    """Time every (collective, schedule) at every rank count and per-rank byte
+    size, for element type ``dtype`` (``f32`` or ``bf16``): median over
+    ``rounds`` rounds of the per-call median of ``iters`` calls."""
     import torch
     import reduce_scatter_amd as ar
+    e = 4 if dtype == "f32" else 2
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
     rows = []                                   # (coll, sched, n, per_rank_bytes, us)
     for n in ns:
         for per_rank in sizes:
-            count = per_rank // 4               # fp32
-            if count < n * 4 or n * per_rank > (16 << 30):
+            count = per_rank // e
+            if count < n * (16 // e) or n * per_rank > (16 << 30):
                 continue
-            xs_t = [torch.randn(count, device="cuda") for _ in range(n)]
+            xs_t = [torch.randn(count, device="cuda").to(tdt) for _ in range(n)]
             ys_t = [torch.empty_like(x) for x in xs_t]
             R = count // n
-            outs_t = [torch.empty(R, device="cuda") for _ in range(n)]
+            outs_t = [torch.empty(R, dtype=tdt, device="cuda") for _ in range(n)]
             # host pointer tables built once: the timings are the library's, not Python's marshalling
             xs, ys, outs = ar.pointers(xs_t), ar.pointers(ys_t), ar.pointers(outs_t)
             calls = {}
             for sched in ("ring", "tree", "fused", "split", "dtree"):
-                calls[("allreduce", sched)] = (lambda s=sched: ar.ar_allreduce(xs, ys, count, "f32", "sum", n=n, sched=s))
+                calls[("allreduce", sched)] = (lambda s=sched: ar.ar_allreduce(xs, ys, count, dtype, "sum", n=n, sched=s))
                 if sched in ("tree", "split", "dtree"):
                     continue
                 calls[("reduce_scatter", sched)] = (
-                    lambda s=sched: ar.ar_reduce_scatter(xs, outs, R, "f32", "sum", n=n, sched=s))
-                calls[("all_gather", sched)] = (lambda s=sched: ar.ar_all_gather(outs, ys, R, "f32", n=n, sched=s))
+                    lambda s=sched: ar.ar_reduce_scatter(xs, outs, R, dtype, "sum", n=n, sched=s))
+                calls[("all_gather", sched)] = (lambda s=sched: ar.ar_all_gather(outs, ys, R, dtype, n=n, sched=s))
             # rounds that visit every call in turn, so no schedule always runs right after the same other one
             # (in the Infinity Cache regime the previous call's traffic decides what is cached)
             times = {k: [] for k in calls}
@@ -93,14 +98,18 @@ def measure(ns, sizes, iters, rounds=3):
                     times[k].append(time_call(fn, iters, warmup=1))
             for (coll, sched), v in times.items():
                 rows.append((coll, sched, n, per_rank, float(np.median(v))))
-            print("calibrate: n=%d %d bytes per rank done" % (n, per_rank), flush=True)
+            print("calibrate: %s n=%d %d bytes per rank done" % (dtype, n, per_rank), flush=True)
             del xs, ys, outs, xs_t, ys_t, outs_t
             torch.cuda.empty_cache()
     return rows
 
 
-def fit(rows):
+def fit(rows, latency=None):
     """Per (coll, sched): launch_us, step_us, bw_gbps, corr[SIZE_BINS].
+
+    ``latency``: a fit of another element type whose launch, step and extra
+    latency terms are kept (only the bandwidth terms are fitted here): the
+    2-byte types share the 4-byte types' latency model.
 
     Fitted by regime: launch and per-step costs from the calls that move at
     most 1 MB (pure latency: t = launch + step * steps), the sustained
@@ -118,20 +127,23 @@ def fit(rows):
                 continue
             small_all = [(n, us) for n, pr, us, b in pts if b <= (1 << 20)]
             small = [(n, us) for n, us in small_all if n <= 16]    # the compile-time-n kernels
-            if sched in ("fused", "split") or len({n for n, _ in small}) < 2:
-                launch = float(np.median([us for _, us in small])) if small else 0.0
-                step = 0.0
+            if latency is not None and (coll, sched) in latency:
+                launch, step, _, _, extra = latency[(coll, sched)]
             else:
-                A = np.array([[1.0, _steps(coll, sched, n)] for n, _ in small])
-                t = np.array([us for _, us in small])
-                (launch, step), *_ = np.linalg.lstsq(A, t, rcond=None)
-                launch, step = max(float(launch), 0.0), max(float(step), 0.0)
-            extra = {}                                    # rank class -> latency beyond launch + step * steps
-            for rc in sorted({math.ceil(math.log2(n)) for n, _ in small_all}):
-                res = [us - launch - step * _steps(coll, sched, n) for n, us in small_all
-                       if math.ceil(math.log2(n)) == rc]
-                if abs(float(np.median(res))) > 1.0:
-                    extra[rc] = float(np.median(res))
+                if sched in ("fused", "split") or len({n for n, _ in small}) < 2:
+                    launch = float(np.median([us for _, us in small])) if small else 0.0
+                    step = 0.0
+                else:
+                    A = np.array([[1.0, _steps(coll, sched, n)] for n, _ in small])
+                    t = np.array([us for _, us in small])
+                    (launch, step), *_ = np.linalg.lstsq(A, t, rcond=None)
+                    launch, step = max(float(launch), 0.0), max(float(step), 0.0)
+                extra = {}                                # rank class -> latency beyond launch + step * steps
+                for rc in sorted({math.ceil(math.log2(n)) for n, _ in small_all}):
+                    res = [us - launch - step * _steps(coll, sched, n) for n, us in small_all
+                           if math.ceil(math.log2(n)) == rc]
+                    if abs(float(np.median(res))) > 1.0:
+                        extra[rc] = float(np.median(res))
             big = [(n, us, b) for n, pr, us, b in pts if b >= (1 << 30)]
             ref = big or [(n, us, b) for n, pr, us, b in pts]
             bws = [b / 1e3 / max(us - launch - step * _steps(coll, sched, n), 1e-3) for n, us, b in ref]
@@ -170,19 +182,27 @@ def fit(rows):
     return out
 
 
-def write(path, model, gpu_name):
+def write(path, model, gpu_name, model2=None):
+    """The calibration file: ``model`` fitted on fp32 (every 4-byte type), and
+    ``model2`` (bandwidth terms only) on bf16 for the 2-byte types."""
     with open(path, "w") as f:
         f.write("# cost-model constants for libar (written by reduce_scatter_amd/calibrate.py)\n")
         f.write("# device: %s\n" % gpu_name)
-        f.write("# <coll> <sched> <launch_us> <step_us> <bw_GBps>\n")
+        f.write("# <coll> <sched> <launch_us> <step_us> <bw_GBps>            (fitted on fp32: every 4-byte type)\n")
         f.write("# corr <coll> <sched> <ceil(log2 n)> <bandwidth factor for log2(total algorithmic bytes) = 0..47>\n")
         f.write("# lat <coll> <sched> <ceil(log2 n)> <latency beyond launch + step * steps, us>\n")
+        f.write("# bw2 / corr2: the same bandwidth terms fitted on bf16 (2-byte types; latency terms shared)\n")
         for (coll, sched), (launch, step, bw, corr, extra) in sorted(model.items()):
             f.write("%s %s %.3f %.4f %.1f\n" % (coll, sched, launch, step, bw))
             for rc, row in sorted(corr.items()):
                 f.write("corr %s %s %d %s\n" % (coll, sched, rc, " ".join("%.3f" % c for c in row)))
             for rc, us in sorted(extra.items()):
                 f.write("lat %s %s %d %.3f\n" % (coll, sched, rc, us))
+            if model2 and (coll, sched) in model2:
+                _, _, bw2, corr2, _ = model2[(coll, sched)]
+                f.write("bw2 %s %s %.1f\n" % (coll, sched, bw2))
+                for rc, row in sorted(corr2.items()):
+                    f.write("corr2 %s %s %d %s\n" % (coll, sched, rc, " ".join("%.3f" % c for c in row)))
 
 
 def main(argv=None):
@@ -199,8 +219,11 @@ def main(argv=None):
     sizes = [1 << k for k in ((12, 16, 20, 24, 28) if a.quick else (10, 12, 14, 16, 18, 20, 21, 22, 23, 24, 25, 26, 27, 28, 29, 30))]
     rows = measure(ns, sizes, iters=3 if a.quick else 5)
     model = fit(rows)
+    ns2 = (8,) if a.quick else (2, 4, 8, 16, 72)
+    rows2 = measure(ns2, sizes, iters=3 if a.quick else 5, dtype="bf16")
+    model2 = fit(rows2, latency=model)
     write(a.out, model, torch.cuda.get_device_name(0) + " " + getattr(torch.cuda.get_device_properties(0),
-                                                                      "gcnArchName", ""))
+                                                                      "gcnArchName", ""), model2)
     for (coll, sched), (launch, step, bw, corr, extra) in sorted(model.items()):
         print("%-15s %-6s launch %7.2f us  step %6.3f us  bw %7.1f GB/s  extra %s" % (
             coll, sched, launch, step, bw, {k: round(v, 1) for k, v in extra.items()}))

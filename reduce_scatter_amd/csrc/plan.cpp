@@ -56,10 +56,21 @@ constexpr int kSizeBins = 48;      // per-size correction for log2(algorithmic b
 
 constexpr int kRankClasses = 8;    // ceil(log2 n) = 0..7 for n = 1..128
 
-struct Entry {
-    double launch_us = 0, step_us = 0, bw_gbps = 0;
+// Bandwidth of one element-size class: a sustained rate and the per-(rank
+// class, footprint) correction.  4-byte types (fp32, int32) and 2-byte types
+// (bf16, fp16) have tables of their own: the per-element work differs (bf16 and
+// fp16 partials are rounded at every hop, the ring stages twice the elements
+// per byte through LDS), so schedules that tie in fp32 can differ in bf16.
+struct Bandwidth {
+    double bw_gbps = 0;
     double corr[kRankClasses][kSizeBins];
     bool measured[kRankClasses];       // a corr row was read for this rank class
+};
+
+struct Entry {
+    double launch_us = 0, step_us = 0;
+    Bandwidth b4, b2;                  // 4-byte and 2-byte element types
+    bool have_b2 = false;              // a 2-byte rate was read (else 2-byte calls use b4)
     double extra_us[kRankClasses];     // measured latency beyond launch + step * steps, per rank class
     bool set = false;
 };
@@ -82,12 +93,15 @@ void set_defaults(Calib &c) {
             e.launch_us = 8.0;
             const bool one_pass = s == AR_SCHED_FUSED || s == AR_SCHED_SPLIT;
             e.step_us = one_pass ? 0.0 : 0.25;
-            e.bw_gbps = s == AR_SCHED_FUSED ? 5000.0 : 4000.0;
-            for (int k2 = 0; k2 < kRankClasses; ++k2) {
-                e.measured[k2] = false;
-                e.extra_us[k2] = 0.0;
-                for (int b = 0; b < kSizeBins; ++b) e.corr[k2][b] = 1.0;
+            for (Bandwidth *bw : {&e.b4, &e.b2}) {
+                bw->bw_gbps = s == AR_SCHED_FUSED ? 5000.0 : 4000.0;
+                for (int k2 = 0; k2 < kRankClasses; ++k2) {
+                    bw->measured[k2] = false;
+                    for (int b = 0; b < kSizeBins; ++b) bw->corr[k2][b] = 1.0;
+                }
             }
+            e.have_b2 = false;
+            for (int k2 = 0; k2 < kRankClasses; ++k2) e.extra_us[k2] = 0.0;
             e.set = true;
         }
 }
@@ -122,6 +136,8 @@ std::string library_dir() {
 //   <coll> <sched> <launch_us> <step_us> <bw_gbps>
 //   corr <coll> <sched> <rank class> <corr_0 ... corr_47>
 //   lat <coll> <sched> <rank class> <extra_us>
+//   bw2 <coll> <sched> <bw_gbps>                     (2-byte element types)
+//   corr2 <coll> <sched> <rank class> <corr_0 ... corr_47>
 // coll in {allreduce, reduce_scatter, all_gather}, sched in {ring, tree, fused, split, dtree};
 // rank class = ceil(log2 n); corr_b multiplies the bandwidth for calls that
 // move 2^b .. 2^(b+1)-1 algorithmic bytes in total (the footprint decides
@@ -146,19 +162,29 @@ void load_file(Calib &c, const std::string &path) {
             if (k >= 0 && s >= 0 && rc >= 0 && rc < kRankClasses) c.e[k][s].extra_us[rc] = extra;
             continue;
         }
-        if (sscanf(line, "corr %31s %31s %d%n", coll, sched, &rc, &used) == 3) {
+        if (sscanf(line, "bw2 %31s %31s %lf", coll, sched, &bw) == 3) {
+            int k = coll_index(coll), s = sched_index(sched);
+            if (k >= 0 && s >= 0 && bw > 0) {
+                c.e[k][s].b2.bw_gbps = bw;
+                c.e[k][s].have_b2 = true;
+            }
+            continue;
+        }
+        const bool two = strncmp(line, "corr2 ", 6) == 0;
+        if ((two && sscanf(line, "corr2 %31s %31s %d%n", coll, sched, &rc, &used) == 3) ||
+            (!two && sscanf(line, "corr %31s %31s %d%n", coll, sched, &rc, &used) == 3)) {
             int k = coll_index(coll), s = sched_index(sched);
             if (k < 0 || s < 0 || rc < 0 || rc >= kRankClasses) continue;
-            Entry &e = c.e[k][s];
+            Bandwidth &bt = two ? c.e[k][s].b2 : c.e[k][s].b4;
             const char *p = line + used;
             for (int b = 0; b < kSizeBins; ++b) {
                 double v;
                 int m = 0;
                 if (sscanf(p, "%lf%n", &v, &m) != 1) break;
-                if (v > 0) e.corr[rc][b] = v;
+                if (v > 0) bt.corr[rc][b] = v;
                 p += m;
             }
-            e.measured[rc] = true;
+            bt.measured[rc] = true;
             continue;
         }
         if (sscanf(line, "%31s %31s %lf %lf %lf%n", coll, sched, &lu, &su, &bw, &used) != 5) continue;
@@ -167,7 +193,7 @@ void load_file(Calib &c, const std::string &path) {
         Entry &e = c.e[k][s];
         e.launch_us = lu;
         e.step_us = su;
-        e.bw_gbps = bw;
+        e.b4.bw_gbps = bw;
         ++loaded;
     }
     fclose(f);
@@ -186,13 +212,25 @@ int rank_class(int n) {
     return k < kRankClasses ? k : kRankClasses - 1;
 }
 
-// The measured correction row nearest to rank class k (all ones if none).
-const double *corr_row(const Entry &e, int k) {
+// The measured correction row nearest to rank class k (nullptr if none).
+const double *corr_row(const Bandwidth &b, int k) {
     for (int d = 0; d < kRankClasses; ++d) {
-        if (k - d >= 0 && e.measured[k - d]) return e.corr[k - d];
-        if (k + d < kRankClasses && e.measured[k + d]) return e.corr[k + d];
+        if (k - d >= 0 && b.measured[k - d]) return b.corr[k - d];
+        if (k + d < kRankClasses && b.measured[k + d]) return b.corr[k + d];
     }
-    return e.corr[k];                              // nothing measured: the all-ones defaults
+    return nullptr;
+}
+
+// Bandwidth (GB/s) of schedule entry ``e`` for a call of element size ``elem``
+// bytes, rank class k and footprint bin ``bin``.  2-byte calls take the 2-byte
+// rate when one was measured, with the 2-byte correction (else the 4-byte one);
+// everything else takes the 4-byte table.  A rank class without a row uses the
+// nearest measured one (all ones when none is).
+double bandwidth(const Entry &e, int elem, int k, int bin) {
+    const bool two = elem == 2 && e.have_b2;
+    const double *row = two ? corr_row(e.b2, k) : nullptr;
+    if (!row) row = corr_row(e.b4, k);
+    return (two ? e.b2.bw_gbps : e.b4.bw_gbps) * (row ? row[bin] : 1.0);
 }
 
 int size_bin(double bytes) {
@@ -256,7 +294,7 @@ ar_status_t make_plan(ar_coll_t coll, size_t count, ar_dtype_t dtype, ar_op_t op
         if (!(out->legal_mask & (1u << s))) continue;
         const Entry &c = g_calib.e[coll][s];
         out->bytes[s] = bytes;
-        const double bw = c.bw_gbps * corr_row(c, rclass)[bin];    // GB/s = 1e3 bytes per microsecond
+        const double bw = bandwidth(c, (int)e, rclass, bin);       // GB/s = 1e3 bytes per microsecond
         out->predicted_us[s] = c.launch_us + c.step_us * out->steps[s] + c.extra_us[rclass] + bytes / (bw * 1e3);
         if (!have || out->predicted_us[s] < best) {
             best = out->predicted_us[s];

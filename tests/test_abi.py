@@ -272,6 +272,30 @@ def test_plan_reads_the_calibration_file(tmp_path):
     assert abs(p16["predicted_us"]["fused"] - (5 + b / 1e3 / (500 * 0.5))) < 1e-6
 
 
+def test_plan_uses_the_two_byte_tables_for_bf16_and_fp16(tmp_path):
+    """bw2 / corr2 records price the 2-byte types; 4-byte types keep the main
+    tables, and a schedule without a 2-byte rate falls back to them."""
+    f = tmp_path / "calib.txt"
+    corr2 = ["1.0"] * 48
+    corr2[27] = "0.25"
+    f.write_text("allreduce ring 10 0 1000\nallreduce fused 5 0 1000\nallreduce split 7 0 1000\n"
+                 "allreduce tree 9 0 1000\nallreduce dtree 9 0 1000\n"
+                 "bw2 allreduce fused 2000\ncorr2 allreduce fused 3 " + " ".join(corr2) + "\n"
+                 "bw2 allreduce ring 500\n")
+    b = 1 << 27                                   # 2*n*S at n = 8 for every dtype below
+    calls = [("allreduce", b // (2 * 8 * e), dt, "sum", 8) for dt, e in (("f32", 4), ("i32", 4), ("bf16", 2), ("f16", 2))]
+    p32, pi32, pbf, pf16 = _plan_in_subprocess(str(f), calls)
+    for p in (p32, pi32):
+        assert abs(p["predicted_us"]["fused"] - (5 + b / 1e3 / 1000)) < 1e-6
+        assert abs(p["predicted_us"]["ring"] - (10 + b / 1e3 / 1000)) < 1e-6
+    for p in (pbf, pf16):
+        assert abs(p["predicted_us"]["fused"] - (5 + b / 1e3 / (2000 * 0.25))) < 1e-6
+        # a 2-byte rate without a 2-byte correction row takes the 4-byte one (none here: all ones)
+        assert abs(p["predicted_us"]["ring"] - (10 + b / 1e3 / 500)) < 1e-6
+        # no 2-byte record at all: the 4-byte table
+        assert abs(p["predicted_us"]["split"] - (7 + b / 1e3 / 1000)) < 1e-6
+
+
 def test_plan_rejects_bad_arguments():
     assert _err(ar.ar_plan, "allreduce", 16, "f32", "sum", 0) == "AR_ERR_INVALID_ARG"
     assert _err(ar.ar_plan, 3, 16, "f32", "sum", 4) == "AR_ERR_INVALID_ARG"

@@ -45,3 +45,19 @@ def test_large_footprints_keep_their_own_correction():
     small, big = 1 << 31, 1 << 35                                   # 2 GB and 32 GB of traffic at n = 16
     assert pred(bw_s, corr_s, small) <= 1.02 * pred(bw_f, corr_f, small)   # split as fast as fused at 2 GB
     assert pred(bw_s, corr_s, big) >= 1.15 * pred(bw_f, corr_f, big)       # and priced slower at 32 GB
+
+
+def test_two_byte_fit_keeps_the_latency_terms():
+    """The bf16 fit takes launch, step and extra latency from the fp32 fit and
+    fits only the bandwidth: a type whose rate differs is priced by its own
+    rate with the shared latency model."""
+    rows4 = _rows(False)
+    model4 = cal.fit(rows4)
+    rows2 = [(c, s, n, pr, us + (pr * 2 * n) / 1e3 / 6000.0 * (0.25 if s == "ring" else 0.0))
+             for c, s, n, pr, us in rows4]                 # the ring 25 % slower on the bandwidth term
+    model2 = cal.fit(rows2, latency=model4)
+    for key in model4:
+        assert model2[key][0] == model4[key][0] and model2[key][1] == model4[key][1]
+        assert model2[key][4] == model4[key][4]
+    assert model2[("allreduce", "ring")][2] < model4[("allreduce", "ring")][2]
+    assert abs(model2[("allreduce", "fused")][2] - model4[("allreduce", "fused")][2]) / model4[("allreduce", "fused")][2] < 0.01
