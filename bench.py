@@ -336,7 +336,7 @@ def sweep():
         xs, ys = ar.pointers(xs_t), ar.pointers(ys_t)
         for op in ("sum", "min", "max", "avg"):
             t = _interleaved_us({s: (lambda s=s: ar.ar_allreduce(xs, ys, count, "i32", op, n=n, sched=s))
-                                 for s in ("ring", "tree", "dtree", "fused", "split")})
+                                 for s in ("ring", "tree", "dtree", "fused", "split")}, rounds=5, iters=8)
             plan = ar.ar_plan("allreduce", count, "i32", op, n).chosen
             win = min(t, key=t.get)
             toll = 100.0 * (t[plan] / t[win] - 1.0)

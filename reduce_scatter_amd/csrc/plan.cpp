@@ -43,8 +43,10 @@
 
 static_assert(ar::kTopoRanks == ar::kTableRanks, "tree shapes cover the rank table");
 
-// Predicted-time margin within which the fused schedule is kept (see make_plan).
+// Predicted-time margin within which the fused schedule is kept, for calls
+// whose footprint is at least kHbmBytes (see make_plan).
 constexpr double kTieMargin = 0.03;
+constexpr double kHbmBytes = 1073741824.0;
 
 namespace ar {
 
@@ -302,11 +304,14 @@ ar_status_t make_plan(ar_coll_t coll, size_t count, ar_dtype_t dtype, ar_op_t op
             have = true;
         }
     }
-    // Schedules that move the same bytes in one pass (fused, tree and dtree in registers, split) run within a
-    // few per cent of one another, less than the spread between calibration runs and boxes: the fused
+    // Calls that stream from HBM (a footprint of kHbmBytes or more, four times the 256 MB Infinity Cache):
+    // schedules that move the same bytes in one pass (fused, tree and dtree in registers, split) run within a
+    // few per cent of one another there, less than the spread between calibration runs and boxes, so the fused
     // schedule, whose pass needs no cross-wave exchange, keeps the call unless another is predicted faster by
-    // more than kTieMargin.
-    if (have && out->chosen != AR_SCHED_FUSED && out->predicted_us[AR_SCHED_FUSED] <= best * (1.0 + kTieMargin))
+    // more than kTieMargin.  Below that footprint the differences between them are real (at 16 ranks and 16 MB
+    // per rank, half in the cache, the trees ran 8-12 % ahead of fused on two boxes) and the argmin stands.
+    if (have && out->chosen != AR_SCHED_FUSED && bytes >= kHbmBytes &&
+        out->predicted_us[AR_SCHED_FUSED] <= best * (1.0 + kTieMargin))
         out->chosen = AR_SCHED_FUSED;
     return AR_OK;
 }

@@ -195,11 +195,12 @@ def test_dtree_parent_is_the_complementary_tree():
     assert ar.ar_dtree_parent(8, 2, 1) == -1 and ar.ar_dtree_parent(8, 1, 8) == -1
 
 
-def _expected_choice(pred):
+def _expected_choice(pred, footprint):
     """The cost model's choice: the least predicted time (ties to the lower
-    schedule code), except that fused is kept within 3 % of the least."""
+    schedule code), except that for footprints of 1 GB and more fused is kept
+    within 3 % of the least."""
     best = min(pred, key=lambda s: (pred[s], ar.SCHEDS[s]))
-    if "fused" in pred and pred["fused"] <= pred[best] * 1.03:
+    if footprint >= (1 << 30) and "fused" in pred and pred["fused"] <= pred[best] * 1.03:
         return "fused"
     return best
 
@@ -214,7 +215,7 @@ def test_plan_steps_bytes_and_legality():
         assert p.steps["fused"] == 1 and p.steps["split"] == 1
         assert p.steps["dtree"] == p.steps["tree"]
         assert all(b == 2 * n * count * 4 for b in p.bytes.values())
-        assert p.chosen == _expected_choice(p.predicted_us)
+        assert p.chosen == _expected_choice(p.predicted_us, max(p.bytes.values()))
         for coll in ("reduce_scatter", "all_gather"):
             q = ar.ar_plan(coll, count, "bf16", "avg", n)
             assert q.legal == ["ring", "fused"]
@@ -257,16 +258,20 @@ def test_plan_reads_the_calibration_file(tmp_path):
     assert abs(p["predicted_us"]["tree"] - (20 + 1 * 6 + b / 1e3 / 1000)) < 1e-6
     assert abs(p["predicted_us"]["fused"] - (5 + b / 1e3 / (500 * 0.5))) < 1e-6
     assert abs(p["predicted_us"]["split"] - (7 + 2.5 + b / 1e3 / 400)) < 1e-6
-    assert p["chosen"] == _expected_choice(p["predicted_us"])
-    # the tie margin: fused within 3 % of a faster prediction keeps the call, beyond it does not
+    assert p["chosen"] == _expected_choice(p["predicted_us"], b)
+    # the tie margin, for calls that stream from HBM (footprint >= 1 GB): fused within 3 % of a faster
+    # prediction keeps the call, beyond it does not; below 1 GB the argmin stands
     g = tmp_path / "tie.txt"
     g.write_text("allreduce ring 1000 0 1000\nallreduce tree 1000 0 1000\nallreduce split 1000 0 1000\n"
-                 "allreduce dtree 0 0 1000\nallreduce fused 2 0 1000\n")
-    near, far = _plan_in_subprocess(str(g), [("allreduce", count, "f32", "sum", 8),
-                                             ("allreduce", count // 64, "f32", "sum", 8)])
+                 "allreduce dtree 0 0 1000\nallreduce fused 10 0 1000\n")
+    big = (1 << 30) // (2 * 8 * 4)       # n = 8 fp32: a 1 GB footprint
+    near, far, cache = _plan_in_subprocess(str(g), [("allreduce", big, "f32", "sum", 8),
+                                                    ("allreduce", big // 64, "f32", "sum", 8),
+                                                    ("allreduce", big // 2, "f32", "sum", 8)])
     assert near["chosen"] == "fused" and near["predicted_us"]["dtree"] < near["predicted_us"]["fused"]
     assert near["predicted_us"]["fused"] <= 1.03 * near["predicted_us"]["dtree"]
     assert far["chosen"] == "dtree" and far["predicted_us"]["fused"] > 1.03 * far["predicted_us"]["dtree"]
+    assert cache["predicted_us"]["fused"] <= 1.03 * cache["predicted_us"]["dtree"] and cache["chosen"] == "dtree"
     # a rank class with no row of its own uses the nearest measured one (class 3 for n = 16)
     p16 = _plan_in_subprocess(str(f), [("allreduce", count // 2, "f32", "sum", 16)])[0]
     assert abs(p16["predicted_us"]["fused"] - (5 + b / 1e3 / (500 * 0.5))) < 1e-6
