@@ -47,6 +47,7 @@ static_assert(ar::kTopoRanks == ar::kTableRanks, "tree shapes cover the rank tab
 // whose footprint is at least kHbmBytes (see make_plan).
 constexpr double kTieMargin = 0.03;
 constexpr double kHbmBytes = 1073741824.0;
+constexpr double kTieUs = 0.5;              // ... and within this many microseconds at any footprint
 
 namespace ar {
 
@@ -310,8 +311,11 @@ ar_status_t make_plan(ar_coll_t coll, size_t count, ar_dtype_t dtype, ar_op_t op
     // schedule, whose pass needs no cross-wave exchange, keeps the call unless another is predicted faster by
     // more than kTieMargin.  Below that footprint the differences between them are real (at 16 ranks and 16 MB
     // per rank, half in the cache, the trees ran 8-12 % ahead of fused on two boxes) and the argmin stands.
-    if (have && out->chosen != AR_SCHED_FUSED && bytes >= kHbmBytes &&
-        out->predicted_us[AR_SCHED_FUSED] <= best * (1.0 + kTieMargin))
+    // At every footprint, a predicted advantage under kTieUs is below the launch-to-launch jitter of about a
+    // microsecond (calls under 1 MB per rank all take 8-11 us whatever the schedule), so fused keeps the call.
+    if (have && out->chosen != AR_SCHED_FUSED &&
+        (out->predicted_us[AR_SCHED_FUSED] <= best + kTieUs ||
+         (bytes >= kHbmBytes && out->predicted_us[AR_SCHED_FUSED] <= best * (1.0 + kTieMargin))))
         out->chosen = AR_SCHED_FUSED;
     return AR_OK;
 }

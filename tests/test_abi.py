@@ -197,10 +197,11 @@ def test_dtree_parent_is_the_complementary_tree():
 
 def _expected_choice(pred, footprint):
     """The cost model's choice: the least predicted time (ties to the lower
-    schedule code), except that for footprints of 1 GB and more fused is kept
-    within 3 % of the least."""
+    schedule code), except that fused is kept within 0.5 us of the least, and
+    for footprints of 1 GB and more within 3 %."""
     best = min(pred, key=lambda s: (pred[s], ar.SCHEDS[s]))
-    if footprint >= (1 << 30) and "fused" in pred and pred["fused"] <= pred[best] * 1.03:
+    if "fused" in pred and (pred["fused"] <= pred[best] + 0.5 or
+                            (footprint >= (1 << 30) and pred["fused"] <= pred[best] * 1.03)):
         return "fused"
     return best
 
