@@ -77,40 +77,94 @@ __global__ __launch_bounds__(kFusedThreads) void fused_allreduce_kernel(const Ra
 // long runs per stream, so each lane owns U vectors of the tile spaced by the
 // wavefront width (a 64*U-vector tile: 16 KB per rank for 4-byte types, 8 KB
 // for 2-byte types, which need twice the registers per vector) and the ranks
-// are walked two at a time.  Measured at n = 72 with 25 MB per rank: 65 % of
-// peak HBM bandwidth, against 53 % for one vector per lane.
+// are walked two at a time, each rank's U loads issued as one run before the
+// next rank's (left to the scheduler, the two ranks' loads alternate vector by
+// vector).  Measured at n = 72 with 25 MB per rank: 65 % of peak HBM
+// bandwidth, against 53 % for one vector per lane.
+//
+// A chunk's tiles are whole except its first and last.  A whole tile takes
+// the lean path (every lane's vectors in range, byte offsets lane*16 + u*1024
+// folded into the scalar rank pointer); the edge tiles take the clamped path,
+// with in-tile positions in 32 bits and the range checks as one bit mask, so
+// both fit a wavefront in 256 registers and two wavefronts share a SIMD.
+// Every tile of a 72-rank call is resident at once, so the call lasts as long
+// as its slowest tile: the edge tiles keep the two-rank batches.  Measured at
+// n = 72, 25 MB per rank, fp32 in place: with 64-bit range checks on every
+// tile the kernel needed 260 registers (one wavefront per SIMD) and ran 62 %
+// of peak.
 template <int DT> struct WideTile {
     static constexpr int U = (DT == BF16 || DT == F16) ? 8 : 16;
     static constexpr int B = 2;
 };
 
 template <int DT, int OP, bool KEEP32>
-__device__ __forceinline__ void fused_allreduce_wide(const RankTable &t, const Geometry &g) {
+__device__ __forceinline__ void wide_whole_tile(const RankTable &t, int n, int c, long long base, const Geometry &g) {
     constexpr int U = WideTile<DT>::U, B = WideTile<DT>::B;
-    const int n = g.n;
-    int c;
-    long long j;
-    tile_coords(c, j);
-    long long vend = chunk_start(c + 1, g) - g.shift;
-    vend = vend < g.Vfull ? vend : g.Vfull;
-    const TileSpan ts = aligned_tile(chunk_start(c, g), vend, j, g.ref, kFusedThreads * U);
-    if (ts.lo >= ts.hi) return;
-    unsigned off[U];
-    bool ok[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) off[u] = tile_lane(ts, ts.start + threadIdx.x + u * kFusedThreads, ok[u]);
-    const long long base = ts.lo * 16;
+    const unsigned lane = threadIdx.x * 16u;
     Pack<DT> acc[U];
     for (int k0 = 0; k0 < n; k0 += B) {
+        const char *ptr[B];
+#pragma unroll
+        for (int kk = 0; kk < B; ++kk) ptr[kk] = (const char *)t.src[hop_rank(c, k0 + kk < n ? k0 + kk : n - 1, n)] + base;
+        __builtin_amdgcn_sched_barrier(0);                     // the batch's rank pointers before its loads
         u32x4 raw[B][U];
 #pragma unroll
         for (int kk = 0; kk < B; ++kk) {
-            const int k = k0 + kk < n ? k0 + kk : n - 1;
-            const char *p = (const char *)t.src[hop_rank(c, k, n)] + base;
 #pragma unroll
-            for (int u = 0; u < U; ++u) raw[kk][u] = __builtin_nontemporal_load((const u32x4 *)(p + off[u]));
+            for (int u = 0; u < U; ++u)
+                raw[kk][u] = __builtin_nontemporal_load((const u32x4 *)(ptr[kk] + u * kFusedThreads * 16 + lane));
+            __builtin_amdgcn_sched_barrier(0);                 // one rank's run issued whole before the next
         }
+#pragma unroll
+        for (int kk = 0; kk < B; ++kk) {
+            if (k0 + kk >= n) break;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (k0 + kk == 0) acc[u] = first<DT, OP, KEEP32>(unpack<DT>(raw[kk][u]), g.s);
+                else hop<DT, OP, KEEP32>(acc[u], unpack<DT>(raw[kk][u]), g.s);
+            }
+        }
+    }
+    u32x4 w[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        finish<DT, OP>(acc[u], n, g);
+        w[u] = pack<DT>(acc[u]);
+    }
+    for (int r = 0; r < n; ++r) {
+        char *p = (char *)t.dst[r] + base;
+#pragma unroll
+        for (int u = 0; u < U; ++u) __builtin_nontemporal_store(w[u], (u32x4 *)(p + u * kFusedThreads * 16 + lane));
+    }
+}
+
+template <int DT, int OP, bool KEEP32>
+__device__ __forceinline__ void wide_edge_tile(const RankTable &t, int n, int c, const TileSpan &ts, const Geometry &g) {
+    constexpr int U = WideTile<DT>::U, B = WideTile<DT>::B;
+    // positions inside the tile in 32 bits: the in-range part is [lo, hi) of [0, 64*U)
+    const int lo = (int)(ts.lo - ts.start), hi = (int)(ts.hi - ts.start);
+    unsigned off[U];
+    unsigned okm = 0;                                          // bit u: vector u of this lane is in range
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int v = (int)threadIdx.x + u * kFusedThreads;
+        okm |= (unsigned)(v >= lo && v < hi) << u;
+        off[u] = (unsigned)((v < lo ? lo : (v >= hi ? hi - 1 : v)) - lo) * 16u;
+    }
+    const long long base = ts.lo * 16;
+    Pack<DT> acc[U];
+    for (int k0 = 0; k0 < n; k0 += B) {
+        const char *ptr[B];
+#pragma unroll
+        for (int kk = 0; kk < B; ++kk) ptr[kk] = (const char *)t.src[hop_rank(c, k0 + kk < n ? k0 + kk : n - 1, n)] + base;
         __builtin_amdgcn_sched_barrier(0);
+        u32x4 raw[B][U];
+#pragma unroll
+        for (int kk = 0; kk < B; ++kk) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) raw[kk][u] = __builtin_nontemporal_load((const u32x4 *)(ptr[kk] + off[u]));
+            __builtin_amdgcn_sched_barrier(0);
+        }
 #pragma unroll
         for (int kk = 0; kk < B; ++kk) {
             if (k0 + kk >= n) break;
@@ -131,19 +185,52 @@ __device__ __forceinline__ void fused_allreduce_wide(const RankTable &t, const G
         char *p = (char *)t.dst[r] + base;
 #pragma unroll
         for (int u = 0; u < U; ++u)
-            if (ok[u]) __builtin_nontemporal_store(w[u], (u32x4 *)(p + off[u]));
+            if ((okm >> u) & 1u) __builtin_nontemporal_store(w[u], (u32x4 *)(p + off[u]));
     }
 }
 
+// The wide kernel's grid is one workgroup per piece, a piece being one tile
+// of one chunk (a tile across a chunk boundary is two pieces), numbered in
+// address order: first[c] is the number of pieces before chunk c.  Workgroups
+// are dealt to the 8 XCDs round robin, and every piece of a 72-rank call is
+// resident at once, so the busiest XCD sets the time: a grid of n rows of
+// equal length, the shorter chunks' rows padded with empty workgroups, left
+// some XCDs 5 % more tiles than others (measured at n = 72, 25 MB per rank:
+// 65 % of peak against 69 % for the same tiles without the holes).
+struct WidePieces {
+    unsigned first[kTableRanks + 1];
+};
+
+template <int DT, int OP, bool KEEP32>
+__device__ __forceinline__ void fused_allreduce_wide(const RankTable &t, const Geometry &g, const WidePieces &pc) {
+    constexpr long long T = (long long)kFusedThreads * WideTile<DT>::U;
+    const unsigned p = blockIdx.x;
+    int lo = 0, hi = g.n;                                      // the chunk c with first[c] <= p < first[c+1]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (pc.first[mid] <= p) lo = mid;
+        else hi = mid;
+    }
+    const int c = lo;
+    const long long j = (long long)(p - pc.first[c]);
+    long long vend = chunk_start(c + 1, g) - g.shift;
+    vend = vend < g.Vfull ? vend : g.Vfull;
+    const TileSpan ts = aligned_tile(chunk_start(c, g), vend, j, g.ref, T);
+    if (ts.lo >= ts.hi) return;
+    if (ts.lo == ts.start && ts.hi == ts.start + T) wide_whole_tile<DT, OP, KEEP32>(t, g.n, c, ts.lo * 16, g);
+    else wide_edge_tile<DT, OP, KEEP32>(t, g.n, c, ts, g);
+}
+
 template <int DT, int OP>
-__global__ __launch_bounds__(kFusedThreads) void fused_allreduce_wide_kernel(const RankTable t, const Geometry g) {
+__global__ __launch_bounds__(kFusedThreads) void fused_allreduce_wide_kernel(const RankTable t, const Geometry g,
+                                                                             const WidePieces pc) {
     if constexpr (DT == BF16 || DT == F16) {
         if (g.acc32) {
-            fused_allreduce_wide<DT, OP, true>(t, g);
+            fused_allreduce_wide<DT, OP, true>(t, g, pc);
             return;
         }
     }
-    fused_allreduce_wide<DT, OP, false>(t, g);
+    fused_allreduce_wide<DT, OP, false>(t, g, pc);
 }
 
 // All-gather: input vector v of piece k is read once and written to vector
@@ -182,19 +269,34 @@ __global__ __launch_bounds__(kFusedThreads) void fused_all_gather_kernel(const R
         if (ok[u]) store_all<NR>(t, n, ((long long)k * g.Rv + ts.lo) * 16, off[u], w[u]);
 }
 
-// Tiles per chunk of the wide (n > 16) all-reduce kernel.
-long long fused_wide_windows(int dt, long long maxlen) {
-    const long long tile = kFusedThreads * ((dt == BF16 || dt == F16) ? WideTile<BF16>::U : WideTile<F32>::U);
-    return aligned_tiles(maxlen, tile);
+// Pieces of the wide (n > 16) all-reduce kernel: chunk c's frame vectors
+// [chunk_start(c), min(chunk_start(c+1) - shift, Vfull)) cut on the tile grid
+// aligned to ``ref``.  Returns the total, or -1 past the grid's x limit.
+long long wide_pieces(int dt, const Geometry &g, WidePieces &pc) {
+    const long long T = kFusedThreads * ((dt == BF16 || dt == F16) ? WideTile<BF16>::U : WideTile<F32>::U);
+    auto start = [&](int c) { return (long long)c * g.q + (g.rem ? ((long long)c * g.rem) / g.n : 0); };
+    long long total = 0;
+    for (int c = 0; c < g.n; ++c) {
+        pc.first[c] = (unsigned)total;
+        const long long lo = start(c);
+        long long hi = start(c + 1) - g.shift;
+        hi = hi < g.Vfull ? hi : g.Vfull;
+        if (hi > lo) total += (g.ref + hi + T - 1) / T - (g.ref + lo) / T;     // ref + lo >= 0
+        if (total > 0x7fffffffLL) return -1;
+    }
+    for (int c = g.n; c <= kTableRanks; ++c) pc.first[c] = (unsigned)total;
+    return total;
 }
 
 hipError_t launch_fused_allreduce(int dt, int op, const RankTable &t, const Geometry &g, int lds, hipStream_t s) {
     if (g.n > 16) {
-        const long long maxlen = (g.V + g.n - 1) / g.n;
-        const dim3 grid((unsigned)fused_wide_windows(dt, maxlen), (unsigned)g.n);
+        WidePieces pc;
+        const long long pieces = wide_pieces(dt, g, pc);
+        if (pieces < 0) return hipErrorInvalidValue;
+        if (pieces == 0) return hipSuccess;
         return dispatch(dt, op, [&](auto D, auto O) {
-            return launch(fused_allreduce_wide_kernel<decltype(D)::value, decltype(O)::value>, grid,
-                          dim3(kFusedThreads), (size_t)lds, s, t, g);
+            return launch(fused_allreduce_wide_kernel<decltype(D)::value, decltype(O)::value>, dim3((unsigned)pieces),
+                          dim3(kFusedThreads), (size_t)lds, s, t, g, pc);
         });
     }
     const dim3 grid((unsigned)g.windows, (unsigned)g.n);

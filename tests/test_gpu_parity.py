@@ -287,6 +287,37 @@ def test_tiles_cut_on_an_aligned_grid(dtype):
                     assert_bits_equal(to_host(g_out[r], dtype), gathered[r], "ag %s n=%d %s" % (sched, n, label))
 
 
+WIDE_CASES = [("f32", "avg"), ("bf16", "sum"), ("f16", "avg"), ("i32", "avg"), ("f32", "max")]
+
+
+@pytest.mark.parametrize("dtype,op", WIDE_CASES)
+def test_wide_fused_whole_and_edge_tiles(dtype, op):
+    """Past 16 ranks the fused all-reduce cuts each chunk into tiles of 64*U
+    vectors (U = 16 for 4-byte types, 8 for 2-byte ones): whole tiles take a
+    path without range checks, a chunk's first and last tiles the clamped one.
+    Chunks here span several whole tiles and end off the tile grid, with the
+    grid shifted by the buffers' offset; every element of every rank is
+    compared, in place and out of place."""
+    u = LANES[dtype]
+    tile_elems = 64 * (16 if u == 4 else 8) * u
+    for n in (17, 72):
+        count = n * (3 * tile_elems + 1000) + 7
+        xs = inputs(31, n, count, dtype, op)
+        ref = oracle.ring_allreduce(xs, dtype, op)
+        for label, off in (("aligned", 0), ("off the tile grid", 48), ("mixed", None)):
+            offsets = [16 * (r % 7) for r in range(n)] if off is None else [off] * n
+            print("wide fused", dtype, op, n, label, flush=True)
+            d_in = [_at_offset(x, dtype, o) for x, o in zip(xs, offsets)]
+            d_out = [_empty_at_offset(count, dtype, (o + 32) % 1024) for o in offsets]
+            ar.ar_allreduce(d_in, d_out, count, dtype, op, sched="fused")
+            ar.ar_allreduce(d_in, d_in, count, dtype, op, sched="fused")              # in place
+            sync()
+            for r in range(n):
+                assert_bits_equal(to_host(d_out[r], dtype), ref[r], "n=%d %s rank %d" % (n, label, r))
+                assert_bits_equal(to_host(d_in[r], dtype), ref[r], "n=%d %s rank %d in place" % (n, label, r))
+            del d_in, d_out
+
+
 NUMERICS = [("storage", "split"), ("fp32", "prescale"), ("fp32", "split")]
 
 
