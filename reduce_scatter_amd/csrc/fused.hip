@@ -189,14 +189,144 @@ __device__ __forceinline__ void wide_edge_tile(const RankTable &t, int n, int c,
     }
 }
 
-// The wide kernel's grid is one workgroup per piece, a piece being one tile
-// of one chunk (a tile across a chunk boundary is two pieces), numbered in
-// address order: first[c] is the number of pieces before chunk c.  Workgroups
-// are dealt to the 8 XCDs round robin, and every piece of a 72-rank call is
-// resident at once, so the busiest XCD sets the time: a grid of n rows of
-// equal length, the shorter chunks' rows padded with empty workgroups, left
-// some XCDs 5 % more tiles than others (measured at n = 72, 25 MB per rank:
-// 65 % of peak against 69 % for the same tiles without the holes).
+// A tile across the boundary of chunks c and c+1 holds the end of chunk c
+// (hop order c+1, c+2, ..., c) and the start of chunk c+1 (c+2, ..., c, c+1):
+// the same ranks, one step apart.  So one workgroup walks the rank sequence
+// c+1, ..., c, c+1 (n+1 loads) over the whole tile: lanes of chunk c take
+// steps 0..n-1, lanes of chunk c+1 steps 1..n, each its own chunk's exact
+// order.  Measured at n = 72, 25 MB per rank (chunk boundaries off the tile
+// grid): two partial-tile workgroups per boundary, each as long as a whole
+// tile, had held the kernel at 64-65 % of peak against 68-70 % with the
+// boundaries on the grid.
+template <int DT, int OP, bool KEEP32>
+__device__ __forceinline__ void wide_shared_tile(const RankTable &t, int n, int c, long long ts, long long b,
+                                                 const Geometry &g) {
+    constexpr int U = WideTile<DT>::U, B = WideTile<DT>::B;
+    const unsigned lane = threadIdx.x * 16u;
+    const long long base = ts * 16;
+    const int bb = (int)(b - ts);                              // chunk c+1 starts at vector bb of the tile
+    unsigned upper = 0, skip = 0;                              // bit u: vector u of this lane is chunk c+1's;
+#pragma unroll                                                 // ... is the shifted frame's vector b-1 (no chunk's)
+    for (int u = 0; u < U; ++u) {
+        const int v = (int)threadIdx.x + u * kFusedThreads;
+        upper |= (unsigned)(v >= bb) << u;
+        skip |= (unsigned)(g.shift != 0 && v == bb - 1) << u;
+    }
+    Pack<DT> acc[U];
+    {                                                          // steps 0 and 1
+        const char *p0 = (const char *)t.src[hop_rank(c, 0, n)] + base;
+        const char *p1 = (const char *)t.src[hop_rank(c, 1, n)] + base;
+        __builtin_amdgcn_sched_barrier(0);
+        u32x4 r0[U], r1[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) r0[u] = __builtin_nontemporal_load((const u32x4 *)(p0 + u * kFusedThreads * 16 + lane));
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < U; ++u) r1[u] = __builtin_nontemporal_load((const u32x4 *)(p1 + u * kFusedThreads * 16 + lane));
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            Pack<DT> lower = first<DT, OP, KEEP32>(unpack<DT>(r0[u]), g.s);
+            hop<DT, OP, KEEP32>(lower, unpack<DT>(r1[u]), g.s);
+            const Pack<DT> up = first<DT, OP, KEEP32>(unpack<DT>(r1[u]), g.s);
+            const bool sel = (upper >> u) & 1u;
+#pragma unroll
+            for (int e = 0; e < Pack<DT>::K; ++e) acc[u].v[e] = sel ? up.v[e] : lower.v[e];   // per lane, no memory
+        }
+    }
+    for (int k0 = 2; k0 < n; k0 += B) {                        // steps 2..n-1: every lane
+        const char *ptr[B];
+#pragma unroll
+        for (int kk = 0; kk < B; ++kk) ptr[kk] = (const char *)t.src[hop_rank(c, k0 + kk < n ? k0 + kk : n - 1, n)] + base;
+        __builtin_amdgcn_sched_barrier(0);
+        u32x4 raw[B][U];
+#pragma unroll
+        for (int kk = 0; kk < B; ++kk) {
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                raw[kk][u] = __builtin_nontemporal_load((const u32x4 *)(ptr[kk] + u * kFusedThreads * 16 + lane));
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int kk = 0; kk < B; ++kk) {
+            if (k0 + kk >= n) break;
+#pragma unroll
+            for (int u = 0; u < U; ++u) hop<DT, OP, KEEP32>(acc[u], unpack<DT>(raw[kk][u]), g.s);
+        }
+    }
+    {                                                          // step n: chunk c+1's last hop (rank c+1)
+        const char *pn = (const char *)t.src[hop_rank(c, n, n)] + base;
+        __builtin_amdgcn_sched_barrier(0);
+        u32x4 rn[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) rn[u] = __builtin_nontemporal_load((const u32x4 *)(pn + u * kFusedThreads * 16 + lane));
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            Pack<DT> h = acc[u];
+            hop<DT, OP, KEEP32>(h, unpack<DT>(rn[u]), g.s);
+            const bool sel = (upper >> u) & 1u;
+#pragma unroll
+            for (int e = 0; e < Pack<DT>::K; ++e) acc[u].v[e] = sel ? h.v[e] : acc[u].v[e];
+        }
+    }
+    u32x4 w[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        finish<DT, OP>(acc[u], n, g);
+        w[u] = pack<DT>(acc[u]);
+    }
+    for (int r = 0; r < n; ++r) {
+        char *p = (char *)t.dst[r] + base;
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (!((skip >> u) & 1u)) __builtin_nontemporal_store(w[u], (u32x4 *)(p + u * kFusedThreads * 16 + lane));
+    }
+}
+
+// Chunk geometry of the wide kernel, shared by the host (the grid) and the
+// device.  Chunk c is frame vectors [lo, hi): the floor cut, less the shifted
+// frame's last vector, clamped to Vfull.  c * rem < 128 * 128 fits 32 bits.
+__host__ __device__ inline long long wide_chunk_start(int c, const Geometry &g) {
+    const long long b = (long long)c * g.q;
+    return g.rem ? b + (long long)((unsigned)(c * g.rem) / (unsigned)g.n) : b;
+}
+
+__host__ __device__ inline void wide_chunk(int c, const Geometry &g, long long &lo, long long &hi) {
+    lo = wide_chunk_start(c, g);
+    hi = wide_chunk_start(c + 1, g) - g.shift;
+    hi = hi < g.Vfull ? hi : g.Vfull;
+}
+
+// Tiles of the ref-aligned T-vector grid that overlap [lo, hi).
+__host__ __device__ inline long long wide_tiles(const Geometry &g, long long lo, long long hi, long long T) {
+    return hi > lo ? (g.ref + hi + T - 1) / T - (g.ref + lo) / T : 0;
+}
+
+// Whether the tile across the boundary of chunks c and c+1 is one shared
+// unit: whole, inside [0, Vfull), holding vectors of both chunks and of no
+// other.  ts: its first vector.
+__host__ __device__ inline bool wide_shared(int c, const Geometry &g, long long T, long long &ts) {
+    if (c + 1 >= g.n) return false;
+    const long long b = wide_chunk_start(c + 1, g);
+    const long long m = (g.ref + b) & (T - 1);
+    if (m <= g.shift) return false;                            // on the grid, or chunk c's part of it is empty
+    ts = b - m;
+    long long lo, hi, lo1, hi1;
+    wide_chunk(c, g, lo, hi);
+    wide_chunk(c + 1, g, lo1, hi1);
+    return ts >= lo && ts + T <= hi1;
+}
+
+// The wide kernel's grid is one workgroup per unit, numbered in address
+// order: a unit is one tile of one chunk, except that a shared boundary tile
+// (above) is one unit, counted with the lower chunk; first[c] is the number
+// of units before chunk c.  Workgroups are dealt to the 8 XCDs round robin,
+// and every unit of a 72-rank call is resident at once, so the busiest XCD
+// sets the time: a grid of n rows of equal length, the shorter chunks' rows
+// padded with empty workgroups, left some XCDs 5 % more tiles than others
+// (measured at n = 72, 25 MB per rank: 65 % of peak against 69 % for the same
+// tiles without the holes).
 struct WidePieces {
     unsigned first[kTableRanks + 1];
 };
@@ -212,13 +342,18 @@ __device__ __forceinline__ void fused_allreduce_wide(const RankTable &t, const G
         else hi = mid;
     }
     const int c = lo;
-    const long long j = (long long)(p - pc.first[c]);
-    long long vend = chunk_start(c + 1, g) - g.shift;
-    vend = vend < g.Vfull ? vend : g.Vfull;
-    const TileSpan ts = aligned_tile(chunk_start(c, g), vend, j, g.ref, T);
-    if (ts.lo >= ts.hi) return;
-    if (ts.lo == ts.start && ts.hi == ts.start + T) wide_whole_tile<DT, OP, KEEP32>(t, g.n, c, ts.lo * 16, g);
-    else wide_edge_tile<DT, OP, KEEP32>(t, g.n, c, ts, g);
+    long long cl, ch, ts;
+    wide_chunk(c, g, cl, ch);
+    long long j = (long long)(p - pc.first[c]);
+    if (c > 0 && wide_shared(c - 1, g, T, ts)) ++j;            // the first tile went with chunk c-1
+    if (j == wide_tiles(g, cl, ch, T) - 1 && wide_shared(c, g, T, ts)) {
+        wide_shared_tile<DT, OP, KEEP32>(t, g.n, c, ts, wide_chunk_start(c + 1, g), g);
+        return;
+    }
+    const TileSpan tsp = aligned_tile(cl, ch, j, g.ref, T);
+    if (tsp.lo >= tsp.hi) return;
+    if (tsp.lo == tsp.start && tsp.hi == tsp.start + T) wide_whole_tile<DT, OP, KEEP32>(t, g.n, c, tsp.lo * 16, g);
+    else wide_edge_tile<DT, OP, KEEP32>(t, g.n, c, tsp, g);
 }
 
 template <int DT, int OP>
@@ -269,19 +404,16 @@ __global__ __launch_bounds__(kFusedThreads) void fused_all_gather_kernel(const R
         if (ok[u]) store_all<NR>(t, n, ((long long)k * g.Rv + ts.lo) * 16, off[u], w[u]);
 }
 
-// Pieces of the wide (n > 16) all-reduce kernel: chunk c's frame vectors
-// [chunk_start(c), min(chunk_start(c+1) - shift, Vfull)) cut on the tile grid
-// aligned to ``ref``.  Returns the total, or -1 past the grid's x limit.
+// Units of the wide (n > 16) all-reduce kernel, first[c] per chunk (see
+// WidePieces).  Returns the total, or -1 past the grid's x limit.
 long long wide_pieces(int dt, const Geometry &g, WidePieces &pc) {
     const long long T = kFusedThreads * ((dt == BF16 || dt == F16) ? WideTile<BF16>::U : WideTile<F32>::U);
-    auto start = [&](int c) { return (long long)c * g.q + (g.rem ? ((long long)c * g.rem) / g.n : 0); };
-    long long total = 0;
+    long long total = 0, ts;
     for (int c = 0; c < g.n; ++c) {
         pc.first[c] = (unsigned)total;
-        const long long lo = start(c);
-        long long hi = start(c + 1) - g.shift;
-        hi = hi < g.Vfull ? hi : g.Vfull;
-        if (hi > lo) total += (g.ref + hi + T - 1) / T - (g.ref + lo) / T;     // ref + lo >= 0
+        long long lo, hi;
+        wide_chunk(c, g, lo, hi);
+        total += wide_tiles(g, lo, hi, T) - ((c > 0 && wide_shared(c - 1, g, T, ts)) ? 1 : 0);
         if (total > 0x7fffffffLL) return -1;
     }
     for (int c = g.n; c <= kTableRanks; ++c) pc.first[c] = (unsigned)total;

@@ -291,31 +291,37 @@ WIDE_CASES = [("f32", "avg"), ("bf16", "sum"), ("f16", "avg"), ("i32", "avg"), (
 
 
 @pytest.mark.parametrize("dtype,op", WIDE_CASES)
-def test_wide_fused_whole_and_edge_tiles(dtype, op):
-    """Past 16 ranks the fused all-reduce cuts each chunk into tiles of 64*U
-    vectors (U = 16 for 4-byte types, 8 for 2-byte ones): whole tiles take a
-    path without range checks, a chunk's first and last tiles the clamped one.
-    Chunks here span several whole tiles and end off the tile grid, with the
-    grid shifted by the buffers' offset; every element of every rank is
-    compared, in place and out of place."""
+def test_wide_fused_whole_shared_and_edge_tiles(dtype, op):
+    """Past 16 ranks the fused all-reduce cuts the chunks on a grid of 64*U
+    vector tiles (U = 16 for 4-byte types, 8 for 2-byte ones): whole tiles
+    inside a chunk, shared tiles across a chunk boundary (one workgroup walks
+    both chunks' hop orders), and partial tiles at the buffer ends or where a
+    tile holds three or more chunks.  Chunks of several tiles, of 1.5 tiles
+    and of a third of a tile; the grid shifted by the buffers' offset; every
+    buffer at one 16-byte phase (the shifted frame, whose vector across each
+    chunk boundary goes to the element-wise kernel); every element of every
+    rank, in place and out of place."""
     u = LANES[dtype]
+    e = 4 if u == 4 else 2
     tile_elems = 64 * (16 if u == 4 else 8) * u
+    layouts = (("aligned", lambda n: [0] * n), ("off the tile grid", lambda n: [48] * n),
+               ("mixed", lambda n: [16 * (r % 7) for r in range(n)]), ("one phase", lambda n: [48 + e] * n))
     for n in (17, 72):
-        count = n * (3 * tile_elems + 1000) + 7
-        xs = inputs(31, n, count, dtype, op)
-        ref = oracle.ring_allreduce(xs, dtype, op)
-        for label, off in (("aligned", 0), ("off the tile grid", 48), ("mixed", None)):
-            offsets = [16 * (r % 7) for r in range(n)] if off is None else [off] * n
-            print("wide fused", dtype, op, n, label, flush=True)
-            d_in = [_at_offset(x, dtype, o) for x, o in zip(xs, offsets)]
-            d_out = [_empty_at_offset(count, dtype, (o + 32) % 1024) for o in offsets]
-            ar.ar_allreduce(d_in, d_out, count, dtype, op, sched="fused")
-            ar.ar_allreduce(d_in, d_in, count, dtype, op, sched="fused")              # in place
-            sync()
-            for r in range(n):
-                assert_bits_equal(to_host(d_out[r], dtype), ref[r], "n=%d %s rank %d" % (n, label, r))
-                assert_bits_equal(to_host(d_in[r], dtype), ref[r], "n=%d %s rank %d in place" % (n, label, r))
-            del d_in, d_out
+        for count in (n * (3 * tile_elems + 1000) + 7, n * (3 * tile_elems // 2) + 13, n * (tile_elems // 3) + 5):
+            xs = inputs(31, n, count, dtype, op)
+            ref = oracle.ring_allreduce(xs, dtype, op)
+            for label, offs in layouts:
+                offsets = offs(n)
+                print("wide fused", dtype, op, n, count, label, flush=True)
+                d_in = [_at_offset(x, dtype, o) for x, o in zip(xs, offsets)]
+                d_out = [_empty_at_offset(count, dtype, (o + 32) % 1024) for o in offsets]
+                ar.ar_allreduce(d_in, d_out, count, dtype, op, sched="fused")
+                ar.ar_allreduce(d_in, d_in, count, dtype, op, sched="fused")          # in place
+                sync()
+                for r in range(n):
+                    assert_bits_equal(to_host(d_out[r], dtype), ref[r], "n=%d %d %s rank %d" % (n, count, label, r))
+                    assert_bits_equal(to_host(d_in[r], dtype), ref[r], "n=%d %d %s rank %d in place" % (n, count, label, r))
+                del d_in, d_out
 
 
 NUMERICS = [("storage", "split"), ("fp32", "prescale"), ("fp32", "split")]
