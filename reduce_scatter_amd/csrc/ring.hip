@@ -232,17 +232,25 @@ __global__ __launch_bounds__(kThreads) void ring_all_gather_kernel(const RankTab
 // ---------------------------------------------------------------------------
 template <int NR> __device__ __forceinline__ int wrap_c(int a) { return (a + NR) % NR; }
 
-// Vectors per rank in one window: 64 (1 KB pieces, as wide as a wavefront's
-// 16-byte access) up to 8 ranks, 32 beyond, which keeps the workgroup at 512
-// threads or fewer.  Threads per workgroup = NR * window.  (64 vectors for
-// 9-16 ranks, 576-1024 threads per workgroup, fits the registers up to 15
-// ranks, but measured on MI355X it ran far slower: 16 ranks int32 at 64 MB
-// per rank 64.9 -> 55.2 % of peak, 12 ranks fp32 at 128 MB 66.8 -> 50.5 %;
-// fewer windows are resident per compute unit, and each window's 2(n-1)
-// barriers span twice the wavefronts.)
-template <int NR> struct RingShape {
-    static constexpr int W = NR > 8 ? 32 : 64;
-    static constexpr int T = NR * W;
+// Window shape: W vectors per rank, each wavefront holding one rank's share
+// of the window (64 threads per rank) or, with two items per thread, two
+// ranks' shares (ranks rr and rr + R2, R2 = ceil(n/2) wavefronts).
+// Workgroups stay at 512 threads or fewer.  Measured on MI355X (% of peak):
+//   * up to 8 ranks, W = 64 (1 KB runs), one item per thread;
+//   * 9-16 ranks, W = 32 (512-byte runs), one item per thread.  W = 64 with
+//     one item per thread (1024-thread workgroups) ran slower (16 ranks int32
+//     at 64 MB per rank 64.9 -> 55.2, 12 ranks fp32 at 128 MB 66.8 -> 50.5:
+//     fewer windows resident per compute unit, and each window's 2(n-1)
+//     barriers span 16 wavefronts);
+//   * the all-reduce at 16 ranks: W = 64 with two items per thread (16 int32
+//     at 1 GB per rank 61 -> 68, fp32 at 64 MB 71 -> 73).  The same shape lost
+//     4-10 points for the all-reduce at 10-14 ranks and 4 for the all-gather
+//     at 16, and left the reduce-scatter level, so only this case has it.
+template <int NR, bool AR> struct RingShape {
+    static constexpr int IPT = (AR && NR == 16) ? 2 : 1;      // items (ranks) per thread
+    static constexpr int W = (IPT == 2 || NR <= 8) ? 64 : 32;
+    static constexpr int R2 = (NR + IPT - 1) / IPT;            // rows of W threads (rank shares)
+    static constexpr int T = R2 * W;
 };
 
 // chunk c of an all-reduce in vectors: [start(c), min(start(c+1), Vfull))
@@ -252,41 +260,50 @@ __device__ __forceinline__ long long ring_chunk_start(int c, const Geometry &g) 
 }
 
 template <int DT, int OP, int NR>
-__global__ __launch_bounds__(RingShape<NR>::T) void ring_allreduce_fast(const RankTableFor<NR> t, const Geometry g) {
-    constexpr int W = RingShape<NR>::W;
+__global__ __launch_bounds__((RingShape<NR, true>::T)) void ring_allreduce_fast(const RankTableFor<NR> t, const Geometry g) {
+    using RS = RingShape<NR, true>;
+    constexpr int W = RS::W, IPT = RS::IPT, R2 = RS::R2;
     __shared__ u32x4 slot[NR * W];                 // the wire: one slot per chunk and vector
-    const int r = threadIdx.x / W, w = threadIdx.x % W;
-    u32x4 raw[NR];
-    long long vv[NR];
-    bool ok[NR];
+    const int rr = threadIdx.x / W, w = threadIdx.x % W;
+    u32x4 raw[IPT][NR];
+    long long vv[IPT][NR];
+    bool ok[IPT][NR];
 #pragma unroll
-    for (int p = 0; p < NR; ++p) {                 // step p: rank r handles chunk (r-1-p) mod n
-        const int c = wrap_c<NR>(r - 1 - p);
-        long long e = ring_chunk_start(c + 1, g) - g.shift;
-        e = e < g.Vfull ? e : g.Vfull;
-        // window blockIdx.x of chunk c, cut on the W-vector grid of rank 0's output addresses
-        const TileSpan ts = aligned_tile(ring_chunk_start(c, g), e, blockIdx.x, g.ref, W);
-        const long long v = ts.start + w;
-        ok[p] = v >= ts.lo && v < ts.hi;
-        vv[p] = ok[p] ? v : 0;                     // an always-valid address for lanes outside the chunk
-        raw[p] = ld_stream(t.src[r], vv[p]);
+    for (int i = 0; i < IPT; ++i) {
+        const bool has = rr + i * R2 < NR;         // no second item for the last wavefront at odd n
+        const int r = has ? rr + i * R2 : 0;
+#pragma unroll
+        for (int p = 0; p < NR; ++p) {             // step p: rank r handles chunk (r-1-p) mod n
+            const int c = wrap_c<NR>(r - 1 - p);
+            long long e = ring_chunk_start(c + 1, g) - g.shift;
+            e = e < g.Vfull ? e : g.Vfull;
+            // window blockIdx.x of chunk c, cut on the W-vector grid of rank 0's output addresses
+            const TileSpan ts = aligned_tile(ring_chunk_start(c, g), e, blockIdx.x, g.ref, W);
+            const long long v = ts.start + w;
+            ok[i][p] = has && v >= ts.lo && v < ts.hi;
+            vv[i][p] = ok[i][p] ? v : 0;           // an always-valid address for lanes outside the chunk
+            raw[i][p] = ld_stream(t.src[r], vv[i][p]);
+        }
     }
     __builtin_amdgcn_sched_barrier(0);
     // reduce-scatter half: send, n-2 x receive-reduce-send, receive-reduce-copy-send with the postOp
 #pragma unroll
     for (int p = 0; p < NR; ++p) {
-        const int c = wrap_c<NR>(r - 1 - p);
-        if (ok[p]) {
+#pragma unroll
+        for (int i = 0; i < IPT; ++i) {
+            const int r = rr + i * R2;
+            const int c = wrap_c<NR>(r - 1 - p);
+            if (!ok[i][p]) continue;
             Pack<DT> acc;
             if (p == 0) {
-                acc = first<DT, OP>(unpack<DT>(raw[p]), g.s);
+                acc = first<DT, OP>(unpack<DT>(raw[i][p]), g.s);
             } else {
                 acc = unpack<DT>(slot[c * W + w]);
-                hop<DT, OP>(acc, unpack<DT>(raw[p]), g.s);
+                hop<DT, OP>(acc, unpack<DT>(raw[i][p]), g.s);
             }
             if (p == NR - 1) {                     // chunk r completes here: postOp, keep it
                 finish<DT, OP>(acc, NR, g);
-                st_stream(t.dst[r], vv[p], pack<DT>(acc));
+                st_stream(t.dst[r], vv[i][p], pack<DT>(acc));
             }
             slot[c * W + w] = pack<DT>(acc);
         }
@@ -295,44 +312,57 @@ __global__ __launch_bounds__(RingShape<NR>::T) void ring_allreduce_fast(const Ra
     // all-gather half: at step p rank r receives finished chunk (r-1-p) mod n and keeps it
 #pragma unroll
     for (int p = 0; p < NR - 1; ++p) {
-        const int c = wrap_c<NR>(r - 1 - p);
-        if (ok[p]) st_stream(t.dst[r], vv[p], slot[c * W + w]);
+#pragma unroll
+        for (int i = 0; i < IPT; ++i) {
+            const int r = rr + i * R2;
+            const int c = wrap_c<NR>(r - 1 - p);
+            if (ok[i][p]) st_stream(t.dst[r], vv[i][p], slot[c * W + w]);
+        }
     }
 }
 
 template <int DT, int OP, int NR>
-__global__ __launch_bounds__(RingShape<NR>::T) void ring_reduce_scatter_fast(const RankTableFor<NR> t, const Geometry g) {
-    constexpr int W = RingShape<NR>::W;
+__global__ __launch_bounds__((RingShape<NR, false>::T)) void ring_reduce_scatter_fast(const RankTableFor<NR> t, const Geometry g) {
+    using RS = RingShape<NR, false>;
+    constexpr int W = RS::W, IPT = RS::IPT, R2 = RS::R2;
     __shared__ u32x4 slot[NR * W];
-    const int r = threadIdx.x / W, w = threadIdx.x % W;
-    u32x4 raw[NR];
-    long long vpos[NR];
-    bool ok[NR];
+    const int rr = threadIdx.x / W, w = threadIdx.x % W;
+    u32x4 raw[IPT][NR];
+    long long vpos[IPT][NR];
+    bool ok[IPT][NR];
 #pragma unroll
-    for (int p = 0; p < NR; ++p) {
-        const int c = wrap_c<NR>(r - 1 - p);
-        // window blockIdx.x of slice c, cut on the W-vector grid of rank 0's input addresses
-        const TileSpan ts = aligned_tile(0, g.Rv, blockIdx.x, g.ref + (long long)c * g.Rv, W);
-        const long long v = ts.start + w;
-        ok[p] = v >= ts.lo && v < ts.hi;
-        vpos[p] = ok[p] ? v : 0;
-        raw[p] = ld_stream(t.src[r], (long long)c * g.Rv + vpos[p]);
+    for (int i = 0; i < IPT; ++i) {
+        const bool has = rr + i * R2 < NR;
+        const int r = has ? rr + i * R2 : 0;
+#pragma unroll
+        for (int p = 0; p < NR; ++p) {
+            const int c = wrap_c<NR>(r - 1 - p);
+            // window blockIdx.x of slice c, cut on the W-vector grid of rank 0's input addresses
+            const TileSpan ts = aligned_tile(0, g.Rv, blockIdx.x, g.ref + (long long)c * g.Rv, W);
+            const long long v = ts.start + w;
+            ok[i][p] = has && v >= ts.lo && v < ts.hi;
+            vpos[i][p] = ok[i][p] ? v : 0;
+            raw[i][p] = ld_stream(t.src[r], (long long)c * g.Rv + vpos[i][p]);
+        }
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int p = 0; p < NR; ++p) {
-        const int c = wrap_c<NR>(r - 1 - p);
-        if (ok[p]) {
+#pragma unroll
+        for (int i = 0; i < IPT; ++i) {
+            const int r = rr + i * R2;
+            const int c = wrap_c<NR>(r - 1 - p);
+            if (!ok[i][p]) continue;
             Pack<DT> acc;
             if (p == 0) {
-                acc = first<DT, OP>(unpack<DT>(raw[p]), g.s);
+                acc = first<DT, OP>(unpack<DT>(raw[i][p]), g.s);
             } else {
                 acc = unpack<DT>(slot[c * W + w]);
-                hop<DT, OP>(acc, unpack<DT>(raw[p]), g.s);
+                hop<DT, OP>(acc, unpack<DT>(raw[i][p]), g.s);
             }
             if (p == NR - 1) {
                 finish<DT, OP>(acc, NR, g);
-                st_stream(t.dst[r], vpos[p], pack<DT>(acc));
+                st_stream(t.dst[r], vpos[i][p], pack<DT>(acc));
             } else {
                 slot[c * W + w] = pack<DT>(acc);
             }
@@ -342,10 +372,11 @@ __global__ __launch_bounds__(RingShape<NR>::T) void ring_reduce_scatter_fast(con
 }
 
 template <int NR>
-__global__ __launch_bounds__(RingShape<NR>::T) void ring_all_gather_fast(const RankTableFor<NR> t, const Geometry g) {
-    constexpr int W = RingShape<NR>::W;
+__global__ __launch_bounds__((RingShape<NR, false>::T)) void ring_all_gather_fast(const RankTableFor<NR> t, const Geometry g) {
+    using RS = RingShape<NR, false>;
+    constexpr int W = RS::W, IPT = RS::IPT, R2 = RS::R2;
     __shared__ u32x4 slot[NR * W];
-    const int r = threadIdx.x / W, w = threadIdx.x % W;
+    const int rr = threadIdx.x / W, w = threadIdx.x % W;
     // window blockIdx.x of piece k, cut on the W-vector grid of rank 0's output addresses
     auto at = [&](int k, bool &ok) {
         const TileSpan ts = aligned_tile(0, g.Rv, blockIdx.x, g.ref + (long long)k * g.Rv, W);
@@ -353,27 +384,37 @@ __global__ __launch_bounds__(RingShape<NR>::T) void ring_all_gather_fast(const R
         ok = v >= ts.lo && v < ts.hi;
         return v;
     };
-    bool mine_ok;
-    const long long mine = at(r, mine_ok);
-    if (mine_ok) {
-        const u32x4 x = ((const u32x4 *)t.src[r])[mine];   // an ordinary load, as the fused all-gather's input
-        slot[r * W + w] = x;
-        st_stream(t.dst[r], (long long)r * g.Rv + mine, x);                // keep my own piece
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) {
+        const int r = rr + i * R2;
+        if (r >= NR) continue;
+        bool mine_ok;
+        const long long mine = at(r, mine_ok);
+        if (mine_ok) {
+            const u32x4 x = ((const u32x4 *)t.src[r])[mine];   // an ordinary load, as the fused all-gather's input
+            slot[r * W + w] = x;
+            st_stream(t.dst[r], (long long)r * g.Rv + mine, x);            // keep my own piece
+        }
     }
     __syncthreads();
 #pragma unroll
     for (int p = 0; p < NR - 1; ++p) {
-        const int c = wrap_c<NR>(r - 1 - p);                              // received from rank r-1
-        bool ok;
-        const long long v = at(c, ok);
-        if (ok) st_stream(t.dst[r], (long long)c * g.Rv + v, slot[c * W + w]);
+#pragma unroll
+        for (int i = 0; i < IPT; ++i) {
+            const int r = rr + i * R2;
+            if (r >= NR) continue;
+            const int c = wrap_c<NR>(r - 1 - p);                          // received from rank r-1
+            bool ok;
+            const long long v = at(c, ok);
+            if (ok) st_stream(t.dst[r], (long long)c * g.Rv + v, slot[c * W + w]);
+        }
     }
 }
 
 // Windows of the fast kernels (one workgroup each): enough aligned W-vector
 // windows for the longest chunk or slice, whatever its alignment.
 long long ring_fast_windows(const Geometry &g, bool allreduce) {
-    const long long W = g.n > 8 ? 32 : 64;
+    const long long W = ((allreduce && g.n == 16) || g.n <= 8) ? 64 : 32;      // RingShape<n, allreduce>::W
     const long long len = allreduce ? (g.V + g.n - 1) / g.n : g.Rv;
     return aligned_tiles(len, W);
 }
@@ -404,7 +445,7 @@ hipError_t launch_ring_allreduce(int dt, int op, const RankTable &t, const Geome
         return dispatch(dt, op, [&](auto D, auto O) {
             return ring_by_ranks(g.n, [&](auto R) {
                 return launch(ring_allreduce_fast<decltype(D)::value, decltype(O)::value, decltype(R)::value>,
-                              blocks, dim3(RingShape<decltype(R)::value>::T), (size_t)lds, s,
+                              blocks, dim3(RingShape<decltype(R)::value, true>::T), (size_t)lds, s,
                               narrow<decltype(R)::value>(t), g);
             });
         });
@@ -422,7 +463,7 @@ hipError_t launch_ring_reduce_scatter(int dt, int op, const RankTable &t, const 
         return dispatch(dt, op, [&](auto D, auto O) {
             return ring_by_ranks(g.n, [&](auto R) {
                 return launch(ring_reduce_scatter_fast<decltype(D)::value, decltype(O)::value, decltype(R)::value>,
-                              blocks, dim3(RingShape<decltype(R)::value>::T), (size_t)lds, s,
+                              blocks, dim3(RingShape<decltype(R)::value, false>::T), (size_t)lds, s,
                               narrow<decltype(R)::value>(t), g);
             });
         });
@@ -437,7 +478,7 @@ hipError_t launch_ring_all_gather(const RankTable &t, const Geometry &g, int gri
     if (ring_fast_ranks(g.n)) {
         const dim3 blocks((unsigned)ring_fast_windows(g, false));
         return ring_by_ranks(g.n, [&](auto R) {
-            return launch(ring_all_gather_fast<decltype(R)::value>, blocks, dim3(RingShape<decltype(R)::value>::T),
+            return launch(ring_all_gather_fast<decltype(R)::value>, blocks, dim3(RingShape<decltype(R)::value, false>::T),
                           (size_t)lds, s, narrow<decltype(R)::value>(t), g);
         });
     }
