@@ -307,16 +307,21 @@ ar_status_t make_plan(ar_coll_t coll, size_t count, ar_dtype_t dtype, ar_op_t op
     }
     // Calls that stream from HBM (a footprint of kHbmBytes or more, four times the 256 MB Infinity Cache):
     // schedules that move the same bytes in one pass (fused, tree and dtree in registers, split) run within a
-    // few per cent of one another there, less than the spread between calibration runs and boxes, so the fused
-    // schedule, whose pass needs no cross-wave exchange, keeps the call unless another is predicted faster by
-    // more than kTieMargin.  Below that footprint the differences between them are real (at 16 ranks and 16 MB
-    // per rank, half in the cache, the trees ran 8-12 % ahead of fused on two boxes) and the argmin stands.
-    // At every footprint, a predicted advantage under kTieUs is below the launch-to-launch jitter of about a
-    // microsecond (calls under 1 MB per rank all take 8-11 us whatever the schedule), so fused keeps the call.
-    if (have && out->chosen != AR_SCHED_FUSED &&
-        (out->predicted_us[AR_SCHED_FUSED] <= best + kTieUs ||
-         (bytes >= kHbmBytes && out->predicted_us[AR_SCHED_FUSED] <= best * (1.0 + kTieMargin))))
-        out->chosen = AR_SCHED_FUSED;
+    // few per cent of one another there, less than the spread between calibration runs and boxes, so one
+    // preferred schedule keeps the call unless another is predicted faster by more than kTieMargin.  Below
+    // that footprint the differences between them are real (at 16 ranks and 16 MB per rank, half in the cache,
+    // the trees ran 8-12 % ahead of fused on two boxes) and the argmin stands.  At every footprint, a
+    // predicted advantage under kTieUs is below the launch-to-launch jitter of about a microsecond (calls
+    // under 1 MB per rank all take 8-11 us whatever the schedule), so the preferred schedule keeps the call.
+    // The preferred schedule is fused, whose pass needs no cross-wave exchange, up to 16 ranks, and split past
+    // 16 where it is legal: there the two differ by less than the buffers' layout moves either (72 ranks,
+    // 25 MB per rank, the same box: 67-77 % of peak for split and 67-73 % for fused across five layouts), and
+    // on the bucketed gradient layout split ran ahead on two boxes of three (by 1-6 %).
+    const ar_sched_t pref = (n > 16 && (out->legal_mask & (1u << AR_SCHED_SPLIT))) ? AR_SCHED_SPLIT : AR_SCHED_FUSED;
+    if (have && out->chosen != pref &&
+        (out->predicted_us[pref] <= best + kTieUs ||
+         (bytes >= kHbmBytes && out->predicted_us[pref] <= best * (1.0 + kTieMargin))))
+        out->chosen = pref;
     return AR_OK;
 }
 

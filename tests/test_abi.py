@@ -195,14 +195,16 @@ def test_dtree_parent_is_the_complementary_tree():
     assert ar.ar_dtree_parent(8, 2, 1) == -1 and ar.ar_dtree_parent(8, 1, 8) == -1
 
 
-def _expected_choice(pred, footprint):
+def _expected_choice(pred, footprint, n):
     """The cost model's choice: the least predicted time (ties to the lower
-    schedule code), except that fused is kept within 0.5 us of the least, and
-    for footprints of 1 GB and more within 3 %."""
+    schedule code), except that the preferred schedule (split past 16 ranks
+    where legal, else fused) is kept within 0.5 us of the least, and for
+    footprints of 1 GB and more within 3 %."""
     best = min(pred, key=lambda s: (pred[s], ar.SCHEDS[s]))
-    if "fused" in pred and (pred["fused"] <= pred[best] + 0.5 or
-                            (footprint >= (1 << 30) and pred["fused"] <= pred[best] * 1.03)):
-        return "fused"
+    pref = "split" if n > 16 and "split" in pred else "fused"
+    if pref in pred and (pred[pref] <= pred[best] + 0.5 or
+                         (footprint >= (1 << 30) and pred[pref] <= pred[best] * 1.03)):
+        return pref
     return best
 
 
@@ -216,7 +218,7 @@ def test_plan_steps_bytes_and_legality():
         assert p.steps["fused"] == 1 and p.steps["split"] == 1
         assert p.steps["dtree"] == p.steps["tree"]
         assert all(b == 2 * n * count * 4 for b in p.bytes.values())
-        assert p.chosen == _expected_choice(p.predicted_us, max(p.bytes.values()))
+        assert p.chosen == _expected_choice(p.predicted_us, max(p.bytes.values()), n)
         for coll in ("reduce_scatter", "all_gather"):
             q = ar.ar_plan(coll, count, "bf16", "avg", n)
             assert q.legal == ["ring", "fused"]
@@ -259,7 +261,7 @@ def test_plan_reads_the_calibration_file(tmp_path):
     assert abs(p["predicted_us"]["tree"] - (20 + 1 * 6 + b / 1e3 / 1000)) < 1e-6
     assert abs(p["predicted_us"]["fused"] - (5 + b / 1e3 / (500 * 0.5))) < 1e-6
     assert abs(p["predicted_us"]["split"] - (7 + 2.5 + b / 1e3 / 400)) < 1e-6
-    assert p["chosen"] == _expected_choice(p["predicted_us"], b)
+    assert p["chosen"] == _expected_choice(p["predicted_us"], b, 8)
     # the tie margin, for calls that stream from HBM (footprint >= 1 GB): fused within 3 % of a faster
     # prediction keeps the call, beyond it does not; below 1 GB the argmin stands
     g = tmp_path / "tie.txt"
@@ -273,6 +275,15 @@ def test_plan_reads_the_calibration_file(tmp_path):
     assert near["predicted_us"]["fused"] <= 1.03 * near["predicted_us"]["dtree"]
     assert far["chosen"] == "dtree" and far["predicted_us"]["fused"] > 1.03 * far["predicted_us"]["dtree"]
     assert cache["predicted_us"]["fused"] <= 1.03 * cache["predicted_us"]["dtree"] and cache["chosen"] == "dtree"
+    # past 16 ranks split is the schedule the margin keeps: fused predicted 2 % faster than split at 72 ranks
+    h = tmp_path / "tie72.txt"
+    h.write_text("allreduce ring 1000 0 1000\nallreduce tree 1000 0 1000\nallreduce dtree 1000 0 1000\n"
+                 "allreduce fused 0 0 1000\nallreduce split 0 0 980\n")
+    c72 = (1 << 30) // (2 * 72 * 4) + 64   # n = 72 fp32: a footprint just over 1 GB
+    p72, p8 = _plan_in_subprocess(str(h), [("allreduce", c72, "f32", "avg", 72), ("allreduce", big, "f32", "sum", 8)])
+    assert p72["predicted_us"]["fused"] < p72["predicted_us"]["split"] <= 1.03 * p72["predicted_us"]["fused"]
+    assert p72["chosen"] == "split" and p8["chosen"] == "fused"
+    assert p72["chosen"] == _expected_choice(p72["predicted_us"], max(p72["bytes"].values()), 72)
     # a rank class with no row of its own uses the nearest measured one (class 3 for n = 16)
     p16 = _plan_in_subprocess(str(f), [("allreduce", count // 2, "f32", "sum", 16)])[0]
     assert abs(p16["predicted_us"]["fused"] - (5 + b / 1e3 / (500 * 0.5))) < 1e-6
