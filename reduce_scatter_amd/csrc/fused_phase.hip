@@ -27,6 +27,33 @@
 
 namespace ar {
 
+// The vector of lane + 1, and ``last`` in lane 63: lane 0's value is replaced
+// by ``last`` and the wavefront rotated left by one lane (ds_bpermute: each
+// lane reads another lane's register through the LDS crossbar, no LDS
+// memory).  The exchange runs with every lane active: a lane reading from a
+// lane that is switched off gets zero, and selecting ``last`` after the read
+// let the compiler switch lane 63 off for it (lane 62 then read zeros).
+__device__ __forceinline__ u32x4 next_lane(u32x4 v, u32x4 last, bool first_lane) {
+    const int src = (int)((((threadIdx.x & 63u) + 1u) & 63u) << 2);   // byte address of lane + 1 mod 64
+    const u32x4 w = first_lane ? last : v;
+    u32x4 r;
+    r.x = (unsigned)__builtin_amdgcn_ds_bpermute(src, (int)w.x);
+    r.y = (unsigned)__builtin_amdgcn_ds_bpermute(src, (int)w.y);
+    r.z = (unsigned)__builtin_amdgcn_ds_bpermute(src, (int)w.z);
+    r.w = (unsigned)__builtin_amdgcn_ds_bpermute(src, (int)w.w);
+    return r;
+}
+
+// Lane 0's vector, in every lane.
+__device__ __forceinline__ u32x4 lane0(u32x4 v) {
+    u32x4 r;
+    r.x = (unsigned)__builtin_amdgcn_readlane((int)v.x, 0);
+    r.y = (unsigned)__builtin_amdgcn_readlane((int)v.y, 0);
+    r.z = (unsigned)__builtin_amdgcn_readlane((int)v.z, 0);
+    r.w = (unsigned)__builtin_amdgcn_readlane((int)v.w, 0);
+    return r;
+}
+
 // Combine the n ranks' 16 bytes at byte ``base + lane_off[u] + ph`` (u < U;
 // ``base`` a multiple of 16, the same for the whole workgroup, and so is the
 // phase ``ph``) in the hop order of chunk c into acc[u].  Each lane loads the
@@ -40,10 +67,48 @@ namespace ar {
 // MI355X, the clamp's separate address on every tile cost the n = 8 bf16
 // reduce-scatter 13 % (5.5 -> 4.8 TB/s).  NR == 0 (any n): U = 1, ranks in
 // batches of 8.
-template <int DT, int OP, int NR, bool KEEP32, bool CLAMP, int U, class TAB>
+//
+// NEXT (whole tiles away from the input's end only; a uniform choice): lane l's
+// second vector is lane l+1's first, taken from its register (next_lane),
+// lane 63's is lane 0's first of the next run, or for the last run one more
+// load at the same address in every lane (one line): each rank costs U + 1
+// load instructions instead of 2U, and the cache serves one request per line
+// instead of two.  Measured on MI355X with R - 1 elements per slice, 256 MB in
+// per rank: n = 8 fp32 72.1 -> 76.3-76.6 % of peak, n = 16 bf16 72.6 -> 74 %,
+// n = 8 bf16 and n = 3 level.  The any-n chain (one vector per lane, past 16
+// ranks) and the phased all-gather measured level or slower with it and keep
+// both loads.
+template <int DT, int OP, int NR, bool KEEP32, bool CLAMP, int U, class TAB, bool NEXT = false>
 __device__ __forceinline__ void chain_phased(const TAB &t, int n, int c, long long base, const unsigned (&lane_off)[U],
                                              const unsigned (&hi_off)[U], unsigned ph, float s, Pack<DT> (&acc)[U]) {
-    if constexpr (NR > 0) {
+    static_assert(!(NEXT && CLAMP), "the register neighbour needs the unclamped layout");
+    static_assert(!(NEXT && NR == 0), "the any-n chain loads both vectors");
+    const bool lane0_ = (threadIdx.x & 63u) == 0u;
+    if constexpr (NR > 0 && NEXT) {
+        const void *ptr[NR];
+#pragma unroll
+        for (int k = 0; k < NR; ++k) ptr[k] = t.src[hop_rank(c, k, NR)];
+        __builtin_amdgcn_sched_barrier(0);
+        u32x4 lo[NR][U], ex[NR];
+#pragma unroll
+        for (int k = 0; k < NR; ++k) {
+            const char *p = (const char *)ptr[k] + base;
+#pragma unroll
+            for (int u = 0; u < U; ++u) lo[k][u] = __builtin_nontemporal_load((const u32x4 *)(p + lane_off[u]));
+            ex[k] = *(const u32x4 *)(p + kFusedTile * U * 16);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+            for (int k = 0; k < NR; ++k) {
+                const u32x4 hi = next_lane(lo[k][u], u + 1 < U ? lane0(lo[k][u + 1 < U ? u + 1 : u]) : ex[k], lane0_);
+                const Pack<DT> x = unpack<DT>(funnel16(lo[k][u], hi, ph));
+                if (k == 0) acc[u] = first<DT, OP, KEEP32>(x, s);
+                else hop<DT, OP, KEEP32>(acc[u], x, s);
+            }
+        }
+    } else if constexpr (NR > 0) {
         const void *ptr[NR];                 // every rank pointer's scalar load issued before the vector loads
 #pragma unroll
         for (int k = 0; k < NR; ++k) ptr[k] = t.src[hop_rank(c, k, NR)];
@@ -125,7 +190,11 @@ __device__ __forceinline__ void rs_phased(const RankTableFor<NR> &t, const Geome
     const long long a = g.in_off + (long long)c * g.slice_bytes + ts.lo * 16;     // the tile's first input byte
     const long long rel = g.last_off - (a & ~15LL);                             // last block, from the tile base
     Pack<DT> acc[U];
-    if (rel >= 16 * (kFusedTile * U + 1)) {  // no lane's second vector can pass the input's last block
+    const bool whole = ts.lo == ts.start && ts.hi == ts.start + kFusedTile * U;
+    if (NR > 0 && whole && rel >= 16 * (kFusedTile * U + 1)) {   // the neighbour's vector from its register
+        chain_phased<DT, OP, NR, KEEP32, false, U, RankTableFor<NR>, (NR > 0)>(t, n, c, a & ~15LL, off, off,
+                                                                               (unsigned)(a & 15), g.s, acc);
+    } else if (rel >= 16 * (kFusedTile * U + 1)) {  // no lane's second vector can pass the input's last block
         chain_phased<DT, OP, NR, KEEP32, false, U>(t, n, c, a & ~15LL, off, off, (unsigned)(a & 15), g.s, acc);
     } else {                                 // the input's last tiles: the second load clamped (a uniform branch)
         unsigned hi_off[U];
