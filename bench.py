@@ -200,6 +200,14 @@ def kernel_calls(reps=5):
         run("all-gather n=8 bf16 R=%d%s" % (r_, tag), kern, (n + 1) * n * r_ * 2,
             lambda: ar.ar_all_gather(ys, full, r_, "bf16", sched="fused"))
     del xs, ys, full, xs_t, ys_t, full_t
+    n16, c16 = 16, 256 * MB // 4                            # the int32 sweep's ranks, 256 MB per rank
+    xs_t = [torch.randint(-(1 << 20), 1 << 20, (c16,), dtype=torch.int32, device="cuda") for _ in range(n16)]
+    ys_t = [torch.empty(c16, dtype=torch.int32, device="cuda") for _ in range(n16)]
+    xs, ys = ar.pointers(xs_t), ar.pointers(ys_t)
+    for sched, kern in (("fused", "fused_allreduce_kernel"), ("ring", "ring_allreduce_fast")):
+        run("all-reduce n=16 i32 256MB/rank sum, %s" % sched, kern, 2 * n16 * c16 * 4,
+            lambda: ar.ar_allreduce(xs, ys, c16, "i32", "sum", sched=sched))
+    del xs, ys, xs_t, ys_t
     n72, c72 = 72, 25 * MB // 4                             # 72 ranks, one 25 MB fp32 bucket, in place
     bufs_t = [wl.device_normal(4, 1, r, c72, 1e-3, "f32") for r in range(n72)]
     bufs = ar.pointers(bufs_t)
