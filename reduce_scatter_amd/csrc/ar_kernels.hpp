@@ -208,11 +208,14 @@ constexpr int kFusedLdsAllGatherKB = 64;
 // Default dynamic-LDS reservation of the compile-time-n ring workgroups, in
 // KB (on top of their static LDS).
 constexpr int kRingLdsKB = 0;
-// The all-reduce ring by n: 48 KB (two workgroups of n waves per CU) for
-// n = 4 and 6-8, where fewer resident windows kept DRAM access local
-// (measured on MI355X at 128 MB per rank: n = 4 5.50 -> 5.99 TB/s, n = 8
-// 5.56 -> 5.73); none elsewhere, where every cap measured level or slower.
-constexpr int kRingLdsAllReduceByN[17] = {0, 0, 0, 0, 48, 0, 48, 48, 48, 0, 0, 0, 0, 0, 0, 0, 0};
+// The all-reduce ring by n, where fewer resident windows kept DRAM access
+// local: 24 KB at n = 3, 32 KB at n = 4, 48 KB at n = 5-8, none at n = 2 and
+// past 8, where every cap measured level or slower.  Measured on MI355X, fp32,
+// 128-256 MB per rank, % of peak in two passes over separate processes:
+// n = 3 76.1 -> 77.9 (24 KB), n = 4 76.8 -> 78.9 (32 KB, against 48), n = 5
+// 69.5 -> 70.7-71.3 (48 KB), n = 8 70.2 -> 74.3 (48 KB); n = 2 uncapped 79-80
+// (a cap cost it up to 38 points); n = 12 level at every cap.
+constexpr int kRingLdsAllReduceByN[17] = {0, 0, 0, 24, 32, 48, 48, 48, 48, 0, 0, 0, 0, 0, 0, 0, 0};
 constexpr int kRingLdsAllGatherKB = 0;
 // Ring/tree kernels: at most this many (rank, vector) items per thread.
 constexpr int kItemsPerThread = 4;
