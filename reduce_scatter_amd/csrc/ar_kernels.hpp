@@ -188,10 +188,13 @@ constexpr int kFusedTile = kFusedThreads;
 // (caps the resident workgroups per CU; see fused.hip and api.cpp).  The
 // all-reduce's reservation grows with the rank count (indexed by n <= 16):
 // every resident wave has 2n DRAM streams open, and the best number of
-// resident waves per CU falls as n grows, to about 50 / n (26 at n = 2, 11 at
+// resident waves per CU falls as n grows, to about 50 / n (20 at n = 2, 13 at
 // n = 4, 6 at n = 8, 4 at n = 16; measured on MI355X at 128 MB - 1 GB per
-// rank, every n from 2 to 16).
-constexpr int kFusedLdsAllReduceByN[17] = {0, 0, 6, 10, 14, 16, 20, 22, 24, 28, 32, 34, 36, 38, 40, 40, 40};
+// rank, every n from 2 to 16; n = 2 and 4 re-swept at 256 MB per rank in two
+// passes: 8 KB at n = 2 79.2-79.9 % of peak against 77.2-77.5 % at 6 KB, 12 KB
+// at n = 4 82.8-83.1 % against 81.0-81.7 % at 14 KB; n = 3, 5-7, 12 and 16 at
+// their best already).
+constexpr int kFusedLdsAllReduceByN[17] = {0, 0, 8, 10, 12, 16, 20, 22, 24, 28, 32, 34, 36, 38, 40, 40, 40};
 // The reduce-scatter (n loads, one store per lane) and the all-gather (one
 // load, n stores) likewise, from the same kind of sweep (128 MB per rank on
 // the big side): reduce-scatter best at 0 KB for n = 2, 14 KB for n = 6-8,
