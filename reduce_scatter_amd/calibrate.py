@@ -72,19 +72,34 @@ def measure(ns, sizes, iters, rounds=3, dtype="f32"):
     tdt = torch.float32 if dtype == "f32" else torch.bfloat16
     rows = []                                   # (coll, sched, n, per_rank_bytes, us)
     for n in ns:
-        for per_rank in sizes:
+        for size in sizes:
+            # past 16 ranks, sizes of 3/4 of a power of two: buffers whose size and stride are powers of two put
+            # the same offset of every rank on the same memory channels, which the split schedule (every rank at
+            # one offset at a time) pays for and ranks do not in practice (gradient buckets have any size); at
+            # 72 ranks on one box fused ran 2-4 % ahead of split at 2^22 elements per rank and 1-5 % behind at
+            # the bucketed workload's sizes
+            per_rank = size * 3 // 4 // 16 * 16 if n > 16 else size
             count = per_rank // e
             if count < n * (16 // e) or n * per_rank > (16 << 30):
                 continue
-            xs_t = [torch.randn(count, device="cuda").to(tdt) for _ in range(n)]
+            if n > 16:
+                # many-rank all-reduces are gradient buckets: each rank's buffer a view into a larger flat gradient
+                # buffer, reduced in place (see ar_out); on one box the all-reduce at 72 ranks ranked fused ahead
+                # of split by 2 % with buffers of their own and split ahead by 4 % with views of a flat buffer
+                flat_t = [torch.randn(2 * count + 1040, device="cuda").to(tdt) for _ in range(n)]
+                xs_t = [f[count // 2 + 1040:count // 2 + 1040 + count] for f in flat_t]
+            else:
+                xs_t = [torch.randn(count, device="cuda").to(tdt) for _ in range(n)]
             ys_t = [torch.empty_like(x) for x in xs_t]
             R = count // n
             outs_t = [torch.empty(R, dtype=tdt, device="cuda") for _ in range(n)]
             # host pointer tables built once: the timings are the library's, not Python's marshalling
             xs, ys, outs = ar.pointers(xs_t), ar.pointers(ys_t), ar.pointers(outs_t)
             calls = {}
+            # past 16 ranks the all-reduce is timed in place, on views of a flat gradient buffer (above)
+            ar_out = xs if n > 16 else ys
             for sched in ("ring", "tree", "fused", "split", "dtree"):
-                calls[("allreduce", sched)] = (lambda s=sched: ar.ar_allreduce(xs, ys, count, dtype, "sum", n=n, sched=s))
+                calls[("allreduce", sched)] = (lambda s=sched: ar.ar_allreduce(xs, ar_out, count, dtype, "sum", n=n, sched=s))
                 if sched in ("tree", "split", "dtree"):
                     continue
                 calls[("reduce_scatter", sched)] = (
@@ -100,6 +115,7 @@ def measure(ns, sizes, iters, rounds=3, dtype="f32"):
                 rows.append((coll, sched, n, per_rank, float(np.median(v))))
             print("calibrate: %s n=%d %d bytes per rank done" % (dtype, n, per_rank), flush=True)
             del xs, ys, outs, xs_t, ys_t, outs_t
+            flat_t = None
             torch.cuda.empty_cache()
     return rows
 

@@ -315,8 +315,8 @@ ar_status_t make_plan(ar_coll_t coll, size_t count, ar_dtype_t dtype, ar_op_t op
     // under 1 MB per rank all take 8-11 us whatever the schedule), so the preferred schedule keeps the call.
     // The preferred schedule is fused, whose pass needs no cross-wave exchange, up to 16 ranks, and split past
     // 16 where it is legal: there the two differ by less than the allocation moves either (72 ranks, 25 MB per
-    // rank, one box: 67-77 % of peak for split and 67-73 % for fused across fresh sets of buffers), and split
-    // ran ahead on three boxes of four (by 1-6 %).
+    // rank, one box: 67-77 % of peak for split and 67-73 % for fused across fresh sets of buffers), and at the
+    // bucketed workload's sizes split ran ahead on most boxes (by 1-5 %).
     const ar_sched_t pref = (n > 16 && (out->legal_mask & (1u << AR_SCHED_SPLIT))) ? AR_SCHED_SPLIT : AR_SCHED_FUSED;
     if (have && out->chosen != pref &&
         (out->predicted_us[pref] <= best + kTieUs ||
