@@ -201,12 +201,12 @@ constexpr int kFusedLdsAllReduceByN[17] = {0, 0, 8, 10, 12, 16, 20, 22, 24, 28, 
 // 22-26 KB for n = 12-16 (6.4-6.7 TB/s).  The all-gather (ordinary input
 // loads) runs best with about 30 / (n + 1) resident waves per CU: 14 KB (11
 // per CU) at n = 2, 26 KB (6) at n = 4, 34 KB (4) at n = 6-7, 48 KB (3) at
-// n = 9-14, 64 KB (2) at n = 8 and from n = 15 on, 24, 32 and 72 included
-// (7.0-7.5 TB/s up to n = 16, 6.9 at 32, 6.1 at 72; n = 8 bf16 at 16 Mi
-// elements per piece re-swept in two passes: 91.9 % of peak at 48 KB, 92.8 %
-// at 64 KB).
+// n = 8-14, 64 KB (2) from n = 15 on, 24, 32 and 72 included (7.0-7.5 TB/s up
+// to n = 16, 6.9 at 32, 6.1 at 72).  (64 KB at n = 8 measured 0.9 points
+// faster for calls back to back but 9 points slower for a single call, and
+// slower for the phased all-gather, which shares the reservation.)
 constexpr int kFusedLdsReduceScatterByN[17] = {0, 0, 0, 6, 10, 12, 14, 14, 14, 16, 18, 20, 22, 22, 24, 24, 24};
-constexpr int kFusedLdsAllGatherByN[17] = {0, 0, 14, 18, 26, 30, 34, 34, 64, 48, 48, 48, 48, 48, 48, 64, 64};
+constexpr int kFusedLdsAllGatherByN[17] = {0, 0, 14, 18, 26, 30, 34, 34, 48, 48, 48, 48, 48, 48, 48, 64, 64};
 constexpr int kFusedLdsAllReduceKB = 0;      // n > 16 (the wide kernel): every cap from 10 to 64 KB measured slower
 constexpr int kFusedLdsReduceScatterKB = 48;   // n > 16, two vectors per lane (3 workgroups per CU)
 constexpr int kFusedLdsAllGatherKB = 64;
