@@ -214,20 +214,36 @@ def kernel_calls(reps=5):
     for sched, kern in (("split", "split_allreduce_kernel"), ("fused", "fused_allreduce_wide_kernel")):
         run("all-reduce n=72 f32 25MB/rank avg in place, %s" % sched, kern, 2 * n72 * c72 * 4,
             lambda: ar.ar_allreduce(bufs, bufs, c72, "f32", "avg", sched=sched))
-    # the LDS-staged tree past 16 ranks, each of its two kernels forced
+    # the tree past 16 ranks: the streaming walk, then the LDS-staged kernels (each forced)
+    run("all-reduce n=72 f32 25MB/rank avg in place, tree (streamed)", "tree_stream_kernel", 2 * n72 * c72 * 4,
+        lambda: ar.ar_allreduce(bufs, bufs, c72, "f32", "avg", sched="tree"))
+    os.environ["AR_TREE_STREAM"] = "0"
     for teams, kern in (("0", "tree_allreduce_kernel"), ("1", "tree_team_kernel")):
         os.environ["AR_TREE_TEAMS"] = teams
         run("all-reduce n=72 f32 25MB/rank avg in place, tree (staged, %s)" % ("teams" if teams == "1" else "level by level"),
             kern, 2 * n72 * c72 * 4, lambda: ar.ar_allreduce(bufs, bufs, c72, "f32", "avg", sched="tree"))
+    os.environ.pop("AR_TREE_STREAM", None)
     del bufs, bufs_t
     n17, c17 = 17, 128 * MB // 4                            # 17 ranks, 128 MB per rank, in place
     bufs_t = [wl.device_normal(4, 1, r, c17, 1e-3, "f32") for r in range(n17)]
     bufs = ar.pointers(bufs_t)
+    run("all-reduce n=17 f32 128MB/rank avg in place, tree (streamed)", "tree_stream_kernel", 2 * n17 * c17 * 4,
+        lambda: ar.ar_allreduce(bufs, bufs, c17, "f32", "avg", sched="tree"))
+    os.environ["AR_TREE_STREAM"] = "0"
     for teams, kern in (("0", "tree_allreduce_kernel"), ("1", "tree_team_kernel")):
         os.environ["AR_TREE_TEAMS"] = teams
         run("all-reduce n=17 f32 128MB/rank avg in place, tree (staged, %s)" % ("teams" if teams == "1" else "level by level"),
             kern, 2 * n17 * c17 * 4, lambda: ar.ar_allreduce(bufs, bufs, c17, "f32", "avg", sched="tree"))
     os.environ.pop("AR_TREE_TEAMS", None)
+    os.environ.pop("AR_TREE_STREAM", None)
+    del bufs, bufs_t
+    n128, c128 = 128, 8 * MB // 4                           # 128 ranks, 8 MB per rank, in place
+    bufs_t = [wl.device_normal(4, 2, r, c128, 1e-3, "f32") for r in range(n128)]
+    bufs = ar.pointers(bufs_t)
+    for sched, kern in (("tree", "tree_stream_kernel"), ("fused", "fused_allreduce_wide_kernel"),
+                        ("split", "split_allreduce_kernel")):
+        run("all-reduce n=128 f32 8MB/rank avg in place, %s" % sched, kern, 2 * n128 * c128 * 4,
+            lambda: ar.ar_allreduce(bufs, bufs, c128, "f32", "avg", sched=sched))
     del bufs, bufs_t
     torch.cuda.empty_cache()
 

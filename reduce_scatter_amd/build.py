@@ -18,7 +18,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libar.so")
-SOURCES = ["tree.hip", "tree_reg.hip", "fused.hip", "fused_rs.hip", "ring.hip", "split.hip", "fused_phase.hip", "elem.hip", "reshard.hip",
+SOURCES = ["tree.hip", "tree_stream.hip", "tree_reg.hip", "fused.hip", "fused_rs.hip", "ring.hip", "split.hip", "fused_phase.hip", "elem.hip", "reshard.hip",
            "api.cpp", "plan.cpp", "reshard_api.cpp"]
 
 ARCH = "gfx950"

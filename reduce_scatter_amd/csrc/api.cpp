@@ -90,9 +90,10 @@ int fused_lds_bytes(ar_coll_t coll, int n) {
     }
 }
 
-// AR_TREE_STAGED=1 sends the n <= 16 tree schedules through the LDS-staged
-// kernels (as for n > 16) instead of the register-evaluated ones; both give
-// the same bits.  Read on every call (a getenv is far below a launch's cost),
+// AR_TREE_STAGED=1 sends the n <= 16 tree schedules through the any-n
+// kernels (as for n > 16: the streaming walk, or the LDS-staged kernels under
+// AR_TREE_STREAM=0) instead of the register-evaluated ones; all give the same
+// bits.  Read on every call (a getenv is far below a launch's cost),
 // so one process can compare the kernels.
 bool tree_staged() {
     const char *e = getenv("AR_TREE_STAGED");

@@ -151,6 +151,11 @@ hipError_t launch_tree_reg_allreduce(bool dual, int dt, int op, const RankTable 
 // of [0, Vfull); double tree: ``tree`` over vectors [0, g.split) and
 // ``tree2`` over [g.split2, Vfull), one launch each.  The launcher sizes its
 // persistent grids from the device's compute units ``cus``.
+// The tree schedule over vectors [lo, hi) in one streaming pass when the tree
+// is an in-order tree (returns true and the launch status in *err); false
+// leaves the call to the LDS-staged kernels.
+bool launch_tree_stream_range(int dt, int op, const RankTable &t, const TreeShape &tree, const Geometry &g,
+                              long long lo, long long hi, hipStream_t s, hipError_t *err);
 hipError_t launch_tree_allreduce(int dt, int op, const RankTable &t, const TreeShape &tree, const Geometry &g,
                                  int cus, hipStream_t s);
 hipError_t launch_dtree_allreduce(int dt, int op, const RankTable &t, const TreeShape &tree, const TreeShape &tree2,

@@ -9,9 +9,12 @@
 // down, every node keeping a copy.  2 * depth dependent steps instead of the
 // ring's 2(n-1).
 //
-// These LDS-staged kernels serve n > 16 (and n <= 16 under AR_TREE_STAGED=1);
-// up to 16 ranks tree_reg.hip evaluates the same trees in registers in one
-// pass, with the same results.
+// Past 16 ranks (and up to 16 under AR_TREE_STAGED=1) a launch first tries
+// the streaming in-order walk of tree_stream.hip, one pass with the same
+// results; these LDS-staged kernels take the trees it cannot hold (the double
+// tree's shifted second tree at 127 ranks) and every tree under
+// AR_TREE_STREAM=0.  Up to 16 ranks tree_reg.hip evaluates the same trees in
+// registers in one pass, with the same results.
 //
 // A workgroup runs the whole tree for a window of W vectors at the same offset
 // of every rank buffer.  Item (rank v, vector w) holds rank v's contribution;
@@ -251,6 +254,8 @@ static bool tree_teams(int n) {
 // One launch over the vectors [lo, hi) with one tree shape.
 static hipError_t launch_tree_range(int dt, int op, const RankTable &t, const TreeShape &tree, const Geometry &g,
                                     long long lo, long long hi, int cus, hipStream_t s) {
+    hipError_t streamed;                                       // in-order trees: one streaming pass (tree_stream.hip)
+    if (launch_tree_stream_range(dt, op, t, tree, g, lo, hi, s, &streamed)) return streamed;
     TreeRange rg;
     rg.lo = lo;
     rg.hi = hi;

@@ -1,0 +1,262 @@
+// tree_stream.hip -- the tree schedule past 16 ranks in one streaming pass.
+//
+// The "NCCL all-reduce" post (rakshithvasudev.github.io), section "The double
+// binary tree": every rank's partial is its own contribution combined with
+// its children's partials (ascending rank order), the root's is the result,
+// and the result is broadcast back to every rank.  In the bit-trick tree every
+// subtree covers a contiguous run of ranks and a node with two children has
+// one below and one above it.  So the ranks can be visited in ascending order
+// with a stack of partials, as an in-order walk:
+//
+//   at rank v:  acc = pre(own(v)); if v has a child below, acc (+)= pop()
+//               if v has a child above: push(acc)            (pending)
+//               else: repeat ``cascade`` times acc = pop() (+) acc, push(acc)
+//
+// where ``cascade`` counts the ancestors whose upper child the finished
+// subtree is.  The double tree's second tree is the mirror image for even n
+// (again in order) and the first tree shifted by one rank for odd n: walked
+// from rank 1 up to n-1 and then rank 0, it is in order too, except that a
+// node whose children are rank 0 and another rank must combine rank 0's
+// subtree first although the walk finishes it last.  Such a node leaves its
+// other child's partial on the stack under its own pending one, and the
+// cascade level that completes it pops both, in rank order.  Every combine is
+// the staged kernels', in the same order, so the results are identical (the
+// host runs each program on node ids and refuses any that would not reproduce
+// the tree).  After the last rank the stack holds the root's partial; the
+// postOp is applied and the value stored to every rank.
+//
+// One wavefront per tile of 64*U vectors on an address-aligned grid, U per
+// lane spaced by the wavefront width: each load is one 1 KB run of one rank,
+// and a tile reads U KB of each rank in turn, the loads of the next D-1 ranks
+// in flight while one is combined (D register buffers in rotation).  The
+// stack lives in LDS, one region per wavefront sized to the program's depth:
+// its depth is a uniform value, so a push or a pop is one LDS access per
+// vector at a uniform offset, each lane to its own words (held in registers
+// instead, the slots needed a branch per slot on every access, which the
+// register allocator answered with copies and spills at one wave per SIMD).
+#include <cstdlib>
+#include <cstring>
+#include <type_traits>
+
+#include "ar_device.hpp"
+#include "ar_kernels.hpp"
+#include "dispatch.hpp"
+
+namespace ar {
+
+// The tile shape by rank count, measured on MI355X (fp32 sum, in place, per
+// cent of 8 TB/s; 2 / 8 vectors per lane with 4 / 2 buffers): 17 ranks at
+// 128 MB per rank 74 / 67, 24 at 64 MB 70 / 65, 33 at 64 MB 69 / 65, 72 at
+// 25 MB 61 / 61-62, 100 at 16 MB 54 / 61, 128 at 8 MB 56 / 71-72.  Few ranks
+// want many waves and deep prefetch; many ranks want long runs of each rank
+// (8 KB per wavefront) and fewer tiles.  Other shapes measured (2 vectors with
+// 3 buffers, 4 with 2-4, 4 waves per workgroup) were no better anywhere.
+constexpr int kStreamWideRanks = 64;
+// Stack slots: enough for every tree of both schedules up to 128 ranks except
+// the shifted tree at 127 ranks (8), which keeps the staged kernels.
+constexpr int kStreamSlots = 7;
+
+// Step v visits rank (first + v) mod n: bit 0, combine the child visited
+// before it (pop); bit 1, a child still to come (push pending); bits 2-4, the
+// cascade count; bit 5 + k, cascade level k also pops the partial its node
+// left under its pending one and combines it after the finished subtree.
+// (Whole words: the kernel reads them with scalar loads, which unlike vector
+// loads do not wait behind the next rank's loads in flight.)
+struct TreeProgram {
+    uint32_t op[kTableRanks];
+    int first;
+};
+
+template <int U> __device__ __forceinline__ void stream_load(u32x4 (&b)[U], const void *src, long long base,
+                                                         const unsigned (&off)[U]) {
+    const char *p = (const char *)src + base;
+#pragma unroll
+    for (int u = 0; u < U; ++u) b[u] = __builtin_nontemporal_load((const u32x4 *)(p + off[u]));
+}
+
+// One step of the walk on the rank whose vectors ``b`` holds.  The stack keeps
+// partials in the storage type (every combine already rounds to it, so
+// packing is exact): 16 bytes per vector whatever the type, slot k of vector
+// u at stack[(k * U + u) * 64] from the lane's own word.
+template <int DT, int OP, int U>
+__device__ __forceinline__ void stream_step(const u32x4 (&b)[U], int op, u32x4 *stack, int &sp, float s) {
+    Pack<DT> acc[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc[u] = first<DT, OP>(unpack<DT>(b[u]), s);
+    if (op & 1) {                                              // the child visited before: its finished partial
+        --sp;
+#pragma unroll
+        for (int u = 0; u < U; ++u) merge<DT, OP>(acc[u], unpack<DT>(stack[(sp * U + u) * kFusedThreads]));
+    }
+    if (!(op & 2)) {                                           // the subtree is finished
+        const int levels = (op >> 2) & 7;
+        for (int k = 0; k < levels; ++k) {                     // ... and with it each ancestor's later child
+            --sp;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                Pack<DT> a = unpack<DT>(stack[(sp * U + u) * kFusedThreads]);
+                merge<DT, OP>(a, acc[u]);
+                acc[u] = a;
+            }
+            if ((op >> (5 + k)) & 1) {                         // the ancestor's other child, the higher rank
+                --sp;
+#pragma unroll
+                for (int u = 0; u < U; ++u) merge<DT, OP>(acc[u], unpack<DT>(stack[(sp * U + u) * kFusedThreads]));
+            }
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) stack[(sp * U + u) * kFusedThreads] = pack<DT>(acc[u]);
+    ++sp;                                                      // pending (child to come) or finished
+}
+
+template <int DT, int OP, int U, int D>
+__global__ __launch_bounds__(kFusedThreads) void tree_stream_kernel(const RankTable t, const TreeProgram prog,
+                                                        const Geometry g, long long lo, long long hi) {
+    constexpr long long T = (long long)kFusedThreads * U;
+    extern __shared__ u32x4 stream_stack[];
+    const int n = g.n;
+    const TileSpan ts = aligned_tile(lo, hi, (long long)blockIdx.x, g.ref, T);
+    if (ts.lo >= ts.hi) return;
+    unsigned off[U];
+    bool ok[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) off[u] = tile_lane(ts, ts.start + threadIdx.x + u * kFusedThreads, ok[u]);
+    const long long base = ts.lo * 16;
+    u32x4 *stack = stream_stack + threadIdx.x;
+    int sp = 0;                                                // uniform: the same program for every lane
+
+    // Step v visits rank (first + v) mod n; buffer v % D holds it.
+    const int f = prog.first;
+    const auto rank_of = [&](int v) { return f + v < n ? f + v : f + v - n; };
+    u32x4 buf[D][U];
+#pragma unroll
+    for (int k = 0; k + 1 < D; ++k)
+        if (k < n) stream_load<U>(buf[k], t.src[rank_of(k)], base, off);
+    // Whole rounds in which every next rank exists, so every load is issued
+    // unconditionally and each step waits only for its own buffer (loads
+    // under a branch make the wait counts conservative: a step then waited
+    // for all loads in flight); then at most 2D - 2 steps of tail.
+    int v = 0;
+    for (; v + 2 * D - 2 < n; v += D) {
+#pragma unroll
+        for (int k = 0; k < D; ++k) {
+            stream_load<U>(buf[(k + D - 1) % D], t.src[rank_of(v + k + D - 1)], base, off);
+            stream_step<DT, OP, U>(buf[k], (int)prog.op[v + k], stack, sp, g.s);
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < 2 * D - 2; ++k) {
+        if (v + k < n) {
+            if (v + k + D - 1 < n) stream_load<U>(buf[(k + D - 1) % D], t.src[rank_of(v + k + D - 1)], base, off);
+            stream_step<DT, OP, U>(buf[k % D], (int)prog.op[v + k], stack, sp, g.s);
+        }
+    }
+
+    Pack<DT> root[U];
+    u32x4 w[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        root[u] = unpack<DT>(stack[u * kFusedThreads]);
+        finish<DT, OP>(root[u], n, g);
+        w[u] = pack<DT>(root[u]);
+    }
+    for (int r = 0; r < n; ++r) {
+        char *p = (char *)t.dst[r] + base;
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (ok[u]) __builtin_nontemporal_store(w[u], (u32x4 *)(p + off[u]));
+    }
+}
+
+// The stream program of a tree walked from rank ``first``, or false when the
+// walk would not reproduce the tree.  The program is run on node ids: every
+// stack entry is a rank's pending partial or a finished subtree's, and every
+// pop must deliver exactly the one the tree combines there, children in
+// ascending rank order after the node's own value.  The walk must end with the
+// root's finished subtree alone on the stack and never hold more than
+// kStreamSlots partials.
+static bool tree_program(const TreeShape &tree, int n, int first, TreeProgram &prog, int &depth) {
+    if (n < 1 || n > kTableRanks || first < 0 || first >= n) return false;
+    int pos[kTableRanks];
+    for (int v = 0; v < n; ++v) pos[(first + v) % n] = v;
+    int stack[kTableRanks + 1];                                // a rank's finished subtree, + kTableRanks if pending
+    int sp = 0;
+    depth = 0;
+    const auto pop = [&](int want) { return sp > 0 && stack[--sp] == want; };
+    for (int v = 0; v < n; ++v) {
+        const int r = (first + v) % n;
+        const int c0 = tree.child[r][0], c1 = tree.child[r][1];  // ascending rank order
+        int before = -1, after = -1;
+        for (const int c : {c0, c1}) {
+            if (c < 0) continue;
+            int &side = pos[c] < v ? before : after;
+            if (side >= 0) return false;
+            side = c;
+        }
+        const bool keep = before >= 0 && after >= 0 && after == c0;   // the later child combines first
+        int code = 0, levels = 0;
+        if (before >= 0 && !keep) {
+            if (!pop(before)) return false;
+            code |= 1;
+        }
+        if (after >= 0) {
+            if (keep && !(sp > 0 && stack[sp - 1] == before)) return false;
+            stack[sp++] = r + kTableRanks;
+            code |= 2;
+        } else {
+            int x = r;
+            for (int p = tree.parent[x]; p >= 0 && pos[p] < pos[x]; x = p, p = tree.parent[x]) {
+                if (levels >= 7 || !pop(p + kTableRanks)) return false;
+                if (tree.child[p][0] == x && tree.child[p][1] >= 0) {   // p kept its other child's partial
+                    if (!pop(tree.child[p][1])) return false;
+                    code |= 1 << (5 + levels);
+                }
+                ++levels;
+            }
+            stack[sp++] = x;
+        }
+        if (sp > kStreamSlots) return false;
+        if (sp > depth) depth = sp;
+        prog.op[v] = (uint32_t)(code | levels << 2);
+    }
+    if (sp != 1 || stack[0] != tree.root) return false;
+    for (int v = n; v < kTableRanks; ++v) prog.op[v] = 0;
+    prog.first = first;
+    return true;
+}
+
+// AR_TREE_STREAM=0 keeps the LDS-staged kernels for every tree.
+static bool tree_stream_enabled() {
+    const char *e = getenv("AR_TREE_STREAM");
+    return !(e && !strcmp(e, "0"));
+}
+
+bool launch_tree_stream_range(int dt, int op, const RankTable &t, const TreeShape &tree, const Geometry &g,
+                              long long lo, long long hi, hipStream_t s, hipError_t *err) {
+    TreeProgram prog;
+    int depth = 0;
+    // the first tree and the mirror image walk from rank 0, the shifted tree from rank 1
+    if (!tree_stream_enabled() ||
+        !(tree_program(tree, g.n, 0, prog, depth) || tree_program(tree, g.n, 1, prog, depth)))
+        return false;
+    *err = hipSuccess;
+    if (lo >= hi) return true;
+    const auto go = [&](auto Uc, auto Dc) {
+        constexpr int U = decltype(Uc)::value, D = decltype(Dc)::value;
+        const long long tiles = aligned_tiles(hi - lo, (long long)kFusedThreads * U);
+        if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
+        const size_t lds = (size_t)depth * U * kFusedThreads * 16;
+        return dispatch(dt, op, [&](auto Dt, auto O) {
+            return launch(tree_stream_kernel<decltype(Dt)::value, decltype(O)::value, U, D>,
+                          dim3((unsigned)tiles), dim3(kFusedThreads), lds, s, t, prog, g, lo, hi);
+        });
+    };
+    if (g.n >= kStreamWideRanks)
+        *err = go(std::integral_constant<int, 8>(), std::integral_constant<int, 2>());
+    else
+        *err = go(std::integral_constant<int, 2>(), std::integral_constant<int, 4>());
+    return true;
+}
+
+}  // namespace ar

@@ -644,12 +644,14 @@ def test_trees_every_rank_count_up_to_17(dtype, sched):
 
 @pytest.mark.parametrize("teams", ["1", "0"])
 def test_staged_trees_match_oracle(teams, monkeypatch):
-    """The LDS-staged tree kernels, with concurrent up/down teams (teams=1)
-    and level by level (teams=0), each forced: every dtype, ops whose order
+    """The LDS-staged tree kernels (the streaming walk switched off), with
+    concurrent up/down teams (teams=1) and level by level (teams=0), each
+    forced: every dtype, ops whose order
     matters, rank counts up to 128 (n <= 16 through AR_TREE_STAGED), counts
     spanning many windows per workgroup with a ragged end, in and out of place,
     against the tree and double-tree oracles bit for bit."""
     monkeypatch.setenv("AR_TREE_STAGED", "1")
+    monkeypatch.setenv("AR_TREE_STREAM", "0")
     monkeypatch.setenv("AR_TREE_TEAMS", teams)
     for n in (2, 3, 8, 16, 17, 33, 72, 128):
         for dtype in DTYPES:
@@ -666,6 +668,35 @@ def test_staged_trees_match_oracle(teams, monkeypatch):
                         for r in (0, n // 2, n - 1):
                             assert_bits_equal(got[r], want[r], "staged %s teams=%s n=%d %s %s rank %d"
                                               % (sched, teams, n, dtype, op, r))
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_streamed_trees_match_oracle(dtype, monkeypatch):
+    """The streaming in-order walk of the trees, at rank counts whose walks
+    differ: shallow and deep stacks, the mirror-image second tree (even n) and
+    the shifted one walked from rank 1 (odd n; with reordered levels at 7, 19
+    and 63 ranks), both
+    tile shapes (below and from 64 ranks), n <= 16 through AR_TREE_STAGED, and
+    127 ranks, whose shifted tree needs more stack than the walk holds and
+    keeps the staged kernels.  Counts spanning several tiles with a ragged end,
+    in and out of place, against the tree and double-tree oracles bit for bit."""
+    monkeypatch.setenv("AR_TREE_STAGED", "1")
+    monkeypatch.delenv("AR_TREE_STREAM", raising=False)
+    u = LANES[dtype]
+    for n in (2, 3, 5, 7, 16, 17, 19, 24, 33, 63, 64, 65, 72, 100, 127, 128):
+        tile = 64 * (8 if n >= 64 else 2)                      # vectors per tile
+        count = (tile * 3 + 5) * u + 3
+        for op in (OPS if n in (17, 65) else ("sum", "avg")):
+            xs = inputs(70 + n, n, count, dtype, op)
+            for sched in ("tree", "dtree"):
+                want = reference(sched, xs, dtype, op)
+                for inplace in ((False, True) if n in (33, 72) else (False,)):
+                    print("streamed %s n=%d %s %s count=%d inplace=%d" % (sched, n, dtype, op, count, inplace),
+                          flush=True)
+                    got = run_allreduce(xs, dtype, op, sched, inplace=inplace)
+                    for r in (0, n // 2, n - 1):
+                        assert_bits_equal(got[r], want[r], "streamed %s n=%d %s %s rank %d inplace=%d"
+                                          % (sched, n, dtype, op, r, inplace))
 
 
 def test_randomized_calls_match_oracle():
