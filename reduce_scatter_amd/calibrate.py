@@ -1,6 +1,10 @@
 """Measure the cost model's constants on the GPU and write ``calib_gfx950.txt``.
 
     python -m reduce_scatter_amd.calibrate [--out PATH] [--quick]
+    python -m reduce_scatter_amd.calibrate --schedules tree,dtree --merge BASE [--out PATH]
+
+The second form re-measures only the named schedules (after a change to their
+kernels) and keeps every other schedule's constants from the file BASE.
 
 The planner prices every legal schedule s of a call as
 
@@ -28,6 +32,7 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 DEFAULT_OUT = os.path.join(HERE, "calib_gfx950.txt")
 COLLS = ("allreduce", "reduce_scatter", "all_gather")
+SCHEDS = ("ring", "tree", "fused", "split", "dtree")
 SIZE_BINS = 48
 HBM_BIN = 30                      # log2 of the footprint from which calls stream from HBM (1 GiB, 4x the MALL)
 
@@ -62,10 +67,11 @@ def time_call(fn, iters, warmup=2):
     return float(np.median([a.elapsed_time(b) * 1e3 for a, b in ev]))
 
 
-def measure(ns, sizes, iters, rounds=3, dtype="f32"):
+def measure(ns, sizes, iters, rounds=3, dtype="f32", scheds=SCHEDS):
     """Time every (collective, schedule) at every rank count and per-rank byte
     size, for element type ``dtype`` (``f32`` or ``bf16``): median over
-    ``rounds`` rounds of the per-call median of ``iters`` calls."""
+    ``rounds`` rounds of the per-call median of ``iters`` calls.  Only the
+    schedules in ``scheds``."""
     import torch
     import reduce_scatter_amd as ar
     e = 4 if dtype == "f32" else 2
@@ -98,7 +104,7 @@ def measure(ns, sizes, iters, rounds=3, dtype="f32"):
             calls = {}
             # past 16 ranks the all-reduce is timed in place, on views of a flat gradient buffer (above)
             ar_out = xs if n > 16 else ys
-            for sched in ("ring", "tree", "fused", "split", "dtree"):
+            for sched in scheds:
                 calls[("allreduce", sched)] = (lambda s=sched: ar.ar_allreduce(xs, ar_out, count, dtype, "sum", n=n, sched=s))
                 if sched in ("tree", "split", "dtree"):
                     continue
@@ -137,7 +143,7 @@ def fit(rows, latency=None):
     Infinity Cache."""
     out = {}
     for coll in COLLS:
-        for sched in ("ring", "tree", "fused", "split", "dtree"):
+        for sched in SCHEDS:
             pts = [(n, pr, us, _bytes(coll, n, pr)) for c, s, n, pr, us in rows if c == coll and s == sched]
             if not pts:
                 continue
@@ -198,34 +204,82 @@ def fit(rows, latency=None):
     return out
 
 
-def write(path, model, gpu_name, model2=None):
+def entry_lines(model, model2=None):
+    """The file's lines for each (collective, schedule) of ``model``."""
+    out = {}
+    for (coll, sched), (launch, step, bw, corr, extra) in sorted(model.items()):
+        lines = ["%s %s %.3f %.4f %.1f" % (coll, sched, launch, step, bw)]
+        for rc, row in sorted(corr.items()):
+            lines.append("corr %s %s %d %s" % (coll, sched, rc, " ".join("%.3f" % c for c in row)))
+        for rc, us in sorted(extra.items()):
+            lines.append("lat %s %s %d %.3f" % (coll, sched, rc, us))
+        if model2 and (coll, sched) in model2:
+            _, _, bw2, corr2, _ = model2[(coll, sched)]
+            lines.append("bw2 %s %s %.1f" % (coll, sched, bw2))
+            for rc, row in sorted(corr2.items()):
+                lines.append("corr2 %s %s %d %s" % (coll, sched, rc, " ".join("%.3f" % c for c in row)))
+        out[(coll, sched)] = lines
+    return out
+
+
+def read_entries(path):
+    """(header lines, {(collective, schedule): lines}) of a calibration file."""
+    header, entries = [], {}
+    for line in open(path):
+        line = line.rstrip("\n")
+        if not line.strip() or line.startswith("#"):
+            header.append(line)
+            continue
+        tok = line.split()
+        key = tuple(tok[1:3]) if tok[0] in ("corr", "lat", "bw2", "corr2") else tuple(tok[0:2])
+        entries.setdefault(key, []).append(line)
+    return header, entries
+
+
+HEADER = ["# cost-model constants for libar (written by reduce_scatter_amd/calibrate.py)",
+          None,
+          "# <coll> <sched> <launch_us> <step_us> <bw_GBps>            (fitted on fp32: every 4-byte type)",
+          "# corr <coll> <sched> <ceil(log2 n)> <bandwidth factor for log2(total algorithmic bytes) = 0..47>",
+          "# lat <coll> <sched> <ceil(log2 n)> <latency beyond launch + step * steps, us>",
+          "# bw2 / corr2: the same bandwidth terms fitted on bf16 (2-byte types; latency terms shared)"]
+
+
+def write(path, model, gpu_name, model2=None, base=None, scheds=SCHEDS):
     """The calibration file: ``model`` fitted on fp32 (every 4-byte type), and
-    ``model2`` (bandwidth terms only) on bf16 for the 2-byte types."""
+    ``model2`` (bandwidth terms only) on bf16 for the 2-byte types.  With
+    ``base`` (a calibration file as ``read_entries`` returns it), the entries
+    of the schedules outside ``scheds`` are kept from it."""
+    entries = entry_lines(model, model2)
+    header = [h if h is not None else "# device: %s" % gpu_name for h in HEADER]
+    if base is not None:
+        base_header, base_entries = base
+        device = [h for h in base_header if h.startswith("# device:")]
+        header[1] = device[0] if device else header[1]
+        header += [h for h in base_header if h.startswith("# re-measured:")]
+        header.append("# re-measured: %s on %s" % (", ".join(scheds), gpu_name))
+        for key, lines in base_entries.items():
+            if key[1] not in scheds:
+                entries[key] = lines
     with open(path, "w") as f:
-        f.write("# cost-model constants for libar (written by reduce_scatter_amd/calibrate.py)\n")
-        f.write("# device: %s\n" % gpu_name)
-        f.write("# <coll> <sched> <launch_us> <step_us> <bw_GBps>            (fitted on fp32: every 4-byte type)\n")
-        f.write("# corr <coll> <sched> <ceil(log2 n)> <bandwidth factor for log2(total algorithmic bytes) = 0..47>\n")
-        f.write("# lat <coll> <sched> <ceil(log2 n)> <latency beyond launch + step * steps, us>\n")
-        f.write("# bw2 / corr2: the same bandwidth terms fitted on bf16 (2-byte types; latency terms shared)\n")
-        for (coll, sched), (launch, step, bw, corr, extra) in sorted(model.items()):
-            f.write("%s %s %.3f %.4f %.1f\n" % (coll, sched, launch, step, bw))
-            for rc, row in sorted(corr.items()):
-                f.write("corr %s %s %d %s\n" % (coll, sched, rc, " ".join("%.3f" % c for c in row)))
-            for rc, us in sorted(extra.items()):
-                f.write("lat %s %s %d %.3f\n" % (coll, sched, rc, us))
-            if model2 and (coll, sched) in model2:
-                _, _, bw2, corr2, _ = model2[(coll, sched)]
-                f.write("bw2 %s %s %.1f\n" % (coll, sched, bw2))
-                for rc, row in sorted(corr2.items()):
-                    f.write("corr2 %s %s %d %s\n" % (coll, sched, rc, " ".join("%.3f" % c for c in row)))
+        for h in header:
+            f.write(h + "\n")
+        for key in sorted(entries):
+            for line in entries[key]:
+                f.write(line + "\n")
 
 
 def main(argv=None):
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--out", default=DEFAULT_OUT)
     p.add_argument("--quick", action="store_true", help="fewer sizes and rank counts")
+    p.add_argument("--schedules", default=",".join(SCHEDS), help="comma-separated schedules to measure")
+    p.add_argument("--merge", metavar="BASE", help="keep the other schedules' constants from this file")
     a = p.parse_args(argv)
+    scheds = tuple(x for x in a.schedules.split(",") if x)
+    if not scheds or any(x not in SCHEDS for x in scheds):
+        p.error("--schedules takes a comma-separated subset of %s" % ",".join(SCHEDS))
+    if scheds != SCHEDS and not a.merge:
+        p.error("measuring a subset of the schedules needs --merge BASE for the others")
     import torch
     if not torch.cuda.is_available():
         print("calibrate: no GPU visible", file=sys.stderr)
@@ -233,13 +287,14 @@ def main(argv=None):
     torch.cuda.set_device(0)
     ns = (2, 8) if a.quick else (2, 4, 8, 16, 32, 72, 128)
     sizes = [1 << k for k in ((12, 16, 20, 24, 28) if a.quick else (10, 12, 14, 16, 18, 20, 21, 22, 23, 24, 25, 26, 27, 28, 29, 30))]
-    rows = measure(ns, sizes, iters=3 if a.quick else 5)
+    base = a.merge and read_entries(a.merge)             # read before --out may overwrite it
+    rows = measure(ns, sizes, iters=3 if a.quick else 5, scheds=scheds)
     model = fit(rows)
     ns2 = (8,) if a.quick else (2, 4, 8, 16, 72)
-    rows2 = measure(ns2, sizes, iters=3 if a.quick else 5, dtype="bf16")
+    rows2 = measure(ns2, sizes, iters=3 if a.quick else 5, dtype="bf16", scheds=scheds)
     model2 = fit(rows2, latency=model)
-    write(a.out, model, torch.cuda.get_device_name(0) + " " + getattr(torch.cuda.get_device_properties(0),
-                                                                      "gcnArchName", ""), model2)
+    gpu = torch.cuda.get_device_name(0) + " " + getattr(torch.cuda.get_device_properties(0), "gcnArchName", "")
+    write(a.out, model, gpu, model2, base=base, scheds=scheds)
     for (coll, sched), (launch, step, bw, corr, extra) in sorted(model.items()):
         print("%-15s %-6s launch %7.2f us  step %6.3f us  bw %7.1f GB/s  extra %s" % (
             coll, sched, launch, step, bw, {k: round(v, 1) for k, v in extra.items()}))

@@ -52,6 +52,16 @@ namespace ar {
 // (8 KB per wavefront) and fewer tiles.  Other shapes measured (2 vectors with
 // 3 buffers, 4 with 2-4, 4 waves per workgroup) were no better anywhere.
 constexpr int kStreamWideRanks = 64;
+
+// Launches under 1 MB per rank keep the staged kernels.  A wavefront walks
+// the n ranks one after another, so a small call costs about n dependent load
+// rounds (measured: 9 us at 17 ranks, 49 at 72, 86 at 128, fp32 sum), while
+// the staged kernels load every rank at once and scale with n times the
+// bytes; both grow with n, so the crossover is about the same per-rank size
+// everywhere (staged / streamed, us: 72 ranks at 256 KB 25 / 51, at 1 MB 89 /
+// 53; 128 ranks at 512 KB per launch 157 / 175, at 1 MB 338 / 112; 33 ranks at
+// 256 KB 11 / 15, at 1 MB 28 / 18).
+constexpr long long kStreamMinBytes = 1 << 20;
 // Stack slots: enough for every tree of both schedules up to 128 ranks except
 // the shifted tree at 127 ranks (8), which keeps the staged kernels.
 constexpr int kStreamSlots = 7;
@@ -226,22 +236,23 @@ static bool tree_program(const TreeShape &tree, int n, int first, TreeProgram &p
     return true;
 }
 
-// AR_TREE_STREAM=0 keeps the LDS-staged kernels for every tree.
-static bool tree_stream_enabled() {
+// AR_TREE_STREAM=0 keeps the LDS-staged kernels for every tree; =1 streams
+// every tree the walk holds at any size; unset, launches of 1 MB per rank and
+// more stream.  Read on every launch, so one process can compare the kernels.
+static int tree_stream_mode() {
     const char *e = getenv("AR_TREE_STREAM");
-    return !(e && !strcmp(e, "0"));
+    if (e && (*e == '0' || *e == '1')) return *e - '0';
+    return 2;
 }
 
 bool launch_tree_stream_range(int dt, int op, const RankTable &t, const TreeShape &tree, const Geometry &g,
                               long long lo, long long hi, hipStream_t s, hipError_t *err) {
+    const int mode = tree_stream_mode();
+    if (mode == 0 || lo >= hi || (mode == 2 && (hi - lo) * 16 < kStreamMinBytes)) return false;
     TreeProgram prog;
     int depth = 0;
     // the first tree and the mirror image walk from rank 0, the shifted tree from rank 1
-    if (!tree_stream_enabled() ||
-        !(tree_program(tree, g.n, 0, prog, depth) || tree_program(tree, g.n, 1, prog, depth)))
-        return false;
-    *err = hipSuccess;
-    if (lo >= hi) return true;
+    if (!(tree_program(tree, g.n, 0, prog, depth) || tree_program(tree, g.n, 1, prog, depth))) return false;
     const auto go = [&](auto Uc, auto Dc) {
         constexpr int U = decltype(Uc)::value, D = decltype(Dc)::value;
         const long long tiles = aligned_tiles(hi - lo, (long long)kFusedThreads * U);

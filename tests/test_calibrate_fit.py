@@ -61,3 +61,27 @@ def test_two_byte_fit_keeps_the_latency_terms():
         assert model2[key][4] == model4[key][4]
     assert model2[("allreduce", "ring")][2] < model4[("allreduce", "ring")][2]
     assert abs(model2[("allreduce", "fused")][2] - model4[("allreduce", "fused")][2]) / model4[("allreduce", "fused")][2] < 0.01
+
+
+def test_merge_replaces_only_the_remeasured_schedules(tmp_path):
+    """``--schedules S --merge BASE``: the file keeps every entry of BASE whose
+    schedule is not in S, takes S's entries from the new fit (dropping BASE's
+    lines for S, including rank classes the new fit has none for), and names
+    the re-measured schedules in its header."""
+    full = cal.fit(_rows(False))
+    base_path = tmp_path / "base.txt"
+    cal.write(str(base_path), full, "box A")
+    base = cal.read_entries(str(base_path))
+    rows = [(c, s, n, pr, us * 1.5) for c, s, n, pr, us in _rows(False) if s == "ring"]
+    part = cal.fit(rows)
+    assert {k[1] for k in part} == {"ring"}
+    out = tmp_path / "merged.txt"
+    cal.write(str(out), part, "box B", base=base, scheds=("ring", "tree"))
+    header, entries = cal.read_entries(str(out))
+    assert "# device: box A" in header and "# re-measured: ring, tree on box B" in header
+    assert set(entries) == set(base[1])
+    for key, lines in entries.items():
+        if key[1] == "ring":
+            assert lines == cal.entry_lines(part)[key] and lines != base[1][key]
+        else:
+            assert lines == base[1][key]

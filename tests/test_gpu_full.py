@@ -249,6 +249,27 @@ def test_c5_split_one_bucket_in_place():
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("sched", ["tree", "dtree"])
+def test_c5_trees_one_bucket_in_place(sched):
+    """The tree and double-tree schedules on the 72-rank workload's first
+    (25 MB) bucket, in place, as a caller gets them (the streaming walk at this
+    size): every element of three ranks against the oracle of the schedule."""
+    n = workloads.C5_N
+    buckets, _ = workloads.c5_buckets()
+    off, nbytes = buckets[0]
+    count = nbytes // 4
+    grads = [workloads.device_spiky_normal(4, r, count, 1e-3, 0.01, 100.0) for r in range(n)]
+    host = [to_host(g, "f32") for g in grads]
+    print("c5 %s oracle" % sched, nbytes, flush=True)
+    want = (oracle.tree_allreduce if sched == "tree" else oracle.dtree_allreduce)(host, "f32", "avg")[0]
+    ar.ar_allreduce(grads, grads, count, "f32", "avg", sched=sched)
+    torch.cuda.synchronize()
+    for r in (0, 35, n - 1):
+        assert_bits_equal(to_host(grads[r], "f32"), want, "c5 %s rank %d" % (sched, r))
+    del grads, host
+    torch.cuda.empty_cache()
+
+
 BIG = (1 << 30) + (1 << 20) + 7          # fp32 elements per rank: 4.3 GB, past every 32-bit byte offset
 
 

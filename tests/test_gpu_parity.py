@@ -681,7 +681,7 @@ def test_streamed_trees_match_oracle(dtype, monkeypatch):
     keeps the staged kernels.  Counts spanning several tiles with a ragged end,
     in and out of place, against the tree and double-tree oracles bit for bit."""
     monkeypatch.setenv("AR_TREE_STAGED", "1")
-    monkeypatch.delenv("AR_TREE_STREAM", raising=False)
+    monkeypatch.setenv("AR_TREE_STREAM", "1")                  # at every size (by default from 1 MB per rank)
     u = LANES[dtype]
     for n in (2, 3, 5, 7, 16, 17, 19, 24, 33, 63, 64, 65, 72, 100, 127, 128):
         tile = 64 * (8 if n >= 64 else 2)                      # vectors per tile
