@@ -1,10 +1,14 @@
 """Measure the cost model's constants on the GPU and write ``calib_gfx950.txt``.
 
     python -m reduce_scatter_amd.calibrate [--out PATH] [--quick]
-    python -m reduce_scatter_amd.calibrate --schedules tree,dtree --merge BASE [--out PATH]
+    python -m reduce_scatter_amd.calibrate --schedules tree,dtree --ranks 32,72,128 --merge BASE [--out PATH]
 
-The second form re-measures only the named schedules (after a change to their
-kernels) and keeps every other schedule's constants from the file BASE.
+The second form re-measures only the named schedules at the named rank counts
+(after a change to the kernels that serve them) and keeps everything else from
+the file BASE: the other schedules, and the named schedules' launch, step and
+bandwidth constants and their other rank classes, so no rank class mixes
+constants measured on two boxes; the new rank classes' latency terms and
+corrections are fitted relative to BASE's constants.
 
 The planner prices every legal schedule s of a call as
 
@@ -126,12 +130,15 @@ def measure(ns, sizes, iters, rounds=3, dtype="f32", scheds=SCHEDS):
     return rows
 
 
-def fit(rows, latency=None):
+def fit(rows, latency=None, fixed=None):
     """Per (coll, sched): launch_us, step_us, bw_gbps, corr[SIZE_BINS].
 
     ``latency``: a fit of another element type whose launch, step and extra
     latency terms are kept (only the bandwidth terms are fitted here): the
-    2-byte types share the 4-byte types' latency model.
+    2-byte types share the 4-byte types' latency model.  ``fixed``:
+    {(coll, sched): (launch_us, step_us, bw_gbps)} kept as given (launch and
+    step ignored where ``latency`` has the entry); only the per-class terms
+    are fitted, relative to them.
 
     Fitted by regime: launch and per-step costs from the calls that move at
     most 1 MB (pure latency: t = launch + step * steps), the sustained
@@ -149,10 +156,13 @@ def fit(rows, latency=None):
                 continue
             small_all = [(n, us) for n, pr, us, b in pts if b <= (1 << 20)]
             small = [(n, us) for n, us in small_all if n <= 16]    # the compile-time-n kernels
+            keep = fixed.get((coll, sched)) if fixed else None
             if latency is not None and (coll, sched) in latency:
                 launch, step, _, _, extra = latency[(coll, sched)]
             else:
-                if sched in ("fused", "split") or len({n for n, _ in small}) < 2:
+                if keep is not None:
+                    launch, step = keep[0], keep[1]
+                elif sched in ("fused", "split") or len({n for n, _ in small}) < 2:
                     launch = float(np.median([us for _, us in small])) if small else 0.0
                     step = 0.0
                 else:
@@ -169,7 +179,7 @@ def fit(rows, latency=None):
             big = [(n, us, b) for n, pr, us, b in pts if b >= (1 << 30)]
             ref = big or [(n, us, b) for n, pr, us, b in pts]
             bws = [b / 1e3 / max(us - launch - step * _steps(coll, sched, n), 1e-3) for n, us, b in ref]
-            bw = float(np.median(bws))
+            bw = keep[2] if keep is not None else float(np.median(bws))
             corr = {}                                     # rank class -> [SIZE_BINS]
             per_bin = {}
             for n, pr, us, b in pts:
@@ -244,11 +254,34 @@ HEADER = ["# cost-model constants for libar (written by reduce_scatter_amd/calib
           "# bw2 / corr2: the same bandwidth terms fitted on bf16 (2-byte types; latency terms shared)"]
 
 
-def write(path, model, gpu_name, model2=None, base=None, scheds=SCHEDS):
+def base_constants(base):
+    """{(coll, sched): (launch, step, bw)} and {(coll, sched): (launch, step,
+    bw2)} of a calibration file as ``read_entries`` returns it."""
+    four, two = {}, {}
+    for key, lines in base[1].items():
+        for line in lines:
+            tok = line.split()
+            if tok[0] == "bw2":
+                two[key] = float(tok[3])
+            elif tok[0] not in ("corr", "lat", "corr2"):
+                four[key] = (float(tok[2]), float(tok[3]), float(tok[4]))
+    return four, {k: (four[k][0], four[k][1], v) for k, v in two.items() if k in four}
+
+
+def _row_class(line):
+    """The rank class of a corr / corr2 / lat line, else None."""
+    tok = line.split()
+    return int(tok[3]) if tok[0] in ("corr", "lat", "corr2") else None
+
+
+def write(path, model, gpu_name, model2=None, base=None, scheds=SCHEDS, classes=None):
     """The calibration file: ``model`` fitted on fp32 (every 4-byte type), and
     ``model2`` (bandwidth terms only) on bf16 for the 2-byte types.  With
     ``base`` (a calibration file as ``read_entries`` returns it), the entries
-    of the schedules outside ``scheds`` are kept from it."""
+    of the schedules outside ``scheds`` are kept from it; with ``classes`` (rank
+    classes ceil(log2 n)) as well, the named schedules keep BASE's lines too,
+    except their latency and correction rows of those classes, which come from
+    ``model`` (fitted relative to BASE's constants)."""
     entries = entry_lines(model, model2)
     header = [h if h is not None else "# device: %s" % gpu_name for h in HEADER]
     if base is not None:
@@ -256,10 +289,14 @@ def write(path, model, gpu_name, model2=None, base=None, scheds=SCHEDS):
         device = [h for h in base_header if h.startswith("# device:")]
         header[1] = device[0] if device else header[1]
         header += [h for h in base_header if h.startswith("# re-measured:")]
-        header.append("# re-measured: %s on %s" % (", ".join(scheds), gpu_name))
+        where = "" if classes is None else " for rank classes %s" % ", ".join(str(c) for c in sorted(classes))
+        header.append("# re-measured: %s%s on %s" % (", ".join(scheds), where, gpu_name))
         for key, lines in base_entries.items():
-            if key[1] not in scheds:
+            if key[1] not in scheds or key not in entries:
                 entries[key] = lines
+            elif classes is not None:
+                entries[key] = ([l for l in lines if _row_class(l) not in classes] +
+                                [l for l in entries[key] if _row_class(l) in classes])
     with open(path, "w") as f:
         for h in header:
             f.write(h + "\n")
@@ -273,13 +310,17 @@ def main(argv=None):
     p.add_argument("--out", default=DEFAULT_OUT)
     p.add_argument("--quick", action="store_true", help="fewer sizes and rank counts")
     p.add_argument("--schedules", default=",".join(SCHEDS), help="comma-separated schedules to measure")
-    p.add_argument("--merge", metavar="BASE", help="keep the other schedules' constants from this file")
+    p.add_argument("--ranks", help="comma-separated rank counts to measure (default: all)")
+    p.add_argument("--merge", metavar="BASE", help="keep everything not re-measured from this file")
     a = p.parse_args(argv)
     scheds = tuple(x for x in a.schedules.split(",") if x)
     if not scheds or any(x not in SCHEDS for x in scheds):
         p.error("--schedules takes a comma-separated subset of %s" % ",".join(SCHEDS))
-    if scheds != SCHEDS and not a.merge:
-        p.error("measuring a subset of the schedules needs --merge BASE for the others")
+    ranks = tuple(int(x) for x in a.ranks.split(",") if x) if a.ranks else None
+    if ranks is not None and (not ranks or any(r < 2 or r > 128 for r in ranks)):
+        p.error("--ranks takes rank counts from 2 to 128")
+    if (scheds != SCHEDS or ranks is not None) and not a.merge:
+        p.error("measuring a subset needs --merge BASE for the rest")
     import torch
     if not torch.cuda.is_available():
         print("calibrate: no GPU visible", file=sys.stderr)
@@ -287,14 +328,19 @@ def main(argv=None):
     torch.cuda.set_device(0)
     ns = (2, 8) if a.quick else (2, 4, 8, 16, 32, 72, 128)
     sizes = [1 << k for k in ((12, 16, 20, 24, 28) if a.quick else (10, 12, 14, 16, 18, 20, 21, 22, 23, 24, 25, 26, 27, 28, 29, 30))]
-    base = a.merge and read_entries(a.merge)             # read before --out may overwrite it
-    rows = measure(ns, sizes, iters=3 if a.quick else 5, scheds=scheds)
-    model = fit(rows)
     ns2 = (8,) if a.quick else (2, 4, 8, 16, 72)
-    rows2 = measure(ns2, sizes, iters=3 if a.quick else 5, dtype="bf16", scheds=scheds)
-    model2 = fit(rows2, latency=model)
+    base = read_entries(a.merge) if a.merge else None   # read before --out may overwrite it
+    fixed = fixed2 = classes = None
+    if ranks is not None:
+        ns, ns2 = ranks, tuple(r for r in ranks if r in ns2)
+        classes = {math.ceil(math.log2(r)) for r in ranks}
+        fixed, fixed2 = base_constants(base)
+    rows = measure(ns, sizes, iters=3 if a.quick else 5, scheds=scheds)
+    model = fit(rows, fixed=fixed)
+    rows2 = measure(ns2, sizes, iters=3 if a.quick else 5, dtype="bf16", scheds=scheds) if ns2 else []
+    model2 = fit(rows2, latency=model, fixed=fixed2)
     gpu = torch.cuda.get_device_name(0) + " " + getattr(torch.cuda.get_device_properties(0), "gcnArchName", "")
-    write(a.out, model, gpu, model2, base=base, scheds=scheds)
+    write(a.out, model, gpu, model2, base=base, scheds=scheds, classes=classes)
     for (coll, sched), (launch, step, bw, corr, extra) in sorted(model.items()):
         print("%-15s %-6s launch %7.2f us  step %6.3f us  bw %7.1f GB/s  extra %s" % (
             coll, sched, launch, step, bw, {k: round(v, 1) for k, v in extra.items()}))

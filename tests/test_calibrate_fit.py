@@ -85,3 +85,32 @@ def test_merge_replaces_only_the_remeasured_schedules(tmp_path):
             assert lines == cal.entry_lines(part)[key] and lines != base[1][key]
         else:
             assert lines == base[1][key]
+
+
+def test_merge_by_rank_class_keeps_the_base_constants(tmp_path):
+    """``--ranks``: the re-measured schedule keeps BASE's launch, step and
+    bandwidth line and its other rank classes; only the named classes' rows
+    are replaced, fitted relative to BASE's bandwidth (a 1.5x slower
+    re-measurement at 16 ranks shows as corrections near 1/1.5 there)."""
+    full = cal.fit(_rows(False))
+    base_path = tmp_path / "base.txt"
+    cal.write(str(base_path), full, "box A")
+    base = cal.read_entries(str(base_path))
+    fixed, _ = cal.base_constants(base)
+    assert fixed[("allreduce", "ring")] == tuple(float(x) for x in base[1][("allreduce", "ring")][0].split()[2:5])
+    rows = [(c, s, n, pr, us * 1.5) for c, s, n, pr, us in _rows(False) if s == "ring" and n == 16]
+    part = cal.fit(rows, fixed=fixed)
+    out = tmp_path / "merged.txt"
+    cal.write(str(out), part, "box B", base=base, scheds=("ring",), classes={4})
+    header, entries = cal.read_entries(str(out))
+    assert "# re-measured: ring for rank classes 4 on box B" in header
+    ring, old = entries[("allreduce", "ring")], base[1][("allreduce", "ring")]
+    assert ring[0] == old[0]                                        # launch, step, bandwidth kept
+    assert [l for l in ring if cal._row_class(l) in (1, 3)] == [l for l in old if cal._row_class(l) in (1, 3)]
+    new4 = [l for l in ring if l.startswith("corr ") and cal._row_class(l) == 4]
+    assert len(new4) == 1
+    big = [float(x) for x in new4[0].split()[4:]][32:]             # footprints of 4 GB and more
+    assert all(abs(c - 1 / 1.5) < 0.05 for c in big)
+    for key, lines in entries.items():
+        if key[1] != "ring":
+            assert lines == base[1][key]
