@@ -29,7 +29,8 @@
 // lane spaced by the wavefront width: each load is one 1 KB run of one rank,
 // and a tile reads U KB of each rank in turn, the loads of the next D-1 ranks
 // in flight while one is combined (D register buffers in rotation).  The
-// stack lives in LDS, one region per wavefront sized to the program's depth:
+// stack lives in LDS, one region per wavefront at least the program's depth
+// (below 96 ranks a larger reservation caps the wavefronts per compute unit):
 // its depth is a uniform value, so a push or a pop is one LDS access per
 // vector at a uniform offset, each lane to its own words (held in registers
 // instead, the slots needed a branch per slot on every access, which the
@@ -45,13 +46,18 @@
 namespace ar {
 
 // The tile shape by rank count, measured on MI355X (fp32 sum, in place, per
-// cent of 8 TB/s; 2 / 8 vectors per lane with 4 / 2 buffers): 17 ranks at
-// 128 MB per rank 74 / 67, 24 at 64 MB 70 / 65, 33 at 64 MB 69 / 65, 72 at
-// 25 MB 61 / 61-62, 100 at 16 MB 54 / 61, 128 at 8 MB 56 / 71-72.  Few ranks
-// want many waves and deep prefetch; many ranks want long runs of each rank
-// (8 KB per wavefront) and fewer tiles.  Other shapes measured (2 vectors with
-// 3 buffers, 4 with 2-4, 4 waves per workgroup) were no better anywhere.
-constexpr int kStreamWideRanks = 64;
+// cent of 8 TB/s).  Below 96 ranks, 2 vectors per lane with 4 buffers, and a
+// 48 KB LDS reservation per wavefront (three per compute unit: more waves
+// means more concurrent rank streams and worse DRAM locality; with 60 VGPRs
+// nothing else limits them): 17 ranks at 128 MB per rank 76-77, 33 at 64 MB
+// 73, 48 at 32 MB 70, 63 at 32 MB 69, 72 at 25 MB 65 (no reservation: 66, 64,
+// -, -, 60; 32 KB: 77, 72, 68, 66, 62; 56 KB: 64, 66, 66, 67, 64).  From 96
+// ranks, 8 vectors per lane with 2 buffers (8 KB runs of each rank; the stack
+// alone reserves 48-56 KB): 100 ranks at 16 MB 62-63 against 59-61, 128 at 8 MB
+// 70-72 against 59.  Other shapes measured (2 vectors with 3 buffers, 4 with
+// 2-4, 4 waves per workgroup) were no better anywhere.
+constexpr int kStreamWideRanks = 96;
+constexpr size_t kStreamNarrowLds = 48 << 10;
 
 // Launches under 1 MB per rank keep the staged kernels.  A wavefront walks
 // the n ranks one after another, so a small call costs about n dependent load
@@ -141,8 +147,8 @@ __global__ __launch_bounds__(kFusedThreads) void tree_stream_kernel(const RankTa
     const auto rank_of = [&](int v) { return f + v < n ? f + v : f + v - n; };
     u32x4 buf[D][U];
 #pragma unroll
-    for (int k = 0; k + 1 < D; ++k)
-        if (k < n) stream_load<U>(buf[k], t.src[rank_of(k)], base, off);
+    for (int k = 0; k + 1 < D; ++k)                            // (past n, a harmless re-read of rank n-1: a load
+        stream_load<U>(buf[k], t.src[rank_of(k < n ? k : n - 1)], base, off);   // under a branch cost copies)
     // Whole rounds in which every next rank exists, so every load is issued
     // unconditionally and each step waits only for its own buffer (loads
     // under a branch make the wait counts conservative: a step then waited
@@ -253,20 +259,20 @@ bool launch_tree_stream_range(int dt, int op, const RankTable &t, const TreeShap
     int depth = 0;
     // the first tree and the mirror image walk from rank 0, the shifted tree from rank 1
     if (!(tree_program(tree, g.n, 0, prog, depth) || tree_program(tree, g.n, 1, prog, depth))) return false;
-    const auto go = [&](auto Uc, auto Dc) {
+    const auto go = [&](auto Uc, auto Dc, size_t lds) {
         constexpr int U = decltype(Uc)::value, D = decltype(Dc)::value;
         const long long tiles = aligned_tiles(hi - lo, (long long)kFusedThreads * U);
         if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
-        const size_t lds = (size_t)depth * U * kFusedThreads * 16;
+        const size_t stack = (size_t)depth * U * kFusedThreads * 16;
         return dispatch(dt, op, [&](auto Dt, auto O) {
-            return launch(tree_stream_kernel<decltype(Dt)::value, decltype(O)::value, U, D>,
-                          dim3((unsigned)tiles), dim3(kFusedThreads), lds, s, t, prog, g, lo, hi);
+            return launch(tree_stream_kernel<decltype(Dt)::value, decltype(O)::value, U, D>, dim3((unsigned)tiles),
+                          dim3(kFusedThreads), stack > lds ? stack : lds, s, t, prog, g, lo, hi);
         });
     };
     if (g.n >= kStreamWideRanks)
-        *err = go(std::integral_constant<int, 8>(), std::integral_constant<int, 2>());
+        *err = go(std::integral_constant<int, 8>(), std::integral_constant<int, 2>(), (size_t)0);
     else
-        *err = go(std::integral_constant<int, 2>(), std::integral_constant<int, 4>());
+        *err = go(std::integral_constant<int, 2>(), std::integral_constant<int, 4>(), kStreamNarrowLds);
     return true;
 }
 
