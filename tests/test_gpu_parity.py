@@ -699,6 +699,26 @@ def test_streamed_trees_match_oracle(dtype, monkeypatch):
                                           % (sched, n, dtype, op, r, inplace))
 
 
+@pytest.mark.parametrize("n", [33, 100])
+def test_streamed_trees_at_their_default_sizes(n, monkeypatch):
+    """The walk as callers get it (no override): 2.5 MB per rank, so each half
+    of the double tree is over the 1 MB-per-rank launch threshold; 33 ranks
+    (2 KB runs with the residency reservation, the shifted second tree walked
+    from rank 1) and 100 ranks (8 KB runs); fp32 avg and bf16 sum, against the
+    tree and double-tree oracles bit for bit on every rank."""
+    monkeypatch.delenv("AR_TREE_STREAM", raising=False)
+    monkeypatch.delenv("AR_TREE_STAGED", raising=False)
+    for dtype, op in (("f32", "avg"), ("bf16", "sum")):
+        count = (5 << 19) // (4 if dtype == "f32" else 2) + LANES[dtype] * 3 + 1
+        xs = inputs(90 + n, n, count, dtype, op)
+        for sched in ("tree", "dtree"):
+            print("default-size streamed %s n=%d %s %s count=%d" % (sched, n, dtype, op, count), flush=True)
+            want = reference(sched, xs, dtype, op)
+            got = run_allreduce(xs, dtype, op, sched)
+            for r in range(n):
+                assert_bits_equal(got[r], want[r], "default-size %s n=%d %s %s rank %d" % (sched, n, dtype, op, r))
+
+
 def test_randomized_calls_match_oracle():
     """400 seeded random calls: collective, n (1-20 and 72), dtype, op,
     schedule, numerics options, element counts (log-uniform, ragged), in place
