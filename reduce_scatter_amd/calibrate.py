@@ -50,6 +50,13 @@ def _steps(coll, sched, n):
     return 2 * depth
 
 
+def rank_class(n):
+    """The planner's rank class: ceil(log2 n), with 97-128 ranks a class (8) of
+    their own apart from 65-96 (7)."""
+    k = math.ceil(math.log2(n)) if n > 1 else 0
+    return (8 if n > 96 else 7) if k >= 7 else k
+
+
 def _bytes(coll, n, per_rank):
     """Algorithmic HBM bytes; per_rank = bytes of one rank's all-reduce buffer,
     reduce-scatter input or all-gather output."""
@@ -171,9 +178,9 @@ def fit(rows, latency=None, fixed=None):
                     (launch, step), *_ = np.linalg.lstsq(A, t, rcond=None)
                     launch, step = max(float(launch), 0.0), max(float(step), 0.0)
                 extra = {}                                # rank class -> latency beyond launch + step * steps
-                for rc in sorted({math.ceil(math.log2(n)) for n, _ in small_all}):
+                for rc in sorted({rank_class(n) for n, _ in small_all}):
                     res = [us - launch - step * _steps(coll, sched, n) for n, us in small_all
-                           if math.ceil(math.log2(n)) == rc]
+                           if rank_class(n) == rc]
                     if abs(float(np.median(res))) > 1.0:
                         extra[rc] = float(np.median(res))
             big = [(n, us, b) for n, pr, us, b in pts if b >= (1 << 30)]
@@ -183,10 +190,10 @@ def fit(rows, latency=None, fixed=None):
             corr = {}                                     # rank class -> [SIZE_BINS]
             per_bin = {}
             for n, pr, us, b in pts:
-                term = us - launch - step * _steps(coll, sched, n) - extra.get(math.ceil(math.log2(n)), 0.0)
+                term = us - launch - step * _steps(coll, sched, n) - extra.get(rank_class(n), 0.0)
                 if term < 0.25 * us:                      # latency-bound: no bandwidth information
                     continue
-                key = (math.ceil(math.log2(n)), int(math.log2(b)))
+                key = (rank_class(n), int(math.log2(b)))
                 per_bin.setdefault(key, []).append(b / 1e3 / term / bw)
             for rc in sorted({k for k, _ in per_bin}):
                 row = [1.0] * SIZE_BINS
@@ -249,8 +256,8 @@ def read_entries(path):
 HEADER = ["# cost-model constants for libar (written by reduce_scatter_amd/calibrate.py)",
           None,
           "# <coll> <sched> <launch_us> <step_us> <bw_GBps>            (fitted on fp32: every 4-byte type)",
-          "# corr <coll> <sched> <ceil(log2 n)> <bandwidth factor for log2(total algorithmic bytes) = 0..47>",
-          "# lat <coll> <sched> <ceil(log2 n)> <latency beyond launch + step * steps, us>",
+          "# corr <coll> <sched> <rank class: ceil(log2 n), 8 above 96> <bandwidth factor for log2(total algorithmic bytes) = 0..47>",
+          "# lat <coll> <sched> <rank class> <latency beyond launch + step * steps, us>",
           "# bw2 / corr2: the same bandwidth terms fitted on bf16 (2-byte types; latency terms shared)"]
 
 
@@ -333,7 +340,7 @@ def main(argv=None):
     fixed = fixed2 = classes = None
     if ranks is not None:
         ns, ns2 = ranks, tuple(r for r in ranks if r in ns2)
-        classes = {math.ceil(math.log2(r)) for r in ranks}
+        classes = {rank_class(r) for r in ranks}
         fixed, fixed2 = base_constants(base)
     rows = measure(ns, sizes, iters=3 if a.quick else 5, scheds=scheds)
     model = fit(rows, fixed=fixed)

@@ -57,7 +57,11 @@ constexpr int kColls = 3;
 constexpr int kScheds = 6;         // indexed by ar_sched_t; 0 (auto) unused
 constexpr int kSizeBins = 48;      // per-size correction for log2(algorithmic bytes of the call) = 0..47
 
-constexpr int kRankClasses = 8;    // ceil(log2 n) = 0..7 for n = 1..128
+// Rank classes: ceil(log2 n) = 0..7 for n = 1..96, and 8 for 97..128.  The
+// top octave is split because the schedules rank differently across it: at
+// 72 ranks split led the one-pass schedules on most boxes, at 128 (8 MB per
+// rank) fused led split by up to 10 %, and one class averaged the two.
+constexpr int kRankClasses = 9;
 
 // Bandwidth of one element-size class: a sustained rate and the per-(rank
 // class, footprint) correction.  4-byte types (fp32, int32) and 2-byte types
@@ -75,6 +79,7 @@ struct Entry {
     Bandwidth b4, b2;                  // 4-byte and 2-byte element types
     bool have_b2 = false;              // a 2-byte rate was read (else 2-byte calls use b4)
     double extra_us[kRankClasses];     // measured latency beyond launch + step * steps, per rank class
+    bool lat_read[kRankClasses];       // a lat row was read for this rank class
     bool set = false;
 };
 
@@ -104,7 +109,10 @@ void set_defaults(Calib &c) {
                 }
             }
             e.have_b2 = false;
-            for (int k2 = 0; k2 < kRankClasses; ++k2) e.extra_us[k2] = 0.0;
+            for (int k2 = 0; k2 < kRankClasses; ++k2) {
+                e.extra_us[k2] = 0.0;
+                e.lat_read[k2] = false;
+            }
             e.set = true;
         }
 }
@@ -162,7 +170,10 @@ void load_file(Calib &c, const std::string &path) {
         double extra = 0;
         if (sscanf(line, "lat %31s %31s %d %lf", coll, sched, &rc, &extra) == 4) {
             int k = coll_index(coll), s = sched_index(sched);
-            if (k >= 0 && s >= 0 && rc >= 0 && rc < kRankClasses) c.e[k][s].extra_us[rc] = extra;
+            if (k >= 0 && s >= 0 && rc >= 0 && rc < kRankClasses) {
+                c.e[k][s].extra_us[rc] = extra;
+                c.e[k][s].lat_read[rc] = true;
+            }
             continue;
         }
         if (sscanf(line, "bw2 %31s %31s %lf", coll, sched, &bw) == 3) {
@@ -212,7 +223,8 @@ void init_calib() {
 int rank_class(int n) {
     int k = 0;
     while ((1 << k) < n) ++k;
-    return k < kRankClasses ? k : kRankClasses - 1;
+    if (k >= 7) return n > 96 ? 8 : 7;
+    return k;
 }
 
 // The measured correction row nearest to rank class k (nullptr if none).
@@ -222,6 +234,19 @@ const double *corr_row(const Bandwidth &b, int k) {
         if (k + d < kRankClasses && b.measured[k + d]) return b.corr[k + d];
     }
     return nullptr;
+}
+
+// Latency beyond launch + step * steps for rank class k: the class's own term
+// where the calibration measured the class (a lat or corr row; zero if it
+// wrote no lat row, having found none worth writing), else that of the
+// nearest measured class.
+double extra_latency(const Entry &e, int k) {
+    const auto measured = [&](int j) { return e.lat_read[j] || e.b4.measured[j]; };
+    for (int d = 0; d < kRankClasses; ++d) {
+        if (k - d >= 0 && measured(k - d)) return e.extra_us[k - d];
+        if (k + d < kRankClasses && measured(k + d)) return e.extra_us[k + d];
+    }
+    return 0.0;
 }
 
 // Bandwidth (GB/s) of schedule entry ``e`` for a call of element size ``elem``
@@ -298,7 +323,7 @@ ar_status_t make_plan(ar_coll_t coll, size_t count, ar_dtype_t dtype, ar_op_t op
         const Entry &c = g_calib.e[coll][s];
         out->bytes[s] = bytes;
         const double bw = bandwidth(c, (int)e, rclass, bin);       // GB/s = 1e3 bytes per microsecond
-        out->predicted_us[s] = c.launch_us + c.step_us * out->steps[s] + c.extra_us[rclass] + bytes / (bw * 1e3);
+        out->predicted_us[s] = c.launch_us + c.step_us * out->steps[s] + extra_latency(c, rclass) + bytes / (bw * 1e3);
         if (!have || out->predicted_us[s] < best) {
             best = out->predicted_us[s];
             out->chosen = (ar_sched_t)s;

@@ -245,6 +245,33 @@ def test_plan_is_monotone_in_size_with_default_constants():
     assert times == sorted(times)
 
 
+def test_plan_rank_classes_split_the_top_octave(tmp_path):
+    """Rank class ceil(log2 n), except 97-128 ranks (class 8) apart from 65-96
+    (class 7): each takes its own correction row, and a class with no row
+    takes the nearest measured one.  The latency term likewise: a class the
+    file measured (a lat or corr row) takes its own, zero without a lat row;
+    a class it did not measure takes the nearest measured class's."""
+    f = tmp_path / "classes.txt"
+    half = " ".join(["0.5"] * 48)
+    one = " ".join(["1.0"] * 48)
+    f.write_text("allreduce fused 10 0 1000\nallreduce split 10 0 1000\nallreduce ring 1000 0 1000\n"
+                 "allreduce tree 1000 0 1000\nallreduce dtree 1000 0 1000\n"
+                 "corr allreduce fused 7 " + one + "\ncorr allreduce fused 8 " + half + "\n"
+                 "corr allreduce split 5 " + one + "\nlat allreduce split 5 3.0\n"
+                 "corr allreduce split 7 " + one + "\n")
+    count = 1 << 16
+    calls = [("allreduce", count, "f32", "sum", n) for n in (72, 96, 97, 128, 40, 33)]
+    p72, p96, p97, p128, p40, p33 = _plan_in_subprocess(str(f), calls)
+    for p, n in ((p72, 72), (p96, 96), (p97, 97), (p128, 128)):
+        b = 2 * n * count * 4
+        corr = 0.5 if n > 96 else 1.0
+        assert abs(p["predicted_us"]["fused"] - (10 + b / 1e3 / (1000 * corr))) < 1e-6, n
+        assert abs(p["predicted_us"]["split"] - (10 + b / 1e3 / 1000)) < 1e-6, n    # class 7 measured, no lat row
+    for p, n in ((p40, 40), (p33, 33)):                         # class 6: no row; split's nearest is class 5
+        b = 2 * n * count * 4
+        assert abs(p["predicted_us"]["split"] - (10 + 3.0 + b / 1e3 / 1000)) < 1e-6, n
+
+
 def test_plan_reads_the_calibration_file(tmp_path):
     """Constants and the (rank class x footprint) correction come from the file:
     t = launch + step * steps + bytes / (bw * corr)."""
