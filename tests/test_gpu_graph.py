@@ -73,6 +73,24 @@ def test_allreduce_captured(sched):
     _replays(g, xs, ys, eager)
 
 
+@pytest.mark.parametrize("sched", ["tree", "dtree"])
+def test_tree_walk_captured(sched):
+    """The streaming tree walk past 16 ranks (33 ranks, 2.5 MB per rank, so
+    each half of the double tree is over the walk's size threshold; the
+    shifted second tree walked from rank 1), captured and replayed."""
+    n, count = 33, (5 << 19) // 4 + 7
+    xs = [torch.empty(count, device="cuda") for _ in range(n)]
+    ys = [torch.empty(count, device="cuda") for _ in range(n)]
+    X, Y = ar.pointers(xs), ar.pointers(ys)
+    g = _capture(lambda: ar.ar_allreduce(X, Y, count, "f32", "avg", sched=sched))
+
+    def eager():
+        zs = [torch.empty_like(y) for y in ys]
+        ar.ar_allreduce([x.clone() for x in xs], zs, count, "f32", "avg", sched=sched)
+        return zs
+    _replays(g, xs, ys, eager)
+
+
 def test_reduce_scatter_then_all_gather_captured():
     n, R = 8, 4096 + 64
     xs = [torch.empty(n * R, dtype=torch.bfloat16, device="cuda") for _ in range(n)]
