@@ -156,6 +156,11 @@ hipError_t launch_tree_reg_allreduce(bool dual, int dt, int op, const RankTable 
 // leaves the call to the LDS-staged kernels.
 bool launch_tree_stream_range(int dt, int op, const RankTable &t, const TreeShape &tree, const Geometry &g,
                               long long lo, long long hi, hipStream_t s, hipError_t *err);
+// Both halves of the double tree, [lo0, hi0) up ``tree`` and [lo1, hi1) up
+// ``tree2``, in one streaming launch when the walk holds both (as above).
+bool launch_dtree_stream(int dt, int op, const RankTable &t, const TreeShape &tree, const TreeShape &tree2,
+                         const Geometry &g, long long lo0, long long hi0, long long lo1, long long hi1, hipStream_t s,
+                         hipError_t *err);
 hipError_t launch_tree_allreduce(int dt, int op, const RankTable &t, const TreeShape &tree, const Geometry &g,
                                  int cus, hipStream_t s);
 hipError_t launch_dtree_allreduce(int dt, int op, const RankTable &t, const TreeShape &tree, const TreeShape &tree2,

@@ -30,7 +30,9 @@
 //
 // The double binary tree (same section: a second tree with the roles of
 // leaves and interior ranks swapped, and half of every buffer sent up each)
-// is two launches of the same kernels, one per half and shape.  On one GPU
+// is one streaming launch for both halves where the walk holds both trees
+// (and they need the same LDS), else one launch per half and shape, each
+// streamed or staged.  On one GPU
 // there are no per-rank links to balance, so it costs what the single tree
 // costs; its results differ from the single tree's in the second half.
 #include <cstdlib>
@@ -284,6 +286,8 @@ hipError_t launch_tree_allreduce(int dt, int op, const RankTable &t, const TreeS
 
 hipError_t launch_dtree_allreduce(int dt, int op, const RankTable &t, const TreeShape &tree, const TreeShape &tree2,
                                   const Geometry &g, int cus, hipStream_t s) {
+    hipError_t streamed;                                       // both halves in one streaming launch
+    if (launch_dtree_stream(dt, op, t, tree, tree2, g, 0, g.split, g.split2, g.Vfull, s, &streamed)) return streamed;
     const hipError_t e = launch_tree_range(dt, op, t, tree, g, 0, g.split, cus, s);
     if (e != hipSuccess) return e;
     return launch_tree_range(dt, op, t, tree2, g, g.split2, g.Vfull, cus, s);

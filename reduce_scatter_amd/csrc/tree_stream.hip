@@ -23,7 +23,9 @@
 // the staged kernels', in the same order, so the results are identical (the
 // host runs each program on node ids and refuses any that would not reproduce
 // the tree).  After the last rank the stack holds the root's partial; the
-// postOp is applied and the value stored to every rank.
+// postOp is applied and the value stored to every rank.  The double tree's two
+// halves, each with its own program, share one launch where they need the
+// same LDS.
 //
 // One wavefront per tile of 64*U vectors on an address-aligned grid, U per
 // lane spaced by the wavefront width: each load is one 1 KB run of one rank,
@@ -83,6 +85,15 @@ struct TreeProgram {
     int first;
 };
 
+// One launch's work: one range of frame vectors, or the double tree's two
+// halves, each range with its own program.  The grid holds range 0's tiles,
+// then range 1's, so the halves share one launch and its drain.
+struct StreamWork {
+    TreeProgram prog[2];
+    long long lo[2], hi[2];
+    long long tiles0;          // grid tiles of range 0
+};
+
 template <int U> __device__ __forceinline__ void stream_load(u32x4 (&b)[U], const void *src, long long base,
                                                          const unsigned (&off)[U]) {
     const char *p = (const char *)src + base;
@@ -90,19 +101,27 @@ template <int U> __device__ __forceinline__ void stream_load(u32x4 (&b)[U], cons
     for (int u = 0; u < U; ++u) b[u] = __builtin_nontemporal_load((const u32x4 *)(p + off[u]));
 }
 
-// One step of the walk on the rank whose vectors ``b`` holds.  The stack keeps
-// partials in the storage type (every combine already rounds to it, so
-// packing is exact): 16 bytes per vector whatever the type, slot k of vector
-// u at stack[(k * U + u) * 64] from the lane's own word.
+// The stack of partials, in the storage type (every combine already rounds
+// to it, so packing is exact): 16 bytes per vector whatever the type, slot k
+// of vector u at lds[(k * U + u) * 64] from the lane's own word.  (Slot 0 in
+// registers instead, one LDS slot less per wavefront, measured -8 to +14
+// points depending on the rank count: not kept.)
+template <int U> struct Stack {
+    u32x4 *lds;
+    __device__ __forceinline__ u32x4 get(int k, int u) const { return lds[(k * U + u) * kFusedThreads]; }
+    __device__ __forceinline__ void put(int k, int u, const u32x4 &v) { lds[(k * U + u) * kFusedThreads] = v; }
+};
+
+// One step of the walk on the rank whose vectors ``b`` holds.
 template <int DT, int OP, int U>
-__device__ __forceinline__ void stream_step(const u32x4 (&b)[U], int op, u32x4 *stack, int &sp, float s) {
+__device__ __forceinline__ void stream_step(const u32x4 (&b)[U], int op, Stack<U> &st, int &sp, float s) {
     Pack<DT> acc[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) acc[u] = first<DT, OP>(unpack<DT>(b[u]), s);
     if (op & 1) {                                              // the child visited before: its finished partial
         --sp;
 #pragma unroll
-        for (int u = 0; u < U; ++u) merge<DT, OP>(acc[u], unpack<DT>(stack[(sp * U + u) * kFusedThreads]));
+        for (int u = 0; u < U; ++u) merge<DT, OP>(acc[u], unpack<DT>(st.get(sp, u)));
     }
     if (!(op & 2)) {                                           // the subtree is finished
         const int levels = (op >> 2) & 7;
@@ -110,36 +129,40 @@ __device__ __forceinline__ void stream_step(const u32x4 (&b)[U], int op, u32x4 *
             --sp;
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                Pack<DT> a = unpack<DT>(stack[(sp * U + u) * kFusedThreads]);
+                Pack<DT> a = unpack<DT>(st.get(sp, u));
                 merge<DT, OP>(a, acc[u]);
                 acc[u] = a;
             }
             if ((op >> (5 + k)) & 1) {                         // the ancestor's other child, the higher rank
                 --sp;
 #pragma unroll
-                for (int u = 0; u < U; ++u) merge<DT, OP>(acc[u], unpack<DT>(stack[(sp * U + u) * kFusedThreads]));
+                for (int u = 0; u < U; ++u) merge<DT, OP>(acc[u], unpack<DT>(st.get(sp, u)));
             }
         }
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) stack[(sp * U + u) * kFusedThreads] = pack<DT>(acc[u]);
+    for (int u = 0; u < U; ++u) st.put(sp, u, pack<DT>(acc[u]));
     ++sp;                                                      // pending (child to come) or finished
 }
 
 template <int DT, int OP, int U, int D>
-__global__ __launch_bounds__(kFusedThreads) void tree_stream_kernel(const RankTable t, const TreeProgram prog,
-                                                        const Geometry g, long long lo, long long hi) {
+__global__ __launch_bounds__(kFusedThreads) void tree_stream_kernel(const RankTable t, const StreamWork wk,
+                                                                    const Geometry g) {
     constexpr long long T = (long long)kFusedThreads * U;
     extern __shared__ u32x4 stream_stack[];
     const int n = g.n;
-    const TileSpan ts = aligned_tile(lo, hi, (long long)blockIdx.x, g.ref, T);
+    const long long b = blockIdx.x;
+    const int h = b < wk.tiles0 ? 0 : 1;                       // uniform: this workgroup's range
+    const TreeProgram &prog = wk.prog[h];
+    const TileSpan ts = aligned_tile(wk.lo[h], wk.hi[h], h ? b - wk.tiles0 : b, g.ref, T);
     if (ts.lo >= ts.hi) return;
     unsigned off[U];
     bool ok[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) off[u] = tile_lane(ts, ts.start + threadIdx.x + u * kFusedThreads, ok[u]);
     const long long base = ts.lo * 16;
-    u32x4 *stack = stream_stack + threadIdx.x;
+    Stack<U> st;
+    st.lds = stream_stack + threadIdx.x;
     int sp = 0;                                                // uniform: the same program for every lane
 
     // Step v visits rank (first + v) mod n; buffer v % D holds it.
@@ -158,14 +181,14 @@ __global__ __launch_bounds__(kFusedThreads) void tree_stream_kernel(const RankTa
 #pragma unroll
         for (int k = 0; k < D; ++k) {
             stream_load<U>(buf[(k + D - 1) % D], t.src[rank_of(v + k + D - 1)], base, off);
-            stream_step<DT, OP, U>(buf[k], (int)prog.op[v + k], stack, sp, g.s);
+            stream_step<DT, OP, U>(buf[k], (int)prog.op[v + k], st, sp, g.s);
         }
     }
 #pragma unroll
     for (int k = 0; k < 2 * D - 2; ++k) {
         if (v + k < n) {
             if (v + k + D - 1 < n) stream_load<U>(buf[(k + D - 1) % D], t.src[rank_of(v + k + D - 1)], base, off);
-            stream_step<DT, OP, U>(buf[k % D], (int)prog.op[v + k], stack, sp, g.s);
+            stream_step<DT, OP, U>(buf[k % D], (int)prog.op[v + k], st, sp, g.s);
         }
     }
 
@@ -173,7 +196,7 @@ __global__ __launch_bounds__(kFusedThreads) void tree_stream_kernel(const RankTa
     u32x4 w[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        root[u] = unpack<DT>(stack[u * kFusedThreads]);
+        root[u] = unpack<DT>(st.get(0, u));
         finish<DT, OP>(root[u], n, g);
         w[u] = pack<DT>(root[u]);
     }
@@ -251,22 +274,48 @@ static int tree_stream_mode() {
     return 2;
 }
 
-bool launch_tree_stream_range(int dt, int op, const RankTable &t, const TreeShape &tree, const Geometry &g,
-                              long long lo, long long hi, hipStream_t s, hipError_t *err) {
+// The walk over ``halves`` ranges, range h of the vectors [lo[h], hi[h]) up
+// ``*trees[h]``, in one launch; false (nothing launched) when a range is under
+// the size threshold or a tree is not one the walk holds.
+static bool launch_stream(int dt, int op, const RankTable &t, const TreeShape *const *trees, int halves,
+                          const Geometry &g, const long long *lo, const long long *hi, hipStream_t s,
+                          hipError_t *err) {
     const int mode = tree_stream_mode();
-    if (mode == 0 || lo >= hi || (mode == 2 && (hi - lo) * 16 < kStreamMinBytes)) return false;
-    TreeProgram prog;
-    int depth = 0;
-    // the first tree and the mirror image walk from rank 0, the shifted tree from rank 1
-    if (!(tree_program(tree, g.n, 0, prog, depth) || tree_program(tree, g.n, 1, prog, depth))) return false;
+    if (mode == 0) return false;
+    StreamWork wk;
+    int depth = 0, depths[2] = {0, 0};
+    bool any = false;
+    for (int h = 0; h < 2; ++h) {
+        wk.lo[h] = h < halves ? lo[h] : 0;
+        wk.hi[h] = h < halves && hi[h] > lo[h] ? hi[h] : wk.lo[h];
+        if (wk.hi[h] == wk.lo[h]) continue;
+        if (mode == 2 && (wk.hi[h] - wk.lo[h]) * 16 < kStreamMinBytes) return false;
+        int d = 0;
+        // the first tree and the mirror image walk from rank 0, the shifted tree from rank 1
+        if (!(tree_program(*trees[h], g.n, 0, wk.prog[h], d) || tree_program(*trees[h], g.n, 1, wk.prog[h], d)))
+            return false;
+        depth = d > depth ? d : depth;
+        depths[h] = d;
+        any = true;
+    }
+    if (!any) return false;
+    // Two ranges share a launch only where they need the same LDS: from 96
+    // ranks the reservation is the stack's depth, and one launch at the deeper
+    // half's depth cut the other half's wavefronts per compute unit (128 ranks,
+    // 8 MB per rank, depths 7 and 6: 69-70 % in one launch, 75 % in two);
+    // below 96 the 48 KB reservation is the same for both, and one launch
+    // gained 1-4 points (17, 33 and 72 ranks) over two.
+    if (halves == 2 && g.n >= kStreamWideRanks && depths[0] && depths[1] && depths[0] != depths[1]) return false;
     const auto go = [&](auto Uc, auto Dc, size_t lds) {
         constexpr int U = decltype(Uc)::value, D = decltype(Dc)::value;
-        const long long tiles = aligned_tiles(hi - lo, (long long)kFusedThreads * U);
+        const long long T = (long long)kFusedThreads * U;
+        wk.tiles0 = wk.hi[0] > wk.lo[0] ? aligned_tiles(wk.hi[0] - wk.lo[0], T) : 0;
+        const long long tiles = wk.tiles0 + (wk.hi[1] > wk.lo[1] ? aligned_tiles(wk.hi[1] - wk.lo[1], T) : 0);
         if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
         const size_t stack = (size_t)depth * U * kFusedThreads * 16;
         return dispatch(dt, op, [&](auto Dt, auto O) {
             return launch(tree_stream_kernel<decltype(Dt)::value, decltype(O)::value, U, D>, dim3((unsigned)tiles),
-                          dim3(kFusedThreads), stack > lds ? stack : lds, s, t, prog, g, lo, hi);
+                          dim3(kFusedThreads), stack > lds ? stack : lds, s, t, wk, g);
         });
     };
     if (g.n >= kStreamWideRanks)
@@ -274,6 +323,20 @@ bool launch_tree_stream_range(int dt, int op, const RankTable &t, const TreeShap
     else
         *err = go(std::integral_constant<int, 2>(), std::integral_constant<int, 4>(), kStreamNarrowLds);
     return true;
+}
+
+bool launch_tree_stream_range(int dt, int op, const RankTable &t, const TreeShape &tree, const Geometry &g,
+                              long long lo, long long hi, hipStream_t s, hipError_t *err) {
+    const TreeShape *trees[1] = {&tree};
+    return launch_stream(dt, op, t, trees, 1, g, &lo, &hi, s, err);
+}
+
+bool launch_dtree_stream(int dt, int op, const RankTable &t, const TreeShape &tree, const TreeShape &tree2,
+                         const Geometry &g, long long lo0, long long hi0, long long lo1, long long hi1, hipStream_t s,
+                         hipError_t *err) {
+    const TreeShape *trees[2] = {&tree, &tree2};
+    const long long lo[2] = {lo0, lo1}, hi[2] = {hi0, hi1};
+    return launch_stream(dt, op, t, trees, 2, g, lo, hi, s, err);
 }
 
 }  // namespace ar
