@@ -54,10 +54,13 @@ namespace ar {
 // nothing else limits them): 17 ranks at 128 MB per rank 76-77, 33 at 64 MB
 // 73, 48 at 32 MB 70, 63 at 32 MB 69, 72 at 25 MB 65 (no reservation: 66, 64,
 // -, -, 60; 32 KB: 77, 72, 68, 66, 62; 56 KB: 64, 66, 66, 67, 64).  From 96
-// ranks, 8 vectors per lane with 2 buffers (8 KB runs of each rank; the stack
-// alone reserves 48-56 KB): 100 ranks at 16 MB 62-63 against 59-61, 128 at 8 MB
-// 70-72 against 59.  Other shapes measured (2 vectors with 3 buffers, 4 with
-// 2-4, 4 waves per workgroup) were no better anywhere.
+// ranks, for 4-byte types, 8 vectors per lane with 2 buffers (8 KB runs of
+// each rank; the stack alone reserves 48-56 KB): 100 ranks at 16 MB 62-65
+// against 59-61, 128 at 8 MB 70-72 against 54-59.  2-byte types keep the
+// narrow shape there (their partials take twice the registers: bf16 at 128
+// ranks and 32 MB 65 against 55, at 100 ranks 60 against 57, at 128 ranks and
+// 8 MB 51.5 against 53).  Other shapes measured (2 vectors with 3 buffers, 4
+// with 2-4, 4 waves per workgroup) were no better anywhere.
 constexpr int kStreamWideRanks = 96;
 constexpr size_t kStreamNarrowLds = 48 << 10;
 
@@ -299,13 +302,14 @@ static bool launch_stream(int dt, int op, const RankTable &t, const TreeShape *c
         any = true;
     }
     if (!any) return false;
-    // Two ranges share a launch only where they need the same LDS: from 96
-    // ranks the reservation is the stack's depth, and one launch at the deeper
+    // Two ranges share a launch only where they need the same LDS: with the
+    // 8 KB runs the reservation is the stack's depth, and one launch at the deeper
     // half's depth cut the other half's wavefronts per compute unit (128 ranks,
     // 8 MB per rank, depths 7 and 6: 69-70 % in one launch, 75 % in two);
     // below 96 the 48 KB reservation is the same for both, and one launch
     // gained 1-4 points (17, 33 and 72 ranks) over two.
-    if (halves == 2 && g.n >= kStreamWideRanks && depths[0] && depths[1] && depths[0] != depths[1]) return false;
+    const bool wide = g.n >= kStreamWideRanks && (dt == F32 || dt == I32);
+    if (halves == 2 && wide && depths[0] && depths[1] && depths[0] != depths[1]) return false;
     const auto go = [&](auto Uc, auto Dc, size_t lds) {
         constexpr int U = decltype(Uc)::value, D = decltype(Dc)::value;
         const long long T = (long long)kFusedThreads * U;
@@ -314,11 +318,14 @@ static bool launch_stream(int dt, int op, const RankTable &t, const TreeShape *c
         if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
         const size_t stack = (size_t)depth * U * kFusedThreads * 16;
         return dispatch(dt, op, [&](auto Dt, auto O) {
-            return launch(tree_stream_kernel<decltype(Dt)::value, decltype(O)::value, U, D>, dim3((unsigned)tiles),
-                          dim3(kFusedThreads), stack > lds ? stack : lds, s, t, wk, g);
+            constexpr int DT = decltype(Dt)::value;
+            if constexpr (U == 8 && Lanes<DT>::value == 8) return hipErrorInvalidValue;   // never chosen (above)
+            else
+                return launch(tree_stream_kernel<DT, decltype(O)::value, U, D>, dim3((unsigned)tiles),
+                              dim3(kFusedThreads), stack > lds ? stack : lds, s, t, wk, g);
         });
     };
-    if (g.n >= kStreamWideRanks)
+    if (wide)
         *err = go(std::integral_constant<int, 8>(), std::integral_constant<int, 2>(), (size_t)0);
     else
         *err = go(std::integral_constant<int, 2>(), std::integral_constant<int, 4>(), kStreamNarrowLds);
