@@ -38,7 +38,6 @@
 // instead, the slots needed a branch per slot on every access, which the
 // register allocator answered with copies and spills at one wave per SIMD).
 #include <cstdlib>
-#include <cstring>
 #include <type_traits>
 
 #include "ar_device.hpp"
