@@ -78,11 +78,11 @@ def time_call(fn, iters, warmup=2):
     return float(np.median([a.elapsed_time(b) * 1e3 for a, b in ev]))
 
 
-def measure(ns, sizes, iters, rounds=3, dtype="f32", scheds=SCHEDS):
+def measure(ns, sizes, iters, rounds=3, dtype="f32", scheds=SCHEDS, colls=COLLS):
     """Time every (collective, schedule) at every rank count and per-rank byte
     size, for element type ``dtype`` (``f32`` or ``bf16``): median over
     ``rounds`` rounds of the per-call median of ``iters`` calls.  Only the
-    schedules in ``scheds``."""
+    schedules in ``scheds`` and the collectives in ``colls``."""
     import torch
     import reduce_scatter_amd as ar
     e = 4 if dtype == "f32" else 2
@@ -116,12 +116,16 @@ def measure(ns, sizes, iters, rounds=3, dtype="f32", scheds=SCHEDS):
             # past 16 ranks the all-reduce is timed in place, on views of a flat gradient buffer (above)
             ar_out = xs if n > 16 else ys
             for sched in scheds:
-                calls[("allreduce", sched)] = (lambda s=sched: ar.ar_allreduce(xs, ar_out, count, dtype, "sum", n=n, sched=s))
+                if "allreduce" in colls:
+                    calls[("allreduce", sched)] = (
+                        lambda s=sched: ar.ar_allreduce(xs, ar_out, count, dtype, "sum", n=n, sched=s))
                 if sched in ("tree", "split", "dtree"):
                     continue
-                calls[("reduce_scatter", sched)] = (
-                    lambda s=sched: ar.ar_reduce_scatter(xs, outs, R, dtype, "sum", n=n, sched=s))
-                calls[("all_gather", sched)] = (lambda s=sched: ar.ar_all_gather(outs, ys, R, dtype, n=n, sched=s))
+                if "reduce_scatter" in colls:
+                    calls[("reduce_scatter", sched)] = (
+                        lambda s=sched: ar.ar_reduce_scatter(xs, outs, R, dtype, "sum", n=n, sched=s))
+                if "all_gather" in colls:
+                    calls[("all_gather", sched)] = (lambda s=sched: ar.ar_all_gather(outs, ys, R, dtype, n=n, sched=s))
             # rounds that visit every call in turn, so no schedule always runs right after the same other one
             # (in the Infinity Cache regime the previous call's traffic decides what is cached)
             times = {k: [] for k in calls}
@@ -281,7 +285,7 @@ def _row_class(line):
     return int(tok[3]) if tok[0] in ("corr", "lat", "corr2") else None
 
 
-def write(path, model, gpu_name, model2=None, base=None, scheds=SCHEDS, classes=None):
+def write(path, model, gpu_name, model2=None, base=None, scheds=SCHEDS, classes=None, colls=COLLS):
     """The calibration file: ``model`` fitted on fp32 (every 4-byte type), and
     ``model2`` (bandwidth terms only) on bf16 for the 2-byte types.  With
     ``base`` (a calibration file as ``read_entries`` returns it), the entries
@@ -297,7 +301,8 @@ def write(path, model, gpu_name, model2=None, base=None, scheds=SCHEDS, classes=
         header[1] = device[0] if device else header[1]
         header += [h for h in base_header if h.startswith("# re-measured:")]
         where = "" if classes is None else " for rank classes %s" % ", ".join(str(c) for c in sorted(classes))
-        header.append("# re-measured: %s%s on %s" % (", ".join(scheds), where, gpu_name))
+        what = ", ".join(scheds) if colls == COLLS else "%s %s" % ("/".join(colls), ", ".join(scheds))
+        header.append("# re-measured: %s%s on %s" % (what, where, gpu_name))
         for key, lines in base_entries.items():
             if key[1] not in scheds or key not in entries:
                 entries[key] = lines
@@ -318,15 +323,19 @@ def main(argv=None):
     p.add_argument("--quick", action="store_true", help="fewer sizes and rank counts")
     p.add_argument("--schedules", default=",".join(SCHEDS), help="comma-separated schedules to measure")
     p.add_argument("--ranks", help="comma-separated rank counts to measure (default: all)")
+    p.add_argument("--collectives", default=",".join(COLLS), help="comma-separated collectives to measure")
     p.add_argument("--merge", metavar="BASE", help="keep everything not re-measured from this file")
     a = p.parse_args(argv)
     scheds = tuple(x for x in a.schedules.split(",") if x)
     if not scheds or any(x not in SCHEDS for x in scheds):
         p.error("--schedules takes a comma-separated subset of %s" % ",".join(SCHEDS))
+    colls = tuple(x for x in a.collectives.split(",") if x)
+    if not colls or any(x not in COLLS for x in colls):
+        p.error("--collectives takes a comma-separated subset of %s" % ",".join(COLLS))
     ranks = tuple(int(x) for x in a.ranks.split(",") if x) if a.ranks else None
     if ranks is not None and (not ranks or any(r < 2 or r > 128 for r in ranks)):
         p.error("--ranks takes rank counts from 2 to 128")
-    if (scheds != SCHEDS or ranks is not None) and not a.merge:
+    if (scheds != SCHEDS or colls != COLLS or ranks is not None) and not a.merge:
         p.error("measuring a subset needs --merge BASE for the rest")
     import torch
     if not torch.cuda.is_available():
@@ -342,12 +351,12 @@ def main(argv=None):
         ns, ns2 = ranks, tuple(r for r in ranks if r in ns2)
         classes = {rank_class(r) for r in ranks}
         fixed, fixed2 = base_constants(base)
-    rows = measure(ns, sizes, iters=3 if a.quick else 5, scheds=scheds)
+    rows = measure(ns, sizes, iters=3 if a.quick else 5, scheds=scheds, colls=colls)
     model = fit(rows, fixed=fixed)
-    rows2 = measure(ns2, sizes, iters=3 if a.quick else 5, dtype="bf16", scheds=scheds) if ns2 else []
+    rows2 = measure(ns2, sizes, iters=3 if a.quick else 5, dtype="bf16", scheds=scheds, colls=colls) if ns2 else []
     model2 = fit(rows2, latency=model, fixed=fixed2)
     gpu = torch.cuda.get_device_name(0) + " " + getattr(torch.cuda.get_device_properties(0), "gcnArchName", "")
-    write(a.out, model, gpu, model2, base=base, scheds=scheds, classes=classes)
+    write(a.out, model, gpu, model2, base=base, scheds=scheds, classes=classes, colls=colls)
     for (coll, sched), (launch, step, bw, corr, extra) in sorted(model.items()):
         print("%-15s %-6s launch %7.2f us  step %6.3f us  bw %7.1f GB/s  extra %s" % (
             coll, sched, launch, step, bw, {k: round(v, 1) for k, v in extra.items()}))

@@ -90,6 +90,22 @@ int fused_lds_bytes(ar_coll_t coll, int n) {
     }
 }
 
+// The all-gather's cap for ``input`` bytes of pieces in all.  The table's caps
+// (three or so one-wave workgroups per CU from 8 ranks on) were measured with
+// the pieces resident in the 256 MB Infinity Cache, where back-to-back calls
+// find them and the stores alone set the pace.  Past the cache every piece
+// streams from HBM and those caps leave too few loads in flight: measured on
+// MI355X with 512 MB-2 GB of pieces (fp32, % of peak, table cap -> 36 KB),
+// 8 ranks 63-66 -> 70-73, 16 ranks 54-60 -> 75-79, 17 ranks 54 -> 68-75, 24
+// ranks 62-64 -> 64-71; the ring ran 63-71, 64, 37 and 27.  At 72 ranks the
+// caps measured level (62.7 against 63.7-64.2 at 64 KB), so past 32 ranks the
+// table's cap stays.
+int gather_lds_bytes(int n, double input) {
+    const int lds = fused_lds_bytes(AR_COLL_ALL_GATHER, n);
+    if (getenv("AR_FUSED_LDS_KB") || input <= kCacheBytes || n > 32) return lds;
+    return lds < kGatherStreamLds ? lds : kGatherStreamLds;
+}
+
 // AR_TREE_STAGED=1 sends the n <= 16 tree schedules through the any-n
 // kernels (as for n > 16: the streaming walk, or the LDS-staged kernels under
 // AR_TREE_STREAM=0) instead of the register-evaluated ones; all give the same
@@ -601,7 +617,7 @@ ar_status_t ar_all_gather(const void *const *sendbufs, void *const *recvbufs, si
         }
         g.ref = (long long)((uintptr_t)tp.dst[0] >> 4);       // tiles follow the outputs' alignment
         if (aligned_tiles(Rb / 16, kFusedTile) > 0x7fffffffLL) return AR_ERR_UNSUPPORTED;
-        const hipError_t h = launch_fused_all_gather_phased(tp, g, fused_lds_bytes(AR_COLL_ALL_GATHER, n), stream);
+        const hipError_t h = launch_fused_all_gather_phased(tp, g, gather_lds_bytes(n, (double)n * Rb), stream);
         if (h != hipSuccess) return hip_status(h);
         return hip_status(launch_elem_all_gather_edges((int)e, t, g, R, stream));
     }
@@ -610,7 +626,7 @@ ar_status_t ar_all_gather(const void *const *sendbufs, void *const *recvbufs, si
     if (use == AR_SCHED_FUSED) {
         g.windows = aligned_tiles(g.Rv, kFusedTile);
         if (g.windows > 0x7fffffffLL) return AR_ERR_UNSUPPORTED;   // grid x limit
-        return hip_status(launch_fused_all_gather(t, g, fused_lds_bytes(AR_COLL_ALL_GATHER, n), stream));
+        return hip_status(launch_fused_all_gather(t, g, gather_lds_bytes(n, (double)n * sendcount * e), stream));
     }
     g.W = lds_window(n);
     g.windows = (g.Rv + g.W - 1) / g.W;

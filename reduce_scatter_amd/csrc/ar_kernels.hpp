@@ -220,6 +220,8 @@ constexpr int kFusedLdsAllGatherByN[17] = {0, 0, 14, 18, 26, 30, 34, 34, 48, 48,
 constexpr int kFusedLdsAllReduceKB = 0;      // n > 16 (the wide kernel): every cap from 10 to 64 KB measured slower
 constexpr int kFusedLdsReduceScatterKB = 48;   // n > 16, two vectors per lane (3 workgroups per CU)
 constexpr int kFusedLdsAllGatherKB = 64;
+constexpr double kCacheBytes = 256.0 * 1024 * 1024;   // the Infinity Cache (MALL) of MI355X
+constexpr int kGatherStreamLds = 36 * 1024;          // all-gather cap once its pieces outgrow that cache
 // Default dynamic-LDS reservation of the compile-time-n ring workgroups, in
 // KB (on top of their static LDS).
 constexpr int kRingLdsKB = 0;
