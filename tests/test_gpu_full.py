@@ -270,6 +270,28 @@ def test_c5_trees_one_bucket_in_place(sched):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("R", [8 << 20, (8 << 20) - 1])
+def test_all_gather_past_the_cache(R):
+    """16 ranks, 512 MB of pieces in all (past the 256 MB Infinity Cache, where
+    the all-gather takes its streaming residency cap), whole 16-byte vectors and
+    a piece length off the vector grid (the phased kernel): every output equals
+    the concatenation of the pieces, bit for bit, on every rank."""
+    n = 16
+    xs = [workloads.device_normal(7, 3, r, R, 1.0, "f32") for r in range(n)]
+    want = torch.cat(xs)
+    ys = [torch.empty(n * R, device="cuda") for _ in range(n)]
+    for sched in ("fused", "auto"):
+        print("all-gather past the cache R=%d %s" % (R, sched), flush=True)
+        for y in ys:
+            y.fill_(-1.0)
+        ar.ar_all_gather(xs, ys, R, "f32", sched=sched)
+        torch.cuda.synchronize()
+        for r in range(n):
+            assert torch.equal(ys[r].view(torch.int32), want.view(torch.int32)), "%s rank %d" % (sched, r)
+    del xs, ys, want
+    torch.cuda.empty_cache()
+
+
 BIG = (1 << 30) + (1 << 20) + 7          # fp32 elements per rank: 4.3 GB, past every 32-bit byte offset
 
 
