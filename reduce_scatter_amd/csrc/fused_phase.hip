@@ -4,11 +4,14 @@
 // Reduce-scatter input slice c of every rank starts c*R*e bytes into a
 // 16-byte-aligned buffer, so with R*e not a multiple of 16 the slices sit at
 // different phases within 16-byte vectors, while every output is aligned.
-// Each lane reads the two aligned vectors around its 16 input bytes and
-// assembles them (funnel16; the phase is the same for every rank of a slice,
-// so it is uniform across the workgroup), combines the n contributions in the
-// ring hop order exactly as the aligned kernel does, and stores one aligned
-// output vector.  (A first form loaded the second vector only for a non-zero
+// Each lane reads its 16 input bytes either as the two aligned vectors around
+// them, assembled by a funnel shift (funnel16), or as one load from the word
+// boundary at or below them (4-byte alignment is enough for a 16-byte global
+// load), shifted by whole bytes only where the phase is not whole words (the
+// phase is the same for every rank of a slice, so either choice is uniform
+// across the workgroup); it combines the n contributions in the ring hop
+// order exactly as the aligned kernel does and stores one aligned output
+// vector.  (A first form loaded the second vector only for a non-zero
 // phase; that branch made the compiler wait for each rank's pair before
 // issuing the next, and n = 16 ran at 3.1 TB/s.)  The all-gather is the mirror image: aligned input pieces,
 // output pieces at phase k*R*e mod 16, each lane assembling the 16 input bytes
@@ -19,6 +22,7 @@
 // another XCD), so the larger the tile, the closer the fetched bytes come to
 // the algorithmic ones.
 #include <cstdlib>
+#include <cstring>
 
 #include "ar_device.hpp"
 #include "ar_kernels.hpp"
@@ -65,8 +69,8 @@ __device__ __forceinline__ u32x4 lane0(u32x4 v) {
 // block (past it the second vector is only reached with ph = 0, where it is
 // not used).  Elsewhere it is addressed as the first plus 16: measured on
 // MI355X, the clamp's separate address on every tile cost the n = 8 bf16
-// reduce-scatter 13 % (5.5 -> 4.8 TB/s).  NR == 0 (any n): U = 1, ranks in
-// batches of 8.
+// reduce-scatter 13 % (5.5 -> 4.8 TB/s).  Compile-time n only (past 16 ranks
+// the word-aligned chain below runs).
 //
 // NEXT (whole tiles away from the input's end only; a uniform choice): lane l's
 // second vector is lane l+1's first, taken from its register (next_lane),
@@ -75,16 +79,16 @@ __device__ __forceinline__ u32x4 lane0(u32x4 v) {
 // load instructions instead of 2U, and the cache serves one request per line
 // instead of two.  Measured on MI355X with R - 1 elements per slice, 256 MB in
 // per rank: n = 8 fp32 72.1 -> 76.3-76.6 % of peak, n = 16 bf16 72.6 -> 74 %,
-// n = 8 bf16 and n = 3 level.  The any-n chain (one vector per lane, past 16
-// ranks) and the phased all-gather measured level or slower with it and keep
-// both loads.
-template <int DT, int OP, int NR, bool KEEP32, bool CLAMP, int U, class TAB, bool NEXT = false>
-__device__ __forceinline__ void chain_phased(const TAB &t, int n, int c, long long base, const unsigned (&lane_off)[U],
-                                             const unsigned (&hi_off)[U], unsigned ph, float s, Pack<DT> (&acc)[U]) {
+// n = 8 bf16 and n = 3 level.  The phased all-gather measured level or slower
+// with it and keeps both loads.
+template <int DT, int OP, int NR, bool KEEP32, bool CLAMP, int U, bool NEXT = false>
+__device__ __forceinline__ void chain_phased(const RankTableFor<NR> &t, int c, long long base,
+                                             const unsigned (&lane_off)[U], const unsigned (&hi_off)[U], unsigned ph,
+                                             float s, Pack<DT> (&acc)[U]) {
+    static_assert(NR > 0, "past 16 ranks the word-aligned chain runs");
     static_assert(!(NEXT && CLAMP), "the register neighbour needs the unclamped layout");
-    static_assert(!(NEXT && NR == 0), "the any-n chain loads both vectors");
-    const bool lane0_ = (threadIdx.x & 63u) == 0u;
-    if constexpr (NR > 0 && NEXT) {
+    if constexpr (NEXT) {
+        const bool lane0_ = (threadIdx.x & 63u) == 0u;
         const void *ptr[NR];
 #pragma unroll
         for (int k = 0; k < NR; ++k) ptr[k] = t.src[hop_rank(c, k, NR)];
@@ -108,7 +112,7 @@ __device__ __forceinline__ void chain_phased(const TAB &t, int n, int c, long lo
                 else hop<DT, OP, KEEP32>(acc[u], x, s);
             }
         }
-    } else if constexpr (NR > 0) {
+    } else {
         const void *ptr[NR];                 // every rank pointer's scalar load issued before the vector loads
 #pragma unroll
         for (int k = 0; k < NR; ++k) ptr[k] = t.src[hop_rank(c, k, NR)];
@@ -130,23 +134,103 @@ __device__ __forceinline__ void chain_phased(const TAB &t, int n, int c, long lo
 #pragma unroll
             for (int k = 1; k < NR; ++k) hop<DT, OP, KEEP32>(acc[u], unpack<DT>(funnel16(lo[k][u], hi[k][u], ph)), s);
         }
+    }
+}
+
+// 16 bytes at a 4-byte-aligned address: gfx9 global loads of several dwords
+// need only dword alignment.
+typedef unsigned int u32x4d __attribute__((ext_vector_type(4), aligned(4)));
+
+// The 16 bytes that start b bytes into v (b < 4), the last b of them from nx,
+// the word after v (v_alignbyte_b32 per word).
+__device__ __forceinline__ u32x4 shift_words(u32x4 v, unsigned nx, unsigned b) {
+    u32x4 r;
+    r.x = __builtin_amdgcn_alignbyte(v.y, v.x, b);
+    r.y = __builtin_amdgcn_alignbyte(v.z, v.y, b);
+    r.z = __builtin_amdgcn_alignbyte(v.w, v.z, b);
+    r.w = __builtin_amdgcn_alignbyte(nx, v.w, b);
+    return r;
+}
+
+// The word w of lane + 1, and ``last`` in lane 63 (as next_lane, one word).
+__device__ __forceinline__ unsigned next_word(unsigned w, unsigned last, bool first_lane) {
+    const int src = (int)((((threadIdx.x & 63u) + 1u) & 63u) << 2);
+    return (unsigned)__builtin_amdgcn_ds_bpermute(src, (int)(first_lane ? last : w));
+}
+
+// Word-aligned form of the chain: each lane loads its 16 input bytes from the
+// word boundary at or just below them, ``wbase + lane_off[u]`` (wbase = the
+// tile's first input byte rounded down to a word, uniform; b = the bytes it
+// was rounded by, uniform), so a rank costs one load per vector, as in the
+// aligned kernel, and 4-byte types need no shift at all.  Only with b != 0
+// (2-byte types at a slice whose phase is an odd number of elements: NX) the
+// last b bytes come from the next word: from the next lane's register on whole
+// tiles (XCHG: lane 63's from lane 0 of the next run, or for the last run one
+// dword load at the tile's end, the same address in every lane), else from a
+// dword load.  Every byte read lies in the word holding the lane's first input
+// byte through the word holding its last, so no load passes the input's last
+// 16-byte block and no clamp is needed.
+template <int DT, int OP, int NR, bool KEEP32, int U, bool NX, bool XCHG, class TAB>
+__device__ __forceinline__ void chain_words(const TAB &t, int n, int c, long long wbase,
+                                            const unsigned (&lane_off)[U], unsigned b, float s, Pack<DT> (&acc)[U]) {
+    static_assert(!(XCHG && !NX), "the exchange only supplies the word after the vector");
+    static_assert(!(XCHG && NR == 0), "the any-n chain loads the word");
+    if constexpr (NR > 0) {
+        const bool lane0_ = (threadIdx.x & 63u) == 0u;
+        const void *ptr[NR];                 // every rank pointer's scalar load issued before the vector loads
+#pragma unroll
+        for (int k = 0; k < NR; ++k) ptr[k] = t.src[hop_rank(c, k, NR)];
+        __builtin_amdgcn_sched_barrier(0);
+        u32x4 v[NR][U];
+        unsigned nx[NR][U], ex[NR];
+#pragma unroll
+        for (int k = 0; k < NR; ++k) {
+            const char *p = (const char *)ptr[k] + wbase;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                v[k][u] = __builtin_nontemporal_load((const u32x4d *)(p + lane_off[u]));
+                if constexpr (NX && !XCHG) nx[k][u] = *(const unsigned *)(p + lane_off[u] + 16);
+            }
+            if constexpr (XCHG) ex[k] = *(const unsigned *)(p + kFusedTile * U * 16);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+            for (int k = 0; k < NR; ++k) {
+                u32x4 w = v[k][u];
+                if constexpr (XCHG) {
+                    const unsigned last =
+                        u + 1 < U ? (unsigned)__builtin_amdgcn_readlane((int)v[k][u + 1 < U ? u + 1 : u].x, 0) : ex[k];
+                    w = shift_words(w, next_word(v[k][u].x, last, lane0_), b);
+                } else if constexpr (NX) {
+                    w = shift_words(w, nx[k][u], b);
+                }
+                const Pack<DT> x = unpack<DT>(w);
+                if (k == 0) acc[u] = first<DT, OP, KEEP32>(x, s);
+                else hop<DT, OP, KEEP32>(acc[u], x, s);
+            }
+        }
     } else {
         static_assert(U == 1, "the any-n chain takes one vector per lane");
         constexpr int B = 8;
         for (int k0 = 0; k0 < n; k0 += B) {
-            u32x4 lo[B], hi[B];
+            u32x4 v[B];
+            unsigned nx[B];
 #pragma unroll
             for (int kk = 0; kk < B; ++kk) {
                 const int k = k0 + kk < n ? k0 + kk : n - 1;                 // past n: a valid, ignored load
-                const char *p = (const char *)t.src[hop_rank(c, k, n)] + base + lane_off[0];
-                lo[kk] = __builtin_nontemporal_load((const u32x4 *)p);
-                hi[kk] = CLAMP ? *(const u32x4 *)(p - lane_off[0] + hi_off[0]) : *(const u32x4 *)(p + 16);
+                const char *p = (const char *)t.src[hop_rank(c, k, n)] + wbase + lane_off[0];
+                v[kk] = __builtin_nontemporal_load((const u32x4d *)p);
+                if constexpr (NX) nx[kk] = *(const unsigned *)(p + 16);
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int kk = 0; kk < B; ++kk) {
                 if (k0 + kk >= n) break;
-                const Pack<DT> x = unpack<DT>(funnel16(lo[kk], hi[kk], ph));
+                u32x4 w = v[kk];
+                if constexpr (NX) w = shift_words(w, nx[kk], b);
+                const Pack<DT> x = unpack<DT>(w);
                 if (k0 + kk == 0) acc[0] = first<DT, OP, KEEP32>(x, s);
                 else hop<DT, OP, KEEP32>(acc[0], x, s);
             }
@@ -191,16 +275,27 @@ __device__ __forceinline__ void rs_phased(const RankTableFor<NR> &t, const Geome
     const long long rel = g.last_off - (a & ~15LL);                             // last block, from the tile base
     Pack<DT> acc[U];
     const bool whole = ts.lo == ts.start && ts.hi == ts.start + kFusedTile * U;
-    if (NR > 0 && whole && rel >= 16 * (kFusedTile * U + 1)) {   // the neighbour's vector from its register
-        chain_phased<DT, OP, NR, KEEP32, false, U, RankTableFor<NR>, (NR > 0)>(t, n, c, a & ~15LL, off, off,
-                                                                               (unsigned)(a & 15), g.s, acc);
-    } else if (rel >= 16 * (kFusedTile * U + 1)) {  // no lane's second vector can pass the input's last block
-        chain_phased<DT, OP, NR, KEEP32, false, U>(t, n, c, a & ~15LL, off, off, (unsigned)(a & 15), g.s, acc);
-    } else {                                 // the input's last tiles: the second load clamped (a uniform branch)
-        unsigned hi_off[U];
+    const unsigned b = (unsigned)(a & 3);                       // 0 for 4-byte types (element-aligned inputs)
+    if (NR == 0 || g.phased_words == 2 || (g.phased_words == 1 && b != 0)) {
+        if (Lanes<DT>::value == 4 || b == 0) {
+            chain_words<DT, OP, NR, KEEP32, U, false, false>(t, n, c, a & ~3LL, off, 0u, g.s, acc);
+        } else if constexpr (Lanes<DT>::value == 8) {
+            if (NR > 0 && whole)
+                chain_words<DT, OP, NR, KEEP32, U, true, (NR > 0)>(t, n, c, a & ~3LL, off, b, g.s, acc);
+            else
+                chain_words<DT, OP, NR, KEEP32, U, true, false>(t, n, c, a & ~3LL, off, b, g.s, acc);
+        }
+    } else if constexpr (NR > 0) {
+        if (whole && rel >= 16 * (kFusedTile * U + 1)) {        // the neighbour's vector from its register
+            chain_phased<DT, OP, NR, KEEP32, false, U, true>(t, c, a & ~15LL, off, off, (unsigned)(a & 15), g.s, acc);
+        } else if (rel >= 16 * (kFusedTile * U + 1)) {   // no lane's second vector can pass the input's last block
+            chain_phased<DT, OP, NR, KEEP32, false, U>(t, c, a & ~15LL, off, off, (unsigned)(a & 15), g.s, acc);
+        } else {                             // the input's last tiles: the second load clamped (a uniform branch)
+            unsigned hi_off[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) hi_off[u] = (long long)off[u] + 16 < rel ? off[u] + 16u : (unsigned)rel;
-        chain_phased<DT, OP, NR, KEEP32, true, U>(t, n, c, a & ~15LL, off, hi_off, (unsigned)(a & 15), g.s, acc);
+            for (int u = 0; u < U; ++u) hi_off[u] = (long long)off[u] + 16 < rel ? off[u] + 16u : (unsigned)rel;
+            chain_phased<DT, OP, NR, KEEP32, true, U>(t, c, a & ~15LL, off, hi_off, (unsigned)(a & 15), g.s, acc);
+        }
     }
     char *p = (char *)t.dst[c] + ts.lo * 16;
 #pragma unroll
@@ -305,19 +400,42 @@ static void phased_rs_shape(int n, int dt, int lds_one_wave, int &waves, int &ld
     lds = (n <= 4 ? 48 : 56) * 1024;
 }
 
+// Which loads the compile-time-n reduce-scatter takes (the any-n chain always
+// takes the word-aligned ones): 0 the aligned pair with the funnel shift, 1
+// the word-aligned load on slices whose phase is not a whole number of words
+// (only 2-byte types have them) and the pair elsewhere, 2 the word-aligned
+// load on every slice.  A misaligned 16-byte load costs more than an aligned
+// one, so the word-aligned form pays where it saves the shift.  Measured on
+// MI355X, R - 1 elements per slice, % of peak (pair / 1 / 2): bf16 n = 2
+// 75.5 / 76.7 / 75.1, n = 4 78.4 / 77.8 / 74.5, fp16 n = 6 68.0 / 71.4 / 75.8,
+// bf16 n = 8 70.4 / 73.9 / 76.0 (another box 73.1 / - / 76.3), n = 12
+// 69.4 / 71.1 / 72.9, n = 16 71.4 / 72.3 / 72.4; fp32 n = 8 75.7 / 75.8 / 75.5
+// (another box 77.3 / - / 75.8), n = 3 77.2 / - / 76.8; past 16 ranks (any n,
+// word-aligned against the pair) fp32 n = 17 66.7 -> 68.6, bf16 n = 24
+// 70.9 -> 74.1.  AR_PHASED_FORM=funnel|hybrid|words overrides.
+static int phased_rs_form(int n, int dt) {
+    const char *f = getenv("AR_PHASED_FORM");
+    if (f && !strcmp(f, "funnel")) return 0;
+    if (f && !strcmp(f, "hybrid")) return 1;
+    if (f && !strcmp(f, "words")) return 2;
+    return (dt == BF16 || dt == F16) && n >= 5 ? 2 : 1;
+}
+
 hipError_t launch_fused_reduce_scatter_phased(int dt, int op, const RankTable &t, const Geometry &g, int lds,
                                               hipStream_t s) {
     if (g.Rv <= 0) return hipSuccess;
     int waves, lds_wg;
     phased_rs_shape(g.n, dt, lds, waves, lds_wg);
     if (getenv("AR_FUSED_LDS_KB") && waves > 1) lds_wg = lds * waves > 65536 ? 65536 : lds * waves;
+    Geometry gw = g;
+    gw.phased_words = phased_rs_form(g.n, dt);
     return dispatch(dt, op, [&](auto D, auto O) {
         return by_ranks(g.n, [&](auto R) {
             constexpr int NR = decltype(R)::value;
             const long long tiles = aligned_tiles(g.Rv, (long long)kFusedTile * PhasedTile<NR>::U);
             const dim3 grid((unsigned)((tiles + waves - 1) / waves), (unsigned)g.n);
             return launch(fused_reduce_scatter_phased_kernel<decltype(D)::value, decltype(O)::value, NR>,
-                          grid, dim3(kFusedThreads * waves), (size_t)lds_wg, s, narrow<NR>(t), g);
+                          grid, dim3(kFusedThreads * waves), (size_t)lds_wg, s, narrow<NR>(t), gw);
         });
     });
 }

@@ -486,6 +486,29 @@ def test_reduce_scatter_and_all_gather_at_phases(dtype):
         assert_bits_equal(to_host(d_out[r], dtype), ref[r], "rs mixed phases rank %d" % r)
 
 
+@pytest.mark.parametrize("form", ["funnel", "hybrid", "words"])
+def test_phased_reduce_scatter_load_forms(form, monkeypatch):
+    """The phased reduce-scatter's two ways of reading a lane's 16 input bytes
+    (an aligned pair and a funnel shift, or one load from the word boundary
+    below them with a byte shift where the phase is not whole words), forced
+    one at a time and mixed per slice: n = 2, 5, 8 and 16 (compile-time
+    kernels, whole and partial tiles, the input's last tiles) and 17 (any n),
+    bf16 / fp16 / fp32 with odd slice lengths, every op, bit for bit against
+    the oracle."""
+    monkeypatch.setenv("AR_PHASED_FORM", form)
+    for dtype in ("bf16", "f16", "f32"):
+        u = LANES[dtype]
+        for n in (2, 5, 8, 16, 17):
+            for R in (64 * u * 2 * 5 + 1, 64 * u * 3 - 1):
+                op = OPS[(n + R) % len(OPS)]
+                print("phased form", form, dtype, op, "n=%d R=%d" % (n, R), flush=True)
+                xs = inputs(40 + n, n, n * R, dtype, op)
+                ref = oracle.ring_reduce_scatter(xs, dtype, op)
+                got = run_rs(xs, dtype, op, "fused")
+                for r in range(n):
+                    assert_bits_equal(got[r], ref[r], "rs %s %s %s n=%d R=%d rank %d" % (form, dtype, op, n, R, r))
+
+
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_slices_off_the_vector_grid(dtype):
     """Slices whose byte length is not a multiple of 16 bytes, with 16-byte

@@ -9,7 +9,9 @@ the element ranges the edge kernels take -- and checks, for every rank count,
 element size, input and output phase, slice lengths around tile boundaries
 and one, two or four vectors per lane, that
 
-* every load stays inside the 16-byte blocks that hold the rank's input bytes;
+* every load stays inside the 16-byte blocks that hold the rank's input bytes
+  (the reduce-scatter's word-aligned form: inside the 4-byte words that hold
+  them, each load at a word-aligned address);
 * the 16 bytes a lane assembles are exactly the input bytes of the element
   positions of the output vector it writes (so the clamp never changes a
   second vector that the shift uses);
@@ -53,10 +55,31 @@ def library_u(n, coll="rs"):
     return 2 if 2 <= n <= 8 else 1
 
 
-def emulate_rs(n, e, R, ps, pr, U, refs, slack=0, edge_shift=0):
+def rs_words_loads(a, off, whole, U):
+    """The word-aligned form's reads for one tile (a = the tile's first input byte, off = the lanes' byte
+    offsets): the 16-byte loads' starts, the starts of the words after them that the shift takes
+    (none when a is a whole word), and whether each of those words comes from another lane's load
+    (whole tiles: lane l + 1's first word, lane 63's from lane 0 of the next run) or is loaded."""
+    w, b = a & ~3, a & 3
+    loads = w + off
+    if b == 0:
+        return loads, None
+    nxt = w + off + 16
+    if whole:
+        starts = set((w + off).tolist())
+        from_lanes = np.array([x in starts for x in nxt.tolist()])
+        # only the last run's lane 63 lies past the tile: one more word load at the tile's end
+        assert (nxt[~from_lanes] == w + TILE * U * 16).all() and (~from_lanes).sum() == 1
+    return loads, nxt
+
+
+def emulate_rs(n, e, R, ps, pr, U, refs, slack=0, edge_shift=0, words=False, shift_mask=3):
     """One phased reduce-scatter call; returns the write count of every output element, per rank.
-    ``slack`` and ``edge_shift`` plant mistakes (a clamp that many bytes short, the edge kernel's upper
-    range moved that many elements) for the test that the model notices them."""
+    ``words`` models the word-aligned form (one load per lane from the word at or below its first input
+    byte, the next word only for a phase that is not a whole word).  ``slack``, ``edge_shift`` and
+    ``shift_mask`` plant mistakes (a clamp that many bytes short, the edge kernel's upper range moved
+    that many elements, the shift taken from the 16-byte phase instead of the word phase) for the test
+    that the model notices them."""
     Rb = R * e
     writes = np.zeros((n, R), dtype=np.int64)
     head = (16 - pr) // e if pr > 0 else 0
@@ -74,6 +97,23 @@ def emulate_rs(n, e, R, ps, pr, U, refs, slack=0, edge_shift=0):
                 continue
             off, ok = lanes(start, lo, hi, U)
             a = in_off + c * Rb + lo * 16
+            if words:
+                # every read inside the words [ps & ~3, end rounded up to a word) holding the input bytes
+                wlo, whi = ps & ~3, (ps + n * Rb + 3) & ~3
+                loads, nxt = rs_words_loads(a, off, lo == start and hi == start + TILE * U, U)
+                assert (loads % 4 == 0).all()
+                assert loads.min() >= wlo and (loads + 16).max() <= whi, (n, e, R, ps, pr, U, c, j)
+                if nxt is not None:
+                    assert nxt.min() >= wlo and (nxt + 4).max() <= whi, (n, e, R, ps, pr, U, c, j)
+                    assert np.array_equal(nxt[ok], loads[ok] + 16)
+                # the lane's 16 bytes start b bytes into its load: the input of its output vector
+                o = lo + off[ok] // 16
+                assert np.array_equal(loads[ok] + (a & shift_mask), ps + c * Rb + out_off + 16 * o)
+                for q in o:
+                    first = (out_off + 16 * int(q)) // e
+                    assert first + 16 // e <= R
+                    writes[c, first:first + 16 // e] += 1
+                continue
             base, ph = a & ~15, a & 15
             rel = last_off - base - slack
             if rel >= 16 * (TILE * U + 1):
@@ -154,8 +194,9 @@ def _cases(rng, e):
     return [R for R in lengths if R * e % 16]
 
 
+@pytest.mark.parametrize("words", [False, True])
 @pytest.mark.parametrize("e", [2, 4])
-def test_phased_reduce_scatter_index_map(e):
+def test_phased_reduce_scatter_index_map(e, words):
     rng = random.Random(11 + e)
     phases = list(range(0, 16, e))
     for n in (1, 2, 3, 5, 8, 9, 17):
@@ -163,7 +204,7 @@ def test_phased_reduce_scatter_index_map(e):
             for U in sorted({1, 2, 4, library_u(n)}):
                 ps, pr = rng.choice(phases), rng.choice(phases)
                 refs = [rng.randrange(0, 1 << 20) for _ in range(n)]
-                w = emulate_rs(n, e, R, ps, pr, U, refs)
+                w = emulate_rs(n, e, R, ps, pr, U, refs, words=words)
                 assert (w == 1).all(), (n, e, R, ps, pr, U)
 
 
@@ -179,9 +220,11 @@ def test_phased_all_gather_index_map(e):
                 assert (w == 1).all(), (n, e, R, ps, pr, U)
 
 
-@pytest.mark.parametrize("mistake", [{"slack": 16}, {"edge_shift": 1}, {"edge_shift": -1}])
+@pytest.mark.parametrize("mistake", [{"slack": 16}, {"edge_shift": 1}, {"edge_shift": -1},
+                                     {"words": True, "shift_mask": 15}])
 def test_model_notices_planted_mistakes(mistake):
-    """A clamp one block short, or an edge range off by one element, fails the checks for some case."""
+    """A clamp one block short, an edge range off by one element, or the word-aligned form shifting by
+    the 16-byte phase instead of the word phase, fails the checks for some case."""
     rng = random.Random(5)
     failed = 0
     for n in (2, 3, 8):
