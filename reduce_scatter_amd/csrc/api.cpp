@@ -116,6 +116,14 @@ bool tree_staged() {
     return e && *e == '1';
 }
 
+// AR_DWORD_VECTORS=0 sends 4-byte all-reduces at mixed 16-byte phases back to
+// the element-wise kernels (same bits) instead of the fused vector kernels on
+// the callers' dword-aligned pointers; read on every call.
+bool dword_vectors() {
+    const char *e = getenv("AR_DWORD_VECTORS");
+    return !(e && *e == '0');
+}
+
 // Dynamic LDS reservation (bytes) of the ring / tree workgroups; the
 // AR_RING_LDS_KB variable overrides the default.
 int env_kb(const char *name, int dflt) {
@@ -454,10 +462,24 @@ ar_status_t ar_allreduce_ex(const void *const *sendbufs, void *const *recvbufs, 
     // take exactly the rest: each chunk's first ``head`` elements and the frame
     // vector across its end (ring order), the head, the vector across the
     // double tree's split and the tail (tree orders).  Otherwise, or for the
-    // LDS-staged ring past 16 ranks, everything goes element-wise.
+    // LDS-staged ring past 16 ranks, 4-byte elements in ring order take the
+    // fused vector kernels on the callers' pointers and everything else goes
+    // element-wise.
     const int ph = common_phase(sendbufs, (const void *const *)recvbufs, n);
     const long long head = ph > 0 ? (long long)((16 - ph) / (int)e) : 0;
-    if (ph <= 0 || (long long)count <= head || (use == AR_SCHED_RING && n > 16)) return hip_status(elem(0));
+    const bool frame = ph > 0 && (long long)count > head && !(use == AR_SCHED_RING && n > 16);
+    if (!frame && e == 4 && (use == AR_SCHED_FUSED || use == AR_SCHED_RING) && dword_vectors()) {
+        // 4-byte elements at mixed phases (or the ring past 16 ranks): every pointer is 4-byte aligned, all
+        // that the fused kernels' 16-byte accesses need, so they run on the callers' pointers, vector v of
+        // every buffer at byte 16*v, in the ring's hop order (the ring schedule's bits), and the
+        // element-wise kernel takes the count mod 4 tail.
+        use = AR_SCHED_FUSED;
+        st = vectors(t);
+        if (st != AR_OK) return st;
+        if (g.Vfull * lanes < (long long)count) return hip_status(elem(g.Vfull * lanes));
+        return AR_OK;
+    }
+    if (!frame) return hip_status(elem(0));
     RankTable tv = t;
     for (int r = 0; r < n; ++r) {
         tv.src[r] = (const char *)sendbufs[r] + head * (long long)e;

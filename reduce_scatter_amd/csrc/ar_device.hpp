@@ -26,6 +26,11 @@ enum Dtype : int { F32 = 0, BF16 = 1, F16 = 2, I32 = 3 };
 enum Op : int { SUM = 0, PROD = 1, MIN = 2, MAX = 3, AVG = 4 };
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+// The same 16 bytes at an address known only to be 4-byte aligned: a 16-byte
+// global load or store on gfx9 needs dword alignment only, so the vector
+// kernels that access memory through this type also serve element-aligned
+// 4-byte buffers (the instruction is the same global_load/store_dwordx4).
+typedef unsigned int u32x4d __attribute__((ext_vector_type(4), aligned(4)));
 
 constexpr int kMaxRanks = 128;
 

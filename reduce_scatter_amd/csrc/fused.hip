@@ -39,9 +39,9 @@ __device__ __forceinline__ void store_all(const TAB &t, int n, long long base, u
     if constexpr (NR > 0) {
 #pragma unroll
         for (int r = 0; r < NR; ++r)
-            __builtin_nontemporal_store(w, (u32x4 *)((char *)t.dst[r] + base + lane_off));
+            __builtin_nontemporal_store(w, (u32x4d *)((char *)t.dst[r] + base + lane_off));
     } else {
-        for (int r = 0; r < n; ++r) __builtin_nontemporal_store(w, (u32x4 *)((char *)t.dst[r] + base + lane_off));
+        for (int r = 0; r < n; ++r) __builtin_nontemporal_store(w, (u32x4d *)((char *)t.dst[r] + base + lane_off));
     }
 }
 
@@ -112,7 +112,7 @@ __device__ __forceinline__ void wide_whole_tile(const RankTable &t, int n, int c
         for (int kk = 0; kk < B; ++kk) {
 #pragma unroll
             for (int u = 0; u < U; ++u)
-                raw[kk][u] = __builtin_nontemporal_load((const u32x4 *)(ptr[kk] + u * kFusedThreads * 16 + lane));
+                raw[kk][u] = __builtin_nontemporal_load((const u32x4d *)(ptr[kk] + u * kFusedThreads * 16 + lane));
             __builtin_amdgcn_sched_barrier(0);                 // one rank's run issued whole before the next
         }
 #pragma unroll
@@ -134,7 +134,7 @@ __device__ __forceinline__ void wide_whole_tile(const RankTable &t, int n, int c
     for (int r = 0; r < n; ++r) {
         char *p = (char *)t.dst[r] + base;
 #pragma unroll
-        for (int u = 0; u < U; ++u) __builtin_nontemporal_store(w[u], (u32x4 *)(p + u * kFusedThreads * 16 + lane));
+        for (int u = 0; u < U; ++u) __builtin_nontemporal_store(w[u], (u32x4d *)(p + u * kFusedThreads * 16 + lane));
     }
 }
 
@@ -162,7 +162,7 @@ __device__ __forceinline__ void wide_edge_tile(const RankTable &t, int n, int c,
 #pragma unroll
         for (int kk = 0; kk < B; ++kk) {
 #pragma unroll
-            for (int u = 0; u < U; ++u) raw[kk][u] = __builtin_nontemporal_load((const u32x4 *)(ptr[kk] + off[u]));
+            for (int u = 0; u < U; ++u) raw[kk][u] = __builtin_nontemporal_load((const u32x4d *)(ptr[kk] + off[u]));
             __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
@@ -185,7 +185,7 @@ __device__ __forceinline__ void wide_edge_tile(const RankTable &t, int n, int c,
         char *p = (char *)t.dst[r] + base;
 #pragma unroll
         for (int u = 0; u < U; ++u)
-            if ((okm >> u) & 1u) __builtin_nontemporal_store(w[u], (u32x4 *)(p + off[u]));
+            if ((okm >> u) & 1u) __builtin_nontemporal_store(w[u], (u32x4d *)(p + off[u]));
     }
 }
 
@@ -219,10 +219,10 @@ __device__ __forceinline__ void wide_shared_tile(const RankTable &t, int n, int 
         __builtin_amdgcn_sched_barrier(0);
         u32x4 r0[U], r1[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) r0[u] = __builtin_nontemporal_load((const u32x4 *)(p0 + u * kFusedThreads * 16 + lane));
+        for (int u = 0; u < U; ++u) r0[u] = __builtin_nontemporal_load((const u32x4d *)(p0 + u * kFusedThreads * 16 + lane));
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int u = 0; u < U; ++u) r1[u] = __builtin_nontemporal_load((const u32x4 *)(p1 + u * kFusedThreads * 16 + lane));
+        for (int u = 0; u < U; ++u) r1[u] = __builtin_nontemporal_load((const u32x4d *)(p1 + u * kFusedThreads * 16 + lane));
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -244,7 +244,7 @@ __device__ __forceinline__ void wide_shared_tile(const RankTable &t, int n, int 
         for (int kk = 0; kk < B; ++kk) {
 #pragma unroll
             for (int u = 0; u < U; ++u)
-                raw[kk][u] = __builtin_nontemporal_load((const u32x4 *)(ptr[kk] + u * kFusedThreads * 16 + lane));
+                raw[kk][u] = __builtin_nontemporal_load((const u32x4d *)(ptr[kk] + u * kFusedThreads * 16 + lane));
             __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
@@ -259,7 +259,7 @@ __device__ __forceinline__ void wide_shared_tile(const RankTable &t, int n, int 
         __builtin_amdgcn_sched_barrier(0);
         u32x4 rn[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) rn[u] = __builtin_nontemporal_load((const u32x4 *)(pn + u * kFusedThreads * 16 + lane));
+        for (int u = 0; u < U; ++u) rn[u] = __builtin_nontemporal_load((const u32x4d *)(pn + u * kFusedThreads * 16 + lane));
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -280,7 +280,7 @@ __device__ __forceinline__ void wide_shared_tile(const RankTable &t, int n, int 
         char *p = (char *)t.dst[r] + base;
 #pragma unroll
         for (int u = 0; u < U; ++u)
-            if (!((skip >> u) & 1u)) __builtin_nontemporal_store(w[u], (u32x4 *)(p + u * kFusedThreads * 16 + lane));
+            if (!((skip >> u) & 1u)) __builtin_nontemporal_store(w[u], (u32x4d *)(p + u * kFusedThreads * 16 + lane));
     }
 }
 

@@ -44,7 +44,7 @@ __device__ __forceinline__ void chain_in(const TAB &t, int n, int c, long long b
         for (int k = 0; k < NR; ++k) {
             const char *p = (const char *)ptr[k] + base;
 #pragma unroll
-            for (int u = 0; u < U; ++u) raw[k][u] = __builtin_nontemporal_load((const u32x4 *)(p + lane_off[u]));
+            for (int u = 0; u < U; ++u) raw[k][u] = __builtin_nontemporal_load((const u32x4d *)(p + lane_off[u]));
         }
         __builtin_amdgcn_sched_barrier(0);                   // every load issued before the first combine
 #pragma unroll
@@ -65,7 +65,7 @@ __device__ __forceinline__ void chain_in(const TAB &t, int n, int c, long long b
             for (int kk = 0; kk < B; ++kk) {
                 const char *p = (const char *)ptr[kk] + base;                // past n: a valid, ignored load
 #pragma unroll
-                for (int u = 0; u < U; ++u) raw[kk][u] = __builtin_nontemporal_load((const u32x4 *)(p + lane_off[u]));
+                for (int u = 0; u < U; ++u) raw[kk][u] = __builtin_nontemporal_load((const u32x4d *)(p + lane_off[u]));
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll

@@ -137,10 +137,6 @@ __device__ __forceinline__ void chain_phased(const RankTableFor<NR> &t, int c, l
     }
 }
 
-// 16 bytes at a 4-byte-aligned address: gfx9 global loads of several dwords
-// need only dword alignment.
-typedef unsigned int u32x4d __attribute__((ext_vector_type(4), aligned(4)));
-
 // The 16 bytes that start b bytes into v (b < 4), the last b of them from nx,
 // the word after v (v_alignbyte_b32 per word).
 __device__ __forceinline__ u32x4 shift_words(u32x4 v, unsigned nx, unsigned b) {

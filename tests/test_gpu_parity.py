@@ -442,6 +442,49 @@ def test_allreduce_buffers_at_one_phase(dtype):
         assert_bits_equal(to_host(d_out[r], dtype), ref[r], "mixed phases rank %d" % r)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "i32"])
+def test_allreduce_4byte_mixed_phases(dtype, monkeypatch):
+    """4-byte elements with every rank's buffers at its own 16-byte phase (in
+    and out of place): the fused kernels run on the callers' dword-aligned
+    pointers in ring order, the element-wise kernel takes the count mod 4
+    tail.  n from 2 to 72 (the wide kernel past 16 ranks, chunk boundaries
+    inside tiles), counts of less than one vector to several tiles per chunk
+    with ragged tails, every op, the fused and ring schedules, bit for bit
+    against the oracle and against the element-wise path."""
+    for n in (2, 3, 8, 16, 17, 72):
+        for count in sorted({3, 4 * n + 1, 64 * 4 * 3 + 4 * n + 5, 64 * 16 * 4 * 3 + 4 * n + 7}):
+            op = OPS[(n + count) % len(OPS)]
+            xs = inputs(110 + n, n, count, dtype, op)
+            ref = oracle.ring_allreduce(xs, dtype, op)
+            print("dword phases", dtype, op, "n=%d count=%d" % (n, count), flush=True)
+            for sched in ("fused", "ring"):
+                d_in = [_at_phase(x, dtype, r % 4) for r, x in enumerate(xs)]
+                d_out = [_at_phase(np.zeros_like(x), dtype, (3 * r + 1) % 4) for r, x in enumerate(xs)]
+                ar.ar_allreduce(d_in, d_out, count, dtype, op, sched=sched)
+                sync()
+                for r in range(n):
+                    assert_bits_equal(to_host(d_out[r], dtype), ref[r], "dword %s %s %s n=%d count=%d rank %d" % (
+                        sched, dtype, op, n, count, r))
+                ar.ar_allreduce(d_in, d_in, count, dtype, op, sched=sched)              # in place
+                sync()
+                for r in (0, n // 2, n - 1):
+                    assert_bits_equal(to_host(d_in[r], dtype), ref[r], "dword in place %s %s %s n=%d count=%d rank %d"
+                                      % (sched, dtype, op, n, count, r))
+    # the element-wise path gives the same bits
+    n, count = 8, 64 * 4 * 5 + 3
+    xs = inputs(119, n, count, dtype, "avg")
+    outs = []
+    for flag in ("1", "0"):
+        monkeypatch.setenv("AR_DWORD_VECTORS", flag)
+        d_in = [_at_phase(x, dtype, r % 4) for r, x in enumerate(xs)]
+        d_out = [_at_phase(np.zeros_like(x), dtype, (r + 2) % 4) for r, x in enumerate(xs)]
+        ar.ar_allreduce(d_in, d_out, count, dtype, "avg", sched="fused")
+        sync()
+        outs.append([to_host(d, dtype) for d in d_out])
+    for r in range(n):
+        assert_bits_equal(outs[0][r], outs[1][r], "dword against element-wise rank %d" % r)
+
+
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_reduce_scatter_and_all_gather_at_phases(dtype):
     """Inputs at one 16-byte phase and outputs at another (every pair of
