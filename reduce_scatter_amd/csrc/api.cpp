@@ -116,9 +116,9 @@ bool tree_staged() {
     return e && *e == '1';
 }
 
-// AR_DWORD_VECTORS=0 sends 4-byte all-reduces at mixed 16-byte phases back to
-// the element-wise kernels (same bits) instead of the fused vector kernels on
-// the callers' dword-aligned pointers; read on every call.
+// AR_DWORD_VECTORS=0 sends 4-byte all-reduces and reduce-scatters at mixed
+// 16-byte phases back to the element-wise kernels (same bits) instead of the
+// vector kernels on the callers' dword-aligned pointers; read on every call.
 bool dword_vectors() {
     const char *e = getenv("AR_DWORD_VECTORS");
     return !(e && *e == '0');
@@ -559,11 +559,24 @@ ar_status_t ar_reduce_scatter_ex(const void *const *sendbufs, void *const *recvb
         // one 16-byte phase and every output at one phase, the phased pass (any schedule: the ring computes
         // the same hop order) writes every whole vector of the output frame that starts at the outputs' first
         // 16-byte boundary, reading the inputs through aligned pairs of vectors; the element-wise kernel
-        // takes each output's first and last few elements.  Mixed phases go element-wise.
+        // takes each output's first and last few elements.  At mixed phases 4-byte elements take the
+        // phased pass's word-aligned loads on the callers' pointers (output vector o of every slice at byte
+        // 16*o, every access 4-byte aligned, which is all a 16-byte access needs, and inside the lane's own
+        // bytes) and the element-wise kernel each slice's last R mod 4 elements; other types go element-wise.
         const long long R = (long long)recvcount, Rb = R * (long long)e;
         const int ps = one_phase(sendbufs, n), pr = one_phase((const void *const *)recvbufs, n);
         const long long head = pr > 0 ? (long long)((16 - pr) / (int)e) : 0;
-        if (ps < 0 || pr < 0 || head >= R) return hip_status(launch_elem_reduce_scatter(dtype, op, t, g, R, 0, 0, stream));
+        if (ps < 0 || pr < 0 || head >= R) {
+            if (e != 4 || !dword_vectors()) return hip_status(launch_elem_reduce_scatter(dtype, op, t, g, R, 0, 0, stream));
+            g.slice_bytes = Rb;
+            g.Rv = Rb / 16;
+            g.phased_words = 2;                                     // the word-aligned loads only
+            if (aligned_tiles(g.Rv, kFusedTile) > 0x7fffffffLL) return AR_ERR_UNSUPPORTED;   // grid x limit
+            const hipError_t h = launch_fused_reduce_scatter_phased(dtype, op, t, g,
+                                                                    fused_lds_bytes(AR_COLL_REDUCE_SCATTER, n), stream);
+            if (h != hipSuccess) return hip_status(h);
+            return hip_status(launch_elem_reduce_scatter(dtype, op, t, g, R, 0, g.Rv * 4, stream));
+        }
         g.slice_bytes = Rb;
         g.out_off = head * (long long)e;
         g.in_off = ps + g.out_off;

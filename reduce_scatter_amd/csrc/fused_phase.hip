@@ -298,7 +298,7 @@ __device__ __forceinline__ void rs_phased(const RankTableFor<NR> &t, const Geome
     for (int u = 0; u < U; ++u) {
         if (!ok[u]) continue;
         finish<DT, OP>(acc[u], n, g);
-        __builtin_nontemporal_store(pack<DT>(acc[u]), (u32x4 *)(p + off[u]));
+        __builtin_nontemporal_store(pack<DT>(acc[u]), (u32x4d *)(p + off[u]));
     }
 }
 
@@ -424,7 +424,7 @@ hipError_t launch_fused_reduce_scatter_phased(int dt, int op, const RankTable &t
     phased_rs_shape(g.n, dt, lds, waves, lds_wg);
     if (getenv("AR_FUSED_LDS_KB") && waves > 1) lds_wg = lds * waves > 65536 ? 65536 : lds * waves;
     Geometry gw = g;
-    gw.phased_words = phased_rs_form(g.n, dt);
+    gw.phased_words = g.phased_words == 2 ? 2 : phased_rs_form(g.n, dt);   // 2 from the caller: mixed phases
     return dispatch(dt, op, [&](auto D, auto O) {
         return by_ranks(g.n, [&](auto R) {
             constexpr int NR = decltype(R)::value;

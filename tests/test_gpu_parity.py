@@ -485,6 +485,49 @@ def test_allreduce_4byte_mixed_phases(dtype, monkeypatch):
         assert_bits_equal(outs[0][r], outs[1][r], "dword against element-wise rank %d" % r)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "i32"])
+def test_reduce_scatter_4byte_mixed_phases(dtype, monkeypatch):
+    """4-byte reduce-scatter with every rank's input and output at its own
+    16-byte phase: the phased kernel's word-aligned loads on the callers'
+    pointers, the element-wise kernel each slice's last R mod 4 elements.
+    n from 2 to 24 (compile-time and any-n kernels), slices shorter than a
+    vector up to several tiles, every op, fused and ring, out of place and in
+    place, bit for bit against the oracle and against the element-wise
+    path."""
+    for n in (2, 3, 8, 16, 17, 24):
+        for R in sorted({3, 4 * 5 + 1, 64 * 4 * 2 * 3 + 2, 64 * 4 * 7 + 4}):
+            op = OPS[(n + R) % len(OPS)]
+            xs = inputs(130 + n, n, n * R, dtype, op)
+            ref = oracle.ring_reduce_scatter(xs, dtype, op)
+            print("dword rs phases", dtype, op, "n=%d R=%d" % (n, R), flush=True)
+            for sched in ("fused", "ring"):
+                d_in = [_at_phase(x, dtype, r % 4) for r, x in enumerate(xs)]
+                d_out = [_at_phase(np.zeros(R, dtype=xs[0].dtype), dtype, (r + 1) % 4) for r in range(n)]
+                ar.ar_reduce_scatter(d_in, d_out, R, dtype, op, sched=sched)
+                sync()
+                for r in range(n):
+                    assert_bits_equal(to_host(d_out[r], dtype), ref[r], "dword rs %s %s %s n=%d R=%d rank %d" % (
+                        sched, dtype, op, n, R, r))
+                d_in = [_at_phase(x, dtype, (2 * r + 1) % 4) for r, x in enumerate(xs)]
+                ar.ar_reduce_scatter(d_in, [d_in[r][r * R:(r + 1) * R] for r in range(n)], R, dtype, op, sched=sched)
+                sync()
+                for r in (0, n // 2, n - 1):
+                    assert_bits_equal(to_host(d_in[r][r * R:(r + 1) * R], dtype), ref[r],
+                                      "dword rs in place %s %s %s n=%d R=%d rank %d" % (sched, dtype, op, n, R, r))
+    n, R = 8, 64 * 4 * 3 + 1
+    xs = inputs(139, n, n * R, dtype, "avg")
+    outs = []
+    for flag in ("1", "0"):
+        monkeypatch.setenv("AR_DWORD_VECTORS", flag)
+        d_in = [_at_phase(x, dtype, r % 4) for r, x in enumerate(xs)]
+        d_out = [_at_phase(np.zeros(R, dtype=xs[0].dtype), dtype, (r + 3) % 4) for r in range(n)]
+        ar.ar_reduce_scatter(d_in, d_out, R, dtype, "avg", sched="fused")
+        sync()
+        outs.append([to_host(d, dtype) for d in d_out])
+    for r in range(n):
+        assert_bits_equal(outs[0][r], outs[1][r], "dword rs against element-wise rank %d" % r)
+
+
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_reduce_scatter_and_all_gather_at_phases(dtype):
     """Inputs at one 16-byte phase and outputs at another (every pair of

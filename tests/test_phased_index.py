@@ -220,6 +220,41 @@ def test_phased_all_gather_index_map(e):
                 assert (w == 1).all(), (n, e, R, ps, pr, U)
 
 
+def test_mixed_phase_reduce_scatter_words_index_map():
+    """4-byte reduce-scatter at mixed phases: the phased kernel's word-aligned loads run on the callers'
+    pointers with no frame shift (output vector o of slice c at byte 16*o, input at c*R*4 + 16*o), the
+    element-wise kernel takes elements [4*Rv, R) of every slice.  Every load is 4-byte aligned and holds
+    exactly the lane's own input bytes; every output element is written once."""
+    rng = random.Random(3)
+    e = 4
+    for n in (1, 2, 3, 8, 9, 17):
+        for R in [1, 3, 4, 5, 63, 64 * 4 + 1] + [rng.randrange(1, 6 * TILE * 4) for _ in range(4)]:
+            Rb = R * e
+            Rv = Rb // 16
+            src = [4 * rng.randrange(0, 1 << 18) for _ in range(n)]       # element-aligned, any 16-byte phase
+            dst = [4 * rng.randrange(0, 1 << 18) for _ in range(n)]
+            writes = np.zeros((n, R), dtype=np.int64)
+            for c in range(n):
+                for U in (1, 2):
+                    if U != library_u(n):
+                        continue
+                    for j in range(aligned_tiles(Rv, TILE * U)):
+                        start, lo, hi = aligned_tile(0, Rv, j, dst[c] >> 4, TILE * U)
+                        if lo >= hi:
+                            continue
+                        off, ok = lanes(start, lo, hi, U)
+                        a = c * Rb + lo * 16
+                        assert a % 4 == 0
+                        for r in range(n):
+                            ld = src[r] + a + off
+                            assert (ld % 4 == 0).all()
+                            assert ld.min() >= src[r] + c * Rb and (ld + 16).max() <= src[r] + c * Rb + 16 * Rv
+                        for q in lo + off[ok] // 16:
+                            writes[c, 4 * q:4 * q + 4] += 1
+            writes[:, 4 * Rv:] += 1
+            assert (writes == 1).all(), (n, R)
+
+
 @pytest.mark.parametrize("mistake", [{"slack": 16}, {"edge_shift": 1}, {"edge_shift": -1},
                                      {"words": True, "shift_mask": 15}])
 def test_model_notices_planted_mistakes(mistake):
