@@ -377,8 +377,13 @@ __global__ __launch_bounds__(kFusedThreads) void fused_all_gather_phased_kernel(
 // 16 64.0 -> 73.3, 24 41.6 -> 71.3, 72 67.6 -> 76.1; fp32 n = 3 72.1 -> 75.6,
 // 8 71.4 -> 72.1, 13-15 level, 17 40.0 -> 69.3, 32 49.1 -> 73.1; fp32 at 16
 // ranks ran 64.9 with one wave and 60.3 with four, so 4-byte types keep one
-// there.  AR_PHASED_WAVES=1|2|4|8 overrides the count (the LDS then scales
-// the one-wave reservation).
+// there.  With the word-aligned loads, 8 wavefronts (the one-wave reservation
+// times 8, at most 64 KB) win up to 4 ranks: bf16 n = 2 77.9 -> 79.3, 3
+// 73.8 -> 76.9, 4 73.7 -> 78.5; fp32 n = 2 76.9 -> 78.9, 3 74.0 -> 76.8, 4
+// 72.2 -> 77.4; while 4 stay ahead at 8 ranks (bf16 76.7 against 74.5, fp32
+// 75.5 against 73.7) and 24 (72.1 against 68.7), level at 16.
+// AR_PHASED_WAVES=1|2|4|8 overrides the count (the LDS then scales the
+// one-wave reservation).
 static void phased_rs_shape(int n, int dt, int lds_one_wave, int &waves, int &lds) {
     const char *e = getenv("AR_PHASED_WAVES");
     if (e && (*e == '1' || *e == '2' || *e == '4' || *e == '8')) {
@@ -392,8 +397,13 @@ static void phased_rs_shape(int n, int dt, int lds_one_wave, int &waves, int &ld
         lds = lds_one_wave;
         return;
     }
+    if (n <= 4) {
+        waves = 8;
+        lds = lds_one_wave * 8 > 65536 ? 65536 : lds_one_wave * 8;
+        return;
+    }
     waves = 4;
-    lds = (n <= 4 ? 48 : 56) * 1024;
+    lds = 56 * 1024;
 }
 
 // Which loads the compile-time-n reduce-scatter takes (the any-n chain always

@@ -273,8 +273,9 @@ def test_model_notices_planted_mistakes(mistake):
 
 
 def phased_rs_waves(n, e):
-    """Wavefronts per workgroup of the library's phased reduce-scatter (4-byte types keep one at 16 ranks)."""
-    return 1 if (n == 16 and e == 4) else 4
+    """Wavefronts per workgroup of the library's phased reduce-scatter (4-byte types keep one at 16 ranks,
+    up to 4 ranks eight)."""
+    return 1 if (n == 16 and e == 4) else (8 if n <= 4 else 4)
 
 
 @pytest.mark.parametrize("waves", [1, 2, 4, 8])
@@ -301,3 +302,4 @@ def test_multi_wave_workgroups_cover_every_tile_once(waves):
                     covered[lo:hi] += 1
         assert (covered == 1).all()
     assert phased_rs_waves(8, 2) == 4 and phased_rs_waves(16, 4) == 1 and phased_rs_waves(16, 2) == 4
+    assert phased_rs_waves(4, 4) == 8 and phased_rs_waves(2, 2) == 8
