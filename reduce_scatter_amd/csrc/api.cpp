@@ -116,9 +116,10 @@ bool tree_staged() {
     return e && *e == '1';
 }
 
-// AR_DWORD_VECTORS=0 sends 4-byte all-reduces and reduce-scatters at mixed
-// 16-byte phases back to the element-wise kernels (same bits) instead of the
-// vector kernels on the callers' dword-aligned pointers; read on every call.
+// AR_DWORD_VECTORS=0 sends all-reduces and reduce-scatters at mixed 16-byte
+// phases with 4-byte-aligned pointers back to the element-wise kernels (same
+// bits) instead of the vector kernels on the callers' pointers; read on every
+// call.
 bool dword_vectors() {
     const char *e = getenv("AR_DWORD_VECTORS");
     return !(e && *e == '0');
@@ -468,11 +469,12 @@ ar_status_t ar_allreduce_ex(const void *const *sendbufs, void *const *recvbufs, 
     const int ph = common_phase(sendbufs, (const void *const *)recvbufs, n);
     const long long head = ph > 0 ? (long long)((16 - ph) / (int)e) : 0;
     const bool frame = ph > 0 && (long long)count > head && !(use == AR_SCHED_RING && n > 16);
-    if (!frame && e == 4 && (use == AR_SCHED_FUSED || use == AR_SCHED_RING) && dword_vectors()) {
-        // 4-byte elements at mixed phases (or the ring past 16 ranks): every pointer is 4-byte aligned, all
-        // that the fused kernels' 16-byte accesses need, so they run on the callers' pointers, vector v of
-        // every buffer at byte 16*v, in the ring's hop order (the ring schedule's bits), and the
-        // element-wise kernel takes the count mod 4 tail.
+    if (!frame && !misaligned(sendbufs, n, 4) && !misaligned((const void *const *)recvbufs, n, 4) &&
+        (use == AR_SCHED_FUSED || use == AR_SCHED_RING) && dword_vectors()) {
+        // Mixed phases (or the ring past 16 ranks) with every pointer 4-byte aligned (always so for 4-byte
+        // elements): that is all the fused kernels' 16-byte accesses need, so they run on the callers'
+        // pointers, vector v of every buffer at byte 16*v, in the ring's hop order (the ring schedule's
+        // bits), and the element-wise kernel takes the count mod lanes tail.
         use = AR_SCHED_FUSED;
         st = vectors(t);
         if (st != AR_OK) return st;
@@ -559,15 +561,17 @@ ar_status_t ar_reduce_scatter_ex(const void *const *sendbufs, void *const *recvb
         // one 16-byte phase and every output at one phase, the phased pass (any schedule: the ring computes
         // the same hop order) writes every whole vector of the output frame that starts at the outputs' first
         // 16-byte boundary, reading the inputs through aligned pairs of vectors; the element-wise kernel
-        // takes each output's first and last few elements.  At mixed phases 4-byte elements take the
-        // phased pass's word-aligned loads on the callers' pointers (output vector o of every slice at byte
-        // 16*o, every access 4-byte aligned, which is all a 16-byte access needs, and inside the lane's own
-        // bytes) and the element-wise kernel each slice's last R mod 4 elements; other types go element-wise.
+        // takes each output's first and last few elements.  At mixed phases with every pointer 4-byte aligned
+        // (always so for 4-byte elements) the phased pass's word-aligned loads run on the callers' pointers
+        // (output vector o of every slice at byte 16*o, every access 4-byte aligned, which is all a 16-byte
+        // access needs, and inside the words holding the lane's own bytes) and the element-wise kernel takes
+        // each slice's last R mod lanes elements; other alignments go element-wise.
         const long long R = (long long)recvcount, Rb = R * (long long)e;
         const int ps = one_phase(sendbufs, n), pr = one_phase((const void *const *)recvbufs, n);
         const long long head = pr > 0 ? (long long)((16 - pr) / (int)e) : 0;
         if (ps < 0 || pr < 0 || head >= R) {
-            if (e != 4 || !dword_vectors()) return hip_status(launch_elem_reduce_scatter(dtype, op, t, g, R, 0, 0, stream));
+            if (misaligned(sendbufs, n, 4) || misaligned((const void *const *)recvbufs, n, 4) || !dword_vectors())
+                return hip_status(launch_elem_reduce_scatter(dtype, op, t, g, R, 0, 0, stream));
             g.slice_bytes = Rb;
             g.Rv = Rb / 16;
             g.phased_words = 2;                                     // the word-aligned loads only
@@ -575,7 +579,7 @@ ar_status_t ar_reduce_scatter_ex(const void *const *sendbufs, void *const *recvb
             const hipError_t h = launch_fused_reduce_scatter_phased(dtype, op, t, g,
                                                                     fused_lds_bytes(AR_COLL_REDUCE_SCATTER, n), stream);
             if (h != hipSuccess) return hip_status(h);
-            return hip_status(launch_elem_reduce_scatter(dtype, op, t, g, R, 0, g.Rv * 4, stream));
+            return hip_status(launch_elem_reduce_scatter(dtype, op, t, g, R, 0, g.Rv * (long long)(16 / e), stream));
         }
         g.slice_bytes = Rb;
         g.out_off = head * (long long)e;

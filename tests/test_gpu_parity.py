@@ -442,24 +442,26 @@ def test_allreduce_buffers_at_one_phase(dtype):
         assert_bits_equal(to_host(d_out[r], dtype), ref[r], "mixed phases rank %d" % r)
 
 
-@pytest.mark.parametrize("dtype", ["f32", "i32"])
-def test_allreduce_4byte_mixed_phases(dtype, monkeypatch):
-    """4-byte elements with every rank's buffers at its own 16-byte phase (in
-    and out of place): the fused kernels run on the callers' dword-aligned
-    pointers in ring order, the element-wise kernel takes the count mod 4
-    tail.  n from 2 to 72 (the wide kernel past 16 ranks, chunk boundaries
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_allreduce_mixed_phases_dword_aligned(dtype, monkeypatch):
+    """Every rank's buffers at its own 16-byte phase, each a multiple of 4
+    bytes (in and out of place): the fused kernels run on the callers'
+    dword-aligned pointers in ring order, the element-wise kernel takes the
+    count mod lanes tail.  n from 2 to 72 (the wide kernel past 16 ranks, chunk boundaries
     inside tiles), counts of less than one vector to several tiles per chunk
     with ragged tails, every op, the fused and ring schedules, bit for bit
     against the oracle and against the element-wise path."""
+    u = LANES[dtype]
+    w = u // 4                                          # elements per 4-byte word
     for n in (2, 3, 8, 16, 17, 72):
-        for count in sorted({3, 4 * n + 1, 64 * 4 * 3 + 4 * n + 5, 64 * 16 * 4 * 3 + 4 * n + 7}):
+        for count in sorted({3, u * n + 1, 64 * u * 3 + u * n + 5, 64 * 8 * u * 3 + u * n + 7}):
             op = OPS[(n + count) % len(OPS)]
             xs = inputs(110 + n, n, count, dtype, op)
             ref = oracle.ring_allreduce(xs, dtype, op)
             print("dword phases", dtype, op, "n=%d count=%d" % (n, count), flush=True)
             for sched in ("fused", "ring"):
-                d_in = [_at_phase(x, dtype, r % 4) for r, x in enumerate(xs)]
-                d_out = [_at_phase(np.zeros_like(x), dtype, (3 * r + 1) % 4) for r, x in enumerate(xs)]
+                d_in = [_at_phase(x, dtype, w * (r % 4)) for r, x in enumerate(xs)]
+                d_out = [_at_phase(np.zeros_like(x), dtype, w * ((3 * r + 1) % 4)) for r, x in enumerate(xs)]
                 ar.ar_allreduce(d_in, d_out, count, dtype, op, sched=sched)
                 sync()
                 for r in range(n):
@@ -471,13 +473,13 @@ def test_allreduce_4byte_mixed_phases(dtype, monkeypatch):
                     assert_bits_equal(to_host(d_in[r], dtype), ref[r], "dword in place %s %s %s n=%d count=%d rank %d"
                                       % (sched, dtype, op, n, count, r))
     # the element-wise path gives the same bits
-    n, count = 8, 64 * 4 * 5 + 3
+    n, count = 8, 64 * u * 5 + 3
     xs = inputs(119, n, count, dtype, "avg")
     outs = []
     for flag in ("1", "0"):
         monkeypatch.setenv("AR_DWORD_VECTORS", flag)
-        d_in = [_at_phase(x, dtype, r % 4) for r, x in enumerate(xs)]
-        d_out = [_at_phase(np.zeros_like(x), dtype, (r + 2) % 4) for r, x in enumerate(xs)]
+        d_in = [_at_phase(x, dtype, w * (r % 4)) for r, x in enumerate(xs)]
+        d_out = [_at_phase(np.zeros_like(x), dtype, w * ((r + 2) % 4)) for r, x in enumerate(xs)]
         ar.ar_allreduce(d_in, d_out, count, dtype, "avg", sched="fused")
         sync()
         outs.append([to_host(d, dtype) for d in d_out])
@@ -485,42 +487,45 @@ def test_allreduce_4byte_mixed_phases(dtype, monkeypatch):
         assert_bits_equal(outs[0][r], outs[1][r], "dword against element-wise rank %d" % r)
 
 
-@pytest.mark.parametrize("dtype", ["f32", "i32"])
-def test_reduce_scatter_4byte_mixed_phases(dtype, monkeypatch):
-    """4-byte reduce-scatter with every rank's input and output at its own
-    16-byte phase: the phased kernel's word-aligned loads on the callers'
-    pointers, the element-wise kernel each slice's last R mod 4 elements.
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_reduce_scatter_mixed_phases_dword_aligned(dtype, monkeypatch):
+    """Reduce-scatter with every rank's input and output at its own 16-byte
+    phase, each a multiple of 4 bytes: the phased kernel's word-aligned loads
+    on the callers' pointers (2-byte slices of an odd length shift by half a
+    word), the element-wise kernel each slice's last R mod lanes elements.
     n from 2 to 24 (compile-time and any-n kernels), slices shorter than a
     vector up to several tiles, every op, fused and ring, out of place and in
     place, bit for bit against the oracle and against the element-wise
     path."""
+    u = LANES[dtype]
+    w = u // 4                                          # elements per 4-byte word
     for n in (2, 3, 8, 16, 17, 24):
-        for R in sorted({3, 4 * 5 + 1, 64 * 4 * 2 * 3 + 2, 64 * 4 * 7 + 4}):
+        for R in sorted({3, u * 5 + 1, 64 * u * 2 * 3 + 2, 64 * u * 7 + u, 64 * u * 2 * 5 + 1}):
             op = OPS[(n + R) % len(OPS)]
             xs = inputs(130 + n, n, n * R, dtype, op)
             ref = oracle.ring_reduce_scatter(xs, dtype, op)
             print("dword rs phases", dtype, op, "n=%d R=%d" % (n, R), flush=True)
             for sched in ("fused", "ring"):
-                d_in = [_at_phase(x, dtype, r % 4) for r, x in enumerate(xs)]
-                d_out = [_at_phase(np.zeros(R, dtype=xs[0].dtype), dtype, (r + 1) % 4) for r in range(n)]
+                d_in = [_at_phase(x, dtype, w * (r % 4)) for r, x in enumerate(xs)]
+                d_out = [_at_phase(np.zeros(R, dtype=xs[0].dtype), dtype, w * ((r + 1) % 4)) for r in range(n)]
                 ar.ar_reduce_scatter(d_in, d_out, R, dtype, op, sched=sched)
                 sync()
                 for r in range(n):
                     assert_bits_equal(to_host(d_out[r], dtype), ref[r], "dword rs %s %s %s n=%d R=%d rank %d" % (
                         sched, dtype, op, n, R, r))
-                d_in = [_at_phase(x, dtype, (2 * r + 1) % 4) for r, x in enumerate(xs)]
+                d_in = [_at_phase(x, dtype, w * ((2 * r + 1) % 4)) for r, x in enumerate(xs)]
                 ar.ar_reduce_scatter(d_in, [d_in[r][r * R:(r + 1) * R] for r in range(n)], R, dtype, op, sched=sched)
                 sync()
                 for r in (0, n // 2, n - 1):
                     assert_bits_equal(to_host(d_in[r][r * R:(r + 1) * R], dtype), ref[r],
                                       "dword rs in place %s %s %s n=%d R=%d rank %d" % (sched, dtype, op, n, R, r))
-    n, R = 8, 64 * 4 * 3 + 1
+    n, R = 8, 64 * u * 3 + 1
     xs = inputs(139, n, n * R, dtype, "avg")
     outs = []
     for flag in ("1", "0"):
         monkeypatch.setenv("AR_DWORD_VECTORS", flag)
-        d_in = [_at_phase(x, dtype, r % 4) for r, x in enumerate(xs)]
-        d_out = [_at_phase(np.zeros(R, dtype=xs[0].dtype), dtype, (r + 3) % 4) for r in range(n)]
+        d_in = [_at_phase(x, dtype, w * (r % 4)) for r, x in enumerate(xs)]
+        d_out = [_at_phase(np.zeros(R, dtype=xs[0].dtype), dtype, w * ((r + 3) % 4)) for r in range(n)]
         ar.ar_reduce_scatter(d_in, d_out, R, dtype, "avg", sched="fused")
         sync()
         outs.append([to_host(d, dtype) for d in d_out])

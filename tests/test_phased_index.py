@@ -220,18 +220,20 @@ def test_phased_all_gather_index_map(e):
                 assert (w == 1).all(), (n, e, R, ps, pr, U)
 
 
-def test_mixed_phase_reduce_scatter_words_index_map():
-    """4-byte reduce-scatter at mixed phases: the phased kernel's word-aligned loads run on the callers'
-    pointers with no frame shift (output vector o of slice c at byte 16*o, input at c*R*4 + 16*o), the
-    element-wise kernel takes elements [4*Rv, R) of every slice.  Every load is 4-byte aligned and holds
-    exactly the lane's own input bytes; every output element is written once."""
-    rng = random.Random(3)
-    e = 4
+@pytest.mark.parametrize("e", [2, 4])
+def test_mixed_phase_reduce_scatter_words_index_map(e):
+    """Reduce-scatter at mixed phases with 4-byte-aligned pointers: the phased kernel's word-aligned loads
+    run on the callers' pointers with no frame shift (output vector o of slice c at byte 16*o, input at
+    c*R*e + 16*o), the element-wise kernel takes elements [lanes*Rv, R) of every slice.  Every load is
+    4-byte aligned and lies in the words holding the lane's input bytes, inside slice c (2-byte slices of
+    an odd length take the next word as well); every output element is written once."""
+    rng = random.Random(3 + e)
+    u = 16 // e
     for n in (1, 2, 3, 8, 9, 17):
-        for R in [1, 3, 4, 5, 63, 64 * 4 + 1] + [rng.randrange(1, 6 * TILE * 4) for _ in range(4)]:
+        for R in [1, 3, 4, 5, 63, 64 * u + 1] + [rng.randrange(1, 6 * TILE * u) for _ in range(4)]:
             Rb = R * e
             Rv = Rb // 16
-            src = [4 * rng.randrange(0, 1 << 18) for _ in range(n)]       # element-aligned, any 16-byte phase
+            src = [4 * rng.randrange(0, 1 << 18) for _ in range(n)]       # 4-byte aligned, any 16-byte phase
             dst = [4 * rng.randrange(0, 1 << 18) for _ in range(n)]
             writes = np.zeros((n, R), dtype=np.int64)
             for c in range(n):
@@ -244,14 +246,19 @@ def test_mixed_phase_reduce_scatter_words_index_map():
                             continue
                         off, ok = lanes(start, lo, hi, U)
                         a = c * Rb + lo * 16
-                        assert a % 4 == 0
+                        whole = lo == start and hi == start + TILE * U
                         for r in range(n):
-                            ld = src[r] + a + off
-                            assert (ld % 4 == 0).all()
-                            assert ld.min() >= src[r] + c * Rb and (ld + 16).max() <= src[r] + c * Rb + 16 * Rv
+                            loads, nxt = rs_words_loads(src[r] + a, off, whole, U)
+                            assert (loads % 4 == 0).all()
+                            # inside the words that hold slice c's bytes
+                            wlo, whi = (src[r] + c * Rb) & ~3, (src[r] + (c + 1) * Rb + 3) & ~3
+                            assert loads.min() >= wlo and (loads + 16).max() <= whi, (n, R, c, r)
+                            if nxt is not None:
+                                assert e == 2 and (nxt + 4).max() <= whi, (n, R, c, r)
+                            assert np.array_equal(loads[ok] + ((src[r] + a) & 3), src[r] + a + off[ok])
                         for q in lo + off[ok] // 16:
-                            writes[c, 4 * q:4 * q + 4] += 1
-            writes[:, 4 * Rv:] += 1
+                            writes[c, u * q:u * q + u] += 1
+            writes[:, u * Rv:] += 1
             assert (writes == 1).all(), (n, R)
 
 
