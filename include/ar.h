@@ -66,10 +66,10 @@
  * when all inputs share one phase and all outputs share one (possibly another)
  * phase, and when R * element size is not a multiple of 16.  At mixed phases
  * with every pointer 4-byte aligned (always so for 4-byte elements),
- * all-reduces in ring order (AR_SCHED_RING, AR_SCHED_FUSED) and
- * reduce-scatters run vector kernels on the pointers as given (a 16-byte
- * access needs only 4-byte alignment), the last count mod lanes (R mod lanes
- * per slice) elements element-wise.  Other alignments take an element-wise
+ * all-reduces in ring order (AR_SCHED_RING, AR_SCHED_FUSED), reduce-scatters
+ * and all-gathers of pieces of whole words run vector kernels on the pointers
+ * as given (a 16-byte access needs only 4-byte alignment), the last count mod
+ * lanes elements (the ends of each slice or piece) element-wise.  Other alignments take an element-wise
  * path.  Every path gives identical results.  Reading
  * through aligned 16-byte vectors, the reduce-scatter and all-gather may read
  * (never write) the rest of the 16-byte blocks that hold an input buffer's

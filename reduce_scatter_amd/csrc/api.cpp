@@ -116,10 +116,10 @@ bool tree_staged() {
     return e && *e == '1';
 }
 
-// AR_DWORD_VECTORS=0 sends all-reduces and reduce-scatters at mixed 16-byte
-// phases with 4-byte-aligned pointers back to the element-wise kernels (same
-// bits) instead of the vector kernels on the callers' pointers; read on every
-// call.
+// AR_DWORD_VECTORS=0 sends all-reduces, reduce-scatters and all-gathers at
+// mixed 16-byte phases with 4-byte-aligned pointers back to the element-wise
+// kernels (same bits) instead of the vector kernels on the callers' pointers;
+// read on every call.
 bool dword_vectors() {
     const char *e = getenv("AR_DWORD_VECTORS");
     return !(e && *e == '0');
@@ -644,7 +644,22 @@ ar_status_t ar_all_gather(const void *const *sendbufs, void *const *recvbufs, si
         // element-wise kernel the few elements at each piece's ends.  Mixed phases go element-wise.
         const long long R = (long long)sendcount, Rb = R * (long long)e;
         const int ps = one_phase(sendbufs, n), pr = one_phase((const void *const *)recvbufs, n);
-        if (ps < 0 || pr < 0) return hip_status(launch_elem_all_gather((int)e, t, g, R, stream));
+        if (ps < 0 || pr < 0) {
+            // Mixed phases with every pointer and the piece length whole 4-byte words: frame vector o of
+            // every output is at byte 16*o and its input bytes start at a 4-byte-aligned address, all that
+            // a 16-byte access needs, so the phased pass runs on the callers' pointers with one load per
+            // vector and no shift; the element-wise kernel takes each piece's ends.
+            if (misaligned(sendbufs, n, 4) || misaligned((const void *const *)recvbufs, n, 4) || Rb % 4 ||
+                !dword_vectors())
+                return hip_status(launch_elem_all_gather((int)e, t, g, R, stream));
+            g.slice_bytes = Rb;
+            g.phased_words = 2;
+            g.ref = (long long)((uintptr_t)recvbufs[0] >> 4);
+            if (aligned_tiles(Rb / 16, kFusedTile) > 0x7fffffffLL) return AR_ERR_UNSUPPORTED;
+            const hipError_t h = launch_fused_all_gather_phased(t, g, gather_lds_bytes(n, (double)n * Rb), stream);
+            if (h != hipSuccess) return hip_status(h);
+            return hip_status(launch_elem_all_gather_edges((int)e, t, g, R, stream));
+        }
         g.slice_bytes = Rb;
         g.out_off = pr > 0 ? 16 - pr : 0;
         g.in_off = ps;

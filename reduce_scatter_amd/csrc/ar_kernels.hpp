@@ -65,8 +65,9 @@ struct Geometry {
     long long last_off;     // phased: offset (from the table pointer) of the last 16-byte block holding input
     int phased_words;       // phased reduce-scatter, compile-time n: 0 funnel loads, 1 word-aligned loads where
                             // the phase is not whole words, 2 word-aligned loads everywhere (any n: always);
-                            // set to 2 by the caller for pointers at mixed phases (4-byte types), else chosen
-                            // at launch
+                            // set to 2 by the caller for pointers at mixed phases (4-byte aligned), else
+                            // chosen at launch; phased all-gather: 2 for pointers at mixed phases (one
+                            // word-aligned load per vector), else the funnel
 };
 
 // Tiles are cut on a grid aligned to absolute T-vector boundaries of a

@@ -340,15 +340,23 @@ __global__ __launch_bounds__(kFusedThreads) void fused_all_gather_phased_kernel(
 #pragma unroll
     for (int u = 0; u < U; ++u) off[u] = tile_lane(ts, ts.start + threadIdx.x + u * kFusedTile, ok[u]);
     const long long in = g.in_off + ts.lo * 16 - b0;                      // the tile's first input byte
-    const long long rel = g.last_off - (in & ~15LL);
-    const char *p = (const char *)t.src[k] + (in & ~15LL);
     u32x4 w[U];
+    if (g.phased_words == 2) {
+        // pointers at mixed phases, every one and the piece length whole words (the caller checked): the
+        // input bytes of every frame vector start at a 4-byte-aligned address, one load each
+        const char *p = (const char *)t.src[k] + in;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const unsigned hi_off = (long long)off[u] + 16 < rel ? off[u] + 16u : (unsigned)rel;
-        const u32x4 lo = *(const u32x4 *)(p + off[u]);                    // ordinary loads, as the aligned
-        const u32x4 hi = *(const u32x4 *)(p + hi_off);                    // all-gather reads its input
-        w[u] = funnel16(lo, hi, (unsigned)(in & 15));
+        for (int u = 0; u < U; ++u) w[u] = *(const u32x4d *)(p + off[u]);
+    } else {
+        const long long rel = g.last_off - (in & ~15LL);
+        const char *p = (const char *)t.src[k] + (in & ~15LL);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const unsigned hi_off = (long long)off[u] + 16 < rel ? off[u] + 16u : (unsigned)rel;
+            const u32x4 lo = *(const u32x4 *)(p + off[u]);                // ordinary loads, as the aligned
+            const u32x4 hi = *(const u32x4 *)(p + hi_off);                // all-gather reads its input
+            w[u] = funnel16(lo, hi, (unsigned)(in & 15));
+        }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -356,9 +364,9 @@ __global__ __launch_bounds__(kFusedThreads) void fused_all_gather_phased_kernel(
         const long long out = ts.lo * 16 + off[u];                        // in the output frame
         if constexpr (NR > 0) {
 #pragma unroll
-            for (int r = 0; r < NR; ++r) __builtin_nontemporal_store(w[u], (u32x4 *)((char *)t.dst[r] + out));
+            for (int r = 0; r < NR; ++r) __builtin_nontemporal_store(w[u], (u32x4d *)((char *)t.dst[r] + out));
         } else {
-            for (int r = 0; r < n; ++r) __builtin_nontemporal_store(w[u], (u32x4 *)((char *)t.dst[r] + out));
+            for (int r = 0; r < n; ++r) __builtin_nontemporal_store(w[u], (u32x4d *)((char *)t.dst[r] + out));
         }
     }
 }

@@ -534,6 +534,51 @@ def test_reduce_scatter_mixed_phases_dword_aligned(dtype, monkeypatch):
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
+def test_all_gather_mixed_phases_dword_aligned(dtype, monkeypatch):
+    """All-gather with every rank's input and output at its own 16-byte phase,
+    pointers and piece length whole 4-byte words: the phased kernel on the
+    callers' pointers with one word-aligned load per vector, the element-wise
+    kernel each piece's ends.  n from 2 to 24, pieces shorter than a vector up
+    to several tiles, out of place and in place, bit for bit against the
+    oracle and against the element-wise path."""
+    u = LANES[dtype]
+    w = u // 4                                          # elements per 4-byte word
+    for n in (2, 3, 8, 16, 17, 24):
+        for R in sorted({2, u * 5 + 2, 64 * u * 2 * 3 + 2, 64 * u * 7 + u}):
+            R = R - R % w if w > 1 else R               # whole words
+            pieces = inputs(150 + n, n, R, dtype, "sum")
+            want = oracle.ring_all_gather(pieces, dtype)
+            print("dword ag phases", dtype, "n=%d R=%d" % (n, R), flush=True)
+            for sched in ("fused", "ring"):
+                g_in = [_at_phase(x, dtype, w * (r % 4)) for r, x in enumerate(pieces)]
+                g_out = [_at_phase(np.zeros(n * R, dtype=pieces[0].dtype), dtype, w * ((3 * r + 2) % 4)) for r in range(n)]
+                ar.ar_all_gather(g_in, g_out, R, dtype, sched=sched)
+                sync()
+                for r in range(n):
+                    assert_bits_equal(to_host(g_out[r], dtype), want[r], "dword ag %s %s n=%d R=%d rank %d" % (
+                        sched, dtype, n, R, r))
+                # in place: rank r's piece already sits at its own place in its output
+                g_full = [_at_phase(np.concatenate(pieces), dtype, w * ((r + 1) % 4)) for r in range(n)]
+                ar.ar_all_gather([g_full[r][r * R:(r + 1) * R] for r in range(n)], g_full, R, dtype, sched=sched)
+                sync()
+                for r in (0, n // 2, n - 1):
+                    assert_bits_equal(to_host(g_full[r], dtype), want[r], "dword ag in place %s %s n=%d R=%d rank %d"
+                                      % (sched, dtype, n, R, r))
+    n, R = 8, 64 * u * 3 + 2 * w
+    pieces = inputs(159, n, R, dtype, "sum")
+    outs = []
+    for flag in ("1", "0"):
+        monkeypatch.setenv("AR_DWORD_VECTORS", flag)
+        g_in = [_at_phase(x, dtype, w * (r % 4)) for r, x in enumerate(pieces)]
+        g_out = [_at_phase(np.zeros(n * R, dtype=pieces[0].dtype), dtype, w * ((r + 3) % 4)) for r in range(n)]
+        ar.ar_all_gather(g_in, g_out, R, dtype, sched="fused")
+        sync()
+        outs.append([to_host(d, dtype) for d in g_out])
+    for r in range(n):
+        assert_bits_equal(outs[0][r], outs[1][r], "dword ag against element-wise rank %d" % r)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
 def test_reduce_scatter_and_all_gather_at_phases(dtype):
     """Inputs at one 16-byte phase and outputs at another (every pair of
     element offsets within a vector): the phased pass writes the output frame

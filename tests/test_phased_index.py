@@ -262,6 +262,43 @@ def test_mixed_phase_reduce_scatter_words_index_map(e):
             assert (writes == 1).all(), (n, R)
 
 
+@pytest.mark.parametrize("e", [2, 4])
+def test_mixed_phase_all_gather_words_index_map(e):
+    """All-gather at mixed phases with every pointer and the piece length whole 4-byte words: the phased
+    kernel on the callers' pointers (output frame from byte 0, piece k at bytes [k*R*e, (k+1)*R*e)), one
+    load per frame vector from its input bytes, every load 4-byte aligned and inside the piece; the
+    element-wise kernel takes each piece's ends; every output element is written once."""
+    rng = random.Random(7 + e)
+    u = 16 // e
+    for n in (1, 2, 3, 8, 9, 17):
+        for R in [2, 4, 6, 64 * u + 2, 2 * TILE * u - 2] + [2 * rng.randrange(1, 3 * TILE * u) for _ in range(4)]:
+            Rb = R * e
+            assert Rb % 4 == 0
+            src = [4 * rng.randrange(0, 1 << 18) for _ in range(n)]
+            ref = 4 * rng.randrange(0, 1 << 18) >> 4
+            U = library_u(n, "ag")
+            writes = np.zeros(n * R, dtype=np.int64)
+            most = Rb >> 4
+            for k in range(n):
+                b0 = k * Rb
+                vlo, vhi = (b0 + 15) >> 4, (b0 + Rb) >> 4
+                for j in range(aligned_tiles(most, TILE * U) if most > 0 else 0):
+                    start, lo, hi = aligned_tile(vlo, vhi, j, ref, TILE * U)
+                    if lo >= hi:
+                        continue
+                    off, ok = lanes(start, lo, hi, U)
+                    inb = lo * 16 - b0
+                    ld = src[k] + inb + off
+                    assert (ld % 4 == 0).all()
+                    assert ld.min() >= src[k] and (ld + 16).max() <= src[k] + Rb, (n, e, R, k, j)
+                    for q in lo + off[ok] // 16:
+                        writes[16 * q // e:16 * q // e + u] += 1
+                head, tail = (R, R) if vhi <= vlo else ((vlo * 16 - b0) // e, (vhi * 16 - b0) // e)
+                writes[k * R:k * R + head] += 1
+                writes[k * R + tail:k * R + R] += 1
+            assert (writes == 1).all(), (n, e, R)
+
+
 @pytest.mark.parametrize("mistake", [{"slack": 16}, {"edge_shift": 1}, {"edge_shift": -1},
                                      {"words": True, "shift_mask": 15}])
 def test_model_notices_planted_mistakes(mistake):
