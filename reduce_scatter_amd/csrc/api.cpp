@@ -125,6 +125,25 @@ bool dword_vectors() {
     return !(e && *e == '0');
 }
 
+// Whether an aligned fused reduce-scatter past 16 ranks takes the phased
+// kernel's layout (its word-aligned chain on aligned slices: four-wavefront
+// workgroups on consecutive tiles, one vector per lane, ranks in batches of 8)
+// instead of the any-n fused kernel's (one-wavefront workgroups, two vectors
+// per lane, batches of 8 ranks per vector pair).  Same hop order, same bits.
+// Measured on MI355X, % of peak (fused -> phased): bf16 n = 17 56.6 -> 70.7,
+// 24 65.3 -> 79.1, 32 70.3 -> 78.3, 72 67.8 -> 76.5, 100 72.9 -> 76.8; fp32
+// n = 17 66.7 -> 72.9, 20 71.0 -> 76.1, 33 71.9 -> 74.1, but 24 76.8 -> 75.7,
+// 40 78.2 -> 75.8, 48 79.9 -> 77.5, 65 74.8 -> 71.7, 72 77.6 -> 75.7, 100
+// 79.0 -> 77.5, 128 80.3 -> 78.8; up to 16 ranks the fused kernels lead or
+// tie.  AR_RS_PHASED=0|1 overrides (read on every call).
+bool rs_through_phased(int n, ar_dtype_t dt) {
+    const char *e = getenv("AR_RS_PHASED");
+    if (e && (*e == '0' || *e == '1')) return *e == '1';
+    if (n <= 16) return false;
+    if (dt == AR_BFLOAT16 || dt == AR_FLOAT16) return true;
+    return n <= 35 && n % 8 != 0;
+}
+
 // Dynamic LDS reservation (bytes) of the ring / tree workgroups; the
 // AR_RING_LDS_KB variable overrides the default.
 int env_kb(const char *name, int dflt) {
@@ -601,6 +620,12 @@ ar_status_t ar_reduce_scatter_ex(const void *const *sendbufs, void *const *recvb
     g.ref = (long long)((uintptr_t)sendbufs[0] >> 4);          // fused tiles follow the input slices' alignment
     if (use == AR_SCHED_FUSED) {
         if (aligned_tiles(g.Rv, kFusedTile) > 0x7fffffffLL) return AR_ERR_UNSUPPORTED;   // grid x limit
+        if (rs_through_phased(n, dtype)) {
+            g.slice_bytes = (long long)recvcount * (long long)e;
+            g.phased_words = 2;
+            return hip_status(launch_fused_reduce_scatter_phased(dtype, op, t, g,
+                                                                 fused_lds_bytes(AR_COLL_REDUCE_SCATTER, n), stream));
+        }
         return hip_status(launch_fused_reduce_scatter(dtype, op, t, g, fused_lds_bytes(AR_COLL_REDUCE_SCATTER, n),
                                                       stream));
     }

@@ -229,6 +229,29 @@ def test_split_many_ranks_every_op(dtype):
                 assert_bits_equal(want, oracle.direct_reduce(xs, dtype, op), "split exact")
 
 
+@pytest.mark.parametrize("layout", ["default", "0", "1"])
+def test_reduce_scatter_many_ranks_both_layouts(layout, monkeypatch):
+    """Aligned reduce-scatter past 16 ranks through the any-n fused kernel
+    (AR_RS_PHASED=0), the phased kernel's layout (1) and the default choice
+    between them: every dtype, rank counts on both sides of the choice, whole
+    tiles and a partial one, fused and ring schedules, bit for bit against
+    the oracle."""
+    if layout != "default":
+        monkeypatch.setenv("AR_RS_PHASED", layout)
+    for dtype in DTYPES:
+        u = LANES[dtype]
+        R = 64 * u * 3 + u
+        for n in (17, 20, 24, 33, 40, 72, 128):
+            op = OPS[(n + u) % len(OPS)]
+            print("rs many ranks", layout, dtype, op, "n=%d R=%d" % (n, R), flush=True)
+            xs = inputs(170 + n, n, n * R, dtype, op)
+            ref = oracle.ring_reduce_scatter(xs, dtype, op)
+            for sched in ("fused",) if n in (40, 128) else ("fused", "ring"):
+                got = run_rs(xs, dtype, op, sched)
+                for r in range(n):
+                    assert_bits_equal(got[r], ref[r], "rs %s %s %s n=%d rank %d" % (layout, dtype, op, n, r))
+
+
 def _at_offset(x, dtype, off_bytes):
     """A device copy of host array x starting off_bytes past a fresh allocation."""
     pad = off_bytes // (4 if dtype in ("f32", "i32") else 2)
