@@ -211,9 +211,9 @@ def kernel_calls(reps=5):
     n72, c72 = 72, 25 * MB // 4                             # 72 ranks, one 25 MB fp32 bucket, in place
     bufs_t = [wl.device_normal(4, 1, r, c72, 1e-3, "f32") for r in range(n72)]
     bufs = ar.pointers(bufs_t)
-    for sched, kern in (("split", "split_allreduce_kernel"), ("fused", "fused_allreduce_wide_kernel")):
-        run("all-reduce n=72 f32 25MB/rank avg in place, %s" % sched, kern, 2 * n72 * c72 * 4,
-            lambda: ar.ar_allreduce(bufs, bufs, c72, "f32", "avg", sched=sched))
+    run("all-reduce n=72 f32 25MB/rank avg in place, split", "split_allreduce_kernel", 2 * n72 * c72 * 4,
+        lambda: ar.ar_allreduce(bufs, bufs, c72, "f32", "avg", sched="split"))
+    halves_rows(run, ar, bufs, 72, c72, "25MB")
     # the tree past 16 ranks: the streaming walk, then the LDS-staged kernels (each forced)
     run("all-reduce n=72 f32 25MB/rank avg in place, tree (streamed)", "tree_stream_kernel", 2 * n72 * c72 * 4,
         lambda: ar.ar_allreduce(bufs, bufs, c72, "f32", "avg", sched="tree"))
@@ -240,12 +240,26 @@ def kernel_calls(reps=5):
     n128, c128 = 128, 8 * MB // 4                           # 128 ranks, 8 MB per rank, in place
     bufs_t = [wl.device_normal(4, 2, r, c128, 1e-3, "f32") for r in range(n128)]
     bufs = ar.pointers(bufs_t)
-    for sched, kern in (("tree", "tree_stream_kernel"), ("fused", "fused_allreduce_wide_kernel"),
-                        ("split", "split_allreduce_kernel")):
+    for sched, kern in (("tree", "tree_stream_kernel"), ("split", "split_allreduce_kernel")):
         run("all-reduce n=128 f32 8MB/rank avg in place, %s" % sched, kern, 2 * n128 * c128 * 4,
             lambda: ar.ar_allreduce(bufs, bufs, c128, "f32", "avg", sched=sched))
+    halves_rows(run, ar, bufs, 128, c128, "8MB")
     del bufs, bufs_t
     torch.cuda.empty_cache()
+
+
+def halves_rows(run, ar, bufs, n, count, size):
+    """The fused schedule past 16 ranks: its reduce-scatter and all-gather halves (one call launches both; each
+    kernel's row carries its own algorithmic bytes: (n+1)*S, then S read and (n-1)*S written), then the wide
+    one-pass kernel (AR_AR_HALVES=0, 2*n*S)."""
+    S = count * 4
+    run("all-reduce n=%d f32 %s/rank avg in place, fused (reduce-scatter half, all-gather half)" % (n, size),
+        ["fused_reduce_scatter_phased_kernel", "allreduce_chunk_gather_kernel"], [(n + 1) * S, n * S],
+        lambda: ar.ar_allreduce(bufs, bufs, count, "f32", "avg", sched="fused"))
+    os.environ["AR_AR_HALVES"] = "0"
+    run("all-reduce n=%d f32 %s/rank avg in place, fused (one pass)" % (n, size), "fused_allreduce_wide_kernel",
+        2 * n * S, lambda: ar.ar_allreduce(bufs, bufs, count, "f32", "avg", sched="fused"))
+    os.environ.pop("AR_AR_HALVES", None)
 
 
 def _median_us(fn, iters=10, warmup=2):

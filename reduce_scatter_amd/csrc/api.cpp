@@ -125,6 +125,20 @@ bool dword_vectors() {
     return !(e && *e == '0');
 }
 
+// Whether a fused all-reduce past 16 ranks runs as the reduce-scatter half
+// (the phased kernel's layout over the all-reduce's own chunks, each finished
+// chunk stored to its owner) then the all-gather half (each chunk copied from
+// its owner to the other ranks), instead of the wide one-pass kernel: S more
+// bytes than the 2*n*S of one pass, the same hop order and bits.  Measured on
+// MI355X, 25 MB per rank in place, % of peak (wide -> halves; split on the same
+// box): fp32 n = 24 62.0 -> 63.5 (70.1), 72 60.7 -> 66.6 (67.3), 128 61.2 ->
+// 68.9 (65.2); bf16 n = 33 60.1 -> 67.4 (68.4), 72 60.0 -> 70.8 (66.3).
+// AR_AR_HALVES=0 keeps the wide kernel (read on every call).
+bool allreduce_halves() {
+    const char *e = getenv("AR_AR_HALVES");
+    return !(e && *e == '0');
+}
+
 // Whether an aligned fused reduce-scatter past 16 ranks takes the phased
 // kernel's layout (its word-aligned chain on aligned slices: four-wavefront
 // workgroups on consecutive tiles, one vector per lane, ranks in batches of 8)
@@ -448,7 +462,11 @@ ar_status_t ar_allreduce_ex(const void *const *sendbufs, void *const *recvbufs, 
             const long long maxlen = (g.V + n - 1) / n;                       // longest chunk, in vectors
             g.windows = aligned_tiles(maxlen, kFusedTile);
             if (g.windows > 0x7fffffffLL) return AR_ERR_UNSUPPORTED;   // grid x limit
-            h = launch_fused_allreduce(dtype, op, tv, g, fused_lds_bytes(AR_COLL_ALLREDUCE, n), stream);
+            if (n > 16 && g.shift == 0 && allreduce_halves())
+                h = launch_allreduce_halves(dtype, op, tv, g, fused_lds_bytes(AR_COLL_REDUCE_SCATTER, n),
+                                            gather_lds_bytes(n, (double)count * (double)e), stream);
+            else
+                h = launch_fused_allreduce(dtype, op, tv, g, fused_lds_bytes(AR_COLL_ALLREDUCE, n), stream);
         } else if (use == AR_SCHED_RING) {
             g.W = lds_window(n);
             const long long maxlen = (g.V + n - 1) / n;

@@ -63,6 +63,8 @@ struct Geometry {
     long long in_off;       // phased: byte offset of the first input byte past the (16-byte aligned) table pointer
     long long out_off;      // phased: byte offset of output vector 0 past the caller's output pointer
     long long last_off;     // phased: offset (from the table pointer) of the last 16-byte block holding input
+    int ar_chunks;          // phased reduce-scatter: slice c is all-reduce chunk c (vectors [floor(c*V/n),
+                            // floor((c+1)*V/n)) of every rank, from q and rem), stored to dst[c] at its offset
     int phased_words;       // phased reduce-scatter, compile-time n: 0 funnel loads, 1 word-aligned loads where
                             // the phase is not whole words, 2 word-aligned loads everywhere (any n: always);
                             // set to 2 by the caller for pointers at mixed phases (4-byte aligned), else
@@ -135,6 +137,8 @@ hipError_t launch_fused_all_gather(const RankTable &t, const Geometry &g, int ld
 hipError_t launch_fused_reduce_scatter_phased(int dt, int op, const RankTable &t, const Geometry &g, int lds,
                                               hipStream_t s);
 hipError_t launch_fused_all_gather_phased(const RankTable &t, const Geometry &g, int lds, hipStream_t s);
+hipError_t launch_allreduce_halves(int dt, int op, const RankTable &t, const Geometry &g, int lds_rs, int lds_ag,
+                                   hipStream_t s);
 // Fused pass in the aligned pairwise order over ranks (all-reduce only): one
 // workgroup of ceil(n / K) waves per 64-vector tile of [0, Vfull).
 hipError_t launch_split_allreduce(int dt, int op, const RankTable &t, const Geometry &g, hipStream_t s);

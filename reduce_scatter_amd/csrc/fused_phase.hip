@@ -253,6 +253,12 @@ template <int NR> struct PhasedTile {
     static constexpr int U = (NR > 0 && NR <= 8) ? 2 : 1;
 };
 
+// Start of all-reduce chunk c in vectors, floor(c*V/n), as c*q + floor(c*rem/n).
+__device__ __forceinline__ long long ar_chunk_lo(int c, const Geometry &g) {
+    const long long b = (long long)c * g.q;
+    return g.rem ? b + (long long)((unsigned)(c * g.rem) / (unsigned)g.n) : b;
+}
+
 template <int DT, int OP, int NR, bool KEEP32>
 __device__ __forceinline__ void rs_phased(const RankTableFor<NR> &t, const Geometry &g) {
     constexpr int U = PhasedTile<NR>::U;
@@ -261,13 +267,19 @@ __device__ __forceinline__ void rs_phased(const RankTableFor<NR> &t, const Geome
     // a workgroup of blockDim.x / 64 wavefronts takes that many consecutive tiles, one per wavefront
     const long long j = (long long)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
     const unsigned lane = threadIdx.x & 63u;
-    const TileSpan ts = aligned_tile(0, g.Rv, j, (long long)((uintptr_t)t.dst[c] >> 4), kFusedTile * U);
+    long long lo = 0, hi = g.Rv;
+    if (g.ar_chunks) {                                       // all-reduce chunk c, at its own offset
+        lo = ar_chunk_lo(c, g);
+        hi = ar_chunk_lo(c + 1, g);
+        hi = hi < g.Vfull ? hi : g.Vfull;
+    }
+    const TileSpan ts = aligned_tile(lo, hi, j, (long long)((uintptr_t)t.dst[c] >> 4), kFusedTile * U);
     if (ts.lo >= ts.hi) return;
     unsigned off[U];
     bool ok[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) off[u] = tile_lane(ts, ts.start + lane + u * kFusedTile, ok[u]);
-    const long long a = g.in_off + (long long)c * g.slice_bytes + ts.lo * 16;     // the tile's first input byte
+    const long long a = g.ar_chunks ? ts.lo * 16 : g.in_off + (long long)c * g.slice_bytes + ts.lo * 16;  // first input byte
     const long long rel = g.last_off - (a & ~15LL);                             // last block, from the tile base
     Pack<DT> acc[U];
     const bool whole = ts.lo == ts.start && ts.hi == ts.start + kFusedTile * U;
@@ -371,6 +383,36 @@ __global__ __launch_bounds__(kFusedThreads) void fused_all_gather_phased_kernel(
     }
 }
 
+// The all-gather half of an all-reduce run as reduce-scatter then
+// all-gather: chunk c (grid y), finished in rank c's output by the
+// reduce-scatter half, copied to every other rank's output at the same
+// offset.  Tiles of 64*U vectors follow rank 0's output (g.ref); the loads are
+// ordinary (the chunk was just written and sits in the caches).
+template <int U>
+__global__ __launch_bounds__(kFusedThreads) void allreduce_chunk_gather_kernel(const RankTable t, const Geometry g) {
+    const int n = g.n;
+    const int c = (int)blockIdx.y;
+    long long hi = ar_chunk_lo(c + 1, g);
+    hi = hi < g.Vfull ? hi : g.Vfull;
+    const TileSpan ts = aligned_tile(ar_chunk_lo(c, g), hi, (long long)blockIdx.x, g.ref, kFusedTile * U);
+    if (ts.lo >= ts.hi) return;
+    unsigned off[U];
+    bool ok[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) off[u] = tile_lane(ts, ts.start + threadIdx.x + u * kFusedTile, ok[u]);
+    const long long base = ts.lo * 16;
+    const char *p = (const char *)t.dst[c] + base;
+    u32x4 w[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) w[u] = *(const u32x4d *)(p + off[u]);
+    for (int r = 0; r < n; ++r) {
+        if (r == c) continue;
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (ok[u]) __builtin_nontemporal_store(w[u], (u32x4d *)((char *)t.dst[r] + base + off[u]));
+    }
+}
+
 // Wavefronts per workgroup of the phased reduce-scatter, and the LDS each
 // workgroup reserves.  The input line where two tiles meet is fetched once per
 // L2 that needs it: with one-wave workgroups neighbouring tiles run on
@@ -452,6 +494,24 @@ hipError_t launch_fused_reduce_scatter_phased(int dt, int op, const RankTable &t
                           grid, dim3(kFusedThreads * waves), (size_t)lds_wg, s, narrow<NR>(t), gw);
         });
     });
+}
+
+// All-reduce past 16 ranks in ring order as reduce-scatter then all-gather:
+// the phased reduce-scatter's layout over the all-reduce's own chunks (each
+// finished chunk stored to its owner only), then each chunk copied from its
+// owner to the other ranks.  Whole vectors [0, g.Vfull) only.
+hipError_t launch_allreduce_halves(int dt, int op, const RankTable &t, const Geometry &g, int lds_rs, int lds_ag,
+                                   hipStream_t s) {
+    if (g.Vfull <= 0) return hipSuccess;
+    Geometry gr = g;
+    gr.ar_chunks = 1;
+    gr.phased_words = 2;
+    gr.Rv = (g.V + g.n - 1) / g.n;                           // the longest chunk, in vectors: sizes the grid
+    hipError_t h = launch_fused_reduce_scatter_phased(dt, op, t, gr, lds_rs, s);
+    if (h != hipSuccess) return h;
+    constexpr int U = 2;
+    const dim3 grid((unsigned)aligned_tiles(gr.Rv, (long long)kFusedTile * U), (unsigned)g.n);
+    return launch(allreduce_chunk_gather_kernel<U>, grid, dim3(kFusedThreads), (size_t)lds_ag, s, t, g);
 }
 
 hipError_t launch_fused_all_gather_phased(const RankTable &t, const Geometry &g, int lds, hipStream_t s) {

@@ -252,6 +252,31 @@ def test_reduce_scatter_many_ranks_both_layouts(layout, monkeypatch):
                     assert_bits_equal(got[r], ref[r], "rs %s %s %s n=%d rank %d" % (layout, dtype, op, n, r))
 
 
+@pytest.mark.parametrize("halves", ["default", "0"])
+def test_allreduce_many_ranks_halves(halves, monkeypatch):
+    """The fused all-reduce past 16 ranks as reduce-scatter half then
+    all-gather half over the all-reduce's own chunks (the default), and as the
+    wide one-pass kernel (AR_AR_HALVES=0): every dtype, ragged counts (chunks
+    of unequal length, a partial last vector), in and out of place, bit for
+    bit against the ring oracle, every rank checked."""
+    if halves != "default":
+        monkeypatch.setenv("AR_AR_HALVES", halves)
+    for dtype in DTYPES:
+        u = LANES[dtype]
+        for n in (17, 24, 33, 72, 128):
+            count = 64 * u * 2 * n + u * (n // 3) + 5
+            op = OPS[(n + u) % len(OPS)]
+            print("ar halves", halves, dtype, op, "n=%d count=%d" % (n, count), flush=True)
+            xs = inputs(190 + n, n, count, dtype, op)
+            ref = oracle.ring_allreduce(xs, dtype, op)
+            got = run_allreduce(xs, dtype, op, "fused")
+            for r in range(n):
+                assert_bits_equal(got[r], ref[r], "ar %s %s %s n=%d rank %d" % (halves, dtype, op, n, r))
+            got = run_allreduce(xs, dtype, op, "fused", inplace=True)
+            for r in (0, n // 2, n - 1):
+                assert_bits_equal(got[r], ref[r], "ar in place %s %s %s n=%d rank %d" % (halves, dtype, op, n, r))
+
+
 def _at_offset(x, dtype, off_bytes):
     """A device copy of host array x starting off_bytes past a fresh allocation."""
     pad = off_bytes // (4 if dtype in ("f32", "i32") else 2)
