@@ -277,6 +277,34 @@ def test_allreduce_many_ranks_halves(halves, monkeypatch):
                 assert_bits_equal(got[r], ref[r], "ar in place %s %s %s n=%d rank %d" % (halves, dtype, op, n, r))
 
 
+@pytest.mark.parametrize("halves", ["default", "0"])
+def test_fused_many_ranks_tiny_counts(halves, monkeypatch):
+    """The fused all-reduce and reduce-scatter past 16 ranks at counts where
+    most chunks hold no vector or one (fewer vectors than ranks, a partial last
+    vector, a count below one vector), both all-reduce paths, against the
+    oracle bit for bit."""
+    if halves != "default":
+        monkeypatch.setenv("AR_AR_HALVES", halves)
+        monkeypatch.setenv("AR_RS_PHASED", "0")
+    for dtype in ("f32", "bf16"):
+        u = LANES[dtype]
+        for n in (17, 72, 128):
+            for count in sorted({1, 3, u + 1, u * (n // 2) + 1, u * n - 1, u * n + 1, u * (n + 1)}):
+                op = OPS[(n + count) % len(OPS)]
+                xs = inputs(210 + count % 97, n, count, dtype, op)
+                ref = oracle.ring_allreduce(xs, dtype, op)
+                got = run_allreduce(xs, dtype, op, "fused")
+                for r in (0, n // 2, n - 1):
+                    assert_bits_equal(got[r], ref[r], "ar tiny %s %s %s n=%d count=%d rank %d" % (
+                        halves, dtype, op, n, count, r))
+            for R in (u, 2 * u):
+                xs = inputs(220 + R, n, n * R, dtype, "sum")
+                ref = oracle.ring_reduce_scatter(xs, dtype, "sum")
+                got = run_rs(xs, dtype, "sum", "fused")
+                for r in range(n):
+                    assert_bits_equal(got[r], ref[r], "rs tiny %s %s n=%d R=%d rank %d" % (halves, dtype, n, R, r))
+
+
 def _at_offset(x, dtype, off_bytes):
     """A device copy of host array x starting off_bytes past a fresh allocation."""
     pad = off_bytes // (4 if dtype in ("f32", "i32") else 2)
