@@ -91,6 +91,35 @@ def test_tree_walk_captured(sched):
     _replays(g, xs, ys, eager)
 
 
+def test_many_rank_fused_halves_captured():
+    """The fused all-reduce past 16 ranks (reduce-scatter half then all-gather
+    half: two launches, a ragged count) and the aligned reduce-scatter through
+    the phased layout at 24 ranks (bf16), captured and replayed."""
+    n, count = 40, (3 << 20) // 4 + 5
+    xs = [torch.empty(count, device="cuda") for _ in range(n)]
+    ys = [torch.empty(count, device="cuda") for _ in range(n)]
+    X, Y = ar.pointers(xs), ar.pointers(ys)
+    g = _capture(lambda: ar.ar_allreduce(X, Y, count, "f32", "avg", sched="fused"))
+
+    def eager():
+        zs = [torch.empty_like(y) for y in ys]
+        ar.ar_allreduce([x.clone() for x in xs], zs, count, "f32", "avg", sched="fused")
+        return zs
+    _replays(g, xs, ys, eager)
+
+    n, R = 24, 8192 + 8
+    xs = [torch.empty(n * R, dtype=torch.bfloat16, device="cuda") for _ in range(n)]
+    ys = [torch.empty(R, dtype=torch.bfloat16, device="cuda") for _ in range(n)]
+    X, Y = ar.pointers(xs), ar.pointers(ys)
+    g = _capture(lambda: ar.ar_reduce_scatter(X, Y, R, "bf16", "sum", sched="fused"))
+
+    def eager_rs():
+        zs = [torch.empty_like(y) for y in ys]
+        ar.ar_reduce_scatter([x.clone() for x in xs], zs, R, "bf16", "sum", sched="fused")
+        return zs
+    _replays(g, xs, ys, eager_rs)
+
+
 def test_reduce_scatter_then_all_gather_captured():
     n, R = 8, 4096 + 64
     xs = [torch.empty(n * R, dtype=torch.bfloat16, device="cuda") for _ in range(n)]
