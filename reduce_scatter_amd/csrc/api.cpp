@@ -462,7 +462,7 @@ ar_status_t ar_allreduce_ex(const void *const *sendbufs, void *const *recvbufs, 
             const long long maxlen = (g.V + n - 1) / n;                       // longest chunk, in vectors
             g.windows = aligned_tiles(maxlen, kFusedTile);
             if (g.windows > 0x7fffffffLL) return AR_ERR_UNSUPPORTED;   // grid x limit
-            if (n > 16 && g.shift == 0 && allreduce_halves())
+            if (n > 16 && allreduce_halves())
                 h = launch_allreduce_halves(dtype, op, tv, g, fused_lds_bytes(AR_COLL_REDUCE_SCATTER, n),
                                             gather_lds_bytes(n, (double)count * (double)e), stream);
             else

@@ -270,7 +270,7 @@ __device__ __forceinline__ void rs_phased(const RankTableFor<NR> &t, const Geome
     long long lo = 0, hi = g.Rv;
     if (g.ar_chunks) {                                       // all-reduce chunk c, at its own offset
         lo = ar_chunk_lo(c, g);
-        hi = ar_chunk_lo(c + 1, g);
+        hi = ar_chunk_lo(c + 1, g) - g.shift;               // shifted frame: the vector across the end is not c's
         hi = hi < g.Vfull ? hi : g.Vfull;
     }
     const TileSpan ts = aligned_tile(lo, hi, j, (long long)((uintptr_t)t.dst[c] >> 4), kFusedTile * U);
@@ -392,7 +392,7 @@ template <int U>
 __global__ __launch_bounds__(kFusedThreads) void allreduce_chunk_gather_kernel(const RankTable t, const Geometry g) {
     const int n = g.n;
     const int c = (int)blockIdx.y;
-    long long hi = ar_chunk_lo(c + 1, g);
+    long long hi = ar_chunk_lo(c + 1, g) - g.shift;
     hi = hi < g.Vfull ? hi : g.Vfull;
     const TileSpan ts = aligned_tile(ar_chunk_lo(c, g), hi, (long long)blockIdx.x, g.ref, kFusedTile * U);
     if (ts.lo >= ts.hi) return;
@@ -499,7 +499,9 @@ hipError_t launch_fused_reduce_scatter_phased(int dt, int op, const RankTable &t
 // All-reduce past 16 ranks in ring order as reduce-scatter then all-gather:
 // the phased reduce-scatter's layout over the all-reduce's own chunks (each
 // finished chunk stored to its owner only), then each chunk copied from its
-// owner to the other ranks.  Whole vectors [0, g.Vfull) only.
+// owner to the other ranks.  Whole vectors [0, g.Vfull) only; in the shifted
+// frame (g.shift = 1) each chunk's vectors stop before the one across its end,
+// as in the one-pass kernel, and the element-wise kernel takes the rest.
 hipError_t launch_allreduce_halves(int dt, int op, const RankTable &t, const Geometry &g, int lds_rs, int lds_ag,
                                    hipStream_t s) {
     if (g.Vfull <= 0) return hipSuccess;
